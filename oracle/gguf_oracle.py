@@ -1,0 +1,339 @@
+"""CPU fp64 oracle for GGUF block-quantized matrix-vector products.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, links or calls
+this module: only tests/, __graft_entry__.smoke() and the cpu_baseline leg of
+bench.py may. It shares no code with the HIP library (no helpers, no tables, no
+constants); the only code both sides consume is the seeded input generator in
+synth/.
+
+What is computed, and where it comes from
+-----------------------------------------
+The memra pages (memra README: the model support table lists Q8_0 and Q4_K_M
+GGUF models, dense and MoE; the speed table's 35B-A3B MoE decode row; the
+memra-bench card, "Drafts": Q4_K_M draft blocks measured faster than Q8_0 and
+K=2..3 speculative drafts) name the formats and the workloads but print no block
+layout, no kernel and no formula. The operation they rest on has a plain
+definition -- a dense matrix product whose weights are the dequantized block
+values -- so this oracle is that definition written out in fp64:
+
+* decode each weight exactly from the stored bytes (every Q8_0 and Q4_K weight
+  is an integer multiple of 2^-24 below 2^50, so fp64 holds it exactly);
+* multiply with numpy's fp64 matmul (a library primitive);
+* MoE: top-k routing on the fp32 logits, softmax renormalised over the k
+  selected experts, silu(gate) * up, down, weighted sum in rank order;
+* prefill: the same product for many rows, plus the variant whose weights are
+  first rounded to fp32 and then to bf16 (the prescribed bf16 tile).
+
+The byte layouts are the public GGUF ones (Q8_0: fp16 d + 32 int8; Q4_K: fp16
+d, fp16 dmin, 12 bytes of packed 6-bit scales and mins, 128 bytes of nibbles),
+restated in this module's own words next to the code that reads them.
+
+Parity pins live in tests/test_oracle_*.py (hand-built blocks written as hex,
+locality invariants, pack/unpack bijection, requantisation round trips, exact
+rational brute force, closed forms, MoE = weighted dense sum).
+
+Parity unpinned: that the Q4_K 6-bit scale/min packing and nibble order used
+here equal those of real llama.cpp-written GGUF tensors. No GGUF file, gguf
+package or llama.cpp is in reach, and the pages print no block bytes, so every
+in-repository check would also pass with a self-consistent mis-layout.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# scalar formats
+# ----------------------------------------------------------------------------
+
+
+def fp16_bits_to_f64(bits) -> np.ndarray:
+    """IEEE binary16 (little-endian bit patterns, subnormals honoured) -> float64."""
+    return np.asarray(bits, dtype=np.uint16).view("<f2").astype(np.float64)
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 (exact: a bf16 is the top half of an fp32)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view("<f4").astype(np.float64)
+
+
+def round_to_f32(values) -> np.ndarray:
+    """Round float64 values to the nearest fp32 (ties to even), returned as fp32."""
+    return np.asarray(values, dtype=np.float64).astype(np.float32)
+
+
+def round_f32_to_bf16_bits(values_f32) -> np.ndarray:
+    """Round fp32 values to the nearest bfloat16 (ties to even); returns uint16 bits.
+
+    Uses torch's CPU bf16 conversion as the library primitive.
+    """
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(values_f32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+# ----------------------------------------------------------------------------
+# Q8_0: 34-byte blocks of 32 weights along K
+# ----------------------------------------------------------------------------
+
+Q8_0_BLOCK_BYTES = 34
+Q8_0_BLOCK_WEIGHTS = 32
+
+
+def _as_bytes(raw) -> np.ndarray:
+    return np.frombuffer(raw, dtype=np.uint8) if isinstance(raw, (bytes, bytearray)) else np.asarray(raw, dtype=np.uint8).reshape(-1)
+
+
+def q8_0_fields(raw, n_rows: int, k: int):
+    """Split a row-major Q8_0 matrix into (d [N, K/32] float64, q [N, K/32, 32] int64).
+
+    Block t of row n starts at byte (n*K/32 + t)*34; bytes 0..1 hold the
+    little-endian fp16 scale d, bytes 2..33 the signed int8 quants q_0..q_31.
+    """
+    if k % Q8_0_BLOCK_WEIGHTS:
+        raise ValueError("Q8_0 needs K to be a multiple of 32")
+    nb = k // Q8_0_BLOCK_WEIGHTS
+    b = _as_bytes(raw)
+    if b.size != n_rows * nb * Q8_0_BLOCK_BYTES:
+        raise ValueError("byte count does not match the Q8_0 shape")
+    blocks = b.reshape(n_rows, nb, Q8_0_BLOCK_BYTES)
+    d_bits = blocks[:, :, 0].astype(np.uint16) | (blocks[:, :, 1].astype(np.uint16) << 8)
+    d = fp16_bits_to_f64(d_bits)
+    q = blocks[:, :, 2:].view(np.int8).astype(np.int64)
+    return d, q
+
+
+def dequant_q8_0(raw, n_rows: int, k: int) -> np.ndarray:
+    """Exact Q8_0 weights: w[n, 32t + j] = d[n, t] * q[n, t, j]  (float64 [N, K])."""
+    d, q = q8_0_fields(raw, n_rows, k)
+    return (d[:, :, None] * q).reshape(n_rows, k)
+
+
+# ----------------------------------------------------------------------------
+# Q4_K: 144-byte super-blocks of 256 weights along K
+# ----------------------------------------------------------------------------
+
+Q4_K_BLOCK_BYTES = 144
+Q4_K_BLOCK_WEIGHTS = 256
+
+
+def q4_k_fields(raw, n_rows: int, k: int):
+    """Decode a row-major Q4_K matrix into its fields.
+
+    Returns (d, dmin, sc, m, q):
+      d, dmin : float64 [N, nb]      the two fp16 super-block scales
+      sc, m   : int64   [N, nb, 8]   6-bit scale and min of sub-block j = 0..7
+      q       : int64   [N, nb, 256] the 4-bit quant of each weight, in weight order
+
+    Byte layout of one super-block (block b of row n starts at (n*K/256 + b)*144):
+      0..1    fp16 d (little-endian)        2..3   fp16 dmin
+      4..15   S[0..11]: packed scales/mins  16..143 Q[0..127]: packed nibbles
+    Scales and mins: for sub-blocks j < 4, sc_j is the low 6 bits of S[j] and
+    m_j the low 6 bits of S[j+4]. For j >= 4 the low 4 bits come from S[j+4]
+    (its low nibble for sc_j, its high nibble for m_j) and the top 2 bits come
+    from the otherwise unused top 2 bits of S[j-4] (for sc_j) and S[j] (for m_j).
+    Quants: the 256 weights form four 64-weight chunks c; byte Q[32c + l] holds
+    weight 64c + l in its low nibble and weight 64c + 32 + l in its high nibble.
+    """
+    if k % Q4_K_BLOCK_WEIGHTS:
+        raise ValueError("Q4_K needs K to be a multiple of 256")
+    nb = k // Q4_K_BLOCK_WEIGHTS
+    b = _as_bytes(raw)
+    if b.size != n_rows * nb * Q4_K_BLOCK_BYTES:
+        raise ValueError("byte count does not match the Q4_K shape")
+    blocks = b.reshape(n_rows, nb, Q4_K_BLOCK_BYTES).astype(np.int64)
+
+    d = fp16_bits_to_f64((blocks[:, :, 0] | (blocks[:, :, 1] << 8)).astype(np.uint16))
+    dmin = fp16_bits_to_f64((blocks[:, :, 2] | (blocks[:, :, 3] << 8)).astype(np.uint16))
+
+    S = blocks[:, :, 4:16]
+    sc = np.empty((n_rows, nb, 8), dtype=np.int64)
+    m = np.empty((n_rows, nb, 8), dtype=np.int64)
+    for j in range(4):
+        sc[:, :, j] = S[:, :, j] & 0x3F
+        m[:, :, j] = S[:, :, j + 4] & 0x3F
+    for j in range(4, 8):
+        sc[:, :, j] = (S[:, :, j + 4] & 0x0F) | ((S[:, :, j - 4] >> 6) << 4)
+        m[:, :, j] = (S[:, :, j + 4] >> 4) | ((S[:, :, j] >> 6) << 4)
+
+    Q = blocks[:, :, 16:]
+    q = np.empty((n_rows, nb, 256), dtype=np.int64)
+    for c in range(4):
+        byte = Q[:, :, 32 * c: 32 * c + 32]
+        q[:, :, 64 * c: 64 * c + 32] = byte & 0x0F
+        q[:, :, 64 * c + 32: 64 * c + 64] = byte >> 4
+    return d, dmin, sc, m, q
+
+
+def dequant_q4_k(raw, n_rows: int, k: int) -> np.ndarray:
+    """Exact Q4_K weights: w = d * sc_j * q - dmin * m_j for weight i of sub-block j.
+
+    float64 [N, K]; weight 256b + 32j + i of row n.
+    """
+    d, dmin, sc, m, q = q4_k_fields(raw, n_rows, k)
+    nb = k // Q4_K_BLOCK_WEIGHTS
+    scale = (d[:, :, None] * sc).repeat(32, axis=2)      # [N, nb, 256]
+    offset = (dmin[:, :, None] * m).repeat(32, axis=2)
+    return (scale * q - offset).reshape(n_rows, nb * 256)
+
+
+def dequant_q4_k_f32(raw, n_rows: int, k: int) -> np.ndarray:
+    """The fp32 dequantization target: each exact weight rounded once to fp32."""
+    return round_to_f32(dequant_q4_k(raw, n_rows, k))
+
+
+def dequant_q8_0_f32(raw, n_rows: int, k: int) -> np.ndarray:
+    """Q8_0 weights in fp32 (exact: d has 11 significant bits, q at most 7)."""
+    return round_to_f32(dequant_q8_0(raw, n_rows, k))
+
+
+def dequant_q4_k_bf16_bits(raw, n_rows: int, k: int) -> np.ndarray:
+    """The bf16 tile target: RN_bf16(RN_fp32(w)), as uint16 bit patterns."""
+    return round_f32_to_bf16_bits(dequant_q4_k_f32(raw, n_rows, k))
+
+
+# ----------------------------------------------------------------------------
+# matrix-vector products (decode and speculative verify)
+# ----------------------------------------------------------------------------
+
+
+def gemv(w: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """y[r, n] = sum_k w[n, k] * x[r, k] in float64 (x: [M, K] or [K])."""
+    x2 = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    return x2 @ np.asarray(w, dtype=np.float64).T
+
+
+def qmv_q8_0(raw, x_f32, n_rows: int, k: int) -> np.ndarray:
+    """Q8_0 matrix times fp32 activation rows -> float64 [M, N]."""
+    return gemv(dequant_q8_0(raw, n_rows, k), np.asarray(x_f32, dtype=np.float32).astype(np.float64))
+
+
+def qmv_q4_k(raw, x_bf16_bits, n_rows: int, k: int) -> np.ndarray:
+    """Q4_K matrix times bf16 activation rows -> float64 [M, N]."""
+    return gemv(dequant_q4_k(raw, n_rows, k), bf16_bits_to_f64(x_bf16_bits))
+
+
+# ----------------------------------------------------------------------------
+# routed-expert MoE
+# ----------------------------------------------------------------------------
+
+
+def route_top_k(logits, top_k: int):
+    """Top-k expert selection with weights renormalised over the selected experts.
+
+    Selection is on the fp32 logits themselves, largest first, ties to the lower
+    expert id. The weights are the softmax restricted to the selected experts,
+    which equals a softmax over all experts followed by renormalisation over the
+    k selected. Returns (ids int32 [T, k], weights float64 [T, k]).
+    """
+    lg = np.atleast_2d(np.asarray(logits, dtype=np.float32)).astype(np.float64)
+    t_count, n_exp = lg.shape
+    if not 1 <= top_k <= n_exp:
+        raise ValueError("top_k out of range")
+    ids = np.empty((t_count, top_k), dtype=np.int32)
+    wts = np.empty((t_count, top_k), dtype=np.float64)
+    expert = np.arange(n_exp)
+    for t in range(t_count):
+        order = np.lexsort((expert, -lg[t]))   # primary: logit descending; secondary: id ascending
+        sel = order[:top_k]
+        e = np.exp(lg[t, sel] - lg[t, sel[0]])
+        ids[t] = sel
+        wts[t] = e / e.sum()
+    return ids, wts
+
+
+def gather_pairs(ids) -> np.ndarray:
+    """All (expert, token) pairs of a routing, sorted by expert then token: int32 [P, 2]."""
+    ids = np.atleast_2d(np.asarray(ids))
+    pairs = [(int(e), t) for t in range(ids.shape[0]) for e in ids[t]]
+    pairs.sort()
+    return np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+
+
+def silu(g):
+    """silu(g) = g / (1 + e^-g)."""
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def expert_matrix(bank_raw, expert: int, n_rows: int, k: int) -> np.ndarray:
+    """Bytes of one expert's matrix inside a bank (experts stored back to back)."""
+    b = _as_bytes(bank_raw)
+    size = n_rows * (k // Q4_K_BLOCK_WEIGHTS) * Q4_K_BLOCK_BYTES
+    return b[expert * size:(expert + 1) * size]
+
+
+def moe_q4_k(gate_raw, up_raw, down_raw, logits, x_bf16_bits, hidden: int, ffn: int,
+             n_experts: int, top_k: int):
+    """Routed-expert FFN for each token t.
+
+    y_t = sum_j r_j * W_down[e_j] @ (silu(W_gate[e_j] @ x_t) * (W_up[e_j] @ x_t)),
+    with (e_j, r_j) from route_top_k and the sum taken in rank order j.
+    Returns (y float64 [T, hidden], ids int32 [T, k], weights float64 [T, k]).
+    """
+    x = bf16_bits_to_f64(np.atleast_2d(x_bf16_bits))
+    t_count = x.shape[0]
+    ids, wts = route_top_k(logits, top_k)
+    if ids.shape[0] != t_count:
+        raise ValueError("logits and activations disagree on the token count")
+    y = np.zeros((t_count, hidden), dtype=np.float64)
+    cache = {}
+    for t in range(t_count):
+        for j in range(top_k):
+            e = int(ids[t, j])
+            if e not in cache:
+                cache[e] = (
+                    dequant_q4_k(expert_matrix(gate_raw, e, ffn, hidden), ffn, hidden),
+                    dequant_q4_k(expert_matrix(up_raw, e, ffn, hidden), ffn, hidden),
+                    dequant_q4_k(expert_matrix(down_raw, e, hidden, ffn), hidden, ffn),
+                )
+            wg, wu, wd = cache[e]
+            h = silu(wg @ x[t]) * (wu @ x[t])
+            y[t] += wts[t, j] * (wd @ h)
+    return y, ids, wts
+
+
+# ----------------------------------------------------------------------------
+# prefill-sized product
+# ----------------------------------------------------------------------------
+
+
+def prefill_q4_k(raw, x_bf16_bits, n_rows: int, k: int):
+    """Y = X @ W^T for many activation rows.
+
+    Returns (Y_exact, Y_bf16w), both float64 [M, N]: the first with the exact
+    weights, the second with the weights rounded to fp32 and then to bf16 (the
+    bf16 tile a prefill GEMM multiplies).
+    """
+    x = bf16_bits_to_f64(x_bf16_bits)
+    w = dequant_q4_k(raw, n_rows, k)
+    wb = bf16_bits_to_f64(round_f32_to_bf16_bits(round_to_f32(w)))
+    return x @ w.T, x @ wb.T
+
+
+# ----------------------------------------------------------------------------
+# comparison metrics used by the parity gates
+# ----------------------------------------------------------------------------
+
+
+def floored_rel_err(y, y_ref, floor_frac: float = 1e-3) -> float:
+    """max_i |y_i - yref_i| / max(|yref_i|, tau), tau = floor_frac * max_i |yref_i| per row.
+
+    Rows are the leading axis (one activation row each); a 1-D input is one row.
+    """
+    y = np.atleast_2d(np.asarray(y, dtype=np.float64))
+    r = np.atleast_2d(np.asarray(y_ref, dtype=np.float64))
+    tau = floor_frac * np.max(np.abs(r), axis=1, keepdims=True)
+    den = np.maximum(np.abs(r), tau)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.abs(y - r) / den)) if r.size else 0.0
+
+
+def frobenius_rel_err(y, y_ref) -> float:
+    """||y - yref||_F / ||yref||_F."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(y_ref, dtype=np.float64)
+    nr = np.linalg.norm(r)
+    return float(np.linalg.norm(y - r) / nr) if nr > 0 else float(np.linalg.norm(y - r))

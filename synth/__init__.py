@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for the block-quantized matrix-vector product.
+
+This module is shared by the tests, the benchmark and the smoke check, and is
+the only code that both the CPU oracle side and the HIP side consume. It holds
+distributions and byte assembly only: no dequantization, no dot product, no
+routing, no rounding that the method itself performs.
+
+Workload shapes follow the memra pages' decode workloads (memra README, speed
+table and model support table: dense Q4_K_M / Q8_0 models and a 128-expert
+top-8 MoE; memra-bench card, "Drafts": K=2..3 speculative verify). The value
+distributions are the synthetic recipe stated with each function.
+
+Why uniform bytes are the right Q4_K generator: the 12-byte scale area of a
+Q4_K super-block stores eight 6-bit scales and eight 6-bit mins in exactly 96
+bits, every bit used once, so the map between the 12 bytes and the 16 fields is
+a bijection. Uniform random bytes there are therefore exactly i.i.d. uniform
+sc, m in [0, 63], and uniform random quant bytes are i.i.d. uniform nibbles in
+[0, 15]. The generator needs no knowledge of the packing.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rng",
+    "q8_0_weights",
+    "q4_k_weights",
+    "bf16_normal",
+    "f32_normal",
+    "moe_bank",
+    "moe_logits",
+    "torch_q4_k_weights",
+]
+
+# Block geometry of the two GGUF formats (bytes per block, weights per block).
+_Q8_0_BYTES, _Q8_0_WEIGHTS = 34, 32
+_Q4_K_BYTES, _Q4_K_WEIGHTS = 144, 256
+
+
+def rng(seed: int, *stream: int) -> np.random.Generator:
+    """PCG64 generator for (seed, stream...) — one independent stream per tuple."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), *map(int, stream)])))
+
+
+def _fp16_abs_normal(g: np.random.Generator, n: int, scale: float) -> np.ndarray:
+    """|N(0,1)| * scale computed in float64, rounded once to IEEE fp16 (RNE)."""
+    v = np.abs(g.standard_normal(n)) * scale
+    return v.astype("<f2")
+
+
+def q8_0_weights(seed: int, n_rows: int, k: int, *, stream: int = 0) -> np.ndarray:
+    """Row-major Q8_0 matrix bytes: d = fp16(|N(0,1)|*0.01), q ~ U[-127, 127] int8.
+
+    Returns a flat uint8 array of n_rows * (k/32) * 34 bytes.
+    """
+    if k % _Q8_0_WEIGHTS:
+        raise ValueError("k must be a multiple of 32")
+    nb = n_rows * (k // _Q8_0_WEIGHTS)
+    g = rng(seed, 8, stream)
+    d = _fp16_abs_normal(g, nb, 0.01)
+    q = g.integers(-127, 128, size=(nb, _Q8_0_WEIGHTS), dtype=np.int8)
+    blocks = np.empty((nb, _Q8_0_BYTES), dtype=np.uint8)
+    blocks[:, 0:2] = d.view(np.uint8).reshape(nb, 2)
+    blocks[:, 2:] = q.view(np.uint8)
+    return blocks.reshape(-1)
+
+
+def q4_k_weights(seed: int, n_rows: int, k: int, *, stream: int = 0,
+                 d_scale: float = 0.002, dmin_scale: float = 0.002) -> np.ndarray:
+    """Row-major Q4_K matrix bytes.
+
+    Per 144-byte super-block: fp16 d = |N(0,1)|*0.002, fp16 dmin = |N(0,1)|*0.002,
+    then 140 uniform random bytes (12 scale/min bytes + 128 quant bytes), which
+    makes sc, m ~ U[0,63] and q ~ U[0,15] i.i.d. (see the module docstring).
+    Returns a flat uint8 array of n_rows * (k/256) * 144 bytes.
+    """
+    if k % _Q4_K_WEIGHTS:
+        raise ValueError("k must be a multiple of 256")
+    nb = n_rows * (k // _Q4_K_WEIGHTS)
+    g = rng(seed, 4, stream)
+    d = _fp16_abs_normal(g, nb, d_scale)
+    dmin = _fp16_abs_normal(g, nb, dmin_scale)
+    blocks = np.empty((nb, _Q4_K_BYTES), dtype=np.uint8)
+    blocks[:, 0:2] = d.view(np.uint8).reshape(nb, 2)
+    blocks[:, 2:4] = dmin.view(np.uint8).reshape(nb, 2)
+    blocks[:, 4:] = g.integers(0, 256, size=(nb, _Q4_K_BYTES - 4), dtype=np.uint8)
+    return blocks.reshape(-1)
+
+
+def bf16_normal(seed: int, shape, *, stream: int = 0) -> np.ndarray:
+    """bf16 bit patterns of fp32 N(0,1) samples rounded to nearest-even bf16.
+
+    These bf16 values are the exact activations given to both sides.
+    """
+    g = rng(seed, 16, stream)
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def f32_normal(seed: int, shape, *, stream: int = 0) -> np.ndarray:
+    """fp32 N(0,1) samples (the Q8_0 activation recipe)."""
+    g = rng(seed, 32, stream)
+    return g.standard_normal(size=shape, dtype=np.float32)
+
+
+def moe_bank(seed: int, n_experts: int, hidden: int, ffn: int, *, stream: int = 0):
+    """One layer's routed-expert bank, every matrix Q4_K with the dense recipe.
+
+    Returns (gate, up, down) flat uint8 arrays: gate/up hold n_experts matrices of
+    ffn x hidden, down holds n_experts matrices of hidden x ffn, each expert's
+    matrix contiguous and in expert order.
+    """
+    gate = q4_k_weights(seed, n_experts * ffn, hidden, stream=3 * stream + 0)
+    up = q4_k_weights(seed, n_experts * ffn, hidden, stream=3 * stream + 1)
+    down = q4_k_weights(seed, n_experts * hidden, ffn, stream=3 * stream + 2)
+    return gate, up, down
+
+
+def moe_logits(seed: int, n_tokens: int, n_experts: int, *, stream: int = 0) -> np.ndarray:
+    """Router logits ~ N(0,1) fp32, shape [n_tokens, n_experts]."""
+    return f32_normal(seed, (n_tokens, n_experts), stream=1000 + stream)
+
+
+def torch_q4_k_weights(seed: int, n_rows: int, k: int, device, *, stream: int = 0):
+    """Device-side Q4_K matrix bytes with the same recipe as q4_k_weights.
+
+    For the large weight pools: generated directly in device memory with torch's
+    device generator, so a multi-GB pool needs no host pass. d and dmin are
+    |N(0,1)|*0.002 rounded from fp32 to fp16 (the host recipe rounds from fp64;
+    the distributions are the same). Returns a flat uint8 device tensor.
+    """
+    import torch
+
+    if k % _Q4_K_WEIGHTS:
+        raise ValueError("k must be a multiple of 256")
+    nb = n_rows * (k // _Q4_K_WEIGHTS)
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1_000_003 + int(stream) * 7919 + 4) & 0x7FFF_FFFF_FFFF_FFFF)
+    blocks = torch.randint(0, 256, (nb, _Q4_K_BYTES), dtype=torch.uint8, device=device, generator=g)
+    scales = torch.randn((nb, 2), dtype=torch.float32, device=device, generator=g).abs_().mul_(0.002)
+    blocks[:, 0:4] = scales.to(torch.float16).view(torch.uint8).view(nb, 4)
+    return blocks.view(-1)

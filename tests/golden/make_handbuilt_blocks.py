@@ -1,0 +1,156 @@
+"""Writes tests/golden/{q8_0,q4_k}_handbuilt.json: hand-built blocks with known values.
+
+Run from the repository root:  python tests/golden/make_handbuilt_blocks.py
+
+Each block is stated by its fields (fp16 scale bit patterns, 6-bit scales and
+mins, quants). Its bytes are assembled from those fields by this script's own
+bit-level encoder of the public GGUF layouts (Q8_0: fp16 d then 32 int8;
+Q4_K: fp16 d, fp16 dmin, 12 packed scale/min bytes, 128 nibble bytes). For the
+Q4_K blocks the 12 scale bytes were also derived by hand and are written below
+as literals; the script stops if its encoder disagrees with them.
+
+The expected weights are computed here from the stated fields with exact
+rational arithmetic (w = d*q for Q8_0, w = d*sc_j*q - dmin*m_j for Q4_K); they
+are closed forms by construction and do not come from the oracle or the GPU.
+The memra pages name these formats (memra README, model support table: Q8_0
+and Q4_K_M GGUF models) but print no block bytes, so no value here is theirs.
+"""
+
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def fp16_value(bits: int) -> Fraction:
+    """Exact value of an IEEE binary16 bit pattern (finite only)."""
+    sign = -1 if bits & 0x8000 else 1
+    exp = (bits >> 10) & 0x1F
+    man = bits & 0x3FF
+    if exp == 0x1F:
+        raise ValueError("non-finite fp16 in a golden block")
+    if exp == 0:
+        return sign * Fraction(man, 1 << 24)
+    return sign * Fraction(1024 + man, 1 << 10) * (Fraction(2) ** (exp - 15))
+
+
+def frac_to_hex(v: Fraction) -> str:
+    f = float(v)
+    assert Fraction(f) == v, "golden value not exact in binary64"
+    return f.hex()
+
+
+# ---------------------------------------------------------------- Q8_0
+
+def q8_0_block(d_bits: int, q: list[int]) -> bytes:
+    assert len(q) == 32 and all(-128 <= v <= 127 for v in q)
+    return bytes([d_bits & 0xFF, d_bits >> 8]) + bytes([v & 0xFF for v in q])
+
+
+Q8_0_BLOCKS = [
+    ("unit_scale_ramp", 0x3C00, [j - 16 for j in range(32)]),
+    ("subnormal_scale", 0x0001, [127, -127, 1, -1] + [0] * 27 + [5]),
+    ("negative_scale", 0xC000, [(-1) ** j * j for j in range(32)]),
+    ("max_finite_scale", 0x7BFF, [127] + [3] * 30 + [-127]),
+    ("zero_scale", 0x0000, [(7 * j) % 255 - 127 for j in range(32)]),
+]
+
+
+# ---------------------------------------------------------------- Q4_K
+
+def pack_scales_mins(sc: list[int], m: list[int]) -> bytes:
+    """Bit-level encoder of the 12 scale/min bytes (this script's own statement).
+
+    j < 4 : sc_j -> bits 0..5 of S[j],   m_j -> bits 0..5 of S[j+4]
+    j >= 4: sc_j bits 0..3 -> bits 0..3 of S[j+4], bits 4..5 -> bits 6..7 of S[j-4]
+            m_j  bits 0..3 -> bits 4..7 of S[j+4], bits 4..5 -> bits 6..7 of S[j]
+    """
+    S = [0] * 12
+    for j in range(8):
+        assert 0 <= sc[j] < 64 and 0 <= m[j] < 64
+    for j in range(4):
+        S[j] |= sc[j]
+        S[j + 4] |= m[j]
+    for j in range(4, 8):
+        S[j + 4] |= (sc[j] & 0xF) | ((m[j] & 0xF) << 4)
+        S[j - 4] |= (sc[j] >> 4) << 6
+        S[j] |= (m[j] >> 4) << 6
+    return bytes(S)
+
+
+def pack_nibbles(q: list[int]) -> bytes:
+    """Quant bytes: Q[32c + l] = q[64c + l] | q[64c + 32 + l] << 4."""
+    assert len(q) == 256 and all(0 <= v < 16 for v in q)
+    out = bytearray(128)
+    for c in range(4):
+        for l in range(32):
+            out[32 * c + l] = q[64 * c + l] | (q[64 * c + 32 + l] << 4)
+    return bytes(out)
+
+
+# (name, d_bits, dmin_bits, sc[8], m[8], q[256], hand-derived scale bytes as hex)
+Q4_K_BLOCKS = [
+    ("distinct_scales", 0x3C00, 0x0000, [1, 2, 3, 4, 5, 6, 7, 8], [0] * 8,
+     [i % 16 for i in range(256)], "010203040000000005060708"),
+    ("distinct_mins", 0x3C00, 0x3C00, [1] * 8, [1, 2, 3, 4, 5, 6, 7, 8],
+     [(i >> 4) & 15 for i in range(256)], "010101010102030451617181"),
+    ("top_bit_carries", 0x3800, 0x3400, [63, 62, 61, 60, 48, 33, 18, 47], [0, 7, 63, 32, 63, 17, 50, 5],
+     [1] * 256, "ffbe7dbcc047ff20f011225f"),
+    ("subnormal_scales", 0x0001, 0x0003, [63] * 8, [63] * 8,
+     [15] * 256, "ffffffffffffffffffffffff"),
+    ("zero_d", 0x0000, 0x3C00, [63, 62, 61, 60, 48, 33, 18, 47], [0, 7, 63, 32, 63, 17, 50, 5],
+     [(5 * i + 3) % 16 for i in range(256)], "ffbe7dbcc047ff20f011225f"),
+    ("position_code", 0x3C00, 0x0000, [1] * 8, [0] * 8,
+     [(i * 7 + (i >> 5)) % 16 for i in range(256)], "010101010000000001010101"),
+]
+
+
+def main() -> None:
+    q8 = []
+    for name, d_bits, q in Q8_0_BLOCKS:
+        raw = q8_0_block(d_bits, q)
+        d = fp16_value(d_bits)
+        q8.append({
+            "name": name,
+            "d_bits": d_bits,
+            "q": q,
+            "hex": raw.hex(),
+            "expect": [frac_to_hex(d * v) for v in q],
+        })
+
+    q4 = []
+    for name, d_bits, dmin_bits, sc, m, q, s_hex in Q4_K_BLOCKS:
+        s_bytes = pack_scales_mins(sc, m)
+        if s_bytes.hex() != s_hex:
+            raise SystemExit(f"{name}: encoder gives {s_bytes.hex()}, hand derivation says {s_hex}")
+        raw = bytes([d_bits & 0xFF, d_bits >> 8, dmin_bits & 0xFF, dmin_bits >> 8]) + s_bytes + pack_nibbles(q)
+        assert len(raw) == 144
+        d, dmin = fp16_value(d_bits), fp16_value(dmin_bits)
+        expect = [d * sc[i // 32] * q[i] - dmin * m[i // 32] for i in range(256)]
+        q4.append({
+            "name": name,
+            "d_bits": d_bits,
+            "dmin_bits": dmin_bits,
+            "sc": sc,
+            "m": m,
+            "q": q,
+            "hex": raw.hex(),
+            "expect": [frac_to_hex(v) for v in expect],
+        })
+
+    note = ("Hand-built blocks with known values (closed forms by construction). "
+            "Formats named on the memra README model support table (Q8_0, Q4_K_M GGUF); "
+            "layouts are the public GGUF ones. Written by tests/golden/make_handbuilt_blocks.py.")
+    with open(os.path.join(HERE, "q8_0_handbuilt.json"), "w") as f:
+        json.dump({"citation": note, "blocks": q8}, f, indent=1)
+        f.write("\n")
+    with open(os.path.join(HERE, "q4_k_handbuilt.json"), "w") as f:
+        json.dump({"citation": note, "blocks": q4}, f, indent=1)
+        f.write("\n")
+
+
+if __name__ == "__main__":
+    main()

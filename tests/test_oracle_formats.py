@@ -1,0 +1,264 @@
+"""Pins for the oracle's block decoding (Q8_0, Q4_K) and scalar formats.
+
+Everything here runs on the CPU. Each check ties the oracle to something other
+than itself: hand-built blocks whose values are known by construction
+(tests/golden), locality invariants of the byte layout, the pack/unpack
+bijection, requantisation round trips and closed-form special values.
+"""
+
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+sys.path.insert(0, os.path.join(os.path.dirname(__file__), "golden"))
+from make_handbuilt_blocks import pack_nibbles, pack_scales_mins  # noqa: E402
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)["blocks"]
+
+
+# ---------------------------------------------------------------- scalars
+
+@pytest.mark.parametrize("bits,value", [
+    (0x3C00, 1.0), (0xC000, -2.0), (0x7BFF, 65504.0), (0x0001, 2.0 ** -24),
+    (0x03FF, 1023 * 2.0 ** -24), (0x0400, 2.0 ** -14), (0x3555, (1 + 0x155 / 1024) * 2.0 ** -2),
+    (0x0000, 0.0),
+])
+def test_fp16_decode_closed_forms(bits, value):
+    assert oracle.fp16_bits_to_f64(np.array([bits]))[0] == value
+
+
+def test_fp16_negative_zero_keeps_sign():
+    v = oracle.fp16_bits_to_f64(np.array([0x8000]))[0]
+    assert v == 0.0 and np.signbit(v)
+
+
+@pytest.mark.parametrize("bits,value", [
+    (0x3F80, 1.0), (0xC000, -2.0), (0x4300, 128.0), (0x0001, 2.0 ** -133), (0x7F7F, (2 - 2 ** -7) * 2.0 ** 127),
+])
+def test_bf16_decode_closed_forms(bits, value):
+    assert oracle.bf16_bits_to_f64(np.array([bits]))[0] == value
+
+
+def test_bf16_round_nearest_even():
+    # ties: 1 + 2^-8 sits halfway between 1 and 1 + 2^-7 -> even (1.0);
+    #       1 + 3*2^-8 sits halfway between 1 + 2^-7 and 1 + 2^-6 -> even (1 + 2^-6)
+    vals = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, -(1 + 2.0 ** -8)], dtype=np.float32)
+    got = oracle.bf16_bits_to_f64(oracle.round_f32_to_bf16_bits(vals))
+    assert list(got) == [1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -1.0]
+
+
+def test_synth_bf16_generator_rounds_like_the_library():
+    bits = synth.bf16_normal(5, (4096,))
+    g = synth.rng(5, 16, 0)
+    x = g.standard_normal(size=(4096,), dtype=np.float32)
+    assert np.array_equal(bits, oracle.round_f32_to_bf16_bits(x))
+
+
+# ---------------------------------------------------------------- Q8_0
+
+def test_q8_0_handbuilt_blocks(golden_dir):
+    for blk in _load(golden_dir, "q8_0_handbuilt.json"):
+        raw = bytes.fromhex(blk["hex"])
+        d, q = oracle.q8_0_fields(raw, 1, 32)
+        assert list(q[0, 0]) == blk["q"], blk["name"]
+        w = oracle.dequant_q8_0(raw, 1, 32)[0]
+        expect = np.array([float.fromhex(v) for v in blk["expect"]])
+        assert np.array_equal(w, expect), blk["name"]
+
+
+def test_q8_0_multi_block_row_major():
+    # Row n, block t must come from bytes (n*K/32 + t)*34: build 3 rows x 2 blocks
+    # whose scale encodes (n, t) and whose quants encode the in-block index.
+    n_rows, k = 3, 64
+    raw = bytearray()
+    for n in range(n_rows):
+        for t in range(2):
+            d_bits = 0x3C00 + (n * 2 + t) * 0x400          # 1, 2, 4, 8, 16, 32
+            raw += bytes([d_bits & 0xFF, d_bits >> 8]) + bytes(range(32))
+    w = oracle.dequant_q8_0(bytes(raw), n_rows, k)
+    for n in range(n_rows):
+        for t in range(2):
+            assert np.array_equal(w[n, 32 * t:32 * t + 32], (2.0 ** (n * 2 + t)) * np.arange(32))
+
+
+def test_q8_0_requant_round_trip():
+    raw = synth.q8_0_weights(11, 64, 256)
+    d, q = oracle.q8_0_fields(raw, 64, 256)
+    w = oracle.dequant_q8_0(raw, 64, 256).reshape(64, 8, 32)
+    nz = d != 0
+    q_back = np.rint(w / np.where(nz, d, 1.0)[:, :, None])
+    assert np.array_equal(q_back[nz], q[nz])
+
+
+def test_q8_0_full_quantiser_round_trip_on_blocks_with_extreme_quant():
+    # A full quantiser d' = RN_fp16(max|w| / 127), q' = round(w / d') reproduces the
+    # block exactly when the block contains +-127 (then max|w| = 127 d).
+    raw = bytearray(synth.q8_0_weights(12, 16, 128))
+    blocks = np.frombuffer(raw, dtype=np.uint8).reshape(-1, 34).copy()
+    blocks[:, 2 + 7] = np.uint8(127)
+    blocks[::2, 2 + 19] = np.uint8(0x81)  # -127
+    raw = blocks.reshape(-1)
+    d, q = oracle.q8_0_fields(raw, 16, 128)
+    w = oracle.dequant_q8_0(raw, 16, 128).reshape(16, 4, 32)
+    d_new = (np.abs(w).max(axis=2) / 127.0).astype(np.float16).astype(np.float64)
+    assert np.array_equal(d_new, d)
+    ok = d_new != 0
+    q_new = np.rint(w / np.where(ok, d_new, 1.0)[:, :, None])
+    assert np.array_equal(q_new[ok], q[ok])
+
+
+def test_q8_0_rejects_wrong_sizes():
+    with pytest.raises(ValueError):
+        oracle.dequant_q8_0(bytes(33), 1, 32)
+    with pytest.raises(ValueError):
+        oracle.dequant_q8_0(bytes(34), 1, 31)
+
+
+# ---------------------------------------------------------------- Q4_K
+
+def test_q4_k_handbuilt_blocks(golden_dir):
+    for blk in _load(golden_dir, "q4_k_handbuilt.json"):
+        raw = bytes.fromhex(blk["hex"])
+        d, dmin, sc, m, q = oracle.q4_k_fields(raw, 1, 256)
+        assert list(sc[0, 0]) == blk["sc"], blk["name"]
+        assert list(m[0, 0]) == blk["m"], blk["name"]
+        assert list(q[0, 0]) == blk["q"], blk["name"]
+        assert d[0, 0] == oracle.fp16_bits_to_f64(np.array([blk["d_bits"]]))[0]
+        assert dmin[0, 0] == oracle.fp16_bits_to_f64(np.array([blk["dmin_bits"]]))[0]
+        w = oracle.dequant_q4_k(raw, 1, 256)[0]
+        expect = np.array([float.fromhex(v) for v in blk["expect"]])
+        assert np.array_equal(w, expect), blk["name"]
+
+
+def test_q4_k_handbuilt_top_bits_by_value(golden_dir):
+    # Values read straight off the hand derivation: d=0.5, dmin=0.25, all q=1.
+    blk = {b["name"]: b for b in _load(golden_dir, "q4_k_handbuilt.json")}["top_bit_carries"]
+    w = oracle.dequant_q4_k(bytes.fromhex(blk["hex"]), 1, 256)[0]
+    assert list(w[::32]) == [31.5, 29.25, 14.75, 22.0, 8.25, 12.25, -3.5, 22.25]
+
+
+def test_q4_k_quant_byte_locality():
+    raw = bytearray(synth.q4_k_weights(21, 1, 256))
+    base = oracle.dequant_q4_k(bytes(raw), 1, 256)[0]
+    _, _, sc, _, _ = oracle.q4_k_fields(bytes(raw), 1, 256)
+    for p in range(128):
+        c, l = divmod(p, 32)
+        for mask, weight in ((0x0F, 64 * c + l), (0xF0, 64 * c + 32 + l)):
+            mod = bytearray(raw)
+            mod[16 + p] ^= mask
+            w = oracle.dequant_q4_k(bytes(mod), 1, 256)[0]
+            changed = np.nonzero(w != base)[0]
+            if sc[0, 0, weight // 32] != 0:
+                assert list(changed) == [weight], (p, mask)
+            else:
+                assert changed.size == 0
+
+
+# (byte index in S, bit) -> (field, sub-block, value of that bit in the field)
+def _scale_bit_owner(i, bit):
+    if i < 4:
+        return ("sc", i, 1 << bit) if bit < 6 else ("sc", i + 4, 1 << (bit - 2))
+    if i < 8:
+        return ("m", i - 4, 1 << bit) if bit < 6 else ("m", i, 1 << (bit - 2))
+    return ("sc", i - 4, 1 << bit) if bit < 4 else ("m", i - 4, 1 << (bit - 4))
+
+
+def test_q4_k_scale_byte_locality():
+    raw = bytearray(synth.q4_k_weights(22, 1, 256))
+    _, _, sc0, m0, _ = oracle.q4_k_fields(bytes(raw), 1, 256)
+    for i in range(12):
+        for bit in range(8):
+            mod = bytearray(raw)
+            mod[4 + i] ^= 1 << bit
+            _, _, sc1, m1, _ = oracle.q4_k_fields(bytes(mod), 1, 256)
+            field, j, val = _scale_bit_owner(i, bit)
+            dsc = (sc1 - sc0)[0, 0]
+            dm = (m1 - m0)[0, 0]
+            hit, other = (dsc, dm) if field == "sc" else (dm, dsc)
+            assert np.count_nonzero(other) == 0, (i, bit)
+            assert list(np.nonzero(hit)[0]) == [j], (i, bit)
+            assert abs(hit[j]) == val, (i, bit)
+
+
+def test_q4_k_pack_unpack_bijection():
+    # every value of every 6-bit field, in every position, survives pack -> decode
+    rng = np.random.default_rng(3)
+    for j in range(8):
+        for v in range(64):
+            for field in ("sc", "m"):
+                sc = list(rng.integers(0, 64, 8))
+                m = list(rng.integers(0, 64, 8))
+                (sc if field == "sc" else m)[j] = v
+                q = list(rng.integers(0, 16, 256))
+                raw = bytes([0, 0x3C, 0, 0x3C]) + pack_scales_mins(sc, m) + pack_nibbles(q)
+                _, _, dsc, dm, dq = oracle.q4_k_fields(raw, 1, 256)
+                assert list(dsc[0, 0]) == sc and list(dm[0, 0]) == m and list(dq[0, 0]) == q
+    # and random bytes survive decode -> pack
+    raw = synth.q4_k_weights(23, 8, 512)
+    _, _, sc, m, q = oracle.q4_k_fields(raw, 8, 512)
+    blocks = raw.reshape(-1, 144)
+    for b in range(blocks.shape[0]):
+        n, t = divmod(b, 2)
+        assert pack_scales_mins(list(sc[n, t]), list(m[n, t])) == bytes(blocks[b, 4:16])
+        assert pack_nibbles(list(q[n, t])) == bytes(blocks[b, 16:])
+
+
+def test_q4_k_requant_round_trip():
+    raw = synth.q4_k_weights(24, 32, 512)
+    d, dmin, sc, m, q = oracle.q4_k_fields(raw, 32, 512)
+    w = oracle.dequant_q4_k(raw, 32, 512).reshape(32, 2, 8, 32)
+    scale = d[:, :, None] * sc
+    off = dmin[:, :, None] * m
+    ok = scale != 0
+    q_back = np.rint((w + off[..., None]) / np.where(ok, scale, 1.0)[..., None])
+    q4 = q.reshape(32, 2, 8, 32)
+    assert np.array_equal(q_back[ok], q4[ok])
+
+
+def test_q4_k_weights_are_exact_dyadics():
+    # every weight is an integer multiple of 2^-24 below 2^50: fp64 holds it exactly
+    raw = synth.q4_k_weights(25, 16, 1024)
+    w = oracle.dequant_q4_k(raw, 16, 1024)
+    scaled = w * 2.0 ** 24
+    assert np.array_equal(scaled, np.rint(scaled))
+    assert np.max(np.abs(scaled)) < 2.0 ** 50
+
+
+def test_q4_k_generator_distributions():
+    raw = synth.q4_k_weights(26, 256, 2048)
+    d, dmin, sc, m, q = oracle.q4_k_fields(raw, 256, 2048)
+    assert sc.min() == 0 and sc.max() == 63 and m.min() == 0 and m.max() == 63
+    assert q.min() == 0 and q.max() == 15
+    assert abs(sc.mean() - 31.5) < 0.5 and abs(m.mean() - 31.5) < 0.5 and abs(q.mean() - 7.5) < 0.05
+    # d ~ |N(0,1)| * 0.002: mean 0.002*sqrt(2/pi)
+    assert abs(d.mean() / (0.002 * np.sqrt(2 / np.pi)) - 1) < 0.02
+    assert abs(dmin.mean() / (0.002 * np.sqrt(2 / np.pi)) - 1) < 0.02
+
+
+def test_q4_k_rejects_wrong_sizes():
+    with pytest.raises(ValueError):
+        oracle.dequant_q4_k(bytes(143), 1, 256)
+    with pytest.raises(ValueError):
+        oracle.dequant_q4_k(bytes(144), 1, 128)
+
+
+def test_fp32_target_rounds_once():
+    # weights that fp32 cannot hold are rounded to nearest: d*sc*q has <= 21 bits,
+    # dmin*m <= 17, their difference can need more than 24 bits.
+    raw = synth.q4_k_weights(27, 64, 1024)
+    w = oracle.dequant_q4_k(raw, 64, 1024)
+    w32 = oracle.dequant_q4_k_f32(raw, 64, 1024)
+    assert w32.dtype == np.float32
+    err = np.abs(w32.astype(np.float64) - w)
+    ulp = np.spacing(np.abs(w32)).astype(np.float64)
+    assert np.all(err <= 0.5 * ulp)
+    assert np.count_nonzero(err) > 0        # some weights really need the rounding
