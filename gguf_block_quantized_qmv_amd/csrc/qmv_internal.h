@@ -1,0 +1,24 @@
+// Internal launch interface between the C-ABI layer (qmv_api.cpp, pure host
+// code) and the HIP kernel files. Arguments are already validated when these
+// are called; each returns QMV_OK or QMV_ERR_HIP.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmv {
+
+void set_error_detail(const char *what, int hip_code, const char *hip_text);
+
+int launch_q8_0_gemv(const void *w, const float *x, float *y, int m, int n, int k, void *stream);
+int launch_q4_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
+int launch_dequant_q4_k(const void *w, void *out, bool bf16, int n, int k, void *stream);
+int launch_dequant_q8_0(const void *w, float *out, int n, int k, void *stream);
+int launch_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
+                    const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs,
+                    void *ws, int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
+size_t moe_workspace_bytes(int t, int hidden, int ffn, int n_experts, int top_k);
+bool moe_fits_lds(int t, int hidden, int ffn, int top_k);
+int launch_q4_k_prefill(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
+
+}  // namespace qmv

@@ -1,0 +1,181 @@
+/*
+ * qmv.h -- C ABI of the MI355X (gfx950) block-quantized matrix-vector library.
+ *
+ * The library computes products of GGUF block-quantized weight matrices with a
+ * few activation rows: the weight stream of plain decode and of speculative
+ * verify, its routed-expert MoE form, and a prefill-sized GEMM form. The memra
+ * pages this follows name the workload -- GGUF Q4_K_M and Q8_0 models decoded
+ * on one GPU, dense and MoE (memra README: model support table, speed table),
+ * speculative decode with K=2..3 drafts that must be byte-identical to plain
+ * decode (memra-bench card, "Drafts"; memra summary page, tagline), and the
+ * rule that one request is never served under two numerical programs (memra
+ * README, recent-fixes list) -- but print no kernel interface, so this ABI is
+ * this library's own.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named w*, x*, y*, out*, logits, topk_*, pairs, ws are DEVICE
+ *    pointers (HIP device memory of the current device). The caller owns every
+ *    buffer; the library never allocates, frees or synchronises, and keeps no
+ *    mutable global state, so calls from several host threads are safe.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    work is enqueued on it asynchronously; a return of QMV_OK means the work
+ *    was enqueued, not that it finished.
+ *  - Every argument is validated on the host before any HIP call is made.
+ *    Invalid arguments return a negative QMV_ERR_* code and touch no memory.
+ *    A failed launch returns QMV_ERR_HIP. Faults during execution surface as
+ *    HIP errors on the caller's next synchronisation.
+ *  - Quantized matrices are row-major: row n (one output feature) is the
+ *    contiguous run of its K/QK blocks along the input dimension K, rows follow
+ *    each other with no padding. `w_bytes` must equal the exact byte size of
+ *    that layout; any other value (a truncated or oversized buffer) is
+ *    QMV_ERR_SIZE.
+ *  - bf16 values travel as uint16_t bit patterns. Outputs are fp32.
+ *  - Outputs must not overlap any input (QMV_ERR_ALIAS).
+ *  - Results are bitwise deterministic from run to run. For the GEMV entry
+ *    points, row r of the output depends only on activation row r: the same
+ *    row gives bit-identical results for every row count 1..4.
+ *
+ * Block formats (the public GGUF layouts; the pages name them, they do not print them)
+ * -------------
+ *  Q8_0 : 34 bytes per 32 weights: fp16 d (little-endian), then int8 q[32];
+ *         w = d * q.
+ *  Q4_K : 144 bytes per 256 weights: fp16 d, fp16 dmin, 12 bytes holding eight
+ *         6-bit scales sc_j and eight 6-bit mins m_j of the 32-weight
+ *         sub-blocks j = 0..7, then 128 bytes of 4-bit quants q (byte 32c + l
+ *         holds weight 64c + l in its low nibble and 64c + 32 + l in its high
+ *         nibble); w = d * sc_j * q - dmin * m_j.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define QMV_OK             0
+#define QMV_ERR_NULL      -1  /* a required pointer is NULL                          */
+#define QMV_ERR_SHAPE     -2  /* N, K, H or F not positive / not a block multiple    */
+#define QMV_ERR_SIZE      -3  /* a byte count does not match the stated shape         */
+#define QMV_ERR_ALIGN     -4  /* a pointer lacks the alignment stated for it          */
+#define QMV_ERR_RANGE     -5  /* a count (M, T, E, top_k) or a size limit is exceeded */
+#define QMV_ERR_WORKSPACE -6  /* workspace NULL or smaller than the required size     */
+#define QMV_ERR_ALIAS     -7  /* an output overlaps an input or another output        */
+#define QMV_ERR_HIP       -8  /* the HIP runtime refused a launch                     */
+
+/* ---- limits ------------------------------------------------------------ */
+#define QMV_MAX_ROWS        4      /* activation rows per GEMV call (verify: K<=3 drafts + 1) */
+#define QMV_LDS_X_BYTES     163840 /* LDS budget for staged activations per workgroup (160 KiB) */
+#define QMV_MOE_MAX_TOKENS  4
+#define QMV_MOE_MAX_EXPERTS 256
+#define QMV_MOE_MAX_TOP_K   8
+
+/* Library version as 10000*major + 100*minor + patch. */
+int qmv_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *qmv_strerror(int code);
+
+/* Detail of the last QMV_ERR_HIP returned to the calling thread: which launch
+ * or attribute call failed and the HIP error code and text ("" if none yet).
+ * The text is thread-local and valid until that thread's next failing call. */
+const char *qmv_last_error(void);
+
+/*
+ * Q8_0 matrix times fp32 activation rows (decode / verify).
+ *   w       [n rows][k/32 blocks] Q8_0, 4-byte aligned; w_bytes == n*(k/32)*34
+ *   x       fp32 [m][k] row-major, 16-byte aligned
+ *   y       fp32 [m][n] row-major, 4-byte aligned
+ *   1 <= m <= QMV_MAX_ROWS, n >= 1, k >= 32 and k % 32 == 0,
+ *   m*k*4 <= QMV_LDS_X_BYTES (m=4 allows k up to 10240).
+ * y[r][i] = sum_k dequant(w)[i][k] * x[r][k], accumulated in fp32.
+ * Workload: the Q8_0 GEMV of the memra README's support table (Q8_0 models and
+ * MTP heads) and the memra-bench card's Q8_0 drafts.
+ */
+int qmv_q8_0(const void *w, size_t w_bytes, const float *x, float *y,
+             int m, int n, int k, void *stream);
+
+/*
+ * Q4_K matrix times bf16 activation rows (decode m=1, speculative verify m=2..4).
+ *   w       [n rows][k/256 blocks] Q4_K, 16-byte aligned; w_bytes == n*(k/256)*144
+ *   x_bf16  bf16 bits [m][k] row-major, 16-byte aligned
+ *   y       fp32 [m][n] row-major, 4-byte aligned
+ *   1 <= m <= QMV_MAX_ROWS, n >= 1, k >= 256 and k % 256 == 0,
+ *   m*k*2 + m*(k/32)*4 <= QMV_LDS_X_BYTES (m=4 allows k up to 19200).
+ * y[r][i] = sum_k dequant(w)[i][k] * x[r][k] with the quants and bf16 inputs
+ * exact and fp32 accumulation. Row r of y is bit-identical for every m.
+ * Workload: the per-token weight stream of the memra README's dense Q4_K_M
+ * models (plain decode) and of the memra-bench card's K-draft verify.
+ */
+int qmv_q4_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
+             int m, int n, int k, void *stream);
+
+/*
+ * Workspace bytes qmv_q4_k_moe needs for t tokens (0 if an argument is out of
+ * range). The caller allocates it in device memory, 256-byte aligned.
+ */
+size_t qmv_q4_k_moe_workspace(int t, int hidden, int ffn, int n_experts, int top_k);
+
+/*
+ * Routed-expert MoE feed-forward on Q4_K experts, for t tokens at once.
+ *   w_gate, w_up  n_experts matrices of [ffn rows][hidden/256 blocks], expert-major
+ *   w_down        n_experts matrices of [hidden rows][ffn/256 blocks], expert-major
+ *   bank_bytes    byte size of EACH of the three arrays; must equal
+ *                 n_experts*ffn*(hidden/256)*144 (== n_experts*hidden*(ffn/256)*144)
+ *   logits        fp32 [t][n_experts] router logits (finite values)
+ *   x_bf16        bf16 bits [t][hidden], 16-byte aligned
+ *   y             fp32 [t][hidden]
+ *   topk_ids      int32 [t][top_k] out, may be NULL: selected experts, rank order
+ *   topk_w        fp32  [t][top_k] out, may be NULL: their renormalised weights
+ *   pairs         int32 [t*top_k][2] out, may be NULL: every (expert, token) pair,
+ *                 sorted by expert then token (the gather list)
+ *   ws, ws_bytes  workspace of at least qmv_q4_k_moe_workspace(...) bytes, 256-B aligned
+ *   1 <= t <= QMV_MOE_MAX_TOKENS, 1 <= top_k <= min(QMV_MOE_MAX_TOP_K, n_experts),
+ *   1 <= n_experts <= QMV_MOE_MAX_EXPERTS, hidden and ffn multiples of 256.
+ * Per token: the top_k largest logits (ties -> lower expert id) select experts
+ * e_j; r_j = softmax over the selected logits; h = silu(W_gate x) * (W_up x) in
+ * fp32; y = sum_j r_j * W_down[e_j] h, summed in rank order j. Each selected
+ * expert's weights are read once per call however many tokens chose it, and a
+ * token's result does not depend on the other tokens in the call.
+ * Workload: the memra README speed table's 35B-A3B MoE decode (128 experts,
+ * top-8) and the memra-bench card's K=2 drafts on it.
+ */
+int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes,
+                 const float *logits, const uint16_t *x_bf16, float *y,
+                 int32_t *topk_ids, float *topk_w, int32_t *pairs,
+                 void *ws, size_t ws_bytes,
+                 int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
+
+/*
+ * Prefill-sized product Y = X W^T on bf16 matrix cores.
+ *   w       [n rows][k/256 blocks] Q4_K, 16-byte aligned; w_bytes == n*(k/256)*144
+ *   x_bf16  bf16 bits [m][k] row-major, 16-byte aligned
+ *   y       fp32 [m][n] row-major, 16-byte aligned
+ *   m >= 1, n >= 1, k % 256 == 0.
+ * Weights are dequantized to fp32, rounded once to bf16 (round to nearest
+ * even) and multiplied with the bf16 activations, accumulating in fp32.
+ * Workload: prompt processing ahead of decode (the time-to-first-token figures
+ * of the memra summary page's performance table).
+ */
+int qmm_q4_k_prefill(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
+                     int m, int n, int k, void *stream);
+
+/*
+ * Dequantization to dense matrices (the bit-exact gate of the decode kernels).
+ *   out  fp32 [n][k] or bf16 bits [n][k], 16-byte aligned
+ * fp32: each weight is the exact block value rounded once to fp32 (nearest
+ * even). bf16: that fp32 value rounded to bf16 (nearest even).
+ */
+int qmv_dequant_q4_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
+int qmv_dequant_q4_k_bf16(const void *w, size_t w_bytes, uint16_t *out, int n, int k, void *stream);
+int qmv_dequant_q8_0_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

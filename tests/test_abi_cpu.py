@@ -1,0 +1,161 @@
+"""The C-ABI library loads, exports every declared symbol and validates arguments.
+
+CPU only: every call here fails host-side validation before any HIP call, so no
+device is needed and no kernel is launched. The memra README's recent-fixes list
+states the rule these tests follow: a truncated or malformed input yields a
+contextual error, never a crash, for every byte-prefix of a valid buffer.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gguf_block_quantized_qmv_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = q.lib
+
+OK, NULL, SHAPE, SIZE, ALIGN, RANGE, WORKSPACE, ALIAS, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+# Fake, never dereferenced device addresses (validation rejects every call below first).
+A = 0x7F0000000000
+W, X, Y, WS = A, A + (1 << 32), A + (2 << 32), A + (3 << 32)
+V = ctypes.c_void_p
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "qmv.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(qm[mv]_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_lists_the_expected_entry_points():
+    assert _header_functions() == sorted([
+        "qmv_version", "qmv_strerror", "qmv_last_error", "qmv_q8_0", "qmv_q4_k", "qmv_q4_k_moe_workspace", "qmv_q4_k_moe",
+        "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16", "qmv_dequant_q8_0_f32"])
+
+
+def test_library_exports_every_declared_symbol():
+    for name in _header_functions():
+        assert hasattr(L, name), name
+    assert set(_header_functions()) == set(q.EXPORTS)
+
+
+def test_version_and_strerror():
+    assert L.qmv_version() > 0
+    for code in (OK, NULL, SHAPE, SIZE, ALIGN, RANGE, WORKSPACE, ALIAS, HIP, -99, 7):
+        s = L.qmv_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 1
+
+
+def q4k(w=W, nbytes=None, x=X, y=Y, m=1, n=2, k=256):
+    nbytes = q.q4_k_bytes(n, k) if nbytes is None else nbytes
+    return L.qmv_q4_k(V(w), nbytes, V(x), V(y), m, n, k, None)
+
+
+def q80(w=W, nbytes=None, x=X, y=Y, m=1, n=2, k=64):
+    nbytes = q.q8_0_bytes(n, k) if nbytes is None else nbytes
+    return L.qmv_q8_0(V(w), nbytes, V(x), V(y), m, n, k, None)
+
+
+def test_q4_k_validation():
+    assert q4k(w=0) == NULL and q4k(x=0) == NULL and q4k(y=0) == NULL
+    assert q4k(m=0) == RANGE and q4k(m=5) == RANGE
+    assert q4k(n=0) == SHAPE and q4k(k=0) == SHAPE and q4k(k=255) == SHAPE and q4k(k=384) == SHAPE
+    assert q4k(w=W + 8) == ALIGN and q4k(x=X + 2) == ALIGN and q4k(y=Y + 2) == ALIGN
+    assert q4k(m=4, k=19456) == RANGE                   # activations exceed the LDS stage
+    assert q4k(y=W + 64) == ALIAS                        # output inside the weights
+    assert q4k(y=X, x=X) == ALIAS
+
+
+def test_q4_k_every_truncated_or_padded_size_is_an_error():
+    n, k = 2, 512
+    full = q.q4_k_bytes(n, k)
+    for b in range(full):
+        assert q4k(nbytes=b, n=n, k=k) == SIZE, b
+    assert q4k(nbytes=full + 1, n=n, k=k) == SIZE
+    assert q4k(nbytes=2 * full, n=n, k=k) == SIZE
+
+
+def test_q8_0_validation():
+    assert q80(w=0) == NULL and q80(x=0) == NULL and q80(y=0) == NULL
+    assert q80(m=0) == RANGE and q80(m=5) == RANGE
+    assert q80(k=48) == SHAPE and q80(n=-1) == SHAPE
+    assert q80(w=W + 2) == ALIGN and q80(x=X + 4) == ALIGN
+    assert q80(m=4, k=10272) == RANGE
+    assert q80(y=W + 4) == ALIAS
+    full = q.q8_0_bytes(2, 64)
+    for b in list(range(full)) + [full + 1]:
+        assert q80(nbytes=b) == SIZE, b
+
+
+def test_dequant_validation():
+    nb = q.q4_k_bytes(2, 256)
+    for fn in (L.qmv_dequant_q4_k_f32, L.qmv_dequant_q4_k_bf16):
+        assert fn(V(0), nb, V(Y), 2, 256, None) == NULL
+        assert fn(V(W), nb, V(0), 2, 256, None) == NULL
+        assert fn(V(W), nb - 1, V(Y), 2, 256, None) == SIZE
+        assert fn(V(W), nb, V(Y + 4), 2, 256, None) == ALIGN
+        assert fn(V(W), nb, V(W), 2, 256, None) == ALIAS
+        assert fn(V(W), nb, V(Y), 2, 100, None) == SHAPE
+    nb8 = q.q8_0_bytes(2, 64)
+    assert L.qmv_dequant_q8_0_f32(V(W), nb8 - 34, V(Y), 2, 64, None) == SIZE
+    assert L.qmv_dequant_q8_0_f32(V(W), nb8, V(Y + 8), 2, 64, None) == ALIGN
+
+
+def test_prefill_validation():
+    nb = q.q4_k_bytes(4, 512)
+    f = L.qmm_q4_k_prefill
+    assert f(V(W), nb, V(X), V(Y), 0, 4, 512, None) == RANGE
+    assert f(V(W), nb, V(0), V(Y), 8, 4, 512, None) == NULL
+    assert f(V(W), nb + 144, V(X), V(Y), 8, 4, 512, None) == SIZE
+    assert f(V(W), nb, V(X), V(Y + 4), 8, 4, 512, None) == ALIGN
+    assert f(V(W), nb, V(X), V(X + 16), 8, 4, 512, None) == ALIAS
+
+
+def moe(**kw):
+    a = dict(wg=W, wu=W + (1 << 28), wd=W + (2 << 28), bank=None, logits=X, x=X + (1 << 20), y=Y,
+             ids=Y + (1 << 20), wts=Y + (2 << 20), pairs=Y + (3 << 20), ws=WS, ws_bytes=None,
+             t=1, h=256, f=256, e=8, k=2)
+    a.update(kw)
+    bank = a["e"] * a["f"] * (a["h"] // 256) * 144 if a["bank"] is None else a["bank"]
+    need = L.qmv_q4_k_moe_workspace(a["t"], a["h"], a["f"], a["e"], a["k"])
+    ws_bytes = need if a["ws_bytes"] is None else a["ws_bytes"]
+    return L.qmv_q4_k_moe(V(a["wg"]), V(a["wu"]), V(a["wd"]), bank, V(a["logits"]), V(a["x"]), V(a["y"]),
+                          V(a["ids"]), V(a["wts"]), V(a["pairs"]), V(a["ws"]), ws_bytes,
+                          a["t"], a["h"], a["f"], a["e"], a["k"], None)
+
+
+def test_moe_validation():
+    assert L.qmv_q4_k_moe_workspace(1, 2048, 768, 128, 8) > 0
+    assert L.qmv_q4_k_moe_workspace(0, 2048, 768, 128, 8) == 0
+    assert L.qmv_q4_k_moe_workspace(5, 2048, 768, 128, 8) == 0
+    assert L.qmv_q4_k_moe_workspace(1, 2048, 768, 128, 9) == 0
+    assert moe(wg=0) == NULL and moe(logits=0) == NULL and moe(y=0) == NULL
+    assert moe(t=0) == RANGE and moe(t=5) == RANGE and moe(k=0) == RANGE and moe(k=9, e=16) == RANGE
+    assert moe(k=4, e=3) == RANGE and moe(e=257) == RANGE
+    assert moe(h=300) == SHAPE and moe(f=0) == SHAPE
+    assert moe(bank=8 * 256 * 144 - 1) == SIZE and moe(bank=8 * 256 * 144 + 144) == SIZE
+    assert moe(wd=W + (2 << 28) + 8) == ALIGN and moe(ws=WS + 128) == ALIGN and moe(x=X + 2) == ALIGN
+    assert moe(ws=0) == WORKSPACE and moe(ws_bytes=16) == WORKSPACE
+    assert moe(y=W + 1024) == ALIAS                       # output inside the gate bank
+    assert moe(ws=Y) == ALIAS                             # workspace over the output
+    assert moe(pairs=Y + (1 << 20)) == ALIAS              # two outputs overlap
+
+
+def test_moe_bank_every_truncated_size_is_an_error():
+    bank = 8 * 256 * 144
+    for b in range(0, bank, 97):
+        assert moe(bank=b) == SIZE, b
+    assert moe(bank=bank - 1) == SIZE
+
+
+def test_one_hip_runtime_in_the_process():
+    # the library must bind to the HIP runtime torch loaded, never load a second one
+    import torch  # noqa: F401
+    with open("/proc/self/maps") as f:
+        paths = {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    real = {os.path.realpath(p) for p in paths}
+    assert len(real) == 1, real
