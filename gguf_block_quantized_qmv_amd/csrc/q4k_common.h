@@ -136,8 +136,9 @@ __device__ __forceinline__ void q4k_chunk_bf16(float (&acc)[M], const int m_act,
 }
 
 // Swizzled position of fp32 granule g (4 activations) when a 64-weight chunk
-// spans 16 granules: granule i of chunk c sits at slot i ^ (c & 7).
-__device__ __forceinline__ int swizzle_granule_f32(int g) { return g ^ ((g >> 4) & 7); }
+// spans 16 granules: granule i of chunk c sits at slot i ^ (c & 15), so 16 lanes
+// reading the same granule of consecutive chunks hit 16 different bank groups.
+__device__ __forceinline__ int swizzle_granule_f32(int g) { return g ^ ((g >> 4) & 15); }
 
 // Activations in fp32 (the MoE down projection's h): hs holds rows of K/4
 // swizzled granules (gpr per row), hsum rows of K/32 sub-block sums.
@@ -183,6 +184,56 @@ __device__ __forceinline__ void q4k_chunk_f32(float (&acc)[M], const int m_act, 
     acc[r] = __builtin_fmaf(cs.a1, s_hi[r], acc[r]);
     acc[r] = __builtin_fmaf(-cs.b1, hsm.y, acc[r]);
   }
+}
+
+// Stage M bf16 activation rows of K values (row r at x + r*K) into LDS: swizzled
+// granules (gpr = K/8 per row) then, after a barrier, each row's K/32 sub-block
+// sums read back from LDS and summed in index order. Loads are batched eight
+// granules per thread so their latencies overlap. Ends with a barrier.
+template <int M, int NT>
+__device__ __forceinline__ void stage_bf16_rows_lds(const uint16_t *__restrict__ x, uint4 *xs, float *xsum,
+                                                    const int gpr, const int nsub) {
+  const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+  const int total = M * gpr;
+  for (int base = 0; base < total; base += NT * 8) {
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = base + (int)threadIdx.x + i * NT;
+      v[i] = xg[g < total ? g : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = base + (int)threadIdx.x + i * NT;
+      if (g < total) {
+        int r = 0;
+#pragma unroll
+        for (int q = 1; q < M; ++q) r += g >= q * gpr;
+        const int gi = g - r * gpr;
+        xs[r * gpr + swizzle_granule(gi)] = v[i];
+      }
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < M * nsub; t += NT) {
+    int r = 0;
+#pragma unroll
+    for (int q = 1; q < M; ++q) r += t >= q * nsub;
+    const int sb = t - r * nsub;
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = xs[r * gpr + swizzle_granule(4 * sb + q)];
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s += bf16_bits_to_f32(wv[e] & 0xFFFFu);
+        s += bf16_bits_to_f32(wv[e] >> 16);
+      }
+    }
+    xsum[r * nsub + sb] = s;
+  }
+  __syncthreads();
 }
 
 // Stage one bf16 activation row (K values) into LDS as swizzled granules plus

@@ -100,7 +100,7 @@ int qmv_q4_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, in
   if (m < 1 || m > QMV_MAX_ROWS) return QMV_ERR_RANGE;
   int rc = check_matrix(w, w_bytes, n, k, 256, 144, 16);
   if (rc) return rc;
-  if ((size_t)m * (size_t)k * 2 + (size_t)m * (size_t)(k / 32) * 4 > QMV_LDS_X_BYTES) return QMV_ERR_RANGE;
+  if ((size_t)m * ((size_t)(k / 128) * 17 * 16 + (size_t)(k / 32) * 4) > QMV_LDS_X_BYTES) return QMV_ERR_RANGE;
   if (!aligned(x_bf16, 16) || !aligned(y, 4)) return QMV_ERR_ALIGN;
   const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 4;
   if (overlap(y, yb, w, w_bytes) || overlap(y, yb, x_bf16, xb)) return QMV_ERR_ALIAS;

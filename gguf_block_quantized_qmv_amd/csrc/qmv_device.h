@@ -70,19 +70,27 @@ __device__ __forceinline__ float row4_sum(float v) {
   return v;
 }
 
-// Sum over groups of G lanes (G in {4, 8, 16}); every lane of a group ends with the same bits.
+// Sum over aligned groups of G lanes (G in {4, 8, 16, 32, 64}); every lane of a
+// group ends with the same bits (each step adds a commutative pair).
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(G == 4 || G == 8 || G == 16, "group size");
-  if constexpr (G == 16) return row16_sum(v);
+  static_assert(G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group size");
+  if constexpr (G == 4) return row4_sum(v);
   else if constexpr (G == 8) return row8_sum(v);
-  else return row4_sum(v);
+  else {
+    v = row16_sum(v);
+    if constexpr (G >= 32) v += __shfl_xor(v, 16);
+    if constexpr (G == 64) v += __shfl_xor(v, 32);
+    return v;
+  }
 }
 
-// Swizzled position of 16-byte granule g of a staged activation row. Lanes that
-// read consecutive 128-byte chunks in the same instruction land on different
-// LDS bank groups: granule i of chunk c sits at slot i ^ (c & 7).
-__device__ __forceinline__ int swizzle_granule(int g) { return g ^ ((g >> 3) & 7); }
+// Swizzled position of 16-byte granule g of a staged activation row (8 granules
+// = one 64-weight chunk of bf16). gfx950 serves a 16-byte LDS read for 16 lanes
+// per cycle across 64 banks; lanes that read the same granule of 16 consecutive
+// chunks land on 16 different bank groups when granule i of chunk c sits at
+// slot i ^ ((c >> 1) & 7).
+__device__ __forceinline__ int swizzle_granule(int g) { return g ^ ((g >> 4) & 7); }
 
 // Record a HIP failure for qmv_last_error() (thread-local text kept by the ABI layer).
 void set_error_detail(const char *what, int hip_code, const char *hip_text);
