@@ -31,15 +31,6 @@ namespace qmv {
 namespace {
 
 
-// Padded LDS layout of a staged bf16 activation row: 16-byte granules, two
-// 64-weight chunks (16 granules) per 17-granule slot. Granule g of chunk ci sits
-// at (ci >> 1) * 17 + (ci & 1) * 8 + g, so 16 lanes reading granule g of 16
-// consecutive chunks hit 16 distinct bank groups (gfx950 serves 16 lanes of a
-// 16-byte read per cycle over 64 banks) while the 8 granules of one chunk stay
-// contiguous and are addressed with immediate offsets.
-__device__ __forceinline__ int padded_granule(int gi) { return (gi >> 4) * 17 + (gi & 15); }
-__host__ __device__ constexpr size_t padded_row_granules(int k) { return (size_t)(k >> 7) * 17; }
-
 template <int M>
 __host__ __device__ constexpr size_t dense_lds_bytes(int k) {
   return (size_t)M * padded_row_granules(k) * 16 + (size_t)M * (size_t)(k >> 5) * 4;

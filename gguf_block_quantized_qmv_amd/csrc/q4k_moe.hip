@@ -8,23 +8,27 @@
 // Two launches on the caller's stream, no host round trip:
 //
 //  1. moe_gate_up_kernel, grid (F/16 row tiles) x (max distinct experts).
-//     Every workgroup's first wave recomputes the routing of the <= 4 tokens
-//     (k rounds of a wave-wide argmax over the logits, ties to the lower id)
-//     and the gather list: all (expert, token) pairs sorted by expert, then
-//     token. The expert ids live in LDS (next to the staged activations).
-//     Workgroup (0, 0) also writes the routing outputs and the tables that
-//     launch 2 reads. Workgroup (tile, s) then computes, for distinct expert s
-//     (ascending id) and the tokens that chose it, 16 rows of W_gate x and
-//     W_up x with the dense GEMV's per-chunk arithmetic (x staged in LDS) and
-//     stores h = silu(g) * u in fp32 for each (expert, token) pair.
-//  2. moe_down_kernel, grid H/16 row tiles. Each workgroup stages every pair's
-//     h in LDS, walks the distinct experts in ascending id, streams 16 rows of
-//     that expert's W_down once for all of its tokens, and accumulates
-//     y_t += r_(t,e) * (W_down[e] h_(e,t)) per token in that fixed order.
+//     The activations of all T tokens start loading at once; meanwhile wave t
+//     routes token t (k rounds of a wave-wide argmax, ties to the lower id,
+//     then the softmax over the k chosen logits). Every wave then sorts the
+//     (expert, token) pairs in registers (rank by comparison, forward lane
+//     permute) and finds its workgroup's distinct expert, the s-th smallest,
+//     and the tokens that chose it, without another barrier. Workgroup (0, 0)
+//     writes the routing outputs and the tables launch 2 reads. The expert's
+//     gate and up rows are requested as soon as the expert is known; the
+//     activation sub-block sums are formed in LDS while they arrive. Each
+//     16-row tile stores h = silu(W_gate x) * (W_up x) in fp32 per pair.
+//  2. moe_down_kernel, grid H/8 row tiles. Four lanes own one W_down row and
+//     the workgroup's eight groups of 32 lanes share its 8 rows, group g taking
+//     the distinct experts g, g + 8, ...; their first (expert, block) weight
+//     loads are issued before every pair's h is staged in LDS. Each (pair, row)
+//     result z lands in LDS, and y_t = sum over token t's experts, in ascending
+//     expert id, of weight * z, accumulated with fma from zero.
 //
 // Each selected expert's weights are read once per call. A token's result is
-// bit-identical whatever other tokens share the call: its experts are visited
-// in the same ascending order and every token slot runs the same instructions.
+// bit-identical whatever other tokens share the call: the arithmetic applied
+// to one (expert, token) pair does not depend on which lanes or waves run it,
+// and a token's experts are combined in the same ascending order.
 #include <limits.h>
 
 #include "q4k_common.h"
@@ -36,116 +40,297 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLanesPerRow = 16;
-constexpr int kRowsPerWave = 64 / kLanesPerRow;
-constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
 constexpr int kMaxPairs = QMV_MOE_MAX_TOKENS * QMV_MOE_MAX_TOP_K;
-constexpr size_t kTableBytes = 4096;  // routing tables at the start of the workspace
+constexpr int kTopK = QMV_MOE_MAX_TOP_K;
+// gate/up: 16 lanes per W row, 4 rows per wave, 16 rows per workgroup
+constexpr int kUpLanes = 16;
+constexpr int kUpRows = kWaves * (64 / kUpLanes);
+constexpr int kUpDepth = 2;  // steps of gate + up loads in flight
+// down: 4 lanes per W row; a workgroup owns 8 rows, and its 8 lane groups of
+// 32 lanes (8 rows x 4 chunks) split the distinct experts
+constexpr int kDnRows = 8;
+constexpr int kDnGroups = kThreads / (4 * kDnRows);
+constexpr int kDnDepth = 6;  // (expert, block) units of loads in flight per lane
 
-struct Routing {
+// Tables at the start of the workspace, written by launch 1 and read by launch 2.
+struct Table {
   int n_pairs;
   int n_slots;
-  int slot_expert[kMaxPairs];  // distinct experts, ascending
-  int slot_pair0[kMaxPairs];   // first gather-list position of each distinct expert
-  int slot_ntok[kMaxPairs];    // number of tokens that chose it
   int pair_expert[kMaxPairs];  // gather list: sorted by expert, then token
   int pair_token[kMaxPairs];
   float pair_weight[kMaxPairs];
-  int sel_id[QMV_MOE_MAX_TOKENS][QMV_MOE_MAX_TOP_K];  // per token, rank order
-  float sel_w[QMV_MOE_MAX_TOKENS][QMV_MOE_MAX_TOP_K];
+  int slot_expert[kMaxPairs];  // distinct experts, ascending
+  int slot_pair0[kMaxPairs];   // first gather-list position of each
+  int slot_ntok[kMaxPairs];    // tokens that chose it
 };
-static_assert(sizeof(Routing) <= kTableBytes, "routing tables exceed their workspace slot");
-static_assert(sizeof(Routing) % 4 == 0, "routing tables are copied as words");
+constexpr size_t kTableBytes = 4096;
+static_assert(sizeof(Table) <= kTableBytes, "routing tables exceed their workspace slot");
+static_assert(sizeof(Table) % 4 == 0, "routing tables are copied as words");
 
-// Wave 0: top-k selection and renormalised weights for every token.
-__device__ __forceinline__ void route_tokens(const float *__restrict__ logits, const int T, const int E, const int K, Routing *R) {
-  const int lane = threadIdx.x;
-  for (int t = 0; t < T; ++t) {
-    float v[4];
-    bool live[4];
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Routing
+// ---------------------------------------------------------------------------
+
+// Logits as order-preserving unsigned keys: for finite a, b (with -0 made +0
+// first), a < b exactly when key(a) < key(b). Key 0 marks an absent or
+// already chosen expert; every finite logit maps above it.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Maximum of k over the wave: DPP butterfly inside each 16-lane row, then the
+// four row maxima on the scalar side.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
+  k = max(k, dpp_u32<0xB1>(k));   // quad_perm [1,0,3,2]
+  k = max(k, dpp_u32<0x4E>(k));   // quad_perm [2,3,0,1]
+  k = max(k, dpp_u32<0x141>(k));  // row_half_mirror
+  k = max(k, dpp_u32<0x140>(k));  // row_mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)k, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)k, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)k, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)k, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// One wave routes token t. Lane l holds experts l, l + 64, l + 128, l + 192.
+// Each of the k rounds takes the largest remaining logit (a wave-wide max of
+// the keys) and, among the experts holding it, the lowest id (the first
+// candidate slot i whose ballot is non-empty, lowest lane in it), then retires
+// that expert. The softmax over the chosen logits follows: exp(l_j - l_0)
+// summed in rank order, each divided by the sum. Writes sid[t][j], swt[t][j]
+// for j < K. Logits must be finite.
+__device__ __forceinline__ void route_token(const float *__restrict__ logits, const int t, const int E, const int K,
+                                            int (*sid)[kTopK], float (*swt)[kTopK]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t kv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      live[i] = e < E;
-      v[i] = live[i] ? logits[(size_t)t * E + e] : 0.0f;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    kv[i] = e < E ? logit_key(logits[(size_t)t * E + e]) : 0u;
+  }
+  // kept in registers: every loop below is fully unrolled with K tested inside
+  uint32_t selk[kTopK];
+  int seli[kTopK];
 #pragma unroll
-    for (int j = 0; j < QMV_MOE_MAX_TOP_K; ++j) {
-      if (j >= K) break;
-      // this lane's best remaining candidate (ids ascend with i, so '>' keeps the lower id on ties)
-      float bv = 0.0f;
-      int bid = INT_MAX;
+  for (int j = 0; j < kTopK; ++j) {
+    selk[j] = 0u;
+    seli[j] = 0;
+    if (j < K) {
+      const uint32_t m = wave_max_u32(max(max(kv[0], kv[1]), max(kv[2], kv[3])));
+      int id = -1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (live[i] && (bid == INT_MAX || v[i] > bv)) {
-          bv = v[i];
-          bid = lane + 64 * i;
-        }
-      // wave-wide argmax: larger logit wins, equal logits go to the lower id
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oid = __shfl_xor(bid, off);
-        if (oid != INT_MAX && (bid == INT_MAX || ov > bv || (ov == bv && oid < bid))) {
-          bv = ov;
-          bid = oid;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const unsigned long long b = __ballot(kv[i] == m);
+        if (id < 0 && b) id = 64 * i + __ffsll((long long)b) - 1;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i == bid) live[i] = false;
-      if (lane == 0) {
-        R->sel_id[t][j] = bid;
-        R->sel_w[t][j] = bv;  // the selected logit, turned into a weight below
-      }
+        if (lane + 64 * i == id) kv[i] = 0u;
+      selk[j] = m;
+      seli[j] = id;
     }
-    if (lane == 0) {
-      // softmax over the selected logits, largest first: exp(l_j - l_0) / sum in rank order
-      const float l0 = R->sel_w[t][0];
-      float sum = 0.0f;
-      for (int j = 0; j < K; ++j) {
-        const float ex = expf(R->sel_w[t][j] - l0);
-        R->sel_w[t][j] = ex;
-        sum += ex;
-      }
-      for (int j = 0; j < K; ++j) R->sel_w[t][j] = R->sel_w[t][j] / sum;
+  }
+  const float l0 = key_logit(selk[0]);
+  float ex[kTopK];
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kTopK; ++j) {
+    ex[j] = 0.0f;
+    if (j < K) {
+      ex[j] = expf(key_logit(selk[j]) - l0);
+      sum += ex[j];
     }
+  }
+#pragma unroll
+  for (int j = 0; j < kTopK; ++j)
+    if (j < K && lane == j) {
+      sid[t][j] = seli[j];
+      swt[t][j] = ex[j] / sum;
+    }
+}
+
+// The T*K (expert, token) pairs, sorted by expert then token, computed by one
+// wave from the routing in LDS. Lane p < P holds pair p in routing order
+// (token p / K, rank p % K); lane r < P holds the r-th pair of the sorted order.
+struct Pairs {
+  int key;                   // expert * 4 + token of this lane's pair in routing order (INT_MAX past P)
+  float wgt;                 // its routing weight
+  int skey;                  // sorted order
+  float sw;
+  unsigned long long heads;  // sorted positions that start a new expert
+};
+
+__device__ __forceinline__ Pairs sort_pairs(const int (*sid)[kTopK], const float (*swt)[kTopK], const int P,
+                                            const int K) {
+  const int lane = threadIdx.x & 63;
+  Pairs s;
+  s.key = INT_MAX;
+  s.wgt = 0.0f;
+  if (lane < P) {
+    const int t = lane / K, j = lane - t * K;
+    s.key = sid[t][j] * QMV_MOE_MAX_TOKENS + t;
+    s.wgt = swt[t][j];
+  }
+  // keys are distinct (a token picks distinct experts), so ranks 0..P-1 are a
+  // permutation; lanes past P keep their own index to complete it
+  int rank = 0;
+  for (int q = 0; q < P; ++q) rank += __builtin_amdgcn_readlane(s.key, q) < s.key;
+  if (lane >= P) rank = lane;
+  s.skey = __builtin_amdgcn_ds_permute(rank * 4, s.key);
+  s.sw = __builtin_bit_cast(float, __builtin_amdgcn_ds_permute(rank * 4, __builtin_bit_cast(int, s.wgt)));
+  const int se = s.skey / QMV_MOE_MAX_TOKENS;
+  const int prev = __shfl(se, (lane + 63) & 63);
+  s.heads = __ballot(lane < P && (lane == 0 || se != prev));
+  return s;
+}
+
+// Distinct expert `slot` (ascending) of the sorted pairs: its id, first sorted
+// position and token count, and its tokens in ascending order. p0 < 0 when
+// fewer experts were chosen. All values are wave-uniform.
+template <int T>
+struct Slot {
+  int e, p0, ntok;
+  int tok[T];
+};
+
+template <int T>
+__device__ __forceinline__ Slot<T> find_slot(const Pairs &s, const int slot, const int P) {
+  const int lane = threadIdx.x & 63;
+  const bool head = (s.heads >> lane) & 1ull;
+  const int below = __popcll(s.heads & ((1ull << lane) - 1ull));
+  const unsigned long long mine = __ballot(head && below == slot);
+  Slot<T> r;
+  r.p0 = __ffsll((long long)mine) - 1;
+  r.e = 0;
+  r.ntok = 0;
+#pragma unroll
+  for (int i = 0; i < T; ++i) r.tok[i] = 0;
+  if (r.p0 < 0) return r;
+  const unsigned long long after = s.heads & ~((2ull << r.p0) - 1ull);
+  const int next = after ? __ffsll((long long)after) - 1 : P;
+  r.ntok = next - r.p0;
+  r.e = __builtin_amdgcn_readlane(s.skey, r.p0) / QMV_MOE_MAX_TOKENS;
+#pragma unroll
+  for (int i = 0; i < T; ++i)
+    if (i < r.ntok) r.tok[i] = __builtin_amdgcn_readlane(s.skey, r.p0 + i) % QMV_MOE_MAX_TOKENS;
+  return r;
+}
+
+// Routing outputs and the tables of launch 2, written by one wave.
+__device__ __forceinline__ void write_routing(const Pairs &s, const int P, int32_t *__restrict__ topk_ids,
+                                              float *__restrict__ topk_w, int32_t *__restrict__ pairs_out,
+                                              Table *__restrict__ tab) {
+  const int lane = threadIdx.x & 63;
+  const int se = s.skey / QMV_MOE_MAX_TOKENS, st = s.skey % QMV_MOE_MAX_TOKENS;
+  if (lane < P) {
+    if (topk_ids) topk_ids[lane] = s.key / QMV_MOE_MAX_TOKENS;
+    if (topk_w) topk_w[lane] = s.wgt;
+    if (pairs_out) {
+      pairs_out[2 * lane] = se;
+      pairs_out[2 * lane + 1] = st;
+    }
+    tab->pair_expert[lane] = se;
+    tab->pair_token[lane] = st;
+    tab->pair_weight[lane] = s.sw;
+  }
+  if ((s.heads >> lane) & 1ull) {
+    const int slot = __popcll(s.heads & ((1ull << lane) - 1ull));
+    const unsigned long long after = s.heads & ~((2ull << lane) - 1ull);
+    const int next = after ? __ffsll((long long)after) - 1 : P;
+    tab->slot_expert[slot] = se;
+    tab->slot_pair0[slot] = lane;
+    tab->slot_ntok[slot] = next - lane;
+  }
+  if (lane == 0) {
+    tab->n_pairs = P;
+    tab->n_slots = __popcll(s.heads);
   }
 }
 
-// Wave 0, after route_tokens is visible: the sorted gather list and the distinct experts.
-__device__ __forceinline__ void build_gather_list(const int T, const int K, Routing *R) {
-  const int lane = threadIdx.x;
-  const int P = T * K;
-  if (lane < P) {
-    const int t = lane / K, j = lane - t * K;
-    const int e = R->sel_id[t][j];
-    const int key = e * QMV_MOE_MAX_TOKENS + t;
-    int rank = 0;
-    for (int q = 0; q < P; ++q) {
-      const int tq = q / K;
-      rank += (R->sel_id[tq][q - tq * K] * QMV_MOE_MAX_TOKENS + tq) < key;
+// ---------------------------------------------------------------------------
+// Launch 1: gate and up projections, silu gating
+// ---------------------------------------------------------------------------
+
+// One 64-weight chunk of a W row against the bf16 activations of `m_act`
+// tokens: token r's chunk granules at xc + xoff[r] (8 contiguous granules of
+// the padded layout), its two sub-block sums at xsc + soff[r].
+template <int T>
+__device__ __forceinline__ void chunk_bf16(float (&acc)[T], const int m_act, const uint4 hdr, const uint4 qa,
+                                           const uint4 qb, const ScaleSel &sel, const uint4 *__restrict__ xc,
+                                           const int (&xoff)[T], const float *__restrict__ xsc, const int (&soff)[T]) {
+  const ChunkScales cs = chunk_scales(hdr, sel);
+  const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+  bf16x2 lo[16], hi[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t l = qw[i] & 0x0F0F0F0Fu;
+    const uint32_t h = (qw[i] >> 4) & 0x0F0F0F0Fu;
+    lo[2 * i] = nibbles_to_bf16x2<false>(l);
+    lo[2 * i + 1] = nibbles_to_bf16x2<true>(l);
+    hi[2 * i] = nibbles_to_bf16x2<false>(h);
+    hi[2 * i + 1] = nibbles_to_bf16x2<true>(h);
+  }
+#pragma unroll
+  for (int r = 0; r < T; ++r) {
+    if (r >= m_act) break;
+    const uint4 *xr = xc + xoff[r];
+    float s_lo = 0.0f, s_hi = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint4 v = xr[g];
+      const uint4 u = xr[4 + g];
+      s_lo = __builtin_amdgcn_fdot2_f32_bf16(lo[4 * g + 0], __builtin_bit_cast(bf16x2, v.x), s_lo, false);
+      s_hi = __builtin_amdgcn_fdot2_f32_bf16(hi[4 * g + 0], __builtin_bit_cast(bf16x2, u.x), s_hi, false);
+      s_lo = __builtin_amdgcn_fdot2_f32_bf16(lo[4 * g + 1], __builtin_bit_cast(bf16x2, v.y), s_lo, false);
+      s_hi = __builtin_amdgcn_fdot2_f32_bf16(hi[4 * g + 1], __builtin_bit_cast(bf16x2, u.y), s_hi, false);
+      s_lo = __builtin_amdgcn_fdot2_f32_bf16(lo[4 * g + 2], __builtin_bit_cast(bf16x2, v.z), s_lo, false);
+      s_hi = __builtin_amdgcn_fdot2_f32_bf16(hi[4 * g + 2], __builtin_bit_cast(bf16x2, u.z), s_hi, false);
+      s_lo = __builtin_amdgcn_fdot2_f32_bf16(lo[4 * g + 3], __builtin_bit_cast(bf16x2, v.w), s_lo, false);
+      s_hi = __builtin_amdgcn_fdot2_f32_bf16(hi[4 * g + 3], __builtin_bit_cast(bf16x2, u.w), s_hi, false);
     }
-    R->pair_expert[rank] = e;
-    R->pair_token[rank] = t;
-    R->pair_weight[rank] = R->sel_w[t][j];
+    const float2 xsm = *reinterpret_cast<const float2 *>(xsc + soff[r]);
+    acc[r] = __builtin_fmaf(cs.a0, s_lo, acc[r]);
+    acc[r] = __builtin_fmaf(-cs.b0, xsm.x, acc[r]);
+    acc[r] = __builtin_fmaf(cs.a1, s_hi, acc[r]);
+    acc[r] = __builtin_fmaf(-cs.b1, xsm.y, acc[r]);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  const bool head = lane < P && (lane == 0 || R->pair_expert[lane] != R->pair_expert[lane - 1]);
-  const unsigned long long mask = __ballot(head);
-  if (head) {
-    const int slot = __popcll(mask & ((1ull << lane) - 1ull));
-    const unsigned long long later = (lane == 63) ? 0ull : (mask >> (lane + 1));
-    const int next = later ? lane + 1 + __ffsll((long long)later) - 1 : P;
-    R->slot_expert[slot] = R->pair_expert[lane];
-    R->slot_pair0[slot] = lane;
-    R->slot_ntok[slot] = next - lane;
+}
+
+constexpr int kStageBatch = 4;  // activation granules per thread per batch
+
+template <int T>
+__device__ __forceinline__ void load_x_batch(const uint4 *__restrict__ xg, const int base, const int total,
+                                             uint4 (&v)[kStageBatch]) {
+#pragma unroll
+  for (int i = 0; i < kStageBatch; ++i) {
+    const int g = base + (int)threadIdx.x + i * kThreads;
+    v[i] = xg[g < total ? g : 0];
   }
-  if (lane == 0) {
-    R->n_pairs = P;
-    R->n_slots = __popcll(mask);
+}
+
+template <int T>
+__device__ __forceinline__ void store_x_batch(uint4 *xs, const int base, const int total, const int gpr,
+                                              const int gpp, const uint4 (&v)[kStageBatch]) {
+#pragma unroll
+  for (int i = 0; i < kStageBatch; ++i) {
+    const int g = base + (int)threadIdx.x + i * kThreads;
+    if (g < total) {
+      int r = 0;
+#pragma unroll
+      for (int q = 1; q < T; ++q) r += g >= q * gpr;
+      xs[r * gpp + padded_granule(g - r * gpr)] = v[i];
+    }
   }
 }
 
@@ -155,184 +340,340 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(
     const uint16_t *__restrict__ x, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
     int32_t *__restrict__ pairs_out, uint8_t *__restrict__ ws, const int hidden, const int ffn, const int E,
     const int K) {
-  __shared__ Routing R;
+  __shared__ int sid[QMV_MOE_MAX_TOKENS][kTopK];
+  __shared__ float swt[QMV_MOE_MAX_TOKENS][kTopK];
   extern __shared__ uint4 lds[];
-  if (threadIdx.x < 64) route_tokens(logits, T, E, K, &R);
-  __syncthreads();
-  if (threadIdx.x < 64) build_gather_list(T, K, &R);
-  __syncthreads();
-
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
-    const int P = T * K;
-    for (int i = threadIdx.x; i < P; i += kThreads) {
-      const int t = i / K, j = i - t * K;
-      if (topk_ids) topk_ids[i] = R.sel_id[t][j];
-      if (topk_w) topk_w[i] = R.sel_w[t][j];
-      if (pairs_out) {
-        pairs_out[2 * i] = R.pair_expert[i];
-        pairs_out[2 * i + 1] = R.pair_token[i];
-      }
-    }
-    const int *src = reinterpret_cast<const int *>(&R);
-    int *dst = reinterpret_cast<int *>(ws);
-    for (int i = threadIdx.x; i < (int)(sizeof(Routing) / 4); i += kThreads) dst[i] = src[i];
-  }
-
-  const int slot = blockIdx.y;
-  if (slot >= R.n_slots) return;  // fewer distinct experts than the grid allows for
-  const int e = R.slot_expert[slot], p0 = R.slot_pair0[slot], ntok = R.slot_ntok[slot];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gpr = hidden >> 3, nsub = hidden >> 5;
+  const int gpp = (int)padded_row_granules(hidden);
   uint4 *xs = lds;
-  float *xsum = reinterpret_cast<float *>(lds + T * gpr);
-  for (int i = 0; i < ntok; ++i)
-    stage_bf16_row(x + (size_t)R.pair_token[p0 + i] * hidden, xs + i * gpr, xsum + i * nsub, gpr, nsub, threadIdx.x,
-                   kThreads);
+  float *xsum = reinterpret_cast<float *>(lds + (size_t)T * gpp);
+
+  // every token's activations: the first batch is in flight while the router runs
+  const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+  const int total = T * gpr;
+  uint4 v[kStageBatch];
+  load_x_batch<T>(xg, 0, total, v);
+  if (wave < T) route_token(logits, wave, E, K, sid, swt);
+  store_x_batch<T>(xs, 0, total, gpr, gpp, v);
+  for (int base = kStageBatch * kThreads; base < total; base += kStageBatch * kThreads) {
+    uint4 vb[kStageBatch];
+    load_x_batch<T>(xg, base, total, vb);
+    store_x_batch<T>(xs, base, total, gpr, gpp, vb);
+  }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
-  const int j = lane & (kLanesPerRow - 1);
-  const int f = (blockIdx.x * kWaves + (threadIdx.x >> 6)) * kRowsPerWave + lane / kLanesPerRow;
-  if (f >= ffn) return;
-  const int c = j & 3;
-  const ScaleSel sel = scale_selectors(c);
+  const int P = T * K;
+  const Pairs pr = sort_pairs(sid, swt, P, K);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && wave == 0)
+    write_routing(pr, P, topk_ids, topk_w, pairs_out, reinterpret_cast<Table *>(ws));
+  const Slot<T> sl = find_slot<T>(pr, (int)blockIdx.y, P);
+  if (sl.p0 < 0) return;  // fewer distinct experts than the grid allows for (uniform over the workgroup)
+
+  const int j = lane & (kUpLanes - 1);
+  const int c = j & 3, jb = j >> 2;
+  const int f = blockIdx.x * kUpRows + wave * (64 / kUpLanes) + lane / kUpLanes;
+  const bool active = f < ffn;
   const int nblk = hidden >> 8;
   const size_t row_bytes = (size_t)nblk * kQ4KBlockBytes;
-  const size_t expert_bytes = (size_t)ffn * row_bytes;
-  const uint8_t *grow = w_gate + (size_t)e * expert_bytes + (size_t)f * row_bytes;
-  const uint8_t *urow = w_up + (size_t)e * expert_bytes + (size_t)f * row_bytes;
+  const size_t off = (size_t)sl.e * (size_t)ffn * row_bytes + (size_t)(active ? f : 0) * row_bytes +
+                     (size_t)jb * kQ4KBlockBytes;
+  const uint8_t *gl = w_gate + off;
+  const uint8_t *ul = w_up + off;
   const int nsteps = (nblk + 3) >> 2;
 
+  uint4 gh[kUpDepth], ga[kUpDepth], gb[kUpDepth], uh[kUpDepth], ua[kUpDepth], ub[kUpDepth];
+#pragma unroll
+  for (int u = 0; u < kUpDepth; ++u) {
+    if (active && u < nsteps && 4 * u + jb < nblk) {
+      const size_t o = (size_t)(4 * u) * kQ4KBlockBytes;
+      gh[u] = *reinterpret_cast<const uint4 *>(gl + o);
+      ga[u] = *reinterpret_cast<const uint4 *>(gl + o + 16 + 32 * c);
+      gb[u] = *reinterpret_cast<const uint4 *>(gl + o + 32 + 32 * c);
+      uh[u] = *reinterpret_cast<const uint4 *>(ul + o);
+      ua[u] = *reinterpret_cast<const uint4 *>(ul + o + 16 + 32 * c);
+      ub[u] = *reinterpret_cast<const uint4 *>(ul + o + 32 + 32 * c);
+    }
+  }
+
+  // sub-block sums of every staged token (index order) while the weights arrive
+  for (int t = threadIdx.x; t < T * nsub; t += kThreads) {
+    int r = 0;
+#pragma unroll
+    for (int q = 1; q < T; ++q) r += t >= q * nsub;
+    const int sb = t - r * nsub;
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 g = xs[r * gpp + padded_granule(4 * sb + q)];
+      const uint32_t wv[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s += bf16_bits_to_f32(wv[e] & 0xFFFFu);
+        s += bf16_bits_to_f32(wv[e] >> 16);
+      }
+    }
+    xsum[r * nsub + sb] = s;
+  }
+  __syncthreads();
+  if (!active) return;
+
+  const ScaleSel sel = scale_selectors(c);
+  int xoff[T], soff[T];
+#pragma unroll
+  for (int r = 0; r < T; ++r) {
+    xoff[r] = sl.tok[r] * gpp;
+    soff[r] = sl.tok[r] * nsub;
+  }
+  // chunk 16s + j of the row sits at padded granule 136 s + (j >> 1) * 17 + (j & 1) * 8
+  const uint4 *xb = xs + (j >> 1) * 17 + (j & 1) * 8;
+  const float *sb = xsum + 2 * j;
   float acc_g[T], acc_u[T];
 #pragma unroll
   for (int r = 0; r < T; ++r) acc_g[r] = acc_u[r] = 0.0f;
 
-  constexpr int D = 2;
-  for (int s0 = 0; s0 < nsteps; s0 += D) {
-    uint4 gh[D], ga[D], gb[D], uh[D], ua[D], ub[D];
-    bool ok[D];
+  for (int s0 = 0; s0 < nsteps; s0 += kUpDepth) {
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int b = (s0 + u) * 4 + (j >> 2);
-      ok[u] = b < nblk;
-      if (ok[u]) {
-        const uint8_t *gp = grow + (size_t)b * kQ4KBlockBytes;
-        const uint8_t *up = urow + (size_t)b * kQ4KBlockBytes;
-        gh[u] = *reinterpret_cast<const uint4 *>(gp);
-        ga[u] = *reinterpret_cast<const uint4 *>(gp + 16 + 32 * c);
-        gb[u] = *reinterpret_cast<const uint4 *>(gp + 32 + 32 * c);
-        uh[u] = *reinterpret_cast<const uint4 *>(up);
-        ua[u] = *reinterpret_cast<const uint4 *>(up + 16 + 32 * c);
-        ub[u] = *reinterpret_cast<const uint4 *>(up + 32 + 32 * c);
+    for (int u = 0; u < kUpDepth; ++u) {
+      const int s = s0 + u;
+      if (s < nsteps && 4 * s + jb < nblk) {
+        chunk_bf16<T>(acc_g, sl.ntok, gh[u], ga[u], gb[u], sel, xb + s * 136, xoff, sb + 32 * s, soff);
+        chunk_bf16<T>(acc_u, sl.ntok, uh[u], ua[u], ub[u], sel, xb + s * 136, xoff, sb + 32 * s, soff);
+      }
+      const int sn = s + kUpDepth;
+      if (sn < nsteps && 4 * sn + jb < nblk) {
+        const size_t o = (size_t)(4 * sn) * kQ4KBlockBytes;
+        gh[u] = *reinterpret_cast<const uint4 *>(gl + o);
+        ga[u] = *reinterpret_cast<const uint4 *>(gl + o + 16 + 32 * c);
+        gb[u] = *reinterpret_cast<const uint4 *>(gl + o + 32 + 32 * c);
+        uh[u] = *reinterpret_cast<const uint4 *>(ul + o);
+        ua[u] = *reinterpret_cast<const uint4 *>(ul + o + 16 + 32 * c);
+        ub[u] = *reinterpret_cast<const uint4 *>(ul + o + 32 + 32 * c);
       }
     }
-#pragma unroll
-    for (int u = 0; u < D; ++u)
-      if (ok[u]) {
-        const int ci = (s0 + u) * 16 + j;
-        q4k_chunk_bf16<T>(acc_g, ntok, gh[u], ga[u], gb[u], ci, sel, xs, xsum, gpr, nsub);
-        q4k_chunk_bf16<T>(acc_u, ntok, uh[u], ua[u], ub[u], ci, sel, xs, xsum, gpr, nsub);
-      }
   }
 
   float *h = reinterpret_cast<float *>(ws + kTableBytes);
 #pragma unroll
   for (int r = 0; r < T; ++r) {
-    if (r >= ntok) break;
+    if (r >= sl.ntok) break;
     const float g = row16_sum(acc_g[r]);
     const float u = row16_sum(acc_u[r]);
-    if (j == r) h[(size_t)(p0 + r) * ffn + f] = g / (1.0f + expf(-g)) * u;
+    if (j == r) h[(size_t)(sl.p0 + r) * ffn + f] = g / (1.0f + expf(-g)) * u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch 2: down projection and the weighted combine
+// ---------------------------------------------------------------------------
+
+// One 64-weight chunk of a W_down row against the fp32 h of `m_act` pairs:
+// pair r's chunk at hc + r * stride (16 contiguous granules), its two sub-block
+// sums at hsc + r * nsub. Quants become exact fp32 two at a time (a nibble byte
+// read as e4m3 is q * 2^-9; the conversion scales by 2^9).
+template <int T>
+__device__ __forceinline__ void chunk_f32(float (&acc)[T], const int m_act, const uint4 hdr, const uint4 qa,
+                                          const uint4 qb, const ScaleSel &sel, const uint4 *__restrict__ hc,
+                                          const int stride, const float *__restrict__ hsc, const int nsub) {
+  const ChunkScales cs = chunk_scales(hdr, sel);
+  const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+  float s_lo[T], s_hi[T];
+#pragma unroll
+  for (int r = 0; r < T; ++r) s_lo[r] = s_hi[r] = 0.0f;
+  // quant word g: weights 4g..4g+3 of sub-block 2c (low nibbles) and of 2c+1 (high nibbles)
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const uint32_t l = qw[g] & 0x0F0F0F0Fu;
+    const uint32_t hb = (qw[g] >> 4) & 0x0F0F0F0Fu;
+    const floatx2 l01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(l, 512.0f, false);
+    const floatx2 l23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(l, 512.0f, true);
+    const floatx2 h01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, 512.0f, false);
+    const floatx2 h23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hb, 512.0f, true);
+#pragma unroll
+    for (int r = 0; r < T; ++r) {
+      if (r >= m_act) break;
+      const uint4 v = hc[r * stride + g];
+      const uint4 u = hc[r * stride + 8 + g];
+      s_lo[r] = __builtin_fmaf(l01.x, __builtin_bit_cast(float, v.x), s_lo[r]);
+      s_hi[r] = __builtin_fmaf(h01.x, __builtin_bit_cast(float, u.x), s_hi[r]);
+      s_lo[r] = __builtin_fmaf(l01.y, __builtin_bit_cast(float, v.y), s_lo[r]);
+      s_hi[r] = __builtin_fmaf(h01.y, __builtin_bit_cast(float, u.y), s_hi[r]);
+      s_lo[r] = __builtin_fmaf(l23.x, __builtin_bit_cast(float, v.z), s_lo[r]);
+      s_hi[r] = __builtin_fmaf(h23.x, __builtin_bit_cast(float, u.z), s_hi[r]);
+      s_lo[r] = __builtin_fmaf(l23.y, __builtin_bit_cast(float, v.w), s_lo[r]);
+      s_hi[r] = __builtin_fmaf(h23.y, __builtin_bit_cast(float, u.w), s_hi[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < T; ++r) {
+    if (r >= m_act) break;
+    const float2 hsm = *reinterpret_cast<const float2 *>(hsc + r * nsub);
+    acc[r] = __builtin_fmaf(cs.a0, s_lo[r], acc[r]);
+    acc[r] = __builtin_fmaf(-cs.b0, hsm.x, acc[r]);
+    acc[r] = __builtin_fmaf(cs.a1, s_hi[r], acc[r]);
+    acc[r] = __builtin_fmaf(-cs.b1, hsm.y, acc[r]);
+  }
+}
+
+// h of all pairs in LDS: chunk q (64 values, 16 granules) of the concatenated
+// pair rows at granules 17q .. 17q + 15. Four lanes of a row read granule i of
+// four consecutive chunks: bank groups (q + i) mod 16, all distinct.
+__device__ __forceinline__ int h_slot(int g) { return (g >> 4) * 17 + (g & 15); }
+
+constexpr int kTableWords = (int)(sizeof(Table) / 4);
+static_assert(kTableWords <= kThreads, "one table word per thread");
+
+constexpr int kHBatch = 4;  // h granules per thread per batch
+
+__device__ __forceinline__ void load_h_batch(const uint4 *__restrict__ hg, const int base, const int total,
+                                             uint4 (&v)[kHBatch]) {
+#pragma unroll
+  for (int i = 0; i < kHBatch; ++i) {
+    const int g = base + (int)threadIdx.x + i * kThreads;
+    v[i] = hg[g < total ? g : 0];
+  }
+}
+
+__device__ __forceinline__ void store_h_batch(uint4 *hs, const int base, const int total,
+                                              const uint4 (&v)[kHBatch]) {
+#pragma unroll
+  for (int i = 0; i < kHBatch; ++i) {
+    const int g = base + (int)threadIdx.x + i * kThreads;
+    if (g < total) hs[h_slot(g)] = v[i];
   }
 }
 
 template <int T>
 __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__restrict__ w_down,
                                                             const uint8_t *__restrict__ ws, float *__restrict__ y,
-                                                            const int hidden, const int ffn) {
-  __shared__ Routing R;
+                                                            const int hidden, const int ffn, const int P) {
+  __shared__ Table R;
+  __shared__ float zbuf[kMaxPairs][kDnRows];
   extern __shared__ uint4 lds[];
-  {
-    const int *src = reinterpret_cast<const int *>(ws);
-    int *dst = reinterpret_cast<int *>(&R);
-    for (int i = threadIdx.x; i < (int)(sizeof(Routing) / 4); i += kThreads) dst[i] = src[i];
-  }
-  __syncthreads();
-  const int P = R.n_pairs, n_slots = R.n_slots;
-  const int gpr = ffn >> 2, nsub = ffn >> 5;
+  const int tid = threadIdx.x;
+  const int cpr = ffn >> 6;   // 64-value chunks per h row
+  const int nsub = ffn >> 5;
+  const int nblk = ffn >> 8;
   uint4 *hs = lds;
-  float *hsum = reinterpret_cast<float *>(lds + (size_t)P * gpr);
-  const float *h = reinterpret_cast<const float *>(ws + kTableBytes);
-  for (int p = 0; p < P; ++p)
-    stage_f32_row(h + (size_t)p * ffn, hs + p * gpr, hsum + p * nsub, gpr, nsub, threadIdx.x, kThreads);
+  float *hsum = reinterpret_cast<float *>(lds + (size_t)P * cpr * 17);
+
+  if (tid < kTableWords) reinterpret_cast<int *>(&R)[tid] = reinterpret_cast<const int *>(ws)[tid];
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
-  const int j = lane & (kLanesPerRow - 1);
-  const int n = (blockIdx.x * kWaves + (threadIdx.x >> 6)) * kRowsPerWave + lane / kLanesPerRow;
-  if (n >= hidden) return;
-  const int c = j & 3;
-  const ScaleSel sel = scale_selectors(c);
-  const int nblk = ffn >> 8;
+  // lane group grp (32 lanes: 8 rows x 4 chunks) takes distinct experts grp, grp + 8, ...
+  const int grp = tid >> 5;
+  const int c = tid & 3;
+  const int i_row = (tid & 31) >> 2;
+  const int n = blockIdx.x * kDnRows + i_row;
   const size_t row_bytes = (size_t)nblk * kQ4KBlockBytes;
   const size_t expert_bytes = (size_t)hidden * row_bytes;
-  const int nsteps = (nblk + 3) >> 2;
+  // rows past the matrix read row 0 (their results are never stored)
+  const uint8_t *wrow = w_down + (size_t)(n < hidden ? n : 0) * row_bytes + 32 * c;
+  const int n_slots = R.n_slots;
+  const int my_slots = n_slots > grp ? (n_slots - grp + kDnGroups - 1) / kDnGroups : 0;
+  const int U = my_slots * nblk;  // units (expert, block), expert-major
 
-  float acc_y[T];
+  uint4 wh[kDnDepth], wa[kDnDepth], wb[kDnDepth];
+  int ls = grp, lb = 0;  // next unit to load
 #pragma unroll
-  for (int r = 0; r < T; ++r) acc_y[r] = 0.0f;
-
-  constexpr int D = 4;  // distinct experts whose rows are loaded together
-  for (int s0 = 0; s0 < n_slots; s0 += D) {
-    float acc_z[D][T];
-#pragma unroll
-    for (int u = 0; u < D; ++u)
-#pragma unroll
-      for (int r = 0; r < T; ++r) acc_z[u][r] = 0.0f;
-    for (int st = 0; st < nsteps; ++st) {
-      const int b = st * 4 + (j >> 2);
-      uint4 hh[D], qa[D], qb[D];
-      bool ok[D];
-#pragma unroll
-      for (int u = 0; u < D; ++u) {
-        ok[u] = (s0 + u < n_slots) && b < nblk;
-        if (ok[u]) {
-          const uint8_t *bp = w_down + (size_t)R.slot_expert[s0 + u] * expert_bytes + (size_t)n * row_bytes +
-                              (size_t)b * kQ4KBlockBytes;
-          hh[u] = *reinterpret_cast<const uint4 *>(bp);
-          qa[u] = *reinterpret_cast<const uint4 *>(bp + 16 + 32 * c);
-          qb[u] = *reinterpret_cast<const uint4 *>(bp + 32 + 32 * c);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < D; ++u)
-        if (ok[u]) {
-          const int p0 = R.slot_pair0[s0 + u];
-          q4k_chunk_f32<T>(acc_z[u], R.slot_ntok[s0 + u], hh[u], qa[u], qb[u], st * 16 + j, sel, hs + p0 * gpr,
-                           hsum + p0 * nsub, gpr, nsub);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-      if (s0 + u >= n_slots) break;
-      const int p0 = R.slot_pair0[s0 + u], ntok = R.slot_ntok[s0 + u];
-#pragma unroll
-      for (int r = 0; r < T; ++r) {
-        if (r >= ntok) break;
-        const float z = row16_sum(acc_z[u][r]);
-        const int t = R.pair_token[p0 + r];
-        const float wgt = R.pair_weight[p0 + r];
-#pragma unroll
-        for (int tt = 0; tt < T; ++tt)
-          if (tt == t) acc_y[tt] = __builtin_fmaf(wgt, z, acc_y[tt]);
+  for (int u = 0; u < kDnDepth; ++u) {
+    if (u < U) {
+      const uint8_t *bp = wrow + (size_t)R.slot_expert[ls] * expert_bytes + (size_t)lb * kQ4KBlockBytes;
+      wh[u] = *reinterpret_cast<const uint4 *>(bp - 32 * c);
+      wa[u] = *reinterpret_cast<const uint4 *>(bp + 16);
+      wb[u] = *reinterpret_cast<const uint4 *>(bp + 32);
+      if (++lb == nblk) {
+        lb = 0;
+        ls += kDnGroups;
       }
     }
   }
+
+  // every pair's h (P = T*K pairs), two batches per round trip
+  const uint4 *hg = reinterpret_cast<const uint4 *>(ws + kTableBytes);
+  const int total = P * (ffn >> 2);
+  for (int base = 0; base < total; base += 2 * kHBatch * kThreads) {
+    uint4 hb0[kHBatch], hb1[kHBatch];
+    load_h_batch(hg, base, total, hb0);
+    load_h_batch(hg, base + kHBatch * kThreads, total, hb1);
+    store_h_batch(hs, base, total, hb0);
+    store_h_batch(hs, base + kHBatch * kThreads, total, hb1);
+  }
+  __syncthreads();
+  // sub-block sums (32 values each, index order); sub-block t is half t & 1 of chunk t >> 1
+  for (int t = tid; t < P * nsub; t += kThreads) {
+    const uint4 *src = hs + (t >> 1) * 17 + (t & 1) * 8;
+    float s = 0.0f;
 #pragma unroll
-  for (int tt = 0; tt < T; ++tt)
-    if (j == tt) y[(size_t)tt * hidden + n] = acc_y[tt];
+    for (int q = 0; q < 8; ++q) {
+      const uint4 g = src[q];
+      s += __builtin_bit_cast(float, g.x);
+      s += __builtin_bit_cast(float, g.y);
+      s += __builtin_bit_cast(float, g.z);
+      s += __builtin_bit_cast(float, g.w);
+    }
+    hsum[t] = s;
+  }
+  __syncthreads();
+
+  const ScaleSel sel = scale_selectors(c);
+  const int stride = cpr * 17;
+  float acc[T];
+#pragma unroll
+  for (int r = 0; r < T; ++r) acc[r] = 0.0f;
+  int cs_ = grp, cb = 0;  // unit being computed
+  for (int u0 = 0; u0 < U; u0 += kDnDepth) {
+#pragma unroll
+    for (int u = 0; u < kDnDepth; ++u) {
+      if (u0 + u < U) {
+        const int p0 = R.slot_pair0[cs_], ntok = R.slot_ntok[cs_];
+        const int ci = 4 * cb + c;
+        chunk_f32<T>(acc, ntok, wh[u], wa[u], wb[u], sel, hs + (p0 * cpr + ci) * 17, stride,
+                     hsum + p0 * nsub + 2 * ci, nsub);
+        if (u0 + u + kDnDepth < U) {
+          const uint8_t *bp = wrow + (size_t)R.slot_expert[ls] * expert_bytes + (size_t)lb * kQ4KBlockBytes;
+          wh[u] = *reinterpret_cast<const uint4 *>(bp - 32 * c);
+          wa[u] = *reinterpret_cast<const uint4 *>(bp + 16);
+          wb[u] = *reinterpret_cast<const uint4 *>(bp + 32);
+          if (++lb == nblk) {
+            lb = 0;
+            ls += kDnGroups;
+          }
+        }
+        if (++cb == nblk) {
+          // the expert's row is complete: one z per token, reduced over the row's four lanes (one quad)
+#pragma unroll
+          for (int r = 0; r < T; ++r) {
+            if (r >= ntok) break;
+            const float z = row4_sum(acc[r]);
+            if (c == r) zbuf[p0 + r][i_row] = z;
+            acc[r] = 0.0f;
+          }
+          cb = 0;
+          cs_ += kDnGroups;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // y[t][n] = sum over token t's experts in ascending id of weight * z
+  if (tid < T * kDnRows) {
+    const int t = tid / kDnRows, i = tid % kDnRows;
+    const int nn = blockIdx.x * kDnRows + i;
+    float out = 0.0f;
+    for (int p = 0; p < P; ++p)
+      if (R.pair_token[p] == t) out = __builtin_fmaf(R.pair_weight[p], zbuf[p][i], out);
+    if (nn < hidden) y[(size_t)t * hidden + nn] = out;
+  }
 }
 
-size_t gate_up_lds(int t, int hidden) { return (size_t)t * ((size_t)(hidden >> 3) * 16 + (size_t)(hidden >> 5) * 4); }
-size_t down_lds(int pairs, int ffn) { return (size_t)pairs * ((size_t)(ffn >> 2) * 16 + (size_t)(ffn >> 5) * 4); }
+size_t gate_up_lds(int t, int hidden) {
+  return (size_t)t * (padded_row_granules(hidden) * 16 + (size_t)(hidden >> 5) * 4);
+}
+size_t down_lds(int pairs, int ffn) {
+  return (size_t)pairs * ((size_t)(ffn >> 6) * 17 * 16 + (size_t)(ffn >> 5) * 4);
+}
 
 template <int T>
 int launch_t(const void *w_gate, const void *w_up, const void *w_down, const float *logits, const uint16_t *x,
@@ -345,13 +686,13 @@ int launch_t(const void *w_gate, const void *w_up, const void *w_down, const flo
       allow_dynamic_lds(reinterpret_cast<const void *>(&moe_down_kernel<T>), lds_b, granted_b, "moe_down_kernel lds"))
     return QMV_ERR_HIP;
   const int max_slots = n_experts < T * top_k ? n_experts : T * top_k;
-  const dim3 grid_a((unsigned)((ffn + kRowsPerGroup - 1) / kRowsPerGroup), (unsigned)max_slots);
+  const dim3 grid_a((unsigned)((ffn + kUpRows - 1) / kUpRows), (unsigned)max_slots);
   int rc = launch_kernel("moe_gate_up_kernel", moe_gate_up_kernel<T>, grid_a, dim3(kThreads), lds_a, s, w_gate, w_up,
                          logits, x, topk_ids, topk_w, pairs, ws, hidden, ffn, n_experts, top_k);
   if (rc) return rc;
-  const dim3 grid_b((unsigned)((hidden + kRowsPerGroup - 1) / kRowsPerGroup));
+  const dim3 grid_b((unsigned)((hidden + kDnRows - 1) / kDnRows));
   return launch_kernel("moe_down_kernel", moe_down_kernel<T>, grid_b, dim3(kThreads), lds_b, s, w_down, ws, y,
-                       hidden, ffn);
+                       hidden, ffn, T * top_k);
 }
 
 }  // namespace
@@ -363,7 +704,8 @@ size_t moe_workspace_bytes(int t, int hidden, int ffn, int n_experts, int top_k)
 }
 
 bool moe_fits_lds(int t, int hidden, int ffn, int top_k) {
-  const size_t budget = (size_t)QMV_LDS_X_BYTES - sizeof(Routing);
+  // static LDS (routing scratch, tables, z buffer) stays under 4 KiB
+  const size_t budget = (size_t)QMV_LDS_X_BYTES - 4096;
   return gate_up_lds(t, hidden) <= budget && down_lds(t * top_k, ffn) <= budget;
 }
 
