@@ -22,13 +22,14 @@
 //     the workgroup's eight groups of 32 lanes share its 8 rows, group g taking
 //     the distinct experts g, g + 8, ...; their first (expert, block) weight
 //     loads are issued before every pair's h is staged in LDS. Each (pair, row)
-//     result z lands in LDS, and y_t = sum over token t's experts, in ascending
-//     expert id, of weight * z, accumulated with fma from zero.
+//     result z lands in LDS, and y_t = sum over token t's experts, in routing
+//     rank order (largest logit first), of weight * z, accumulated with fma
+//     from zero.
 //
 // Each selected expert's weights are read once per call. A token's result is
 // bit-identical whatever other tokens share the call: the arithmetic applied
 // to one (expert, token) pair does not depend on which lanes or waves run it,
-// and a token's experts are combined in the same ascending order.
+// and a token's experts are combined in its own rank order.
 #include <limits.h>
 
 #include "q4k_common.h"
@@ -62,6 +63,7 @@ struct Table {
   int slot_expert[kMaxPairs];  // distinct experts, ascending
   int slot_pair0[kMaxPairs];   // first gather-list position of each
   int slot_ntok[kMaxPairs];    // tokens that chose it
+  int rank_pair[kMaxPairs];    // gather-list position of routing pair t*K + j (token t, rank j)
 };
 constexpr size_t kTableBytes = 4096;
 static_assert(sizeof(Table) <= kTableBytes, "routing tables exceed their workspace slot");
@@ -166,6 +168,7 @@ __device__ __forceinline__ void route_token(const float *__restrict__ logits, co
 struct Pairs {
   int key;                   // expert * 4 + token of this lane's pair in routing order (INT_MAX past P)
   float wgt;                 // its routing weight
+  int rank;                  // gather-list position of this lane's pair
   int skey;                  // sorted order
   float sw;
   unsigned long long heads;  // sorted positions that start a new expert
@@ -187,6 +190,7 @@ __device__ __forceinline__ Pairs sort_pairs(const int (*sid)[kTopK], const float
   int rank = 0;
   for (int q = 0; q < P; ++q) rank += __builtin_amdgcn_readlane(s.key, q) < s.key;
   if (lane >= P) rank = lane;
+  s.rank = rank;
   s.skey = __builtin_amdgcn_ds_permute(rank * 4, s.key);
   s.sw = __builtin_bit_cast(float, __builtin_amdgcn_ds_permute(rank * 4, __builtin_bit_cast(int, s.wgt)));
   const int se = s.skey / QMV_MOE_MAX_TOKENS;
@@ -243,6 +247,7 @@ __device__ __forceinline__ void write_routing(const Pairs &s, const int P, int32
     tab->pair_expert[lane] = se;
     tab->pair_token[lane] = st;
     tab->pair_weight[lane] = s.sw;
+    tab->rank_pair[lane] = s.rank;
   }
   if ((s.heads >> lane) & 1ull) {
     const int slot = __popcll(s.heads & ((1ull << lane) - 1ull));
@@ -657,13 +662,16 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__res
   }
   __syncthreads();
 
-  // y[t][n] = sum over token t's experts in ascending id of weight * z
+  // y[t][n] = sum over token t's experts in routing rank order of weight * z
   if (tid < T * kDnRows) {
     const int t = tid / kDnRows, i = tid % kDnRows;
     const int nn = blockIdx.x * kDnRows + i;
+    const int K = P / T;
     float out = 0.0f;
-    for (int p = 0; p < P; ++p)
-      if (R.pair_token[p] == t) out = __builtin_fmaf(R.pair_weight[p], zbuf[p][i], out);
+    for (int j = 0; j < K; ++j) {
+      const int p = R.rank_pair[t * K + j];
+      out = __builtin_fmaf(R.pair_weight[p], zbuf[p][i], out);
+    }
     if (nn < hidden) y[(size_t)t * hidden + nn] = out;
   }
 }

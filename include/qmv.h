@@ -105,7 +105,8 @@ int qmv_q8_0(const void *w, size_t w_bytes, const float *x, float *y,
  *   x_bf16  bf16 bits [m][k] row-major, 16-byte aligned
  *   y       fp32 [m][n] row-major, 4-byte aligned
  *   1 <= m <= QMV_MAX_ROWS, n >= 1, k >= 256 and k % 256 == 0,
- *   m*k*2 + m*(k/32)*4 <= QMV_LDS_X_BYTES (m=4 allows k up to 19200).
+ *   m*((k/128)*272 + (k/32)*4) <= QMV_LDS_X_BYTES (the activations are staged
+ *   with one 16-byte pad per 128 values; m=4 allows k up to 18176).
  * y[r][i] = sum_k dequant(w)[i][k] * x[r][k] with the quants and bf16 inputs
  * exact and fp32 accumulation. Row r of y is bit-identical for every m.
  * Workload: the per-token weight stream of the memra README's dense Q4_K_M
@@ -136,6 +137,9 @@ size_t qmv_q4_k_moe_workspace(int t, int hidden, int ffn, int n_experts, int top
  *   ws, ws_bytes  workspace of at least qmv_q4_k_moe_workspace(...) bytes, 256-B aligned
  *   1 <= t <= QMV_MOE_MAX_TOKENS, 1 <= top_k <= min(QMV_MOE_MAX_TOP_K, n_experts),
  *   1 <= n_experts <= QMV_MOE_MAX_EXPERTS, hidden and ffn multiples of 256.
+ *   The staged activations and h must fit in LDS next to 4 KiB of tables:
+ *   t*((hidden/128)*272 + (hidden/32)*4) and t*top_k*((ffn/64)*272 + (ffn/32)*4)
+ *   bytes each <= QMV_LDS_X_BYTES - 4096, else QMV_ERR_RANGE.
  * Per token: the top_k largest logits (ties -> lower expert id) select experts
  * e_j; r_j = softmax over the selected logits; h = silu(W_gate x) * (W_up x) in
  * fp32; y = sum_j r_j * W_down[e_j] h, summed in rank order j. Each selected

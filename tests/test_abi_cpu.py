@@ -137,6 +137,8 @@ def test_moe_validation():
     assert moe(t=0) == RANGE and moe(t=5) == RANGE and moe(k=0) == RANGE and moe(k=9, e=16) == RANGE
     assert moe(k=4, e=3) == RANGE and moe(e=257) == RANGE
     assert moe(h=300) == SHAPE and moe(f=0) == SHAPE
+    assert moe(t=4, k=8, e=16, f=1280) == RANGE          # 32 pairs' h exceed the LDS stage
+    assert moe(t=4, h=18432) == RANGE                     # 4 tokens' activations exceed it
     assert moe(bank=8 * 256 * 144 - 1) == SIZE and moe(bank=8 * 256 * 144 + 144) == SIZE
     assert moe(wd=W + (2 << 28) + 8) == ALIGN and moe(ws=WS + 128) == ALIGN and moe(x=X + 2) == ALIGN
     assert moe(ws=0) == WORKSPACE and moe(ws_bytes=16) == WORKSPACE
