@@ -36,29 +36,59 @@ __host__ __device__ constexpr size_t dense_lds_bytes(int k) {
   return (size_t)M * padded_row_granules(k) * 16 + (size_t)M * (size_t)(k >> 5) * 4;
 }
 
-// Stage M activation rows (row r at x + r*K) in the padded layout, then each
-// row's K/32 sub-block sums from LDS (summed in index order). Ends with a barrier.
-template <int M, int kThreads>
-__device__ __forceinline__ void stage_dense(const uint16_t *__restrict__ x, uint4 *xs, float *xsum, const int gpr,
-                                            const int gpp, const int nsub) {
-  const uint4 *xg = reinterpret_cast<const uint4 *>(x);
-  const int total = M * gpr;
-  for (int base = 0; base < total; base += kThreads * 8) {
-    uint4 v[8];
+// Activation staging, in two parts so the weight loads can be issued in
+// between. Granule g of the M concatenated rows (row r = g / gpr) goes to LDS
+// slot r * gpp + padded_granule(g - r * gpr).
+template <int M>
+__device__ __forceinline__ void store_x_granule(uint4 *xs, const int g, const int gpr, const int gpp, const uint4 v) {
+  int r = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+  for (int q = 1; q < M; ++q) r += g >= q * gpr;
+  xs[r * gpp + padded_granule(g - r * gpr)] = v;
+}
+
+// Part 1: the first kXHead granules of this thread (g = tid + i * kThreads),
+// loaded into registers before any weight load is issued. Vector loads return
+// in issue order, so waiting for these never waits for the weights behind them.
+template <int kThreads, int kXHead>
+__device__ __forceinline__ void load_x_head(const uint4 *__restrict__ xg, const int total, uint4 (&v)[kXHead]) {
+#pragma unroll
+  for (int i = 0; i < kXHead; ++i) {
+    const int g = (int)threadIdx.x + i * kThreads;
+    if (g < total) v[i] = xg[g];
+  }
+}
+
+// Part 2: write the head to LDS (no barrier yet).
+template <int M, int kThreads, int kXHead>
+__device__ __forceinline__ void store_x_head(const uint4 (&v)[kXHead], uint4 *xs, const int gpr, const int gpp) {
+  const int total = M * gpr;
+#pragma unroll
+  for (int i = 0; i < kXHead; ++i) {
+    const int g = (int)threadIdx.x + i * kThreads;
+    if (g < total) store_x_granule<M>(xs, g, gpr, gpp, v[i]);
+  }
+}
+
+// Part 3: stage any granules beyond the head (rows longer than it covers), then
+// each row's K/32 sub-block sums from LDS, summed in index order. Ends with a
+// barrier.
+template <int M, int kThreads, int kXHead>
+__device__ __forceinline__ void finish_x_stage(const uint4 *__restrict__ xg, uint4 *xs, float *xsum, const int gpr,
+                                               const int gpp, const int nsub) {
+  const int total = M * gpr;
+  // (small batches: the weight ring is already in flight and holds its registers)
+  for (int base = kXHead * kThreads; base < total; base += kThreads * 2) {
+    uint4 t[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
       const int g = base + (int)threadIdx.x + i * kThreads;
-      v[i] = xg[g < total ? g : 0];
+      t[i] = xg[g < total ? g : 0];
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int g = base + (int)threadIdx.x + i * kThreads;
-      if (g < total) {
-        int r = 0;
-#pragma unroll
-        for (int q = 1; q < M; ++q) r += g >= q * gpr;
-        xs[r * gpp + padded_granule(g - r * gpr)] = v[i];
-      }
+      if (g < total) store_x_granule<M>(xs, g, gpr, gpp, t[i]);
     }
   }
   __syncthreads();
@@ -70,8 +100,8 @@ __device__ __forceinline__ void stage_dense(const uint16_t *__restrict__ x, uint
     float s = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint4 v = xs[r * gpp + padded_granule(4 * sb + q)];
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      const uint4 g = xs[r * gpp + padded_granule(4 * sb + q)];
+      const uint32_t wv[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         s += bf16_bits_to_f32(wv[e] & 0xFFFFu);
@@ -85,41 +115,44 @@ __device__ __forceinline__ void stage_dense(const uint16_t *__restrict__ x, uint
 
 // One 64-weight chunk against M activation rows: xc points at the chunk's first
 // granule in row 0 (its 8 granules are xc[0..7]), xsc at its two sub-block sums.
+// Quant words 2g, 2g+1 hold weights 8g..8g+7 of both sub-blocks; they are
+// converted right before the dot products that use them, so only 8 converted
+// pairs are live at a time. Each row keeps four dot2 chains (two per sub-block)
+// joined in a fixed order; the chain order does not depend on M.
 template <int M>
 __device__ __forceinline__ void dense_chunk(float (&acc)[M], const uint4 hdr, const uint4 qa, const uint4 qb,
                                             const ScaleSel &sel, const uint4 *__restrict__ xc, const int gpp,
                                             const float *__restrict__ xsc, const int nsub) {
-  const ChunkScales cs = chunk_scales(hdr, sel);
   const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-  bf16x2 lo[16], hi[16];
+  float s_lo0[M], s_lo1[M], s_hi0[M], s_hi1[M];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t l = qw[i] & 0x0F0F0F0Fu;
-    const uint32_t h = (qw[i] >> 4) & 0x0F0F0F0Fu;
-    lo[2 * i] = nibbles_to_bf16x2<false>(l);
-    lo[2 * i + 1] = nibbles_to_bf16x2<true>(l);
-    hi[2 * i] = nibbles_to_bf16x2<false>(h);
-    hi[2 * i + 1] = nibbles_to_bf16x2<true>(h);
+  for (int r = 0; r < M; ++r) s_lo0[r] = s_lo1[r] = s_hi0[r] = s_hi1[r] = 0.0f;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t l0 = qw[2 * g] & 0x0F0F0F0Fu, h0 = (qw[2 * g] >> 4) & 0x0F0F0F0Fu;
+    const uint32_t l1 = qw[2 * g + 1] & 0x0F0F0F0Fu, h1 = (qw[2 * g + 1] >> 4) & 0x0F0F0F0Fu;
+    const bf16x2 lo0 = nibbles_to_bf16x2<false>(l0), lo1 = nibbles_to_bf16x2<true>(l0);
+    const bf16x2 lo2 = nibbles_to_bf16x2<false>(l1), lo3 = nibbles_to_bf16x2<true>(l1);
+    const bf16x2 hi0 = nibbles_to_bf16x2<false>(h0), hi1 = nibbles_to_bf16x2<true>(h0);
+    const bf16x2 hi2 = nibbles_to_bf16x2<false>(h1), hi3 = nibbles_to_bf16x2<true>(h1);
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+      const uint4 v = xc[r * gpp + g];
+      const uint4 u = xc[r * gpp + 4 + g];
+      s_lo0[r] = __builtin_amdgcn_fdot2_f32_bf16(lo0, __builtin_bit_cast(bf16x2, v.x), s_lo0[r], false);
+      s_hi0[r] = __builtin_amdgcn_fdot2_f32_bf16(hi0, __builtin_bit_cast(bf16x2, u.x), s_hi0[r], false);
+      s_lo1[r] = __builtin_amdgcn_fdot2_f32_bf16(lo1, __builtin_bit_cast(bf16x2, v.y), s_lo1[r], false);
+      s_hi1[r] = __builtin_amdgcn_fdot2_f32_bf16(hi1, __builtin_bit_cast(bf16x2, u.y), s_hi1[r], false);
+      s_lo0[r] = __builtin_amdgcn_fdot2_f32_bf16(lo2, __builtin_bit_cast(bf16x2, v.z), s_lo0[r], false);
+      s_hi0[r] = __builtin_amdgcn_fdot2_f32_bf16(hi2, __builtin_bit_cast(bf16x2, u.z), s_hi0[r], false);
+      s_lo1[r] = __builtin_amdgcn_fdot2_f32_bf16(lo3, __builtin_bit_cast(bf16x2, v.w), s_lo1[r], false);
+      s_hi1[r] = __builtin_amdgcn_fdot2_f32_bf16(hi3, __builtin_bit_cast(bf16x2, u.w), s_hi1[r], false);
+    }
   }
+  const ChunkScales cs = chunk_scales(hdr, sel);
 #pragma unroll
   for (int r = 0; r < M; ++r) {
-    const uint4 *xr = xc + r * gpp;
-    // four independent dot2 chains (two per sub-block), joined in a fixed order
-    float s_lo0 = 0.0f, s_lo1 = 0.0f, s_hi0 = 0.0f, s_hi1 = 0.0f;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint4 v = xr[g];
-      const uint4 u = xr[4 + g];
-      s_lo0 = __builtin_amdgcn_fdot2_f32_bf16(lo[4 * g + 0], __builtin_bit_cast(bf16x2, v.x), s_lo0, false);
-      s_hi0 = __builtin_amdgcn_fdot2_f32_bf16(hi[4 * g + 0], __builtin_bit_cast(bf16x2, u.x), s_hi0, false);
-      s_lo1 = __builtin_amdgcn_fdot2_f32_bf16(lo[4 * g + 1], __builtin_bit_cast(bf16x2, v.y), s_lo1, false);
-      s_hi1 = __builtin_amdgcn_fdot2_f32_bf16(hi[4 * g + 1], __builtin_bit_cast(bf16x2, u.y), s_hi1, false);
-      s_lo0 = __builtin_amdgcn_fdot2_f32_bf16(lo[4 * g + 2], __builtin_bit_cast(bf16x2, v.z), s_lo0, false);
-      s_hi0 = __builtin_amdgcn_fdot2_f32_bf16(hi[4 * g + 2], __builtin_bit_cast(bf16x2, u.z), s_hi0, false);
-      s_lo1 = __builtin_amdgcn_fdot2_f32_bf16(lo[4 * g + 3], __builtin_bit_cast(bf16x2, v.w), s_lo1, false);
-      s_hi1 = __builtin_amdgcn_fdot2_f32_bf16(hi[4 * g + 3], __builtin_bit_cast(bf16x2, u.w), s_hi1, false);
-    }
-    const float s_lo = s_lo0 + s_lo1, s_hi = s_hi0 + s_hi1;
+    const float s_lo = s_lo0[r] + s_lo1[r], s_hi = s_hi0[r] + s_hi1[r];
     const float2 xsm = *reinterpret_cast<const float2 *>(xsc + r * nsub);
     acc[r] = __builtin_fmaf(cs.a0, s_lo, acc[r]);
     acc[r] = __builtin_fmaf(-cs.b0, xsm.x, acc[r]);
@@ -130,9 +163,18 @@ __device__ __forceinline__ void dense_chunk(float (&acc)[M], const uint4 hdr, co
 
 // G lanes own one output row (G = 16, 32 or 64): a step covers G/4 super-blocks
 // of the row, lane j holding chunk j % 4 of block j / 4. A wave owns 64/G rows.
-// The first D steps of weight loads are issued before the activations are
-// staged; afterwards a ring of D steps stays in flight. FULL: the row is a whole
-// number of steps, so no lane needs a block-range test.
+// Order of the prologue: the first kXHead activation granules per thread are
+// requested, then the first D steps of weights, then the activations are
+// written to LDS (and the sub-block sums formed) as soon as they arrive, while
+// the weights are still in flight; afterwards a ring of D steps stays in
+// flight. FULL: the row is a whole number of steps, so no lane needs a
+// block-range test.
+// kXHead: activation granules per thread loaded ahead of the weights -- enough
+// for the rows the launcher sends to each G (K <= 8192 with G = 16, K <= 18432
+// otherwise) at 256 threads, capped at 9 so the head never sets the register peak.
+template <int M, int G>
+constexpr int x_head() { return (G == 16 ? 4 * M : 9 * M) < 9 ? (G == 16 ? 4 * M : 9 * M) : 9; }
+
 template <int M, int G, int D, bool FULL, int kWaves>
 __global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__restrict__ w,
                                                             const uint16_t *__restrict__ x,
@@ -157,9 +199,17 @@ __global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__
   const int nsteps = (nblk + kBlocksPerStep - 1) / kBlocksPerStep;
   const uint8_t *wl = w + (size_t)(active ? row : 0) * (size_t)nblk * kQ4KBlockBytes + (size_t)jb * kQ4KBlockBytes;
 
+  const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+  constexpr int kXHead = x_head<M, G>();
+  uint4 xv[kXHead];
+  load_x_head<64 * kWaves, kXHead>(xg, M * gpr, xv);
+  // the first kD1 steps of weights go out behind the activation head; the head
+  // is written to LDS before the remaining D - kD1 steps are requested, so its
+  // registers are free again by the time the whole ring is in flight
+  constexpr int kD1 = D < 2 ? D : 2;
   uint4 hdr[D], qa[D], qb[D];
 #pragma unroll
-  for (int u = 0; u < D; ++u) {
+  for (int u = 0; u < kD1; ++u) {
     if (active && u < nsteps && (FULL || u * kBlocksPerStep + jb < nblk)) {
       const uint8_t *bp = wl + (size_t)(u * kBlocksPerStep) * kQ4KBlockBytes;
       hdr[u] = *reinterpret_cast<const uint4 *>(bp);
@@ -167,7 +217,17 @@ __global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__
       qb[u] = *reinterpret_cast<const uint4 *>(bp + 32 + 32 * c);
     }
   }
-  stage_dense<M, 64 * kWaves>(x, xs, xsum, gpr, gpp, nsub);
+  store_x_head<M, 64 * kWaves, kXHead>(xv, xs, gpr, gpp);
+#pragma unroll
+  for (int u = kD1; u < D; ++u) {
+    if (active && u < nsteps && (FULL || u * kBlocksPerStep + jb < nblk)) {
+      const uint8_t *bp = wl + (size_t)(u * kBlocksPerStep) * kQ4KBlockBytes;
+      hdr[u] = *reinterpret_cast<const uint4 *>(bp);
+      qa[u] = *reinterpret_cast<const uint4 *>(bp + 16 + 32 * c);
+      qb[u] = *reinterpret_cast<const uint4 *>(bp + 32 + 32 * c);
+    }
+  }
+  finish_x_stage<M, 64 * kWaves, kXHead>(xg, xs, xsum, gpr, gpp, nsub);
   if (!active) return;
 
   const ScaleSel sel = scale_selectors(c);
