@@ -55,7 +55,7 @@ __device__ __forceinline__ void load_x_head(const uint4 *__restrict__ xg, const 
 #pragma unroll
   for (int i = 0; i < kXHead; ++i) {
     const int g = (int)threadIdx.x + i * kThreads;
-    if (g < total) v[i] = xg[g];
+    v[i] = xg[g < total ? g : 0];  // unconditional, like the weight loads behind it
   }
 }
 
@@ -73,22 +73,24 @@ __device__ __forceinline__ void store_x_head(const uint4 (&v)[kXHead], uint4 *xs
 // Part 3: stage any granules beyond the head (rows longer than it covers), then
 // each row's K/32 sub-block sums from LDS, summed in index order. Ends with a
 // barrier.
-template <int M, int kThreads, int kXHead>
+template <int M, int kThreads, int kXHead, bool TAIL>
 __device__ __forceinline__ void finish_x_stage(const uint4 *__restrict__ xg, uint4 *xs, float *xsum, const int gpr,
                                                const int gpp, const int nsub) {
   const int total = M * gpr;
-  // (small batches: the weight ring is already in flight and holds its registers)
-  for (int base = kXHead * kThreads; base < total; base += kThreads * 2) {
-    uint4 t[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int g = base + (int)threadIdx.x + i * kThreads;
-      t[i] = xg[g < total ? g : 0];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int g = base + (int)threadIdx.x + i * kThreads;
-      if (g < total) store_x_granule<M>(xs, g, gpr, gpp, t[i]);
+  if constexpr (TAIL) {
+    // (small batches: the weight ring is already in flight and holds its registers)
+    for (int base = kXHead * kThreads; base < total; base += kThreads * 2) {
+      uint4 t[2];
+  #pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int g = base + (int)threadIdx.x + i * kThreads;
+        t[i] = xg[g < total ? g : 0];
+      }
+  #pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int g = base + (int)threadIdx.x + i * kThreads;
+        if (g < total) store_x_granule<M>(xs, g, gpr, gpp, t[i]);
+      }
     }
   }
   __syncthreads();
@@ -161,21 +163,50 @@ __device__ __forceinline__ void dense_chunk(float (&acc)[M], const uint4 hdr, co
   }
 }
 
-// G lanes own one output row (G = 16, 32 or 64): a step covers G/4 super-blocks
-// of the row, lane j holding chunk j % 4 of block j / 4. A wave owns 64/G rows.
-// Order of the prologue: the first kXHead activation granules per thread are
-// requested, then the first D steps of weights, then the activations are
-// written to LDS (and the sub-block sums formed) as soon as they arrive, while
-// the weights are still in flight; afterwards a ring of D steps stays in
-// flight. FULL: the row is a whole number of steps, so no lane needs a
-// block-range test.
+// The three 16-byte weight loads of one step for the lane holding chunk c of a
+// block at bp: the block header and the chunk's 32 quant bytes.
+__device__ __forceinline__ void load_step(const uint8_t *__restrict__ bp, const int c, uint4 &hdr, uint4 &qa,
+                                          uint4 &qb) {
+  hdr = *reinterpret_cast<const uint4 *>(bp);
+  qa = *reinterpret_cast<const uint4 *>(bp + 16 + 32 * c);
+  qb = *reinterpret_cast<const uint4 *>(bp + 32 + 32 * c);
+}
+
+// Block address of step t for this lane, or the matrix's first block when the
+// step does not exist for it (see the kernel); every address loaded stays
+// inside the weights.
+template <bool FULL, int kBlocksPerStep>
+__device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *w, const uint8_t *wl, const bool active, const int t,
+                                                   const int nsteps, const int jb, const int nblk) {
+  const bool ok = active && t < nsteps && (FULL || t * kBlocksPerStep + jb < nblk);
+  return ok ? wl + (size_t)(t * kBlocksPerStep) * kQ4KBlockBytes : w;
+}
+
+// G lanes own one output row (G = 16 or 32): a step covers G/4 super-blocks of
+// the row, lane j holding chunk j % 4 of block j / 4. A wave owns 64/G rows.
+//
+// Prologue order: the first kXHead activation granules per thread are
+// requested, then the first D steps of weights; the activations are written to
+// LDS (and the sub-block sums formed) as soon as they arrive, while the weights
+// are still in flight. Afterwards a ring of D steps stays in flight.
+//
+// Every weight load is issued unconditionally -- a step past the row, blocks
+// past a partial last step and rows past the matrix read the matrix's first
+// block instead and are never used -- so the number of loads in flight is known
+// at every point and each step waits only for its own ring slot.
+//
+// NS > 0: the row is exactly NS steps (the last one possibly partial) and the
+// step loop is unrolled, which keeps the ring in fixed registers and every wait
+// exact. NS == 0: rows of any length, runtime step loop (FULL: a whole number of
+// steps, so no lane needs a block-range test).
+//
 // kXHead: activation granules per thread loaded ahead of the weights -- enough
 // for the rows the launcher sends to each G (K <= 8192 with G = 16, K <= 18432
-// otherwise) at 256 threads, capped at 9 so the head never sets the register peak.
+// otherwise) at M = 1, capped at 9 so the head never sets the register peak.
 template <int M, int G>
 constexpr int x_head() { return (G == 16 ? 4 * M : 9 * M) < 9 ? (G == 16 ? 4 * M : 9 * M) : 9; }
 
-template <int M, int G, int D, bool FULL, int kWaves>
+template <int M, int G, int D, bool FULL, int NS, int kWaves>
 __global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__restrict__ w,
                                                             const uint16_t *__restrict__ x,
                                                             float *__restrict__ y, const int n, const int k) {
@@ -196,38 +227,32 @@ __global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__
   const int jb = j >> 2;
   const int row = (blockIdx.x * kWaves + (threadIdx.x >> 6)) * kRows + lane / G;
   const bool active = row < n;
-  const int nsteps = (nblk + kBlocksPerStep - 1) / kBlocksPerStep;
+  const int nsteps = NS > 0 ? NS : (nblk + kBlocksPerStep - 1) / kBlocksPerStep;
+  // with NS > 0 only the last step can be partial: lanes past its blocks skip it
+  const bool last_ok = jb < nblk - (nsteps - 1) * kBlocksPerStep;
   const uint8_t *wl = w + (size_t)(active ? row : 0) * (size_t)nblk * kQ4KBlockBytes + (size_t)jb * kQ4KBlockBytes;
 
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
   constexpr int kXHead = x_head<M, G>();
   uint4 xv[kXHead];
   load_x_head<64 * kWaves, kXHead>(xg, M * gpr, xv);
-  // the first kD1 steps of weights go out behind the activation head; the head
-  // is written to LDS before the remaining D - kD1 steps are requested, so its
-  // registers are free again by the time the whole ring is in flight
-  constexpr int kD1 = D < 2 ? D : 2;
+  // one step of weights goes out behind the activation head; the rest of the
+  // ring only after the head has arrived and is in LDS. Requests queue in the
+  // memory system in issue order, so every weight request issued before a
+  // wave's activations are back delays them (and with them its first step).
+  constexpr int kD1 = D < 1 ? D : 1;
   uint4 hdr[D], qa[D], qb[D];
 #pragma unroll
-  for (int u = 0; u < kD1; ++u) {
-    if (active && u < nsteps && (FULL || u * kBlocksPerStep + jb < nblk)) {
-      const uint8_t *bp = wl + (size_t)(u * kBlocksPerStep) * kQ4KBlockBytes;
-      hdr[u] = *reinterpret_cast<const uint4 *>(bp);
-      qa[u] = *reinterpret_cast<const uint4 *>(bp + 16 + 32 * c);
-      qb[u] = *reinterpret_cast<const uint4 *>(bp + 32 + 32 * c);
-    }
-  }
+  for (int u = 0; u < kD1; ++u)
+    load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
   store_x_head<M, 64 * kWaves, kXHead>(xv, xs, gpr, gpp);
 #pragma unroll
-  for (int u = kD1; u < D; ++u) {
-    if (active && u < nsteps && (FULL || u * kBlocksPerStep + jb < nblk)) {
-      const uint8_t *bp = wl + (size_t)(u * kBlocksPerStep) * kQ4KBlockBytes;
-      hdr[u] = *reinterpret_cast<const uint4 *>(bp);
-      qa[u] = *reinterpret_cast<const uint4 *>(bp + 16 + 32 * c);
-      qb[u] = *reinterpret_cast<const uint4 *>(bp + 32 + 32 * c);
-    }
-  }
-  finish_x_stage<M, 64 * kWaves, kXHead>(xg, xs, xsum, gpr, gpp, nsub);
+  for (int u = kD1; u < D; ++u)
+    load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
+  // rows up to NS steps are covered by the head when this holds, and the loop
+  // that stages the rest is compiled out
+  constexpr bool kTail = NS == 0 || M * NS * G * 8 > kXHead * 64 * kWaves;
+  finish_x_stage<M, 64 * kWaves, kXHead, kTail>(xg, xs, xsum, gpr, gpp, nsub);
   if (!active) return;
 
   const ScaleSel sel = scale_selectors(c);
@@ -237,18 +262,25 @@ __global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__
 #pragma unroll
   for (int r = 0; r < M; ++r) acc[r] = 0.0f;
 
-  for (int s0 = 0; s0 < nsteps; s0 += D) {
+  if constexpr (NS > 0) {
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int s = s0 + u;
-      if (s < nsteps && (FULL || s * kBlocksPerStep + jb < nblk))
+    for (int s = 0; s < NS; ++s) {
+      constexpr int kD = D;
+      const int u = s % kD;
+      if (s < NS - 1 || last_ok)
         dense_chunk<M>(acc, hdr[u], qa[u], qb[u], sel, xb + s * kStepGranules, gpp, sb + s * 2 * G, nsub);
-      const int sn = s + D;
-      if (sn < nsteps && (FULL || sn * kBlocksPerStep + jb < nblk)) {
-        const uint8_t *bp = wl + (size_t)(sn * kBlocksPerStep) * kQ4KBlockBytes;
-        hdr[u] = *reinterpret_cast<const uint4 *>(bp);
-        qa[u] = *reinterpret_cast<const uint4 *>(bp + 16 + 32 * c);
-        qb[u] = *reinterpret_cast<const uint4 *>(bp + 32 + 32 * c);
+      if (s + D < NS)
+        load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, s + D, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
+    }
+  } else {
+    for (int s0 = 0; s0 < nsteps; s0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const int s = s0 + u;
+        if (s < nsteps && (FULL || s * kBlocksPerStep + jb < nblk))
+          dense_chunk<M>(acc, hdr[u], qa[u], qb[u], sel, xb + s * kStepGranules, gpp, sb + s * 2 * G, nsub);
+        load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, s + D, nsteps, jb, nblk), c, hdr[u], qa[u],
+                  qb[u]);
       }
     }
   }
@@ -260,28 +292,53 @@ __global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__
   }
 }
 
-template <int M, int G, int D, int W>
-int launch_mgd(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
+constexpr int kWaves = 4;
+
+template <int M, int G, int D, bool FULL, int NS>
+int launch_cfg(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
   const size_t lds = dense_lds_bytes<M>(k);
-  const bool full = ((k >> 8) % (G / 4)) == 0;
-  const void *fn = full ? reinterpret_cast<const void *>(&q4k_gemv_kernel<M, G, D, true, W>)
-                        : reinterpret_cast<const void *>(&q4k_gemv_kernel<M, G, D, false, W>);
-  static std::atomic<size_t> granted_full{0}, granted_part{0};
-  if (allow_dynamic_lds(fn, lds, full ? granted_full : granted_part, "q4k_gemv_kernel lds")) return QMV_ERR_HIP;
-  const int rows_per_group = W * (64 / G);
+  auto *fn = q4k_gemv_kernel<M, G, D, FULL, NS, kWaves>;
+  static std::atomic<size_t> granted{0};
+  if (allow_dynamic_lds(reinterpret_cast<const void *>(fn), lds, granted, "q4k_gemv_kernel lds")) return QMV_ERR_HIP;
+  const int rows_per_group = kWaves * (64 / G);
   const unsigned grid = (unsigned)((n + rows_per_group - 1) / rows_per_group);
-  if (full)
-    return launch_kernel("q4k_gemv_kernel", q4k_gemv_kernel<M, G, D, true, W>, dim3(grid), dim3(64 * W), lds, stream,
-                         w, x, y, n, k);
-  return launch_kernel("q4k_gemv_kernel", q4k_gemv_kernel<M, G, D, false, W>, dim3(grid), dim3(64 * W), lds, stream,
-                       w, x, y, n, k);
+  return launch_kernel("q4k_gemv_kernel", fn, dim3(grid), dim3(64 * kWaves), lds, stream, w, x, y, n, k);
 }
 
-// Lanes per row and ring depth by row length.
+// Runtime-length rows (any K).
+template <int M, int G, int D>
+int launch_any(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
+  if (((k >> 8) % (G / 4)) == 0) return launch_cfg<M, G, D, true, 0>(w, x, y, n, k, stream);
+  return launch_cfg<M, G, D, false, 0>(w, x, y, n, k, stream);
+}
+
+// Lanes per row by row length: 16 up to K = 8192 (1..8 steps of 4 blocks), 32
+// beyond (steps of 8 blocks; 5..9 steps up to K = 18432, runtime loop after).
+// The ring is 4 steps deep.
 template <int M>
 int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
-  if (k <= 8192) return launch_mgd<M, 16, 4, 4>(w, x, y, n, k, stream);
-  return launch_mgd<M, 32, 4, 4>(w, x, y, n, k, stream);
+  constexpr int D = 4;
+  const int nblk = k >> 8;
+  if (k <= 8192) {
+    switch ((nblk + 3) / 4) {
+      case 1: return launch_cfg<M, 16, D, true, 1>(w, x, y, n, k, stream);
+      case 2: return launch_cfg<M, 16, D, true, 2>(w, x, y, n, k, stream);
+      case 3: return launch_cfg<M, 16, D, true, 3>(w, x, y, n, k, stream);
+      case 4: return launch_cfg<M, 16, D, true, 4>(w, x, y, n, k, stream);
+      case 5: return launch_cfg<M, 16, D, true, 5>(w, x, y, n, k, stream);
+      case 6: return launch_cfg<M, 16, D, true, 6>(w, x, y, n, k, stream);
+      case 7: return launch_cfg<M, 16, D, true, 7>(w, x, y, n, k, stream);
+      default: return launch_cfg<M, 16, D, true, 8>(w, x, y, n, k, stream);
+    }
+  }
+  switch ((nblk + 7) / 8) {
+    case 5: return launch_cfg<M, 32, D, true, 5>(w, x, y, n, k, stream);
+    case 6: return launch_cfg<M, 32, D, true, 6>(w, x, y, n, k, stream);
+    case 7: return launch_cfg<M, 32, D, true, 7>(w, x, y, n, k, stream);
+    case 8: return launch_cfg<M, 32, D, true, 8>(w, x, y, n, k, stream);
+    case 9: return launch_cfg<M, 32, D, true, 9>(w, x, y, n, k, stream);
+    default: return launch_any<M, 32, D>(w, x, y, n, k, stream);
+  }
 }
 
 }  // namespace
