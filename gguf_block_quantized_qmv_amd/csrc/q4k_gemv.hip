@@ -47,25 +47,27 @@ __device__ __forceinline__ void store_x_granule(uint4 *xs, const int g, const in
   xs[r * gpp + padded_granule(g - r * gpr)] = v;
 }
 
-// Part 1: the first kXHead granules of this thread (g = tid + i * kThreads),
+// Part 1: the first kXHead granules of this thread (g = tid + i * nthreads),
 // loaded into registers before any weight load is issued. Vector loads return
 // in issue order, so waiting for these never waits for the weights behind them.
-template <int kThreads, int kXHead>
-__device__ __forceinline__ void load_x_head(const uint4 *__restrict__ xg, const int total, uint4 (&v)[kXHead]) {
+template <int kXHead>
+__device__ __forceinline__ void load_x_head(const uint4 *__restrict__ xg, const int total, const int nthreads,
+                                            uint4 (&v)[kXHead]) {
 #pragma unroll
   for (int i = 0; i < kXHead; ++i) {
-    const int g = (int)threadIdx.x + i * kThreads;
+    const int g = (int)threadIdx.x + i * nthreads;
     v[i] = xg[g < total ? g : 0];  // unconditional, like the weight loads behind it
   }
 }
 
 // Part 2: write the head to LDS (no barrier yet).
-template <int M, int kThreads, int kXHead>
-__device__ __forceinline__ void store_x_head(const uint4 (&v)[kXHead], uint4 *xs, const int gpr, const int gpp) {
+template <int M, int kXHead>
+__device__ __forceinline__ void store_x_head(const uint4 (&v)[kXHead], uint4 *xs, const int gpr, const int gpp,
+                                             const int nthreads) {
   const int total = M * gpr;
 #pragma unroll
   for (int i = 0; i < kXHead; ++i) {
-    const int g = (int)threadIdx.x + i * kThreads;
+    const int g = (int)threadIdx.x + i * nthreads;
     if (g < total) store_x_granule<M>(xs, g, gpr, gpp, v[i]);
   }
 }
@@ -73,28 +75,28 @@ __device__ __forceinline__ void store_x_head(const uint4 (&v)[kXHead], uint4 *xs
 // Part 3: stage any granules beyond the head (rows longer than it covers), then
 // each row's K/32 sub-block sums from LDS, summed in index order. Ends with a
 // barrier.
-template <int M, int kThreads, int kXHead, bool TAIL>
+template <int M, int kXHead, bool TAIL>
 __device__ __forceinline__ void finish_x_stage(const uint4 *__restrict__ xg, uint4 *xs, float *xsum, const int gpr,
-                                               const int gpp, const int nsub) {
+                                               const int gpp, const int nsub, const int nthreads) {
   const int total = M * gpr;
   if constexpr (TAIL) {
     // (small batches: the weight ring is already in flight and holds its registers)
-    for (int base = kXHead * kThreads; base < total; base += kThreads * 2) {
+    for (int base = kXHead * nthreads; base < total; base += nthreads * 2) {
       uint4 t[2];
   #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int g = base + (int)threadIdx.x + i * kThreads;
+        const int g = base + (int)threadIdx.x + i * nthreads;
         t[i] = xg[g < total ? g : 0];
       }
   #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int g = base + (int)threadIdx.x + i * kThreads;
+        const int g = base + (int)threadIdx.x + i * nthreads;
         if (g < total) store_x_granule<M>(xs, g, gpr, gpp, t[i]);
       }
     }
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < M * nsub; t += kThreads) {
+  for (int t = threadIdx.x; t < M * nsub; t += nthreads) {
     int r = 0;
 #pragma unroll
     for (int q = 1; q < M; ++q) r += t >= q * nsub;
@@ -203,14 +205,17 @@ __device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *w, const uint8
 // kXHead: activation granules per thread loaded ahead of the weights -- enough
 // for the rows the launcher sends to each G (K <= 8192 with G = 16, K <= 18432
 // otherwise) at M = 1, capped at 9 so the head never sets the register peak.
+// Workgroups have kMinThreads..kMaxThreads threads (see pick_rows).
+constexpr int kMinThreads = 256;
+constexpr int kMaxThreads = 512;
+
 template <int M, int G>
 constexpr int x_head() { return (G == 16 ? 4 * M : 9 * M) < 9 ? (G == 16 ? 4 * M : 9 * M) : 9; }
 
-template <int M, int G, int D, bool FULL, int NS, int kWaves>
-__global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__restrict__ w,
+template <int M, int G, int D, bool FULL, int NS>
+__global__ __launch_bounds__(kMaxThreads) void q4k_gemv_kernel(const uint8_t *__restrict__ w,
                                                             const uint16_t *__restrict__ x,
                                                             float *__restrict__ y, const int n, const int k) {
-  constexpr int kRows = 64 / G;
   constexpr int kBlocksPerStep = G / 4;
   constexpr int kStepGranules = (G / 2) * 17;   // padded LDS granules per step
   extern __shared__ uint4 lds[];
@@ -225,7 +230,9 @@ __global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__
   const int j = lane & (G - 1);
   const int c = j & 3;
   const int jb = j >> 2;
-  const int row = (blockIdx.x * kWaves + (threadIdx.x >> 6)) * kRows + lane / G;
+  // blockDim.x = (rows per workgroup) * G; the last wave may be partial
+  const int nthreads = (int)blockDim.x;
+  const int row = blockIdx.x * (nthreads / G) + (int)threadIdx.x / G;
   const bool active = row < n;
   const int nsteps = NS > 0 ? NS : (nblk + kBlocksPerStep - 1) / kBlocksPerStep;
   // with NS > 0 only the last step can be partial: lanes past its blocks skip it
@@ -235,7 +242,7 @@ __global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
   constexpr int kXHead = x_head<M, G>();
   uint4 xv[kXHead];
-  load_x_head<64 * kWaves, kXHead>(xg, M * gpr, xv);
+  load_x_head<kXHead>(xg, M * gpr, nthreads, xv);
   // one step of weights goes out behind the activation head; the rest of the
   // ring only after the head has arrived and is in LDS. Requests queue in the
   // memory system in issue order, so every weight request issued before a
@@ -245,14 +252,14 @@ __global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__
 #pragma unroll
   for (int u = 0; u < kD1; ++u)
     load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
-  store_x_head<M, 64 * kWaves, kXHead>(xv, xs, gpr, gpp);
+  store_x_head<M, kXHead>(xv, xs, gpr, gpp, nthreads);
 #pragma unroll
   for (int u = kD1; u < D; ++u)
     load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
   // rows up to NS steps are covered by the head when this holds, and the loop
   // that stages the rest is compiled out
-  constexpr bool kTail = NS == 0 || M * NS * G * 8 > kXHead * 64 * kWaves;
-  finish_x_stage<M, 64 * kWaves, kXHead, kTail>(xg, xs, xsum, gpr, gpp, nsub);
+  constexpr bool kTail = NS == 0 || M * NS * G * 8 > kXHead * kMinThreads;
+  finish_x_stage<M, kXHead, kTail>(xg, xs, xsum, gpr, gpp, nsub, nthreads);
   if (!active) return;
 
   const ScaleSel sel = scale_selectors(c);
@@ -292,17 +299,35 @@ __global__ __launch_bounds__(64 * kWaves) void q4k_gemv_kernel(const uint8_t *__
   }
 }
 
-constexpr int kWaves = 4;
+// Rows per workgroup. A launch is balanced when every CU gets the same number
+// of rows: with N rows over 256 CUs, q workgroups of N / (256 q) rows each
+// (10 rows of 32 lanes for N = 5120). The workgroup must be whole waves with
+// 256..512 threads (a partial wave costs a full wave's issue slots), and q of
+// them must fit in LDS; otherwise (or for M > 1, whose register use varies)
+// 256 threads.
+inline int pick_rows(const int m, const int n, const int G, const size_t lds) {
+  const int dflt = kMinThreads / G;
+  if (m != 1 || n % 256 != 0) return dflt;
+  const int per_cu = n / 256;
+  for (int q = 1; q <= 8; ++q) {
+    if (per_cu % q != 0) continue;
+    const int threads = (per_cu / q) * G;
+    if (threads > kMaxThreads || threads % 64 != 0) continue;   // whole waves only
+    if (threads < kMinThreads || (size_t)q * lds > (size_t)QMV_LDS_X_BYTES) break;
+    return per_cu / q;
+  }
+  return dflt;
+}
 
 template <int M, int G, int D, bool FULL, int NS>
 int launch_cfg(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
   const size_t lds = dense_lds_bytes<M>(k);
-  auto *fn = q4k_gemv_kernel<M, G, D, FULL, NS, kWaves>;
+  auto *fn = q4k_gemv_kernel<M, G, D, FULL, NS>;
   static std::atomic<size_t> granted{0};
   if (allow_dynamic_lds(reinterpret_cast<const void *>(fn), lds, granted, "q4k_gemv_kernel lds")) return QMV_ERR_HIP;
-  const int rows_per_group = kWaves * (64 / G);
-  const unsigned grid = (unsigned)((n + rows_per_group - 1) / rows_per_group);
-  return launch_kernel("q4k_gemv_kernel", fn, dim3(grid), dim3(64 * kWaves), lds, stream, w, x, y, n, k);
+  const int rows = pick_rows(M, n, G, lds);
+  const unsigned grid = (unsigned)((n + rows - 1) / rows);
+  return launch_kernel("q4k_gemv_kernel", fn, dim3(grid), dim3(rows * G), lds, stream, w, x, y, n, k);
 }
 
 // Runtime-length rows (any K).
