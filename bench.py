@@ -27,6 +27,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+
+# HBM bytes per q4k_gemv_kernel launch at M=1 (mean over gate, up and down) from
+# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes (profiles/q4k_gemv_m1_hbm_traffic.md),
+# each scaled by what the same counter reads for a 4 GiB device copy in the same
+# run (FETCH_SIZE reads half the bytes copied, WRITE_SIZE all of them). The figure
+# describes the kernel sources hashed here and is reported as null once they change.
+GEMV_TRAFFIC = {
+    "sources": ("gguf_block_quantized_qmv_amd/csrc/q4k_gemv.hip", "gguf_block_quantized_qmv_amd/csrc/q4k_common.h",
+                "gguf_block_quantized_qmv_amd/csrc/qmv_device.h"),
+    "sha256": "58f995293430be36e4b60b7763893e96ac560aaaf997e6b14aaaadbfd2cdf8dc",
+    "bytes_per_launch": 51133919,
+}
+
+
+def gemv_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMV_TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return GEMV_TRAFFIC["bytes_per_launch"] if h.hexdigest() == GEMV_TRAFFIC["sha256"] else None
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "Q4_K GEMV achieved HBM GB/s (% of 8 TB/s peak) at M=1; MoE tok-equiv/s"
 SHAPES = (("gate", 17408, 5120), ("up", 17408, 5120), ("down", 5120, 17408))
@@ -176,10 +197,15 @@ def main():
     for i, (name, n, k) in enumerate(SHAPES):
         d = float(np.mean(dur[name]))
         per_shape[name] = {"us": d * 1e6, "GBps": (wbytes[i] + k * 2 + n * 4) / d / 1e9}
+    # roofline: the timed region is a pass over the pool made of this kernel only, so its
+    # average launch duration is the region's time over the launches in it (HIP events on
+    # the launch stream, back-to-back launches); the per-launch bracketing above adds the
+    # launch overhead of each isolated call and is reported separately
     launch_bytes = float(np.mean([wb + k * 2 + n * 4 for wb, (_, n, k) in zip(wbytes, SHAPES)]))
-    avg_dur = float(np.mean([np.mean(v) for v in dur.values()]))
+    avg_dur = best_t / (args.copies * len(SHAPES))
     achieved = launch_bytes / avg_dur / 1e9
     res["per_shape_m1"] = per_shape
+    res["isolated_launch_us_mean"] = float(np.mean([np.mean(v) for v in dur.values()])) * 1e6
     log(f"[bench] per-launch: " + ", ".join(f"{k} {v['us']:.2f} us {v['GBps']:.0f} GB/s" for k, v in per_shape.items()))
 
     # speculative verify: GB/s vs M
@@ -263,7 +289,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": gemv_traffic(),
+            "traffic_unit": "HBM bytes per launch",
             "avg_launch_us": round(avg_dur * 1e6, 3),
             "algorithmic_bytes_per_launch": launch_bytes,
         },
