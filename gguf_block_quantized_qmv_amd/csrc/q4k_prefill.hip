@@ -18,8 +18,6 @@
 // Every load is unconditional (steps past K reload the last step) and the step
 // loop is unrolled by kDepth, which divides the step count because K is a
 // multiple of 256, so each wait covers exactly the slot being consumed.
-// Workgroups (n, m) and (n, m + 1) are n_tiles apart in launch order, so with
-// n_tiles a multiple of 8 they run on the same XCD and share the W rows in its L2.
 //
 // Dequantization matches the bf16 dequant entry point bit for bit: each weight
 // is fma(d*sc, q, -(dmin*m)) (one rounding of the exact value to fp32), then
@@ -36,49 +34,67 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BK = 64;
 constexpr int kThreads = 256;
-constexpr int kDepth = 4;                    // steps of global loads in flight
-constexpr int kXGran = BM * 8;               // 16-byte granules of an X tile
-constexpr int kWGran = BN * 8;               // and of a W tile
-constexpr int kStageGran = kXGran + kWGran;
-constexpr size_t kLdsBytes = 2 * (size_t)kStageGran * 16;
-constexpr int kXPerThread = kXGran / kThreads;   // 4
 
-// Granule g (8 bf16 of K) of tile row r. A 16-byte LDS read serves 16 lanes per
-// cycle over 64 banks, i.e. 16 granule slots of a 256-byte line; 16 consecutive
-// rows read at one g land on 16 distinct slots because rows of equal parity get
-// distinct g ^ ((r >> 1) & 7).
-__device__ __forceinline__ int tslot(int r, int g) { return r * 8 + (g ^ ((r >> 1) & 7)); }
+// Tile shape: BM rows of X x BN rows of W per workgroup, four waves of
+// (BM / WM_WAVES) x (BN / WN_WAVES), DEPTH steps of global loads in flight.
+template <int BM_, int BN_, int DEPTH_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, kDepth = DEPTH_;
+  static constexpr int WN_WAVES = BN / 64, WM_WAVES = 4 / WN_WAVES;   // wave tile 64 x 64
+  static constexpr int kXGran = BM * 8, kWGran = BN * 8, kStageGran = kXGran + kWGran;
+  static constexpr size_t kLdsBytes = 2 * (size_t)kStageGran * 16;
+  static constexpr int kXPerThread = kXGran / kThreads;
+  static constexpr int kWThreadsPerRow = kThreads / BN;          // 2 or 4
+  static constexpr int kQBytes = 32 / kWThreadsPerRow;            // quant bytes per thread: 16 or 8
+  static_assert(WM_WAVES * 64 == BM && WN_WAVES * 64 == BN, "four 64x64 wave tiles");
+};
+
+// Granule g (8 bf16 of K) of tile row r, rotated by the row so that the MFMA
+// fragment reads (consecutive rows, one granule) and the tile writes spread
+// over the LDS banks (chosen by measurement among xor and rotate patterns; an
+// unswizzled tile runs 1.7x slower).
+__device__ __forceinline__ int tslot(int r, int g) { return r * 8 + ((g + r) & 7); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2v p = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, p);
 }
 
-// One step's global data for this thread: four X granules, and for W row
-// n0 + tid / 2 the block header and quant bytes 16 * (tid % 2) .. + 15 of chunk s % 4.
+// One step's global data for this thread: its X granules, and for W row
+// n0 + tid / kWThreadsPerRow the block header and kQBytes quant bytes of chunk s % 4.
+template <class C>
 struct StepRegs {
-  uint4 x[kXPerThread];
-  uint4 hdr, q;
+  uint4 x[C::kXPerThread];
+  uint4 hdr;
+  uint32_t q[C::kQBytes / 4];
 };
 
-// Rows past M read row 0 and rows past N row 0 of W (the caller zeroes their
+// Rows past M read row 0 and rows past N row 0 of W (the store zeroes their
 // contribution); steps past K read the last step.
+template <class C>
 __device__ __forceinline__ void load_step(const uint16_t *__restrict__ x, const uint8_t *__restrict__ w_rowp,
                                           const int m0, const int M, const int K, const int nsteps, int s,
-                                          StepRegs &r) {
+                                          StepRegs<C> &r) {
   s = s < nsteps ? s : nsteps - 1;
   const int k0 = s * BK;
 #pragma unroll
-  for (int i = 0; i < kXPerThread; ++i) {
+  for (int i = 0; i < C::kXPerThread; ++i) {
     const int g = (int)threadIdx.x + kThreads * i;
     const int row = m0 + (g >> 3);
     r.x[i] = reinterpret_cast<const uint4 *>(x + (size_t)(row < M ? row : 0) * K + k0)[g & 7];
   }
   const uint8_t *bp = w_rowp + (size_t)(s >> 2) * kQ4KBlockBytes;
   r.hdr = *reinterpret_cast<const uint4 *>(bp);
-  r.q = *reinterpret_cast<const uint4 *>(bp + 16 + 32 * (s & 3) + 16 * (threadIdx.x & 1));
+  const uint8_t *qp = bp + 16 + 32 * (s & 3) + C::kQBytes * (threadIdx.x % C::kWThreadsPerRow);
+  if constexpr (C::kQBytes == 16) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(qp);
+    r.q[0] = v.x; r.q[1] = v.y; r.q[2] = v.z; r.q[3] = v.w;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2 *>(qp);
+    r.q[0] = v.x; r.q[1] = v.y;
+  }
 }
 
 // Eight nibbles (the low or high nibbles of two quant words, already masked to
@@ -92,50 +108,82 @@ __device__ __forceinline__ void nibbles_f32(uint32_t b0, uint32_t b1, float (&f)
 }
 
 // Write a step into a stage: X granules as loaded (rows past M as zeros), the
-// W half-chunk dequantized to bf16 (rows past N as zeros).
+// W part-chunk dequantized to bf16 (rows past N as zeros).
+template <class C>
 __device__ __forceinline__ void store_step(uint4 *__restrict__ xt, uint4 *__restrict__ wt, const int s,
-                                           const StepRegs &r, const int m0, const int M, const bool w_ok) {
+                                           const StepRegs<C> &r, const int m0, const int M, const bool w_ok) {
 #pragma unroll
-  for (int i = 0; i < kXPerThread; ++i) {
+  for (int i = 0; i < C::kXPerThread; ++i) {
     const int g = (int)threadIdx.x + kThreads * i;
-    xt[tslot(g >> 3, g & 7)] = m0 + (g >> 3) < M ? r.x[i] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t keep = m0 + (g >> 3) < M ? 0xFFFFFFFFu : 0u;   // a mask, not a branch
+    xt[tslot(g >> 3, g & 7)] = make_uint4(r.x[i].x & keep, r.x[i].y & keep, r.x[i].z & keep, r.x[i].w & keep);
   }
-  const uint4 hdr = w_ok ? r.hdr : make_uint4(0u, 0u, 0u, 0u);   // d = dmin = 0: zero weights
+  const uint32_t wkeep = w_ok ? 0xFFFFFFFFu : 0u;   // d = dmin = 0: zero weights
+  const uint4 hdr = make_uint4(r.hdr.x & wkeep, r.hdr.y & wkeep, r.hdr.z & wkeep, r.hdr.w & wkeep);
   const ChunkScales cs = chunk_scales(hdr, scale_selectors(s & 3));
-  const uint32_t qw[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
-  uint32_t pl[8], ph[8];
+  constexpr int kPairs = C::kQBytes / 8;   // word pairs: 8 low and 8 high weights each
+  uint32_t pl[4 * kPairs], ph[4 * kPairs];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kPairs; ++h) {
     float lo[8], hi[8];
-    nibbles_f32(qw[2 * h] & 0x0F0F0F0Fu, qw[2 * h + 1] & 0x0F0F0F0Fu, lo);
-    nibbles_f32((qw[2 * h] >> 4) & 0x0F0F0F0Fu, (qw[2 * h + 1] >> 4) & 0x0F0F0F0Fu, hi);
+    nibbles_f32(r.q[2 * h] & 0x0F0F0F0Fu, r.q[2 * h + 1] & 0x0F0F0F0Fu, lo);
+    nibbles_f32((r.q[2 * h] >> 4) & 0x0F0F0F0Fu, (r.q[2 * h + 1] >> 4) & 0x0F0F0F0Fu, hi);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       pl[4 * h + e] = pack_bf16x2(__builtin_fmaf(cs.a0, lo[2 * e], -cs.b0), __builtin_fmaf(cs.a0, lo[2 * e + 1], -cs.b0));
       ph[4 * h + e] = pack_bf16x2(__builtin_fmaf(cs.a1, hi[2 * e], -cs.b1), __builtin_fmaf(cs.a1, hi[2 * e + 1], -cs.b1));
     }
   }
-  // this thread's weights: local k 16 h2 .. +15 (sub-block 2c) and 32 + 16 h2 .. +15 (2c + 1)
-  const int row = threadIdx.x >> 1, h2 = threadIdx.x & 1;
-  wt[tslot(row, 2 * h2)] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-  wt[tslot(row, 2 * h2 + 1)] = make_uint4(pl[4], pl[5], pl[6], pl[7]);
-  wt[tslot(row, 4 + 2 * h2)] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-  wt[tslot(row, 5 + 2 * h2)] = make_uint4(ph[4], ph[5], ph[6], ph[7]);
+  // this thread's weights: local k p*kQBytes .. + kQBytes - 1 (sub-block 2c) and 32 + the same (2c + 1)
+  const int row = threadIdx.x / C::kWThreadsPerRow, p = threadIdx.x % C::kWThreadsPerRow;
+  constexpr int kG = C::kQBytes / 8;   // granules per sub-block part
+#pragma unroll
+  for (int h = 0; h < kG; ++h) {
+    wt[tslot(row, kG * p + h)] = make_uint4(pl[4 * h], pl[4 * h + 1], pl[4 * h + 2], pl[4 * h + 3]);
+    wt[tslot(row, 4 + kG * p + h)] = make_uint4(ph[4 * h], ph[4 * h + 1], ph[4 * h + 2], ph[4 * h + 3]);
+  }
 }
 
+// MFMA fragments of K slice kk (16 values) for a wave's 64 x 64 tile: lane l
+// supplies row l % 32 and K granule l / 32 of each 32 x 16 operand.
+__device__ __forceinline__ void read_frags(const uint4 *__restrict__ xt, const uint4 *__restrict__ wt, const int wm,
+                                           const int wn, const int kk, bf16x8 (&fa)[2], bf16x8 (&fb)[2]) {
+  const int lane = threadIdx.x & 63, frow = lane & 31, fg = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) fa[i] = __builtin_bit_cast(bf16x8, xt[tslot(wm + 32 * i + frow, 2 * kk + fg)]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fb[j] = __builtin_bit_cast(bf16x8, wt[tslot(wn + 32 * j + frow, 2 * kk + fg)]);
+}
+
+template <class C>
 __global__ __launch_bounds__(kThreads) void q4k_prefill_kernel(const uint8_t *__restrict__ w,
                                                                const uint16_t *__restrict__ x,
                                                                float *__restrict__ y, const int M, const int N,
                                                                const int K) {
+  constexpr int BM = C::BM, BN = C::BN, kDepth = C::kDepth;
   extern __shared__ uint4 lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  // Tile order. Workgroups are dealt to the 8 XCDs round robin by launch order;
+  // when the M tiles divide 8, XCD x works only on M tile x % m_tiles, so the X
+  // rows of a tile stay in that XCD's L2 for all its N tiles.
+  const int n_tiles = (N + BN - 1) / BN, m_tiles = (M + BM - 1) / BM;
+  int nt, mt;
+  if (8 % m_tiles == 0 && n_tiles % (8 / m_tiles) == 0) {
+    const int b = blockIdx.x, xcd = b & 7, per = 8 / m_tiles;
+    mt = xcd % m_tiles;
+    nt = (xcd / m_tiles) + per * (b >> 3);
+  } else {
+    nt = blockIdx.x % n_tiles;
+    mt = blockIdx.x / n_tiles;
+  }
+  const int n0 = nt * BN, m0 = mt * BM;
+  const int wm = (wave / C::WN_WAVES) * 64, wn = (wave % C::WN_WAVES) * 64;
   const int nblk = K >> 8;
-  const int nsteps = K / BK;   // a multiple of kDepth
+  const int nsteps = K / BK;   // a multiple of 4, so of kDepth in {2, 4}
 
-  const bool w_ok = n0 + (tid >> 1) < N;
-  const uint8_t *w_rowp = w + (size_t)(w_ok ? n0 + (tid >> 1) : 0) * (size_t)nblk * kQ4KBlockBytes;
+  const int w_row = tid / C::kWThreadsPerRow;
+  const bool w_ok = n0 + w_row < N;
+  const uint8_t *w_rowp = w + (size_t)(w_ok ? n0 + w_row : 0) * (size_t)nblk * kQ4KBlockBytes;
 
   floatx16 acc[2][2];
 #pragma unroll
@@ -145,42 +193,41 @@ __global__ __launch_bounds__(kThreads) void q4k_prefill_kernel(const uint8_t *__
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  StepRegs ring[kDepth];
+  StepRegs<C> ring[kDepth];
 #pragma unroll
-  for (int u = 0; u < kDepth; ++u) load_step(x, w_rowp, m0, M, K, nsteps, u, ring[u]);
-  store_step(lds, lds + kXGran, 0, ring[0], m0, M, w_ok);
-  load_step(x, w_rowp, m0, M, K, nsteps, kDepth, ring[0]);
+  for (int u = 0; u < kDepth; ++u) load_step<C>(x, w_rowp, m0, M, K, nsteps, u, ring[u]);
+  store_step<C>(lds, lds + C::kXGran, 0, ring[0], m0, M, w_ok);
+  load_step<C>(x, w_rowp, m0, M, K, nsteps, kDepth, ring[0]);
   __syncthreads();
 
-  // MFMA operands: lane l supplies row (l % 32) and K granule (l / 32) of a 32 x 16 slice
+  // The fragments of K slice kk + 1 are read while slice kk's MFMAs run, and
+  // slice 0 of the next stage right after the barrier.
   const int frow = lane & 31, fg = lane >> 5;
+  bf16x8 a[2][2], b[2][2];
+  read_frags(lds, lds + C::kXGran, wm, wn, 0, a[0], b[0]);
   for (int s0 = 0; s0 < nsteps; s0 += kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
       const int s = s0 + u;
-      const uint4 *xt = lds + (u & 1) * kStageGran;   // s & 1 == u & 1: kDepth is even
-      const uint4 *wt = xt + kXGran;
+      const uint4 *xt = lds + (u & 1) * C::kStageGran;   // s & 1 == u & 1: kDepth is even
+      const uint4 *wt = xt + C::kXGran;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 a[2], b[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = __builtin_bit_cast(bf16x8, xt[tslot(wm + 32 * i + frow, 2 * kk + fg)]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) b[j] = __builtin_bit_cast(bf16x8, wt[tslot(wn + 32 * j + frow, 2 * kk + fg)]);
+        if (kk < 3) read_frags(xt, wt, wm, wn, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
       }
       // step s + 1 into the other stage (past the last step this writes a copy
       // of the last step, which nobody reads), then its ring slot is refilled
-      constexpr int kD = kDepth;
-      const int un = (u + 1) % kD;
-      uint4 *nx = lds + ((u + 1) & 1) * kStageGran;
-      store_step(nx, nx + kXGran, s + 1, ring[un], m0, M, w_ok);
-      load_step(x, w_rowp, m0, M, K, nsteps, s + 1 + kDepth, ring[un]);
+      const int un = (u + 1) % kDepth;
+      uint4 *nx = lds + ((u + 1) & 1) * C::kStageGran;
+      store_step<C>(nx, nx + C::kXGran, s + 1, ring[un], m0, M, w_ok);
+      load_step<C>(x, w_rowp, m0, M, K, nsteps, s + 1 + kDepth, ring[un]);
       __syncthreads();
+      read_frags(nx, nx + C::kXGran, wm, wn, 0, a[0], b[0]);
     }
   }
 
@@ -202,16 +249,21 @@ __global__ __launch_bounds__(kThreads) void q4k_prefill_kernel(const uint8_t *__
     }
 }
 
+template <class C>
+int launch_cfg(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t stream) {
+  static std::atomic<size_t> granted{0};
+  if (allow_dynamic_lds(reinterpret_cast<const void *>(&q4k_prefill_kernel<C>), C::kLdsBytes, granted,
+                        "q4k_prefill_kernel lds"))
+    return QMV_ERR_HIP;
+  const dim3 grid((unsigned)(((n + C::BN - 1) / C::BN) * ((m + C::BM - 1) / C::BM)));
+  return launch_kernel("q4k_prefill_kernel", q4k_prefill_kernel<C>, grid, dim3(kThreads), C::kLdsBytes, stream, w,
+                       x, y, m, n, k);
+}
+
 }  // namespace
 
 int launch_q4_k_prefill(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream) {
-  static std::atomic<size_t> granted{0};
-  if (allow_dynamic_lds(reinterpret_cast<const void *>(&q4k_prefill_kernel), kLdsBytes, granted,
-                        "q4k_prefill_kernel lds"))
-    return QMV_ERR_HIP;
-  const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
-  return launch_kernel("q4k_prefill_kernel", q4k_prefill_kernel, grid, dim3(kThreads), kLdsBytes,
-                       static_cast<hipStream_t>(stream), w, x, y, m, n, k);
+  return launch_cfg<Cfg<128, 128, 4>>(w, x, y, m, n, k, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace qmv
