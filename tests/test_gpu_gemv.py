@@ -132,6 +132,53 @@ def test_q4_k_gemv_parity(q, dev, n, k, m):
     assert guards_intact(buf)
 
 
+# Row lengths that reach every unrolled step count of both lane widths (16 lanes:
+# 1..8 steps of 4 blocks, 32 lanes: 5..9 steps of 8 blocks, with and without a
+# partial last step) and the runtime-loop kernel beyond 18432 (whole and partial
+# last step); M = 1..4 as far as the activations fit in LDS.
+K_SWEEP = [2560, 3840, 6144, 7168, 8192, 8448, 10240, 12288, 14336, 16384, 18432, 19712, 20480, 36864]
+
+
+def _lds_fits(m, k):
+    return m * ((k // 128) * 272 + (k // 32) * 4) <= 163840
+
+
+@pytest.mark.parametrize("k", K_SWEEP)
+def test_q4_k_step_counts_parity_and_bit_identity(q, dev, k):
+    n = 23
+    raw = synth.q4_k_weights(800 + k // 256, n, k)
+    ms = [m for m in (1, 2, 3, 4) if _lds_fits(m, k)]
+    x = synth.bf16_normal(900 + k // 256, (max(ms), k))
+    wd = to_dev(raw, dev)
+    ref = oracle.qmv_q4_k(raw, x, n, k)
+    single = None
+    for m in ms:
+        y, buf = guarded((m, n), torch.float32, dev)
+        q.qmv_q4_k(wd, to_dev(x[:m], dev), n, k, y=y)
+        torch.cuda.synchronize()
+        got = host(y)
+        assert guards_intact(buf)
+        err = oracle.floored_rel_err(got, ref[:m])
+        assert err <= GEMV_TOL, (m, err)
+        if m == 1:
+            single = got[0]
+        else:
+            assert np.array_equal(got[0].view(np.uint32), single.view(np.uint32)), m
+
+
+@pytest.mark.parametrize("n,k", [(5120, 2048), (2560, 8448)])
+def test_q4_k_balanced_workgroups_parity(q, dev, n, k):
+    # row counts that divide evenly over the CUs take the balanced launch (20 rows of
+    # 16 lanes, 10 rows of 32 lanes per workgroup); rows must match the default launch
+    raw = synth.q4_k_weights(950, n, k)
+    x = synth.bf16_normal(951, (2, k))
+    wd = to_dev(raw, dev)
+    y1 = host(q.qmv_q4_k(wd, to_dev(x[:1], dev), n, k))
+    assert oracle.floored_rel_err(y1, oracle.qmv_q4_k(raw, x[:1], n, k)) <= GEMV_TOL
+    y2 = host(q.qmv_q4_k(wd, to_dev(x, dev), n, k))   # M = 2 uses 256-thread workgroups
+    assert np.array_equal(y1[0].view(np.uint32), y2[0].view(np.uint32))
+
+
 def test_q4_k_gemv_handbuilt_blocks(q, dev):
     # zero and subnormal scales, top-bit carries: one row per hand-built block
     raw, nb = _golden_q4k_matrix()
