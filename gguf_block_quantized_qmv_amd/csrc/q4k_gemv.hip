@@ -72,29 +72,31 @@ __device__ __forceinline__ void store_x_head(const uint4 (&v)[kXHead], uint4 *xs
   }
 }
 
-// Part 3: stage any granules beyond the head (rows longer than it covers), then
-// each row's K/32 sub-block sums from LDS, summed in index order. Ends with a
-// barrier.
-template <int M, int kXHead, bool TAIL>
-__device__ __forceinline__ void finish_x_stage(const uint4 *__restrict__ xg, uint4 *xs, float *xsum, const int gpr,
-                                               const int gpp, const int nsub, const int nthreads) {
+// Part 3: stage the granules beyond the head (rows longer than it covers), BATCH
+// per thread per round trip.
+template <int M, int kXHead, int BATCH>
+__device__ __forceinline__ void stage_x_tail(const uint4 *__restrict__ xg, uint4 *xs, const int gpr, const int gpp,
+                                             const int nthreads) {
   const int total = M * gpr;
-  if constexpr (TAIL) {
-    // (small batches: the weight ring is already in flight and holds its registers)
-    for (int base = kXHead * nthreads; base < total; base += nthreads * 2) {
-      uint4 t[2];
-  #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int g = base + (int)threadIdx.x + i * nthreads;
-        t[i] = xg[g < total ? g : 0];
-      }
-  #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int g = base + (int)threadIdx.x + i * nthreads;
-        if (g < total) store_x_granule<M>(xs, g, gpr, gpp, t[i]);
-      }
+  for (int base = kXHead * nthreads; base < total; base += nthreads * BATCH) {
+    uint4 t[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int g = base + (int)threadIdx.x + i * nthreads;
+      t[i] = xg[g < total ? g : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int g = base + (int)threadIdx.x + i * nthreads;
+      if (g < total) store_x_granule<M>(xs, g, gpr, gpp, t[i]);
     }
   }
+}
+
+// Part 4: after a barrier, each row's K/32 sub-block sums from LDS, summed in
+// index order. Ends with a barrier.
+template <int M>
+__device__ __forceinline__ void x_sums(const uint4 *xs, float *xsum, const int gpp, const int nsub, const int nthreads) {
   __syncthreads();
   for (int t = threadIdx.x; t < M * nsub; t += nthreads) {
     int r = 0;
@@ -207,13 +209,14 @@ __device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *w, const uint8
 // otherwise) at M = 1, capped at 9 so the head never sets the register peak.
 // Workgroups have kMinThreads..kMaxThreads threads (see pick_rows).
 constexpr int kMinThreads = 256;
-constexpr int kMaxThreads = 512;
+constexpr int kMaxThreads = 512;       // M = 1
+constexpr int kMaxThreadsRows = 768;   // M = 2..4: register use allows 3 waves per SIMD
 
 template <int M, int G>
 constexpr int x_head() { return (G == 16 ? 4 * M : 9 * M) < 9 ? (G == 16 ? 4 * M : 9 * M) : 9; }
 
 template <int M, int G, int D, bool FULL, int NS>
-__global__ __launch_bounds__(kMaxThreads) void q4k_gemv_kernel(const uint8_t *__restrict__ w,
+__global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q4k_gemv_kernel(const uint8_t *__restrict__ w,
                                                             const uint16_t *__restrict__ x,
                                                             float *__restrict__ y, const int n, const int k) {
   constexpr int kBlocksPerStep = G / 4;
@@ -243,23 +246,31 @@ __global__ __launch_bounds__(kMaxThreads) void q4k_gemv_kernel(const uint8_t *__
   constexpr int kXHead = x_head<M, G>();
   uint4 xv[kXHead];
   load_x_head<kXHead>(xg, M * gpr, nthreads, xv);
-  // one step of weights goes out behind the activation head; the rest of the
-  // ring only after the head has arrived and is in LDS. Requests queue in the
-  // memory system in issue order, so every weight request issued before a
-  // wave's activations are back delays them (and with them its first step).
-  constexpr int kD1 = D < 1 ? D : 1;
   uint4 hdr[D], qa[D], qb[D];
+  if constexpr (M == 1) {
+    // One step of weights goes out behind the activation head; the rest of the
+    // ring only after the head has arrived and is in LDS. Requests queue in the
+    // memory system in issue order, so every weight request issued before a
+    // wave's activations are back delays them (and with them its first step).
+    load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, 0, nsteps, jb, nblk), c, hdr[0], qa[0], qb[0]);
+    store_x_head<M, kXHead>(xv, xs, gpr, gpp, nthreads);
 #pragma unroll
-  for (int u = 0; u < kD1; ++u)
-    load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
-  store_x_head<M, kXHead>(xv, xs, gpr, gpp, nthreads);
+    for (int u = 1; u < D; ++u)
+      load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
+    // rows up to NS steps are covered by the head when this holds, and the
+    // loop that stages the rest is compiled out
+    if constexpr (NS == 0 || NS * G * 8 > kXHead * kMinThreads) stage_x_tail<M, kXHead, 2>(xg, xs, gpr, gpp, nthreads);
+  } else {
+    // Several rows fill most of the LDS and allow few workgroups per CU: all the
+    // activations are staged (eight granules per thread per round trip) before
+    // the first weight request, so no staging load waits behind the weights.
+    store_x_head<M, kXHead>(xv, xs, gpr, gpp, nthreads);
+    stage_x_tail<M, kXHead, 8>(xg, xs, gpr, gpp, nthreads);
 #pragma unroll
-  for (int u = kD1; u < D; ++u)
-    load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
-  // rows up to NS steps are covered by the head when this holds, and the loop
-  // that stages the rest is compiled out
-  constexpr bool kTail = NS == 0 || M * NS * G * 8 > kXHead * kMinThreads;
-  finish_x_stage<M, kXHead, kTail>(xg, xs, xsum, gpr, gpp, nsub, nthreads);
+    for (int u = 0; u < D; ++u)
+      load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
+  }
+  x_sums<M>(xs, xsum, gpp, nsub, nthreads);
   if (!active) return;
 
   const ScaleSel sel = scale_selectors(c);
@@ -301,18 +312,19 @@ __global__ __launch_bounds__(kMaxThreads) void q4k_gemv_kernel(const uint8_t *__
 
 // Rows per workgroup. A launch is balanced when every CU gets the same number
 // of rows: with N rows over 256 CUs, q workgroups of N / (256 q) rows each
-// (10 rows of 32 lanes for N = 5120). The workgroup must be whole waves with
-// 256..512 threads (a partial wave costs a full wave's issue slots), and q of
-// them must fit in LDS; otherwise (or for M > 1, whose register use varies)
-// 256 threads.
+// (10 rows of 32 lanes for N = 5120 at M = 1, 20 rows at M = 2..4 where the
+// activations fill the LDS). The workgroup must be whole waves with 256..512
+// threads (768 for M > 1; a partial wave costs a full wave's issue slots), and
+// q of them must fit in LDS; otherwise 256 threads.
 inline int pick_rows(const int m, const int n, const int G, const size_t lds) {
   const int dflt = kMinThreads / G;
-  if (m != 1 || n % 256 != 0) return dflt;
+  if (n % 256 != 0) return dflt;
+  const int max_threads = m == 1 ? kMaxThreads : kMaxThreadsRows;
   const int per_cu = n / 256;
   for (int q = 1; q <= 8; ++q) {
     if (per_cu % q != 0) continue;
     const int threads = (per_cu / q) * G;
-    if (threads > kMaxThreads || threads % 64 != 0) continue;   // whole waves only
+    if (threads > max_threads || threads % 64 != 0) continue;   // whole waves only
     if (threads < kMinThreads || (size_t)q * lds > (size_t)QMV_LDS_X_BYTES) break;
     return per_cu / q;
   }
