@@ -36,8 +36,8 @@ HBM_PEAK_GBPS = 8000.0
 GEMV_TRAFFIC = {
     "sources": ("gguf_block_quantized_qmv_amd/csrc/q4k_gemv.hip", "gguf_block_quantized_qmv_amd/csrc/q4k_common.h",
                 "gguf_block_quantized_qmv_amd/csrc/qmv_device.h"),
-    "sha256": "58f995293430be36e4b60b7763893e96ac560aaaf997e6b14aaaadbfd2cdf8dc",
-    "bytes_per_launch": 51133919,
+    "sha256": "03236d18d6f0c2ca6f9e311b7dad1c1768dec4ceb5a74d9761ac94b0b0703dec",
+    "bytes_per_launch": 51136543,
 }
 
 
