@@ -20,8 +20,9 @@
 //     16-row tile stores h = silu(W_gate x) * (W_up x) in fp32 per pair.
 //  2. moe_down_kernel, grid H/8 row tiles. Four lanes own one W_down row and
 //     the workgroup's eight groups of 32 lanes share its 8 rows, group g taking
-//     the distinct experts g, g + 8, ...; their first (expert, block) weight
-//     loads are issued before every pair's h is staged in LDS. Each (pair, row)
+//     the distinct experts g, g + 8, ...; the first h granules come with the
+//     routing tables, and the first (expert, block) weight loads are issued
+//     before the rest of every pair's h is staged in LDS. Each (pair, row)
 //     result z lands in LDS, and y_t = sum over token t's experts, in routing
 //     rank order (largest logit first), of weight * z, accumulated with fma
 //     from zero.
@@ -562,7 +563,19 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__res
   uint4 *hs = lds;
   float *hsum = reinterpret_cast<float *>(lds + (size_t)P * cpr * 17);
 
-  if (tid < kTableWords) reinterpret_cast<int *>(&R)[tid] = reinterpret_cast<const int *>(ws)[tid];
+  // The tables and the first h granules are requested together; that h batch is
+  // in LDS before the barrier (no register is carried across it).
+  const uint4 *hg = reinterpret_cast<const uint4 *>(ws + kTableBytes);
+  const int total = P * (ffn >> 2);
+  {
+    const int tword = reinterpret_cast<const int *>(ws)[tid < kTableWords ? tid : 0];
+    uint4 hb0[kHBatch], hb1[kHBatch];
+    load_h_batch(hg, 0, total, hb0);
+    load_h_batch(hg, kHBatch * kThreads, total, hb1);
+    store_h_batch(hs, 0, total, hb0);
+    store_h_batch(hs, kHBatch * kThreads, total, hb1);
+    if (tid < kTableWords) reinterpret_cast<int *>(&R)[tid] = tword;
+  }
   __syncthreads();
 
   // lane group grp (32 lanes: 8 rows x 4 chunks) takes distinct experts grp, grp + 8, ...
@@ -594,10 +607,8 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__res
     }
   }
 
-  // every pair's h (P = T*K pairs), two batches per round trip
-  const uint4 *hg = reinterpret_cast<const uint4 *>(ws + kTableBytes);
-  const int total = P * (ffn >> 2);
-  for (int base = 0; base < total; base += 2 * kHBatch * kThreads) {
+  // the rest of every pair's h (P = T*K pairs), two batches per round trip
+  for (int base = 2 * kHBatch * kThreads; base < total; base += 2 * kHBatch * kThreads) {
     uint4 hb0[kHBatch], hb1[kHBatch];
     load_h_batch(hg, base, total, hb0);
     load_h_batch(hg, base + kHBatch * kThreads, total, hb1);
