@@ -32,7 +32,8 @@ HBM_PEAK_GBPS = 8000.0
 # rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes (profiles/q4k_gemv_m1_hbm_traffic.md),
 # each scaled by what the same counter reads for a 4 GiB device copy in the same
 # run (FETCH_SIZE reads half the bytes copied, WRITE_SIZE all of them). The figure
-# describes the kernel sources hashed here and is reported as null once they change.
+# describes the kernel code hashed here (comments and whitespace excluded) and is
+# reported as null once it changes.
 GEMV_TRAFFIC = {
     "sources": ("gguf_block_quantized_qmv_amd/csrc/q4k_gemv.hip", "gguf_block_quantized_qmv_amd/csrc/q4k_common.h",
                 "gguf_block_quantized_qmv_amd/csrc/qmv_device.h"),
@@ -41,13 +42,22 @@ GEMV_TRAFFIC = {
 }
 
 
-def gemv_traffic():
+def gemv_sources_sha256():
+    """sha256 of the kernel's sources with comments and whitespace removed (code only)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in GEMV_TRAFFIC["sources"]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return GEMV_TRAFFIC["bytes_per_launch"] if h.hexdigest() == GEMV_TRAFFIC["sha256"] else None
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
+def gemv_traffic():
+    return GEMV_TRAFFIC["bytes_per_launch"] if gemv_sources_sha256() == GEMV_TRAFFIC["sha256"] else None
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "Q4_K GEMV achieved HBM GB/s (% of 8 TB/s peak) at M=1; MoE tok-equiv/s"
 SHAPES = (("gate", 17408, 5120), ("up", 17408, 5120), ("down", 5120, 17408))

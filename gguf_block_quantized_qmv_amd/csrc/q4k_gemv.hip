@@ -1,12 +1,14 @@
 // Q4_K matrix x bf16 activation rows (decode M=1, speculative verify M=2..4), gfx950.
 //
-// Work mapping. A group of 16 lanes (one DPP row) owns one output row; a wave
-// owns 4 rows and a 256-thread workgroup 16 rows. Lane j of a group reads, at
-// step s, 64-weight chunk c = j % 4 of super-block b = 4s + j / 4 of its row:
-// the 16-byte block header and the 32 quant bytes of that chunk, as 16-byte
-// loads (the four lanes of a block cover its 144 bytes). Rows of 5120 and 17408
-// weights are exactly 5 and 17 steps. The chunk fixes the lane's two sub-blocks
-// (2c, 2c+1), so each lane unpacks two scales and two mins per step.
+// Work mapping. A group of G lanes (16 for rows up to 8192 weights, 32 beyond)
+// owns one output row. Lane j of a group reads, at step s, 64-weight chunk
+// c = j % 4 of super-block b = (G/4) s + j / 4 of its row: the 16-byte block
+// header and the 32 quant bytes of that chunk, as 16-byte loads (the four lanes
+// of a block cover its 144 bytes). Rows of 5120 weights are 5 steps of 16 lanes,
+// rows of 17408 are 8.5 steps of 32 lanes. The chunk fixes the lane's two
+// sub-blocks (2c, 2c+1), so each lane unpacks two scales and two mins per step.
+// A workgroup is 256..512 threads (768 for M > 1) of whole rows, sized so that
+// every CU gets the same rows when the row count allows it.
 //
 // Arithmetic per chunk and activation row r:
 //   S_lo = sum q_i x_i over the 32 weights of sub-block 2c   (v_dot2 on exact bf16 q)
@@ -16,13 +18,14 @@
 // workgroup. The quants are converted exactly (q is an e4m3 value q*2^-9 scaled
 // by 2^9), products of q with bf16 x are exact in fp32, and accumulation is fp32.
 //
-// LDS holds only the activations: M rows of bf16 in swizzled 16-byte granules,
-// then the M x K/32 sub-block sums. Each row is reduced inside its 16-lane DPP
-// row; nothing crosses waves.
+// LDS holds only the activations: M rows of bf16 in a padded layout of 16-byte
+// granules, then the M x K/32 sub-block sums. Each row is reduced inside its
+// G-lane group (DPP, then cross-row shuffles for G = 32); nothing crosses waves.
 //
 // Batch invariance: the instruction sequence applied to activation row r does
-// not depend on M (every row runs the same unrolled body, explicit fma/dot
-// builtins, no reassociation), so row r is bit-identical for M = 1..4.
+// not depend on M or on the workgroup shape (every row runs the same unrolled
+// body, explicit fma/dot builtins, no reassociation), so row r is bit-identical
+// for M = 1..4.
 #include "q4k_common.h"
 #include "qmv_internal.h"
 #include "../../include/qmv.h"

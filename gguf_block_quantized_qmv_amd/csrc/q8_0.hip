@@ -20,6 +20,12 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kLanesPerRow = 32;
 constexpr int kRowsPerWave = 64 / kLanesPerRow;
 
+// LDS slot of fp32 granule g (4 activations) of a staged row: a 32-weight block
+// spans 8 granules, and granule i of block b sits at 8 b + (i ^ ((b >> 1) & 7)),
+// so the lanes of a row, which read granule i of consecutive blocks, spread over
+// eight slot positions (at most two lanes of a 16-lane read share a bank group).
+__device__ __forceinline__ int swizzle_granule(int g) { return g ^ ((g >> 4) & 7); }
+
 // Load Q8_0 block starting at byte offset `off` (even) from a dword-aligned base.
 // Returns d and the 32 quants as 8 little-endian words (q[4i..4i+3] in word i).
 __device__ __forceinline__ float load_q8_0_block(const uint8_t *__restrict__ base, size_t off, uint32_t (&q)[8]) {

@@ -85,13 +85,6 @@ __device__ __forceinline__ float group_sum(float v) {
   }
 }
 
-// Swizzled position of 16-byte granule g of a staged activation row (8 granules
-// = one 64-weight chunk of bf16). gfx950 serves a 16-byte LDS read for 16 lanes
-// per cycle across 64 banks; lanes that read the same granule of 16 consecutive
-// chunks land on 16 different bank groups when granule i of chunk c sits at
-// slot i ^ ((c >> 1) & 7).
-__device__ __forceinline__ int swizzle_granule(int g) { return g ^ ((g >> 4) & 7); }
-
 // Record a HIP failure for qmv_last_error() (thread-local text kept by the ABI layer).
 void set_error_detail(const char *what, int hip_code, const char *hip_text);
 
