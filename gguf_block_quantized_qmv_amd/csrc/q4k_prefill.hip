@@ -71,19 +71,20 @@ struct StepRegs {
   uint32_t q[C::kQBytes / 4];
 };
 
-// Rows past M read row 0 and rows past N row 0 of W (the store zeroes their
-// contribution); steps past K read the last step.
+// Rows past M read row 0 of X and rows past N row 0 of W: they only feed
+// outputs that are never stored. Steps past K read the last step. X granules
+// are addressed by 32-bit granule index (X is at most 2^31 granules: the
+// argument checks bound M * K).
 template <class C>
-__device__ __forceinline__ void load_step(const uint16_t *__restrict__ x, const uint8_t *__restrict__ w_rowp,
-                                          const int m0, const int M, const int K, const int nsteps, int s,
+__device__ __forceinline__ void load_step(const uint4 *__restrict__ xg, const int m0, const int M, const int gpr,
+                                          const uint8_t *__restrict__ w_rowp, const int nsteps, int s,
                                           StepRegs<C> &r) {
   s = s < nsteps ? s : nsteps - 1;
-  const int k0 = s * BK;
 #pragma unroll
   for (int i = 0; i < C::kXPerThread; ++i) {
     const int g = (int)threadIdx.x + kThreads * i;
     const int row = m0 + (g >> 3);
-    r.x[i] = reinterpret_cast<const uint4 *>(x + (size_t)(row < M ? row : 0) * K + k0)[g & 7];
+    r.x[i] = xg[(uint32_t)(row < M ? row : 0) * (uint32_t)gpr + (uint32_t)(s * 8 + (g & 7))];
   }
   const uint8_t *bp = w_rowp + (size_t)(s >> 2) * kQ4KBlockBytes;
   r.hdr = *reinterpret_cast<const uint4 *>(bp);
@@ -107,20 +108,17 @@ __device__ __forceinline__ void nibbles_f32(uint32_t b0, uint32_t b1, float (&f)
   f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y; f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
 }
 
-// Write a step into a stage: X granules as loaded (rows past M as zeros), the
-// W part-chunk dequantized to bf16 (rows past N as zeros).
+// Write a step into a stage: X granules as loaded, the W part-chunk dequantized to bf16.
 template <class C>
 __device__ __forceinline__ void store_step(uint4 *__restrict__ xt, uint4 *__restrict__ wt, const int s,
-                                           const StepRegs<C> &r, const int m0, const int M, const bool w_ok) {
+                                           const StepRegs<C> &r) {
 #pragma unroll
   for (int i = 0; i < C::kXPerThread; ++i) {
     const int g = (int)threadIdx.x + kThreads * i;
-    const uint32_t keep = m0 + (g >> 3) < M ? 0xFFFFFFFFu : 0u;   // a mask, not a branch
-    xt[tslot(g >> 3, g & 7)] = make_uint4(r.x[i].x & keep, r.x[i].y & keep, r.x[i].z & keep, r.x[i].w & keep);
+    const uint4 v = r.x[i];
+    xt[tslot(g >> 3, g & 7)] = make_uint4(v.x, v.y, v.z, v.w);   // element-wise: keeps the ring in registers
   }
-  const uint32_t wkeep = w_ok ? 0xFFFFFFFFu : 0u;   // d = dmin = 0: zero weights
-  const uint4 hdr = make_uint4(r.hdr.x & wkeep, r.hdr.y & wkeep, r.hdr.z & wkeep, r.hdr.w & wkeep);
-  const ChunkScales cs = chunk_scales(hdr, scale_selectors(s & 3));
+  const ChunkScales cs = chunk_scales(r.hdr, scale_selectors(s & 3));
   constexpr int kPairs = C::kQBytes / 8;   // word pairs: 8 low and 8 high weights each
   uint32_t pl[4 * kPairs], ph[4 * kPairs];
 #pragma unroll
@@ -182,8 +180,9 @@ __global__ __launch_bounds__(kThreads) void q4k_prefill_kernel(const uint8_t *__
   const int nsteps = K / BK;   // a multiple of 4, so of kDepth in {2, 4}
 
   const int w_row = tid / C::kWThreadsPerRow;
-  const bool w_ok = n0 + w_row < N;
-  const uint8_t *w_rowp = w + (size_t)(w_ok ? n0 + w_row : 0) * (size_t)nblk * kQ4KBlockBytes;
+  const uint8_t *w_rowp = w + (size_t)(n0 + w_row < N ? n0 + w_row : 0) * (size_t)nblk * kQ4KBlockBytes;
+  const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+  const int gpr = K >> 3;   // X granules per row
 
   floatx16 acc[2][2];
 #pragma unroll
@@ -195,9 +194,9 @@ __global__ __launch_bounds__(kThreads) void q4k_prefill_kernel(const uint8_t *__
 
   StepRegs<C> ring[kDepth];
 #pragma unroll
-  for (int u = 0; u < kDepth; ++u) load_step<C>(x, w_rowp, m0, M, K, nsteps, u, ring[u]);
-  store_step<C>(lds, lds + C::kXGran, 0, ring[0], m0, M, w_ok);
-  load_step<C>(x, w_rowp, m0, M, K, nsteps, kDepth, ring[0]);
+  for (int u = 0; u < kDepth; ++u) load_step<C>(xg, m0, M, gpr, w_rowp, nsteps, u, ring[u]);
+  store_step<C>(lds, lds + C::kXGran, 0, ring[0]);
+  load_step<C>(xg, m0, M, gpr, w_rowp, nsteps, kDepth, ring[0]);
   __syncthreads();
 
   // The fragments of K slice kk + 1 are read while slice kk's MFMAs run, and
@@ -224,8 +223,8 @@ __global__ __launch_bounds__(kThreads) void q4k_prefill_kernel(const uint8_t *__
       // of the last step, which nobody reads), then its ring slot is refilled
       const int un = (u + 1) % kDepth;
       uint4 *nx = lds + ((u + 1) & 1) * C::kStageGran;
-      store_step<C>(nx, nx + C::kXGran, s + 1, ring[un], m0, M, w_ok);
-      load_step<C>(x, w_rowp, m0, M, K, nsteps, s + 1 + kDepth, ring[un]);
+      store_step<C>(nx, nx + C::kXGran, s + 1, ring[un]);
+      load_step<C>(xg, m0, M, gpr, w_rowp, nsteps, s + 1 + kDepth, ring[un]);
       __syncthreads();
       read_frags(nx, nx + C::kXGran, wm, wn, 0, a[0], b[0]);
     }
