@@ -37,8 +37,8 @@ HBM_PEAK_GBPS = 8000.0
 GEMV_TRAFFIC = {
     "sources": ("gguf_block_quantized_qmv_amd/csrc/q4k_gemv.hip", "gguf_block_quantized_qmv_amd/csrc/q4k_common.h",
                 "gguf_block_quantized_qmv_amd/csrc/qmv_device.h"),
-    "sha256": "03236d18d6f0c2ca6f9e311b7dad1c1768dec4ceb5a74d9761ac94b0b0703dec",
-    "bytes_per_launch": 51136543,
+    "sha256": "8113dc3561110aeb437cd228536f9d7989c75b57a2554c7e8e33614b25f1ab14",
+    "bytes_per_launch": 51161335,
 }
 
 
