@@ -8,9 +8,10 @@
 // Two launches on the caller's stream, no host round trip:
 //
 //  1. moe_gate_up_kernel, grid (F/16 row tiles) x (max distinct experts).
-//     The activations of all T tokens start loading at once; meanwhile wave t
-//     routes token t (k rounds of a wave-wide argmax, ties to the lower id,
-//     then the softmax over the k chosen logits). Every wave then sorts the
+//     The activations of all T tokens and the router logits are requested at
+//     once; then wave t routes token t (k rounds of a wave-wide argmax, ties
+//     to the lower id, then the softmax over the k chosen logits; waves past T
+//     repeat token T-1's routing without storing it). Every wave then sorts the
 //     (expert, token) pairs in registers (rank by comparison, forward lane
 //     permute) and finds its workgroup's distinct expert, the s-th smallest,
 //     and the tokens that chose it, without another barrier. Workgroup (0, 0)
@@ -20,12 +21,12 @@
 //     16-row tile stores h = silu(W_gate x) * (W_up x) in fp32 per pair.
 //  2. moe_down_kernel, grid H/8 row tiles. Four lanes own one W_down row and
 //     the workgroup's eight groups of 32 lanes share its 8 rows, group g taking
-//     the distinct experts g, g + 8, ...; the first h granules come with the
-//     routing tables, and the first (expert, block) weight loads are issued
-//     before the rest of every pair's h is staged in LDS. Each (pair, row)
-//     result z lands in LDS, and y_t = sum over token t's experts, in routing
-//     rank order (largest logit first), of weight * z, accumulated with fma
-//     from zero.
+//     the distinct experts g, g + 8, ...; every pair's h is staged in LDS
+//     together with the routing tables, then the first (expert, block) weight
+//     loads go out and the h sub-block sums are formed while they arrive. Each
+//     (pair, row) result z lands in LDS, and y_t = sum over token t's experts,
+//     in routing rank order (largest logit first), of weight * z, accumulated
+//     with fma from zero.
 //
 // Each selected expert's weights are read once per call. A token's result is
 // bit-identical whatever other tokens share the call: the arithmetic applied
@@ -106,22 +107,36 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
   return max(max(r0, r1), max(r2, r3));
 }
 
-// One wave routes token t. Lane l holds experts l, l + 64, l + 128, l + 192.
-// Each of the k rounds takes the largest remaining logit (a wave-wide max of
-// the keys) and, among the experts holding it, the lowest id (the first
-// candidate slot i whose ballot is non-empty, lowest lane in it), then retires
-// that expert. The softmax over the chosen logits follows: exp(l_j - l_0)
-// summed in rank order, each divided by the sum. Writes sid[t][j], swt[t][j]
-// for j < K. Logits must be finite.
-__device__ __forceinline__ void route_token(const float *__restrict__ logits, const int t, const int E, const int K,
+// Token t's logits for lanes l, l + 64, l + 128, l + 192: four loads in flight
+// at once (clamped, never guarded).
+struct Logits {
+  float v[4];
+};
+__device__ __forceinline__ Logits load_logits(const float *__restrict__ logits, const int t, const int E) {
+  const int lane = threadIdx.x & 63;
+  Logits r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    r.v[i] = logits[(size_t)t * E + (e < E ? e : E - 1)];
+  }
+  return r;
+}
+
+// One wave routes token t from its logits. Lane l holds experts l, l + 64,
+// l + 128, l + 192. Each of the k rounds takes the largest remaining logit (a
+// wave-wide max of the keys) and, among the experts holding it, the lowest id
+// (the first candidate slot i whose ballot is non-empty, lowest lane in it),
+// then retires that expert. The softmax over the chosen logits follows:
+// exp(l_j - l_0) summed in rank order, each divided by the sum. Writes
+// sid[t][j], swt[t][j] for j < K when `write`; every wave routes, so that no
+// wave's logit loads wait inside a branch. Logits must be finite.
+__device__ __forceinline__ void route_token(const Logits &lg, const int t, const bool write, const int E, const int K,
                                             int (*sid)[kTopK], float (*swt)[kTopK]) {
   const int lane = threadIdx.x & 63;
   uint32_t kv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    kv[i] = e < E ? logit_key(logits[(size_t)t * E + e]) : 0u;
-  }
+  for (int i = 0; i < 4; ++i) kv[i] = lane + 64 * i < E ? logit_key(lg.v[i]) : 0u;
   // kept in registers: every loop below is fully unrolled with K tested inside
   uint32_t selk[kTopK];
   int seli[kTopK];
@@ -157,7 +172,7 @@ __device__ __forceinline__ void route_token(const float *__restrict__ logits, co
   }
 #pragma unroll
   for (int j = 0; j < kTopK; ++j)
-    if (j < K && lane == j) {
+    if (write && j < K && lane == j) {
       sid[t][j] = seli[j];
       swt[t][j] = ex[j] / sum;
     }
@@ -325,18 +340,20 @@ __device__ __forceinline__ void load_x_batch(const uint4 *__restrict__ xg, const
   }
 }
 
+// Lanes past the end hold granule 0 (their load was clamped) and store it to
+// granule 0's slot again: no store is guarded, so the compiler cannot sink a
+// load into a store's branch, where each load would wait before the next.
 template <int T>
 __device__ __forceinline__ void store_x_batch(uint4 *xs, const int base, const int total, const int gpr,
                                               const int gpp, const uint4 (&v)[kStageBatch]) {
 #pragma unroll
   for (int i = 0; i < kStageBatch; ++i) {
-    const int g = base + (int)threadIdx.x + i * kThreads;
-    if (g < total) {
-      int r = 0;
+    const int g0 = base + (int)threadIdx.x + i * kThreads;
+    const int g = g0 < total ? g0 : 0;
+    int r = 0;
 #pragma unroll
-      for (int q = 1; q < T; ++q) r += g >= q * gpr;
-      xs[r * gpp + padded_granule(g - r * gpr)] = v[i];
-    }
+    for (int q = 1; q < T; ++q) r += g >= q * gpr;
+    xs[r * gpp + padded_granule(g - r * gpr)] = v[i];
   }
 }
 
@@ -355,13 +372,15 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(
   uint4 *xs = lds;
   float *xsum = reinterpret_cast<float *>(lds + (size_t)T * gpp);
 
-  // every token's activations: the first batch is in flight while the router runs
+  // every token's activations and the router logits are requested together
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
   const int total = T * gpr;
   uint4 v[kStageBatch];
   load_x_batch<T>(xg, 0, total, v);
-  if (wave < T) route_token(logits, wave, E, K, sid, swt);
+  const int rt = wave < T ? wave : T - 1;
+  const Logits lg = load_logits(logits, rt, E);
   store_x_batch<T>(xs, 0, total, gpr, gpp, v);
+  route_token(lg, rt, wave < T, E, K, sid, swt);
   for (int base = kStageBatch * kThreads; base < total; base += kStageBatch * kThreads) {
     uint4 vb[kStageBatch];
     load_x_batch<T>(xg, base, total, vb);
@@ -540,12 +559,14 @@ __device__ __forceinline__ void load_h_batch(const uint4 *__restrict__ hg, const
   }
 }
 
+// Lanes past the end store their clamped load (granule 0) to granule 0's slot
+// (unguarded, as in store_x_batch).
 __device__ __forceinline__ void store_h_batch(uint4 *hs, const int base, const int total,
                                               const uint4 (&v)[kHBatch]) {
 #pragma unroll
   for (int i = 0; i < kHBatch; ++i) {
     const int g = base + (int)threadIdx.x + i * kThreads;
-    if (g < total) hs[h_slot(g)] = v[i];
+    hs[h_slot(g < total ? g : 0)] = v[i];
   }
 }
 
@@ -563,18 +584,21 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__res
   uint4 *hs = lds;
   float *hsum = reinterpret_cast<float *>(lds + (size_t)P * cpr * 17);
 
-  // The tables and the first h granules are requested together; that h batch is
-  // in LDS before the barrier (no register is carried across it).
+  // The tables and every pair's h are in LDS before the barrier, two h batches
+  // per round trip; no load is outstanding yet, so each round's waits are
+  // exact and its loads are all in flight together.
   const uint4 *hg = reinterpret_cast<const uint4 *>(ws + kTableBytes);
   const int total = P * (ffn >> 2);
   {
     const int tword = reinterpret_cast<const int *>(ws)[tid < kTableWords ? tid : 0];
-    uint4 hb0[kHBatch], hb1[kHBatch];
-    load_h_batch(hg, 0, total, hb0);
-    load_h_batch(hg, kHBatch * kThreads, total, hb1);
-    store_h_batch(hs, 0, total, hb0);
-    store_h_batch(hs, kHBatch * kThreads, total, hb1);
-    if (tid < kTableWords) reinterpret_cast<int *>(&R)[tid] = tword;
+    for (int base = 0; base < total; base += 2 * kHBatch * kThreads) {
+      uint4 hb0[kHBatch], hb1[kHBatch];
+      load_h_batch(hg, base, total, hb0);
+      load_h_batch(hg, base + kHBatch * kThreads, total, hb1);
+      store_h_batch(hs, base, total, hb0);
+      store_h_batch(hs, base + kHBatch * kThreads, total, hb1);
+    }
+    reinterpret_cast<int *>(&R)[tid < kTableWords ? tid : 0] = tword;  // lanes past the table rewrite word 0
   }
   __syncthreads();
 
@@ -607,15 +631,6 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__res
     }
   }
 
-  // the rest of every pair's h (P = T*K pairs), two batches per round trip
-  for (int base = 2 * kHBatch * kThreads; base < total; base += 2 * kHBatch * kThreads) {
-    uint4 hb0[kHBatch], hb1[kHBatch];
-    load_h_batch(hg, base, total, hb0);
-    load_h_batch(hg, base + kHBatch * kThreads, total, hb1);
-    store_h_batch(hs, base, total, hb0);
-    store_h_batch(hs, base + kHBatch * kThreads, total, hb1);
-  }
-  __syncthreads();
   // sub-block sums (32 values each, index order); sub-block t is half t & 1 of chunk t >> 1
   for (int t = tid; t < P * nsub; t += kThreads) {
     const uint4 *src = hs + (t >> 1) * 17 + (t & 1) * 8;
