@@ -385,8 +385,13 @@ def bench_prefill(args, torch, np, q, synth, timer, dev, sp, pool):
                 rc = L.qmm_q4_k_prefill(*a)
                 if rc:
                     raise q.QmvError(rc, "qmm_q4_k_prefill")
-        step()
-        tp = timer.run(step, 2) / copies
+        # matrix-core clocks settle only after sustained work: about 0.3 s of
+        # untimed passes before the timed ones
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            step()
+            torch.cuda.synchronize()
+        tp = timer.run(step, 5) / copies
         flops = 2.0 * m * n * k
         # dense bf16 torch GEMM of the same shape, as an achievable-rate reference
         a = torch.randn((m, k), device=dev, dtype=torch.bfloat16)

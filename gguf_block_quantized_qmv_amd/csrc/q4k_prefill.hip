@@ -6,18 +6,21 @@
 // are dequantized into bf16 tiles in LDS and fed to v_mfma_f32_32x32x16_bf16
 // with fp32 accumulation.
 //
-// Tiling. A 256-thread workgroup owns a 128 (rows of X) x 128 (rows of W) tile
-// of Y; each of its four waves owns a 64 x 64 quarter, four 32x32 MFMA tiles
-// (64 fp32 accumulators per lane). K advances 64 at a time -- one 64-weight
-// chunk of each W row's super-block -- through two LDS stages of 32 KiB (X tile
-// + W tile, rows of eight 16-byte granules, swizzled so that the 16 lanes a
-// 16-byte read serves per cycle hit 16 distinct bank groups). Global loads run
-// kDepth steps ahead through a ring of registers: while the matrix cores work
-// on stage s, step s + 1 (loaded kDepth - 1 steps earlier) is written into the
-// other stage, W dequantized, and the loads for step s + 1 + kDepth go out.
-// Every load is unconditional (steps past K reload the last step) and the step
-// loop is unrolled by kDepth, which divides the step count because K is a
-// multiple of 256, so each wait covers exactly the slot being consumed.
+// Tiling. A 512-thread workgroup owns a 128 (rows of X) x 128 (rows of W) tile
+// of Y. K advances 64 at a time -- one 64-weight chunk of each W row's
+// super-block -- through two LDS stages of 32 KiB (X tile + W tile, rows of
+// eight 16-byte granules, swizzled so that no 16-byte access conflicts on the
+// LDS banks). The waves split into two kinds. Four consumers each own a 64 x 64
+// quarter, four 32x32 MFMA tiles (64 fp32 accumulators per lane), and only read
+// fragments and issue matrix instructions. Four producers run kDepth steps of
+// global loads ahead through a ring of registers: while the consumers work on
+// stage s, the producers write step s + 1 (loaded kDepth - 1 steps earlier) into
+// the other stage, dequantizing W, and send the loads of step s + 1 + kDepth.
+// Each SIMD runs one wave of each kind, so the dequantization issues while the
+// other wave's matrix instructions execute. Every load is unconditional (steps
+// past K reload the last step) and the step loop is unrolled by kDepth, which
+// divides the step count because K is a multiple of 256, so each wait covers
+// exactly the slot being consumed.
 //
 // Dequantization matches the bf16 dequant entry point bit for bit: each weight
 // is fma(d*sc, q, -(dmin*m)) (one rounding of the exact value to fp32), then
@@ -37,8 +40,9 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 constexpr int BK = 64;
 constexpr int kThreads = 256;
 
-// Tile shape: BM rows of X x BN rows of W per workgroup, four waves of
-// (BM / WM_WAVES) x (BN / WN_WAVES), DEPTH steps of global loads in flight.
+// Tile shape: BM rows of X x BN rows of W per workgroup, four consumer waves of
+// (BM / WM_WAVES) x (BN / WN_WAVES), DEPTH steps of global loads in flight;
+// kThreads is the size of each kind's half of the workgroup.
 template <int BM_, int BN_, int DEPTH_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, kDepth = DEPTH_;
@@ -51,11 +55,23 @@ struct Cfg {
   static_assert(WM_WAVES * 64 == BM && WN_WAVES * 64 == BN, "four 64x64 wave tiles");
 };
 
-// Granule g (8 bf16 of K) of tile row r, rotated by the row so that the MFMA
-// fragment reads (consecutive rows, one granule) and the tile writes spread
-// over the LDS banks (chosen by measurement among xor and rotate patterns; an
-// unswizzled tile runs 1.7x slower).
-__device__ __forceinline__ int tslot(int r, int g) { return r * 8 + ((g + r) & 7); }
+// Granule g (8 bf16 of K) of tile row r sits at slot (g + f) & 7 of the row,
+// f being t = (r >> 1) & 7 with bits 1 and 2 swapped. LDS serves 16 lanes of a
+// 16-byte access per cycle from 16 bank groups (a group = 16 bytes; a row is
+// 8 groups, so rows of one parity share the same 8):
+//  * MFMA fragment reads (16 consecutive rows, one granule): the 8 rows of each
+//    parity take 8 distinct t, so 8 distinct f;
+//  * X tile writes (2 rows, all 8 granules each): distinct within a row;
+//  * W tile writes (8 rows, granules g and g + 2 from the two lanes of a row):
+//    the 4 rows of each parity take f in {0, 1, 4, 5} or {2, 3, 6, 7}, so f and
+//    f + 2 cover 8 distinct slots.
+// (A rotation by r alone put rows r and r + 8 on one group: a 2-way conflict
+// on every fragment read.)
+__device__ __forceinline__ int tslot(int r, int g) {
+  const int t = (r >> 1) & 7;
+  const int f = (t & 1) | ((t & 2) << 1) | ((t & 4) >> 1);
+  return r * 8 + ((g + f) & 7);
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2v p = {(__bf16)lo, (__bf16)hi};
@@ -76,19 +92,19 @@ struct StepRegs {
 // are addressed by 32-bit granule index (X is at most 2^31 granules: the
 // argument checks bound M * K).
 template <class C>
-__device__ __forceinline__ void load_step(const uint4 *__restrict__ xg, const int m0, const int M, const int gpr,
-                                          const uint8_t *__restrict__ w_rowp, const int nsteps, int s,
+__device__ __forceinline__ void load_step(const int pt, const uint4 *__restrict__ xg, const int m0, const int M,
+                                          const int gpr, const uint8_t *__restrict__ w_rowp, const int nsteps, int s,
                                           StepRegs<C> &r) {
   s = s < nsteps ? s : nsteps - 1;
 #pragma unroll
   for (int i = 0; i < C::kXPerThread; ++i) {
-    const int g = (int)threadIdx.x + kThreads * i;
+    const int g = pt + kThreads * i;
     const int row = m0 + (g >> 3);
     r.x[i] = xg[(uint32_t)(row < M ? row : 0) * (uint32_t)gpr + (uint32_t)(s * 8 + (g & 7))];
   }
   const uint8_t *bp = w_rowp + (size_t)(s >> 2) * kQ4KBlockBytes;
   r.hdr = *reinterpret_cast<const uint4 *>(bp);
-  const uint8_t *qp = bp + 16 + 32 * (s & 3) + C::kQBytes * (threadIdx.x % C::kWThreadsPerRow);
+  const uint8_t *qp = bp + 16 + 32 * (s & 3) + C::kQBytes * (pt % C::kWThreadsPerRow);
   if constexpr (C::kQBytes == 16) {
     const uint4 v = *reinterpret_cast<const uint4 *>(qp);
     r.q[0] = v.x; r.q[1] = v.y; r.q[2] = v.z; r.q[3] = v.w;
@@ -110,11 +126,11 @@ __device__ __forceinline__ void nibbles_f32(uint32_t b0, uint32_t b1, float (&f)
 
 // Write a step into a stage: X granules as loaded, the W part-chunk dequantized to bf16.
 template <class C>
-__device__ __forceinline__ void store_step(uint4 *__restrict__ xt, uint4 *__restrict__ wt, const int s,
+__device__ __forceinline__ void store_step(const int pt, uint4 *__restrict__ xt, uint4 *__restrict__ wt, const int s,
                                            const StepRegs<C> &r) {
 #pragma unroll
   for (int i = 0; i < C::kXPerThread; ++i) {
-    const int g = (int)threadIdx.x + kThreads * i;
+    const int g = pt + kThreads * i;
     const uint4 v = r.x[i];
     xt[tslot(g >> 3, g & 7)] = make_uint4(v.x, v.y, v.z, v.w);   // element-wise: keeps the ring in registers
   }
@@ -133,7 +149,7 @@ __device__ __forceinline__ void store_step(uint4 *__restrict__ xt, uint4 *__rest
     }
   }
   // this thread's weights: local k p*kQBytes .. + kQBytes - 1 (sub-block 2c) and 32 + the same (2c + 1)
-  const int row = threadIdx.x / C::kWThreadsPerRow, p = threadIdx.x % C::kWThreadsPerRow;
+  const int row = pt / C::kWThreadsPerRow, p = pt % C::kWThreadsPerRow;
   constexpr int kG = C::kQBytes / 8;   // granules per sub-block part
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
@@ -153,19 +169,11 @@ __device__ __forceinline__ void read_frags(const uint4 *__restrict__ xt, const u
   for (int j = 0; j < 2; ++j) fb[j] = __builtin_bit_cast(bf16x8, wt[tslot(wn + 32 * j + frow, 2 * kk + fg)]);
 }
 
-template <class C>
-__global__ __launch_bounds__(kThreads) void q4k_prefill_kernel(const uint8_t *__restrict__ w,
-                                                               const uint16_t *__restrict__ x,
-                                                               float *__restrict__ y, const int M, const int N,
-                                                               const int K) {
-  constexpr int BM = C::BM, BN = C::BN, kDepth = C::kDepth;
-  extern __shared__ uint4 lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Tile order. Workgroups are dealt to the 8 XCDs round robin by launch order;
-  // when the M tiles divide 8, XCD x works only on M tile x % m_tiles, so the X
-  // rows of a tile stay in that XCD's L2 for all its N tiles.
+// Tile (mt, nt) of the launch: when the M tiles divide 8, XCD x works only on
+// M tile x % m_tiles, so the X rows of a tile stay in that XCD's L2 for all
+// its N tiles (workgroups are dealt to the 8 XCDs round robin by launch order).
+__device__ __forceinline__ void tile_of(const int M, const int N, const int BM, const int BN, int &mt, int &nt) {
   const int n_tiles = (N + BN - 1) / BN, m_tiles = (M + BM - 1) / BM;
-  int nt, mt;
   if (8 % m_tiles == 0 && n_tiles % (8 / m_tiles) == 0) {
     const int b = blockIdx.x, xcd = b & 7, per = 8 / m_tiles;
     mt = xcd % m_tiles;
@@ -174,16 +182,58 @@ __global__ __launch_bounds__(kThreads) void q4k_prefill_kernel(const uint8_t *__
     nt = blockIdx.x % n_tiles;
     mt = blockIdx.x / n_tiles;
   }
+}
+
+// Wave-specialised form: eight waves per workgroup. Waves 4..7 produce -- they
+// load X and the Q4_K blocks kDepth steps ahead, dequantize W and write the
+// next LDS stage -- while waves 0..3 consume the current stage with MFMAs (a
+// 64 x 64 quarter each). Each SIMD runs one wave of each kind, so the
+// dequantization VALU work issues while the other wave's matrix instructions
+// execute. One barrier per step hands a stage from the producers to the
+// consumers and back; both kinds pass the same number of barriers.
+template <class C>
+__global__ __launch_bounds__(2 * kThreads) void q4k_prefill_ws_kernel(const uint8_t *__restrict__ w,
+                                                                      const uint16_t *__restrict__ x,
+                                                                      float *__restrict__ y, const int M,
+                                                                      const int N, const int K) {
+  constexpr int BM = C::BM, BN = C::BN, kDepth = C::kDepth;
+  extern __shared__ uint4 lds[];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int mt, nt;
+  tile_of(M, N, BM, BN, mt, nt);
   const int n0 = nt * BN, m0 = mt * BM;
-  const int wm = (wave / C::WN_WAVES) * 64, wn = (wave % C::WN_WAVES) * 64;
-  const int nblk = K >> 8;
   const int nsteps = K / BK;   // a multiple of 4, so of kDepth in {2, 4}
 
-  const int w_row = tid / C::kWThreadsPerRow;
-  const uint8_t *w_rowp = w + (size_t)(n0 + w_row < N ? n0 + w_row : 0) * (size_t)nblk * kQ4KBlockBytes;
-  const uint4 *xg = reinterpret_cast<const uint4 *>(x);
-  const int gpr = K >> 3;   // X granules per row
+  if (wave >= 4) {
+    const int pt = tid - kThreads;
+    const int nblk = K >> 8;
+    const int w_row = pt / C::kWThreadsPerRow;
+    const uint8_t *w_rowp = w + (size_t)(n0 + w_row < N ? n0 + w_row : 0) * (size_t)nblk * kQ4KBlockBytes;
+    const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+    const int gpr = K >> 3;
+    StepRegs<C> ring[kDepth];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) load_step<C>(pt, xg, m0, M, gpr, w_rowp, nsteps, u, ring[u]);
+    store_step<C>(pt, lds, lds + C::kXGran, 0, ring[0]);
+    load_step<C>(pt, xg, m0, M, gpr, w_rowp, nsteps, kDepth, ring[0]);
+    __syncthreads();
+    for (int s0 = 0; s0 < nsteps; s0 += kDepth) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        // step s + 1 into the stage the consumers are not reading (past the last
+        // step a copy of the last step, which nobody reads), then refill its slot
+        const int s = s0 + u, un = (u + 1) % kDepth;
+        uint4 *nx = lds + ((u + 1) & 1) * C::kStageGran;
+        store_step<C>(pt, nx, nx + C::kXGran, s + 1, ring[un]);
+        load_step<C>(pt, xg, m0, M, gpr, w_rowp, nsteps, s + 1 + kDepth, ring[un]);
+        __syncthreads();
+      }
+    }
+    return;
+  }
 
+  const int lane = tid & 63;
+  const int wm = (wave / C::WN_WAVES) * 64, wn = (wave % C::WN_WAVES) * 64;
   floatx16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -191,24 +241,14 @@ __global__ __launch_bounds__(kThreads) void q4k_prefill_kernel(const uint8_t *__
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  StepRegs<C> ring[kDepth];
-#pragma unroll
-  for (int u = 0; u < kDepth; ++u) load_step<C>(xg, m0, M, gpr, w_rowp, nsteps, u, ring[u]);
-  store_step<C>(lds, lds + C::kXGran, 0, ring[0]);
-  load_step<C>(xg, m0, M, gpr, w_rowp, nsteps, kDepth, ring[0]);
   __syncthreads();
-
-  // The fragments of K slice kk + 1 are read while slice kk's MFMAs run, and
-  // slice 0 of the next stage right after the barrier.
   const int frow = lane & 31, fg = lane >> 5;
   bf16x8 a[2][2], b[2][2];
   read_frags(lds, lds + C::kXGran, wm, wn, 0, a[0], b[0]);
   for (int s0 = 0; s0 < nsteps; s0 += kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
-      const int s = s0 + u;
-      const uint4 *xt = lds + (u & 1) * C::kStageGran;   // s & 1 == u & 1: kDepth is even
+      const uint4 *xt = lds + (u & 1) * C::kStageGran;
       const uint4 *wt = xt + C::kXGran;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -219,19 +259,11 @@ __global__ __launch_bounds__(kThreads) void q4k_prefill_kernel(const uint8_t *__
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
       }
-      // step s + 1 into the other stage (past the last step this writes a copy
-      // of the last step, which nobody reads), then its ring slot is refilled
-      const int un = (u + 1) % kDepth;
-      uint4 *nx = lds + ((u + 1) & 1) * C::kStageGran;
-      store_step<C>(nx, nx + C::kXGran, s + 1, ring[un]);
-      load_step<C>(xg, m0, M, gpr, w_rowp, nsteps, s + 1 + kDepth, ring[un]);
       __syncthreads();
+      const uint4 *nx = lds + ((u + 1) & 1) * C::kStageGran;
       read_frags(nx, nx + C::kXGran, wm, wn, 0, a[0], b[0]);
     }
   }
-
-  // 32x32 accumulator layout: lane l holds column l % 32 and, in register
-  // 4 q + e, row 8 q + 4 (l / 32) + e
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -249,20 +281,20 @@ __global__ __launch_bounds__(kThreads) void q4k_prefill_kernel(const uint8_t *__
 }
 
 template <class C>
-int launch_cfg(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t stream) {
+int launch_ws(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t stream) {
   static std::atomic<size_t> granted{0};
-  if (allow_dynamic_lds(reinterpret_cast<const void *>(&q4k_prefill_kernel<C>), C::kLdsBytes, granted,
-                        "q4k_prefill_kernel lds"))
+  if (allow_dynamic_lds(reinterpret_cast<const void *>(&q4k_prefill_ws_kernel<C>), C::kLdsBytes, granted,
+                        "q4k_prefill_ws_kernel lds"))
     return QMV_ERR_HIP;
   const dim3 grid((unsigned)(((n + C::BN - 1) / C::BN) * ((m + C::BM - 1) / C::BM)));
-  return launch_kernel("q4k_prefill_kernel", q4k_prefill_kernel<C>, grid, dim3(kThreads), C::kLdsBytes, stream, w,
-                       x, y, m, n, k);
+  return launch_kernel("q4k_prefill_ws_kernel", q4k_prefill_ws_kernel<C>, grid, dim3(2 * kThreads), C::kLdsBytes,
+                       stream, w, x, y, m, n, k);
 }
 
 }  // namespace
 
 int launch_q4_k_prefill(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream) {
-  return launch_cfg<Cfg<128, 128, 4>>(w, x, y, m, n, k, static_cast<hipStream_t>(stream));
+  return launch_ws<Cfg<128, 128, 4>>(w, x, y, m, n, k, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace qmv
