@@ -377,8 +377,11 @@ def bench_prefill(args, torch, np, q, synth, timer, dev, sp, pool):
         x = torch.from_numpy(synth.bf16_normal(31, (m, k)).view(np.int16)).to(dev)
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         copies = min(20, len(pool))
+        need = L.qmm_q4_k_prefill_workspace(m, n, k)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        ws_arg = ctypes.c_void_p(ws.data_ptr()) if need else None
         calls = [(ctypes.c_void_p(pool[c][i].data_ptr()), pool[c][i].numel(), ctypes.c_void_p(x.data_ptr()),
-                  ctypes.c_void_p(y.data_ptr()), m, n, k, sp) for c in range(copies)]
+                  ctypes.c_void_p(y.data_ptr()), m, n, k, ws_arg, need, sp) for c in range(copies)]
 
         def step():
             for a in calls:
@@ -399,7 +402,7 @@ def bench_prefill(args, torch, np, q, synth, timer, dev, sp, pool):
         torch.matmul(a, b.t())
         tt = timer.run(lambda: torch.matmul(a, b.t()), 10)
         out[name] = {"us": tp * 1e6, "TFLOPs": flops / tp / 1e12, "frac_of_bf16_peak": flops / tp / 1e12 / BF16_PEAK_TFLOPS,
-                     "torch_bf16_dense_TFLOPs": flops / tt / 1e12}
+                     "torch_bf16_dense_TFLOPs": flops / tt / 1e12, "k_split_workspace_bytes": need}
         log(f"[bench] prefill {name} {m}x{n}x{k}: {tp * 1e6:.1f} us, {flops / tp / 1e12:.0f} TFLOP/s "
             f"(torch dense bf16: {flops / tt / 1e12:.0f})")
     return out

@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "QmvError", "lib", "LIB_PATH", "version",
-    "qmv_q8_0", "qmv_q4_k", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmm_q4_k_prefill",
+    "qmv_q8_0", "qmv_q4_k", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmm_q4_k_prefill_workspace", "qmm_q4_k_prefill",
     "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16", "qmv_dequant_q8_0_f32",
     "q4_k_bytes", "q8_0_bytes", "EXPORTS",
 ]
@@ -33,7 +33,8 @@ EXPORTS = {
     "qmv_q4_k_moe_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "qmv_q4_k_moe": (_c_int, [_vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
                               _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
-    "qmm_q4_k_prefill": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
+    "qmm_q4_k_prefill_workspace": (_c_size, [_c_int, _c_int, _c_int]),
+    "qmm_q4_k_prefill": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_size, _vp]),
     "qmv_dequant_q4_k_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
     "qmv_dequant_q4_k_bf16": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
     "qmv_dequant_q8_0_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
@@ -111,7 +112,7 @@ def _ptr(t):
 
 
 def _nbytes(t):
-    return t.numel() * t.element_size()
+    return t.numel() * t.element_size() if t is not None else 0
 
 
 def _stream(stream):
@@ -186,8 +187,16 @@ def qmv_q4_k_moe(w_gate, w_up, w_down, logits, x, hidden: int, ffn: int, n_exper
     return y, ids, wts, pairs
 
 
-def qmm_q4_k_prefill(w, x, n: int, k: int, y=None, stream=None):
-    """Y[m, n] = X[m, k] @ bf16(dequant(w))^T on bf16 matrix cores, fp32 accumulation."""
+def qmm_q4_k_prefill_workspace(m: int, n: int, k: int) -> int:
+    return lib.qmm_q4_k_prefill_workspace(m, n, k)
+
+
+def qmm_q4_k_prefill(w, x, n: int, k: int, y=None, ws="auto", stream=None):
+    """Y[m, n] = X[m, k] @ bf16(dequant(w))^T on bf16 matrix cores, fp32 accumulation.
+
+    ws: "auto" allocates a workspace when the shape uses the K split, None runs
+    every output tile whole, or a uint8 device tensor to reuse.
+    """
     torch = _torch()
     _dev(w, "w", (torch.uint8,))
     _dev(x, "x", _bf16_types())
@@ -195,8 +204,15 @@ def qmm_q4_k_prefill(w, x, n: int, k: int, y=None, stream=None):
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _dev(y, "y", (torch.float32,))
-    _check(lib.qmm_q4_k_prefill(_ptr(w), _nbytes(w), _ptr(x), _ptr(y), m, n, k, _stream(stream)),
-           "qmm_q4_k_prefill")
+    if isinstance(ws, str):
+        if ws != "auto":
+            raise ValueError("ws must be 'auto', None or a tensor")
+        need = qmm_q4_k_prefill_workspace(m, n, k)
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    if ws is not None:
+        _dev(ws, "ws", (torch.uint8,))
+    _check(lib.qmm_q4_k_prefill(_ptr(w), _nbytes(w), _ptr(x), _ptr(y), m, n, k, _ptr(ws), _nbytes(ws),
+                                _stream(stream)), "qmm_q4_k_prefill")
     return y
 
 

@@ -169,18 +169,18 @@ __device__ __forceinline__ void read_frags(const uint4 *__restrict__ xt, const u
   for (int j = 0; j < 2; ++j) fb[j] = __builtin_bit_cast(bf16x8, wt[tslot(wn + 32 * j + frow, 2 * kk + fg)]);
 }
 
-// Tile (mt, nt) of the launch: when the M tiles divide 8, XCD x works only on
-// M tile x % m_tiles, so the X rows of a tile stay in that XCD's L2 for all
-// its N tiles (workgroups are dealt to the 8 XCDs round robin by launch order).
-__device__ __forceinline__ void tile_of(const int M, const int N, const int BM, const int BN, int &mt, int &nt) {
-  const int n_tiles = (N + BN - 1) / BN, m_tiles = (M + BM - 1) / BM;
+// Tile t as (mt, nt): when the M tiles divide 8, tile t goes where block t of
+// a one-tile-per-block launch runs -- workgroups are dealt to the 8 XCDs round
+// robin by launch order -- and XCD x works only on M tile x % m_tiles, so the
+// X rows of a tile stay in that XCD's L2 for all its N tiles.
+__device__ __forceinline__ void tile_of(const int t, const int m_tiles, const int n_tiles, int &mt, int &nt) {
   if (8 % m_tiles == 0 && n_tiles % (8 / m_tiles) == 0) {
-    const int b = blockIdx.x, xcd = b & 7, per = 8 / m_tiles;
+    const int xcd = t & 7, per = 8 / m_tiles;
     mt = xcd % m_tiles;
-    nt = (xcd / m_tiles) + per * (b >> 3);
+    nt = (xcd / m_tiles) + per * (t >> 3);
   } else {
-    nt = blockIdx.x % n_tiles;
-    mt = blockIdx.x / n_tiles;
+    nt = t % n_tiles;
+    mt = t / n_tiles;
   }
 }
 
@@ -191,25 +191,46 @@ __device__ __forceinline__ void tile_of(const int M, const int N, const int BM, 
 // dequantization VALU work issues while the other wave's matrix instructions
 // execute. One barrier per step hands a stage from the producers to the
 // consumers and back; both kinds pass the same number of barriers.
+//
+// Blocks below t_main each compute a whole tile (tile = block) into Y. The
+// r_tiles tiles after them, when the tile count does not divide over the
+// workgroups the device holds at once, are split along K: block t_main + s *
+// r_tiles + r computes part s of tile t_main + r -- a run of whole 256-value
+// K blocks -- and stores its 128 x 128 sums to that part's slot of `part`;
+// q4k_prefill_reduce_kernel adds the parts in order afterwards.
 template <class C>
 __global__ __launch_bounds__(2 * kThreads) void q4k_prefill_ws_kernel(const uint8_t *__restrict__ w,
                                                                       const uint16_t *__restrict__ x,
-                                                                      float *__restrict__ y, const int M,
-                                                                      const int N, const int K) {
+                                                                      float *__restrict__ y, float *__restrict__ part,
+                                                                      const int M, const int N, const int K,
+                                                                      const int t_main, const int r_tiles,
+                                                                      const int splits) {
   constexpr int BM = C::BM, BN = C::BN, kDepth = C::kDepth;
   extern __shared__ uint4 lds[];
   const int tid = threadIdx.x, wave = tid >> 6;
+  const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
+  const int blk = (int)blockIdx.x;
+  // this block's tile and its K steps [s_begin, s_begin + nsteps), both
+  // multiples of 4 (whole K blocks), so of kDepth in {2, 4}
+  int tile = blk, s_begin = 0, nsteps = K / BK, slot = -1;
+  if (blk >= t_main) {
+    const int rb = blk - t_main, r = rb % r_tiles, sp = rb / r_tiles, nkb = K >> 8;
+    tile = t_main + r;
+    s_begin = 4 * (sp * nkb / splits);
+    nsteps = 4 * ((sp + 1) * nkb / splits) - s_begin;
+    slot = sp * r_tiles + r;
+  }
   int mt, nt;
-  tile_of(M, N, BM, BN, mt, nt);
+  tile_of(tile, m_tiles, n_tiles, mt, nt);
   const int n0 = nt * BN, m0 = mt * BM;
-  const int nsteps = K / BK;   // a multiple of 4, so of kDepth in {2, 4}
 
   if (wave >= 4) {
     const int pt = tid - kThreads;
     const int nblk = K >> 8;
     const int w_row = pt / C::kWThreadsPerRow;
-    const uint8_t *w_rowp = w + (size_t)(n0 + w_row < N ? n0 + w_row : 0) * (size_t)nblk * kQ4KBlockBytes;
-    const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+    const uint8_t *w_rowp = w + (size_t)(n0 + w_row < N ? n0 + w_row : 0) * (size_t)nblk * kQ4KBlockBytes +
+                            (size_t)(s_begin >> 2) * kQ4KBlockBytes;
+    const uint4 *xg = reinterpret_cast<const uint4 *>(x) + s_begin * 8;   // step s_begin of row 0
     const int gpr = K >> 3;
     StepRegs<C> ring[kDepth];
 #pragma unroll
@@ -264,6 +285,21 @@ __global__ __launch_bounds__(2 * kThreads) void q4k_prefill_ws_kernel(const uint
       read_frags(nx, nx + C::kXGran, wm, wn, 0, a[0], b[0]);
     }
   }
+  // 32x32 accumulator layout: lane l holds column l % 32 and, in register
+  // 4 q + e, row 8 q + 4 (l / 32) + e
+  if (slot >= 0) {
+    float *pt = part + (size_t)slot * BM * BN;   // the part's 128 x 128 sums, row-major
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pt[(size_t)(wm + 32 * i + 8 * q + 4 * fg + e) * BN + wn + 32 * j + frow] = acc[i][j][4 * q + e];
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -280,21 +316,106 @@ __global__ __launch_bounds__(2 * kThreads) void q4k_prefill_ws_kernel(const uint
     }
 }
 
+// Y of the K-split tiles: each thread sums four adjacent values of one tile
+// row over the parts, in part order (so in K order), and stores those inside Y.
 template <class C>
-int launch_ws(const void *w, const uint16_t *x, float *y, int m, int n, int k, hipStream_t stream) {
-  static std::atomic<size_t> granted{0};
-  if (allow_dynamic_lds(reinterpret_cast<const void *>(&q4k_prefill_ws_kernel<C>), C::kLdsBytes, granted,
-                        "q4k_prefill_ws_kernel lds"))
-    return QMV_ERR_HIP;
-  const dim3 grid((unsigned)(((n + C::BN - 1) / C::BN) * ((m + C::BM - 1) / C::BM)));
-  return launch_kernel("q4k_prefill_ws_kernel", q4k_prefill_ws_kernel<C>, grid, dim3(2 * kThreads), C::kLdsBytes,
-                       stream, w, x, y, m, n, k);
+__global__ __launch_bounds__(256) void q4k_prefill_reduce_kernel(const float *__restrict__ part, float *__restrict__ y,
+                                                                 const int M, const int N, const int t_main,
+                                                                 const int r_tiles, const int splits) {
+  constexpr int BM = C::BM, BN = C::BN, kQuads = BM * BN / 4;
+  const int idx = (int)(blockIdx.x * 256 + threadIdx.x);
+  const int r = idx / kQuads, within = idx % kQuads;
+  if (r >= r_tiles) return;
+  const int row = within / (BN / 4), c4 = within % (BN / 4);
+  int mt, nt;
+  tile_of(t_main + r, (M + BM - 1) / BM, (N + BN - 1) / BN, mt, nt);
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int sp = 0; sp < splits; ++sp) {
+    const float4 v = reinterpret_cast<const float4 *>(part + (size_t)(sp * r_tiles + r) * BM * BN)[within];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  const int grow = mt * BM + row, gcol = nt * BN + 4 * c4;
+  if (grow >= M) return;
+  float *yr = y + (size_t)grow * N;
+  if (gcol < N) yr[gcol] = acc.x;
+  if (gcol + 1 < N) yr[gcol + 1] = acc.y;
+  if (gcol + 2 < N) yr[gcol + 2] = acc.z;
+  if (gcol + 3 < N) yr[gcol + 3] = acc.w;
+}
+
+using PrefillCfg = Cfg<128, 128, 4>;
+
+// Workgroups of the GEMM kernel resident at once on the current device (0 if
+// the runtime cannot say), cached per device.
+int resident_capacity() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&q4k_prefill_ws_kernel<PrefillCfg>),
+                                                   2 * kThreads, PrefillCfg::kLdsBytes) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  c = per_cu * cus;
+  cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+// The split of an m x n x k product: t_main whole tiles (a multiple of the
+// resident capacity), then r_tiles tiles in `splits` K parts each so that the
+// last round fills the device. splits == 0: every tile whole.
+struct Plan {
+  int t_main, r_tiles, splits;
+};
+Plan plan_for(int m, int n, int k) {
+  using C = PrefillCfg;
+  const int tiles = ((n + C::BN - 1) / C::BN) * ((m + C::BM - 1) / C::BM);
+  const int cap = resident_capacity();
+  Plan p{tiles, 0, 0};
+  if (cap <= 0) return p;
+  const int t_main = tiles / cap * cap, r = tiles - t_main;
+  if (r == 0) return p;
+  int splits = cap / r;
+  if (splits > k / 256) splits = k / 256;   // parts of whole K blocks
+  if (splits < 2) return p;
+  return Plan{t_main, r, splits};
+}
+
+size_t plan_bytes(const Plan &p) {
+  return (size_t)p.splits * p.r_tiles * PrefillCfg::BM * PrefillCfg::BN * sizeof(float);
 }
 
 }  // namespace
 
-int launch_q4_k_prefill(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream) {
-  return launch_ws<Cfg<128, 128, 4>>(w, x, y, m, n, k, static_cast<hipStream_t>(stream));
+size_t prefill_workspace_bytes(int m, int n, int k) { return plan_bytes(plan_for(m, n, k)); }
+
+int launch_q4_k_prefill(const void *w, const uint16_t *x, float *y, void *ws, size_t ws_bytes, int m, int n, int k,
+                        void *stream) {
+  using C = PrefillCfg;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  static std::atomic<size_t> granted{0};
+  if (allow_dynamic_lds(reinterpret_cast<const void *>(&q4k_prefill_ws_kernel<C>), C::kLdsBytes, granted,
+                        "q4k_prefill_ws_kernel lds"))
+    return QMV_ERR_HIP;
+  const int tiles = ((n + C::BN - 1) / C::BN) * ((m + C::BM - 1) / C::BM);
+  Plan p{tiles, 0, 0};
+  if (ws) {
+    const Plan q = plan_for(m, n, k);
+    if (q.splits > 0 && ws_bytes >= plan_bytes(q)) p = q;
+  }
+  float *part = static_cast<float *>(ws);
+  const int blocks = p.t_main + p.r_tiles * p.splits;
+  int rc = launch_kernel("q4k_prefill_ws_kernel", q4k_prefill_ws_kernel<C>, dim3((unsigned)blocks),
+                         dim3(2 * kThreads), C::kLdsBytes, s, w, x, y, part, m, n, k, p.t_main, p.r_tiles, p.splits);
+  if (rc || p.splits == 0) return rc;
+  const int threads = p.r_tiles * (C::BM * C::BN / 4);
+  return launch_kernel("q4k_prefill_reduce_kernel", q4k_prefill_reduce_kernel<C>, dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, s, static_cast<const float *>(part), y, m, n, p.t_main, p.r_tiles, p.splits);
 }
 
 }  // namespace qmv

@@ -151,17 +151,28 @@ int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_
                               n_experts, top_k, stream);
 }
 
-int qmm_q4_k_prefill(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, int m, int n, int k,
-                     void *stream) {
+size_t qmm_q4_k_prefill_workspace(int m, int n, int k) {
+  if (m < 1 || n < 1 || k < 256 || k % 256) return 0;
+  return qmv::prefill_workspace_bytes(m, n, k);
+}
+
+int qmm_q4_k_prefill(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, int m, int n, int k, void *ws,
+                     size_t ws_bytes, void *stream) {
   if (!w || !x_bf16 || !y) return QMV_ERR_NULL;
   if (m < 1) return QMV_ERR_RANGE;
   int rc = check_matrix(w, w_bytes, n, k, 256, 144, 16);
   if (rc) return rc;
-  if (!aligned(x_bf16, 16) || !aligned(y, 16)) return QMV_ERR_ALIGN;
+  if (!aligned(x_bf16, 16) || !aligned(y, 16) || !aligned(ws, 256)) return QMV_ERR_ALIGN;
   size_t xb = 0, yb = 0;
   if (!mul_size((size_t)m, (size_t)k * 2, &xb) || !mul_size((size_t)m, (size_t)n * 4, &yb)) return QMV_ERR_RANGE;
   if (overlap(y, yb, w, w_bytes) || overlap(y, yb, x_bf16, xb)) return QMV_ERR_ALIAS;
-  return qmv::launch_q4_k_prefill(w, x_bf16, y, m, n, k, stream);
+  if (ws) {
+    const size_t need = qmv::prefill_workspace_bytes(m, n, k);
+    if (ws_bytes < need) return QMV_ERR_WORKSPACE;
+    const size_t wsb = need ? need : ws_bytes;
+    if (overlap(ws, wsb, w, w_bytes) || overlap(ws, wsb, x_bf16, xb) || overlap(ws, wsb, y, yb)) return QMV_ERR_ALIAS;
+  }
+  return qmv::launch_q4_k_prefill(w, x_bf16, y, ws, ws_bytes, m, n, k, stream);
 }
 
 int qmv_dequant_q4_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream) {

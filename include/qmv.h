@@ -155,18 +155,33 @@ int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_
                  int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
 
 /*
+ * Workspace bytes qmm_q4_k_prefill can use for an m x n x k product on the
+ * current device: 0 when the output tiles divide evenly over the workgroups
+ * the device holds at once (or too few K blocks to split). Otherwise the tiles
+ * past the largest multiple of that count are split along K so that the last
+ * round fills the device, and this many bytes hold their parts' fp32 sums.
+ */
+size_t qmm_q4_k_prefill_workspace(int m, int n, int k);
+
+/*
  * Prefill-sized product Y = X W^T on bf16 matrix cores.
  *   w       [n rows][k/256 blocks] Q4_K, 16-byte aligned; w_bytes == n*(k/256)*144
  *   x_bf16  bf16 bits [m][k] row-major, 16-byte aligned
  *   y       fp32 [m][n] row-major, 16-byte aligned
+ *   ws      NULL, or device memory of ws_bytes >= qmm_q4_k_prefill_workspace(m, n, k),
+ *           256-byte aligned (its contents on entry do not matter)
  *   m >= 1, n >= 1, k % 256 == 0.
  * Weights are dequantized to fp32, rounded once to bf16 (round to nearest
  * even) and multiplied with the bf16 activations, accumulating in fp32.
+ * Each output tile is one workgroup's sequential fp32 sum over K, except, with
+ * a workspace, the split tiles: there each part sums a run of whole K blocks
+ * and a second launch adds the parts in K order. Results are deterministic
+ * for a given shape and device.
  * Workload: prompt processing ahead of decode (the time-to-first-token figures
  * of the memra summary page's performance table).
  */
 int qmm_q4_k_prefill(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
-                     int m, int n, int k, void *stream);
+                     int m, int n, int k, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Dequantization to dense matrices (the bit-exact gate of the decode kernels).

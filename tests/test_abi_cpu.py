@@ -34,7 +34,8 @@ def _header_functions():
 def test_header_lists_the_expected_entry_points():
     assert _header_functions() == sorted([
         "qmv_version", "qmv_strerror", "qmv_last_error", "qmv_q8_0", "qmv_q4_k", "qmv_q4_k_moe_workspace", "qmv_q4_k_moe",
-        "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16", "qmv_dequant_q8_0_f32"])
+        "qmm_q4_k_prefill_workspace", "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16",
+        "qmv_dequant_q8_0_f32"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -108,11 +109,16 @@ def test_dequant_validation():
 def test_prefill_validation():
     nb = q.q4_k_bytes(4, 512)
     f = L.qmm_q4_k_prefill
-    assert f(V(W), nb, V(X), V(Y), 0, 4, 512, None) == RANGE
-    assert f(V(W), nb, V(0), V(Y), 8, 4, 512, None) == NULL
-    assert f(V(W), nb + 144, V(X), V(Y), 8, 4, 512, None) == SIZE
-    assert f(V(W), nb, V(X), V(Y + 4), 8, 4, 512, None) == ALIGN
-    assert f(V(W), nb, V(X), V(X + 16), 8, 4, 512, None) == ALIAS
+    assert f(V(W), nb, V(X), V(Y), 0, 4, 512, None, 0, None) == RANGE
+    assert f(V(W), nb, V(0), V(Y), 8, 4, 512, None, 0, None) == NULL
+    assert f(V(W), nb + 144, V(X), V(Y), 8, 4, 512, None, 0, None) == SIZE
+    assert f(V(W), nb, V(X), V(Y + 4), 8, 4, 512, None, 0, None) == ALIGN
+    assert f(V(W), nb, V(X), V(X + 16), 8, 4, 512, None, 0, None) == ALIAS
+    assert f(V(W), nb, V(X), V(Y), 8, 4, 512, V(WS + 128), 1 << 20, None) == ALIGN   # workspace alignment
+    assert f(V(W), nb, V(X), V(Y), 8, 4, 512, V(X), 1 << 20, None) == ALIAS          # workspace over an input
+    # without a device the split form is never chosen: no workspace is needed
+    assert L.qmm_q4_k_prefill_workspace(512, 17408, 5120) == 0
+    assert L.qmm_q4_k_prefill_workspace(0, 16, 256) == 0 and L.qmm_q4_k_prefill_workspace(1, 16, 100) == 0
 
 
 def moe(**kw):
