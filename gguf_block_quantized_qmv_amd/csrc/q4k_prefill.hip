@@ -380,9 +380,14 @@ Plan plan_for(int m, int n, int k) {
   if (cap <= 0) return p;
   const int t_main = tiles / cap * cap, r = tiles - t_main;
   if (r == 0) return p;
-  int splits = cap / r;
-  if (splits > k / 256) splits = k / 256;   // parts of whole K blocks
-  if (splits < 2) return p;
+  const int nkb = k / 256;   // parts are runs of whole K blocks
+  const int most = cap / r < nkb ? cap / r : nkb;
+  if (most < 2) return p;
+  // the longest part decides the round; the fewest parts that reach it keep
+  // the partial sums (and the second launch's reads) smallest
+  const int longest = (nkb + most - 1) / most;
+  int splits = (nkb + longest - 1) / longest;
+  if (splits < 2) splits = 2;
   return Plan{t_main, r, splits};
 }
 
