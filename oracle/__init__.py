@@ -6,11 +6,15 @@ this package; the product path never does.
 
 from .gguf_oracle import *  # noqa: F401,F403
 from .gguf_oracle import (  # noqa: F401
+    IQ4_GRID,
+    IQ4_XS_BLOCK_BYTES,
+    IQ4_XS_BLOCK_WEIGHTS,
     Q4_K_BLOCK_BYTES,
     Q4_K_BLOCK_WEIGHTS,
     Q8_0_BLOCK_BYTES,
     Q8_0_BLOCK_WEIGHTS,
     bf16_bits_to_f64,
+    dequant_iq4_xs,
     dequant_q4_k,
     dequant_q4_k_bf16_bits,
     dequant_q4_k_f32,
@@ -22,10 +26,12 @@ from .gguf_oracle import (  # noqa: F401
     frobenius_rel_err,
     gather_pairs,
     gemv,
+    iq4_xs_fields,
     moe_q4_k,
     prefill_q4_k,
     q4_k_fields,
     q8_0_fields,
+    qmv_iq4_xs,
     qmv_q4_k,
     qmv_q8_0,
     round_f32_to_bf16_bits,

@@ -25,15 +25,18 @@ values -- so this oracle is that definition written out in fp64:
   first rounded to fp32 and then to bf16 (the prescribed bf16 tile).
 
 The byte layouts are the public GGUF ones (Q8_0: fp16 d + 32 int8; Q4_K: fp16
-d, fp16 dmin, 12 bytes of packed 6-bit scales and mins, 128 bytes of nibbles),
-restated in this module's own words next to the code that reads them.
+d, fp16 dmin, 12 bytes of packed 6-bit scales and mins, 128 bytes of nibbles;
+IQ4_XS: fp16 d, 6-bit sub-block scales in 6 bytes, 128 bytes of 4-bit indices
+into a 16-entry integer grid), restated in this module's own words next to the
+code that reads them.
 
 Parity pins live in tests/test_oracle_*.py (hand-built blocks written as hex,
 locality invariants, pack/unpack bijection, requantisation round trips, exact
 rational brute force, closed forms, MoE = weighted dense sum).
 
-Parity unpinned: that the Q4_K 6-bit scale/min packing and nibble order used
-here equal those of real llama.cpp-written GGUF tensors. No GGUF file, gguf
+Parity unpinned: that the Q4_K 6-bit scale/min packing and nibble order, and
+the IQ4_XS scale packing, index order and 16-entry grid, used here equal those
+of real llama.cpp-written GGUF tensors. No GGUF file, gguf
 package or llama.cpp is in reach, and the pages print no block bytes, so every
 in-repository check would also pass with a self-consistent mis-layout.
 """
@@ -192,6 +195,80 @@ def dequant_q8_0_f32(raw, n_rows: int, k: int) -> np.ndarray:
 def dequant_q4_k_bf16_bits(raw, n_rows: int, k: int) -> np.ndarray:
     """The bf16 tile target: RN_bf16(RN_fp32(w)), as uint16 bit patterns."""
     return round_f32_to_bf16_bits(dequant_q4_k_f32(raw, n_rows, k))
+
+
+# ----------------------------------------------------------------------------
+# IQ4_XS: 136-byte super-blocks of 256 weights along K
+# ----------------------------------------------------------------------------
+#
+# The memra README's model support table ships its 35B-A3B MoE in IQ4_XS and
+# the memra-bench card's Drafts section carries a UD-IQ4_XS draft of it; the
+# pages print no layout, so the one below is the public GGUF format, restated
+# here: eight sub-blocks of 32 weights, each with a 6-bit scale ls_j, and
+# 4-bit indices into a fixed 16-entry table of signed integers.
+
+IQ4_XS_BLOCK_BYTES = 136
+IQ4_XS_BLOCK_WEIGHTS = 256
+# the non-linear 4-bit grid of the format (index 0..15 -> integer value)
+IQ4_GRID = (-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113)
+
+
+def iq4_xs_fields(raw, n_rows: int, k: int):
+    """Decode a row-major IQ4_XS matrix into its fields.
+
+    Returns (d, ls, q):
+      d  : float64 [N, nb]       the fp16 super-block scale
+      ls : int64   [N, nb, 8]    6-bit scale of sub-block j = 0..7 (the weight scale is ls - 32)
+      q  : int64   [N, nb, 256]  the 4-bit grid index of each weight, in weight order
+
+    Byte layout of one super-block (block b of row n starts at (n*K/256 + b)*136):
+      0..1   fp16 d (little-endian)
+      2..3   H: 16 bits, bits 2j..2j+1 are the top two bits of ls_j
+      4..7   L[0..3]: the low 4 bits of ls_j in the low nibble of L[j/2] for even j,
+             in its high nibble for odd j
+      8..135 the indices: sub-block j owns bytes 8 + 16j .. 8 + 16j + 15; byte i of
+             those holds weight 32j + i in its low nibble and weight 32j + 16 + i in
+             its high nibble
+    """
+    if k % IQ4_XS_BLOCK_WEIGHTS:
+        raise ValueError("IQ4_XS needs K to be a multiple of 256")
+    nb = k // IQ4_XS_BLOCK_WEIGHTS
+    b = _as_bytes(raw)
+    if b.size != n_rows * nb * IQ4_XS_BLOCK_BYTES:
+        raise ValueError("byte count does not match the IQ4_XS shape")
+    blocks = b.reshape(n_rows, nb, IQ4_XS_BLOCK_BYTES).astype(np.int64)
+    d = fp16_bits_to_f64((blocks[:, :, 0] | (blocks[:, :, 1] << 8)).astype(np.uint16))
+    H = blocks[:, :, 2] | (blocks[:, :, 3] << 8)
+    L = blocks[:, :, 4:8]
+    ls = np.empty((n_rows, nb, 8), dtype=np.int64)
+    for j in range(8):
+        low = (L[:, :, j // 2] >> (4 * (j % 2))) & 0x0F
+        ls[:, :, j] = low | (((H >> (2 * j)) & 0x3) << 4)
+    Q = blocks[:, :, 8:]
+    q = np.empty((n_rows, nb, 256), dtype=np.int64)
+    for j in range(8):
+        byte = Q[:, :, 16 * j: 16 * j + 16]
+        q[:, :, 32 * j: 32 * j + 16] = byte & 0x0F
+        q[:, :, 32 * j + 16: 32 * j + 32] = byte >> 4
+    return d, ls, q
+
+
+def dequant_iq4_xs(raw, n_rows: int, k: int) -> np.ndarray:
+    """Exact IQ4_XS weights: w = d * (ls_j - 32) * grid[q] for weight i of sub-block j.
+
+    float64 [N, K]. d has 11 significant bits, ls - 32 at most 6 and a grid value
+    at most 7, so every weight is exact in fp64 (and in fp32).
+    """
+    d, ls, q = iq4_xs_fields(raw, n_rows, k)
+    nb = k // IQ4_XS_BLOCK_WEIGHTS
+    grid = np.asarray(IQ4_GRID, dtype=np.int64)
+    scale = (d[:, :, None] * (ls - 32)).repeat(32, axis=2)   # [N, nb, 256]
+    return (scale * grid[q]).reshape(n_rows, nb * 256)
+
+
+def qmv_iq4_xs(raw, x_bf16_bits, n_rows: int, k: int) -> np.ndarray:
+    """IQ4_XS matrix times bf16 activation rows -> float64 [M, N]."""
+    return gemv(dequant_iq4_xs(raw, n_rows, k), bf16_bits_to_f64(x_bf16_bits))
 
 
 # ----------------------------------------------------------------------------

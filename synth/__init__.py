@@ -16,6 +16,10 @@ bits, every bit used once, so the map between the 12 bytes and the 16 fields is
 a bijection. Uniform random bytes there are therefore exactly i.i.d. uniform
 sc, m in [0, 63], and uniform random quant bytes are i.i.d. uniform nibbles in
 [0, 15]. The generator needs no knowledge of the packing.
+
+The same holds for IQ4_XS: after its fp16 d, 6 bytes store eight 6-bit
+sub-block scales in exactly 48 bits and 128 bytes store the 4-bit grid indices,
+so uniform bytes are i.i.d. uniform scales in [0, 63] and indices in [0, 15].
 """
 
 from __future__ import annotations
@@ -31,11 +35,14 @@ __all__ = [
     "moe_bank",
     "moe_logits",
     "torch_q4_k_weights",
+    "iq4_xs_weights",
+    "torch_iq4_xs_weights",
 ]
 
 # Block geometry of the two GGUF formats (bytes per block, weights per block).
 _Q8_0_BYTES, _Q8_0_WEIGHTS = 34, 32
 _Q4_K_BYTES, _Q4_K_WEIGHTS = 144, 256
+_IQ4_XS_BYTES, _IQ4_XS_WEIGHTS = 136, 256
 
 
 def rng(seed: int, *stream: int) -> np.random.Generator:
@@ -142,4 +149,41 @@ def torch_q4_k_weights(seed: int, n_rows: int, k: int, device, *, stream: int = 
     blocks = torch.randint(0, 256, (nb, _Q4_K_BYTES), dtype=torch.uint8, device=device, generator=g)
     scales = torch.randn((nb, 2), dtype=torch.float32, device=device, generator=g).abs_().mul_(0.002)
     blocks[:, 0:4] = scales.to(torch.float16).view(torch.uint8).view(nb, 4)
+    return blocks.view(-1)
+
+
+def iq4_xs_weights(seed: int, n_rows: int, k: int, *, stream: int = 0, d_scale: float = 0.0005) -> np.ndarray:
+    """Row-major IQ4_XS matrix bytes.
+
+    Per 136-byte super-block: fp16 d = |N(0,1)|*0.0005, then 134 uniform random
+    bytes (6 scale bytes + 128 index bytes): sub-block scales ~ U[0,63] and grid
+    indices ~ U[0,15] i.i.d. (see the module docstring). With grid values up to
+    127 in magnitude and (scale - 32) up to 32, the weights have the Q4_K
+    recipe's order of magnitude. Returns a flat uint8 array of
+    n_rows * (k/256) * 136 bytes.
+    """
+    if k % _IQ4_XS_WEIGHTS:
+        raise ValueError("k must be a multiple of 256")
+    nb = n_rows * (k // _IQ4_XS_WEIGHTS)
+    g = rng(seed, 44, stream)
+    d = _fp16_abs_normal(g, nb, d_scale)
+    blocks = np.empty((nb, _IQ4_XS_BYTES), dtype=np.uint8)
+    blocks[:, 0:2] = d.view(np.uint8).reshape(nb, 2)
+    blocks[:, 2:] = g.integers(0, 256, size=(nb, _IQ4_XS_BYTES - 2), dtype=np.uint8)
+    return blocks.reshape(-1)
+
+
+def torch_iq4_xs_weights(seed: int, n_rows: int, k: int, device, *, stream: int = 0, d_scale: float = 0.0005):
+    """Device-side IQ4_XS matrix bytes with the recipe of iq4_xs_weights (d rounded
+    from fp32 rather than fp64). Returns a flat uint8 device tensor."""
+    import torch
+
+    if k % _IQ4_XS_WEIGHTS:
+        raise ValueError("k must be a multiple of 256")
+    nb = n_rows * (k // _IQ4_XS_WEIGHTS)
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1_000_003 + int(stream) * 7919 + 44) & 0x7FFF_FFFF_FFFF_FFFF)
+    blocks = torch.randint(0, 256, (nb, _IQ4_XS_BYTES), dtype=torch.uint8, device=device, generator=g)
+    d = torch.randn((nb, 1), dtype=torch.float32, device=device, generator=g).abs_().mul_(d_scale)
+    blocks[:, 0:2] = d.to(torch.float16).view(torch.uint8).view(nb, 2)
     return blocks.view(-1)

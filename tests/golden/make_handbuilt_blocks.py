@@ -1,4 +1,4 @@
-"""Writes tests/golden/{q8_0,q4_k}_handbuilt.json: hand-built blocks with known values.
+"""Writes tests/golden/{q8_0,q4_k,iq4_xs}_handbuilt.json: hand-built blocks with known values.
 
 Run from the repository root:  python tests/golden/make_handbuilt_blocks.py
 
@@ -10,10 +10,12 @@ Q4_K blocks the 12 scale bytes were also derived by hand and are written below
 as literals; the script stops if its encoder disagrees with them.
 
 The expected weights are computed here from the stated fields with exact
-rational arithmetic (w = d*q for Q8_0, w = d*sc_j*q - dmin*m_j for Q4_K); they
-are closed forms by construction and do not come from the oracle or the GPU.
-The memra pages name these formats (memra README, model support table: Q8_0
-and Q4_K_M GGUF models) but print no block bytes, so no value here is theirs.
+rational arithmetic (w = d*q for Q8_0, w = d*sc_j*q - dmin*m_j for Q4_K,
+w = d*(ls_j - 32)*grid[q] for IQ4_XS); they are closed forms by construction
+and do not come from the oracle or the GPU. The memra pages name these formats
+(memra README, model support table: Q8_0, Q4_K_M and IQ4_XS GGUF models) but
+print no block bytes, so no value here is theirs. The IQ4_XS grid below is this
+script's own transcription of the public format's 16 values.
 """
 
 from __future__ import annotations
@@ -108,6 +110,48 @@ Q4_K_BLOCKS = [
 ]
 
 
+# ---------------------------------------------------------------- IQ4_XS
+
+IQ4_XS_GRID = [-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113]
+
+
+def pack_iq4_xs_scales(ls: list[int]) -> bytes:
+    """The 6 scale bytes (this script's own statement of the layout).
+
+    bytes 0..1: little-endian 16-bit H, bits 2j..2j+1 = bits 4..5 of ls_j
+    bytes 2..5: L[0..3], L[j // 2] holds bits 0..3 of ls_j (low nibble for even j)
+    """
+    assert len(ls) == 8 and all(0 <= v < 64 for v in ls)
+    h = 0
+    low = [0] * 4
+    for j, v in enumerate(ls):
+        h |= (v >> 4) << (2 * j)
+        low[j // 2] |= (v & 0xF) << (4 * (j % 2))
+    return bytes([h & 0xFF, h >> 8]) + bytes(low)
+
+
+def pack_iq4_indices(q: list[int]) -> bytes:
+    """Index bytes: byte 16j + i = q[32j + i] | q[32j + 16 + i] << 4."""
+    assert len(q) == 256 and all(0 <= v < 16 for v in q)
+    out = bytearray(128)
+    for j in range(8):
+        for i in range(16):
+            out[16 * j + i] = q[32 * j + i] | (q[32 * j + 16 + i] << 4)
+    return bytes(out)
+
+
+# (name, d_bits, ls[8], q[256], hand-derived scale bytes as hex)
+IQ4_XS_BLOCKS = [
+    ("grid_walk", 0x3C00, [33] * 8, [i % 16 for i in range(256)], "aaaa11111111"),
+    ("signed_scales", 0x3800, [32, 33, 31, 0, 63, 16, 48, 47], [(7 * i + 3) % 16 for i in range(256)],
+     "1ab7100f0ff0"),
+    ("zero_point_scale", 0x3C00, [32] * 8, [(11 * i + 5) % 16 for i in range(256)], "aaaa00000000"),
+    ("subnormal_d", 0x0001, [63, 0, 63, 0, 63, 0, 63, 0], [15 - i % 16 for i in range(256)], "33330f0f0f0f"),
+    ("position_code", 0x3C00, [34] * 8, [(5 * i + (i >> 4)) % 16 for i in range(256)], "aaaa22222222"),
+    ("negative_d", 0xBC00, [40, 24, 35, 29, 32, 60, 5, 50], [(3 * i) % 16 for i in range(256)], "66ce88d3c025"),
+]
+
+
 def main() -> None:
     q8 = []
     for name, d_bits, q in Q8_0_BLOCKS:
@@ -141,6 +185,24 @@ def main() -> None:
             "expect": [frac_to_hex(v) for v in expect],
         })
 
+    iq4 = []
+    for name, d_bits, ls, q, s_hex in IQ4_XS_BLOCKS:
+        s_bytes = pack_iq4_xs_scales(ls)
+        if s_bytes.hex() != s_hex:
+            raise SystemExit(f"{name}: encoder gives {s_bytes.hex()}, hand derivation says {s_hex}")
+        raw = bytes([d_bits & 0xFF, d_bits >> 8]) + s_bytes + pack_iq4_indices(q)
+        assert len(raw) == 136
+        d = fp16_value(d_bits)
+        expect = [d * (ls[i // 32] - 32) * IQ4_XS_GRID[q[i]] for i in range(256)]
+        iq4.append({
+            "name": name,
+            "d_bits": d_bits,
+            "ls": ls,
+            "q": q,
+            "hex": raw.hex(),
+            "expect": [frac_to_hex(v) for v in expect],
+        })
+
     note = ("Hand-built blocks with known values (closed forms by construction). "
             "Formats named on the memra README model support table (Q8_0, Q4_K_M GGUF); "
             "layouts are the public GGUF ones. Written by tests/golden/make_handbuilt_blocks.py.")
@@ -149,6 +211,10 @@ def main() -> None:
         f.write("\n")
     with open(os.path.join(HERE, "q4_k_handbuilt.json"), "w") as f:
         json.dump({"citation": note, "blocks": q4}, f, indent=1)
+        f.write("\n")
+    with open(os.path.join(HERE, "iq4_xs_handbuilt.json"), "w") as f:
+        json.dump({"citation": note.replace("(Q8_0, Q4_K_M GGUF)", "(Q8_0, Q4_K_M, IQ4_XS GGUF)"), "blocks": iq4},
+                  f, indent=1)
         f.write("\n")
 
 

@@ -1,4 +1,4 @@
-"""Pins for the oracle's block decoding (Q8_0, Q4_K) and scalar formats.
+"""Pins for the oracle's block decoding (Q8_0, Q4_K, IQ4_XS) and scalar formats.
 
 Everything here runs on the CPU. Each check ties the oracle to something other
 than itself: hand-built blocks whose values are known by construction
@@ -17,7 +17,8 @@ import oracle
 import synth
 
 sys.path.insert(0, os.path.join(os.path.dirname(__file__), "golden"))
-from make_handbuilt_blocks import pack_nibbles, pack_scales_mins  # noqa: E402
+from make_handbuilt_blocks import (  # noqa: E402
+    IQ4_XS_GRID, pack_iq4_indices, pack_iq4_xs_scales, pack_nibbles, pack_scales_mins)
 
 
 def _load(golden_dir, name):
@@ -262,3 +263,128 @@ def test_fp32_target_rounds_once():
     ulp = np.spacing(np.abs(w32)).astype(np.float64)
     assert np.all(err <= 0.5 * ulp)
     assert np.count_nonzero(err) > 0        # some weights really need the rounding
+
+
+# ---------------------------------------------------------------- IQ4_XS
+
+def test_iq4_xs_handbuilt_blocks(golden_dir):
+    for blk in _load(golden_dir, "iq4_xs_handbuilt.json"):
+        raw = bytes.fromhex(blk["hex"])
+        d, ls, q = oracle.iq4_xs_fields(raw, 1, 256)
+        assert list(ls[0, 0]) == blk["ls"], blk["name"]
+        assert list(q[0, 0]) == blk["q"], blk["name"]
+        assert d[0, 0] == oracle.fp16_bits_to_f64(np.array([blk["d_bits"]]))[0]
+        w = oracle.dequant_iq4_xs(raw, 1, 256)[0]
+        expect = np.array([float.fromhex(v) for v in blk["expect"]])
+        assert np.array_equal(w, expect), blk["name"]
+
+
+def test_iq4_xs_handbuilt_values_by_hand(golden_dir):
+    blocks = {b["name"]: b for b in _load(golden_dir, "iq4_xs_handbuilt.json")}
+    # d = 1, every scale 33 (weight scale 1): the weights walk the grid
+    w = oracle.dequant_iq4_xs(bytes.fromhex(blocks["grid_walk"]["hex"]), 1, 256)[0]
+    assert list(w[:16]) == [-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113]
+    # d = 0.5, weight scales 0, 1, -1, -32, 31, -16, 16, 15; at i = 32j the index (7i + 3) % 16
+    # is 3 (grid value -65) for every j, so the first weights are 0.5 * s * -65
+    w = oracle.dequant_iq4_xs(bytes.fromhex(blocks["signed_scales"]["hex"]), 1, 256)[0]
+    assert list(w[::32]) == [0.0, -32.5, 32.5, 1040.0, -1007.5, 520.0, -520.0, -487.5]
+    # a scale of 32 zeroes the whole block, whatever the indices
+    assert not oracle.dequant_iq4_xs(bytes.fromhex(blocks["zero_point_scale"]["hex"]), 1, 256).any()
+
+
+def test_iq4_xs_grid_shape():
+    g = np.asarray(oracle.IQ4_GRID)
+    assert g.shape == (16,) and np.all(np.diff(g) > 0)     # 16 distinct, increasing
+    assert g.min() == -127 and g.max() == 113              # the int8-range endpoints of the format
+    assert list(g) == IQ4_XS_GRID                           # the golden script's own transcription
+
+
+def test_iq4_xs_index_byte_locality():
+    raw = bytearray(synth.iq4_xs_weights(61, 1, 256))
+    base = oracle.dequant_iq4_xs(bytes(raw), 1, 256)[0]
+    _, ls, _ = oracle.iq4_xs_fields(bytes(raw), 1, 256)
+    for p in range(128):
+        j, i = divmod(p, 16)
+        for mask, weight in ((0x0F, 32 * j + i), (0xF0, 32 * j + 16 + i)):
+            mod = bytearray(raw)
+            mod[8 + p] ^= mask
+            w = oracle.dequant_iq4_xs(bytes(mod), 1, 256)[0]
+            changed = np.nonzero(w != base)[0]
+            if ls[0, 0, weight // 32] != 32 and base.any():
+                assert list(changed) == [weight], (p, mask)
+            else:
+                assert changed.size == 0
+
+
+def test_iq4_xs_scale_bit_locality():
+    # bit b of byte 2..7 belongs to exactly one sub-block scale: H bit 2j + t is bit 4 + t of
+    # ls_j; L[j // 2] bit 4 (j % 2) + t is bit t of ls_j
+    raw = bytearray(synth.iq4_xs_weights(62, 1, 256))
+    _, ls0, _ = oracle.iq4_xs_fields(bytes(raw), 1, 256)
+    for byte in range(6):
+        for bit in range(8):
+            mod = bytearray(raw)
+            mod[2 + byte] ^= 1 << bit
+            _, ls1, _ = oracle.iq4_xs_fields(bytes(mod), 1, 256)
+            diff = (ls1 - ls0)[0, 0]
+            if byte < 2:
+                hb = 8 * byte + bit
+                j, val = hb // 2, 1 << (4 + hb % 2)
+            else:
+                j, val = 2 * (byte - 2) + bit // 4, 1 << (bit % 4)
+            assert list(np.nonzero(diff)[0]) == [j], (byte, bit)
+            assert abs(diff[j]) == val, (byte, bit)
+
+
+def test_iq4_xs_pack_unpack_bijection():
+    rng = np.random.default_rng(5)
+    for j in range(8):
+        for v in range(64):
+            ls = list(rng.integers(0, 64, 8))
+            ls[j] = v
+            q = list(rng.integers(0, 16, 256))
+            raw = bytes([0, 0x3C]) + pack_iq4_xs_scales(ls) + pack_iq4_indices(q)
+            _, dls, dq = oracle.iq4_xs_fields(raw, 1, 256)
+            assert list(dls[0, 0]) == ls and list(dq[0, 0]) == q
+    raw = synth.iq4_xs_weights(63, 4, 768)
+    _, ls, q = oracle.iq4_xs_fields(raw, 4, 768)
+    blocks = raw.reshape(-1, 136)
+    for b in range(blocks.shape[0]):
+        n, t = divmod(b, 3)
+        assert pack_iq4_xs_scales(list(ls[n, t])) == bytes(blocks[b, 2:8])
+        assert pack_iq4_indices(list(q[n, t])) == bytes(blocks[b, 8:])
+
+
+def test_iq4_xs_requant_round_trip():
+    # nearest-grid requantisation of the exact weights recovers every index (grid values are distinct)
+    raw = synth.iq4_xs_weights(64, 16, 512)
+    d, ls, q = oracle.iq4_xs_fields(raw, 16, 512)
+    w = oracle.dequant_iq4_xs(raw, 16, 512).reshape(16, 2, 8, 32)
+    scale = d[:, :, None] * (ls - 32)
+    ok = scale != 0
+    t = w / np.where(ok, scale, 1.0)[..., None]
+    q_back = np.argmin(np.abs(t[..., None] - np.asarray(oracle.IQ4_GRID)[None, None, None, None, :]), axis=-1)
+    assert np.array_equal(q_back[ok], q.reshape(16, 2, 8, 32)[ok])
+
+
+def test_iq4_xs_weights_are_exact_in_fp32():
+    raw = synth.iq4_xs_weights(65, 16, 1024)
+    w = oracle.dequant_iq4_xs(raw, 16, 1024)
+    assert np.array_equal(w, w.astype(np.float32).astype(np.float64))
+    scaled = w * 2.0 ** 24
+    assert np.array_equal(scaled, np.rint(scaled))
+
+
+def test_iq4_xs_generator_distributions():
+    raw = synth.iq4_xs_weights(66, 256, 2048)
+    d, ls, q = oracle.iq4_xs_fields(raw, 256, 2048)
+    assert ls.min() == 0 and ls.max() == 63 and q.min() == 0 and q.max() == 15
+    assert abs(ls.mean() - 31.5) < 0.5 and abs(q.mean() - 7.5) < 0.05
+    assert abs(d.mean() / (0.0005 * np.sqrt(2 / np.pi)) - 1) < 0.02
+
+
+def test_iq4_xs_rejects_wrong_sizes():
+    with pytest.raises(ValueError):
+        oracle.dequant_iq4_xs(bytes(135), 1, 256)
+    with pytest.raises(ValueError):
+        oracle.dequant_iq4_xs(bytes(136), 1, 128)

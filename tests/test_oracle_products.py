@@ -54,6 +54,19 @@ def test_q8_0_gemv_matches_exact_rational(n_rows, k, m):
             assert abs(Fraction(float(y[r, n])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
 
 
+@pytest.mark.parametrize("n_rows,k,m", [(3, 256, 1), (2, 512, 4)])
+def test_iq4_xs_gemv_matches_exact_rational(n_rows, k, m):
+    raw = synth.iq4_xs_weights(71 + m, n_rows, k)
+    x = synth.bf16_normal(72 + m, (m, k))
+    y = oracle.qmv_iq4_xs(raw, x, n_rows, k)
+    exact = _exact_dot_rows(oracle.dequant_iq4_xs(raw, n_rows, k), oracle.bf16_bits_to_f64(x))
+    assert y.shape == (m, n_rows)
+    for r in range(m):
+        for n in range(n_rows):
+            e = exact[r][n]
+            assert abs(Fraction(float(y[r, n])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
+
+
 def test_gemv_unit_vector_selects_a_column():
     n_rows, k = 7, 512
     raw = synth.q4_k_weights(61, n_rows, k)
