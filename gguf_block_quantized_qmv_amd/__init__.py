@@ -14,9 +14,9 @@ import os
 
 __all__ = [
     "QmvError", "lib", "LIB_PATH", "version",
-    "qmv_q8_0", "qmv_q4_k", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmm_q4_k_prefill_workspace", "qmm_q4_k_prefill",
-    "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16", "qmv_dequant_q8_0_f32",
-    "q4_k_bytes", "q8_0_bytes", "EXPORTS",
+    "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmm_q4_k_prefill_workspace",
+    "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16", "qmv_dequant_q8_0_f32",
+    "qmv_dequant_iq4_xs_f32", "q4_k_bytes", "q8_0_bytes", "iq4_xs_bytes", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmv.so")
@@ -30,6 +30,7 @@ EXPORTS = {
     "qmv_last_error": (ctypes.c_char_p, []),
     "qmv_q8_0": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "qmv_q4_k": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
+    "qmv_iq4_xs": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "qmv_q4_k_moe_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "qmv_q4_k_moe": (_c_int, [_vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
                               _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
@@ -38,6 +39,7 @@ EXPORTS = {
     "qmv_dequant_q4_k_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
     "qmv_dequant_q4_k_bf16": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
     "qmv_dequant_q8_0_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
+    "qmv_dequant_iq4_xs_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
 }
 
 
@@ -245,3 +247,32 @@ def qmv_dequant_q8_0_f32(w, n: int, k: int, out=None, stream=None):
     _dev(out, "out", (torch.float32,))
     _check(lib.qmv_dequant_q8_0_f32(_ptr(w), _nbytes(w), _ptr(out), n, k, _stream(stream)), "qmv_dequant_q8_0_f32")
     return out
+
+
+def qmv_iq4_xs(w, x, n: int, k: int, y=None, stream=None):
+    """y[m, n] = x[m, k] @ dequant_iq4_xs(w)^T for m = 1..4 bf16 rows (fp32 out)."""
+    torch = _torch()
+    _dev(w, "w", (torch.uint8,))
+    _dev(x, "x", _bf16_types())
+    m = x.shape[0] if x.dim() == 2 else 1
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(y, "y", (torch.float32,))
+    _check(lib.qmv_iq4_xs(_ptr(w), _nbytes(w), _ptr(x), _ptr(y), m, n, k, _stream(stream)), "qmv_iq4_xs")
+    return y
+
+
+def qmv_dequant_iq4_xs_f32(w, n: int, k: int, out=None, stream=None):
+    torch = _torch()
+    _dev(w, "w", (torch.uint8,))
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    _dev(out, "out", (torch.float32,))
+    _check(lib.qmv_dequant_iq4_xs_f32(_ptr(w), _nbytes(w), _ptr(out), n, k, _stream(stream)),
+           "qmv_dequant_iq4_xs_f32")
+    return out
+
+
+def iq4_xs_bytes(n: int, k: int) -> int:
+    """Byte size of an n x k IQ4_XS matrix (136-byte blocks of 256 weights along k)."""
+    return n * (k // 256) * 136

@@ -107,6 +107,18 @@ int qmv_q4_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, in
   return qmv::launch_q4_k_gemv(w, x_bf16, y, m, n, k, stream);
 }
 
+int qmv_iq4_xs(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, int m, int n, int k, void *stream) {
+  if (!w || !x_bf16 || !y) return QMV_ERR_NULL;
+  if (m < 1 || m > QMV_MAX_ROWS) return QMV_ERR_RANGE;
+  int rc = check_matrix(w, w_bytes, n, k, 256, 136, 8);
+  if (rc) return rc;
+  if (!qmv::iq4xs_fits_lds(m, k)) return QMV_ERR_RANGE;
+  if (!aligned(x_bf16, 16) || !aligned(y, 4)) return QMV_ERR_ALIGN;
+  const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 4;
+  if (overlap(y, yb, w, w_bytes) || overlap(y, yb, x_bf16, xb)) return QMV_ERR_ALIAS;
+  return qmv::launch_iq4_xs_gemv(w, x_bf16, y, m, n, k, stream);
+}
+
 size_t qmv_q4_k_moe_workspace(int t, int hidden, int ffn, int n_experts, int top_k) {
   if (t < 1 || t > QMV_MOE_MAX_TOKENS || n_experts < 1 || n_experts > QMV_MOE_MAX_EXPERTS || top_k < 1 ||
       top_k > QMV_MOE_MAX_TOP_K || top_k > n_experts || hidden <= 0 || ffn <= 0 || hidden % 256 || ffn % 256 ||
@@ -191,6 +203,15 @@ int qmv_dequant_q4_k_bf16(const void *w, size_t w_bytes, uint16_t *out, int n, i
   if (!aligned(out, 16)) return QMV_ERR_ALIGN;
   if (overlap(out, (size_t)n * k * 2, w, w_bytes)) return QMV_ERR_ALIAS;
   return qmv::launch_dequant_q4_k(w, out, true, n, k, stream);
+}
+
+int qmv_dequant_iq4_xs_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream) {
+  if (!w || !out) return QMV_ERR_NULL;
+  int rc = check_matrix(w, w_bytes, n, k, 256, 136, 8);
+  if (rc) return rc;
+  if (!aligned(out, 16)) return QMV_ERR_ALIGN;
+  if (overlap(out, (size_t)n * k * 4, w, w_bytes)) return QMV_ERR_ALIAS;
+  return qmv::launch_dequant_iq4_xs(w, out, n, k, stream);
 }
 
 int qmv_dequant_q8_0_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream) {

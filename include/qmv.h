@@ -116,6 +116,27 @@ int qmv_q4_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
              int m, int n, int k, void *stream);
 
 /*
+ * IQ4_XS matrix times bf16 activation rows (decode m=1, verify m=2..4).
+ *   w       [n rows][k/256 blocks] IQ4_XS (136-byte super-blocks of 256 weights:
+ *           fp16 d, 16 bits holding the top two bits of eight 6-bit sub-block
+ *           scales, 4 bytes holding their low four bits, 128 bytes of 4-bit
+ *           indices into the format's 16-value grid), 8-byte aligned;
+ *           w_bytes == n*(k/256)*136
+ *   x_bf16  bf16 bits [m][k] row-major, 16-byte aligned
+ *   y       fp32 [m][n] row-major, 4-byte aligned
+ *   1 <= m <= QMV_MAX_ROWS, n >= 1, k >= 256 and k % 256 == 0,
+ *   1024 + m*((k/32)*64 + (k/128)*16) <= QMV_LDS_X_BYTES (m=4 allows k up to 18944).
+ * y[r][i] = sum_k w[i][k] * x[r][k], w = d * (ls_j - 32) * grid[index], with
+ * the weights and bf16 inputs exact and fp32 accumulation. Row r of y is
+ * bit-identical for every m.
+ * Workload: the memra README model support table's 35B-A3B MoE in IQ4_XS and
+ * the memra-bench card's UD-IQ4_XS draft of it (the expert and attention
+ * matrices of that model).
+ */
+int qmv_iq4_xs(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
+               int m, int n, int k, void *stream);
+
+/*
  * Workspace bytes qmv_q4_k_moe needs for t tokens (0 if an argument is out of
  * range). The caller allocates it in device memory, 256-byte aligned.
  */
@@ -187,11 +208,13 @@ int qmm_q4_k_prefill(const void *w, size_t w_bytes, const uint16_t *x_bf16, floa
  * Dequantization to dense matrices (the bit-exact gate of the decode kernels).
  *   out  fp32 [n][k] or bf16 bits [n][k], 16-byte aligned
  * fp32: each weight is the exact block value rounded once to fp32 (nearest
- * even). bf16: that fp32 value rounded to bf16 (nearest even).
+ * even; Q8_0 and IQ4_XS weights are exact in fp32). bf16: that fp32 value
+ * rounded to bf16 (nearest even). IQ4_XS: w is 8-byte aligned, 136-byte blocks.
  */
 int qmv_dequant_q4_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 int qmv_dequant_q4_k_bf16(const void *w, size_t w_bytes, uint16_t *out, int n, int k, void *stream);
 int qmv_dequant_q8_0_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
+int qmv_dequant_iq4_xs_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,8 @@ def _header_functions():
 
 def test_header_lists_the_expected_entry_points():
     assert _header_functions() == sorted([
-        "qmv_version", "qmv_strerror", "qmv_last_error", "qmv_q8_0", "qmv_q4_k", "qmv_q4_k_moe_workspace", "qmv_q4_k_moe",
+        "qmv_version", "qmv_strerror", "qmv_last_error", "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe_workspace",
+        "qmv_q4_k_moe", "qmv_dequant_iq4_xs_f32",
         "qmm_q4_k_prefill_workspace", "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16",
         "qmv_dequant_q8_0_f32"])
 
@@ -78,6 +79,28 @@ def test_q4_k_every_truncated_or_padded_size_is_an_error():
         assert q4k(nbytes=b, n=n, k=k) == SIZE, b
     assert q4k(nbytes=full + 1, n=n, k=k) == SIZE
     assert q4k(nbytes=2 * full, n=n, k=k) == SIZE
+
+
+def iq4(w=W, nbytes=None, x=X, y=Y, m=1, n=2, k=256):
+    nbytes = q.iq4_xs_bytes(n, k) if nbytes is None else nbytes
+    return L.qmv_iq4_xs(V(w), nbytes, V(x), V(y), m, n, k, None)
+
+
+def test_iq4_xs_validation():
+    assert iq4(w=0) == NULL and iq4(x=0) == NULL and iq4(y=0) == NULL
+    assert iq4(m=0) == RANGE and iq4(m=5) == RANGE
+    assert iq4(n=0) == SHAPE and iq4(k=0) == SHAPE and iq4(k=255) == SHAPE and iq4(k=384) == SHAPE
+    assert iq4(w=W + 4) == ALIGN and iq4(x=X + 8) == ALIGN and iq4(y=Y + 2) == ALIGN
+    assert iq4(w=W + 8) != ALIGN                          # 136-byte blocks: 8-byte alignment suffices
+    assert iq4(m=4, k=19200) == RANGE and iq4(m=3, k=19200) != RANGE   # LDS: m=4 stops at k = 18944
+    assert iq4(y=W + 64) == ALIAS
+    full = q.iq4_xs_bytes(2, 512)
+    for b in list(range(full)) + [full + 1, full + 136]:
+        assert iq4(nbytes=b, k=512) == SIZE, b
+    nb = q.iq4_xs_bytes(2, 256)
+    fn = L.qmv_dequant_iq4_xs_f32
+    assert fn(V(0), nb, V(Y), 2, 256, None) == NULL and fn(V(W), nb - 1, V(Y), 2, 256, None) == SIZE
+    assert fn(V(W), nb, V(Y + 8), 2, 256, None) == ALIGN and fn(V(W), nb, V(W), 2, 256, None) == ALIAS
 
 
 def test_q8_0_validation():
