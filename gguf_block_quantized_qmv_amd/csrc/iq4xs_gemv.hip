@@ -21,12 +21,12 @@
 // per activation row and the scale decode; the sub-block sum is scaled by
 // d * (ls - 32), which is exact in fp32, and accumulated in fp32.
 //
-// Work mapping: G lanes per W row (16, or 32 for long rows), 256 / G rows per
-// workgroup; lane l of a row takes the row's sub-blocks l, l + G, ... Loads
-// run kDepth units ahead through a register ring; they are unconditional
-// (units past the row re-read the row's first sub-block with a zero scale) and
-// the unit loop is unrolled by kDepth, so every wait is exact. Row r of the
-// output is computed by the same instruction sequence for every M.
+// Work mapping: G lanes per W row (16, or 32 for long rows), T / G rows per
+// workgroup of T threads; lane l of a row takes the row's sub-blocks l, l + G,
+// ... Loads run kDepth units ahead through a register ring; they are
+// unconditional (units past the row re-read the row's first sub-block with a
+// zero scale) and the unit loop is unrolled by kDepth, so every wait is exact.
+// Row r of the output is computed by the same instruction sequence for every M.
 #include "qmv_device.h"
 #include "qmv_internal.h"
 #include "../../include/qmv.h"
@@ -35,8 +35,7 @@ namespace qmv {
 namespace {
 
 constexpr int kIQ4XSBlockBytes = 136;
-constexpr int kThreads = 256;
-constexpr int kDepth = 4;          // units of loads in flight per lane
+constexpr int kDepth = 2;          // units of loads in flight per lane
 constexpr int kTableEntries = 256;  // LDS table: one bf16 pair per index byte
 
 // The format's 16 grid values, packed as signed bytes (index 4w + b in byte b of word w).
@@ -73,6 +72,7 @@ __device__ __forceinline__ void interleave(const uint4 g0, const uint4 g1, const
 }
 
 constexpr int kStageSub = 2;   // sub-blocks per thread per staging round trip
+constexpr size_t kLdsPerCu = 160 * 1024;
 
 // One unit's global data for a lane: the block's 8 header bytes and the
 // sub-block's 16 index bytes (blocks are only 8-byte aligned: 8-byte loads).
@@ -80,102 +80,163 @@ struct Unit {
   uint2 hdr, q0, q1;
 };
 
-__device__ __forceinline__ void load_unit(const uint8_t *__restrict__ row_ptr, const int u, Unit &r) {
-  const uint8_t *bp = row_ptr + (size_t)(u >> 3) * kIQ4XSBlockBytes;
-  const uint8_t *qp = bp + 8 + 16 * (u & 7);
+// bp: the super-block; qoff = 8 + 16 j: the lane's sub-block j.
+__device__ __forceinline__ void load_unit(const uint8_t *__restrict__ bp, const int qoff, Unit &r) {
   r.hdr = *reinterpret_cast<const uint2 *>(bp);
-  r.q0 = *reinterpret_cast<const uint2 *>(qp);
-  r.q1 = *reinterpret_cast<const uint2 *>(qp + 8);
+  r.q0 = *reinterpret_cast<const uint2 *>(bp + qoff);
+  r.q1 = *reinterpret_cast<const uint2 *>(bp + qoff + 8);
 }
 
-// dot2 of the four table entries of index word w with four activation pairs.
-__device__ __forceinline__ float word_dot(const uint32_t *__restrict__ tbl, const uint32_t w, const uint4 xp,
-                                          float s) {
-  const bf16x2 e0 = __builtin_bit_cast(bf16x2, tbl[w & 0xFF]);
-  const bf16x2 e1 = __builtin_bit_cast(bf16x2, tbl[(w >> 8) & 0xFF]);
-  const bf16x2 e2 = __builtin_bit_cast(bf16x2, tbl[(w >> 16) & 0xFF]);
-  const bf16x2 e3 = __builtin_bit_cast(bf16x2, tbl[w >> 24]);
-  s = __builtin_amdgcn_fdot2_f32_bf16(e0, __builtin_bit_cast(bf16x2, xp.x), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(e1, __builtin_bit_cast(bf16x2, xp.y), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(e2, __builtin_bit_cast(bf16x2, xp.z), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(e3, __builtin_bit_cast(bf16x2, xp.w), s, false);
+// Byte B of w times 4 (the table's byte offset for that index byte) in one
+// instruction: the shift reads the byte through an SDWA source select.
+template <int B>
+__device__ __forceinline__ uint32_t byte_x4(const uint32_t w) {
+  uint32_t r;
+  if constexpr (B == 0)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(r) : "v"(w));
+  else if constexpr (B == 1)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "v"(w));
+  else if constexpr (B == 2)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(r) : "v"(w));
+  else
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(r) : "v"(w));
+  return r;
+}
+
+template <int B>
+__device__ __forceinline__ bf16x2 table_pair(const uint8_t *__restrict__ tbl_bytes, const uint32_t w) {
+  return __builtin_bit_cast(bf16x2, *reinterpret_cast<const uint32_t *>(tbl_bytes + byte_x4<B>(w)));
+}
+
+// The four table entries of index word w (four index bytes).
+struct Pairs {
+  bf16x2 e[4];
+};
+
+__device__ __forceinline__ Pairs word_pairs(const uint8_t *__restrict__ tbl_bytes, const uint32_t w) {
+  return Pairs{{table_pair<0>(tbl_bytes, w), table_pair<1>(tbl_bytes, w), table_pair<2>(tbl_bytes, w),
+                table_pair<3>(tbl_bytes, w)}};
+}
+
+__device__ __forceinline__ float pairs_dot(const Pairs &p, const uint4 xp, float s) {
+  s = __builtin_amdgcn_fdot2_f32_bf16(p.e[0], __builtin_bit_cast(bf16x2, xp.x), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(p.e[1], __builtin_bit_cast(bf16x2, xp.y), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(p.e[2], __builtin_bit_cast(bf16x2, xp.z), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(p.e[3], __builtin_bit_cast(bf16x2, xp.w), s, false);
   return s;
 }
 
-template <int M, int G>
-__global__ __launch_bounds__(kThreads) void iq4xs_gemv_kernel(const uint8_t *__restrict__ w,
-                                                              const uint16_t *__restrict__ x,
-                                                              float *__restrict__ y, const int n, const int k) {
-  extern __shared__ uint4 lds[];
-  uint32_t *tbl = reinterpret_cast<uint32_t *>(lds);
-  uint4 *xs = lds + kTableEntries / 4;
-  const int tid = threadIdx.x;
-  const int nblk = k >> 8, nsub = nblk * 8, rg = row_granules(nsub);
-  const int row = blockIdx.x * (kThreads / G) + tid / G;
-  const int l = tid % G;
-  const uint8_t *row_ptr = w + (size_t)(row < n ? row : 0) * (size_t)nblk * kIQ4XSBlockBytes;
-  const int nunits = (nsub + G - 1) / G;              // units of this lane, the last may be past the row
-  const int nslots = (nunits + kDepth - 1) / kDepth * kDepth;
-
-  // the first weights are requested before anything else
-  Unit ring[kDepth];
+// Stage sub-block s of activation row r, pair-interleaved, at xs[r * rg + x_slot(s)].
+__device__ __forceinline__ void stage_one(const uint4 *__restrict__ xg, uint4 *__restrict__ xs, const int t,
+                                          const int nsub, const int k, const int rg) {
+  const int r = t / nsub, s = t - r * nsub;
+  const uint4 *src = xg + (size_t)r * (k >> 3) + 4 * s;
+  uint4 o[4];
+  interleave(src[0], src[1], src[2], src[3], o);
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) {
-    const int u = l + G * d;
-    load_unit(row_ptr, u < nsub && d < nunits ? u : 0, ring[d]);
-  }
+  for (int q = 0; q < 4; ++q) xs[r * rg + x_slot(s) + q] = o[q];
+}
 
-  // table and activations
-  tbl[tid] = grid_bf16((uint32_t)tid & 15u) | (grid_bf16((uint32_t)tid >> 4) << 16);
-  const uint4 *xg = reinterpret_cast<const uint4 *>(x);
-  const int total = M * nsub;   // sub-blocks to stage
-  for (int base = 0; base < total; base += kStageSub * kThreads) {
+// All M * nsub sub-blocks of the activations, kStageSub per thread per round
+// trip; only the last round is partial (each staged sub-block is read once).
+template <int M, int T>
+__device__ __forceinline__ void stage_activations(const uint4 *__restrict__ xg, uint4 *__restrict__ xs,
+                                                  const int tid, const int nsub, const int k, const int rg) {
+  const int total = M * nsub;
+  int base = 0;
+  for (; base + kStageSub * T <= total; base += kStageSub * T) {
     uint4 g[kStageSub][4];
 #pragma unroll
     for (int i = 0; i < kStageSub; ++i) {
-      const int t0 = base + tid + i * kThreads, t = t0 < total ? t0 : 0;   // a clamped lane rewrites sub-block 0
-      const int r = t / nsub, s = t - r * nsub;
+      const int t = base + tid + i * T, r = t / nsub, s = t - r * nsub;
 #pragma unroll
       for (int q = 0; q < 4; ++q) g[i][q] = xg[(size_t)r * (k >> 3) + 4 * s + q];
     }
 #pragma unroll
     for (int i = 0; i < kStageSub; ++i) {
-      const int t0 = base + tid + i * kThreads, t = t0 < total ? t0 : 0;
-      const int r = t / nsub, s = t - r * nsub;
+      const int t = base + tid + i * T, r = t / nsub, s = t - r * nsub;
       uint4 o[4];
       interleave(g[i][0], g[i][1], g[i][2], g[i][3], o);
 #pragma unroll
       for (int q = 0; q < 4; ++q) xs[r * rg + x_slot(s) + q] = o[q];
     }
   }
+  for (int t = base + tid; t < total; t += T) stage_one(xg, xs, t, nsub, k, rg);
+}
+
+template <int M, int G, int T>
+__global__ __launch_bounds__(T) void iq4xs_gemv_kernel(const uint8_t *__restrict__ w,
+                                                       const uint16_t *__restrict__ x,
+                                                       float *__restrict__ y, const int n, const int k) {
+  static_assert(G % 8 == 0, "a lane's sub-block index inside the super-block must stay fixed");
+  // the table is static LDS, so its address is a compile-time constant and the
+  // scaled index byte is the whole read address
+  __shared__ uint32_t tbl[kTableEntries];
+  extern __shared__ uint4 xs[];
+  const uint8_t *tbl_bytes = reinterpret_cast<const uint8_t *>(tbl);
+  const int tid = threadIdx.x;
+  const int nblk = k >> 8, nsub = nblk * 8, rg = row_granules(nsub);
+  const int row = blockIdx.x * (T / G) + tid / G;
+  const int l = tid % G;
+  const uint8_t *row_ptr = w + (size_t)(row < n ? row : 0) * (size_t)nblk * kIQ4XSBlockBytes;
+  // Lane l takes sub-blocks u = l + G t: super-block (l >> 3) + (G / 8) t, sub-block j = l & 7.
+  const int j = l & 7, qoff = 8 + 16 * j;
+  const uint8_t *lane_ptr = row_ptr + (size_t)(l >> 3) * kIQ4XSBlockBytes;
+  constexpr int kUnitBytes = (G / 8) * kIQ4XSBlockBytes;
+  const int nlive = l < nsub ? (nsub - l + G - 1) / G : 0;   // live units of this lane
+  const int nmax = (nsub + G - 1) / G;                        // live units of lane 0
+  const int nslots = (nmax + kDepth - 1) / kDepth * kDepth;
+  // activation granule of unit t: x_slot(l + G t) = x_slot(l) + t * (4 G + G / 4)
+  constexpr int kXStride = 4 * G + G / 4;
+  const int x_l = x_slot(l < nsub ? l : 0);
+
+  // the first weights are requested before anything else; a unit past the
+  // lane's last re-reads sub-block j of the row's first super-block
+  Unit ring[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    load_unit(d < nlive ? lane_ptr + (size_t)d * kUnitBytes : row_ptr, qoff, ring[d]);
+
+  // table and activations
+  if (tid < kTableEntries) tbl[tid] = grid_bf16((uint32_t)tid & 15u) | (grid_bf16((uint32_t)tid >> 4) << 16);
+  const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+  stage_activations<M, T>(xg, xs, tid, nsub, k, rg);
   __syncthreads();
 
+  const int sh_lo = 4 * j, sh_hi = 16 + 2 * j;
   float acc[M];
 #pragma unroll
   for (int r = 0; r < M; ++r) acc[r] = 0.0f;
   for (int t0 = 0; t0 < nslots; t0 += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-      const int t = t0 + d, u = l + G * t;
-      const bool live = u < nsub;
-      const Unit cur = ring[d];
+      const int t = t0 + d;
+      const bool live = t < nlive;
+      const Unit &cur = ring[d];
+      // the slot's data is consumed (scale decoded, table reads issued) before
+      // the slot is refilled, so the refill can land in the same registers
+      const uint32_t ls = ((cur.hdr.y >> sh_lo) & 15u) | (((cur.hdr.x >> sh_hi) & 3u) << 4);
+      const float dl_raw = fp16_bits_to_f32(cur.hdr.x & 0xFFFFu) * (float)((int)ls - 32);
+      const float dl = live ? dl_raw : 0.0f;
+      const int xg0 = live ? x_l + t * kXStride : x_l;
+      const Pairs p0 = word_pairs(tbl_bytes, cur.q0.x), p1 = word_pairs(tbl_bytes, cur.q0.y);
+      const Pairs p2 = word_pairs(tbl_bytes, cur.q1.x), p3 = word_pairs(tbl_bytes, cur.q1.y);
       // refill the slot kDepth units ahead (clamped, never guarded)
       {
-        const int un = u + G * kDepth;
-        load_unit(row_ptr, un < nsub ? un : 0, ring[d]);
+        const int tn = t + kDepth;
+        load_unit(tn < nlive ? lane_ptr + (size_t)tn * kUnitBytes : row_ptr, qoff, ring[d]);
       }
-      const int j = u & 7;
-      const uint32_t ls = ((cur.hdr.y >> (4 * j)) & 15u) | (((cur.hdr.x >> (16 + 2 * j)) & 3u) << 4);
-      const float dl = live ? fp16_bits_to_f32(cur.hdr.x & 0xFFFFu) * (float)((int)ls - 32) : 0.0f;
-      const int s = live ? u : 0;
 #pragma unroll
       for (int r = 0; r < M; ++r) {
-        const uint4 *xp = xs + r * rg + x_slot(s);
-        float s0 = 0.0f, s1 = 0.0f;
-        s0 = word_dot(tbl, cur.q0.x, xp[0], s0);
-        s1 = word_dot(tbl, cur.q0.y, xp[1], s1);
-        s0 = word_dot(tbl, cur.q1.x, xp[2], s0);
-        s1 = word_dot(tbl, cur.q1.y, xp[3], s1);
+        const uint4 *xp = xs + r * rg + xg0;
+        float s0 = pairs_dot(p0, xp[0], 0.0f);
+        float s1 = pairs_dot(p1, xp[1], 0.0f);
+        s0 = pairs_dot(p2, xp[2], s0);
+        s1 = pairs_dot(p3, xp[3], s1);
         acc[r] = __builtin_fmaf(dl, s0 + s1, acc[r]);
       }
     }
@@ -219,26 +280,30 @@ __global__ __launch_bounds__(256) void iq4xs_dequant_kernel(const uint8_t *__res
   }
 }
 
-size_t gemv_lds(int m, int k) {
-  return (size_t)kTableEntries * 4 + (size_t)m * row_granules((k >> 8) * 8) * 16;
-}
+// dynamic LDS of the GEMV: the staged activations (the table is static, 1 KiB)
+size_t gemv_dyn_lds(int m, int k) { return (size_t)m * row_granules((k >> 8) * 8) * 16; }
+size_t gemv_lds(int m, int k) { return (size_t)kTableEntries * 4 + gemv_dyn_lds(m, k); }
 
-template <int M, int G>
-int launch_mg(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t s) {
+template <int M, int G, int T>
+int launch_mgt(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t s) {
   static std::atomic<size_t> granted{0};
-  const size_t lds = gemv_lds(M, k);
-  if (allow_dynamic_lds(reinterpret_cast<const void *>(&iq4xs_gemv_kernel<M, G>), lds, granted,
+  const size_t lds = gemv_dyn_lds(M, k);
+  if (allow_dynamic_lds(reinterpret_cast<const void *>(&iq4xs_gemv_kernel<M, G, T>), lds, granted,
                         "iq4xs_gemv_kernel lds"))
     return QMV_ERR_HIP;
-  const int rows = kThreads / G;
-  return launch_kernel("iq4xs_gemv_kernel", iq4xs_gemv_kernel<M, G>, dim3((unsigned)((n + rows - 1) / rows)),
-                       dim3(kThreads), lds, s, static_cast<const uint8_t *>(w), x, y, n, k);
+  constexpr int rows = T / G;
+  return launch_kernel("iq4xs_gemv_kernel", iq4xs_gemv_kernel<M, G, T>, dim3((unsigned)((n + rows - 1) / rows)),
+                       dim3(T), lds, s, static_cast<const uint8_t *>(w), x, y, n, k);
 }
 
 template <int M>
 int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t s) {
-  // long rows take 32 lanes (more independent loads per row, fewer rows per workgroup)
-  return k > 8192 ? launch_mg<M, 32>(w, x, y, n, k, s) : launch_mg<M, 16>(w, x, y, n, k, s);
+  // Long rows take 32 lanes (more independent loads per row, fewer rows per
+  // workgroup). Once the staged activations leave room for a single workgroup
+  // per CU, that workgroup takes 512 threads, so a CU still holds 8 waves.
+  if (k <= 8192) return launch_mgt<M, 16, 256>(w, x, y, n, k, s);
+  if (2 * gemv_lds(M, k) > kLdsPerCu) return launch_mgt<M, 32, 512>(w, x, y, n, k, s);
+  return launch_mgt<M, 32, 256>(w, x, y, n, k, s);
 }
 
 }  // namespace
