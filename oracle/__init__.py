@@ -27,6 +27,7 @@ from .gguf_oracle import (  # noqa: F401
     gather_pairs,
     gemv,
     iq4_xs_fields,
+    moe_iq4_xs,
     moe_q4_k,
     prefill_q4_k,
     q4_k_fields,

@@ -335,21 +335,18 @@ def silu(g):
     return g / (1.0 + np.exp(-g))
 
 
-def expert_matrix(bank_raw, expert: int, n_rows: int, k: int) -> np.ndarray:
-    """Bytes of one expert's matrix inside a bank (experts stored back to back)."""
+def expert_matrix(bank_raw, expert: int, n_rows: int, k: int, block_bytes: int = Q4_K_BLOCK_BYTES) -> np.ndarray:
+    """Bytes of one expert's matrix inside a bank (experts stored back to back).
+
+    block_bytes: bytes per 256-weight super-block (144 for Q4_K, 136 for IQ4_XS).
+    """
     b = _as_bytes(bank_raw)
-    size = n_rows * (k // Q4_K_BLOCK_WEIGHTS) * Q4_K_BLOCK_BYTES
+    size = n_rows * (k // Q4_K_BLOCK_WEIGHTS) * block_bytes
     return b[expert * size:(expert + 1) * size]
 
 
-def moe_q4_k(gate_raw, up_raw, down_raw, logits, x_bf16_bits, hidden: int, ffn: int,
-             n_experts: int, top_k: int):
-    """Routed-expert FFN for each token t.
-
-    y_t = sum_j r_j * W_down[e_j] @ (silu(W_gate[e_j] @ x_t) * (W_up[e_j] @ x_t)),
-    with (e_j, r_j) from route_top_k and the sum taken in rank order j.
-    Returns (y float64 [T, hidden], ids int32 [T, k], weights float64 [T, k]).
-    """
+def _moe(dequant, block_bytes: int, gate_raw, up_raw, down_raw, logits, x_bf16_bits, hidden: int, ffn: int,
+         n_experts: int, top_k: int):
     x = bf16_bits_to_f64(np.atleast_2d(x_bf16_bits))
     t_count = x.shape[0]
     ids, wts = route_top_k(logits, top_k)
@@ -362,14 +359,34 @@ def moe_q4_k(gate_raw, up_raw, down_raw, logits, x_bf16_bits, hidden: int, ffn: 
             e = int(ids[t, j])
             if e not in cache:
                 cache[e] = (
-                    dequant_q4_k(expert_matrix(gate_raw, e, ffn, hidden), ffn, hidden),
-                    dequant_q4_k(expert_matrix(up_raw, e, ffn, hidden), ffn, hidden),
-                    dequant_q4_k(expert_matrix(down_raw, e, hidden, ffn), hidden, ffn),
+                    dequant(expert_matrix(gate_raw, e, ffn, hidden, block_bytes), ffn, hidden),
+                    dequant(expert_matrix(up_raw, e, ffn, hidden, block_bytes), ffn, hidden),
+                    dequant(expert_matrix(down_raw, e, hidden, ffn, block_bytes), hidden, ffn),
                 )
             wg, wu, wd = cache[e]
             h = silu(wg @ x[t]) * (wu @ x[t])
             y[t] += wts[t, j] * (wd @ h)
     return y, ids, wts
+
+
+def moe_q4_k(gate_raw, up_raw, down_raw, logits, x_bf16_bits, hidden: int, ffn: int,
+             n_experts: int, top_k: int):
+    """Routed-expert FFN for each token t, Q4_K experts.
+
+    y_t = sum_j r_j * W_down[e_j] @ (silu(W_gate[e_j] @ x_t) * (W_up[e_j] @ x_t)),
+    with (e_j, r_j) from route_top_k and the sum taken in rank order j.
+    Returns (y float64 [T, hidden], ids int32 [T, k], weights float64 [T, k]).
+    """
+    return _moe(dequant_q4_k, Q4_K_BLOCK_BYTES, gate_raw, up_raw, down_raw, logits, x_bf16_bits, hidden, ffn,
+                n_experts, top_k)
+
+
+def moe_iq4_xs(gate_raw, up_raw, down_raw, logits, x_bf16_bits, hidden: int, ffn: int,
+               n_experts: int, top_k: int):
+    """The same routed-expert FFN with IQ4_XS experts (the format the memra README's
+    model support table lists for its 35B-A3B MoE); banks of 136-byte blocks."""
+    return _moe(dequant_iq4_xs, IQ4_XS_BLOCK_BYTES, gate_raw, up_raw, down_raw, logits, x_bf16_bits, hidden, ffn,
+                n_experts, top_k)
 
 
 # ----------------------------------------------------------------------------

@@ -33,6 +33,7 @@ __all__ = [
     "bf16_normal",
     "f32_normal",
     "moe_bank",
+    "moe_bank_iq4_xs",
     "moe_logits",
     "torch_q4_k_weights",
     "iq4_xs_weights",
@@ -123,6 +124,15 @@ def moe_bank(seed: int, n_experts: int, hidden: int, ffn: int, *, stream: int = 
     gate = q4_k_weights(seed, n_experts * ffn, hidden, stream=3 * stream + 0)
     up = q4_k_weights(seed, n_experts * ffn, hidden, stream=3 * stream + 1)
     down = q4_k_weights(seed, n_experts * hidden, ffn, stream=3 * stream + 2)
+    return gate, up, down
+
+
+def moe_bank_iq4_xs(seed: int, n_experts: int, hidden: int, ffn: int, *, stream: int = 0):
+    """One layer's routed-expert bank with IQ4_XS matrices (the recipe of
+    iq4_xs_weights); same expert-major layout as moe_bank."""
+    gate = iq4_xs_weights(seed, n_experts * ffn, hidden, stream=3 * stream + 0)
+    up = iq4_xs_weights(seed, n_experts * ffn, hidden, stream=3 * stream + 1)
+    down = iq4_xs_weights(seed, n_experts * hidden, ffn, stream=3 * stream + 2)
     return gate, up, down
 
 

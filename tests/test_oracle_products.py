@@ -204,6 +204,57 @@ def test_moe_token_output_independent_of_batch():
         assert np.allclose(y1[0], y3[t], rtol=1e-13, atol=0)
 
 
+def test_moe_iq4_xs_equals_weighted_sum_of_dense_expert_products():
+    # IQ4_XS experts: every product written out dot by dot from the exact weights
+    hidden, ffn, n_exp, top_k = 256, 256, 8, 3
+    gate, up, down = synth.moe_bank_iq4_xs(84, n_exp, hidden, ffn)
+    logits = synth.moe_logits(84, 2, n_exp)
+    x = synth.bf16_normal(85, (2, hidden))
+    y, ids, w = oracle.moe_iq4_xs(gate, up, down, logits, x, hidden, ffn, n_exp, top_k)
+    from scipy.special import expit
+    xs = oracle.bf16_bits_to_f64(x)
+    for t in range(2):
+        acc = np.zeros(hidden)
+        for j in range(top_k):
+            e = int(ids[t, j])
+            size = ffn * (hidden // 256) * 136
+            wg = oracle.dequant_iq4_xs(gate[e * size:(e + 1) * size], ffn, hidden)
+            wu = oracle.dequant_iq4_xs(up[e * size:(e + 1) * size], ffn, hidden)
+            wd = oracle.dequant_iq4_xs(down[e * size:(e + 1) * size], hidden, ffn)
+            g = np.array([np.dot(wg[i], xs[t]) for i in range(ffn)])
+            u = np.array([np.dot(wu[i], xs[t]) for i in range(ffn)])
+            h = g * expit(g) * u
+            acc += w[t, j] * np.array([np.dot(wd[i], h) for i in range(hidden)])
+        assert np.allclose(y[t], acc, rtol=1e-12, atol=1e-12 * np.abs(acc).max())
+
+
+def test_moe_iq4_xs_single_expert_is_the_dense_ffn():
+    # top_k = 1: the routing weight is exactly 1 and y is one expert's FFN
+    hidden, ffn, n_exp = 256, 512, 4
+    gate, up, down = synth.moe_bank_iq4_xs(86, n_exp, hidden, ffn)
+    logits = np.full((1, n_exp), -3.0, dtype=np.float32)
+    logits[0, 2] = 1.0
+    x = synth.bf16_normal(87, (1, hidden))
+    y, ids, w = oracle.moe_iq4_xs(gate, up, down, logits, x, hidden, ffn, n_exp, 1)
+    assert ids.tolist() == [[2]] and w.tolist() == [[1.0]]
+    size = ffn * (hidden // 256) * 136
+    xs = oracle.bf16_bits_to_f64(x)[0]
+    g = oracle.qmv_iq4_xs(gate[2 * size:3 * size], x, ffn, hidden)[0]
+    u = oracle.qmv_iq4_xs(up[2 * size:3 * size], x, ffn, hidden)[0]
+    h = g / (1 + np.exp(-g)) * u
+    wd = oracle.dequant_iq4_xs(down[2 * size:3 * size], hidden, ffn)
+    assert np.allclose(y[0], wd @ h, rtol=1e-13, atol=0)
+    assert np.isfinite(xs).all()
+
+
+def test_moe_iq4_xs_bank_layout_is_expert_major():
+    gate, up, down = synth.moe_bank_iq4_xs(88, 4, 256, 512)
+    size = 512 * 1 * 136
+    assert gate.size == 4 * size and down.size == 4 * 256 * 2 * 136
+    assert np.array_equal(oracle.expert_matrix(gate, 3, 512, 256, 136), gate[3 * size:4 * size])
+    assert oracle.expert_matrix(down, 1, 256, 512, 136).size == 256 * 2 * 136
+
+
 # ---------------------------------------------------------------- prefill
 
 def test_prefill_identity_rows_reproduce_weights():
