@@ -74,8 +74,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--copies", type=int, default=128, help="layer copies in the dense weight pool")
     p.add_argument("--moe-banks", type=int, default=48)
+    p.add_argument("--iq4-copies", type=int, default=48, help="layer copies in the IQ4_XS weight pool")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
-    p.add_argument("--skip", default="", help="comma list of sections to skip: verify,q8,moe,prefill,cpu")
+    p.add_argument("--skip", default="", help="comma list of sections to skip: verify,q8,moe,prefill,iq4,cpu")
     return p.parse_args()
 
 
@@ -265,6 +266,11 @@ def main():
 
     del pool
     torch.cuda.empty_cache()
+    if "iq4" not in skip:
+        res["iq4_xs_gemv"] = bench_iq4(args, torch, np, q, synth, timer, dev, sp)
+        if "moe" not in skip:
+            res["moe_iq4_xs"] = bench_moe(args, torch, np, q, synth, timer, dev, sp, fmt="iq4_xs")
+        torch.cuda.empty_cache()
 
     cpu = None
     if "cpu" not in skip:
@@ -310,21 +316,25 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def bench_moe(args, torch, np, q, synth, timer, dev, sp):
+def bench_moe(args, torch, np, q, synth, timer, dev, sp, fmt="q4_k"):
     hidden, ffn, ne, tk = 2048, 768, 128, 8
+    L = q.lib
+    gen = synth.torch_q4_k_weights if fmt == "q4_k" else synth.torch_iq4_xs_weights
+    entry = L.qmv_q4_k_moe if fmt == "q4_k" else L.qmv_iq4_xs_moe
+    ws_fn = L.qmv_q4_k_moe_workspace if fmt == "q4_k" else L.qmv_iq4_xs_moe_workspace
+    name = f"qmv_{fmt}_moe"
     banks = []
-    log(f"[bench] generating the MoE pool: {args.moe_banks} banks x {ne} experts")
+    log(f"[bench] generating the {fmt} MoE pool: {args.moe_banks} banks x {ne} experts")
     for b in range(args.moe_banks):
-        banks.append([synth.torch_q4_k_weights(21, ne * (ffn if i < 2 else hidden), hidden if i < 2 else ffn, dev,
-                                               stream=3 * b + i) for i in range(3)])
+        banks.append([gen(21, ne * (ffn if i < 2 else hidden), hidden if i < 2 else ffn, dev, stream=3 * b + i)
+                      for i in range(3)])
     bank_bytes = banks[0][0].numel()
     out = {}
-    L = q.lib
     for t in (1, 3):
         logits = torch.from_numpy(synth.moe_logits(22, t * args.moe_banks, ne)).to(dev).view(args.moe_banks, t, ne)
         x = torch.from_numpy(synth.bf16_normal(23, (t, hidden)).view(np.int16)).to(dev)
         y = torch.empty((t, hidden), dtype=torch.float32, device=dev)
-        need = L.qmv_q4_k_moe_workspace(t, hidden, ffn, ne, tk)
+        need = ws_fn(t, hidden, ffn, ne, tk)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         ids = torch.empty((args.moe_banks, t, tk), dtype=torch.int32, device=dev)
         def make_calls(stream_ptr):
@@ -339,9 +349,9 @@ def bench_moe(args, torch, np, q, synth, timer, dev, sp):
 
             def step():
                 for a in cl:
-                    rc = L.qmv_q4_k_moe(*a)
+                    rc = entry(*a)
                     if rc:
-                        raise q.QmvError(rc, "qmv_q4_k_moe")
+                        raise q.QmvError(rc, name)
             return step
         step = make_step(sp)
         step()
@@ -363,9 +373,50 @@ def bench_moe(args, torch, np, q, synth, timer, dev, sp):
             "GBps_distinct_expert_bytes": distinct * expert_bytes / tl / 1e9,
             "launch": "hipGraph" if t_graph < t_eager else "stream",
         }
-        log(f"[bench] MoE T={t}: {tl * 1e6:.2f} us/layer, {out[f'T{t}']['tok_equiv_per_s']:.0f} tok-equiv/s, "
+        log(f"[bench] {fmt} MoE T={t}: {tl * 1e6:.2f} us/layer, {out[f'T{t}']['tok_equiv_per_s']:.0f} tok-equiv/s, "
             f"{out[f'T{t}']['GBps_distinct_expert_bytes']:.0f} GB/s")
     del banks
+    return out
+
+
+def bench_iq4(args, torch, np, q, synth, timer, dev, sp):
+    """IQ4_XS GEMV over a pool of layer copies (the dense FFN shapes), M = 1..4."""
+    L = q.lib
+    copies = args.iq4_copies
+    log(f"[bench] generating the IQ4_XS pool: {copies} layer copies")
+    pool = [[synth.torch_iq4_xs_weights(41, n, k, dev, stream=3 * c + i) for i, (_, n, k) in enumerate(SHAPES)]
+            for c in range(copies)]
+    xs = {k: torch.from_numpy(synth.bf16_normal(42, (4, k)).view(np.int16)).to(dev) for _, _, k in SHAPES}
+    ys = {n: torch.empty((4, n), dtype=torch.float32, device=dev) for _, n, _ in SHAPES}
+    shape_bytes = [q.iq4_xs_bytes(n, k) for _, n, k in SHAPES]
+    out = {}
+
+    def calls_for(m, shapes):
+        return [(ctypes.c_void_p(pool[c][i].data_ptr()), pool[c][i].numel(), ctypes.c_void_p(xs[k].data_ptr()),
+                 ctypes.c_void_p(ys[n].data_ptr()), m, n, k, sp)
+                for c in range(copies) for i, (_, n, k) in enumerate(SHAPES) if i in shapes]
+
+    def stepper(cl):
+        def step():
+            for a in cl:
+                rc = L.qmv_iq4_xs(*a)
+                if rc:
+                    raise q.QmvError(rc, "qmv_iq4_xs")
+        return step
+
+    for m in (1, 2, 3, 4):
+        step = stepper(calls_for(m, (0, 1, 2)))
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            step()
+        t = timer.run(step, max(2, args.steps // 2))
+        out[f"M{m}"] = {"GBps": copies * sum(shape_bytes) / t / 1e9, "us_per_launch": t / (3 * copies) * 1e6}
+    for i, (name, n, k) in enumerate(SHAPES):
+        t = timer.run(stepper(calls_for(1, (i,))), max(2, args.steps // 2)) / copies
+        out[f"M1_{name}"] = {"us_per_launch": t * 1e6, "GBps": shape_bytes[i] / t / 1e9}
+    log("[bench] IQ4_XS GEMV: " + ", ".join(f"M={m} {out[f'M{m}']['GBps']:.0f} GB/s" for m in (1, 2, 3, 4)) +
+        "; M=1 per launch " + ", ".join(f"{nm} {out[f'M1_{nm}']['us_per_launch']:.2f} us" for nm, _, _ in SHAPES))
+    del pool
     return out
 
 

@@ -14,7 +14,8 @@ import os
 
 __all__ = [
     "QmvError", "lib", "LIB_PATH", "version",
-    "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmm_q4_k_prefill_workspace",
+    "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmv_iq4_xs_moe",
+    "qmv_iq4_xs_moe_workspace", "qmm_q4_k_prefill_workspace",
     "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16", "qmv_dequant_q8_0_f32",
     "qmv_dequant_iq4_xs_f32", "q4_k_bytes", "q8_0_bytes", "iq4_xs_bytes", "EXPORTS",
 ]
@@ -34,6 +35,9 @@ EXPORTS = {
     "qmv_q4_k_moe_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "qmv_q4_k_moe": (_c_int, [_vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
                               _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "qmv_iq4_xs_moe_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "qmv_iq4_xs_moe": (_c_int, [_vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
+                                _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "qmm_q4_k_prefill_workspace": (_c_size, [_c_int, _c_int, _c_int]),
     "qmm_q4_k_prefill": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_size, _vp]),
     "qmv_dequant_q4_k_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
@@ -160,12 +164,10 @@ def qmv_q4_k_moe_workspace(t: int, hidden: int, ffn: int, n_experts: int, top_k:
     return lib.qmv_q4_k_moe_workspace(t, hidden, ffn, n_experts, top_k)
 
 
-def qmv_q4_k_moe(w_gate, w_up, w_down, logits, x, hidden: int, ffn: int, n_experts: int, top_k: int,
-                 y=None, ws=None, routing: bool = True, stream=None):
-    """Routed-expert MoE FFN; returns (y, topk_ids, topk_w, pairs) (the last three None if not routing)."""
+def _moe(fn, ws_fn, name, w_gate, w_up, w_down, logits, x, hidden, ffn, n_experts, top_k, y, ws, routing, stream):
     torch = _torch()
-    for name, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
-        _dev(t, name, (torch.uint8,))
+    for wname, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _dev(t, wname, (torch.uint8,))
     _dev(logits, "logits", (torch.float32,))
     _dev(x, "x", _bf16_types())
     tc = x.shape[0] if x.dim() == 2 else 1
@@ -173,7 +175,7 @@ def qmv_q4_k_moe(w_gate, w_up, w_down, logits, x, hidden: int, ffn: int, n_exper
     if y is None:
         y = torch.empty((tc, hidden), dtype=torch.float32, device=dev)
     _dev(y, "y", (torch.float32,))
-    need = qmv_q4_k_moe_workspace(tc, hidden, ffn, n_experts, top_k)
+    need = ws_fn(tc, hidden, ffn, n_experts, top_k)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _dev(ws, "ws", (torch.uint8,))
@@ -182,11 +184,29 @@ def qmv_q4_k_moe(w_gate, w_up, w_down, logits, x, hidden: int, ffn: int, n_exper
         ids = torch.empty((tc, top_k), dtype=torch.int32, device=dev)
         wts = torch.empty((tc, top_k), dtype=torch.float32, device=dev)
         pairs = torch.empty((tc * top_k, 2), dtype=torch.int32, device=dev)
-    rc = lib.qmv_q4_k_moe(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _nbytes(w_gate), _ptr(logits), _ptr(x),
-                          _ptr(y), _ptr(ids), _ptr(wts), _ptr(pairs), _ptr(ws), _nbytes(ws),
-                          tc, hidden, ffn, n_experts, top_k, _stream(stream))
-    _check(rc, "qmv_q4_k_moe")
+    rc = fn(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _nbytes(w_gate), _ptr(logits), _ptr(x),
+            _ptr(y), _ptr(ids), _ptr(wts), _ptr(pairs), _ptr(ws), _nbytes(ws),
+            tc, hidden, ffn, n_experts, top_k, _stream(stream))
+    _check(rc, name)
     return y, ids, wts, pairs
+
+
+def qmv_q4_k_moe(w_gate, w_up, w_down, logits, x, hidden: int, ffn: int, n_experts: int, top_k: int,
+                 y=None, ws=None, routing: bool = True, stream=None):
+    """Routed-expert MoE FFN; returns (y, topk_ids, topk_w, pairs) (the last three None if not routing)."""
+    return _moe(lib.qmv_q4_k_moe, qmv_q4_k_moe_workspace, "qmv_q4_k_moe", w_gate, w_up, w_down, logits, x,
+                hidden, ffn, n_experts, top_k, y, ws, routing, stream)
+
+
+def qmv_iq4_xs_moe_workspace(t: int, hidden: int, ffn: int, n_experts: int, top_k: int) -> int:
+    return lib.qmv_iq4_xs_moe_workspace(t, hidden, ffn, n_experts, top_k)
+
+
+def qmv_iq4_xs_moe(w_gate, w_up, w_down, logits, x, hidden: int, ffn: int, n_experts: int, top_k: int,
+                   y=None, ws=None, routing: bool = True, stream=None):
+    """Routed-expert MoE FFN on IQ4_XS expert banks; returns (y, topk_ids, topk_w, pairs)."""
+    return _moe(lib.qmv_iq4_xs_moe, qmv_iq4_xs_moe_workspace, "qmv_iq4_xs_moe", w_gate, w_up, w_down, logits, x,
+                hidden, ffn, n_experts, top_k, y, ws, routing, stream)
 
 
 def qmm_q4_k_prefill_workspace(m: int, n: int, k: int) -> int:

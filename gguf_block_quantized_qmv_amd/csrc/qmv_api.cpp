@@ -62,6 +62,62 @@ int check_matrix(const void *w, size_t w_bytes, int n, int k, int block_weights,
 
 }  // namespace
 
+namespace {
+
+enum class MoeFormat { kQ4K, kIQ4XS };
+
+bool moe_args_ok(MoeFormat f, int t, int hidden, int ffn, int n_experts, int top_k) {
+  return t >= 1 && t <= QMV_MOE_MAX_TOKENS && n_experts >= 1 && n_experts <= QMV_MOE_MAX_EXPERTS && top_k >= 1 &&
+         top_k <= QMV_MOE_MAX_TOP_K && top_k <= n_experts && hidden > 0 && ffn > 0 && hidden % 256 == 0 &&
+         ffn % 256 == 0 &&
+         (f == MoeFormat::kQ4K ? qmv::moe_fits_lds(t, hidden, ffn, top_k)
+                               : qmv::iq4xs_moe_fits_lds(t, hidden, ffn, top_k));
+}
+
+int moe_entry(MoeFormat f, const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes,
+              const float *logits, const uint16_t *x_bf16, float *y, int32_t *topk_ids, float *topk_w,
+              int32_t *pairs, void *ws, size_t ws_bytes, int t, int hidden, int ffn, int n_experts, int top_k,
+              void *stream) {
+  if (!w_gate || !w_up || !w_down || !logits || !x_bf16 || !y) return QMV_ERR_NULL;
+  if (t < 1 || t > QMV_MOE_MAX_TOKENS || n_experts < 1 || n_experts > QMV_MOE_MAX_EXPERTS || top_k < 1 ||
+      top_k > QMV_MOE_MAX_TOP_K || top_k > n_experts)
+    return QMV_ERR_RANGE;
+  if (hidden <= 0 || ffn <= 0 || hidden % 256 || ffn % 256) return QMV_ERR_SHAPE;
+  if (!moe_args_ok(f, t, hidden, ffn, n_experts, top_k)) return QMV_ERR_RANGE;
+  const size_t block_bytes = f == MoeFormat::kQ4K ? 144 : 136;
+  const size_t w_align = f == MoeFormat::kQ4K ? 16 : 8;
+  size_t expert_bytes = 0, bank = 0;
+  if (!mul_size((size_t)ffn, (size_t)(hidden / 256) * block_bytes, &expert_bytes) ||
+      !mul_size(expert_bytes, (size_t)n_experts, &bank) || bank_bytes != bank)
+    return QMV_ERR_SIZE;
+  if (!aligned(w_gate, w_align) || !aligned(w_up, w_align) || !aligned(w_down, w_align) || !aligned(x_bf16, 16) ||
+      !aligned(logits, 4) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(pairs, 4) ||
+      !aligned(ws, 256))
+    return QMV_ERR_ALIGN;
+  const size_t need = qmv::moe_workspace_bytes(t, hidden, ffn, n_experts, top_k);
+  if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
+
+  // every output (and the workspace) must be disjoint from every input and from each other
+  const size_t yb = (size_t)t * hidden * 4, idb = (size_t)t * top_k * 4, pb = (size_t)t * top_k * 8;
+  const void *in_p[] = {w_gate, w_up, w_down, logits, x_bf16};
+  const size_t in_b[] = {bank, bank, bank, (size_t)t * n_experts * 4, (size_t)t * hidden * 2};
+  const void *out_p[] = {y, topk_ids, topk_w, pairs, ws};
+  const size_t out_b[] = {yb, topk_ids ? idb : 0, topk_w ? idb : 0, pairs ? pb : 0, need};
+  for (int o = 0; o < 5; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (overlap(out_p[o], out_b[o], in_p[i], in_b[i])) return QMV_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 5; ++o2)
+      if (overlap(out_p[o], out_b[o], out_p[o2], out_b[o2])) return QMV_ERR_ALIAS;
+  }
+  if (f == MoeFormat::kQ4K)
+    return qmv::launch_q4_k_moe(w_gate, w_up, w_down, logits, x_bf16, y, topk_ids, topk_w, pairs, ws, t, hidden,
+                                ffn, n_experts, top_k, stream);
+  return qmv::launch_iq4_xs_moe(w_gate, w_up, w_down, logits, x_bf16, y, topk_ids, topk_w, pairs, ws, t, hidden, ffn,
+                                n_experts, top_k, stream);
+}
+
+}  // namespace
+
 extern "C" {
 
 int qmv_version(void) { return kVersion; }
@@ -120,47 +176,27 @@ int qmv_iq4_xs(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, 
 }
 
 size_t qmv_q4_k_moe_workspace(int t, int hidden, int ffn, int n_experts, int top_k) {
-  if (t < 1 || t > QMV_MOE_MAX_TOKENS || n_experts < 1 || n_experts > QMV_MOE_MAX_EXPERTS || top_k < 1 ||
-      top_k > QMV_MOE_MAX_TOP_K || top_k > n_experts || hidden <= 0 || ffn <= 0 || hidden % 256 || ffn % 256 ||
-      !qmv::moe_fits_lds(t, hidden, ffn, top_k))
-    return 0;
+  if (!moe_args_ok(MoeFormat::kQ4K, t, hidden, ffn, n_experts, top_k)) return 0;
   return qmv::moe_workspace_bytes(t, hidden, ffn, n_experts, top_k);
 }
 
 int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes, const float *logits,
                  const uint16_t *x_bf16, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, void *ws,
                  size_t ws_bytes, int t, int hidden, int ffn, int n_experts, int top_k, void *stream) {
-  if (!w_gate || !w_up || !w_down || !logits || !x_bf16 || !y) return QMV_ERR_NULL;
-  if (t < 1 || t > QMV_MOE_MAX_TOKENS || n_experts < 1 || n_experts > QMV_MOE_MAX_EXPERTS || top_k < 1 ||
-      top_k > QMV_MOE_MAX_TOP_K || top_k > n_experts)
-    return QMV_ERR_RANGE;
-  if (hidden <= 0 || ffn <= 0 || hidden % 256 || ffn % 256) return QMV_ERR_SHAPE;
-  if (!qmv::moe_fits_lds(t, hidden, ffn, top_k)) return QMV_ERR_RANGE;
-  size_t expert_bytes = 0, bank = 0;
-  if (!mul_size((size_t)ffn, (size_t)(hidden / 256) * 144, &expert_bytes) ||
-      !mul_size(expert_bytes, (size_t)n_experts, &bank) || bank_bytes != bank)
-    return QMV_ERR_SIZE;
-  if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(x_bf16, 16) ||
-      !aligned(logits, 4) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(pairs, 4) ||
-      !aligned(ws, 256))
-    return QMV_ERR_ALIGN;
-  const size_t need = qmv::moe_workspace_bytes(t, hidden, ffn, n_experts, top_k);
-  if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
+  return moe_entry(MoeFormat::kQ4K, w_gate, w_up, w_down, bank_bytes, logits, x_bf16, y, topk_ids, topk_w, pairs, ws,
+                   ws_bytes, t, hidden, ffn, n_experts, top_k, stream);
+}
 
-  // every output (and the workspace) must be disjoint from every input and from each other
-  const size_t yb = (size_t)t * hidden * 4, idb = (size_t)t * top_k * 4, pb = (size_t)t * top_k * 8;
-  const void *in_p[] = {w_gate, w_up, w_down, logits, x_bf16};
-  const size_t in_b[] = {bank, bank, bank, (size_t)t * n_experts * 4, (size_t)t * hidden * 2};
-  const void *out_p[] = {y, topk_ids, topk_w, pairs, ws};
-  const size_t out_b[] = {yb, topk_ids ? idb : 0, topk_w ? idb : 0, pairs ? pb : 0, need};
-  for (int o = 0; o < 5; ++o) {
-    for (int i = 0; i < 5; ++i)
-      if (overlap(out_p[o], out_b[o], in_p[i], in_b[i])) return QMV_ERR_ALIAS;
-    for (int o2 = o + 1; o2 < 5; ++o2)
-      if (overlap(out_p[o], out_b[o], out_p[o2], out_b[o2])) return QMV_ERR_ALIAS;
-  }
-  return qmv::launch_q4_k_moe(w_gate, w_up, w_down, logits, x_bf16, y, topk_ids, topk_w, pairs, ws, t, hidden, ffn,
-                              n_experts, top_k, stream);
+size_t qmv_iq4_xs_moe_workspace(int t, int hidden, int ffn, int n_experts, int top_k) {
+  if (!moe_args_ok(MoeFormat::kIQ4XS, t, hidden, ffn, n_experts, top_k)) return 0;
+  return qmv::moe_workspace_bytes(t, hidden, ffn, n_experts, top_k);
+}
+
+int qmv_iq4_xs_moe(const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes, const float *logits,
+                   const uint16_t *x_bf16, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, void *ws,
+                   size_t ws_bytes, int t, int hidden, int ffn, int n_experts, int top_k, void *stream) {
+  return moe_entry(MoeFormat::kIQ4XS, w_gate, w_up, w_down, bank_bytes, logits, x_bf16, y, topk_ids, topk_w, pairs,
+                   ws, ws_bytes, t, hidden, ffn, n_experts, top_k, stream);
 }
 
 size_t qmm_q4_k_prefill_workspace(int m, int n, int k) {

@@ -176,6 +176,31 @@ int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_
                  int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
 
 /*
+ * Workspace bytes qmv_iq4_xs_moe needs for t tokens (0 if an argument is out of
+ * range); the same layout and size as qmv_q4_k_moe's.
+ */
+size_t qmv_iq4_xs_moe_workspace(int t, int hidden, int ffn, int n_experts, int top_k);
+
+/*
+ * Routed-expert MoE feed-forward on IQ4_XS experts (the memra README's model
+ * support table lists its 35B-A3B MoE in IQ4_XS). Arguments, routing, outputs
+ * and error codes as qmv_q4_k_moe, except:
+ *   w_gate, w_up, w_down  8-byte aligned banks of 136-byte IQ4_XS blocks;
+ *                 bank_bytes must equal n_experts*ffn*(hidden/256)*136
+ *   LDS limits    t*(hidden/32)*68 and t*top_k*(ffn/32)*144 bytes each
+ *                 <= QMV_LDS_X_BYTES - 8192, else QMV_ERR_RANGE.
+ * h = silu(W_gate x) * (W_up x) is formed in fp32 from bf16 weight pairs and
+ * bf16 activations (dot2, fp32 accumulation) and W_down h in fp32 (fma). The
+ * selection, its tie rule, the weights and the rank-order combine are those
+ * of qmv_q4_k_moe.
+ */
+int qmv_iq4_xs_moe(const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes,
+                   const float *logits, const uint16_t *x_bf16, float *y,
+                   int32_t *topk_ids, float *topk_w, int32_t *pairs,
+                   void *ws, size_t ws_bytes,
+                   int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
+
+/*
  * Workspace bytes qmm_q4_k_prefill can use for an m x n x k product on the
  * current device: 0 when the output tiles divide evenly over the workgroups
  * the device holds at once (or too few K blocks to split). Otherwise the tiles

@@ -34,7 +34,7 @@ def _header_functions():
 def test_header_lists_the_expected_entry_points():
     assert _header_functions() == sorted([
         "qmv_version", "qmv_strerror", "qmv_last_error", "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe_workspace",
-        "qmv_q4_k_moe", "qmv_dequant_iq4_xs_f32",
+        "qmv_q4_k_moe", "qmv_dequant_iq4_xs_f32", "qmv_iq4_xs_moe_workspace", "qmv_iq4_xs_moe",
         "qmm_q4_k_prefill_workspace", "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16",
         "qmv_dequant_q8_0_f32"])
 
@@ -181,6 +181,39 @@ def test_moe_bank_every_truncated_size_is_an_error():
     for b in range(0, bank, 97):
         assert moe(bank=b) == SIZE, b
     assert moe(bank=bank - 1) == SIZE
+
+
+def moe_iq4(**kw):
+    a = dict(wg=W, wu=W + (1 << 28), wd=W + (2 << 28), bank=None, logits=X, x=X + (1 << 20), y=Y,
+             ids=Y + (1 << 20), wts=Y + (2 << 20), pairs=Y + (3 << 20), ws=WS, ws_bytes=None,
+             t=1, h=256, f=256, e=8, k=2)
+    a.update(kw)
+    bank = a["e"] * a["f"] * (a["h"] // 256) * 136 if a["bank"] is None else a["bank"]
+    need = L.qmv_iq4_xs_moe_workspace(a["t"], a["h"], a["f"], a["e"], a["k"])
+    ws_bytes = need if a["ws_bytes"] is None else a["ws_bytes"]
+    return L.qmv_iq4_xs_moe(V(a["wg"]), V(a["wu"]), V(a["wd"]), bank, V(a["logits"]), V(a["x"]), V(a["y"]),
+                            V(a["ids"]), V(a["wts"]), V(a["pairs"]), V(a["ws"]), ws_bytes,
+                            a["t"], a["h"], a["f"], a["e"], a["k"], None)
+
+
+def test_iq4_xs_moe_validation():
+    assert L.qmv_iq4_xs_moe_workspace(1, 2048, 768, 128, 8) == L.qmv_q4_k_moe_workspace(1, 2048, 768, 128, 8)
+    assert L.qmv_iq4_xs_moe_workspace(0, 2048, 768, 128, 8) == 0
+    assert L.qmv_iq4_xs_moe_workspace(5, 2048, 768, 128, 8) == 0
+    assert L.qmv_iq4_xs_moe_workspace(1, 2048, 768, 128, 9) == 0
+    assert moe_iq4(wg=0) == NULL and moe_iq4(logits=0) == NULL and moe_iq4(y=0) == NULL
+    assert moe_iq4(t=0) == RANGE and moe_iq4(t=5) == RANGE and moe_iq4(k=0) == RANGE
+    assert moe_iq4(k=4, e=3) == RANGE and moe_iq4(e=257) == RANGE
+    assert moe_iq4(h=300) == SHAPE and moe_iq4(f=0) == SHAPE
+    assert moe_iq4(t=4, k=8, e=16, f=1280) == RANGE      # 32 pairs' h exceed the LDS stage
+    assert moe_iq4(t=4, k=8, e=16, f=1024) != RANGE      # ... and fit below it
+    assert moe_iq4(t=4, h=20480) == RANGE                 # 4 tokens' activations exceed it
+    assert moe_iq4(bank=8 * 256 * 136 - 1) == SIZE and moe_iq4(bank=8 * 256 * 144) == SIZE
+    assert moe_iq4(wd=W + (2 << 28) + 4) == ALIGN and moe_iq4(x=X + 8) == ALIGN and moe_iq4(ws=WS + 128) == ALIGN
+    assert moe_iq4(ws=0) == WORKSPACE and moe_iq4(ws_bytes=16) == WORKSPACE
+    assert moe_iq4(y=W + 1024) == ALIAS
+    assert moe_iq4(ws=Y) == ALIAS
+    assert moe_iq4(pairs=Y + (1 << 20)) == ALIAS
 
 
 def test_one_hip_runtime_in_the_process():
