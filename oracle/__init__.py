@@ -11,6 +11,7 @@ from .gguf_oracle import (  # noqa: F401
     IQ4_XS_BLOCK_WEIGHTS,
     Q4_K_BLOCK_BYTES,
     Q4_K_BLOCK_WEIGHTS,
+    Q5_K_BLOCK_BYTES,
     Q8_0_BLOCK_BYTES,
     Q8_0_BLOCK_WEIGHTS,
     bf16_bits_to_f64,
@@ -18,6 +19,8 @@ from .gguf_oracle import (  # noqa: F401
     dequant_q4_k,
     dequant_q4_k_bf16_bits,
     dequant_q4_k_f32,
+    dequant_q5_k,
+    dequant_q5_k_f32,
     dequant_q8_0,
     dequant_q8_0_f32,
     expert_matrix,
@@ -31,9 +34,11 @@ from .gguf_oracle import (  # noqa: F401
     moe_q4_k,
     prefill_q4_k,
     q4_k_fields,
+    q5_k_fields,
     q8_0_fields,
     qmv_iq4_xs,
     qmv_q4_k,
+    qmv_q5_k,
     qmv_q8_0,
     round_f32_to_bf16_bits,
     round_to_f32,

@@ -151,23 +151,34 @@ def q4_k_fields(raw, n_rows: int, k: int):
     d = fp16_bits_to_f64((blocks[:, :, 0] | (blocks[:, :, 1] << 8)).astype(np.uint16))
     dmin = fp16_bits_to_f64((blocks[:, :, 2] | (blocks[:, :, 3] << 8)).astype(np.uint16))
 
-    S = blocks[:, :, 4:16]
-    sc = np.empty((n_rows, nb, 8), dtype=np.int64)
-    m = np.empty((n_rows, nb, 8), dtype=np.int64)
-    for j in range(4):
-        sc[:, :, j] = S[:, :, j] & 0x3F
-        m[:, :, j] = S[:, :, j + 4] & 0x3F
-    for j in range(4, 8):
-        sc[:, :, j] = (S[:, :, j + 4] & 0x0F) | ((S[:, :, j - 4] >> 6) << 4)
-        m[:, :, j] = (S[:, :, j + 4] >> 4) | ((S[:, :, j] >> 6) << 4)
-
-    Q = blocks[:, :, 16:]
-    q = np.empty((n_rows, nb, 256), dtype=np.int64)
-    for c in range(4):
-        byte = Q[:, :, 32 * c: 32 * c + 32]
-        q[:, :, 64 * c: 64 * c + 32] = byte & 0x0F
-        q[:, :, 64 * c + 32: 64 * c + 64] = byte >> 4
+    sc, m = _k_scales_mins(blocks[:, :, 4:16])
+    q = _k_nibbles(blocks[:, :, 16:])
     return d, dmin, sc, m, q
+
+
+def _k_scales_mins(S):
+    """The eight 6-bit scales and mins of a K-quant super-block from its 12 packed
+    bytes S (int64 [..., 12]); see q4_k_fields for the bit positions."""
+    sc = np.empty(S.shape[:-1] + (8,), dtype=np.int64)
+    m = np.empty(S.shape[:-1] + (8,), dtype=np.int64)
+    for j in range(4):
+        sc[..., j] = S[..., j] & 0x3F
+        m[..., j] = S[..., j + 4] & 0x3F
+    for j in range(4, 8):
+        sc[..., j] = (S[..., j + 4] & 0x0F) | ((S[..., j - 4] >> 6) << 4)
+        m[..., j] = (S[..., j + 4] >> 4) | ((S[..., j] >> 6) << 4)
+    return sc, m
+
+
+def _k_nibbles(Q):
+    """The 256 low 4-bit quants from 128 packed bytes Q (int64 [..., 128]): byte
+    Q[32c + l] holds weight 64c + l (low nibble) and 64c + 32 + l (high nibble)."""
+    q = np.empty(Q.shape[:-1] + (256,), dtype=np.int64)
+    for c in range(4):
+        byte = Q[..., 32 * c: 32 * c + 32]
+        q[..., 64 * c: 64 * c + 32] = byte & 0x0F
+        q[..., 64 * c + 32: 64 * c + 64] = byte >> 4
+    return q
 
 
 def dequant_q4_k(raw, n_rows: int, k: int) -> np.ndarray:
@@ -185,6 +196,67 @@ def dequant_q4_k(raw, n_rows: int, k: int) -> np.ndarray:
 def dequant_q4_k_f32(raw, n_rows: int, k: int) -> np.ndarray:
     """The fp32 dequantization target: each exact weight rounded once to fp32."""
     return round_to_f32(dequant_q4_k(raw, n_rows, k))
+
+
+# ----------------------------------------------------------------------------
+# Q5_K: 176-byte super-blocks of 256 weights along K
+# ----------------------------------------------------------------------------
+#
+# The sibling K-quant of Q4_K (the memra README's model support table lists
+# Q4_K_M GGUF files, which mix K-quants, and the memra-bench card flags a Q5_K
+# expert mix). Public GGUF layout, restated: the Q4_K header, then a plane of
+# 32 bytes holding the fifth bit of every quant, then the Q4_K nibbles.
+
+Q5_K_BLOCK_BYTES = 176
+
+
+def q5_k_fields(raw, n_rows: int, k: int):
+    """Decode a row-major Q5_K matrix into its fields.
+
+    Returns (d, dmin, sc, m, q) with the shapes of q4_k_fields; q is 5-bit.
+
+    Byte layout of one super-block (block b of row n starts at (n*K/256 + b)*176):
+      0..1    fp16 d         2..3    fp16 dmin
+      4..15   S[0..11]: scales/mins packed exactly as in Q4_K
+      16..47  H[0..31]: the high-bit plane
+      48..175 Q[0..127]: low nibbles, in Q4_K's order
+    Weight 64c + l (c = 0..3, l < 32) has low bits Q[32c + l] & 15 and high bit
+    (H[l] >> 2c) & 1; weight 64c + 32 + l has low bits Q[32c + l] >> 4 and high
+    bit (H[l] >> (2c + 1)) & 1. The quant is low + 16 * high, in [0, 31].
+    """
+    if k % Q4_K_BLOCK_WEIGHTS:
+        raise ValueError("Q5_K needs K to be a multiple of 256")
+    nb = k // Q4_K_BLOCK_WEIGHTS
+    b = _as_bytes(raw)
+    if b.size != n_rows * nb * Q5_K_BLOCK_BYTES:
+        raise ValueError("byte count does not match the Q5_K shape")
+    blocks = b.reshape(n_rows, nb, Q5_K_BLOCK_BYTES).astype(np.int64)
+    d = fp16_bits_to_f64((blocks[:, :, 0] | (blocks[:, :, 1] << 8)).astype(np.uint16))
+    dmin = fp16_bits_to_f64((blocks[:, :, 2] | (blocks[:, :, 3] << 8)).astype(np.uint16))
+    sc, m = _k_scales_mins(blocks[:, :, 4:16])
+    H = blocks[:, :, 16:48]
+    q = _k_nibbles(blocks[:, :, 48:])
+    for c in range(4):
+        q[:, :, 64 * c: 64 * c + 32] += ((H >> (2 * c)) & 1) << 4
+        q[:, :, 64 * c + 32: 64 * c + 64] += ((H >> (2 * c + 1)) & 1) << 4
+    return d, dmin, sc, m, q
+
+
+def dequant_q5_k(raw, n_rows: int, k: int) -> np.ndarray:
+    """Exact Q5_K weights: w = d * sc_j * q - dmin * m_j, as Q4_K with 5-bit q.
+
+    float64 [N, K]; every weight is an integer multiple of 2^-24 below 2^50.
+    """
+    d, dmin, sc, m, q = q5_k_fields(raw, n_rows, k)
+    nb = k // Q4_K_BLOCK_WEIGHTS
+    scale = (d[:, :, None] * sc).repeat(32, axis=2)
+    offset = (dmin[:, :, None] * m).repeat(32, axis=2)
+    return (scale * q - offset).reshape(n_rows, nb * 256)
+
+
+def dequant_q5_k_f32(raw, n_rows: int, k: int) -> np.ndarray:
+    """The fp32 dequantization target: each exact Q5_K weight rounded once to fp32."""
+    return round_to_f32(dequant_q5_k(raw, n_rows, k))
 
 
 def dequant_q8_0_f32(raw, n_rows: int, k: int) -> np.ndarray:
@@ -285,6 +357,11 @@ def gemv(w: np.ndarray, x: np.ndarray) -> np.ndarray:
 def qmv_q8_0(raw, x_f32, n_rows: int, k: int) -> np.ndarray:
     """Q8_0 matrix times fp32 activation rows -> float64 [M, N]."""
     return gemv(dequant_q8_0(raw, n_rows, k), np.asarray(x_f32, dtype=np.float32).astype(np.float64))
+
+
+def qmv_q5_k(raw, x_bf16_bits, n_rows: int, k: int) -> np.ndarray:
+    """Q5_K matrix times bf16 activation rows -> float64 [M, N]."""
+    return gemv(dequant_q5_k(raw, n_rows, k), bf16_bits_to_f64(x_bf16_bits))
 
 
 def qmv_q4_k(raw, x_bf16_bits, n_rows: int, k: int) -> np.ndarray:

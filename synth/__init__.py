@@ -37,6 +37,8 @@ __all__ = [
     "moe_logits",
     "torch_q4_k_weights",
     "iq4_xs_weights",
+    "q5_k_weights",
+    "torch_q5_k_weights",
     "torch_iq4_xs_weights",
 ]
 
@@ -44,6 +46,7 @@ __all__ = [
 _Q8_0_BYTES, _Q8_0_WEIGHTS = 34, 32
 _Q4_K_BYTES, _Q4_K_WEIGHTS = 144, 256
 _IQ4_XS_BYTES, _IQ4_XS_WEIGHTS = 136, 256
+_Q5_K_BYTES = 176
 
 
 def rng(seed: int, *stream: int) -> np.random.Generator:
@@ -112,6 +115,47 @@ def f32_normal(seed: int, shape, *, stream: int = 0) -> np.ndarray:
     """fp32 N(0,1) samples (the Q8_0 activation recipe)."""
     g = rng(seed, 32, stream)
     return g.standard_normal(size=shape, dtype=np.float32)
+
+
+def q5_k_weights(seed: int, n_rows: int, k: int, *, stream: int = 0,
+                 d_scale: float = 0.001, dmin_scale: float = 0.002) -> np.ndarray:
+    """Row-major Q5_K matrix bytes.
+
+    Per 176-byte super-block: fp16 d = |N(0,1)|*0.001, fp16 dmin = |N(0,1)|*0.002,
+    then 172 uniform random bytes (12 scale/min bytes, 32 high-bit bytes, 128
+    nibble bytes): sc, m ~ U[0,63] and q ~ U[0,31] i.i.d. d is half the Q4_K
+    recipe's, so that d*sc*q keeps its magnitude with q twice as large.
+    Returns a flat uint8 array of n_rows * (k/256) * 176 bytes.
+    """
+    if k % _Q4_K_WEIGHTS:
+        raise ValueError("k must be a multiple of 256")
+    nb = n_rows * (k // _Q4_K_WEIGHTS)
+    g = rng(seed, 5, stream)
+    out = g.integers(0, 256, size=(nb, _Q5_K_BYTES), dtype=np.uint8)
+    d = (np.abs(g.standard_normal(nb)) * d_scale).astype(np.float16)
+    dmin = (np.abs(g.standard_normal(nb)) * dmin_scale).astype(np.float16)
+    out[:, 0:2] = d.view(np.uint8).reshape(nb, 2)
+    out[:, 2:4] = dmin.view(np.uint8).reshape(nb, 2)
+    return out.reshape(-1)
+
+
+def torch_q5_k_weights(seed: int, n_rows: int, k: int, device, *, stream: int = 0,
+                       d_scale: float = 0.001, dmin_scale: float = 0.002):
+    """Device-side Q5_K matrix bytes with the recipe of q5_k_weights (d, dmin
+    rounded from fp32). Returns a flat uint8 device tensor."""
+    import torch
+
+    if k % _Q4_K_WEIGHTS:
+        raise ValueError("k must be a multiple of 256")
+    nb = n_rows * (k // _Q4_K_WEIGHTS)
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1_000_003 + int(stream) * 7919 + 55) & 0x7FFF_FFFF_FFFF_FFFF)
+    blocks = torch.randint(0, 256, (nb, _Q5_K_BYTES), dtype=torch.uint8, device=device, generator=g)
+    d = torch.randn((nb, 1), dtype=torch.float32, device=device, generator=g).abs_().mul_(d_scale)
+    dm = torch.randn((nb, 1), dtype=torch.float32, device=device, generator=g).abs_().mul_(dmin_scale)
+    blocks[:, 0:2] = d.to(torch.float16).view(torch.uint8).view(nb, 2)
+    blocks[:, 2:4] = dm.to(torch.float16).view(torch.uint8).view(nb, 2)
+    return blocks.reshape(-1)
 
 
 def moe_bank(seed: int, n_experts: int, hidden: int, ffn: int, *, stream: int = 0):

@@ -1,4 +1,4 @@
-"""Writes tests/golden/{q8_0,q4_k,iq4_xs}_handbuilt.json: hand-built blocks with known values.
+"""Writes tests/golden/{q8_0,q4_k,q5_k,iq4_xs}_handbuilt.json: hand-built blocks with known values.
 
 Run from the repository root:  python tests/golden/make_handbuilt_blocks.py
 
@@ -11,7 +11,8 @@ as literals; the script stops if its encoder disagrees with them.
 
 The expected weights are computed here from the stated fields with exact
 rational arithmetic (w = d*q for Q8_0, w = d*sc_j*q - dmin*m_j for Q4_K,
-w = d*(ls_j - 32)*grid[q] for IQ4_XS); they are closed forms by construction
+w = d*(ls_j - 32)*grid[q] for IQ4_XS, the Q4_K form with 5-bit q for Q5_K);
+they are closed forms by construction
 and do not come from the oracle or the GPU. The memra pages name these formats
 (memra README, model support table: Q8_0, Q4_K_M and IQ4_XS GGUF models) but
 print no block bytes, so no value here is theirs. The IQ4_XS grid below is this
@@ -110,6 +111,37 @@ Q4_K_BLOCKS = [
 ]
 
 
+# ---------------------------------------------------------------- Q5_K
+
+def pack_q5_high_bits(q: list[int]) -> bytes:
+    """The 32 high-bit bytes: bit 2c of H[l] is bit 4 of q[64c + l], bit 2c + 1
+    is bit 4 of q[64c + 32 + l]."""
+    assert len(q) == 256 and all(0 <= v < 32 for v in q)
+    out = bytearray(32)
+    for c in range(4):
+        for l in range(32):
+            out[l] |= (q[64 * c + l] >> 4) << (2 * c)
+            out[l] |= (q[64 * c + 32 + l] >> 4) << (2 * c + 1)
+    return bytes(out)
+
+
+# (name, d_bits, dmin_bits, sc[8], m[8], q[256], hand-derived scale bytes, hand-derived high-bit bytes)
+Q5_K_BLOCKS = [
+    ("high_plane_all", 0x3C00, 0x0000, [1, 2, 3, 4, 5, 6, 7, 8], [0] * 8,
+     [16] * 256, "010203040000000005060708", "ff" * 32),
+    ("high_halves", 0x3800, 0x3400, [63, 62, 61, 60, 48, 33, 18, 47], [0, 7, 63, 32, 63, 17, 50, 5],
+     [(i % 16) + (16 if i % 64 >= 32 else 0) for i in range(256)], "ffbe7dbcc047ff20f011225f", "aa" * 32),
+    ("chunk2_plane", 0x3C00, 0x3C00, [1] * 8, [1, 2, 3, 4, 5, 6, 7, 8],
+     [(i % 16) + (16 if 128 <= i < 192 else 0) for i in range(256)], "010101010102030451617181", "30" * 32),
+    ("odd_positions", 0x0001, 0x0003, [63] * 8, [63] * 8,
+     [31 if i % 2 else 15 for i in range(256)], "ff" * 12, "00ff" * 16),
+    ("zero_plane", 0x3C00, 0x0000, [1] * 8, [0] * 8,
+     [(i * 7 + (i >> 5)) % 16 for i in range(256)], "010101010000000001010101", "00" * 32),
+    ("negative_zero_d", 0x8000, 0x3C00, [63, 62, 61, 60, 48, 33, 18, 47], [0, 7, 63, 32, 63, 17, 50, 5],
+     [16 + (5 * i + 3) % 16 for i in range(256)], "ffbe7dbcc047ff20f011225f", "ff" * 32),
+]
+
+
 # ---------------------------------------------------------------- IQ4_XS
 
 IQ4_XS_GRID = [-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113]
@@ -185,6 +217,30 @@ def main() -> None:
             "expect": [frac_to_hex(v) for v in expect],
         })
 
+    q5 = []
+    for name, d_bits, dmin_bits, sc, m, q, s_hex, h_hex in Q5_K_BLOCKS:
+        s_bytes = pack_scales_mins(sc, m)
+        if s_bytes.hex() != s_hex:
+            raise SystemExit(f"{name}: encoder gives {s_bytes.hex()}, hand derivation says {s_hex}")
+        h_bytes = pack_q5_high_bits(q)
+        if h_bytes.hex() != h_hex:
+            raise SystemExit(f"{name}: encoder gives high bits {h_bytes.hex()}, hand derivation says {h_hex}")
+        raw = (bytes([d_bits & 0xFF, d_bits >> 8, dmin_bits & 0xFF, dmin_bits >> 8]) + s_bytes + h_bytes +
+               pack_nibbles([v & 15 for v in q]))
+        assert len(raw) == 176
+        d, dmin = fp16_value(d_bits), fp16_value(dmin_bits)
+        expect = [d * sc[i // 32] * q[i] - dmin * m[i // 32] for i in range(256)]
+        q5.append({
+            "name": name,
+            "d_bits": d_bits,
+            "dmin_bits": dmin_bits,
+            "sc": sc,
+            "m": m,
+            "q": q,
+            "hex": raw.hex(),
+            "expect": [frac_to_hex(v) for v in expect],
+        })
+
     iq4 = []
     for name, d_bits, ls, q, s_hex in IQ4_XS_BLOCKS:
         s_bytes = pack_iq4_xs_scales(ls)
@@ -211,6 +267,10 @@ def main() -> None:
         f.write("\n")
     with open(os.path.join(HERE, "q4_k_handbuilt.json"), "w") as f:
         json.dump({"citation": note, "blocks": q4}, f, indent=1)
+        f.write("\n")
+    with open(os.path.join(HERE, "q5_k_handbuilt.json"), "w") as f:
+        json.dump({"citation": note.replace("(Q8_0, Q4_K_M GGUF)", "(Q8_0, Q4_K_M GGUF, whose K-quant mix includes Q5_K)"),
+                   "blocks": q5}, f, indent=1)
         f.write("\n")
     with open(os.path.join(HERE, "iq4_xs_handbuilt.json"), "w") as f:
         json.dump({"citation": note.replace("(Q8_0, Q4_K_M GGUF)", "(Q8_0, Q4_K_M, IQ4_XS GGUF)"), "blocks": iq4},

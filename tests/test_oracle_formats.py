@@ -1,4 +1,4 @@
-"""Pins for the oracle's block decoding (Q8_0, Q4_K, IQ4_XS) and scalar formats.
+"""Pins for the oracle's block decoding (Q8_0, Q4_K, Q5_K, IQ4_XS) and scalar formats.
 
 Everything here runs on the CPU. Each check ties the oracle to something other
 than itself: hand-built blocks whose values are known by construction
@@ -18,7 +18,7 @@ import synth
 
 sys.path.insert(0, os.path.join(os.path.dirname(__file__), "golden"))
 from make_handbuilt_blocks import (  # noqa: E402
-    IQ4_XS_GRID, pack_iq4_indices, pack_iq4_xs_scales, pack_nibbles, pack_scales_mins)
+    IQ4_XS_GRID, pack_iq4_indices, pack_iq4_xs_scales, pack_nibbles, pack_q5_high_bits, pack_scales_mins)
 
 
 def _load(golden_dir, name):
@@ -263,6 +263,151 @@ def test_fp32_target_rounds_once():
     ulp = np.spacing(np.abs(w32)).astype(np.float64)
     assert np.all(err <= 0.5 * ulp)
     assert np.count_nonzero(err) > 0        # some weights really need the rounding
+
+
+# ---------------------------------------------------------------- Q5_K
+
+def test_q5_k_handbuilt_blocks(golden_dir):
+    for blk in _load(golden_dir, "q5_k_handbuilt.json"):
+        raw = bytes.fromhex(blk["hex"])
+        d, dmin, sc, m, q = oracle.q5_k_fields(raw, 1, 256)
+        assert list(sc[0, 0]) == blk["sc"], blk["name"]
+        assert list(m[0, 0]) == blk["m"], blk["name"]
+        assert list(q[0, 0]) == blk["q"], blk["name"]
+        assert d[0, 0] == oracle.fp16_bits_to_f64(np.array([blk["d_bits"]]))[0]
+        assert dmin[0, 0] == oracle.fp16_bits_to_f64(np.array([blk["dmin_bits"]]))[0]
+        w = oracle.dequant_q5_k(raw, 1, 256)[0]
+        expect = np.array([float.fromhex(v) for v in blk["expect"]])
+        assert np.array_equal(w, expect), blk["name"]
+
+
+def test_q5_k_handbuilt_values_by_hand(golden_dir):
+    blocks = {b["name"]: b for b in _load(golden_dir, "q5_k_handbuilt.json")}
+    # d = 1, dmin = 0, sc_j = j + 1, every q = 16: w = 16 (j + 1)
+    w = oracle.dequant_q5_k(bytes.fromhex(blocks["high_plane_all"]["hex"]), 1, 256)[0]
+    assert list(w[::32]) == [16.0, 32.0, 48.0, 64.0, 80.0, 96.0, 112.0, 128.0]
+    # d = 1, dmin = 1, sc = 1, m_j = j + 1; chunk 2 (weights 128..191) carries the high bit
+    w = oracle.dequant_q5_k(bytes.fromhex(blocks["chunk2_plane"]["hex"]), 1, 256)[0]
+    assert list(w[[0, 5, 127, 128, 133, 191, 192, 255]]) == [-1.0, 4.0, 11.0, 11.0, 16.0, 25.0, -7.0, 7.0]
+    # d = -0: the scale term vanishes and w = -dmin * m_j exactly
+    w = oracle.dequant_q5_k(bytes.fromhex(blocks["negative_zero_d"]["hex"]), 1, 256)[0]
+    assert list(w[::32]) == [0.0, -7.0, -63.0, -32.0, -63.0, -17.0, -50.0, -5.0]
+
+
+def _q5_to_q4_bytes(raw5):
+    """The Q4_K block with Q5_K's header and nibbles (the high-bit plane dropped)."""
+    b = np.asarray(raw5, dtype=np.uint8).reshape(-1, 176)
+    return np.concatenate([b[:, :16], b[:, 48:]], axis=1).reshape(-1)
+
+
+def test_q5_k_without_high_bits_is_q4_k():
+    raw = synth.q5_k_weights(71, 8, 512).reshape(-1, 176).copy()
+    raw[:, 16:48] = 0
+    w5 = oracle.dequant_q5_k(raw.reshape(-1), 8, 512)
+    w4 = oracle.dequant_q4_k(_q5_to_q4_bytes(raw), 8, 512)
+    assert np.array_equal(w5, w4)
+
+
+def test_q5_k_all_high_bits_add_sixteen_scales():
+    raw = synth.q5_k_weights(72, 8, 512).reshape(-1, 176).copy()
+    lo = raw.copy()
+    lo[:, 16:48] = 0
+    hi = raw.copy()
+    hi[:, 16:48] = 0xFF
+    d, _, sc, _, _ = oracle.q5_k_fields(lo.reshape(-1), 8, 512)
+    step = (16 * d[:, :, None] * sc).repeat(32, axis=2).reshape(8, 512)
+    diff = oracle.dequant_q5_k(hi.reshape(-1), 8, 512) - oracle.dequant_q5_k(lo.reshape(-1), 8, 512)
+    assert np.array_equal(diff, step)
+
+
+def test_q5_k_high_bit_locality():
+    raw = bytearray(synth.q5_k_weights(73, 1, 256))
+    base = oracle.dequant_q5_k(bytes(raw), 1, 256)[0]
+    d, _, sc, _, q = oracle.q5_k_fields(bytes(raw), 1, 256)
+    for l in range(32):
+        for bit in range(8):
+            weight = 64 * (bit // 2) + 32 * (bit % 2) + l
+            mod = bytearray(raw)
+            mod[16 + l] ^= 1 << bit
+            w = oracle.dequant_q5_k(bytes(mod), 1, 256)[0]
+            changed = np.nonzero(w != base)[0]
+            step = 16 * d[0, 0] * sc[0, 0, weight // 32]
+            if step != 0:
+                assert list(changed) == [weight], (l, bit)
+                sign = -1 if q[0, 0, weight] >= 16 else 1
+                assert w[weight] - base[weight] == sign * step
+            else:
+                assert changed.size == 0
+
+
+def test_q5_k_nibble_byte_locality():
+    raw = bytearray(synth.q5_k_weights(74, 1, 256))
+    base = oracle.dequant_q5_k(bytes(raw), 1, 256)[0]
+    _, _, sc, _, _ = oracle.q5_k_fields(bytes(raw), 1, 256)
+    for p in range(128):
+        c, l = divmod(p, 32)
+        for mask, weight in ((0x0F, 64 * c + l), (0xF0, 64 * c + 32 + l)):
+            mod = bytearray(raw)
+            mod[48 + p] ^= mask
+            changed = np.nonzero(oracle.dequant_q5_k(bytes(mod), 1, 256)[0] != base)[0]
+            assert list(changed) == ([weight] if sc[0, 0, weight // 32] != 0 else []), (p, mask)
+
+
+def test_q5_k_pack_unpack_bijection():
+    # every 5-bit quant value in every position survives pack -> decode, and random bytes decode -> pack
+    rng = np.random.default_rng(5)
+    for v in range(32):
+        q = list(rng.integers(0, 32, 256))
+        for i in range(v, 256, 32):
+            q[i] = v
+        raw = bytes([0, 0x3C, 0, 0x3C]) + pack_scales_mins([1] * 8, [0] * 8) + pack_q5_high_bits(q) + \
+            pack_nibbles([t & 15 for t in q])
+        assert list(oracle.q5_k_fields(raw, 1, 256)[4][0, 0]) == q
+    raw = synth.q5_k_weights(75, 4, 512)
+    _, _, sc, m, q = oracle.q5_k_fields(raw, 4, 512)
+    blocks = raw.reshape(-1, 176)
+    for b in range(blocks.shape[0]):
+        n, t = divmod(b, 2)
+        assert pack_scales_mins(list(sc[n, t]), list(m[n, t])) == bytes(blocks[b, 4:16])
+        assert pack_q5_high_bits(list(q[n, t])) == bytes(blocks[b, 16:48])
+        assert pack_nibbles([v & 15 for v in q[n, t]]) == bytes(blocks[b, 48:])
+
+
+def test_q5_k_requant_round_trip():
+    raw = synth.q5_k_weights(76, 16, 512)
+    d, dmin, sc, m, q = oracle.q5_k_fields(raw, 16, 512)
+    w = oracle.dequant_q5_k(raw, 16, 512).reshape(16, 2, 8, 32)
+    scale = d[:, :, None] * sc
+    off = dmin[:, :, None] * m
+    ok = scale != 0
+    q_back = np.rint((w + off[..., None]) / np.where(ok, scale, 1.0)[..., None])
+    assert np.array_equal(q_back[ok], q.reshape(16, 2, 8, 32)[ok])
+
+
+def test_q5_k_weights_exact_and_fp32_target_rounds_once():
+    raw = synth.q5_k_weights(77, 32, 1024)
+    w = oracle.dequant_q5_k(raw, 32, 1024)
+    scaled = w * 2.0 ** 24
+    assert np.array_equal(scaled, np.rint(scaled)) and np.max(np.abs(scaled)) < 2.0 ** 50
+    w32 = oracle.dequant_q5_k_f32(raw, 32, 1024)
+    err = np.abs(w32.astype(np.float64) - w)
+    assert np.all(err <= 0.5 * np.spacing(np.abs(w32)).astype(np.float64))
+
+
+def test_q5_k_generator_distributions():
+    raw = synth.q5_k_weights(78, 128, 2048)
+    d, dmin, sc, m, q = oracle.q5_k_fields(raw, 128, 2048)
+    assert q.min() == 0 and q.max() == 31 and abs(q.mean() - 15.5) < 0.1
+    assert sc.min() == 0 and sc.max() == 63 and abs(m.mean() - 31.5) < 0.5
+    assert abs(d.mean() / (0.001 * np.sqrt(2 / np.pi)) - 1) < 0.03
+    assert abs(dmin.mean() / (0.002 * np.sqrt(2 / np.pi)) - 1) < 0.03
+
+
+def test_q5_k_rejects_wrong_sizes():
+    with pytest.raises(ValueError):
+        oracle.dequant_q5_k(bytes(175), 1, 256)
+    with pytest.raises(ValueError):
+        oracle.dequant_q5_k(bytes(176), 1, 128)
 
 
 # ---------------------------------------------------------------- IQ4_XS

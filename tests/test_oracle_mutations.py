@@ -21,12 +21,15 @@ SRC = inspect.getsource(gg)
 
 MUTATIONS = {
     "nibbles_swapped": [("= byte & 0x0F", "= byte >> 5"), ("= byte >> 4", "= byte & 0x0F"), ("= byte >> 5", "= byte >> 4")],
-    "chunk_order": [("byte = Q[:, :, 32 * c: 32 * c + 32]", "byte = Q[:, :, 32 * (3 - c): 32 * (3 - c) + 32]")],
-    "sc_from_min_byte": [("sc[:, :, j] = S[:, :, j] & 0x3F", "sc[:, :, j] = S[:, :, j + 4] & 0x3F")],
-    "sc_top_bits_wrong_byte": [("((S[:, :, j - 4] >> 6) << 4)", "((S[:, :, j] >> 6) << 4)")],
-    "m_top_bits_wrong_byte": [("m[:, :, j] = (S[:, :, j + 4] >> 4) | ((S[:, :, j] >> 6) << 4)",
-                               "m[:, :, j] = (S[:, :, j + 4] >> 4) | ((S[:, :, j - 4] >> 6) << 4)")],
-    "m_low_bits_from_low_nibble": [("m[:, :, j] = (S[:, :, j + 4] >> 4)", "m[:, :, j] = (S[:, :, j + 4] & 0x0F)")],
+    "chunk_order": [("byte = Q[..., 32 * c: 32 * c + 32]", "byte = Q[..., 32 * (3 - c): 32 * (3 - c) + 32]")],
+    "sc_from_min_byte": [("sc[..., j] = S[..., j] & 0x3F", "sc[..., j] = S[..., j + 4] & 0x3F")],
+    "sc_top_bits_wrong_byte": [("((S[..., j - 4] >> 6) << 4)", "((S[..., j] >> 6) << 4)")],
+    "m_top_bits_wrong_byte": [("m[..., j] = (S[..., j + 4] >> 4) | ((S[..., j] >> 6) << 4)",
+                               "m[..., j] = (S[..., j + 4] >> 4) | ((S[..., j - 4] >> 6) << 4)")],
+    "q5_high_bit_of_other_half": [("((H >> (2 * c)) & 1) << 4", "((H >> (2 * c + 1)) & 1) << 4")],
+    "q5_high_bit_weight_eight": [("q[:, :, 64 * c + 32: 64 * c + 64] += ((H >> (2 * c + 1)) & 1) << 4",
+                                  "q[:, :, 64 * c + 32: 64 * c + 64] += ((H >> (2 * c + 1)) & 1) << 3")],
+    "m_low_bits_from_low_nibble": [("m[..., j] = (S[..., j + 4] >> 4)", "m[..., j] = (S[..., j + 4] & 0x0F)")],
     "fp16_big_endian": [("(blocks[:, :, 0] | (blocks[:, :, 1] << 8))", "(blocks[:, :, 1] | (blocks[:, :, 0] << 8))")],
     "min_sign_flipped": [("return (scale * q - offset)", "return (scale * q + offset)")],
     "dmin_as_scale": [("scale = (d[:, :, None] * sc)", "scale = (dmin[:, :, None] * sc)")],
@@ -73,6 +76,13 @@ def _pins(o) -> list:
     def golden_q4():
         for blk in _golden("q4_k_handbuilt.json"):
             w = o.dequant_q4_k(bytes.fromhex(blk["hex"]), 1, 256)[0]
+            if not np.array_equal(w, [float.fromhex(v) for v in blk["expect"]]):
+                return False
+        return True
+
+    def golden_q5():
+        for blk in _golden("q5_k_handbuilt.json"):
+            w = o.dequant_q5_k(bytes.fromhex(blk["hex"]), 1, 256)[0]
             if not np.array_equal(w, [float.fromhex(v) for v in blk["expect"]]):
                 return False
         return True
@@ -134,6 +144,7 @@ def _pins(o) -> list:
         return list(got[0]) == [1 + 2.0 ** -7, 1.0] and np.array_equal(yb, wb_ref[:, :64].T)
 
     check("golden_q4", golden_q4)
+    check("golden_q5", golden_q5)
     check("golden_q8", golden_q8)
     check("gemv_unit_vectors", gemv_unit_vectors)
     check("route_hand_set", route_hand_set)

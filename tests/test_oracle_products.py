@@ -67,6 +67,35 @@ def test_iq4_xs_gemv_matches_exact_rational(n_rows, k, m):
             assert abs(Fraction(float(y[r, n])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
 
 
+@pytest.mark.parametrize("n_rows,k,m", [(3, 256, 1), (2, 512, 4)])
+def test_q5_k_gemv_matches_exact_rational(n_rows, k, m):
+    raw = synth.q5_k_weights(81 + m, n_rows, k)
+    x = synth.bf16_normal(82 + m, (m, k))
+    y = oracle.qmv_q5_k(raw, x, n_rows, k)
+    exact = _exact_dot_rows(oracle.dequant_q5_k(raw, n_rows, k), oracle.bf16_bits_to_f64(x))
+    assert y.shape == (m, n_rows)
+    for r in range(m):
+        for n in range(n_rows):
+            e = exact[r][n]
+            assert abs(Fraction(float(y[r, n])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
+
+
+def test_q5_k_gemv_constant_over_one_subblock_closed_form(golden_dir):
+    # x = 1 on sub-block j only: y = d sc_j sum(q over j) - 32 dmin m_j, from the stated fields
+    with open(os.path.join(golden_dir, "q5_k_handbuilt.json")) as f:
+        blocks = json.load(f)["blocks"]
+    for blk in blocks:
+        raw = bytes.fromhex(blk["hex"])
+        d = oracle.fp16_bits_to_f64(np.array([blk["d_bits"]]))[0]
+        dmin = oracle.fp16_bits_to_f64(np.array([blk["dmin_bits"]]))[0]
+        for j in range(8):
+            x = np.zeros((1, 256), dtype=np.uint16)
+            x[0, 32 * j:32 * j + 32] = 0x3F80
+            y = oracle.qmv_q5_k(raw, x, 1, 256)[0, 0]
+            qsum = sum(blk["q"][32 * j:32 * j + 32])
+            assert y == d * blk["sc"][j] * qsum - 32 * dmin * blk["m"][j], (blk["name"], j)
+
+
 def test_gemv_unit_vector_selects_a_column():
     n_rows, k = 7, 512
     raw = synth.q4_k_weights(61, n_rows, k)
