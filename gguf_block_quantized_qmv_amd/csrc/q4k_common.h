@@ -14,6 +14,7 @@
 namespace qmv {
 
 constexpr int kQ4KBlockBytes = 144;
+constexpr int kQ5KBlockBytes = 176;   // Q5_K: the Q4_K header, 32 bytes of fifth bits, the Q4_K nibbles
 constexpr int kQ4KBlockWeights = 256;
 
 // Byte-permute selectors and masks that extract, for 64-weight chunk c of a

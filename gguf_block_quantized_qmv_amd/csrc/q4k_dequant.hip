@@ -1,4 +1,4 @@
-// Q4_K dequantization to dense fp32 or bf16, gfx950.
+// Q4_K dequantization to dense fp32 or bf16, and Q5_K to fp32, gfx950.
 //
 // One thread per 16-byte quant granule (32 weights): granule g of a block holds
 // quant bytes 16g..16g+15, i.e. chunk c = g / 2, weights 64c + 16(g%2) + 0..15 in
@@ -65,7 +65,55 @@ __global__ __launch_bounds__(256) void q4k_dequant_kernel(const uint8_t *__restr
   }
 }
 
+// Q5_K to fp32: one thread per 16-byte nibble granule, as above, with the fifth
+// bit of weight 64c + 16(g%2) + i from bit 2c of high-plane byte 16(g%2) + i
+// and of weight 64c + 32 + 16(g%2) + i from bit 2c + 1. d*sc*q (q <= 31) is
+// still exact inside the fma, so the result is RN_fp32 of the exact weight.
+__global__ __launch_bounds__(256) void q5k_dequant_kernel(const uint8_t *__restrict__ w, float *__restrict__ out,
+                                                          const size_t ngran) {
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= ngran) return;
+  const size_t blk = t >> 3;
+  const int g = (int)(t & 7);
+  const int c = g >> 1;
+  const uint8_t *bp = w + blk * kQ5KBlockBytes;
+  const uint4 hdr = *reinterpret_cast<const uint4 *>(bp);
+  const uint4 hv = *reinterpret_cast<const uint4 *>(bp + 16 + 16 * (g & 1));
+  const uint4 qv = *reinterpret_cast<const uint4 *>(bp + 48 + 16 * g);
+  const uint32_t scm = unpack_scale_mins(hdr.y, hdr.z, hdr.w, scale_selectors(c));
+  const float d = fp16_bits_to_f32(hdr.x & 0xFFFFu);
+  const float dmin = fp16_bits_to_f32(hdr.x >> 16);
+  const float ds0 = d * (float)(scm & 0xFFu), ds1 = d * (float)((scm >> 8) & 0xFFu);
+  const float dm0 = dmin * (float)((scm >> 16) & 0xFFu), dm1 = dmin * (float)(scm >> 24);
+
+  const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+  const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+  float lo[16], hi[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t byte = (qw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+    const uint32_t hbits = (hw[i >> 2] >> (8 * (i & 3) + 2 * c)) & 3u;
+    lo[i] = __builtin_fmaf(ds0, (float)((byte & 0xFu) | ((hbits & 1u) << 4)), -dm0);
+    hi[i] = __builtin_fmaf(ds1, (float)((byte >> 4) | ((hbits >> 1) << 4)), -dm1);
+  }
+  const size_t base = blk * kQ4KBlockWeights + 64 * c + 16 * (g & 1);
+  float4 *o_lo = reinterpret_cast<float4 *>(out + base);
+  float4 *o_hi = reinterpret_cast<float4 *>(out + base + 32);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    o_lo[v] = make_float4(lo[4 * v], lo[4 * v + 1], lo[4 * v + 2], lo[4 * v + 3]);
+    o_hi[v] = make_float4(hi[4 * v], hi[4 * v + 1], hi[4 * v + 2], hi[4 * v + 3]);
+  }
+}
+
 }  // namespace
+
+int launch_dequant_q5_k(const void *w, float *out, int n, int k, void *stream) {
+  const size_t ngran = (size_t)n * (size_t)(k >> 8) * 8;
+  const unsigned grid = (unsigned)((ngran + 255) / 256);
+  return launch_kernel("q5k_dequant_kernel", q5k_dequant_kernel, dim3(grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint8_t *>(w), out, ngran);
+}
 
 int launch_dequant_q4_k(const void *w, void *out, bool bf16, int n, int k, void *stream) {
   const size_t ngran = (size_t)n * (size_t)(k >> 8) * 8;

@@ -128,11 +128,26 @@ __device__ __forceinline__ void x_sums(const uint4 *xs, float *xsum, const int g
 // converted right before the dot products that use them, so only 8 converted
 // pairs are live at a time. Each row keeps four dot2 chains (two per sub-block)
 // joined in a fixed order; the chain order does not depend on M.
-template <int M>
+// Q5_K (Q5 = true): the quants are 5-bit, q = nibble + 16 h with h from the
+// high-bit plane (hb0, hb1: its 32 bytes; bit hsh = 2c of byte l belongs to
+// weight 64c + l, bit 2c + 1 to weight 64c + 32 + l). q in [0, 31] is not exact
+// through the fp8 conversion, so each bf16 quant is built as 128 + q (bits
+// 0x43 | q: exact) with one byte permute per pair, and 128 X_j is taken off
+// per sub-block: acc += (d sc) (S' - 128 X) - (dmin m) X, S' = sum (128 + q) x.
+__device__ __forceinline__ bf16x2 biased_q5_pair_lo(const uint32_t q) {
+  return __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(0x43434343u, q, 0x04010400u));
+}
+__device__ __forceinline__ bf16x2 biased_q5_pair_hi(const uint32_t q) {
+  return __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(0x43434343u, q, 0x04030402u));
+}
+
+template <int M, bool Q5>
 __device__ __forceinline__ void dense_chunk(float (&acc)[M], const uint4 hdr, const uint4 qa, const uint4 qb,
-                                            const ScaleSel &sel, const uint4 *__restrict__ xc, const int gpp,
+                                            const uint4 hb0, const uint4 hb1, const int hsh, const ScaleSel &sel,
+                                            const uint4 *__restrict__ xc, const int gpp,
                                             const float *__restrict__ xsc, const int nsub) {
   const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+  const uint32_t hw[8] = {hb0.x, hb0.y, hb0.z, hb0.w, hb1.x, hb1.y, hb1.z, hb1.w};
   float s_lo0[M], s_lo1[M], s_hi0[M], s_hi1[M];
 #pragma unroll
   for (int r = 0; r < M; ++r) s_lo0[r] = s_lo1[r] = s_hi0[r] = s_hi1[r] = 0.0f;
@@ -140,10 +155,22 @@ __device__ __forceinline__ void dense_chunk(float (&acc)[M], const uint4 hdr, co
   for (int g = 0; g < 4; ++g) {
     const uint32_t l0 = qw[2 * g] & 0x0F0F0F0Fu, h0 = (qw[2 * g] >> 4) & 0x0F0F0F0Fu;
     const uint32_t l1 = qw[2 * g + 1] & 0x0F0F0F0Fu, h1 = (qw[2 * g + 1] >> 4) & 0x0F0F0F0Fu;
-    const bf16x2 lo0 = nibbles_to_bf16x2<false>(l0), lo1 = nibbles_to_bf16x2<true>(l0);
-    const bf16x2 lo2 = nibbles_to_bf16x2<false>(l1), lo3 = nibbles_to_bf16x2<true>(l1);
-    const bf16x2 hi0 = nibbles_to_bf16x2<false>(h0), hi1 = nibbles_to_bf16x2<true>(h0);
-    const bf16x2 hi2 = nibbles_to_bf16x2<false>(h1), hi3 = nibbles_to_bf16x2<true>(h1);
+    bf16x2 lo0, lo1, lo2, lo3, hi0, hi1, hi2, hi3;
+    if constexpr (Q5) {
+      // bit 0 of each byte of t: the low-nibble weight's fifth bit; bit 1: the high-nibble weight's
+      const uint32_t t0 = hw[2 * g] >> hsh, t1 = hw[2 * g + 1] >> hsh;
+      const uint32_t ql0 = l0 | ((t0 << 4) & 0x10101010u), qh0 = h0 | ((t0 << 3) & 0x10101010u);
+      const uint32_t ql1 = l1 | ((t1 << 4) & 0x10101010u), qh1 = h1 | ((t1 << 3) & 0x10101010u);
+      lo0 = biased_q5_pair_lo(ql0), lo1 = biased_q5_pair_hi(ql0);
+      lo2 = biased_q5_pair_lo(ql1), lo3 = biased_q5_pair_hi(ql1);
+      hi0 = biased_q5_pair_lo(qh0), hi1 = biased_q5_pair_hi(qh0);
+      hi2 = biased_q5_pair_lo(qh1), hi3 = biased_q5_pair_hi(qh1);
+    } else {
+      lo0 = nibbles_to_bf16x2<false>(l0), lo1 = nibbles_to_bf16x2<true>(l0);
+      lo2 = nibbles_to_bf16x2<false>(l1), lo3 = nibbles_to_bf16x2<true>(l1);
+      hi0 = nibbles_to_bf16x2<false>(h0), hi1 = nibbles_to_bf16x2<true>(h0);
+      hi2 = nibbles_to_bf16x2<false>(h1), hi3 = nibbles_to_bf16x2<true>(h1);
+    }
 #pragma unroll
     for (int r = 0; r < M; ++r) {
       const uint4 v = xc[r * gpp + g];
@@ -164,29 +191,43 @@ __device__ __forceinline__ void dense_chunk(float (&acc)[M], const uint4 hdr, co
     const float s_lo = s_lo0[r] + s_lo1[r], s_hi = s_hi0[r] + s_hi1[r];
     const float2 xsm = *reinterpret_cast<const float2 *>(xsc + r * nsub);
     acc[r] = __builtin_fmaf(cs.a0, s_lo, acc[r]);
+    if constexpr (Q5) acc[r] = __builtin_fmaf(-cs.a0, 128.0f * xsm.x, acc[r]);
     acc[r] = __builtin_fmaf(-cs.b0, xsm.x, acc[r]);
     acc[r] = __builtin_fmaf(cs.a1, s_hi, acc[r]);
+    if constexpr (Q5) acc[r] = __builtin_fmaf(-cs.a1, 128.0f * xsm.y, acc[r]);
     acc[r] = __builtin_fmaf(-cs.b1, xsm.y, acc[r]);
   }
 }
 
-// The three 16-byte weight loads of one step for the lane holding chunk c of a
-// block at bp: the block header and the chunk's 32 quant bytes.
+template <bool Q5>
+constexpr int block_bytes() { return Q5 ? kQ5KBlockBytes : kQ4KBlockBytes; }
+
+// The 16-byte weight loads of one step for the lane holding chunk c of a block
+// at bp: the block header and the chunk's 32 quant bytes, and for Q5_K the 32
+// bytes of the high-bit plane (every chunk's lane reads all of them).
+template <bool Q5>
 __device__ __forceinline__ void load_step(const uint8_t *__restrict__ bp, const int c, uint4 &hdr, uint4 &qa,
-                                          uint4 &qb) {
+                                          uint4 &qb, uint4 &hb0, uint4 &hb1) {
   hdr = *reinterpret_cast<const uint4 *>(bp);
-  qa = *reinterpret_cast<const uint4 *>(bp + 16 + 32 * c);
-  qb = *reinterpret_cast<const uint4 *>(bp + 32 + 32 * c);
+  if constexpr (Q5) {
+    hb0 = *reinterpret_cast<const uint4 *>(bp + 16);
+    hb1 = *reinterpret_cast<const uint4 *>(bp + 32);
+    qa = *reinterpret_cast<const uint4 *>(bp + 48 + 32 * c);
+    qb = *reinterpret_cast<const uint4 *>(bp + 64 + 32 * c);
+  } else {
+    qa = *reinterpret_cast<const uint4 *>(bp + 16 + 32 * c);
+    qb = *reinterpret_cast<const uint4 *>(bp + 32 + 32 * c);
+  }
 }
 
 // Block address of step t for this lane, or the matrix's first block when the
 // step does not exist for it (see the kernel); every address loaded stays
 // inside the weights.
-template <bool FULL, int kBlocksPerStep>
+template <bool FULL, int kBlocksPerStep, bool Q5>
 __device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *w, const uint8_t *wl, const bool active, const int t,
                                                    const int nsteps, const int jb, const int nblk) {
   const bool ok = active && t < nsteps && (FULL || t * kBlocksPerStep + jb < nblk);
-  return ok ? wl + (size_t)(t * kBlocksPerStep) * kQ4KBlockBytes : w;
+  return ok ? wl + (size_t)(t * kBlocksPerStep) * block_bytes<Q5>() : w;
 }
 
 // G lanes own one output row (G = 16 or 32): a step covers G/4 super-blocks of
@@ -214,14 +255,14 @@ __device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *w, const uint8
 constexpr int kMinThreads = 256;
 constexpr int kMaxThreads = 512;       // M = 1
 constexpr int kMaxThreadsRows = 768;   // M = 2..4: register use allows 3 waves per SIMD
+constexpr int kQ5Depth = 4;            // ring depth (steps) of the Q5_K instantiation
 
 template <int M, int G>
 constexpr int x_head() { return (G == 16 ? 4 * M : 9 * M) < 9 ? (G == 16 ? 4 * M : 9 * M) : 9; }
 
-template <int M, int G, int D, bool FULL, int NS>
-__global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q4k_gemv_kernel(const uint8_t *__restrict__ w,
-                                                            const uint16_t *__restrict__ x,
-                                                            float *__restrict__ y, const int n, const int k) {
+template <int M, int G, int D, bool FULL, int NS, bool Q5>
+__device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const uint16_t *__restrict__ x,
+                                          float *__restrict__ y, const int n, const int k) {
   constexpr int kBlocksPerStep = G / 4;
   constexpr int kStepGranules = (G / 2) * 17;   // padded LDS granules per step
   extern __shared__ uint4 lds[];
@@ -243,23 +284,26 @@ __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q4k_ge
   const int nsteps = NS > 0 ? NS : (nblk + kBlocksPerStep - 1) / kBlocksPerStep;
   // with NS > 0 only the last step can be partial: lanes past its blocks skip it
   const bool last_ok = jb < nblk - (nsteps - 1) * kBlocksPerStep;
-  const uint8_t *wl = w + (size_t)(active ? row : 0) * (size_t)nblk * kQ4KBlockBytes + (size_t)jb * kQ4KBlockBytes;
+  const uint8_t *wl = w + (size_t)(active ? row : 0) * (size_t)nblk * block_bytes<Q5>() +
+                      (size_t)jb * block_bytes<Q5>();
 
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
   constexpr int kXHead = x_head<M, G>();
   uint4 xv[kXHead];
   load_x_head<kXHead>(xg, M * gpr, nthreads, xv);
-  uint4 hdr[D], qa[D], qb[D];
+  uint4 hdr[D], qa[D], qb[D], hb0[D], hb1[D];
   if constexpr (M == 1) {
     // One step of weights goes out behind the activation head; the rest of the
     // ring only after the head has arrived and is in LDS. Requests queue in the
     // memory system in issue order, so every weight request issued before a
     // wave's activations are back delays them (and with them its first step).
-    load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, 0, nsteps, jb, nblk), c, hdr[0], qa[0], qb[0]);
+    load_step<Q5>(step_ptr<FULL, kBlocksPerStep, Q5>(w, wl, active, 0, nsteps, jb, nblk), c, hdr[0], qa[0], qb[0],
+                  hb0[0], hb1[0]);
     store_x_head<M, kXHead>(xv, xs, gpr, gpp, nthreads);
 #pragma unroll
     for (int u = 1; u < D; ++u)
-      load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
+      load_step<Q5>(step_ptr<FULL, kBlocksPerStep, Q5>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u],
+                    hb0[u], hb1[u]);
     // rows up to NS steps are covered by the head when this holds, and the
     // loop that stages the rest is compiled out
     if constexpr (NS == 0 || NS * G * 8 > kXHead * kMinThreads) stage_x_tail<M, kXHead, 2>(xg, xs, gpr, gpp, nthreads);
@@ -271,7 +315,8 @@ __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q4k_ge
     stage_x_tail<M, kXHead, 8>(xg, xs, gpr, gpp, nthreads);
 #pragma unroll
     for (int u = 0; u < D; ++u)
-      load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
+      load_step<Q5>(step_ptr<FULL, kBlocksPerStep, Q5>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u],
+                    hb0[u], hb1[u]);
   }
   x_sums<M>(xs, xsum, gpp, nsub, nthreads);
   if (!active) return;
@@ -289,9 +334,11 @@ __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q4k_ge
       constexpr int kD = D;
       const int u = s % kD;
       if (s < NS - 1 || last_ok)
-        dense_chunk<M>(acc, hdr[u], qa[u], qb[u], sel, xb + s * kStepGranules, gpp, sb + s * 2 * G, nsub);
+        dense_chunk<M, Q5>(acc, hdr[u], qa[u], qb[u], hb0[u], hb1[u], 2 * c, sel, xb + s * kStepGranules, gpp,
+                           sb + s * 2 * G, nsub);
       if (s + D < NS)
-        load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, s + D, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u]);
+        load_step<Q5>(step_ptr<FULL, kBlocksPerStep, Q5>(w, wl, active, s + D, nsteps, jb, nblk), c, hdr[u], qa[u],
+                      qb[u], hb0[u], hb1[u]);
     }
   } else {
     for (int s0 = 0; s0 < nsteps; s0 += D) {
@@ -299,9 +346,10 @@ __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q4k_ge
       for (int u = 0; u < D; ++u) {
         const int s = s0 + u;
         if (s < nsteps && (FULL || s * kBlocksPerStep + jb < nblk))
-          dense_chunk<M>(acc, hdr[u], qa[u], qb[u], sel, xb + s * kStepGranules, gpp, sb + s * 2 * G, nsub);
-        load_step(step_ptr<FULL, kBlocksPerStep>(w, wl, active, s + D, nsteps, jb, nblk), c, hdr[u], qa[u],
-                  qb[u]);
+          dense_chunk<M, Q5>(acc, hdr[u], qa[u], qb[u], hb0[u], hb1[u], 2 * c, sel, xb + s * kStepGranules, gpp,
+                             sb + s * 2 * G, nsub);
+        load_step<Q5>(step_ptr<FULL, kBlocksPerStep, Q5>(w, wl, active, s + D, nsteps, jb, nblk), c, hdr[u], qa[u],
+                      qb[u], hb0[u], hb1[u]);
       }
     }
   }
@@ -311,6 +359,20 @@ __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q4k_ge
     const float v = group_sum<G>(acc[r]);
     if (j == r) y[(size_t)r * n + row] = v;
   }
+}
+
+template <int M, int G, int D, bool FULL, int NS>
+__global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q4k_gemv_kernel(const uint8_t *__restrict__ w,
+                                                            const uint16_t *__restrict__ x,
+                                                            float *__restrict__ y, const int n, const int k) {
+  gemv_body<M, G, D, FULL, NS, false>(w, x, y, n, k);
+}
+
+template <int M, int G, int D, bool FULL, int NS>
+__global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q5k_gemv_kernel(const uint8_t *__restrict__ w,
+                                                            const uint16_t *__restrict__ x,
+                                                            float *__restrict__ y, const int n, const int k) {
+  gemv_body<M, G, D, FULL, NS, true>(w, x, y, n, k);
 }
 
 // Rows per workgroup. A launch is balanced when every CU gets the same number
@@ -334,50 +396,51 @@ inline int pick_rows(const int m, const int n, const int G, const size_t lds) {
   return dflt;
 }
 
-template <int M, int G, int D, bool FULL, int NS>
+template <int M, int G, int D, bool FULL, int NS, bool Q5>
 int launch_cfg(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
   const size_t lds = dense_lds_bytes<M>(k);
-  auto *fn = q4k_gemv_kernel<M, G, D, FULL, NS>;
+  auto *fn = Q5 ? q5k_gemv_kernel<M, G, D, FULL, NS> : q4k_gemv_kernel<M, G, D, FULL, NS>;
+  const char *name = Q5 ? "q5k_gemv_kernel" : "q4k_gemv_kernel";
   static std::atomic<size_t> granted{0};
-  if (allow_dynamic_lds(reinterpret_cast<const void *>(fn), lds, granted, "q4k_gemv_kernel lds")) return QMV_ERR_HIP;
+  if (allow_dynamic_lds(reinterpret_cast<const void *>(fn), lds, granted, name)) return QMV_ERR_HIP;
   const int rows = pick_rows(M, n, G, lds);
   const unsigned grid = (unsigned)((n + rows - 1) / rows);
-  return launch_kernel("q4k_gemv_kernel", fn, dim3(grid), dim3(rows * G), lds, stream, w, x, y, n, k);
+  return launch_kernel(name, fn, dim3(grid), dim3(rows * G), lds, stream, w, x, y, n, k);
 }
 
 // Runtime-length rows (any K).
-template <int M, int G, int D>
+template <int M, int G, int D, bool Q5>
 int launch_any(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
-  if (((k >> 8) % (G / 4)) == 0) return launch_cfg<M, G, D, true, 0>(w, x, y, n, k, stream);
-  return launch_cfg<M, G, D, false, 0>(w, x, y, n, k, stream);
+  if (((k >> 8) % (G / 4)) == 0) return launch_cfg<M, G, D, true, 0, Q5>(w, x, y, n, k, stream);
+  return launch_cfg<M, G, D, false, 0, Q5>(w, x, y, n, k, stream);
 }
 
 // Lanes per row by row length: 16 up to K = 8192 (1..8 steps of 4 blocks), 32
 // beyond (steps of 8 blocks; 5..9 steps up to K = 18432, runtime loop after).
 // The ring is 4 steps deep.
-template <int M>
+template <int M, bool Q5>
 int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
-  constexpr int D = 4;
+  constexpr int D = Q5 ? kQ5Depth : 4;
   const int nblk = k >> 8;
   if (k <= 8192) {
     switch ((nblk + 3) / 4) {
-      case 1: return launch_cfg<M, 16, D, true, 1>(w, x, y, n, k, stream);
-      case 2: return launch_cfg<M, 16, D, true, 2>(w, x, y, n, k, stream);
-      case 3: return launch_cfg<M, 16, D, true, 3>(w, x, y, n, k, stream);
-      case 4: return launch_cfg<M, 16, D, true, 4>(w, x, y, n, k, stream);
-      case 5: return launch_cfg<M, 16, D, true, 5>(w, x, y, n, k, stream);
-      case 6: return launch_cfg<M, 16, D, true, 6>(w, x, y, n, k, stream);
-      case 7: return launch_cfg<M, 16, D, true, 7>(w, x, y, n, k, stream);
-      default: return launch_cfg<M, 16, D, true, 8>(w, x, y, n, k, stream);
+      case 1: return launch_cfg<M, 16, D, true, 1, Q5>(w, x, y, n, k, stream);
+      case 2: return launch_cfg<M, 16, D, true, 2, Q5>(w, x, y, n, k, stream);
+      case 3: return launch_cfg<M, 16, D, true, 3, Q5>(w, x, y, n, k, stream);
+      case 4: return launch_cfg<M, 16, D, true, 4, Q5>(w, x, y, n, k, stream);
+      case 5: return launch_cfg<M, 16, D, true, 5, Q5>(w, x, y, n, k, stream);
+      case 6: return launch_cfg<M, 16, D, true, 6, Q5>(w, x, y, n, k, stream);
+      case 7: return launch_cfg<M, 16, D, true, 7, Q5>(w, x, y, n, k, stream);
+      default: return launch_cfg<M, 16, D, true, 8, Q5>(w, x, y, n, k, stream);
     }
   }
   switch ((nblk + 7) / 8) {
-    case 5: return launch_cfg<M, 32, D, true, 5>(w, x, y, n, k, stream);
-    case 6: return launch_cfg<M, 32, D, true, 6>(w, x, y, n, k, stream);
-    case 7: return launch_cfg<M, 32, D, true, 7>(w, x, y, n, k, stream);
-    case 8: return launch_cfg<M, 32, D, true, 8>(w, x, y, n, k, stream);
-    case 9: return launch_cfg<M, 32, D, true, 9>(w, x, y, n, k, stream);
-    default: return launch_any<M, 32, D>(w, x, y, n, k, stream);
+    case 5: return launch_cfg<M, 32, D, true, 5, Q5>(w, x, y, n, k, stream);
+    case 6: return launch_cfg<M, 32, D, true, 6, Q5>(w, x, y, n, k, stream);
+    case 7: return launch_cfg<M, 32, D, true, 7, Q5>(w, x, y, n, k, stream);
+    case 8: return launch_cfg<M, 32, D, true, 8, Q5>(w, x, y, n, k, stream);
+    case 9: return launch_cfg<M, 32, D, true, 9, Q5>(w, x, y, n, k, stream);
+    default: return launch_any<M, 32, D, Q5>(w, x, y, n, k, stream);
   }
 }
 
@@ -386,10 +449,21 @@ int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream
 int launch_q4_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (m) {
-    case 1: return launch_m<1>(w, x, y, n, k, s);
-    case 2: return launch_m<2>(w, x, y, n, k, s);
-    case 3: return launch_m<3>(w, x, y, n, k, s);
-    case 4: return launch_m<4>(w, x, y, n, k, s);
+    case 1: return launch_m<1, false>(w, x, y, n, k, s);
+    case 2: return launch_m<2, false>(w, x, y, n, k, s);
+    case 3: return launch_m<3, false>(w, x, y, n, k, s);
+    case 4: return launch_m<4, false>(w, x, y, n, k, s);
+    default: return QMV_ERR_RANGE;
+  }
+}
+
+int launch_q5_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (m) {
+    case 1: return launch_m<1, true>(w, x, y, n, k, s);
+    case 2: return launch_m<2, true>(w, x, y, n, k, s);
+    case 3: return launch_m<3, true>(w, x, y, n, k, s);
+    case 4: return launch_m<4, true>(w, x, y, n, k, s);
     default: return QMV_ERR_RANGE;
   }
 }

@@ -116,6 +116,21 @@ int qmv_q4_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
              int m, int n, int k, void *stream);
 
 /*
+ * Q5_K matrix times bf16 activation rows (m = 1..4): the K-quant sibling that
+ * Q4_K_M files mix in (memra README model support table; the memra-bench card
+ * flags a Q5_K expert mix). 176-byte blocks: the Q4_K header, 32 bytes whose
+ * bit 2c (2c + 1) of byte l is the fifth bit of weight 64c + l (64c + 32 + l),
+ * then the Q4_K nibbles; weight = d*sc_j*q - dmin*m_j with q in [0, 31].
+ *   w       [n rows][k/256 blocks] Q5_K, 16-byte aligned; w_bytes == n*(k/256)*176
+ *   x_bf16, y, m, n, k and the LDS limit as for qmv_q4_k.
+ * The quants enter the products as the exact bf16 values 128 + q and 128 times
+ * each sub-block's activation sum is taken off in fp32, so the result carries
+ * fp32 rounding only. Row r of y is bit-identical for every m.
+ */
+int qmv_q5_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
+             int m, int n, int k, void *stream);
+
+/*
  * IQ4_XS matrix times bf16 activation rows (decode m=1, verify m=2..4).
  *   w       [n rows][k/256 blocks] IQ4_XS (136-byte super-blocks of 256 weights:
  *           fp16 d, 16 bits holding the top two bits of eight 6-bit sub-block
@@ -235,11 +250,13 @@ int qmm_q4_k_prefill(const void *w, size_t w_bytes, const uint16_t *x_bf16, floa
  * fp32: each weight is the exact block value rounded once to fp32 (nearest
  * even; Q8_0 and IQ4_XS weights are exact in fp32). bf16: that fp32 value
  * rounded to bf16 (nearest even). IQ4_XS: w is 8-byte aligned, 136-byte blocks.
+ * Q5_K: 16-byte aligned, 176-byte blocks.
  */
 int qmv_dequant_q4_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 int qmv_dequant_q4_k_bf16(const void *w, size_t w_bytes, uint16_t *out, int n, int k, void *stream);
 int qmv_dequant_q8_0_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 int qmv_dequant_iq4_xs_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
+int qmv_dequant_q5_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 
 #ifdef __cplusplus
 }

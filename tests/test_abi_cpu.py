@@ -35,6 +35,7 @@ def test_header_lists_the_expected_entry_points():
     assert _header_functions() == sorted([
         "qmv_version", "qmv_strerror", "qmv_last_error", "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe_workspace",
         "qmv_q4_k_moe", "qmv_dequant_iq4_xs_f32", "qmv_iq4_xs_moe_workspace", "qmv_iq4_xs_moe",
+        "qmv_q5_k", "qmv_dequant_q5_k_f32",
         "qmm_q4_k_prefill_workspace", "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16",
         "qmv_dequant_q8_0_f32"])
 
@@ -79,6 +80,28 @@ def test_q4_k_every_truncated_or_padded_size_is_an_error():
         assert q4k(nbytes=b, n=n, k=k) == SIZE, b
     assert q4k(nbytes=full + 1, n=n, k=k) == SIZE
     assert q4k(nbytes=2 * full, n=n, k=k) == SIZE
+
+
+def q5k(w=W, nbytes=None, x=X, y=Y, m=1, n=2, k=256):
+    nbytes = q.q5_k_bytes(n, k) if nbytes is None else nbytes
+    return L.qmv_q5_k(V(w), nbytes, V(x), V(y), m, n, k, None)
+
+
+def test_q5_k_validation():
+    assert q5k(w=0) == NULL and q5k(x=0) == NULL and q5k(y=0) == NULL
+    assert q5k(m=0) == RANGE and q5k(m=5) == RANGE
+    assert q5k(n=0) == SHAPE and q5k(k=0) == SHAPE and q5k(k=255) == SHAPE and q5k(k=384) == SHAPE
+    assert q5k(w=W + 8) == ALIGN and q5k(x=X + 2) == ALIGN and q5k(y=Y + 2) == ALIGN
+    assert q5k(m=4, k=19456) == RANGE
+    assert q5k(y=W + 64) == ALIAS
+    full = q.q5_k_bytes(2, 512)
+    assert q.q5_k_bytes(2, 512) == 2 * 2 * 176
+    for b in list(range(full)) + [full + 1, full + 176, q.q4_k_bytes(2, 512)]:
+        assert q5k(nbytes=b, k=512) == SIZE, b
+    nb = q.q5_k_bytes(2, 256)
+    f = L.qmv_dequant_q5_k_f32
+    assert f(V(0), nb, V(Y), 2, 256, None) == NULL and f(V(W), nb - 1, V(Y), 2, 256, None) == SIZE
+    assert f(V(W), nb, V(Y + 4), 2, 256, None) == ALIGN and f(V(W), nb, V(W), 2, 256, None) == ALIAS
 
 
 def iq4(w=W, nbytes=None, x=X, y=Y, m=1, n=2, k=256):
