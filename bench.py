@@ -37,8 +37,8 @@ HBM_PEAK_GBPS = 8000.0
 GEMV_TRAFFIC = {
     "sources": ("gguf_block_quantized_qmv_amd/csrc/q4k_gemv.hip", "gguf_block_quantized_qmv_amd/csrc/q4k_common.h",
                 "gguf_block_quantized_qmv_amd/csrc/qmv_device.h"),
-    "sha256": "8113dc3561110aeb437cd228536f9d7989c75b57a2554c7e8e33614b25f1ab14",
-    "bytes_per_launch": 51161335,
+    "sha256": "c4e34d16d635d2b6d8af29870d1f3d85c99bf16ce5e3944859b33665088c7f29",
+    "bytes_per_launch": 51159505,
 }
 
 
@@ -74,9 +74,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--copies", type=int, default=128, help="layer copies in the dense weight pool")
     p.add_argument("--moe-banks", type=int, default=48)
-    p.add_argument("--iq4-copies", type=int, default=48, help="layer copies in the IQ4_XS weight pool")
+    p.add_argument("--iq4-copies", type=int, default=48, help="layer copies in the IQ4_XS and Q5_K weight pools")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
-    p.add_argument("--skip", default="", help="comma list of sections to skip: verify,q8,moe,prefill,iq4,cpu")
+    p.add_argument("--skip", default="", help="comma list of sections to skip: verify,q8,moe,prefill,iq4,q5,cpu")
     return p.parse_args()
 
 
@@ -267,9 +267,12 @@ def main():
     del pool
     torch.cuda.empty_cache()
     if "iq4" not in skip:
-        res["iq4_xs_gemv"] = bench_iq4(args, torch, np, q, synth, timer, dev, sp)
+        res["iq4_xs_gemv"] = bench_format(args, torch, np, q, synth, timer, dev, sp, "iq4_xs")
         if "moe" not in skip:
             res["moe_iq4_xs"] = bench_moe(args, torch, np, q, synth, timer, dev, sp, fmt="iq4_xs")
+        torch.cuda.empty_cache()
+    if "q5" not in skip:
+        res["q5_k_gemv"] = bench_format(args, torch, np, q, synth, timer, dev, sp, "q5_k")
         torch.cuda.empty_cache()
 
     cpu = None
@@ -379,16 +382,19 @@ def bench_moe(args, torch, np, q, synth, timer, dev, sp, fmt="q4_k"):
     return out
 
 
-def bench_iq4(args, torch, np, q, synth, timer, dev, sp):
-    """IQ4_XS GEMV over a pool of layer copies (the dense FFN shapes), M = 1..4."""
+def bench_format(args, torch, np, q, synth, timer, dev, sp, fmt):
+    """GEMV of another block format (IQ4_XS or Q5_K) over a pool of layer copies
+    (the dense FFN shapes), M = 1..4."""
     L = q.lib
     copies = args.iq4_copies
-    log(f"[bench] generating the IQ4_XS pool: {copies} layer copies")
-    pool = [[synth.torch_iq4_xs_weights(41, n, k, dev, stream=3 * c + i) for i, (_, n, k) in enumerate(SHAPES)]
-            for c in range(copies)]
+    gen = {"iq4_xs": synth.torch_iq4_xs_weights, "q5_k": synth.torch_q5_k_weights}[fmt]
+    entry = {"iq4_xs": L.qmv_iq4_xs, "q5_k": L.qmv_q5_k}[fmt]
+    nbytes = {"iq4_xs": q.iq4_xs_bytes, "q5_k": q.q5_k_bytes}[fmt]
+    log(f"[bench] generating the {fmt} pool: {copies} layer copies")
+    pool = [[gen(41, n, k, dev, stream=3 * c + i) for i, (_, n, k) in enumerate(SHAPES)] for c in range(copies)]
     xs = {k: torch.from_numpy(synth.bf16_normal(42, (4, k)).view(np.int16)).to(dev) for _, _, k in SHAPES}
     ys = {n: torch.empty((4, n), dtype=torch.float32, device=dev) for _, n, _ in SHAPES}
-    shape_bytes = [q.iq4_xs_bytes(n, k) for _, n, k in SHAPES]
+    shape_bytes = [nbytes(n, k) for _, n, k in SHAPES]
     out = {}
 
     def calls_for(m, shapes):
@@ -399,9 +405,9 @@ def bench_iq4(args, torch, np, q, synth, timer, dev, sp):
     def stepper(cl):
         def step():
             for a in cl:
-                rc = L.qmv_iq4_xs(*a)
+                rc = entry(*a)
                 if rc:
-                    raise q.QmvError(rc, "qmv_iq4_xs")
+                    raise q.QmvError(rc, f"qmv_{fmt}")
         return step
 
     for m in (1, 2, 3, 4):
@@ -414,7 +420,7 @@ def bench_iq4(args, torch, np, q, synth, timer, dev, sp):
     for i, (name, n, k) in enumerate(SHAPES):
         t = timer.run(stepper(calls_for(1, (i,))), max(2, args.steps // 2)) / copies
         out[f"M1_{name}"] = {"us_per_launch": t * 1e6, "GBps": shape_bytes[i] / t / 1e9}
-    log("[bench] IQ4_XS GEMV: " + ", ".join(f"M={m} {out[f'M{m}']['GBps']:.0f} GB/s" for m in (1, 2, 3, 4)) +
+    log(f"[bench] {fmt} GEMV: " + ", ".join(f"M={m} {out[f'M{m}']['GBps']:.0f} GB/s" for m in (1, 2, 3, 4)) +
         "; M=1 per launch " + ", ".join(f"{nm} {out[f'M1_{nm}']['us_per_launch']:.2f} us" for nm, _, _ in SHAPES))
     del pool
     return out
