@@ -26,6 +26,8 @@ values -- so this oracle is that definition written out in fp64:
 
 The byte layouts are the public GGUF ones (Q8_0: fp16 d + 32 int8; Q4_K: fp16
 d, fp16 dmin, 12 bytes of packed 6-bit scales and mins, 128 bytes of nibbles;
+Q5_K: Q4_K plus a 32-byte plane of fifth bits; Q6_K: a 4-bit and a 2-bit plane
+of signed 6-bit quants, 16 int8 scales, fp16 d;
 IQ4_XS: fp16 d, 6-bit sub-block scales in 6 bytes, 128 bytes of 4-bit indices
 into a 16-entry integer grid), restated in this module's own words next to the
 code that reads them.
@@ -34,8 +36,9 @@ Parity pins live in tests/test_oracle_*.py (hand-built blocks written as hex,
 locality invariants, pack/unpack bijection, requantisation round trips, exact
 rational brute force, closed forms, MoE = weighted dense sum).
 
-Parity unpinned: that the Q4_K 6-bit scale/min packing and nibble order, and
-the IQ4_XS scale packing, index order and 16-entry grid, used here equal those
+Parity unpinned: that the Q4_K 6-bit scale/min packing and nibble order, the
+Q5_K and Q6_K bit planes, and the IQ4_XS scale packing, index order and
+16-entry grid, used here equal those
 of real llama.cpp-written GGUF tensors. No GGUF file, gguf
 package or llama.cpp is in reach, and the pages print no block bytes, so every
 in-repository check would also pass with a self-consistent mis-layout.
@@ -259,6 +262,74 @@ def dequant_q5_k_f32(raw, n_rows: int, k: int) -> np.ndarray:
     return round_to_f32(dequant_q5_k(raw, n_rows, k))
 
 
+# ----------------------------------------------------------------------------
+# Q6_K: 210-byte super-blocks of 256 weights along K
+# ----------------------------------------------------------------------------
+#
+# The other sibling K-quant a Q4_K_M file mixes in (the memra README's model
+# support table lists Q4_K_M GGUF files). Public GGUF layout, restated: signed
+# 6-bit quants in a 4-bit plane and a 2-bit plane, one int8 scale per 16
+# weights, one fp16 d; no min term.
+
+Q6_K_BLOCK_BYTES = 210
+
+
+def q6_k_fields(raw, n_rows: int, k: int):
+    """Decode a row-major Q6_K matrix into its fields.
+
+    Returns (d, sc, q):
+      d  : float64 [N, nb]       the fp16 super-block scale
+      sc : int64   [N, nb, 16]   the int8 scale of weights 16i .. 16i + 15
+      q  : int64   [N, nb, 256]  the signed quant of each weight, in [-32, 31]
+
+    Byte layout of one super-block (block b of row n starts at (n*K/256 + b)*210):
+      0..127    L[0..127]: low 4 bits of the quants
+      128..191  H[0..63]:  high 2 bits of the quants
+      192..207  S[0..15]:  int8 scales
+      208..209  fp16 d
+    Weight 128h + 32c + l (half h = 0, 1; quarter c = 0..3; l < 32) takes its
+    low bits from L[64h + 32(c % 2) + l] (the low nibble for c < 2, the high
+    nibble for c >= 2), its high bits from bits 2c, 2c + 1 of H[32h + l], and
+    its scale from S[8h + 2c + l // 16]; q = low + 16 * high - 32.
+    """
+    if k % Q4_K_BLOCK_WEIGHTS:
+        raise ValueError("Q6_K needs K to be a multiple of 256")
+    nb = k // Q4_K_BLOCK_WEIGHTS
+    b = _as_bytes(raw)
+    if b.size != n_rows * nb * Q6_K_BLOCK_BYTES:
+        raise ValueError("byte count does not match the Q6_K shape")
+    blocks = b.reshape(n_rows, nb, Q6_K_BLOCK_BYTES).astype(np.int64)
+    L = blocks[:, :, 0:128]
+    H = blocks[:, :, 128:192]
+    sc = blocks[:, :, 192:208].astype(np.uint8).view(np.int8).astype(np.int64)
+    d = fp16_bits_to_f64((blocks[:, :, 208] | (blocks[:, :, 209] << 8)).astype(np.uint16))
+    q = np.empty((n_rows, nb, 256), dtype=np.int64)
+    for h in range(2):
+        for c in range(4):
+            low_src = L[:, :, 64 * h + 32 * (c % 2): 64 * h + 32 * (c % 2) + 32]
+            low = (low_src & 0x0F) if c < 2 else (low_src >> 4)
+            high = (H[:, :, 32 * h: 32 * h + 32] >> (2 * c)) & 3
+            q[:, :, 128 * h + 32 * c: 128 * h + 32 * c + 32] = low + 16 * high - 32
+    return d, sc, q
+
+
+def dequant_q6_k(raw, n_rows: int, k: int) -> np.ndarray:
+    """Exact Q6_K weights: w = d * sc_i * q for weight 16i + t of a super-block.
+
+    float64 [N, K]; every weight is an integer multiple of 2^-24 below 2^40.
+    """
+    d, sc, q = q6_k_fields(raw, n_rows, k)
+    nb = k // Q4_K_BLOCK_WEIGHTS
+    scale = (d[:, :, None] * sc).repeat(16, axis=2)
+    return (scale * q).reshape(n_rows, nb * 256)
+
+
+def dequant_q6_k_f32(raw, n_rows: int, k: int) -> np.ndarray:
+    """The fp32 dequantization target: each exact Q6_K weight rounded once to fp32
+    (d*sc*q can need 25 significant bits)."""
+    return round_to_f32(dequant_q6_k(raw, n_rows, k))
+
+
 def dequant_q8_0_f32(raw, n_rows: int, k: int) -> np.ndarray:
     """Q8_0 weights in fp32 (exact: d has 11 significant bits, q at most 7)."""
     return round_to_f32(dequant_q8_0(raw, n_rows, k))
@@ -362,6 +433,11 @@ def qmv_q8_0(raw, x_f32, n_rows: int, k: int) -> np.ndarray:
 def qmv_q5_k(raw, x_bf16_bits, n_rows: int, k: int) -> np.ndarray:
     """Q5_K matrix times bf16 activation rows -> float64 [M, N]."""
     return gemv(dequant_q5_k(raw, n_rows, k), bf16_bits_to_f64(x_bf16_bits))
+
+
+def qmv_q6_k(raw, x_bf16_bits, n_rows: int, k: int) -> np.ndarray:
+    """Q6_K matrix times bf16 activation rows -> float64 [M, N]."""
+    return gemv(dequant_q6_k(raw, n_rows, k), bf16_bits_to_f64(x_bf16_bits))
 
 
 def qmv_q4_k(raw, x_bf16_bits, n_rows: int, k: int) -> np.ndarray:

@@ -38,6 +38,8 @@ __all__ = [
     "torch_q4_k_weights",
     "iq4_xs_weights",
     "q5_k_weights",
+    "q6_k_weights",
+    "torch_q6_k_weights",
     "torch_q5_k_weights",
     "torch_iq4_xs_weights",
 ]
@@ -47,6 +49,7 @@ _Q8_0_BYTES, _Q8_0_WEIGHTS = 34, 32
 _Q4_K_BYTES, _Q4_K_WEIGHTS = 144, 256
 _IQ4_XS_BYTES, _IQ4_XS_WEIGHTS = 136, 256
 _Q5_K_BYTES = 176
+_Q6_K_BYTES = 210
 
 
 def rng(seed: int, *stream: int) -> np.random.Generator:
@@ -155,6 +158,40 @@ def torch_q5_k_weights(seed: int, n_rows: int, k: int, device, *, stream: int = 
     dm = torch.randn((nb, 1), dtype=torch.float32, device=device, generator=g).abs_().mul_(dmin_scale)
     blocks[:, 0:2] = d.to(torch.float16).view(torch.uint8).view(nb, 2)
     blocks[:, 2:4] = dm.to(torch.float16).view(torch.uint8).view(nb, 2)
+    return blocks.reshape(-1)
+
+
+def q6_k_weights(seed: int, n_rows: int, k: int, *, stream: int = 0, d_scale: float = 0.0002) -> np.ndarray:
+    """Row-major Q6_K matrix bytes.
+
+    Per 210-byte super-block: 208 uniform random bytes (the two quant planes and
+    16 int8 scales: q ~ U[-32, 31], sc ~ U[-128, 127] i.i.d.), then fp16
+    d = |N(0,1)|*0.0002, which puts d*sc*q at the Q4_K recipe's magnitude.
+    Returns a flat uint8 array of n_rows * (k/256) * 210 bytes.
+    """
+    if k % _Q4_K_WEIGHTS:
+        raise ValueError("k must be a multiple of 256")
+    nb = n_rows * (k // _Q4_K_WEIGHTS)
+    g = rng(seed, 6, stream)
+    out = g.integers(0, 256, size=(nb, _Q6_K_BYTES), dtype=np.uint8)
+    d = (np.abs(g.standard_normal(nb)) * d_scale).astype(np.float16)
+    out[:, 208:210] = d.view(np.uint8).reshape(nb, 2)
+    return out.reshape(-1)
+
+
+def torch_q6_k_weights(seed: int, n_rows: int, k: int, device, *, stream: int = 0, d_scale: float = 0.0002):
+    """Device-side Q6_K matrix bytes with the recipe of q6_k_weights (d rounded
+    from fp32). Returns a flat uint8 device tensor."""
+    import torch
+
+    if k % _Q4_K_WEIGHTS:
+        raise ValueError("k must be a multiple of 256")
+    nb = n_rows * (k // _Q4_K_WEIGHTS)
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1_000_003 + int(stream) * 7919 + 66) & 0x7FFF_FFFF_FFFF_FFFF)
+    blocks = torch.randint(0, 256, (nb, _Q6_K_BYTES), dtype=torch.uint8, device=device, generator=g)
+    d = torch.randn((nb, 1), dtype=torch.float32, device=device, generator=g).abs_().mul_(d_scale)
+    blocks[:, 208:210] = d.to(torch.float16).view(torch.uint8).view(nb, 2)
     return blocks.reshape(-1)
 
 

@@ -1,4 +1,4 @@
-"""Writes tests/golden/{q8_0,q4_k,q5_k,iq4_xs}_handbuilt.json: hand-built blocks with known values.
+"""Writes tests/golden/{q8_0,q4_k,q5_k,q6_k,iq4_xs}_handbuilt.json: hand-built blocks with known values.
 
 Run from the repository root:  python tests/golden/make_handbuilt_blocks.py
 
@@ -11,7 +11,8 @@ as literals; the script stops if its encoder disagrees with them.
 
 The expected weights are computed here from the stated fields with exact
 rational arithmetic (w = d*q for Q8_0, w = d*sc_j*q - dmin*m_j for Q4_K,
-w = d*(ls_j - 32)*grid[q] for IQ4_XS, the Q4_K form with 5-bit q for Q5_K);
+w = d*(ls_j - 32)*grid[q] for IQ4_XS, the Q4_K form with 5-bit q for Q5_K,
+w = d*sc_i*q for Q6_K);
 they are closed forms by construction
 and do not come from the oracle or the GPU. The memra pages name these formats
 (memra README, model support table: Q8_0, Q4_K_M and IQ4_XS GGUF models) but
@@ -142,6 +143,38 @@ Q5_K_BLOCKS = [
 ]
 
 
+# ---------------------------------------------------------------- Q6_K
+
+def pack_q6_planes(q: list[int]) -> bytes:
+    """The 128 low-bit and 64 high-bit bytes of signed 6-bit quants q in [-32, 31]:
+    weight 128h + 32c + l (u = q + 32) puts u & 15 in L[64h + 32(c % 2) + l] (low
+    nibble for c < 2, high nibble otherwise) and u >> 4 in bits 2c, 2c + 1 of H[32h + l]."""
+    assert len(q) == 256 and all(-32 <= v < 32 for v in q)
+    low = bytearray(128)
+    high = bytearray(64)
+    for h in range(2):
+        for c in range(4):
+            for l in range(32):
+                u = q[128 * h + 32 * c + l] + 32
+                low[64 * h + 32 * (c % 2) + l] |= (u & 15) << (0 if c < 2 else 4)
+                high[32 * h + l] |= (u >> 4) << (2 * c)
+    return bytes(low) + bytes(high)
+
+
+# (name, d_bits, sc[16] int8, q[256], hand-derived low-plane bytes, hand-derived high-plane bytes)
+Q6_K_BLOCKS = [
+    ("all_min", 0x3C00, [1] * 16, [-32] * 256, "00" * 128, "00" * 64),
+    ("all_max", 0x3800, [127, -128] * 8, [31] * 256, "ff" * 128, "ff" * 64),
+    ("all_zero_quants", 0x3C00, [5] * 16, [0] * 256, "00" * 128, "aa" * 64),
+    ("quarter_code", 0x3C00, [1, -1, 2, -2, 3, -3, 4, -4, 5, -5, 6, -6, 7, -7, 8, -8],
+     [16 * ((i % 128) // 32) + 1 - 32 for i in range(256)], "11" * 128, "e4" * 64),
+    ("position_code", 0x0001, [1, 2, 4, 8, 16, 32, 64, 127, -1, -2, -4, -8, -16, -32, -64, -128],
+     [(i % 32) % 16 - 32 for i in range(256)], "00112233445566778899aabbccddeeff" * 8, "00" * 64),
+    ("negative_d", 0xB400, [100, -100, 50, -50, 25, -25, 12, -12, 6, -6, 3, -3, 1, -1, 0, 0],
+     [-1] * 256, "ff" * 128, "55" * 64),
+]
+
+
 # ---------------------------------------------------------------- IQ4_XS
 
 IQ4_XS_GRID = [-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113]
@@ -241,6 +274,25 @@ def main() -> None:
             "expect": [frac_to_hex(v) for v in expect],
         })
 
+    q6 = []
+    for name, d_bits, sc, q, l_hex, h_hex in Q6_K_BLOCKS:
+        planes = pack_q6_planes(q)
+        if planes[:128].hex() != l_hex or planes[128:].hex() != h_hex:
+            raise SystemExit(f"{name}: encoder gives {planes.hex()}, hand derivation says {l_hex}{h_hex}")
+        assert all(-128 <= v < 128 for v in sc)
+        raw = planes + bytes([v & 0xFF for v in sc]) + bytes([d_bits & 0xFF, d_bits >> 8])
+        assert len(raw) == 210
+        d = fp16_value(d_bits)
+        expect = [d * sc[i // 16] * q[i] for i in range(256)]
+        q6.append({
+            "name": name,
+            "d_bits": d_bits,
+            "sc": sc,
+            "q": q,
+            "hex": raw.hex(),
+            "expect": [frac_to_hex(v) for v in expect],
+        })
+
     iq4 = []
     for name, d_bits, ls, q, s_hex in IQ4_XS_BLOCKS:
         s_bytes = pack_iq4_xs_scales(ls)
@@ -271,6 +323,10 @@ def main() -> None:
     with open(os.path.join(HERE, "q5_k_handbuilt.json"), "w") as f:
         json.dump({"citation": note.replace("(Q8_0, Q4_K_M GGUF)", "(Q8_0, Q4_K_M GGUF, whose K-quant mix includes Q5_K)"),
                    "blocks": q5}, f, indent=1)
+        f.write("\n")
+    with open(os.path.join(HERE, "q6_k_handbuilt.json"), "w") as f:
+        json.dump({"citation": note.replace("(Q8_0, Q4_K_M GGUF)", "(Q8_0, Q4_K_M GGUF, whose K-quant mix includes Q6_K)"),
+                   "blocks": q6}, f, indent=1)
         f.write("\n")
     with open(os.path.join(HERE, "iq4_xs_handbuilt.json"), "w") as f:
         json.dump({"citation": note.replace("(Q8_0, Q4_K_M GGUF)", "(Q8_0, Q4_K_M, IQ4_XS GGUF)"), "blocks": iq4},

@@ -1,4 +1,4 @@
-"""Pins for the oracle's block decoding (Q8_0, Q4_K, Q5_K, IQ4_XS) and scalar formats.
+"""Pins for the oracle's block decoding (Q8_0, Q4_K, Q5_K, Q6_K, IQ4_XS) and scalar formats.
 
 Everything here runs on the CPU. Each check ties the oracle to something other
 than itself: hand-built blocks whose values are known by construction
@@ -18,7 +18,8 @@ import synth
 
 sys.path.insert(0, os.path.join(os.path.dirname(__file__), "golden"))
 from make_handbuilt_blocks import (  # noqa: E402
-    IQ4_XS_GRID, pack_iq4_indices, pack_iq4_xs_scales, pack_nibbles, pack_q5_high_bits, pack_scales_mins)
+    IQ4_XS_GRID, pack_iq4_indices, pack_iq4_xs_scales, pack_nibbles, pack_q5_high_bits, pack_q6_planes,
+    pack_scales_mins)
 
 
 def _load(golden_dir, name):
@@ -408,6 +409,137 @@ def test_q5_k_rejects_wrong_sizes():
         oracle.dequant_q5_k(bytes(175), 1, 256)
     with pytest.raises(ValueError):
         oracle.dequant_q5_k(bytes(176), 1, 128)
+
+
+# ---------------------------------------------------------------- Q6_K
+
+def test_q6_k_handbuilt_blocks(golden_dir):
+    for blk in _load(golden_dir, "q6_k_handbuilt.json"):
+        raw = bytes.fromhex(blk["hex"])
+        d, sc, q = oracle.q6_k_fields(raw, 1, 256)
+        assert list(sc[0, 0]) == blk["sc"], blk["name"]
+        assert list(q[0, 0]) == blk["q"], blk["name"]
+        assert d[0, 0] == oracle.fp16_bits_to_f64(np.array([blk["d_bits"]]))[0]
+        w = oracle.dequant_q6_k(raw, 1, 256)[0]
+        expect = np.array([float.fromhex(v) for v in blk["expect"]])
+        assert np.array_equal(w, expect), blk["name"]
+
+
+def test_q6_k_handbuilt_values_by_hand(golden_dir):
+    blocks = {b["name"]: b for b in _load(golden_dir, "q6_k_handbuilt.json")}
+    # d = 1, every q = -32, sc = 1: every weight is -32
+    assert set(oracle.dequant_q6_k(bytes.fromhex(blocks["all_min"]["hex"]), 1, 256)[0]) == {-32.0}
+    # d = 0.5, q = 31, scales alternate 127, -128: 0.5 * 127 * 31 and 0.5 * -128 * 31
+    w = oracle.dequant_q6_k(bytes.fromhex(blocks["all_max"]["hex"]), 1, 256)[0]
+    assert list(w[[0, 15, 16, 31, 255]]) == [1968.5, 1968.5, -1984.0, -1984.0, -1984.0]
+    # d = 1, quarter c of each half holds q = 16c - 31; scales 1, -1, 2, -2, ...
+    w = oracle.dequant_q6_k(bytes.fromhex(blocks["quarter_code"]["hex"]), 1, 256)[0]
+    assert list(w[[0, 16, 32, 48, 64, 96, 128, 255]]) == [-31.0, 31.0, -30.0, 30.0, 3.0, 68.0, -155.0, -136.0]
+    # d = -0.25, q = -1: w = 0.25 * sc
+    w = oracle.dequant_q6_k(bytes.fromhex(blocks["negative_d"]["hex"]), 1, 256)[0]
+    assert list(w[::16]) == [25.0, -25.0, 12.5, -12.5, 6.25, -6.25, 3.0, -3.0, 1.5, -1.5, 0.75, -0.75,
+                             0.25, -0.25, 0.0, 0.0]
+
+
+def test_q6_k_low_plane_byte_locality():
+    raw = bytearray(synth.q6_k_weights(81, 1, 256))
+    base = oracle.dequant_q6_k(bytes(raw), 1, 256)[0]
+    _, sc, _ = oracle.q6_k_fields(bytes(raw), 1, 256)
+    for p in range(128):
+        h, r = divmod(p, 64)
+        c0, l = divmod(r, 32)
+        for mask, c in ((0x0F, c0), (0xF0, c0 + 2)):
+            weight = 128 * h + 32 * c + l
+            mod = bytearray(raw)
+            mod[p] ^= mask
+            changed = np.nonzero(oracle.dequant_q6_k(bytes(mod), 1, 256)[0] != base)[0]
+            assert list(changed) == ([weight] if sc[0, 0, weight // 16] != 0 else []), (p, mask)
+
+
+def test_q6_k_high_plane_bit_locality():
+    raw = bytearray(synth.q6_k_weights(82, 1, 256))
+    base = oracle.dequant_q6_k(bytes(raw), 1, 256)[0]
+    d, sc, q = oracle.q6_k_fields(bytes(raw), 1, 256)
+    for p in range(64):
+        h, l = divmod(p, 32)
+        for bit in range(8):
+            c = bit // 2
+            weight = 128 * h + 32 * c + l
+            mod = bytearray(raw)
+            mod[128 + p] ^= 1 << bit
+            w = oracle.dequant_q6_k(bytes(mod), 1, 256)[0]
+            changed = np.nonzero(w != base)[0]
+            step = d[0, 0] * sc[0, 0, weight // 16] * (16 << (bit % 2))
+            if step != 0:
+                assert list(changed) == [weight], (p, bit)
+                assert abs(w[weight] - base[weight]) == abs(step)
+            else:
+                assert changed.size == 0
+
+
+def test_q6_k_scale_byte_owns_sixteen_weights():
+    raw = bytearray(synth.q6_k_weights(83, 1, 256))
+    base = oracle.dequant_q6_k(bytes(raw), 1, 256)[0]
+    d, sc, q = oracle.q6_k_fields(bytes(raw), 1, 256)
+    for i in range(16):
+        mod = bytearray(raw)
+        mod[192 + i] = (sc[0, 0, i] + 1) & 0xFF if sc[0, 0, i] != 127 else 0x80
+        w = oracle.dequant_q6_k(bytes(mod), 1, 256)[0]
+        changed = set(np.nonzero(w != base)[0])
+        expected = {16 * i + t for t in range(16) if q[0, 0, 16 * i + t] != 0}
+        assert changed == expected, i
+
+
+def test_q6_k_pack_unpack_bijection():
+    rng = np.random.default_rng(7)
+    for v in range(-32, 32):
+        q = list(rng.integers(-32, 32, 256))
+        for i in range((v + 32) % 16, 256, 16):
+            q[i] = v
+        raw = pack_q6_planes(q) + bytes([1] * 16) + bytes([0, 0x3C])
+        assert list(oracle.q6_k_fields(raw, 1, 256)[2][0, 0]) == q
+    raw = synth.q6_k_weights(84, 4, 512)
+    _, sc, q = oracle.q6_k_fields(raw, 4, 512)
+    blocks = raw.reshape(-1, 210)
+    for b in range(blocks.shape[0]):
+        n, t = divmod(b, 2)
+        assert pack_q6_planes([int(v) for v in q[n, t]]) == bytes(blocks[b, :192])
+        assert bytes([int(v) & 0xFF for v in sc[n, t]]) == bytes(blocks[b, 192:208])
+
+
+def test_q6_k_requant_round_trip():
+    raw = synth.q6_k_weights(85, 16, 512)
+    d, sc, q = oracle.q6_k_fields(raw, 16, 512)
+    w = oracle.dequant_q6_k(raw, 16, 512).reshape(16, 2, 16, 16)
+    scale = d[:, :, None] * sc
+    ok = scale != 0
+    q_back = np.rint(w / np.where(ok, scale, 1.0)[..., None])
+    assert np.array_equal(q_back[ok], q.reshape(16, 2, 16, 16)[ok])
+
+
+def test_q6_k_weights_exact_and_fp32_target_rounds_once():
+    raw = synth.q6_k_weights(86, 32, 1024)
+    w = oracle.dequant_q6_k(raw, 32, 1024)
+    scaled = w * 2.0 ** 24
+    assert np.array_equal(scaled, np.rint(scaled)) and np.max(np.abs(scaled)) < 2.0 ** 50
+    w32 = oracle.dequant_q6_k_f32(raw, 32, 1024)
+    err = np.abs(w32.astype(np.float64) - w)
+    assert np.all(err <= 0.5 * np.spacing(np.abs(w32)).astype(np.float64))
+
+
+def test_q6_k_generator_distributions():
+    raw = synth.q6_k_weights(87, 128, 2048)
+    d, sc, q = oracle.q6_k_fields(raw, 128, 2048)
+    assert q.min() == -32 and q.max() == 31 and abs(q.mean() + 0.5) < 0.1
+    assert sc.min() == -128 and sc.max() == 127 and abs(sc.mean() + 0.5) < 1.0
+    assert abs(d.mean() / (0.0002 * np.sqrt(2 / np.pi)) - 1) < 0.03
+
+
+def test_q6_k_rejects_wrong_sizes():
+    with pytest.raises(ValueError):
+        oracle.dequant_q6_k(bytes(209), 1, 256)
+    with pytest.raises(ValueError):
+        oracle.dequant_q6_k(bytes(210), 1, 128)
 
 
 # ---------------------------------------------------------------- IQ4_XS

@@ -29,6 +29,11 @@ MUTATIONS = {
     "q5_high_bit_of_other_half": [("((H >> (2 * c)) & 1) << 4", "((H >> (2 * c + 1)) & 1) << 4")],
     "q5_high_bit_weight_eight": [("q[:, :, 64 * c + 32: 64 * c + 64] += ((H >> (2 * c + 1)) & 1) << 4",
                                   "q[:, :, 64 * c + 32: 64 * c + 64] += ((H >> (2 * c + 1)) & 1) << 3")],
+    "q6_high_bits_of_next_quarter": [("high = (H[:, :, 32 * h: 32 * h + 32] >> (2 * c)) & 3",
+                                      "high = (H[:, :, 32 * h: 32 * h + 32] >> (2 * (c ^ 1))) & 3")],
+    "q6_quant_not_centred": [("low + 16 * high - 32", "low + 16 * high - 31")],
+    "q6_scale_per_32": [("scale = (d[:, :, None] * sc).repeat(16, axis=2)",
+                         "scale = (d[:, :, None] * sc[:, :, ::2]).repeat(32, axis=2)")],
     "m_low_bits_from_low_nibble": [("m[..., j] = (S[..., j + 4] >> 4)", "m[..., j] = (S[..., j + 4] & 0x0F)")],
     "fp16_big_endian": [("(blocks[:, :, 0] | (blocks[:, :, 1] << 8))", "(blocks[:, :, 1] | (blocks[:, :, 0] << 8))")],
     "min_sign_flipped": [("return (scale * q - offset)", "return (scale * q + offset)")],
@@ -83,6 +88,13 @@ def _pins(o) -> list:
     def golden_q5():
         for blk in _golden("q5_k_handbuilt.json"):
             w = o.dequant_q5_k(bytes.fromhex(blk["hex"]), 1, 256)[0]
+            if not np.array_equal(w, [float.fromhex(v) for v in blk["expect"]]):
+                return False
+        return True
+
+    def golden_q6():
+        for blk in _golden("q6_k_handbuilt.json"):
+            w = o.dequant_q6_k(bytes.fromhex(blk["hex"]), 1, 256)[0]
             if not np.array_equal(w, [float.fromhex(v) for v in blk["expect"]]):
                 return False
         return True
@@ -145,6 +157,7 @@ def _pins(o) -> list:
 
     check("golden_q4", golden_q4)
     check("golden_q5", golden_q5)
+    check("golden_q6", golden_q6)
     check("golden_q8", golden_q8)
     check("gemv_unit_vectors", gemv_unit_vectors)
     check("route_hand_set", route_hand_set)

@@ -80,6 +80,33 @@ def test_q5_k_gemv_matches_exact_rational(n_rows, k, m):
             assert abs(Fraction(float(y[r, n])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
 
 
+@pytest.mark.parametrize("n_rows,k,m", [(3, 256, 1), (2, 512, 4)])
+def test_q6_k_gemv_matches_exact_rational(n_rows, k, m):
+    raw = synth.q6_k_weights(91 + m, n_rows, k)
+    x = synth.bf16_normal(92 + m, (m, k))
+    y = oracle.qmv_q6_k(raw, x, n_rows, k)
+    exact = _exact_dot_rows(oracle.dequant_q6_k(raw, n_rows, k), oracle.bf16_bits_to_f64(x))
+    assert y.shape == (m, n_rows)
+    for r in range(m):
+        for n in range(n_rows):
+            e = exact[r][n]
+            assert abs(Fraction(float(y[r, n])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
+
+
+def test_q6_k_gemv_constant_over_sixteen_weights_closed_form(golden_dir):
+    # x = 1 on weights 16i .. 16i + 15 only: y = d sc_i sum(q), from the stated fields
+    with open(os.path.join(golden_dir, "q6_k_handbuilt.json")) as f:
+        blocks = json.load(f)["blocks"]
+    for blk in blocks:
+        raw = bytes.fromhex(blk["hex"])
+        d = oracle.fp16_bits_to_f64(np.array([blk["d_bits"]]))[0]
+        for i in range(16):
+            x = np.zeros((1, 256), dtype=np.uint16)
+            x[0, 16 * i:16 * i + 16] = 0x3F80
+            y = oracle.qmv_q6_k(raw, x, 1, 256)[0, 0]
+            assert y == d * blk["sc"][i] * sum(blk["q"][16 * i:16 * i + 16]), (blk["name"], i)
+
+
 def test_q5_k_gemv_constant_over_one_subblock_closed_form(golden_dir):
     # x = 1 on sub-block j only: y = d sc_j sum(q over j) - 32 dmin m_j, from the stated fields
     with open(os.path.join(golden_dir, "q5_k_handbuilt.json")) as f:
