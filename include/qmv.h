@@ -131,6 +131,30 @@ int qmv_q5_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
              int m, int n, int k, void *stream);
 
 /*
+ * Q6_K matrix times bf16 activation rows (m = 1..4): the other K-quant that
+ * Q4_K_M files mix in (memra README model support table, Q4_K_M files).
+ * 210-byte blocks of 256 weights: 128 bytes of low quant nibbles, 64 bytes of
+ * top quant bit pairs, 16 int8 scales (one per 16 weights), fp16 d. Weight
+ * 128h + 32c + l takes its low bits from byte 64h + 32(c & 1) + l (low nibble
+ * for c < 2, high for c >= 2), its top bits from bits 2c, 2c + 1 of byte
+ * 128 + 32h + l, its scale from byte 192 + 8h + 2c + l/16;
+ * w = d * sc * (low + 16 top - 32).
+ *   w       [n rows][k/256 blocks] Q6_K, 16-byte aligned (blocks themselves are
+ *           only 2-byte aligned); w_bytes == n*(k/256)*210
+ *   x_bf16  bf16 bits [m][k] row-major, 16-byte aligned
+ *   y       fp32 [m][n] row-major, 4-byte aligned
+ *   1 <= m <= QMV_MAX_ROWS, n >= 1, k >= 256 and k % 256 == 0,
+ *   m*(k*2 + (k/16)*4) <= QMV_LDS_X_BYTES (m = 4 allows k up to 18176).
+ * The quants enter the products as the exact bf16 values 160 + q and 160 times
+ * each 16-weight group's activation sum is taken off in fp32, so the result
+ * carries fp32 rounding only. Row r of y is bit-identical for every m.
+ * Returns QMV_ERR_NULL, _SHAPE, _SIZE, _ALIGN, _RANGE, _ALIAS before any HIP
+ * call, or QMV_ERR_HIP on a launch failure.
+ */
+int qmv_q6_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
+             int m, int n, int k, void *stream);
+
+/*
  * IQ4_XS matrix times bf16 activation rows (decode m=1, verify m=2..4).
  *   w       [n rows][k/256 blocks] IQ4_XS (136-byte super-blocks of 256 weights:
  *           fp16 d, 16 bits holding the top two bits of eight 6-bit sub-block
@@ -250,13 +274,14 @@ int qmm_q4_k_prefill(const void *w, size_t w_bytes, const uint16_t *x_bf16, floa
  * fp32: each weight is the exact block value rounded once to fp32 (nearest
  * even; Q8_0 and IQ4_XS weights are exact in fp32). bf16: that fp32 value
  * rounded to bf16 (nearest even). IQ4_XS: w is 8-byte aligned, 136-byte blocks.
- * Q5_K: 16-byte aligned, 176-byte blocks.
+ * Q5_K: 16-byte aligned, 176-byte blocks. Q6_K: 16-byte aligned, 210-byte blocks.
  */
 int qmv_dequant_q4_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 int qmv_dequant_q4_k_bf16(const void *w, size_t w_bytes, uint16_t *out, int n, int k, void *stream);
 int qmv_dequant_q8_0_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 int qmv_dequant_iq4_xs_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 int qmv_dequant_q5_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
+int qmv_dequant_q6_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 
 #ifdef __cplusplus
 }

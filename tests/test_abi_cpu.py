@@ -35,7 +35,7 @@ def test_header_lists_the_expected_entry_points():
     assert _header_functions() == sorted([
         "qmv_version", "qmv_strerror", "qmv_last_error", "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe_workspace",
         "qmv_q4_k_moe", "qmv_dequant_iq4_xs_f32", "qmv_iq4_xs_moe_workspace", "qmv_iq4_xs_moe",
-        "qmv_q5_k", "qmv_dequant_q5_k_f32",
+        "qmv_q5_k", "qmv_dequant_q5_k_f32", "qmv_q6_k", "qmv_dequant_q6_k_f32",
         "qmm_q4_k_prefill_workspace", "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16",
         "qmv_dequant_q8_0_f32"])
 
@@ -102,6 +102,32 @@ def test_q5_k_validation():
     f = L.qmv_dequant_q5_k_f32
     assert f(V(0), nb, V(Y), 2, 256, None) == NULL and f(V(W), nb - 1, V(Y), 2, 256, None) == SIZE
     assert f(V(W), nb, V(Y + 4), 2, 256, None) == ALIGN and f(V(W), nb, V(W), 2, 256, None) == ALIAS
+
+
+def q6k(w=W, nbytes=None, x=X, y=Y, m=1, n=2, k=256):
+    nbytes = q.q6_k_bytes(n, k) if nbytes is None else nbytes
+    return L.qmv_q6_k(V(w), nbytes, V(x), V(y), m, n, k, None)
+
+
+def test_q6_k_validation():
+    assert q6k(w=0) == NULL and q6k(x=0) == NULL and q6k(y=0) == NULL
+    assert q6k(m=0) == RANGE and q6k(m=5) == RANGE
+    assert q6k(n=0) == SHAPE and q6k(k=0) == SHAPE and q6k(k=255) == SHAPE and q6k(k=384) == SHAPE
+    assert q6k(w=W + 8) == ALIGN and q6k(w=W + 2) == ALIGN and q6k(x=X + 2) == ALIGN and q6k(y=Y + 2) == ALIGN
+    # the LDS stage: m * k * 2.25 bytes; m = 4 allows k up to 18176, m = 3 up to 24064
+    assert q6k(m=4, k=18176, n=1, y=Y + 2) == ALIGN   # passes the LDS check, stops at alignment
+    assert q6k(m=3, k=24064, n=1, y=Y + 2) == ALIGN
+    assert q6k(m=4, k=18432, n=1) == RANGE and q6k(m=3, k=24320, n=1) == RANGE
+    assert q6k(y=W + 64) == ALIAS
+    full = q.q6_k_bytes(2, 512)
+    assert full == 2 * 2 * 210
+    for b in list(range(full)) + [full + 1, full + 210, q.q5_k_bytes(2, 512), q.q4_k_bytes(2, 512)]:
+        assert q6k(nbytes=b, k=512) == SIZE, b
+    nb = q.q6_k_bytes(2, 256)
+    f = L.qmv_dequant_q6_k_f32
+    assert f(V(0), nb, V(Y), 2, 256, None) == NULL and f(V(W), nb - 1, V(Y), 2, 256, None) == SIZE
+    assert f(V(W), nb, V(Y + 4), 2, 256, None) == ALIGN and f(V(W), nb, V(W), 2, 256, None) == ALIAS
+    assert f(V(W), nb, V(Y), 2, 255, None) == SHAPE
 
 
 def iq4(w=W, nbytes=None, x=X, y=Y, m=1, n=2, k=256):
