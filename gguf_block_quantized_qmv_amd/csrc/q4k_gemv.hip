@@ -223,10 +223,16 @@ __device__ __forceinline__ void load_step(const uint8_t *__restrict__ bp, const 
 // Block address of step t for this lane, or the matrix's first block when the
 // step does not exist for it (see the kernel); every address loaded stays
 // inside the weights.
-template <bool FULL, int kBlocksPerStep, bool Q5>
+// NS > 0 (unrolled, t a compile-time step): only step NS - 1 can be partial,
+// and last_ok says whether this lane's block exists there. NS == 0: FULL says
+// the row is a whole number of steps.
+template <bool FULL, int NS, int kBlocksPerStep, bool Q5>
 __device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *w, const uint8_t *wl, const bool active, const int t,
-                                                   const int nsteps, const int jb, const int nblk) {
-  const bool ok = active && t < nsteps && (FULL || t * kBlocksPerStep + jb < nblk);
+                                                   const int nsteps, const int jb, const int nblk,
+                                                   const bool last_ok) {
+  bool ok;
+  if constexpr (NS > 0) ok = active && t < NS && (t < NS - 1 || last_ok);
+  else ok = active && t < nsteps && (FULL || t * kBlocksPerStep + jb < nblk);
   return ok ? wl + (size_t)(t * kBlocksPerStep) * block_bytes<Q5>() : w;
 }
 
@@ -255,7 +261,16 @@ __device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *w, const uint8
 constexpr int kMinThreads = 256;
 constexpr int kMaxThreads = 512;       // M = 1
 constexpr int kMaxThreadsRows = 768;   // M = 2..4: register use allows 3 waves per SIMD
-constexpr int kQ5Depth = 4;            // ring depth (steps) of the Q5_K instantiation
+// Q5_K ring depths (steps), 16 and 32 lanes per row: at M = 1 as for Q4_K; at
+// M = 2..4 (more registers per step) 4 for both.
+template <int M>
+constexpr int q5_depth16() { return M == 1 ? 5 : 4; }
+template <int M>
+constexpr int q5_depth32() { return M == 1 ? 2 : 4; }
+// Q4_K ring depths (steps): a 5-step row (K = 5120, 16 lanes) keeps every load in
+// flight from the start; the 9-step rows of 32 lanes are fastest with 2.
+constexpr int kQ4Depth16 = 5;
+constexpr int kQ4Depth32 = 2;
 
 template <int M, int G>
 constexpr int x_head() { return (G == 16 ? 4 * M : 9 * M) < 9 ? (G == 16 ? 4 * M : 9 * M) : 9; }
@@ -297,12 +312,12 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
     // ring only after the head has arrived and is in LDS. Requests queue in the
     // memory system in issue order, so every weight request issued before a
     // wave's activations are back delays them (and with them its first step).
-    load_step<Q5>(step_ptr<FULL, kBlocksPerStep, Q5>(w, wl, active, 0, nsteps, jb, nblk), c, hdr[0], qa[0], qb[0],
+    load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(w, wl, active, 0, nsteps, jb, nblk, last_ok), c, hdr[0], qa[0], qb[0],
                   hb0[0], hb1[0]);
     store_x_head<M, kXHead>(xv, xs, gpr, gpp, nthreads);
 #pragma unroll
     for (int u = 1; u < D; ++u)
-      load_step<Q5>(step_ptr<FULL, kBlocksPerStep, Q5>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u],
+      load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(w, wl, active, u, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u], qb[u],
                     hb0[u], hb1[u]);
     // rows up to NS steps are covered by the head when this holds, and the
     // loop that stages the rest is compiled out
@@ -315,7 +330,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
     stage_x_tail<M, kXHead, 8>(xg, xs, gpr, gpp, nthreads);
 #pragma unroll
     for (int u = 0; u < D; ++u)
-      load_step<Q5>(step_ptr<FULL, kBlocksPerStep, Q5>(w, wl, active, u, nsteps, jb, nblk), c, hdr[u], qa[u], qb[u],
+      load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(w, wl, active, u, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u], qb[u],
                     hb0[u], hb1[u]);
   }
   x_sums<M>(xs, xsum, gpp, nsub, nthreads);
@@ -337,7 +352,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
         dense_chunk<M, Q5>(acc, hdr[u], qa[u], qb[u], hb0[u], hb1[u], 2 * c, sel, xb + s * kStepGranules, gpp,
                            sb + s * 2 * G, nsub);
       if (s + D < NS)
-        load_step<Q5>(step_ptr<FULL, kBlocksPerStep, Q5>(w, wl, active, s + D, nsteps, jb, nblk), c, hdr[u], qa[u],
+        load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(w, wl, active, s + D, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u],
                       qb[u], hb0[u], hb1[u]);
     }
   } else {
@@ -348,7 +363,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
         if (s < nsteps && (FULL || s * kBlocksPerStep + jb < nblk))
           dense_chunk<M, Q5>(acc, hdr[u], qa[u], qb[u], hb0[u], hb1[u], 2 * c, sel, xb + s * kStepGranules, gpp,
                              sb + s * 2 * G, nsub);
-        load_step<Q5>(step_ptr<FULL, kBlocksPerStep, Q5>(w, wl, active, s + D, nsteps, jb, nblk), c, hdr[u], qa[u],
+        load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(w, wl, active, s + D, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u],
                       qb[u], hb0[u], hb1[u]);
       }
     }
@@ -417,30 +432,32 @@ int launch_any(const void *w, const uint16_t *x, float *y, int n, int k, hipStre
 
 // Lanes per row by row length: 16 up to K = 8192 (1..8 steps of 4 blocks), 32
 // beyond (steps of 8 blocks; 5..9 steps up to K = 18432, runtime loop after).
-// The ring is 4 steps deep.
+// (FULL matters only to the runtime loop; the unrolled kernels test their
+// possibly partial last step themselves.)
 template <int M, bool Q5>
 int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
-  constexpr int D = Q5 ? kQ5Depth : 4;
+  constexpr int D = Q5 ? q5_depth16<M>() : kQ4Depth16;
+  constexpr int D32 = Q5 ? q5_depth32<M>() : kQ4Depth32;
   const int nblk = k >> 8;
   if (k <= 8192) {
     switch ((nblk + 3) / 4) {
-      case 1: return launch_cfg<M, 16, D, true, 1, Q5>(w, x, y, n, k, stream);
-      case 2: return launch_cfg<M, 16, D, true, 2, Q5>(w, x, y, n, k, stream);
-      case 3: return launch_cfg<M, 16, D, true, 3, Q5>(w, x, y, n, k, stream);
-      case 4: return launch_cfg<M, 16, D, true, 4, Q5>(w, x, y, n, k, stream);
-      case 5: return launch_cfg<M, 16, D, true, 5, Q5>(w, x, y, n, k, stream);
-      case 6: return launch_cfg<M, 16, D, true, 6, Q5>(w, x, y, n, k, stream);
-      case 7: return launch_cfg<M, 16, D, true, 7, Q5>(w, x, y, n, k, stream);
-      default: return launch_cfg<M, 16, D, true, 8, Q5>(w, x, y, n, k, stream);
+      case 1: return launch_cfg<M, 16, D, false, 1, Q5>(w, x, y, n, k, stream);
+      case 2: return launch_cfg<M, 16, D, false, 2, Q5>(w, x, y, n, k, stream);
+      case 3: return launch_cfg<M, 16, D, false, 3, Q5>(w, x, y, n, k, stream);
+      case 4: return launch_cfg<M, 16, D, false, 4, Q5>(w, x, y, n, k, stream);
+      case 5: return launch_cfg<M, 16, D, false, 5, Q5>(w, x, y, n, k, stream);
+      case 6: return launch_cfg<M, 16, D, false, 6, Q5>(w, x, y, n, k, stream);
+      case 7: return launch_cfg<M, 16, D, false, 7, Q5>(w, x, y, n, k, stream);
+      default: return launch_cfg<M, 16, D, false, 8, Q5>(w, x, y, n, k, stream);
     }
   }
   switch ((nblk + 7) / 8) {
-    case 5: return launch_cfg<M, 32, D, true, 5, Q5>(w, x, y, n, k, stream);
-    case 6: return launch_cfg<M, 32, D, true, 6, Q5>(w, x, y, n, k, stream);
-    case 7: return launch_cfg<M, 32, D, true, 7, Q5>(w, x, y, n, k, stream);
-    case 8: return launch_cfg<M, 32, D, true, 8, Q5>(w, x, y, n, k, stream);
-    case 9: return launch_cfg<M, 32, D, true, 9, Q5>(w, x, y, n, k, stream);
-    default: return launch_any<M, 32, D, Q5>(w, x, y, n, k, stream);
+    case 5: return launch_cfg<M, 32, D32, false, 5, Q5>(w, x, y, n, k, stream);
+    case 6: return launch_cfg<M, 32, D32, false, 6, Q5>(w, x, y, n, k, stream);
+    case 7: return launch_cfg<M, 32, D32, false, 7, Q5>(w, x, y, n, k, stream);
+    case 8: return launch_cfg<M, 32, D32, false, 8, Q5>(w, x, y, n, k, stream);
+    case 9: return launch_cfg<M, 32, D32, false, 9, Q5>(w, x, y, n, k, stream);
+    default: return launch_any<M, 32, D32, Q5>(w, x, y, n, k, stream);
   }
 }
 

@@ -49,7 +49,7 @@ namespace {
 constexpr int kQ6KBlockBytes = 210;
 constexpr int kMinThreads = 256;
 constexpr int kMaxThreads = 512;      // M = 1
-constexpr int kMaxThreadsRows = 512;  // M = 2..4 (up to 166 VGPRs: 768 threads would spill)
+constexpr int kMaxThreadsRows = 640;  // M = 2..4: 20 rows of 32 lanes, one workgroup per CU at K = 17408
 
 // LDS slot of activation granule g of a staged row (see the header comment).
 __host__ __device__ constexpr int q6_slot(int g) { return g ^ (((g >> 4) & 1) | ((g >> 3) & 12)); }
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256) void q6k_dequant_kernel(const uint8_t *__restr
 }
 
 // Rows per workgroup: every CU gets the same rows when N splits over 256 CUs
-// into whole-wave workgroups of 256..512 threads that fit the
+// into whole-wave workgroups of 256..512 threads (640 for M > 1) that fit the
 // LDS q at a time; otherwise 256 threads.
 inline int q6_pick_rows(const int m, const int n, const int G, const size_t lds) {
   const int dflt = kMinThreads / G;
@@ -405,11 +405,17 @@ int q6_launch(const void *w, const uint16_t *x, float *y, int n, int k, hipStrea
   return launch_kernel("q6k_gemv_kernel", fn, dim3(grid), dim3(rows * G), lds, stream, w, x, y, n, k);
 }
 
-constexpr int kQ6Depth = 3;
+// Ring depths (steps). At M = 1 a 5-step row of 16 lanes keeps every load in
+// flight from the start, and the 9-step rows of 32 lanes run fastest with 2;
+// at M = 2..4 (more registers per step, fewer waves) 3 is fastest for both.
+template <int M>
+constexpr int q6_depth16() { return M == 1 ? 5 : 3; }
+template <int M>
+constexpr int q6_depth32() { return M == 1 ? 2 : 3; }
 
 template <int M>
 int q6_launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
-  constexpr int D = kQ6Depth;
+  constexpr int D = q6_depth16<M>(), D32 = q6_depth32<M>();
   const int nblk = k >> 8;
   if (k <= 8192) {
     switch ((nblk + 3) / 4) {
@@ -424,12 +430,12 @@ int q6_launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStr
     }
   }
   switch ((nblk + 7) / 8) {
-    case 5: return q6_launch<M, 32, D, 5>(w, x, y, n, k, stream);
-    case 6: return q6_launch<M, 32, D, 6>(w, x, y, n, k, stream);
-    case 7: return q6_launch<M, 32, D, 7>(w, x, y, n, k, stream);
-    case 8: return q6_launch<M, 32, D, 8>(w, x, y, n, k, stream);
-    case 9: return q6_launch<M, 32, D, 9>(w, x, y, n, k, stream);
-    default: return q6_launch<M, 32, D, 0>(w, x, y, n, k, stream);
+    case 5: return q6_launch<M, 32, D32, 5>(w, x, y, n, k, stream);
+    case 6: return q6_launch<M, 32, D32, 6>(w, x, y, n, k, stream);
+    case 7: return q6_launch<M, 32, D32, 7>(w, x, y, n, k, stream);
+    case 8: return q6_launch<M, 32, D32, 8>(w, x, y, n, k, stream);
+    case 9: return q6_launch<M, 32, D32, 9>(w, x, y, n, k, stream);
+    default: return q6_launch<M, 32, D32, 0>(w, x, y, n, k, stream);
   }
 }
 
