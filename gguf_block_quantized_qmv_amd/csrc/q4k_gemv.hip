@@ -220,20 +220,20 @@ __device__ __forceinline__ void load_step(const uint8_t *__restrict__ bp, const 
   }
 }
 
-// Block address of step t for this lane, or the matrix's first block when the
+// Block address of step t for this lane, or the fallback block wfb when the
 // step does not exist for it (see the kernel); every address loaded stays
 // inside the weights.
 // NS > 0 (unrolled, t a compile-time step): only step NS - 1 can be partial,
 // and last_ok says whether this lane's block exists there. NS == 0: FULL says
 // the row is a whole number of steps.
 template <bool FULL, int NS, int kBlocksPerStep, bool Q5>
-__device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *w, const uint8_t *wl, const bool active, const int t,
+__device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *wfb, const uint8_t *wl, const bool active, const int t,
                                                    const int nsteps, const int jb, const int nblk,
                                                    const bool last_ok) {
   bool ok;
   if constexpr (NS > 0) ok = active && t < NS && (t < NS - 1 || last_ok);
   else ok = active && t < nsteps && (FULL || t * kBlocksPerStep + jb < nblk);
-  return ok ? wl + (size_t)(t * kBlocksPerStep) * block_bytes<Q5>() : w;
+  return ok ? wl + (size_t)(t * kBlocksPerStep) * block_bytes<Q5>() : wfb;
 }
 
 // G lanes own one output row (G = 16 or 32): a step covers G/4 super-blocks of
@@ -245,9 +245,10 @@ __device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *w, const uint8
 // are still in flight. Afterwards a ring of D steps stays in flight.
 //
 // Every weight load is issued unconditionally -- a step past the row, blocks
-// past a partial last step and rows past the matrix read the matrix's first
-// block instead and are never used -- so the number of loads in flight is known
-// at every point and each step waits only for its own ring slot.
+// past a partial last step and rows past the matrix read the last block of the
+// lane's row (or of the matrix) instead and are never used -- so the number of
+// loads in flight is known at every point and each step waits only for its own
+// ring slot.
 //
 // NS > 0: the row is exactly NS steps (the last one possibly partial) and the
 // step loop is unrolled, which keeps the ring in fixed registers and every wait
@@ -299,6 +300,10 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
   const int nsteps = NS > 0 ? NS : (nblk + kBlocksPerStep - 1) / kBlocksPerStep;
   // with NS > 0 only the last step can be partial: lanes past its blocks skip it
   const bool last_ok = jb < nblk - (nsteps - 1) * kBlocksPerStep;
+  // loads with no block of their own (past the row, past the matrix, past a
+  // partial last step) read the last block of the lane's row (of the last row
+  // when the row is past the matrix), which the same or a recent load also reads
+  const uint8_t *wfb = w + ((size_t)(active ? row : n - 1) * (size_t)nblk + (size_t)(nblk - 1)) * block_bytes<Q5>();
   const uint8_t *wl = w + (size_t)(active ? row : 0) * (size_t)nblk * block_bytes<Q5>() +
                       (size_t)jb * block_bytes<Q5>();
 
@@ -312,12 +317,12 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
     // ring only after the head has arrived and is in LDS. Requests queue in the
     // memory system in issue order, so every weight request issued before a
     // wave's activations are back delays them (and with them its first step).
-    load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(w, wl, active, 0, nsteps, jb, nblk, last_ok), c, hdr[0], qa[0], qb[0],
+    load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(wfb, wl, active, 0, nsteps, jb, nblk, last_ok), c, hdr[0], qa[0], qb[0],
                   hb0[0], hb1[0]);
     store_x_head<M, kXHead>(xv, xs, gpr, gpp, nthreads);
 #pragma unroll
     for (int u = 1; u < D; ++u)
-      load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(w, wl, active, u, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u], qb[u],
+      load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(wfb, wl, active, u, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u], qb[u],
                     hb0[u], hb1[u]);
     // rows up to NS steps are covered by the head when this holds, and the
     // loop that stages the rest is compiled out
@@ -330,7 +335,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
     stage_x_tail<M, kXHead, 8>(xg, xs, gpr, gpp, nthreads);
 #pragma unroll
     for (int u = 0; u < D; ++u)
-      load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(w, wl, active, u, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u], qb[u],
+      load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(wfb, wl, active, u, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u], qb[u],
                     hb0[u], hb1[u]);
   }
   x_sums<M>(xs, xsum, gpp, nsub, nthreads);
@@ -352,7 +357,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
         dense_chunk<M, Q5>(acc, hdr[u], qa[u], qb[u], hb0[u], hb1[u], 2 * c, sel, xb + s * kStepGranules, gpp,
                            sb + s * 2 * G, nsub);
       if (s + D < NS)
-        load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(w, wl, active, s + D, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u],
+        load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(wfb, wl, active, s + D, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u],
                       qb[u], hb0[u], hb1[u]);
     }
   } else {
@@ -363,7 +368,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
         if (s < nsteps && (FULL || s * kBlocksPerStep + jb < nblk))
           dense_chunk<M, Q5>(acc, hdr[u], qa[u], qb[u], hb0[u], hb1[u], 2 * c, sel, xb + s * kStepGranules, gpp,
                              sb + s * 2 * G, nsub);
-        load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(w, wl, active, s + D, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u],
+        load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(wfb, wl, active, s + D, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u],
                       qb[u], hb0[u], hb1[u]);
       }
     }
