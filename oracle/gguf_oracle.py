@@ -24,7 +24,8 @@ values -- so this oracle is that definition written out in fp64:
 * prefill: the same product for many rows, plus the variant whose weights are
   first rounded to fp32 and then to bf16 (the prescribed bf16 tile).
 
-The byte layouts are the public GGUF ones (Q8_0: fp16 d + 32 int8; Q4_K: fp16
+The byte layouts are the public GGUF ones (Q8_0: fp16 d + 32 int8; Q4_0: fp16 d
++ 16 bytes of nibbles, low nibbles first in weight order; Q4_K: fp16
 d, fp16 dmin, 12 bytes of packed 6-bit scales and mins, 128 bytes of nibbles;
 Q5_K: Q4_K plus a 32-byte plane of fifth bits; Q6_K: a 4-bit and a 2-bit plane
 of signed 6-bit quants, 16 int8 scales, fp16 d;
@@ -115,6 +116,49 @@ def dequant_q8_0(raw, n_rows: int, k: int) -> np.ndarray:
     """Exact Q8_0 weights: w[n, 32t + j] = d[n, t] * q[n, t, j]  (float64 [N, K])."""
     d, q = q8_0_fields(raw, n_rows, k)
     return (d[:, :, None] * q).reshape(n_rows, k)
+
+
+# ----------------------------------------------------------------------------
+# Q4_0: 18-byte blocks of 32 weights along K
+# ----------------------------------------------------------------------------
+#
+# The format of the Gemma-4 QAT rows of the memra README's model support table.
+# Public GGUF layout, restated: a little-endian fp16 scale d, then 16 bytes;
+# byte j holds weight j in its low nibble and weight 16 + j in its high nibble.
+# Each weight is d times its nibble minus 8 (a signed 4-bit value in [-8, 7]).
+
+Q4_0_BLOCK_BYTES = 18
+Q4_0_BLOCK_WEIGHTS = 32
+
+
+def q4_0_fields(raw, n_rows: int, k: int):
+    """Split a row-major Q4_0 matrix into (d [N, K/32] float64, q [N, K/32, 32] int64).
+
+    Block t of row n starts at byte (n*K/32 + t)*18; q holds the stored nibbles
+    in [0, 15] in weight order (the 16 low nibbles, then the 16 high nibbles).
+    """
+    if k % Q4_0_BLOCK_WEIGHTS:
+        raise ValueError("Q4_0 needs K to be a multiple of 32")
+    nb = k // Q4_0_BLOCK_WEIGHTS
+    b = _as_bytes(raw)
+    if b.size != n_rows * nb * Q4_0_BLOCK_BYTES:
+        raise ValueError("byte count does not match the Q4_0 shape")
+    blocks = b.reshape(n_rows, nb, Q4_0_BLOCK_BYTES)
+    d = fp16_bits_to_f64(blocks[:, :, 0].astype(np.uint16) | (blocks[:, :, 1].astype(np.uint16) << 8))
+    qs = blocks[:, :, 2:].astype(np.int64)
+    q = np.concatenate([qs & 0x0F, qs >> 4], axis=2)
+    return d, q
+
+
+def dequant_q4_0(raw, n_rows: int, k: int) -> np.ndarray:
+    """Exact Q4_0 weights: w[n, 32t + j] = d[n, t] * (q[n, t, j] - 8)  (float64 [N, K])."""
+    d, q = q4_0_fields(raw, n_rows, k)
+    return (d[:, :, None] * (q - 8)).reshape(n_rows, k)
+
+
+def dequant_q4_0_f32(raw, n_rows: int, k: int) -> np.ndarray:
+    """Q4_0 weights in fp32 (exact: d has 11 significant bits, q - 8 at most 4)."""
+    return round_to_f32(dequant_q4_0(raw, n_rows, k))
 
 
 # ----------------------------------------------------------------------------
@@ -428,6 +472,11 @@ def gemv(w: np.ndarray, x: np.ndarray) -> np.ndarray:
 def qmv_q8_0(raw, x_f32, n_rows: int, k: int) -> np.ndarray:
     """Q8_0 matrix times fp32 activation rows -> float64 [M, N]."""
     return gemv(dequant_q8_0(raw, n_rows, k), np.asarray(x_f32, dtype=np.float32).astype(np.float64))
+
+
+def qmv_q4_0(raw, x_bf16_bits, n_rows: int, k: int) -> np.ndarray:
+    """Q4_0 matrix times bf16 activation rows -> float64 [M, N]."""
+    return gemv(dequant_q4_0(raw, n_rows, k), bf16_bits_to_f64(x_bf16_bits))
 
 
 def qmv_q5_k(raw, x_bf16_bits, n_rows: int, k: int) -> np.ndarray:

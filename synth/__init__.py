@@ -29,6 +29,8 @@ import numpy as np
 __all__ = [
     "rng",
     "q8_0_weights",
+    "q4_0_weights",
+    "torch_q4_0_weights",
     "q4_k_weights",
     "bf16_normal",
     "f32_normal",
@@ -50,6 +52,7 @@ _Q4_K_BYTES, _Q4_K_WEIGHTS = 144, 256
 _IQ4_XS_BYTES, _IQ4_XS_WEIGHTS = 136, 256
 _Q5_K_BYTES = 176
 _Q6_K_BYTES = 210
+_Q4_0_BYTES, _Q4_0_WEIGHTS = 18, 32
 
 
 def rng(seed: int, *stream: int) -> np.random.Generator:
@@ -220,6 +223,42 @@ def moe_bank_iq4_xs(seed: int, n_experts: int, hidden: int, ffn: int, *, stream:
 def moe_logits(seed: int, n_tokens: int, n_experts: int, *, stream: int = 0) -> np.ndarray:
     """Router logits ~ N(0,1) fp32, shape [n_tokens, n_experts]."""
     return f32_normal(seed, (n_tokens, n_experts), stream=1000 + stream)
+
+
+def q4_0_weights(seed: int, n_rows: int, k: int, *, stream: int = 0, d_scale: float = 0.1) -> np.ndarray:
+    """Row-major Q4_0 matrix bytes.
+
+    Per 18-byte block: fp16 d = N(0,1)*0.1 (signed, as a quantiser that takes
+    the largest-magnitude weight's sign would write it), then 16 uniform random
+    bytes: i.i.d. uniform nibbles in [0, 15]. |d| (q - 8) then has the Q4_K
+    recipe's order of magnitude. Returns a flat uint8 array of
+    n_rows * (k/32) * 18 bytes.
+    """
+    if k % _Q4_0_WEIGHTS:
+        raise ValueError("k must be a multiple of 32")
+    nb = n_rows * (k // _Q4_0_WEIGHTS)
+    g = rng(seed, 40, stream)
+    d = (g.standard_normal(nb) * d_scale).astype("<f2")
+    blocks = np.empty((nb, _Q4_0_BYTES), dtype=np.uint8)
+    blocks[:, 0:2] = d.view(np.uint8).reshape(nb, 2)
+    blocks[:, 2:] = g.integers(0, 256, size=(nb, _Q4_0_BYTES - 2), dtype=np.uint8)
+    return blocks.reshape(-1)
+
+
+def torch_q4_0_weights(seed: int, n_rows: int, k: int, device, *, stream: int = 0, d_scale: float = 0.1):
+    """Device-side Q4_0 matrix bytes with the recipe of q4_0_weights (d rounded
+    from fp32). Returns a flat uint8 device tensor."""
+    import torch
+
+    if k % _Q4_0_WEIGHTS:
+        raise ValueError("k must be a multiple of 32")
+    nb = n_rows * (k // _Q4_0_WEIGHTS)
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1_000_003 + int(stream) * 7919 + 40) & 0x7FFF_FFFF_FFFF_FFFF)
+    blocks = torch.randint(0, 256, (nb, _Q4_0_BYTES), dtype=torch.uint8, device=device, generator=g)
+    d = torch.randn((nb, 1), dtype=torch.float32, device=device, generator=g).mul_(d_scale)
+    blocks[:, 0:2] = d.to(torch.float16).view(torch.uint8).view(nb, 2)
+    return blocks.reshape(-1)
 
 
 def torch_q4_k_weights(seed: int, n_rows: int, k: int, device, *, stream: int = 0):

@@ -1,4 +1,4 @@
-"""Writes tests/golden/{q8_0,q4_k,q5_k,q6_k,iq4_xs}_handbuilt.json: hand-built blocks with known values.
+"""Writes tests/golden/{q8_0,q4_0,q4_k,q5_k,q6_k,iq4_xs}_handbuilt.json: hand-built blocks with known values.
 
 Run from the repository root:  python tests/golden/make_handbuilt_blocks.py
 
@@ -10,7 +10,7 @@ Q4_K blocks the 12 scale bytes were also derived by hand and are written below
 as literals; the script stops if its encoder disagrees with them.
 
 The expected weights are computed here from the stated fields with exact
-rational arithmetic (w = d*q for Q8_0, w = d*sc_j*q - dmin*m_j for Q4_K,
+rational arithmetic (w = d*q for Q8_0, w = d*(q - 8) for Q4_0, w = d*sc_j*q - dmin*m_j for Q4_K,
 w = d*(ls_j - 32)*grid[q] for IQ4_XS, the Q4_K form with 5-bit q for Q5_K,
 w = d*sc_i*q for Q6_K);
 they are closed forms by construction
@@ -143,6 +143,26 @@ Q5_K_BLOCKS = [
 ]
 
 
+# ---------------------------------------------------------------- Q4_0
+
+def pack_q4_0_quants(q: list[int]) -> bytes:
+    """The 16 quant bytes of a Q4_0 block: weight j (j < 16) in the low nibble of
+    byte j, weight 16 + j in its high nibble; q are the stored nibbles in [0, 15]."""
+    assert len(q) == 32 and all(0 <= v < 16 for v in q)
+    return bytes([q[j] | (q[16 + j] << 4) for j in range(16)])
+
+
+# (name, d_bits, q[32] stored nibbles, hand-derived quant bytes)
+Q4_0_BLOCKS = [
+    ("unit_scale_ramp", 0x3C00, [j % 16 for j in range(32)], "00112233445566778899aabbccddeeff"),
+    ("halves_differ", 0x3800, [0] * 16 + [15] * 16, "f0" * 16),
+    ("position_code", 0x3C00, [15 - j for j in range(16)] + list(range(16)), "0f1e2d3c4b5a69788796a5b4c3d2e1f0"),
+    ("subnormal_scale", 0x0001, [8] * 31 + [0], "88" * 15 + "08"),
+    ("negative_scale", 0xC000, [3] * 32, "33" * 16),
+    ("zero_scale", 0x0000, [5, 9] * 16, "5599" * 8),
+]
+
+
 # ---------------------------------------------------------------- Q6_K
 
 def pack_q6_planes(q: list[int]) -> bytes:
@@ -228,6 +248,22 @@ def main() -> None:
             "q": q,
             "hex": raw.hex(),
             "expect": [frac_to_hex(d * v) for v in q],
+        })
+
+    q40 = []
+    for name, d_bits, q, q_hex in Q4_0_BLOCKS:
+        qb = pack_q4_0_quants(q)
+        if qb.hex() != q_hex:
+            raise SystemExit(f"{name}: encoder gives {qb.hex()}, hand derivation says {q_hex}")
+        raw = bytes([d_bits & 0xFF, d_bits >> 8]) + qb
+        assert len(raw) == 18
+        d = fp16_value(d_bits)
+        q40.append({
+            "name": name,
+            "d_bits": d_bits,
+            "q": q,
+            "hex": raw.hex(),
+            "expect": [frac_to_hex(d * (v - 8)) for v in q],
         })
 
     q4 = []
@@ -316,6 +352,10 @@ def main() -> None:
             "layouts are the public GGUF ones. Written by tests/golden/make_handbuilt_blocks.py.")
     with open(os.path.join(HERE, "q8_0_handbuilt.json"), "w") as f:
         json.dump({"citation": note, "blocks": q8}, f, indent=1)
+        f.write("\n")
+    with open(os.path.join(HERE, "q4_0_handbuilt.json"), "w") as f:
+        json.dump({"citation": note.replace("(Q8_0, Q4_K_M GGUF)", "(Q8_0, Q4_K_M GGUF; the Gemma-4 QAT rows: Q4_0)"),
+                   "blocks": q40}, f, indent=1)
         f.write("\n")
     with open(os.path.join(HERE, "q4_k_handbuilt.json"), "w") as f:
         json.dump({"citation": note, "blocks": q4}, f, indent=1)

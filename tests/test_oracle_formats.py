@@ -1,4 +1,4 @@
-"""Pins for the oracle's block decoding (Q8_0, Q4_K, Q5_K, Q6_K, IQ4_XS) and scalar formats.
+"""Pins for the oracle's block decoding (Q8_0, Q4_0, Q4_K, Q5_K, Q6_K, IQ4_XS) and scalar formats.
 
 Everything here runs on the CPU. Each check ties the oracle to something other
 than itself: hand-built blocks whose values are known by construction
@@ -18,8 +18,8 @@ import synth
 
 sys.path.insert(0, os.path.join(os.path.dirname(__file__), "golden"))
 from make_handbuilt_blocks import (  # noqa: E402
-    IQ4_XS_GRID, pack_iq4_indices, pack_iq4_xs_scales, pack_nibbles, pack_q5_high_bits, pack_q6_planes,
-    pack_scales_mins)
+    IQ4_XS_GRID, pack_iq4_indices, pack_iq4_xs_scales, pack_nibbles, pack_q4_0_quants, pack_q5_high_bits,
+    pack_q6_planes, pack_scales_mins)
 
 
 def _load(golden_dir, name):
@@ -665,3 +665,102 @@ def test_iq4_xs_rejects_wrong_sizes():
         oracle.dequant_iq4_xs(bytes(135), 1, 256)
     with pytest.raises(ValueError):
         oracle.dequant_iq4_xs(bytes(136), 1, 128)
+
+
+# ---------------------------------------------------------------- Q4_0
+
+def test_q4_0_handbuilt_blocks(golden_dir):
+    for blk in _load(golden_dir, "q4_0_handbuilt.json"):
+        raw = bytes.fromhex(blk["hex"])
+        d, q = oracle.q4_0_fields(raw, 1, 32)
+        assert list(q[0, 0]) == blk["q"], blk["name"]
+        assert d[0, 0] == oracle.fp16_bits_to_f64(np.array([blk["d_bits"]]))[0]
+        w = oracle.dequant_q4_0(raw, 1, 32)[0]
+        assert np.array_equal(w, [float.fromhex(v) for v in blk["expect"]]), blk["name"]
+
+
+def test_q4_0_handbuilt_values_by_hand(golden_dir):
+    blocks = {b["name"]: bytes.fromhex(b["hex"]) for b in _load(golden_dir, "q4_0_handbuilt.json")}
+    w = lambda name: list(oracle.dequant_q4_0(blocks[name], 1, 32)[0])  # noqa: E731
+    # d = 1, byte j = 0x11 * j: weights j and 16 + j both j - 8
+    assert w("unit_scale_ramp") == [float(j - 8) for j in range(16)] * 2
+    # d = 0.5, bytes 0xF0: the first 16 weights -4, the last 16 weights 3.5
+    assert w("halves_differ") == [-4.0] * 16 + [3.5] * 16
+    # d = 1, byte j = (j << 4) | (15 - j): weight j is 7 - j, weight 16 + j is j - 8
+    assert w("position_code") == [float(7 - j) for j in range(16)] + [float(j - 8) for j in range(16)]
+    # d = 2^-24, all nibbles 8 except weight 31's: zeros, then -8 * 2^-24
+    assert w("subnormal_scale") == [0.0] * 31 + [-8 * 2.0 ** -24]
+    # d = -2, nibbles 3: every weight 10
+    assert w("negative_scale") == [10.0] * 32
+    assert w("zero_scale") == [0.0] * 32
+
+
+def test_q4_0_nibble_locality():
+    raw = bytearray(synth.q4_0_weights(85, 1, 32))
+    base = oracle.dequant_q4_0(bytes(raw), 1, 32)[0]
+    d, _ = oracle.q4_0_fields(bytes(raw), 1, 32)
+    for j in range(16):
+        for mask, weight in ((0x0F, j), (0xF0, 16 + j)):
+            mod = bytearray(raw)
+            mod[2 + j] ^= mask
+            w = oracle.dequant_q4_0(bytes(mod), 1, 32)[0]
+            changed = np.nonzero(w != base)[0]
+            assert list(changed) == ([weight] if d[0, 0] != 0 else []), (j, mask)
+            step = abs(w[weight] - base[weight])
+            assert step == abs(d[0, 0]) * abs(((raw[2 + j] ^ mask) & mask) - (raw[2 + j] & mask)) / (16 if mask == 0xF0 else 1)
+
+
+def test_q4_0_scale_bytes_own_the_block():
+    raw = bytearray(synth.q4_0_weights(86, 2, 64))
+    base = oracle.dequant_q4_0(bytes(raw), 2, 64)
+    _, q = oracle.q4_0_fields(bytes(raw), 2, 64)
+    for blk in range(4):
+        for byte in (0, 1):
+            mod = bytearray(raw)
+            mod[18 * blk + byte] ^= 0x04
+            changed = set(map(tuple, np.argwhere(oracle.dequant_q4_0(bytes(mod), 2, 64) != base)))
+            n, t = divmod(blk, 2)
+            assert changed == {(n, 32 * t + j) for j in range(32) if q[n, t, j] != 8}, (blk, byte)
+
+
+def test_q4_0_pack_unpack_bijection():
+    for v in range(16):
+        for pos in range(32):
+            q = [(pos + 3 * i) % 16 for i in range(32)]
+            q[pos] = v
+            raw = bytes([0x00, 0x3C]) + pack_q4_0_quants(q)
+            assert list(oracle.q4_0_fields(raw, 1, 32)[1][0, 0]) == q
+    raw = synth.q4_0_weights(87, 3, 96)
+    _, q = oracle.q4_0_fields(raw, 3, 96)
+    blocks = raw.reshape(-1, 18)
+    for b in range(blocks.shape[0]):
+        n, t = divmod(b, 3)
+        assert pack_q4_0_quants([int(v) for v in q[n, t]]) == bytes(blocks[b, 2:])
+
+
+def test_q4_0_requant_round_trip():
+    raw = synth.q4_0_weights(88, 4, 256)
+    w = oracle.dequant_q4_0(raw, 4, 256).reshape(4, 8, 32)
+    d, q = oracle.q4_0_fields(raw, 4, 256)
+    nz = d != 0
+    q_back = np.rint(w / np.where(nz, d, 1.0)[:, :, None]) + 8
+    assert np.array_equal(q_back[nz], q[nz])
+    assert np.all(w[~nz] == 0)
+
+
+def test_q4_0_weights_exact_in_fp32_and_generator_distribution():
+    raw = synth.q4_0_weights(89, 64, 1024)
+    w = oracle.dequant_q4_0(raw, 64, 1024)
+    assert np.array_equal(oracle.dequant_q4_0_f32(raw, 64, 1024).astype(np.float64), w)
+    d, q = oracle.q4_0_fields(raw, 64, 1024)
+    counts = np.bincount(q.reshape(-1), minlength=16)
+    assert counts.min() > 0.9 * q.size / 16 and counts.max() < 1.1 * q.size / 16
+    assert (d < 0).mean() > 0.4 and (d > 0).mean() > 0.4
+
+
+def test_q4_0_rejects_wrong_sizes():
+    with pytest.raises(ValueError):
+        oracle.dequant_q4_0(bytes(17), 1, 32)
+    with pytest.raises(ValueError):
+        oracle.dequant_q4_0(bytes(18), 1, 16)
+

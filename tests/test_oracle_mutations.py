@@ -41,6 +41,12 @@ MUTATIONS = {
     "min_term_dropped": [("return (scale * q - offset)", "return (scale * q)")],
     "subblock_index_shift": [("scale = (d[:, :, None] * sc).repeat(32, axis=2)",
                               "scale = np.roll(d[:, :, None] * sc, 1, axis=2).repeat(32, axis=2)")],
+    "q4_0_nibble_halves_swapped": [("q = np.concatenate([qs & 0x0F, qs >> 4], axis=2)",
+                                    "q = np.concatenate([qs >> 4, qs & 0x0F], axis=2)")],
+    "q4_0_offset_dropped": [("(d[:, :, None] * (q - 8))", "(d[:, :, None] * q)")],
+    "q4_0_offset_off_by_one": [("(d[:, :, None] * (q - 8))", "(d[:, :, None] * (q - 7))")],
+    "q4_0_interleaved_nibbles": [("q = np.concatenate([qs & 0x0F, qs >> 4], axis=2)",
+                                  "q = np.stack([qs & 0x0F, qs >> 4], axis=3).reshape(qs.shape[0], qs.shape[1], 32)")],
     "q8_0_unsigned_quants": [("q = blocks[:, :, 2:].view(np.int8).astype(np.int64)",
                               "q = blocks[:, :, 2:].astype(np.int64)")],
     "gemv_transposed": [("return x2 @ np.asarray(w, dtype=np.float64).T", "return (np.asarray(w, dtype=np.float64) @ x2.T)")],
@@ -95,6 +101,13 @@ def _pins(o) -> list:
     def golden_q6():
         for blk in _golden("q6_k_handbuilt.json"):
             w = o.dequant_q6_k(bytes.fromhex(blk["hex"]), 1, 256)[0]
+            if not np.array_equal(w, [float.fromhex(v) for v in blk["expect"]]):
+                return False
+        return True
+
+    def golden_q40():
+        for blk in _golden("q4_0_handbuilt.json"):
+            w = o.dequant_q4_0(bytes.fromhex(blk["hex"]), 1, 32)[0]
             if not np.array_equal(w, [float.fromhex(v) for v in blk["expect"]]):
                 return False
         return True
@@ -159,6 +172,7 @@ def _pins(o) -> list:
     check("golden_q5", golden_q5)
     check("golden_q6", golden_q6)
     check("golden_q8", golden_q8)
+    check("golden_q40", golden_q40)
     check("gemv_unit_vectors", gemv_unit_vectors)
     check("route_hand_set", route_hand_set)
     check("silu_closed_form", silu_closed_form)

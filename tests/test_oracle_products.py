@@ -93,6 +93,34 @@ def test_q6_k_gemv_matches_exact_rational(n_rows, k, m):
             assert abs(Fraction(float(y[r, n])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
 
 
+@pytest.mark.parametrize("n_rows,k,m", [(3, 64, 1), (2, 256, 4), (4, 96, 3)])
+def test_q4_0_gemv_matches_exact_rational(n_rows, k, m):
+    raw = synth.q4_0_weights(61 + m, n_rows, k)
+    x = synth.bf16_normal(62 + m, (m, k))
+    y = oracle.qmv_q4_0(raw, x, n_rows, k)
+    exact = _exact_dot_rows(oracle.dequant_q4_0(raw, n_rows, k), oracle.bf16_bits_to_f64(x))
+    assert y.shape == (m, n_rows)
+    for r in range(m):
+        for n in range(n_rows):
+            e = exact[r][n]
+            assert abs(Fraction(float(y[r, n])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
+
+
+def test_q4_0_gemv_half_block_closed_form(golden_dir):
+    # x = 1 on the low-nibble half (weights 0..15) or the high-nibble half
+    # (16..31): y = d * (sum of that half's nibbles - 128), from the stated fields
+    with open(os.path.join(golden_dir, "q4_0_handbuilt.json")) as f:
+        blocks = json.load(f)["blocks"]
+    for blk in blocks:
+        raw = bytes.fromhex(blk["hex"])
+        d = oracle.fp16_bits_to_f64(np.array([blk["d_bits"]]))[0]
+        for half in (0, 1):
+            x = np.zeros((1, 32), dtype=np.uint16)
+            x[0, 16 * half:16 * half + 16] = 0x3F80
+            y = oracle.qmv_q4_0(raw, x, 1, 32)[0, 0]
+            assert y == d * (sum(blk["q"][16 * half:16 * half + 16]) - 128), (blk["name"], half)
+
+
 def test_q6_k_gemv_constant_over_sixteen_weights_closed_form(golden_dir):
     # x = 1 on weights 16i .. 16i + 15 only: y = d sc_i sum(q), from the stated fields
     with open(os.path.join(golden_dir, "q6_k_handbuilt.json")) as f:
