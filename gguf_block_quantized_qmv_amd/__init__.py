@@ -17,7 +17,8 @@ __all__ = [
     "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmv_iq4_xs_moe",
     "qmv_iq4_xs_moe_workspace", "qmm_q4_k_prefill_workspace",
     "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16", "qmv_dequant_q8_0_f32",
-    "qmv_dequant_iq4_xs_f32", "qmv_q5_k", "qmv_dequant_q5_k_f32", "qmv_q6_k", "qmv_dequant_q6_k_f32",
+    "qmv_dequant_iq4_xs_f32", "qmv_q5_k", "qmv_dequant_q5_k_f32", "qmv_q6_k", "qmv_dequant_q6_k_f32", "qmv_q4_0",
+    "qmv_dequant_q4_0_f32", "q4_0_bytes",
     "q4_k_bytes", "q5_k_bytes", "q6_k_bytes", "q8_0_bytes",
     "iq4_xs_bytes", "EXPORTS",
 ]
@@ -36,6 +37,7 @@ EXPORTS = {
     "qmv_iq4_xs": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "qmv_q5_k": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "qmv_q6_k": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
+    "qmv_q4_0": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "qmv_q4_k_moe_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "qmv_q4_k_moe": (_c_int, [_vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
                               _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
@@ -50,6 +52,7 @@ EXPORTS = {
     "qmv_dequant_iq4_xs_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
     "qmv_dequant_q5_k_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
     "qmv_dequant_q6_k_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
+    "qmv_dequant_q4_0_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
 }
 
 
@@ -101,6 +104,10 @@ def q5_k_bytes(n: int, k: int) -> int:
 
 def q6_k_bytes(n: int, k: int) -> int:
     return n * (k // 256) * 210
+
+
+def q4_0_bytes(n: int, k: int) -> int:
+    return n * (k // 32) * 18
 
 
 def q8_0_bytes(n: int, k: int) -> int:
@@ -355,4 +362,27 @@ def qmv_dequant_q6_k_f32(w, n: int, k: int, out=None, stream=None):
         out = torch.empty((n, k), dtype=torch.float32, device=w.device)
     _dev(out, "out", (torch.float32,))
     _check(lib.qmv_dequant_q6_k_f32(_ptr(w), _nbytes(w), _ptr(out), n, k, _stream(stream)), "qmv_dequant_q6_k_f32")
+    return out
+
+
+def qmv_q4_0(w, x, n: int, k: int, y=None, stream=None):
+    """y[m, n] = x[m, k] @ dequant(w)^T for a Q4_0 matrix w (uint8 bytes) and bf16 x (1 <= m <= 4)."""
+    torch = _torch()
+    _dev(w, "w", (torch.uint8,))
+    _dev(x, "x", _bf16_types())
+    m = x.shape[0] if x.dim() == 2 else 1
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(y, "y", (torch.float32,))
+    _check(lib.qmv_q4_0(_ptr(w), _nbytes(w), _ptr(x), _ptr(y), m, n, k, _stream(stream)), "qmv_q4_0")
+    return y
+
+
+def qmv_dequant_q4_0_f32(w, n: int, k: int, out=None, stream=None):
+    torch = _torch()
+    _dev(w, "w", (torch.uint8,))
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    _dev(out, "out", (torch.float32,))
+    _check(lib.qmv_dequant_q4_0_f32(_ptr(w), _nbytes(w), _ptr(out), n, k, _stream(stream)), "qmv_dequant_q4_0_f32")
     return out

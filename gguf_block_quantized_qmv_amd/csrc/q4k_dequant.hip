@@ -1,4 +1,4 @@
-// Q4_K dequantization to dense fp32 or bf16, and Q5_K to fp32, gfx950.
+// Q4_K dequantization to dense fp32 or bf16, and Q5_K and Q4_0 to fp32, gfx950.
 //
 // One thread per 16-byte quant granule (32 weights): granule g of a block holds
 // quant bytes 16g..16g+15, i.e. chunk c = g / 2, weights 64c + 16(g%2) + 0..15 in
@@ -106,6 +106,29 @@ __global__ __launch_bounds__(256) void q5k_dequant_kernel(const uint8_t *__restr
   }
 }
 
+// Q4_0 to fp32: one thread per 18-byte block, read as nine 16-bit halves (the
+// blocks are only 2-byte aligned). Byte i holds weight i (low nibble) and
+// weight 16 + i (high nibble); d (q - 8) is exact in fp32.
+__global__ __launch_bounds__(256) void q40_dequant_kernel(const uint8_t *__restrict__ w, float *__restrict__ out,
+                                                          const size_t nblocks) {
+  const size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const uint16_t *p = reinterpret_cast<const uint16_t *>(w + b * 18);
+  const float d = fp16_bits_to_f32(p[0]);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t h = p[1 + i];  // quant bytes 2i (low half) and 2i + 1
+    v[2 * i] = d * (float)((int)(h & 0xFu) - 8);
+    v[2 * i + 1] = d * (float)((int)((h >> 8) & 0xFu) - 8);
+    v[16 + 2 * i] = d * (float)((int)((h >> 4) & 0xFu) - 8);
+    v[16 + 2 * i + 1] = d * (float)((int)((h >> 12) & 0xFu) - 8);
+  }
+  float4 *o = reinterpret_cast<float4 *>(out + b * 32);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) o[g] = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+}
+
 }  // namespace
 
 int launch_dequant_q5_k(const void *w, float *out, int n, int k, void *stream) {
@@ -121,6 +144,13 @@ int launch_dequant_q4_k(const void *w, void *out, bool bf16, int n, int k, void 
   hipStream_t s = static_cast<hipStream_t>(stream);
   return bf16 ? launch_kernel("q4k_dequant_kernel", q4k_dequant_kernel<true>, dim3(grid), dim3(256), 0, s, w, out, ngran)
               : launch_kernel("q4k_dequant_kernel", q4k_dequant_kernel<false>, dim3(grid), dim3(256), 0, s, w, out, ngran);
+}
+
+int launch_dequant_q4_0(const void *w, float *out, int n, int k, void *stream) {
+  const size_t nblocks = (size_t)n * (size_t)(k >> 5);
+  const unsigned grid = (unsigned)((nblocks + 255) / 256);
+  return launch_kernel("q40_dequant_kernel", q40_dequant_kernel, dim3(grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint8_t *>(w), out, nblocks);
 }
 
 }  // namespace qmv

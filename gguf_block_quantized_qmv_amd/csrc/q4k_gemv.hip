@@ -33,6 +33,9 @@
 namespace qmv {
 namespace {
 
+// Block formats of this kernel body.
+constexpr int kFmtQ4K = 0, kFmtQ5K = 1, kFmtQ40 = 2;
+
 
 template <int M>
 __host__ __device__ constexpr size_t dense_lds_bytes(int k) {
@@ -141,11 +144,71 @@ __device__ __forceinline__ bf16x2 biased_q5_pair_hi(const uint32_t q) {
   return __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(0x43434343u, q, 0x04030402u));
 }
 
-template <int M, bool Q5>
+// Q4_0: the lane's chunk is the pair of 18-byte blocks at byte 36c of a group
+// of eight (w0..w3 = w03, w4..w7 = w47, w8). Block A (weights 64c .. 64c + 31,
+// sub-block 2c) has d in the low half of w0 and its 16 quant bytes at pair
+// bytes 2..17 (realigned by 16 bits); block B (sub-block 2c + 1) has d in the
+// high half of w4 and its quant bytes in w5..w8. Byte i of a block holds weight
+// i in its low nibble and weight 16 + i in its high nibble; a weight is
+// d (q - 8), so per block acc += d S - 8 d X with S = sum q x over the block
+// (exact bf16 nibbles, exact products) and X its activation sum.
+template <int M>
+__device__ __forceinline__ void q40_chunk(float (&acc)[M], const uint4 w03, const uint4 w47, const uint32_t w8,
+                                          const uint4 *__restrict__ xc, const int gpp, const float *__restrict__ xsc,
+                                          const int nsub) {
+  const uint32_t qa[4] = {__builtin_amdgcn_alignbit(w03.y, w03.x, 16), __builtin_amdgcn_alignbit(w03.z, w03.y, 16),
+                          __builtin_amdgcn_alignbit(w03.w, w03.z, 16), __builtin_amdgcn_alignbit(w47.x, w03.w, 16)};
+  const uint32_t qb[4] = {w47.y, w47.z, w47.w, w8};
+  const float da = fp16_bits_to_f32(w03.x & 0xFFFFu), db = fp16_bits_to_f32(w47.x >> 16);
+  float sa_lo[M], sa_hi[M], sb_lo[M], sb_hi[M];
+#pragma unroll
+  for (int r = 0; r < M; ++r) sa_lo[r] = sa_hi[r] = sb_lo[r] = sb_hi[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t la = qa[i] & 0x0F0F0F0Fu, ha = (qa[i] >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lb = qb[i] & 0x0F0F0F0Fu, hb = (qb[i] >> 4) & 0x0F0F0F0Fu;
+    const bf16x2 la0 = nibbles_to_bf16x2<false>(la), la1 = nibbles_to_bf16x2<true>(la);
+    const bf16x2 ha0 = nibbles_to_bf16x2<false>(ha), ha1 = nibbles_to_bf16x2<true>(ha);
+    const bf16x2 lb0 = nibbles_to_bf16x2<false>(lb), lb1 = nibbles_to_bf16x2<true>(lb);
+    const bf16x2 hb0 = nibbles_to_bf16x2<false>(hb), hb1 = nibbles_to_bf16x2<true>(hb);
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+      // weights 4i .. 4i + 3 (low nibbles) and 16 + 4i .. 16 + 4i + 3 (high)
+      const uint4 xal = xc[r * gpp + (i >> 1)], xah = xc[r * gpp + 2 + (i >> 1)];
+      const uint4 xbl = xc[r * gpp + 4 + (i >> 1)], xbh = xc[r * gpp + 6 + (i >> 1)];
+      const uint32_t al0 = (i & 1) ? xal.z : xal.x, al1 = (i & 1) ? xal.w : xal.y;
+      const uint32_t ah0 = (i & 1) ? xah.z : xah.x, ah1 = (i & 1) ? xah.w : xah.y;
+      const uint32_t bl0 = (i & 1) ? xbl.z : xbl.x, bl1 = (i & 1) ? xbl.w : xbl.y;
+      const uint32_t bh0 = (i & 1) ? xbh.z : xbh.x, bh1 = (i & 1) ? xbh.w : xbh.y;
+      sa_lo[r] = __builtin_amdgcn_fdot2_f32_bf16(la0, __builtin_bit_cast(bf16x2, al0), sa_lo[r], false);
+      sa_hi[r] = __builtin_amdgcn_fdot2_f32_bf16(ha0, __builtin_bit_cast(bf16x2, ah0), sa_hi[r], false);
+      sb_lo[r] = __builtin_amdgcn_fdot2_f32_bf16(lb0, __builtin_bit_cast(bf16x2, bl0), sb_lo[r], false);
+      sb_hi[r] = __builtin_amdgcn_fdot2_f32_bf16(hb0, __builtin_bit_cast(bf16x2, bh0), sb_hi[r], false);
+      sa_lo[r] = __builtin_amdgcn_fdot2_f32_bf16(la1, __builtin_bit_cast(bf16x2, al1), sa_lo[r], false);
+      sa_hi[r] = __builtin_amdgcn_fdot2_f32_bf16(ha1, __builtin_bit_cast(bf16x2, ah1), sa_hi[r], false);
+      sb_lo[r] = __builtin_amdgcn_fdot2_f32_bf16(lb1, __builtin_bit_cast(bf16x2, bl1), sb_lo[r], false);
+      sb_hi[r] = __builtin_amdgcn_fdot2_f32_bf16(hb1, __builtin_bit_cast(bf16x2, bh1), sb_hi[r], false);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < M; ++r) {
+    const float2 xsm = *reinterpret_cast<const float2 *>(xsc + r * nsub);
+    acc[r] = __builtin_fmaf(da, sa_lo[r] + sa_hi[r], acc[r]);
+    acc[r] = __builtin_fmaf(-8.0f * da, xsm.x, acc[r]);
+    acc[r] = __builtin_fmaf(db, sb_lo[r] + sb_hi[r], acc[r]);
+    acc[r] = __builtin_fmaf(-8.0f * db, xsm.y, acc[r]);
+  }
+}
+
+template <int M, int F>
 __device__ __forceinline__ void dense_chunk(float (&acc)[M], const uint4 hdr, const uint4 qa, const uint4 qb,
                                             const uint4 hb0, const uint4 hb1, const int hsh, const ScaleSel &sel,
                                             const uint4 *__restrict__ xc, const int gpp,
                                             const float *__restrict__ xsc, const int nsub) {
+  if constexpr (F == kFmtQ40) {
+    q40_chunk<M>(acc, hdr, qa, qb.x, xc, gpp, xsc, nsub);
+    return;
+  }
   const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
   const uint32_t hw[8] = {hb0.x, hb0.y, hb0.z, hb0.w, hb1.x, hb1.y, hb1.z, hb1.w};
   float s_lo0[M], s_lo1[M], s_hi0[M], s_hi1[M];
@@ -156,7 +219,7 @@ __device__ __forceinline__ void dense_chunk(float (&acc)[M], const uint4 hdr, co
     const uint32_t l0 = qw[2 * g] & 0x0F0F0F0Fu, h0 = (qw[2 * g] >> 4) & 0x0F0F0F0Fu;
     const uint32_t l1 = qw[2 * g + 1] & 0x0F0F0F0Fu, h1 = (qw[2 * g + 1] >> 4) & 0x0F0F0F0Fu;
     bf16x2 lo0, lo1, lo2, lo3, hi0, hi1, hi2, hi3;
-    if constexpr (Q5) {
+    if constexpr (F == kFmtQ5K) {
       // bit 0 of each byte of t: the low-nibble weight's fifth bit; bit 1: the high-nibble weight's
       const uint32_t t0 = hw[2 * g] >> hsh, t1 = hw[2 * g + 1] >> hsh;
       const uint32_t ql0 = l0 | ((t0 << 4) & 0x10101010u), qh0 = h0 | ((t0 << 3) & 0x10101010u);
@@ -191,25 +254,34 @@ __device__ __forceinline__ void dense_chunk(float (&acc)[M], const uint4 hdr, co
     const float s_lo = s_lo0[r] + s_lo1[r], s_hi = s_hi0[r] + s_hi1[r];
     const float2 xsm = *reinterpret_cast<const float2 *>(xsc + r * nsub);
     acc[r] = __builtin_fmaf(cs.a0, s_lo, acc[r]);
-    if constexpr (Q5) acc[r] = __builtin_fmaf(-cs.a0, 128.0f * xsm.x, acc[r]);
+    if constexpr (F == kFmtQ5K) acc[r] = __builtin_fmaf(-cs.a0, 128.0f * xsm.x, acc[r]);
     acc[r] = __builtin_fmaf(-cs.b0, xsm.x, acc[r]);
     acc[r] = __builtin_fmaf(cs.a1, s_hi, acc[r]);
-    if constexpr (Q5) acc[r] = __builtin_fmaf(-cs.a1, 128.0f * xsm.y, acc[r]);
+    if constexpr (F == kFmtQ5K) acc[r] = __builtin_fmaf(-cs.a1, 128.0f * xsm.y, acc[r]);
     acc[r] = __builtin_fmaf(-cs.b1, xsm.y, acc[r]);
   }
 }
 
-template <bool Q5>
-constexpr int block_bytes() { return Q5 ? kQ5KBlockBytes : kQ4KBlockBytes; }
+// Bytes per 256-weight group: a Q4_K or Q5_K super-block, or eight Q4_0 blocks.
+template <int F>
+constexpr int block_bytes() { return F == kFmtQ5K ? kQ5KBlockBytes : kQ4KBlockBytes; }
 
 // The 16-byte weight loads of one step for the lane holding chunk c of a block
 // at bp: the block header and the chunk's 32 quant bytes, and for Q5_K the 32
 // bytes of the high-bit plane (every chunk's lane reads all of them).
-template <bool Q5>
+template <int F>
 __device__ __forceinline__ void load_step(const uint8_t *__restrict__ bp, const int c, uint4 &hdr, uint4 &qa,
                                           uint4 &qb, uint4 &hb0, uint4 &hb1) {
+  if constexpr (F == kFmtQ40) {
+    // the pair of 18-byte blocks at byte 36c: 4-byte aligned, read as dwords
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(bp + 36 * c);
+    hdr = make_uint4(p[0], p[1], p[2], p[3]);
+    qa = make_uint4(p[4], p[5], p[6], p[7]);
+    qb = make_uint4(p[8], 0u, 0u, 0u);
+    return;
+  }
   hdr = *reinterpret_cast<const uint4 *>(bp);
-  if constexpr (Q5) {
+  if constexpr (F == kFmtQ5K) {
     hb0 = *reinterpret_cast<const uint4 *>(bp + 16);
     hb1 = *reinterpret_cast<const uint4 *>(bp + 32);
     qa = *reinterpret_cast<const uint4 *>(bp + 48 + 32 * c);
@@ -226,14 +298,14 @@ __device__ __forceinline__ void load_step(const uint8_t *__restrict__ bp, const 
 // NS > 0 (unrolled, t a compile-time step): only step NS - 1 can be partial,
 // and last_ok says whether this lane's block exists there. NS == 0: FULL says
 // the row is a whole number of steps.
-template <bool FULL, int NS, int kBlocksPerStep, bool Q5>
+template <bool FULL, int NS, int kBlocksPerStep, int F>
 __device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *wfb, const uint8_t *wl, const bool active, const int t,
                                                    const int nsteps, const int jb, const int nblk,
                                                    const bool last_ok) {
   bool ok;
   if constexpr (NS > 0) ok = active && t < NS && (t < NS - 1 || last_ok);
   else ok = active && t < nsteps && (FULL || t * kBlocksPerStep + jb < nblk);
-  return ok ? wl + (size_t)(t * kBlocksPerStep) * block_bytes<Q5>() : wfb;
+  return ok ? wl + (size_t)(t * kBlocksPerStep) * block_bytes<F>() : wfb;
 }
 
 // G lanes own one output row (G = 16 or 32): a step covers G/4 super-blocks of
@@ -276,7 +348,7 @@ constexpr int kQ4Depth32 = 2;
 template <int M, int G>
 constexpr int x_head() { return (G == 16 ? 4 * M : 9 * M) < 9 ? (G == 16 ? 4 * M : 9 * M) : 9; }
 
-template <int M, int G, int D, bool FULL, int NS, bool Q5>
+template <int M, int G, int D, bool FULL, int NS, int F>
 __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const uint16_t *__restrict__ x,
                                           float *__restrict__ y, const int n, const int k) {
   constexpr int kBlocksPerStep = G / 4;
@@ -303,9 +375,9 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
   // loads with no block of their own (past the row, past the matrix, past a
   // partial last step) read the last block of the lane's row (of the last row
   // when the row is past the matrix), which the same or a recent load also reads
-  const uint8_t *wfb = w + ((size_t)(active ? row : n - 1) * (size_t)nblk + (size_t)(nblk - 1)) * block_bytes<Q5>();
-  const uint8_t *wl = w + (size_t)(active ? row : 0) * (size_t)nblk * block_bytes<Q5>() +
-                      (size_t)jb * block_bytes<Q5>();
+  const uint8_t *wfb = w + ((size_t)(active ? row : n - 1) * (size_t)nblk + (size_t)(nblk - 1)) * block_bytes<F>();
+  const uint8_t *wl = w + (size_t)(active ? row : 0) * (size_t)nblk * block_bytes<F>() +
+                      (size_t)jb * block_bytes<F>();
 
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
   constexpr int kXHead = x_head<M, G>();
@@ -317,12 +389,12 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
     // ring only after the head has arrived and is in LDS. Requests queue in the
     // memory system in issue order, so every weight request issued before a
     // wave's activations are back delays them (and with them its first step).
-    load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(wfb, wl, active, 0, nsteps, jb, nblk, last_ok), c, hdr[0], qa[0], qb[0],
+    load_step<F>(step_ptr<FULL, NS, kBlocksPerStep, F>(wfb, wl, active, 0, nsteps, jb, nblk, last_ok), c, hdr[0], qa[0], qb[0],
                   hb0[0], hb1[0]);
     store_x_head<M, kXHead>(xv, xs, gpr, gpp, nthreads);
 #pragma unroll
     for (int u = 1; u < D; ++u)
-      load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(wfb, wl, active, u, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u], qb[u],
+      load_step<F>(step_ptr<FULL, NS, kBlocksPerStep, F>(wfb, wl, active, u, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u], qb[u],
                     hb0[u], hb1[u]);
     // rows up to NS steps are covered by the head when this holds, and the
     // loop that stages the rest is compiled out
@@ -335,7 +407,7 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
     stage_x_tail<M, kXHead, 8>(xg, xs, gpr, gpp, nthreads);
 #pragma unroll
     for (int u = 0; u < D; ++u)
-      load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(wfb, wl, active, u, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u], qb[u],
+      load_step<F>(step_ptr<FULL, NS, kBlocksPerStep, F>(wfb, wl, active, u, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u], qb[u],
                     hb0[u], hb1[u]);
   }
   x_sums<M>(xs, xsum, gpp, nsub, nthreads);
@@ -354,10 +426,10 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
       constexpr int kD = D;
       const int u = s % kD;
       if (s < NS - 1 || last_ok)
-        dense_chunk<M, Q5>(acc, hdr[u], qa[u], qb[u], hb0[u], hb1[u], 2 * c, sel, xb + s * kStepGranules, gpp,
+        dense_chunk<M, F>(acc, hdr[u], qa[u], qb[u], hb0[u], hb1[u], 2 * c, sel, xb + s * kStepGranules, gpp,
                            sb + s * 2 * G, nsub);
       if (s + D < NS)
-        load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(wfb, wl, active, s + D, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u],
+        load_step<F>(step_ptr<FULL, NS, kBlocksPerStep, F>(wfb, wl, active, s + D, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u],
                       qb[u], hb0[u], hb1[u]);
     }
   } else {
@@ -366,9 +438,9 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
       for (int u = 0; u < D; ++u) {
         const int s = s0 + u;
         if (s < nsteps && (FULL || s * kBlocksPerStep + jb < nblk))
-          dense_chunk<M, Q5>(acc, hdr[u], qa[u], qb[u], hb0[u], hb1[u], 2 * c, sel, xb + s * kStepGranules, gpp,
+          dense_chunk<M, F>(acc, hdr[u], qa[u], qb[u], hb0[u], hb1[u], 2 * c, sel, xb + s * kStepGranules, gpp,
                              sb + s * 2 * G, nsub);
-        load_step<Q5>(step_ptr<FULL, NS, kBlocksPerStep, Q5>(wfb, wl, active, s + D, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u],
+        load_step<F>(step_ptr<FULL, NS, kBlocksPerStep, F>(wfb, wl, active, s + D, nsteps, jb, nblk, last_ok), c, hdr[u], qa[u],
                       qb[u], hb0[u], hb1[u]);
       }
     }
@@ -385,14 +457,21 @@ template <int M, int G, int D, bool FULL, int NS>
 __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q4k_gemv_kernel(const uint8_t *__restrict__ w,
                                                             const uint16_t *__restrict__ x,
                                                             float *__restrict__ y, const int n, const int k) {
-  gemv_body<M, G, D, FULL, NS, false>(w, x, y, n, k);
+  gemv_body<M, G, D, FULL, NS, kFmtQ4K>(w, x, y, n, k);
+}
+
+template <int M, int G, int D, bool FULL, int NS>
+__global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q40_gemv_kernel(const uint8_t *__restrict__ w,
+                                                            const uint16_t *__restrict__ x,
+                                                            float *__restrict__ y, const int n, const int k) {
+  gemv_body<M, G, D, FULL, NS, kFmtQ40>(w, x, y, n, k);
 }
 
 template <int M, int G, int D, bool FULL, int NS>
 __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q5k_gemv_kernel(const uint8_t *__restrict__ w,
                                                             const uint16_t *__restrict__ x,
                                                             float *__restrict__ y, const int n, const int k) {
-  gemv_body<M, G, D, FULL, NS, true>(w, x, y, n, k);
+  gemv_body<M, G, D, FULL, NS, kFmtQ5K>(w, x, y, n, k);
 }
 
 // Rows per workgroup. A launch is balanced when every CU gets the same number
@@ -416,11 +495,15 @@ inline int pick_rows(const int m, const int n, const int G, const size_t lds) {
   return dflt;
 }
 
-template <int M, int G, int D, bool FULL, int NS, bool Q5>
+template <int M, int G, int D, bool FULL, int NS, int F>
 int launch_cfg(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
   const size_t lds = dense_lds_bytes<M>(k);
-  auto *fn = Q5 ? q5k_gemv_kernel<M, G, D, FULL, NS> : q4k_gemv_kernel<M, G, D, FULL, NS>;
-  const char *name = Q5 ? "q5k_gemv_kernel" : "q4k_gemv_kernel";
+  // only the launched format's kernel is instantiated
+  void (*fn)(const uint8_t *, const uint16_t *, float *, int, int);
+  const char *name;
+  if constexpr (F == kFmtQ5K) fn = q5k_gemv_kernel<M, G, D, FULL, NS>, name = "q5k_gemv_kernel";
+  else if constexpr (F == kFmtQ40) fn = q40_gemv_kernel<M, G, D, FULL, NS>, name = "q40_gemv_kernel";
+  else fn = q4k_gemv_kernel<M, G, D, FULL, NS>, name = "q4k_gemv_kernel";
   static std::atomic<size_t> granted{0};
   if (allow_dynamic_lds(reinterpret_cast<const void *>(fn), lds, granted, name)) return QMV_ERR_HIP;
   const int rows = pick_rows(M, n, G, lds);
@@ -429,40 +512,40 @@ int launch_cfg(const void *w, const uint16_t *x, float *y, int n, int k, hipStre
 }
 
 // Runtime-length rows (any K).
-template <int M, int G, int D, bool Q5>
+template <int M, int G, int D, int F>
 int launch_any(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
-  if (((k >> 8) % (G / 4)) == 0) return launch_cfg<M, G, D, true, 0, Q5>(w, x, y, n, k, stream);
-  return launch_cfg<M, G, D, false, 0, Q5>(w, x, y, n, k, stream);
+  if (((k >> 8) % (G / 4)) == 0) return launch_cfg<M, G, D, true, 0, F>(w, x, y, n, k, stream);
+  return launch_cfg<M, G, D, false, 0, F>(w, x, y, n, k, stream);
 }
 
 // Lanes per row by row length: 16 up to K = 8192 (1..8 steps of 4 blocks), 32
 // beyond (steps of 8 blocks; 5..9 steps up to K = 18432, runtime loop after).
 // (FULL matters only to the runtime loop; the unrolled kernels test their
 // possibly partial last step themselves.)
-template <int M, bool Q5>
+template <int M, int F>
 int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
-  constexpr int D = Q5 ? q5_depth16<M>() : kQ4Depth16;
-  constexpr int D32 = Q5 ? q5_depth32<M>() : kQ4Depth32;
+  constexpr int D = F == kFmtQ5K ? q5_depth16<M>() : kQ4Depth16;
+  constexpr int D32 = F == kFmtQ5K ? q5_depth32<M>() : kQ4Depth32;
   const int nblk = k >> 8;
   if (k <= 8192) {
     switch ((nblk + 3) / 4) {
-      case 1: return launch_cfg<M, 16, D, false, 1, Q5>(w, x, y, n, k, stream);
-      case 2: return launch_cfg<M, 16, D, false, 2, Q5>(w, x, y, n, k, stream);
-      case 3: return launch_cfg<M, 16, D, false, 3, Q5>(w, x, y, n, k, stream);
-      case 4: return launch_cfg<M, 16, D, false, 4, Q5>(w, x, y, n, k, stream);
-      case 5: return launch_cfg<M, 16, D, false, 5, Q5>(w, x, y, n, k, stream);
-      case 6: return launch_cfg<M, 16, D, false, 6, Q5>(w, x, y, n, k, stream);
-      case 7: return launch_cfg<M, 16, D, false, 7, Q5>(w, x, y, n, k, stream);
-      default: return launch_cfg<M, 16, D, false, 8, Q5>(w, x, y, n, k, stream);
+      case 1: return launch_cfg<M, 16, D, false, 1, F>(w, x, y, n, k, stream);
+      case 2: return launch_cfg<M, 16, D, false, 2, F>(w, x, y, n, k, stream);
+      case 3: return launch_cfg<M, 16, D, false, 3, F>(w, x, y, n, k, stream);
+      case 4: return launch_cfg<M, 16, D, false, 4, F>(w, x, y, n, k, stream);
+      case 5: return launch_cfg<M, 16, D, false, 5, F>(w, x, y, n, k, stream);
+      case 6: return launch_cfg<M, 16, D, false, 6, F>(w, x, y, n, k, stream);
+      case 7: return launch_cfg<M, 16, D, false, 7, F>(w, x, y, n, k, stream);
+      default: return launch_cfg<M, 16, D, false, 8, F>(w, x, y, n, k, stream);
     }
   }
   switch ((nblk + 7) / 8) {
-    case 5: return launch_cfg<M, 32, D32, false, 5, Q5>(w, x, y, n, k, stream);
-    case 6: return launch_cfg<M, 32, D32, false, 6, Q5>(w, x, y, n, k, stream);
-    case 7: return launch_cfg<M, 32, D32, false, 7, Q5>(w, x, y, n, k, stream);
-    case 8: return launch_cfg<M, 32, D32, false, 8, Q5>(w, x, y, n, k, stream);
-    case 9: return launch_cfg<M, 32, D32, false, 9, Q5>(w, x, y, n, k, stream);
-    default: return launch_any<M, 32, D32, Q5>(w, x, y, n, k, stream);
+    case 5: return launch_cfg<M, 32, D32, false, 5, F>(w, x, y, n, k, stream);
+    case 6: return launch_cfg<M, 32, D32, false, 6, F>(w, x, y, n, k, stream);
+    case 7: return launch_cfg<M, 32, D32, false, 7, F>(w, x, y, n, k, stream);
+    case 8: return launch_cfg<M, 32, D32, false, 8, F>(w, x, y, n, k, stream);
+    case 9: return launch_cfg<M, 32, D32, false, 9, F>(w, x, y, n, k, stream);
+    default: return launch_any<M, 32, D32, F>(w, x, y, n, k, stream);
   }
 }
 
@@ -471,10 +554,10 @@ int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream
 int launch_q4_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (m) {
-    case 1: return launch_m<1, false>(w, x, y, n, k, s);
-    case 2: return launch_m<2, false>(w, x, y, n, k, s);
-    case 3: return launch_m<3, false>(w, x, y, n, k, s);
-    case 4: return launch_m<4, false>(w, x, y, n, k, s);
+    case 1: return launch_m<1, kFmtQ4K>(w, x, y, n, k, s);
+    case 2: return launch_m<2, kFmtQ4K>(w, x, y, n, k, s);
+    case 3: return launch_m<3, kFmtQ4K>(w, x, y, n, k, s);
+    case 4: return launch_m<4, kFmtQ4K>(w, x, y, n, k, s);
     default: return QMV_ERR_RANGE;
   }
 }
@@ -482,10 +565,21 @@ int launch_q4_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, i
 int launch_q5_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (m) {
-    case 1: return launch_m<1, true>(w, x, y, n, k, s);
-    case 2: return launch_m<2, true>(w, x, y, n, k, s);
-    case 3: return launch_m<3, true>(w, x, y, n, k, s);
-    case 4: return launch_m<4, true>(w, x, y, n, k, s);
+    case 1: return launch_m<1, kFmtQ5K>(w, x, y, n, k, s);
+    case 2: return launch_m<2, kFmtQ5K>(w, x, y, n, k, s);
+    case 3: return launch_m<3, kFmtQ5K>(w, x, y, n, k, s);
+    case 4: return launch_m<4, kFmtQ5K>(w, x, y, n, k, s);
+    default: return QMV_ERR_RANGE;
+  }
+}
+
+int launch_q4_0_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (m) {
+    case 1: return launch_m<1, kFmtQ40>(w, x, y, n, k, s);
+    case 2: return launch_m<2, kFmtQ40>(w, x, y, n, k, s);
+    case 3: return launch_m<3, kFmtQ40>(w, x, y, n, k, s);
+    case 4: return launch_m<4, kFmtQ40>(w, x, y, n, k, s);
     default: return QMV_ERR_RANGE;
   }
 }

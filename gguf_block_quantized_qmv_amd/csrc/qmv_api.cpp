@@ -244,6 +244,28 @@ int qmv_dequant_q5_k_f32(const void *w, size_t w_bytes, float *out, int n, int k
   return qmv::launch_dequant_q5_k(w, out, n, k, stream);
 }
 
+int qmv_q4_0(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, int m, int n, int k, void *stream) {
+  if (!w || !x_bf16 || !y) return QMV_ERR_NULL;
+  if (m < 1 || m > QMV_MAX_ROWS) return QMV_ERR_RANGE;
+  if (k <= 0 || k % 256) return QMV_ERR_SHAPE;   // the kernel steps over groups of eight blocks
+  int rc = check_matrix(w, w_bytes, n, k, 32, 18, 16);
+  if (rc) return rc;
+  if ((size_t)m * ((size_t)(k / 128) * 17 * 16 + (size_t)(k / 32) * 4) > QMV_LDS_X_BYTES) return QMV_ERR_RANGE;
+  if (!aligned(x_bf16, 16) || !aligned(y, 4)) return QMV_ERR_ALIGN;
+  const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 4;
+  if (overlap(y, yb, w, w_bytes) || overlap(y, yb, x_bf16, xb)) return QMV_ERR_ALIAS;
+  return qmv::launch_q4_0_gemv(w, x_bf16, y, m, n, k, stream);
+}
+
+int qmv_dequant_q4_0_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream) {
+  if (!w || !out) return QMV_ERR_NULL;
+  int rc = check_matrix(w, w_bytes, n, k, 32, 18, 2);
+  if (rc) return rc;
+  if (!aligned(out, 16)) return QMV_ERR_ALIGN;
+  if (overlap(out, (size_t)n * k * 4, w, w_bytes)) return QMV_ERR_ALIAS;
+  return qmv::launch_dequant_q4_0(w, out, n, k, stream);
+}
+
 int qmv_q6_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, int m, int n, int k, void *stream) {
   if (!w || !x_bf16 || !y) return QMV_ERR_NULL;
   if (m < 1 || m > QMV_MAX_ROWS) return QMV_ERR_RANGE;

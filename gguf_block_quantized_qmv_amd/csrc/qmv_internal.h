@@ -14,12 +14,14 @@ int launch_q8_0_gemv(const void *w, const float *x, float *y, int m, int n, int 
 int launch_q4_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
 int launch_q5_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
 int launch_q6_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
+int launch_q4_0_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
 int launch_iq4_xs_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
 bool iq4xs_fits_lds(int m, int k);
 int launch_dequant_iq4_xs(const void *w, float *out, int n, int k, void *stream);
 int launch_dequant_q4_k(const void *w, void *out, bool bf16, int n, int k, void *stream);
 int launch_dequant_q5_k(const void *w, float *out, int n, int k, void *stream);
 int launch_dequant_q6_k(const void *w, float *out, int n, int k, void *stream);
+int launch_dequant_q4_0(const void *w, float *out, int n, int k, void *stream);
 int launch_dequant_q8_0(const void *w, float *out, int n, int k, void *stream);
 int launch_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
                     const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs,

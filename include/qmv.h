@@ -131,6 +131,27 @@ int qmv_q5_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
              int m, int n, int k, void *stream);
 
 /*
+ * Q4_0 matrix times bf16 activation rows (m = 1..4): the format of the Gemma-4
+ * QAT models on the memra README model support table. 18-byte blocks of 32
+ * weights: fp16 d, then 16 bytes whose byte i holds weight i in its low nibble
+ * and weight 16 + i in its high nibble; w = d * (q - 8).
+ *   w       [n rows][k/32 blocks] Q4_0, 16-byte aligned (blocks themselves are
+ *           only 2-byte aligned); w_bytes == n*(k/32)*18
+ *   x_bf16  bf16 bits [m][k] row-major, 16-byte aligned
+ *   y       fp32 [m][n] row-major, 4-byte aligned
+ *   1 <= m <= QMV_MAX_ROWS, n >= 1, k >= 256 and k % 256 == 0 (the kernel steps
+ *   over groups of eight blocks, 144 bytes, as over a Q4_K super-block; other k
+ *   give QMV_ERR_SHAPE), and the LDS limit of qmv_q4_k.
+ * y[r][i] = sum_k w[i][k] * x[r][k] with the quants and bf16 inputs exact and
+ * fp32 accumulation (per block d * sum(q x) - 8 d * sum(x)). Row r of y is
+ * bit-identical for every m.
+ * Returns QMV_ERR_NULL, _SHAPE, _SIZE, _ALIGN, _RANGE, _ALIAS before any HIP
+ * call, or QMV_ERR_HIP on a launch failure.
+ */
+int qmv_q4_0(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
+             int m, int n, int k, void *stream);
+
+/*
  * Q6_K matrix times bf16 activation rows (m = 1..4): the other K-quant that
  * Q4_K_M files mix in (memra README model support table, Q4_K_M files).
  * 210-byte blocks of 256 weights: 128 bytes of low quant nibbles, 64 bytes of
@@ -275,6 +296,7 @@ int qmm_q4_k_prefill(const void *w, size_t w_bytes, const uint16_t *x_bf16, floa
  * even; Q8_0 and IQ4_XS weights are exact in fp32). bf16: that fp32 value
  * rounded to bf16 (nearest even). IQ4_XS: w is 8-byte aligned, 136-byte blocks.
  * Q5_K: 16-byte aligned, 176-byte blocks. Q6_K: 16-byte aligned, 210-byte blocks.
+ * Q4_0: 2-byte aligned, 18-byte blocks, any k % 32 == 0 (weights exact in fp32).
  */
 int qmv_dequant_q4_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 int qmv_dequant_q4_k_bf16(const void *w, size_t w_bytes, uint16_t *out, int n, int k, void *stream);
@@ -282,6 +304,7 @@ int qmv_dequant_q8_0_f32(const void *w, size_t w_bytes, float *out, int n, int k
 int qmv_dequant_iq4_xs_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 int qmv_dequant_q5_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 int qmv_dequant_q6_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
+int qmv_dequant_q4_0_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 
 #ifdef __cplusplus
 }

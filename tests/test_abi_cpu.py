@@ -35,7 +35,8 @@ def test_header_lists_the_expected_entry_points():
     assert _header_functions() == sorted([
         "qmv_version", "qmv_strerror", "qmv_last_error", "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe_workspace",
         "qmv_q4_k_moe", "qmv_dequant_iq4_xs_f32", "qmv_iq4_xs_moe_workspace", "qmv_iq4_xs_moe",
-        "qmv_q5_k", "qmv_dequant_q5_k_f32", "qmv_q6_k", "qmv_dequant_q6_k_f32",
+        "qmv_q5_k", "qmv_dequant_q5_k_f32", "qmv_q6_k", "qmv_dequant_q6_k_f32", "qmv_q4_0",
+        "qmv_dequant_q4_0_f32",
         "qmm_q4_k_prefill_workspace", "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16",
         "qmv_dequant_q8_0_f32"])
 
@@ -102,6 +103,31 @@ def test_q5_k_validation():
     f = L.qmv_dequant_q5_k_f32
     assert f(V(0), nb, V(Y), 2, 256, None) == NULL and f(V(W), nb - 1, V(Y), 2, 256, None) == SIZE
     assert f(V(W), nb, V(Y + 4), 2, 256, None) == ALIGN and f(V(W), nb, V(W), 2, 256, None) == ALIAS
+
+
+def q40(w=W, nbytes=None, x=X, y=Y, m=1, n=2, k=256):
+    nbytes = q.q4_0_bytes(n, k) if nbytes is None else nbytes
+    return L.qmv_q4_0(V(w), nbytes, V(x), V(y), m, n, k, None)
+
+
+def test_q4_0_validation():
+    assert q40(w=0) == NULL and q40(x=0) == NULL and q40(y=0) == NULL
+    assert q40(m=0) == RANGE and q40(m=5) == RANGE
+    assert q40(n=0) == SHAPE and q40(k=0) == SHAPE and q40(k=32) == SHAPE and q40(k=224) == SHAPE
+    assert q40(k=288) == SHAPE and q40(k=255) == SHAPE
+    assert q40(w=W + 8) == ALIGN and q40(w=W + 2) == ALIGN and q40(x=X + 2) == ALIGN and q40(y=Y + 2) == ALIGN
+    assert q40(m=4, k=19456) == RANGE
+    assert q40(y=W + 64) == ALIAS
+    full = q.q4_0_bytes(2, 512)
+    assert full == 2 * 16 * 18
+    # (a Q4_K matrix of the same shape has the same size: 144 bytes per 256 weights)
+    for b in list(range(full)) + [full + 1, full + 18, q.q5_k_bytes(2, 512)]:
+        assert q40(nbytes=b, k=512) == SIZE, b
+    f = L.qmv_dequant_q4_0_f32
+    nb = q.q4_0_bytes(2, 32)
+    assert f(V(0), nb, V(Y), 2, 32, None) == NULL and f(V(W), nb - 1, V(Y), 2, 32, None) == SIZE
+    assert f(V(W), nb, V(Y + 4), 2, 32, None) == ALIGN and f(V(W), nb, V(W), 2, 32, None) == ALIAS
+    assert f(V(W + 1), nb, V(Y), 2, 32, None) == ALIGN and f(V(W), nb, V(Y), 2, 16, None) == SHAPE
 
 
 def q6k(w=W, nbytes=None, x=X, y=Y, m=1, n=2, k=256):
