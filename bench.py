@@ -74,9 +74,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--copies", type=int, default=128, help="layer copies in the dense weight pool")
     p.add_argument("--moe-banks", type=int, default=48)
-    p.add_argument("--iq4-copies", type=int, default=48, help="layer copies in the IQ4_XS, Q5_K and Q6_K weight pools")
+    p.add_argument("--iq4-copies", type=int, default=48, help="layer copies in the IQ4_XS, Q5_K, Q6_K and Q4_0 weight pools")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
-    p.add_argument("--skip", default="", help="comma list of sections to skip: verify,q8,moe,prefill,iq4,q5,q6,cpu")
+    p.add_argument("--skip", default="", help="comma list of sections to skip: verify,q8,moe,prefill,iq4,q5,q6,q40,cpu")
     return p.parse_args()
 
 
@@ -277,6 +277,9 @@ def main():
     if "q6" not in skip:
         res["q6_k_gemv"] = bench_format(args, torch, np, q, synth, timer, dev, sp, "q6_k")
         torch.cuda.empty_cache()
+    if "q40" not in skip:
+        res["q4_0_gemv"] = bench_format(args, torch, np, q, synth, timer, dev, sp, "q4_0")
+        torch.cuda.empty_cache()
 
     cpu = None
     if "cpu" not in skip:
@@ -386,14 +389,14 @@ def bench_moe(args, torch, np, q, synth, timer, dev, sp, fmt="q4_k"):
 
 
 def bench_format(args, torch, np, q, synth, timer, dev, sp, fmt):
-    """GEMV of another block format (IQ4_XS, Q5_K or Q6_K) over a pool of layer copies
+    """GEMV of another block format (IQ4_XS, Q5_K, Q6_K or Q4_0) over a pool of layer copies
     (the dense FFN shapes), M = 1..4."""
     L = q.lib
     copies = args.iq4_copies
     gen = {"iq4_xs": synth.torch_iq4_xs_weights, "q5_k": synth.torch_q5_k_weights,
-           "q6_k": synth.torch_q6_k_weights}[fmt]
-    entry = {"iq4_xs": L.qmv_iq4_xs, "q5_k": L.qmv_q5_k, "q6_k": L.qmv_q6_k}[fmt]
-    nbytes = {"iq4_xs": q.iq4_xs_bytes, "q5_k": q.q5_k_bytes, "q6_k": q.q6_k_bytes}[fmt]
+           "q6_k": synth.torch_q6_k_weights, "q4_0": synth.torch_q4_0_weights}[fmt]
+    entry = {"iq4_xs": L.qmv_iq4_xs, "q5_k": L.qmv_q5_k, "q6_k": L.qmv_q6_k, "q4_0": L.qmv_q4_0}[fmt]
+    nbytes = {"iq4_xs": q.iq4_xs_bytes, "q5_k": q.q5_k_bytes, "q6_k": q.q6_k_bytes, "q4_0": q.q4_0_bytes}[fmt]
     log(f"[bench] generating the {fmt} pool: {copies} layer copies")
     pool = [[gen(41, n, k, dev, stream=3 * c + i) for i, (_, n, k) in enumerate(SHAPES)] for c in range(copies)]
     xs = {k: torch.from_numpy(synth.bf16_normal(42, (4, k)).view(np.int16)).to(dev) for _, _, k in SHAPES}
