@@ -37,8 +37,8 @@ HBM_PEAK_GBPS = 8000.0
 GEMV_TRAFFIC = {
     "sources": ("gguf_block_quantized_qmv_amd/csrc/q4k_gemv.hip", "gguf_block_quantized_qmv_amd/csrc/q4k_common.h",
                 "gguf_block_quantized_qmv_amd/csrc/qmv_device.h"),
-    "sha256": "c4e34d16d635d2b6d8af29870d1f3d85c99bf16ce5e3944859b33665088c7f29",
-    "bytes_per_launch": 51159505,
+    "sha256": "e2f82a7bfb9b4910f66acc2c9acd9d81a339a99a104cd8ed6f8fa4606edfd976",
+    "bytes_per_launch": 50875056,
 }
 
 
