@@ -384,6 +384,29 @@ def bench_moe(args, torch, np, q, synth, timer, dev, sp, fmt="q4_k"):
         }
         log(f"[bench] {fmt} MoE T={t}: {tl * 1e6:.2f} us/layer, {out[f'T{t}']['tok_equiv_per_s']:.0f} tok-equiv/s, "
             f"{out[f'T{t}']['GBps_distinct_expert_bytes']:.0f} GB/s")
+    if fmt == "q4_k":
+        # prompt-sized form: 512 tokens per call over 8 of the pool's banks
+        t, nb = 512, min(8, args.moe_banks)
+        logits = torch.from_numpy(synth.moe_logits(24, t * nb, ne)).to(dev).view(nb, t, ne)
+        x = torch.from_numpy(synth.bf16_normal(25, (t, hidden)).view(np.int16)).to(dev)
+        y = torch.empty((t, hidden), dtype=torch.float32, device=dev)
+        need = L.qmv_q4_k_moe_prefill_workspace(t, hidden, ffn, ne, tk)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        calls = [(*(ctypes.c_void_p(banks[b][i].data_ptr()) for i in range(3)), bank_bytes,
+                  ctypes.c_void_p(logits[b].data_ptr()), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                  None, None, ctypes.c_void_p(ws.data_ptr()), need, t, hidden, ffn, ne, tk, sp) for b in range(nb)]
+
+        def pstep():
+            for a in calls:
+                rc = L.qmv_q4_k_moe_prefill(*a)
+                if rc:
+                    raise q.QmvError(rc, "qmv_q4_k_moe_prefill")
+        pstep()
+        tl = timer.run(pstep, 2) / nb
+        out["prefill_T512"] = {"us_per_layer": tl * 1e6, "tokens_per_s_per_layer": t / tl,
+                               "groups_per_call": (t + 3) // 4}
+        log(f"[bench] {fmt} MoE prefill T={t}: {tl * 1e3:.2f} ms/layer, {t / tl:.0f} tokens/s per layer "
+            f"(groups of 4 tokens)")
     del banks
     return out
 

@@ -14,7 +14,8 @@ import os
 
 __all__ = [
     "QmvError", "lib", "LIB_PATH", "version",
-    "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmv_iq4_xs_moe",
+    "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmv_q4_k_moe_prefill",
+    "qmv_q4_k_moe_prefill_workspace", "qmv_iq4_xs_moe",
     "qmv_iq4_xs_moe_workspace", "qmm_q4_k_prefill_workspace",
     "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16", "qmv_dequant_q8_0_f32",
     "qmv_dequant_iq4_xs_f32", "qmv_q5_k", "qmv_dequant_q5_k_f32", "qmv_q6_k", "qmv_dequant_q6_k_f32", "qmv_q4_0",
@@ -41,6 +42,9 @@ EXPORTS = {
     "qmv_q4_k_moe_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "qmv_q4_k_moe": (_c_int, [_vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
                               _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "qmv_q4_k_moe_prefill_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "qmv_q4_k_moe_prefill": (_c_int, [_vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
+                                      _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "qmv_iq4_xs_moe_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "qmv_iq4_xs_moe": (_c_int, [_vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
                                 _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
@@ -217,6 +221,37 @@ def qmv_q4_k_moe(w_gate, w_up, w_down, logits, x, hidden: int, ffn: int, n_exper
     """Routed-expert MoE FFN; returns (y, topk_ids, topk_w, pairs) (the last three None if not routing)."""
     return _moe(lib.qmv_q4_k_moe, qmv_q4_k_moe_workspace, "qmv_q4_k_moe", w_gate, w_up, w_down, logits, x,
                 hidden, ffn, n_experts, top_k, y, ws, routing, stream)
+
+
+def qmv_q4_k_moe_prefill_workspace(t: int, hidden: int, ffn: int, n_experts: int, top_k: int) -> int:
+    return lib.qmv_q4_k_moe_prefill_workspace(t, hidden, ffn, n_experts, top_k)
+
+
+def qmv_q4_k_moe_prefill(w_gate, w_up, w_down, logits, x, hidden: int, ffn: int, n_experts: int, top_k: int,
+                         y=None, ws=None, routing: bool = True, stream=None):
+    """Routed-expert MoE FFN over a prompt's tokens; returns (y, topk_ids, topk_w) (the last two None if not routing)."""
+    torch = _torch()
+    for wname, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _dev(t, wname, (torch.uint8,))
+    _dev(logits, "logits", (torch.float32,))
+    _dev(x, "x", _bf16_types())
+    tc = x.shape[0] if x.dim() == 2 else 1
+    dev = x.device
+    if y is None:
+        y = torch.empty((tc, hidden), dtype=torch.float32, device=dev)
+    _dev(y, "y", (torch.float32,))
+    need = qmv_q4_k_moe_prefill_workspace(tc, hidden, ffn, n_experts, top_k)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(ws, "ws", (torch.uint8,))
+    ids = wts = None
+    if routing:
+        ids = torch.empty((tc, top_k), dtype=torch.int32, device=dev)
+        wts = torch.empty((tc, top_k), dtype=torch.float32, device=dev)
+    _check(lib.qmv_q4_k_moe_prefill(_ptr(w_gate), _ptr(w_up), _ptr(w_down), _nbytes(w_gate), _ptr(logits), _ptr(x),
+                                    _ptr(y), _ptr(ids), _ptr(wts), _ptr(ws), _nbytes(ws), tc, hidden, ffn, n_experts,
+                                    top_k, _stream(stream)), "qmv_q4_k_moe_prefill")
+    return y, ids, wts
 
 
 def qmv_iq4_xs_moe_workspace(t: int, hidden: int, ffn: int, n_experts: int, top_k: int) -> int:

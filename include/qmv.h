@@ -73,6 +73,7 @@ extern "C" {
 #define QMV_MOE_MAX_TOKENS  4
 #define QMV_MOE_MAX_EXPERTS 256
 #define QMV_MOE_MAX_TOP_K   8
+#define QMV_MOE_PREFILL_MAX_TOKENS 65536 /* tokens per qmv_q4_k_moe_prefill call */
 
 /* Library version as 10000*major + 100*minor + patch. */
 int qmv_version(void);
@@ -234,6 +235,27 @@ int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_
                  int32_t *topk_ids, float *topk_w, int32_t *pairs,
                  void *ws, size_t ws_bytes,
                  int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
+
+/*
+ * Routed-expert MoE feed-forward for a prompt's tokens (prefill), Q4_K experts.
+ * Arguments, routing, outputs and error codes as qmv_q4_k_moe, except:
+ *   1 <= t <= QMV_MOE_PREFILL_MAX_TOKENS; logits, x_bf16, y, topk_ids and
+ *   topk_w hold all t tokens; there is no gather-list output;
+ *   ws, ws_bytes  at least qmv_q4_k_moe_prefill_workspace(...) bytes (the
+ *                 workspace of one group of QMV_MOE_MAX_TOKENS tokens).
+ * The tokens run as consecutive groups of up to QMV_MOE_MAX_TOKENS through the
+ * routed-expert kernels of qmv_q4_k_moe, in token order on `stream`, reusing
+ * the workspace. Each group reads its selected experts' weights once. A
+ * token's result is bit-identical to qmv_q4_k_moe on that token alone (the one
+ * numerical program per request of the memra README's recent-fixes list).
+ * Workload: the prompt phase of the memra README's 35B-A3B MoE (its summary
+ * page's time-to-first-token figures).
+ */
+size_t qmv_q4_k_moe_prefill_workspace(int t, int hidden, int ffn, int n_experts, int top_k);
+int qmv_q4_k_moe_prefill(const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes,
+                         const float *logits, const uint16_t *x_bf16, float *y,
+                         int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
+                         int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
 
 /*
  * Workspace bytes qmv_iq4_xs_moe needs for t tokens (0 if an argument is out of

@@ -34,7 +34,8 @@ def _header_functions():
 def test_header_lists_the_expected_entry_points():
     assert _header_functions() == sorted([
         "qmv_version", "qmv_strerror", "qmv_last_error", "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe_workspace",
-        "qmv_q4_k_moe", "qmv_dequant_iq4_xs_f32", "qmv_iq4_xs_moe_workspace", "qmv_iq4_xs_moe",
+        "qmv_q4_k_moe", "qmv_q4_k_moe_prefill",
+        "qmv_q4_k_moe_prefill_workspace", "qmv_dequant_iq4_xs_f32", "qmv_iq4_xs_moe_workspace", "qmv_iq4_xs_moe",
         "qmv_q5_k", "qmv_dequant_q5_k_f32", "qmv_q6_k", "qmv_dequant_q6_k_f32", "qmv_q4_0",
         "qmv_dequant_q4_0_f32",
         "qmm_q4_k_prefill_workspace", "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16",
@@ -249,6 +250,37 @@ def test_moe_validation():
     assert moe(y=W + 1024) == ALIAS                       # output inside the gate bank
     assert moe(ws=Y) == ALIAS                             # workspace over the output
     assert moe(pairs=Y + (1 << 20)) == ALIAS              # two outputs overlap
+
+
+def moe_prefill(**kw):
+    a = dict(wg=W, wu=W + (1 << 28), wd=W + (2 << 28), bank=None, logits=X, x=X + (1 << 20), y=Y,
+             ids=Y + (1 << 20), wts=Y + (2 << 20), ws=WS, ws_bytes=None, t=9, h=256, f=256, e=8, k=2)
+    a.update(kw)
+    bank = a["e"] * a["f"] * (a["h"] // 256) * 144 if a["bank"] is None else a["bank"]
+    need = L.qmv_q4_k_moe_prefill_workspace(a["t"], a["h"], a["f"], a["e"], a["k"])
+    ws_bytes = need if a["ws_bytes"] is None else a["ws_bytes"]
+    return L.qmv_q4_k_moe_prefill(V(a["wg"]), V(a["wu"]), V(a["wd"]), bank, V(a["logits"]), V(a["x"]), V(a["y"]),
+                                  V(a["ids"]), V(a["wts"]), V(a["ws"]), ws_bytes,
+                                  a["t"], a["h"], a["f"], a["e"], a["k"], None)
+
+
+def test_moe_prefill_validation():
+    # the workspace is one group's (QMV_MOE_MAX_TOKENS tokens), whatever t is
+    w4 = L.qmv_q4_k_moe_workspace(4, 2048, 768, 128, 8)
+    assert L.qmv_q4_k_moe_prefill_workspace(512, 2048, 768, 128, 8) == w4
+    assert L.qmv_q4_k_moe_prefill_workspace(3, 2048, 768, 128, 8) == L.qmv_q4_k_moe_workspace(3, 2048, 768, 128, 8)
+    assert L.qmv_q4_k_moe_prefill_workspace(0, 2048, 768, 128, 8) == 0
+    assert L.qmv_q4_k_moe_prefill_workspace(65537, 2048, 768, 128, 8) == 0
+    assert moe_prefill(wg=0) == NULL and moe_prefill(logits=0) == NULL and moe_prefill(y=0) == NULL
+    assert moe_prefill(t=0) == RANGE and moe_prefill(t=65537) == RANGE and moe_prefill(k=9, e=16) == RANGE
+    assert moe_prefill(h=300) == SHAPE
+    assert moe_prefill(bank=8 * 256 * 144 - 1) == SIZE
+    assert moe_prefill(ws=0) == WORKSPACE and moe_prefill(ws_bytes=16) == WORKSPACE
+    assert moe_prefill(x=X + 2) == ALIGN
+    # the aliasing checks cover all t tokens, not one group: y of 9 tokens (9 KiB)
+    # reaches the topk ids placed 8 KiB after it; 4 tokens' y would not
+    assert moe_prefill(ids=Y + 8192) == ALIAS
+    assert moe_prefill(t=600, y=X + (1 << 20) + 1024) == ALIAS   # y inside the 600 tokens' activations
 
 
 def test_moe_bank_every_truncated_size_is_an_error():
