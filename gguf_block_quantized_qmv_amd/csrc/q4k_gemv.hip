@@ -1,4 +1,8 @@
 // Q4_K matrix x bf16 activation rows (decode M=1, speculative verify M=2..4), gfx950.
+// The same kernel body, with the block format as a template parameter, serves
+// Q5_K (the Q4_K header and nibbles plus a 32-byte plane of fifth bits) and
+// Q4_0 (eight 18-byte blocks are 256 weights in 144 bytes, so a group of eight
+// is stepped over exactly like a Q4_K super-block; see q40_chunk).
 //
 // Work mapping. A group of G lanes (16 for rows up to 8192 weights, 32 beyond)
 // owns one output row. Lane j of a group reads, at step s, 64-weight chunk
