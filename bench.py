@@ -403,10 +403,8 @@ def bench_moe(args, torch, np, q, synth, timer, dev, sp, fmt="q4_k"):
                     raise q.QmvError(rc, "qmv_q4_k_moe_prefill")
         pstep()
         tl = timer.run(pstep, 2) / nb
-        out["prefill_T512"] = {"us_per_layer": tl * 1e6, "tokens_per_s_per_layer": t / tl,
-                               "groups_per_call": (t + 3) // 4}
-        log(f"[bench] {fmt} MoE prefill T={t}: {tl * 1e3:.2f} ms/layer, {t / tl:.0f} tokens/s per layer "
-            f"(groups of 4 tokens)")
+        out["prefill_T512"] = {"us_per_layer": tl * 1e6, "tokens_per_s_per_layer": t / tl}
+        log(f"[bench] {fmt} MoE prefill T={t}: {tl * 1e3:.3f} ms/layer, {t / tl:.0f} tokens/s per layer")
     del banks
     return out
 

@@ -1,0 +1,473 @@
+// Routed-expert MoE over a prompt's tokens as grouped products on the matrix
+// cores (Q4_K experts), gfx950.
+//
+// Launches, in order on one stream:
+//  1. route:   per token, the top-k logits (ties to the lower id) and the
+//              softmax over them (the decode form's routing, one wave a token);
+//  2. group:   per expert, how many (token, rank) pairs chose it, how many
+//              chose a lower expert, and its pairs in token order: the pair
+//              list, sorted by expert then token;
+//  3. chunks:  each expert's pairs cut into chunks of 16; the (expert, chunk)
+//              list;
+//  4. gate/up: per (16-row tile of W_gate and W_up, chunk): the 16 gathered
+//              tokens' activations times the tile with one
+//              v_mfma_f32_16x16x32_bf16 per 32-weight sub-block and matrix
+//              (A = the tokens' activations, B = the quants as exact bf16
+//              integers), per sub-block acc += (d sc) D - (dmin m) X; then
+//              h = silu(g) u in fp32 per pair;
+//  5. down:    per (16-row tile of W_down, chunk): the same with A = h split
+//              into two bf16 halves (h_hi = bf16(h), h_lo = bf16(h - h_hi),
+//              so the product keeps about 17 bits of h), z per pair;
+//  6. combine: y_t = sum over ranks j of w_tj z_tj, in rank order.
+// Each expert's weights are read once per chunk of 16 of its tokens. Every
+// step has a fixed order, so results are bitwise reproducible.
+//
+// MFMA lane layout (16x16x32 bf16): lane l supplies A row l % 16 and B column
+// l % 16 with k = 8 (l / 16) .. + 7, and holds D[4 (l / 16) + e][l % 16] in
+// register e. Lane group g = l / 16 takes positions 8g .. 8g + 7 of every
+// sub-block: the low and high nibbles of quant bytes 32c + 8g .. + 7 of chunk c.
+#include "moe_routing.h"
+#include "q4k_common.h"
+#include "qmv_internal.h"
+#include "../../include/qmv.h"
+
+namespace qmv {
+namespace {
+
+using moe::kTopK;
+using moe::Logits;
+using moe::load_logits;
+using moe::route_token;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 16;   // pairs per chunk (the MFMA's M)
+constexpr int kTile = 16;    // weight rows per tile (the MFMA's N)
+constexpr int kWv = 4;       // waves per workgroup; they split the super-blocks
+constexpr int kThr = 64 * kWv;
+
+struct GLayout {
+  size_t ids, wts, cnt, off, choff, chunks, plist, h, z, total;
+};
+
+inline size_t g_round(size_t b) { return (b + 255) & ~(size_t)255; }
+
+inline GLayout g_layout(int t, int hidden, int ffn, int E, int K) {
+  GLayout L;
+  const size_t P = (size_t)t * (size_t)K;
+  const size_t maxch = (P + kChunk - 1) / kChunk + (size_t)E;
+  size_t o = 0;
+  L.ids = o; o += g_round(P * 4);
+  L.wts = o; o += g_round(P * 4);
+  L.cnt = o; o += g_round((size_t)E * 4);
+  L.off = o; o += g_round((size_t)E * 4);
+  L.choff = o; o += g_round(((size_t)E + 1) * 4);
+  L.chunks = o; o += g_round(maxch * 8);
+  L.plist = o; o += g_round(P * 4);
+  L.h = o; o += g_round(P * (size_t)ffn * 4);
+  L.z = o; o += g_round(P * (size_t)hidden * 4);
+  L.total = o;
+  return L;
+}
+
+// Eight nibbles (bytes 0..3 of lo, then of hi) as eight exact bf16 integers.
+__device__ __forceinline__ bf16x8 nibbles8(const uint32_t lo, const uint32_t hi) {
+  const bf16x2 a = nibbles_to_bf16x2<false>(lo), b = nibbles_to_bf16x2<true>(lo);
+  const bf16x2 c = nibbles_to_bf16x2<false>(hi), d = nibbles_to_bf16x2<true>(hi);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// ---------------------------------------------------------------- 1. route
+
+__global__ __launch_bounds__(kThr) void g_route_kernel(const float *__restrict__ logits, int *__restrict__ ids,
+                                                        float *__restrict__ wts, int32_t *__restrict__ topk_ids,
+                                                        float *__restrict__ topk_w, const int T, const int E,
+                                                        const int K) {
+  __shared__ int sid[kWv][kTopK];
+  __shared__ float swt[kWv][kTopK];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = (int)blockIdx.x * kWv + wave;
+  const Logits lg = load_logits(logits, t < T ? t : T - 1, E);
+  route_token(lg, wave, t < T, E, K, sid, swt);
+  __syncthreads();
+  if (t < T && lane < K) {
+    ids[(size_t)t * K + lane] = sid[wave][lane];
+    wts[(size_t)t * K + lane] = swt[wave][lane];
+    if (topk_ids) topk_ids[(size_t)t * K + lane] = sid[wave][lane];
+    if (topk_w) topk_w[(size_t)t * K + lane] = swt[wave][lane];
+  }
+}
+
+// ---------------------------------------------------------------- 2. group
+
+// Workgroup e: counts, then the pairs p (= t K + j) with ids[p] == e in
+// increasing p, written at off[e] .. off[e] + cnt[e].
+__global__ __launch_bounds__(kThr) void g_group_kernel(const int *__restrict__ ids, int *__restrict__ cnt,
+                                                        int *__restrict__ off, int *__restrict__ plist, const int P) {
+  __shared__ int red[2][kWv];
+  __shared__ int wbase[kWv + 1];
+  const int e = (int)blockIdx.x;
+  const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int lt = 0, eq = 0;
+  for (int p = tid; p < P; p += kThr) {
+    const int v = ids[p];
+    lt += v < e;
+    eq += v == e;
+  }
+  for (int s = 32; s >= 1; s >>= 1) {
+    lt += __shfl_xor(lt, s);
+    eq += __shfl_xor(eq, s);
+  }
+  if (lane == 0) red[0][wave] = lt, red[1][wave] = eq;
+  __syncthreads();
+  int o = 0, n = 0;
+#pragma unroll
+  for (int w = 0; w < kWv; ++w) o += red[0][w], n += red[1][w];
+  if (tid == 0) cnt[e] = n, off[e] = o;
+  int run = o;
+  for (int base = 0; base < P; base += kThr) {
+    const int p = base + tid;
+    const bool f = p < P && ids[p] == e;
+    const unsigned long long bal = __ballot(f);
+    const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+    __syncthreads();
+    if (lane == 0) wbase[wave] = __popcll(bal);
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWv; ++w) {
+      before += w < wave ? wbase[w] : 0;
+      total += wbase[w];
+    }
+    if (f) plist[run + before + rank] = p;
+    run += total;
+  }
+}
+
+// ---------------------------------------------------------------- 3. chunks
+
+// One workgroup: chunk offsets per expert (an exclusive scan in expert order)
+// and the (expert, chunk) list.
+__global__ __launch_bounds__(kThr) void g_chunks_kernel(const int *__restrict__ cnt, int *__restrict__ choff,
+                                                         int2 *__restrict__ chunks, const int E) {
+  __shared__ int nch[QMV_MOE_MAX_EXPERTS + 1];
+  const int tid = (int)threadIdx.x;
+  for (int e = tid; e < E; e += kThr) nch[e] = (cnt[e] + kChunk - 1) / kChunk;
+  __syncthreads();
+  if (tid == 0) {
+    int s = 0;
+    for (int e = 0; e < E; ++e) {
+      const int c = nch[e];
+      nch[e] = s;
+      s += c;
+    }
+    nch[E] = s;
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += kThr) choff[e] = nch[e];
+  for (int e = tid; e < E; e += kThr)
+    for (int c = 0; c < nch[e + 1] - nch[e]; ++c) chunks[nch[e] + c] = make_int2(e, c);
+}
+
+// ---------------------------------------------------------------- 4. gate/up
+
+// Super-block b of one W row for lane group kg: the 16-byte header and the
+// lane's 8 quant bytes of each 64-weight chunk.
+struct SbLoad {
+  uint4 hdr;
+  uint2 q[4];
+};
+__device__ __forceinline__ SbLoad load_sb(const uint8_t *__restrict__ bp, const int kg) {
+  SbLoad r;
+  r.hdr = *reinterpret_cast<const uint4 *>(bp);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const uint2 *>(bp + 16 + 32 * c + 8 * kg);
+  return r;
+}
+
+// Chunk y's pairs: expert e, the list positions pos0 .. pos0 + n - 1 (n <= 16).
+struct ChunkInfo {
+  int e, pos0, n;
+};
+__device__ __forceinline__ ChunkInfo chunk_info(const int2 *__restrict__ chunks, const int *__restrict__ cnt,
+                                                const int *__restrict__ off, const int y) {
+  const int2 ec = chunks[y];
+  ChunkInfo ci;
+  ci.e = ec.x;
+  const int first = ec.y * kChunk;
+  ci.pos0 = off[ec.x] + first;
+  const int left = cnt[ec.x] - first;
+  ci.n = left < kChunk ? left : kChunk;
+  return ci;
+}
+
+__global__ __launch_bounds__(kThr) void g_gate_up_kernel(const uint8_t *__restrict__ w_gate,
+                                                          const uint8_t *__restrict__ w_up,
+                                                          const uint16_t *__restrict__ x,
+                                                          const int *__restrict__ cnt, const int *__restrict__ off,
+                                                          const int *__restrict__ choff,
+                                                          const int2 *__restrict__ chunks,
+                                                          const int *__restrict__ plist, float *__restrict__ h,
+                                                          const int hidden, const int ffn, const int E, const int K) {
+  extern __shared__ uint4 lds[];
+  const int y = (int)blockIdx.y;
+  if (y >= choff[E]) return;   // uniform over the workgroup
+  const ChunkInfo ci = chunk_info(chunks, cnt, off, y);
+  const int gpr = hidden >> 3, rs = gpr + 4, nsub = hidden >> 5, nblk = hidden >> 8;
+  uint4 *xs = lds;                                                    // [16][rs]
+  float *xsum = reinterpret_cast<float *>(lds + (size_t)kChunk * rs); // [16][nsub]
+  float *red = xsum + (size_t)kChunk * nsub;                          // [2][kWv][16 rows][16 pairs]
+  const int tid = (int)threadIdx.x, wv = tid >> 6, l = tid & 63, nl = l & 15, kg = l >> 4;
+
+  // stage the chunk's activation rows (zeros past its pairs)
+  const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+  for (int g = tid; g < kChunk * gpr; g += kThr) {
+    const int i = g / gpr, gg = g - i * gpr;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (i < ci.n) v = xg[(size_t)(plist[ci.pos0 + i] / K) * gpr + gg];
+    xs[i * rs + gg] = v;
+  }
+  __syncthreads();
+  for (int t = tid; t < kChunk * nsub; t += kThr) {
+    const int i = t / nsub, sb = t - i * nsub;
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 g = xs[i * rs + 4 * sb + q];
+      const uint32_t v4[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s += bf16_bits_to_f32(v4[u] & 0xFFFFu);
+        s += bf16_bits_to_f32(v4[u] >> 16);
+      }
+    }
+    xsum[t] = s;
+  }
+  __syncthreads();
+
+  const int f = (int)blockIdx.x * kTile + nl;   // this lane's W row (ffn is a multiple of 16)
+  const size_t row_bytes = (size_t)nblk * kQ4KBlockBytes;
+  const uint8_t *gr = w_gate + ((size_t)ci.e * ffn + f) * row_bytes;
+  const uint8_t *ur = w_up + ((size_t)ci.e * ffn + f) * row_bytes;
+  float ag[4] = {0.0f, 0.0f, 0.0f, 0.0f}, au[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const uint4 *xa = xs + nl * rs + kg;
+  for (int b = wv; b < nblk; b += kWv) {
+    const SbLoad lgt = load_sb(gr + (size_t)b * kQ4KBlockBytes, kg);
+    const SbLoad lup = load_sb(ur + (size_t)b * kQ4KBlockBytes, kg);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const ScaleSel sel = scale_selectors(c);
+      const ChunkScales cg = chunk_scales(lgt.hdr, sel), cu = chunk_scales(lup.hdr, sel);
+      const uint2 qg = lgt.q[c], qu = lup.q[c];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int jg = 8 * b + 2 * c + hh;
+        const bf16x8 bg = hh ? nibbles8((qg.x >> 4) & 0x0F0F0F0Fu, (qg.y >> 4) & 0x0F0F0F0Fu)
+                             : nibbles8(qg.x & 0x0F0F0F0Fu, qg.y & 0x0F0F0F0Fu);
+        const bf16x8 bu = hh ? nibbles8((qu.x >> 4) & 0x0F0F0F0Fu, (qu.y >> 4) & 0x0F0F0F0Fu)
+                             : nibbles8(qu.x & 0x0F0F0F0Fu, qu.y & 0x0F0F0F0Fu);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, xa[4 * jg]);
+        f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f}, du = {0.0f, 0.0f, 0.0f, 0.0f};
+        dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, dg, 0, 0, 0);
+        du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, du, 0, 0, 0);
+        const float sag = hh ? cg.a1 : cg.a0, sbg = hh ? cg.b1 : cg.b0;
+        const float sau = hh ? cu.a1 : cu.a0, sbu = hh ? cu.b1 : cu.b0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float xsr = xsum[(4 * kg + r) * nsub + jg];
+          ag[r] = __builtin_fmaf(sag, dg[r], ag[r]);
+          ag[r] = __builtin_fmaf(-sbg, xsr, ag[r]);
+          au[r] = __builtin_fmaf(sau, du[r], au[r]);
+          au[r] = __builtin_fmaf(-sbu, xsr, au[r]);
+        }
+      }
+    }
+  }
+  // lane l holds pairs 4 kg .. 4 kg + 3 of W row nl; add the waves in order
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    red[((0 * kWv + wv) * kTile + nl) * kChunk + 4 * kg + r] = ag[r];
+    red[((1 * kWv + wv) * kTile + nl) * kChunk + 4 * kg + r] = au[r];
+  }
+  __syncthreads();
+  {
+    const int row = tid / kChunk, i = tid - row * kChunk;   // 256 threads = 16 rows x 16 pairs
+    float g = red[(0 * kWv + 0) * kTile * kChunk + row * kChunk + i];
+    float u = red[(1 * kWv + 0) * kTile * kChunk + row * kChunk + i];
+#pragma unroll
+    for (int w = 1; w < kWv; ++w) {
+      g += red[(0 * kWv + w) * kTile * kChunk + row * kChunk + i];
+      u += red[(1 * kWv + w) * kTile * kChunk + row * kChunk + i];
+    }
+    if (i < ci.n) h[(size_t)(ci.pos0 + i) * ffn + (int)blockIdx.x * kTile + row] = g / (1.0f + expf(-g)) * u;
+  }
+}
+
+// ---------------------------------------------------------------- 5. down
+
+__global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict__ w_down,
+                                                       const int *__restrict__ cnt, const int *__restrict__ off,
+                                                       const int *__restrict__ choff, const int2 *__restrict__ chunks,
+                                                       const int *__restrict__ plist, const float *__restrict__ h,
+                                                       float *__restrict__ z, const int hidden, const int ffn,
+                                                       const int E) {
+  extern __shared__ uint4 lds[];
+  const int y = (int)blockIdx.y;
+  if (y >= choff[E]) return;
+  const ChunkInfo ci = chunk_info(chunks, cnt, off, y);
+  const int gpr = ffn >> 3, rs = gpr + 4, nsub = ffn >> 5, nblk = ffn >> 8;
+  uint4 *hs_hi = lds;                                                   // [16][rs]
+  uint4 *hs_lo = lds + (size_t)kChunk * rs;                             // [16][rs]
+  float *hsum = reinterpret_cast<float *>(lds + (size_t)2 * kChunk * rs); // [16][nsub]
+  float *red = hsum + (size_t)kChunk * nsub;                            // [kWv][16 rows][16 pairs]
+  const int tid = (int)threadIdx.x, wv = tid >> 6, l = tid & 63, nl = l & 15, kg = l >> 4;
+
+  // stage h of the chunk's pairs as bf16 halves (zeros past its pairs)
+  for (int g = tid; g < kChunk * gpr; g += kThr) {
+    const int i = g / gpr, gg = g - i * gpr;
+    uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+    if (i < ci.n) {
+      const float4 *hp = reinterpret_cast<const float4 *>(h + (size_t)(ci.pos0 + i) * ffn + 8 * gg);
+      const float4 a = hp[0], b = hp[1];
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t h0 = f32_to_bf16_rne(v[2 * q]), h1 = f32_to_bf16_rne(v[2 * q + 1]);
+        const uint32_t l0 = f32_to_bf16_rne(v[2 * q] - bf16_bits_to_f32(h0));
+        const uint32_t l1 = f32_to_bf16_rne(v[2 * q + 1] - bf16_bits_to_f32(h1));
+        hi[q] = h0 | (h1 << 16);
+        lo[q] = l0 | (l1 << 16);
+      }
+    }
+    hs_hi[i * rs + gg] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    hs_lo[i * rs + gg] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
+  __syncthreads();
+  // per-sub-block sums of the values the products see (h_hi + h_lo), in index order
+  for (int t = tid; t < kChunk * nsub; t += kThr) {
+    const int i = t / nsub, sb = t - i * nsub;
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 gh = hs_hi[i * rs + 4 * sb + q], gl = hs_lo[i * rs + 4 * sb + q];
+      const uint32_t vh[4] = {gh.x, gh.y, gh.z, gh.w}, vl[4] = {gl.x, gl.y, gl.z, gl.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s += bf16_bits_to_f32(vh[u] & 0xFFFFu) + bf16_bits_to_f32(vl[u] & 0xFFFFu);
+        s += bf16_bits_to_f32(vh[u] >> 16) + bf16_bits_to_f32(vl[u] >> 16);
+      }
+    }
+    hsum[t] = s;
+  }
+  __syncthreads();
+
+  const int n = (int)blockIdx.x * kTile + nl;   // this lane's W_down row (hidden is a multiple of 16)
+  const uint8_t *dr = w_down + ((size_t)ci.e * hidden + n) * (size_t)nblk * kQ4KBlockBytes;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const uint4 *ha = hs_hi + nl * rs + kg, *la = hs_lo + nl * rs + kg;
+  for (int b = wv; b < nblk; b += kWv) {
+    const SbLoad ld = load_sb(dr + (size_t)b * kQ4KBlockBytes, kg);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const ChunkScales cs = chunk_scales(ld.hdr, scale_selectors(c));
+      const uint2 qd = ld.q[c];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int jg = 8 * b + 2 * c + hh;
+        const bf16x8 bq = hh ? nibbles8((qd.x >> 4) & 0x0F0F0F0Fu, (qd.y >> 4) & 0x0F0F0F0Fu)
+                             : nibbles8(qd.x & 0x0F0F0F0Fu, qd.y & 0x0F0F0F0Fu);
+        f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ha[4 * jg]), bq, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, la[4 * jg]), bq, d, 0, 0, 0);
+        const float sa = hh ? cs.a1 : cs.a0, sb = hh ? cs.b1 : cs.b0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[r] = __builtin_fmaf(sa, d[r], acc[r]);
+          acc[r] = __builtin_fmaf(-sb, hsum[(4 * kg + r) * nsub + jg], acc[r]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(wv * kTile + nl) * kChunk + 4 * kg + r] = acc[r];
+  __syncthreads();
+  {
+    const int row = tid / kChunk, i = tid - row * kChunk;
+    float v = red[row * kChunk + i];
+#pragma unroll
+    for (int w = 1; w < kWv; ++w) v += red[(w * kTile + row) * kChunk + i];
+    if (i < ci.n) z[(size_t)plist[ci.pos0 + i] * hidden + (int)blockIdx.x * kTile + row] = v;
+  }
+}
+
+// ---------------------------------------------------------------- 6. combine
+
+__global__ __launch_bounds__(kThr) void g_combine_kernel(const float *__restrict__ z, const float *__restrict__ wts,
+                                                          float *__restrict__ y, const int hidden, const int K) {
+  const int t = (int)blockIdx.x;
+  const int nn = (int)blockIdx.y * kThr + (int)threadIdx.x;
+  if (nn >= hidden) return;
+  float acc = 0.0f;
+  for (int j = 0; j < K; ++j) acc = __builtin_fmaf(wts[(size_t)t * K + j], z[((size_t)t * K + j) * hidden + nn], acc);
+  y[(size_t)t * hidden + nn] = acc;
+}
+
+}  // namespace
+
+size_t moe_grouped_workspace_bytes(int t, int hidden, int ffn, int n_experts, int top_k) {
+  return g_layout(t, hidden, ffn, n_experts, top_k).total;
+}
+
+bool moe_grouped_fits_lds(int hidden, int ffn) {
+  const size_t a = (size_t)kChunk * ((hidden >> 3) + 4) * 16 + (size_t)kChunk * (hidden >> 5) * 4 +
+                   (size_t)2 * kWv * kTile * kChunk * 4;
+  const size_t b = (size_t)2 * kChunk * ((ffn >> 3) + 4) * 16 + (size_t)kChunk * (ffn >> 5) * 4 +
+                   (size_t)kWv * kTile * kChunk * 4;
+  return a <= (size_t)QMV_LDS_X_BYTES && b <= (size_t)QMV_LDS_X_BYTES;
+}
+
+int launch_q4_k_moe_grouped(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
+                            const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, void *ws, int t,
+                            int hidden, int ffn, int n_experts, int top_k, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const GLayout L = g_layout(t, hidden, ffn, n_experts, top_k);
+  uint8_t *wb = static_cast<uint8_t *>(ws);
+  int *ids = reinterpret_cast<int *>(wb + L.ids);
+  float *wts = reinterpret_cast<float *>(wb + L.wts);
+  int *cnt = reinterpret_cast<int *>(wb + L.cnt);
+  int *off = reinterpret_cast<int *>(wb + L.off);
+  int *choff = reinterpret_cast<int *>(wb + L.choff);
+  int2 *chunks = reinterpret_cast<int2 *>(wb + L.chunks);
+  int *plist = reinterpret_cast<int *>(wb + L.plist);
+  float *h = reinterpret_cast<float *>(wb + L.h);
+  float *z = reinterpret_cast<float *>(wb + L.z);
+  const int P = t * top_k;
+  const unsigned maxch = (unsigned)((P + kChunk - 1) / kChunk + n_experts);
+  int rc = launch_kernel("g_route_kernel", g_route_kernel, dim3((unsigned)((t + kWv - 1) / kWv)), dim3(kThr), 0, s,
+                         logits, ids, wts, topk_ids, topk_w, t, n_experts, top_k);
+  if (!rc) rc = launch_kernel("g_group_kernel", g_group_kernel, dim3((unsigned)n_experts), dim3(kThr), 0, s, ids,
+                              cnt, off, plist, P);
+  if (!rc) rc = launch_kernel("g_chunks_kernel", g_chunks_kernel, dim3(1), dim3(kThr), 0, s, cnt, choff, chunks,
+                              n_experts);
+  static std::atomic<size_t> granted_a{0}, granted_b{0};
+  const size_t lds_a = (size_t)kChunk * ((hidden >> 3) + 4) * 16 + (size_t)kChunk * (hidden >> 5) * 4 +
+                       (size_t)2 * kWv * kTile * kChunk * 4;
+  const size_t lds_b = (size_t)2 * kChunk * ((ffn >> 3) + 4) * 16 + (size_t)kChunk * (ffn >> 5) * 4 +
+                       (size_t)kWv * kTile * kChunk * 4;
+  if (!rc && (allow_dynamic_lds(reinterpret_cast<const void *>(&g_gate_up_kernel), lds_a, granted_a,
+                                "g_gate_up_kernel lds") ||
+              allow_dynamic_lds(reinterpret_cast<const void *>(&g_down_kernel), lds_b, granted_b, "g_down_kernel lds")))
+    rc = QMV_ERR_HIP;
+  if (!rc) rc = launch_kernel("g_gate_up_kernel", g_gate_up_kernel, dim3((unsigned)(ffn / kTile), maxch), dim3(kThr),
+                              lds_a, s, static_cast<const uint8_t *>(w_gate), static_cast<const uint8_t *>(w_up), x,
+                              cnt, off, choff, chunks, plist, h, hidden, ffn, n_experts, top_k);
+  if (!rc) rc = launch_kernel("g_down_kernel", g_down_kernel, dim3((unsigned)(hidden / kTile), maxch), dim3(kThr),
+                              lds_b, s, static_cast<const uint8_t *>(w_down), cnt, off, choff, chunks, plist, h, z,
+                              hidden, ffn, n_experts);
+  if (!rc) rc = launch_kernel("g_combine_kernel", g_combine_kernel, dim3((unsigned)t,
+                              (unsigned)((hidden + kThr - 1) / kThr)), dim3(kThr), 0, s, z, wts, y, hidden, top_k);
+  return rc;
+}
+
+}  // namespace qmv

@@ -74,15 +74,13 @@ bool moe_args_ok(MoeFormat f, int t, int hidden, int ffn, int n_experts, int top
                                : qmv::iq4xs_moe_fits_lds(t, hidden, ffn, top_k));
 }
 
-// Host-side checks of a routed-expert call: t tokens per launch (the kernels'
-// limit), t_all tokens in the caller's buffers (t_all >= t; the prefill entry
-// runs t_all tokens as consecutive launches of up to t).
+// Host-side checks of a routed-expert decode call of t tokens.
 int moe_check(MoeFormat f, const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes,
               const float *logits, const uint16_t *x_bf16, float *y, int32_t *topk_ids, float *topk_w,
-              int32_t *pairs, void *ws, size_t ws_bytes, int t, int t_all, int hidden, int ffn, int n_experts,
+              int32_t *pairs, void *ws, size_t ws_bytes, int t, int hidden, int ffn, int n_experts,
               int top_k) {
   if (!w_gate || !w_up || !w_down || !logits || !x_bf16 || !y) return QMV_ERR_NULL;
-  if (t < 1 || t > QMV_MOE_MAX_TOKENS || t_all < t || n_experts < 1 || n_experts > QMV_MOE_MAX_EXPERTS ||
+  if (t < 1 || t > QMV_MOE_MAX_TOKENS || n_experts < 1 || n_experts > QMV_MOE_MAX_EXPERTS ||
       top_k < 1 || top_k > QMV_MOE_MAX_TOP_K || top_k > n_experts)
     return QMV_ERR_RANGE;
   if (hidden <= 0 || ffn <= 0 || hidden % 256 || ffn % 256) return QMV_ERR_SHAPE;
@@ -101,7 +99,7 @@ int moe_check(MoeFormat f, const void *w_gate, const void *w_up, const void *w_d
   if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
 
   // every output (and the workspace) must be disjoint from every input and from each other
-  const size_t ta = (size_t)t_all;
+  const size_t ta = (size_t)t;
   const size_t yb = ta * hidden * 4, idb = ta * top_k * 4, pb = ta * top_k * 8;
   const void *in_p[] = {w_gate, w_up, w_down, logits, x_bf16};
   const size_t in_b[] = {bank, bank, bank, ta * n_experts * 4, ta * hidden * 2};
@@ -131,7 +129,7 @@ int moe_entry(MoeFormat f, const void *w_gate, const void *w_up, const void *w_d
               int32_t *pairs, void *ws, size_t ws_bytes, int t, int hidden, int ffn, int n_experts, int top_k,
               void *stream) {
   const int rc = moe_check(f, w_gate, w_up, w_down, bank_bytes, logits, x_bf16, y, topk_ids, topk_w, pairs, ws,
-                           ws_bytes, t, t, hidden, ffn, n_experts, top_k);
+                           ws_bytes, t, hidden, ffn, n_experts, top_k);
   if (rc) return rc;
   return moe_launch(f, w_gate, w_up, w_down, logits, x_bf16, y, topk_ids, topk_w, pairs, ws, t, hidden, ffn,
                     n_experts, top_k, stream);
@@ -209,32 +207,45 @@ int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_
 }
 
 size_t qmv_q4_k_moe_prefill_workspace(int t, int hidden, int ffn, int n_experts, int top_k) {
-  if (t < 1 || t > QMV_MOE_PREFILL_MAX_TOKENS) return 0;
-  const int g = t < QMV_MOE_MAX_TOKENS ? t : QMV_MOE_MAX_TOKENS;
-  if (!moe_args_ok(MoeFormat::kQ4K, g, hidden, ffn, n_experts, top_k)) return 0;
-  return qmv::moe_workspace_bytes(g, hidden, ffn, n_experts, top_k);
+  if (t < 1 || t > QMV_MOE_PREFILL_MAX_TOKENS || n_experts < 1 || n_experts > QMV_MOE_MAX_EXPERTS || top_k < 1 ||
+      top_k > QMV_MOE_MAX_TOP_K || top_k > n_experts || hidden <= 0 || ffn <= 0 || hidden % 256 || ffn % 256 ||
+      !qmv::moe_grouped_fits_lds(hidden, ffn))
+    return 0;
+  return qmv::moe_grouped_workspace_bytes(t, hidden, ffn, n_experts, top_k);
 }
 
 int qmv_q4_k_moe_prefill(const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes,
                          const float *logits, const uint16_t *x_bf16, float *y, int32_t *topk_ids, float *topk_w,
                          void *ws, size_t ws_bytes, int t, int hidden, int ffn, int n_experts, int top_k,
                          void *stream) {
-  if (t < 1 || t > QMV_MOE_PREFILL_MAX_TOKENS) return QMV_ERR_RANGE;
-  const int g = t < QMV_MOE_MAX_TOKENS ? t : QMV_MOE_MAX_TOKENS;
-  const int rc = moe_check(MoeFormat::kQ4K, w_gate, w_up, w_down, bank_bytes, logits, x_bf16, y, topk_ids, topk_w,
-                           nullptr, ws, ws_bytes, g, t, hidden, ffn, n_experts, top_k);
-  if (rc) return rc;
-  // consecutive groups of g tokens on one stream, so the workspace is reused in order
-  for (int t0 = 0; t0 < t; t0 += g) {
-    const int tg = t - t0 < g ? t - t0 : g;
-    const size_t o = (size_t)t0;
-    const int r = moe_launch(MoeFormat::kQ4K, w_gate, w_up, w_down, logits + o * n_experts, x_bf16 + o * hidden,
-                             y + o * hidden, topk_ids ? topk_ids + o * top_k : nullptr,
-                             topk_w ? topk_w + o * top_k : nullptr, nullptr, ws, tg, hidden, ffn, n_experts, top_k,
-                             stream);
-    if (r) return r;
+  if (!w_gate || !w_up || !w_down || !logits || !x_bf16 || !y) return QMV_ERR_NULL;
+  if (t < 1 || t > QMV_MOE_PREFILL_MAX_TOKENS || n_experts < 1 || n_experts > QMV_MOE_MAX_EXPERTS || top_k < 1 ||
+      top_k > QMV_MOE_MAX_TOP_K || top_k > n_experts)
+    return QMV_ERR_RANGE;
+  if (hidden <= 0 || ffn <= 0 || hidden % 256 || ffn % 256) return QMV_ERR_SHAPE;
+  if (!qmv::moe_grouped_fits_lds(hidden, ffn)) return QMV_ERR_RANGE;
+  size_t expert_bytes = 0, bank = 0;
+  if (!mul_size((size_t)ffn, (size_t)(hidden / 256) * 144, &expert_bytes) ||
+      !mul_size(expert_bytes, (size_t)n_experts, &bank) || bank_bytes != bank)
+    return QMV_ERR_SIZE;
+  if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(x_bf16, 16) ||
+      !aligned(logits, 4) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(ws, 256))
+    return QMV_ERR_ALIGN;
+  const size_t need = qmv::moe_grouped_workspace_bytes(t, hidden, ffn, n_experts, top_k);
+  if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
+  const size_t ta = (size_t)t, yb = ta * hidden * 4, idb = ta * top_k * 4;
+  const void *in_p[] = {w_gate, w_up, w_down, logits, x_bf16};
+  const size_t in_b[] = {bank, bank, bank, ta * n_experts * 4, ta * hidden * 2};
+  const void *out_p[] = {y, topk_ids, topk_w, ws};
+  const size_t out_b[] = {yb, topk_ids ? idb : 0, topk_w ? idb : 0, need};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (overlap(out_p[o], out_b[o], in_p[i], in_b[i])) return QMV_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlap(out_p[o], out_b[o], out_p[o2], out_b[o2])) return QMV_ERR_ALIAS;
   }
-  return QMV_OK;
+  return qmv::launch_q4_k_moe_grouped(w_gate, w_up, w_down, logits, x_bf16, y, topk_ids, topk_w, ws, t, hidden, ffn,
+                                      n_experts, top_k, stream);
 }
 
 size_t qmv_iq4_xs_moe_workspace(int t, int hidden, int ffn, int n_experts, int top_k) {

@@ -27,6 +27,11 @@ int launch_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, co
                     const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs,
                     void *ws, int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
 size_t moe_workspace_bytes(int t, int hidden, int ffn, int n_experts, int top_k);
+size_t moe_grouped_workspace_bytes(int t, int hidden, int ffn, int n_experts, int top_k);
+bool moe_grouped_fits_lds(int hidden, int ffn);
+int launch_q4_k_moe_grouped(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
+                            const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, void *ws, int t,
+                            int hidden, int ffn, int n_experts, int top_k, void *stream);
 bool moe_fits_lds(int t, int hidden, int ffn, int top_k);
 int launch_iq4_xs_moe(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
                       const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, void *ws, int t,

@@ -241,13 +241,21 @@ int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_
  * Arguments, routing, outputs and error codes as qmv_q4_k_moe, except:
  *   1 <= t <= QMV_MOE_PREFILL_MAX_TOKENS; logits, x_bf16, y, topk_ids and
  *   topk_w hold all t tokens; there is no gather-list output;
- *   ws, ws_bytes  at least qmv_q4_k_moe_prefill_workspace(...) bytes (the
- *                 workspace of one group of QMV_MOE_MAX_TOKENS tokens).
- * The tokens run as consecutive groups of up to QMV_MOE_MAX_TOKENS through the
- * routed-expert kernels of qmv_q4_k_moe, in token order on `stream`, reusing
- * the workspace. Each group reads its selected experts' weights once. A
- * token's result is bit-identical to qmv_q4_k_moe on that token alone (the one
- * numerical program per request of the memra README's recent-fixes list).
+ *   16 rows of x (bf16) and of h (two bf16 halves) must fit in
+ *   QMV_LDS_X_BYTES with their per-32 sums (QMV_ERR_RANGE otherwise): hidden
+ *   up to 4352 and ffn up to 2304;
+ *   ws, ws_bytes  at least qmv_q4_k_moe_prefill_workspace(...) bytes: the
+ *                 routing, the per-expert pair lists, h (t top_k ffn fp32)
+ *                 and the per-pair down products (t top_k hidden fp32),
+ *                 each 256-byte aligned; it grows linearly with t.
+ * The (token, expert) pairs are grouped by expert into chunks of 16, and each
+ * chunk's gate/up and down products run on the matrix cores (bf16 MFMA, exact
+ * quants; h enters the down product as two bf16 halves that keep about 17
+ * bits of it), so each expert's weights are read once per 16 of its tokens.
+ * Results are within the same 2e-3 floored relative bound of the exact layer
+ * as qmv_q4_k_moe, but not bit-identical to it: the products are summed in
+ * another order. A token's result does not depend on the other tokens in the
+ * call, and repeated calls are bitwise identical.
  * Workload: the prompt phase of the memra README's 35B-A3B MoE (its summary
  * page's time-to-first-token figures).
  */

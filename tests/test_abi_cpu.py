@@ -265,22 +265,28 @@ def moe_prefill(**kw):
 
 
 def test_moe_prefill_validation():
-    # the workspace is one group's (QMV_MOE_MAX_TOKENS tokens), whatever t is
-    w4 = L.qmv_q4_k_moe_workspace(4, 2048, 768, 128, 8)
-    assert L.qmv_q4_k_moe_prefill_workspace(512, 2048, 768, 128, 8) == w4
-    assert L.qmv_q4_k_moe_prefill_workspace(3, 2048, 768, 128, 8) == L.qmv_q4_k_moe_workspace(3, 2048, 768, 128, 8)
+    # the workspace holds the routing, the per-expert lists and every pair's h and z
+    w512 = L.qmv_q4_k_moe_prefill_workspace(512, 2048, 768, 128, 8)
+    assert w512 > 512 * 8 * (768 + 2048) * 4
+    assert L.qmv_q4_k_moe_prefill_workspace(1024, 2048, 768, 128, 8) > w512
     assert L.qmv_q4_k_moe_prefill_workspace(0, 2048, 768, 128, 8) == 0
     assert L.qmv_q4_k_moe_prefill_workspace(65537, 2048, 768, 128, 8) == 0
+    assert L.qmv_q4_k_moe_prefill_workspace(8, 2048, 768, 128, 9) == 0
     assert moe_prefill(wg=0) == NULL and moe_prefill(logits=0) == NULL and moe_prefill(y=0) == NULL
     assert moe_prefill(t=0) == RANGE and moe_prefill(t=65537) == RANGE and moe_prefill(k=9, e=16) == RANGE
-    assert moe_prefill(h=300) == SHAPE
+    assert moe_prefill(h=300) == SHAPE and moe_prefill(f=0) == SHAPE
+    assert moe_prefill(h=10240) == RANGE                      # 16 tokens' activations exceed the LDS stage
+    # the LDS stage limits: hidden 4352 and ffn 2304 fit, one more super-block of either does not
+    assert L.qmv_q4_k_moe_prefill_workspace(1, 4352, 2304, 8, 2) > 0
+    assert L.qmv_q4_k_moe_prefill_workspace(1, 4608, 256, 8, 2) == 0
+    assert L.qmv_q4_k_moe_prefill_workspace(1, 256, 2560, 8, 2) == 0
     assert moe_prefill(bank=8 * 256 * 144 - 1) == SIZE
     assert moe_prefill(ws=0) == WORKSPACE and moe_prefill(ws_bytes=16) == WORKSPACE
-    assert moe_prefill(x=X + 2) == ALIGN
-    # the aliasing checks cover all t tokens, not one group: y of 9 tokens (9 KiB)
-    # reaches the topk ids placed 8 KiB after it; 4 tokens' y would not
+    assert moe_prefill(x=X + 2) == ALIGN and moe_prefill(ws=WS + 128) == ALIGN
+    # the aliasing checks cover all t tokens: y of 9 tokens (9 KiB) reaches ids 8 KiB after it
     assert moe_prefill(ids=Y + 8192) == ALIAS
     assert moe_prefill(t=600, y=X + (1 << 20) + 1024) == ALIAS   # y inside the 600 tokens' activations
+    assert moe_prefill(ws=Y + 4096) == ALIAS                      # workspace over the output
 
 
 def test_moe_bank_every_truncated_size_is_an_error():
