@@ -9,13 +9,14 @@
 //              list, sorted by expert then token;
 //  3. chunks:  each expert's pairs cut into chunks of 16; the (expert, chunk)
 //              list;
-//  4. gate/up: per (16-row tile of W_gate and W_up, chunk): the 16 gathered
-//              tokens' activations times the tile with one
+//  4. gate/up: per (64 TPW rows of W_gate and W_up, chunk), each wave owning
+//              TPW tiles of 16 rows over all of K: the 16 gathered
+//              tokens' activations times each tile with one
 //              v_mfma_f32_16x16x32_bf16 per 32-weight sub-block and matrix
 //              (A = the tokens' activations, B = the quants as exact bf16
 //              integers), per sub-block acc += (d sc) D - (dmin m) X; then
 //              h = silu(g) u in fp32 per pair;
-//  5. down:    per (16-row tile of W_down, chunk): the same with A = h split
+//  5. down:    per (64 TPW rows of W_down, chunk): the same with A = h split
 //              into two bf16 halves (h_hi = bf16(h), h_lo = bf16(h - h_hi),
 //              so the product keeps about 17 bits of h), z per pair;
 //  6. combine: y_t = sum over ranks j of w_tj z_tj, in rank order.
@@ -202,6 +203,11 @@ __device__ __forceinline__ ChunkInfo chunk_info(const int2 *__restrict__ chunks,
   return ci;
 }
 
+// Each wave owns TPW tiles of 16 weight rows over the whole of K; the
+// workgroup's four waves cover 64 TPW consecutive rows and share the chunk's
+// staged activations. The next super-block's weights are loaded while the
+// current one is multiplied.
+template <int TPW>
 __global__ __launch_bounds__(kThr) void g_gate_up_kernel(const uint8_t *__restrict__ w_gate,
                                                           const uint8_t *__restrict__ w_up,
                                                           const uint16_t *__restrict__ x,
@@ -217,7 +223,6 @@ __global__ __launch_bounds__(kThr) void g_gate_up_kernel(const uint8_t *__restri
   const int gpr = hidden >> 3, rs = gpr + 4, nsub = hidden >> 5, nblk = hidden >> 8;
   uint4 *xs = lds;                                                    // [16][rs]
   float *xsum = reinterpret_cast<float *>(lds + (size_t)kChunk * rs); // [16][nsub]
-  float *red = xsum + (size_t)kChunk * nsub;                          // [2][kWv][16 rows][16 pairs]
   const int tid = (int)threadIdx.x, wv = tid >> 6, l = tid & 63, nl = l & 15, kg = l >> 4;
 
   // stage the chunk's activation rows (zeros past its pairs)
@@ -246,66 +251,83 @@ __global__ __launch_bounds__(kThr) void g_gate_up_kernel(const uint8_t *__restri
   }
   __syncthreads();
 
-  const int f = (int)blockIdx.x * kTile + nl;   // this lane's W row (ffn is a multiple of 16)
+  // rows rb .. rb + 16 TPW - 1 (the grid covers ffn exactly)
+  const int rb = ((int)blockIdx.x * kWv + wv) * (TPW * kTile);
   const size_t row_bytes = (size_t)nblk * kQ4KBlockBytes;
-  const uint8_t *gr = w_gate + ((size_t)ci.e * ffn + f) * row_bytes;
-  const uint8_t *ur = w_up + ((size_t)ci.e * ffn + f) * row_bytes;
-  float ag[4] = {0.0f, 0.0f, 0.0f, 0.0f}, au[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const uint8_t *gr[TPW], *ur[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    gr[tt] = w_gate + ((size_t)ci.e * ffn + rb + kTile * tt + nl) * row_bytes;
+    ur[tt] = w_up + ((size_t)ci.e * ffn + rb + kTile * tt + nl) * row_bytes;
+  }
+  float ag[TPW][4], au[TPW][4];
+  SbLoad lg[TPW], lu[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ag[tt][r] = 0.0f, au[tt][r] = 0.0f;
+    lg[tt] = load_sb(gr[tt], kg);
+    lu[tt] = load_sb(ur[tt], kg);
+  }
   const uint4 *xa = xs + nl * rs + kg;
-  for (int b = wv; b < nblk; b += kWv) {
-    const SbLoad lgt = load_sb(gr + (size_t)b * kQ4KBlockBytes, kg);
-    const SbLoad lup = load_sb(ur + (size_t)b * kQ4KBlockBytes, kg);
+  for (int b = 0; b < nblk; ++b) {
+    const size_t nb = (size_t)(b + 1 < nblk ? b + 1 : b) * kQ4KBlockBytes;   // last block re-read at the end
+    SbLoad ng[TPW], nu[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      ng[tt] = load_sb(gr[tt] + nb, kg);
+      nu[tt] = load_sb(ur[tt] + nb, kg);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const ScaleSel sel = scale_selectors(c);
-      const ChunkScales cg = chunk_scales(lgt.hdr, sel), cu = chunk_scales(lup.hdr, sel);
-      const uint2 qg = lgt.q[c], qu = lup.q[c];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int jg = 8 * b + 2 * c + hh;
-        const bf16x8 bg = hh ? nibbles8((qg.x >> 4) & 0x0F0F0F0Fu, (qg.y >> 4) & 0x0F0F0F0Fu)
-                             : nibbles8(qg.x & 0x0F0F0F0Fu, qg.y & 0x0F0F0F0Fu);
-        const bf16x8 bu = hh ? nibbles8((qu.x >> 4) & 0x0F0F0F0Fu, (qu.y >> 4) & 0x0F0F0F0Fu)
-                             : nibbles8(qu.x & 0x0F0F0F0Fu, qu.y & 0x0F0F0F0Fu);
         const bf16x8 av = __builtin_bit_cast(bf16x8, xa[4 * jg]);
-        f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f}, du = {0.0f, 0.0f, 0.0f, 0.0f};
-        dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, dg, 0, 0, 0);
-        du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, du, 0, 0, 0);
-        const float sag = hh ? cg.a1 : cg.a0, sbg = hh ? cg.b1 : cg.b0;
-        const float sau = hh ? cu.a1 : cu.a0, sbu = hh ? cu.b1 : cu.b0;
+        float xsr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float xsr = xsum[(4 * kg + r) * nsub + jg];
-          ag[r] = __builtin_fmaf(sag, dg[r], ag[r]);
-          ag[r] = __builtin_fmaf(-sbg, xsr, ag[r]);
-          au[r] = __builtin_fmaf(sau, du[r], au[r]);
-          au[r] = __builtin_fmaf(-sbu, xsr, au[r]);
+        for (int r = 0; r < 4; ++r) xsr[r] = xsum[(4 * kg + r) * nsub + jg];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+          const ChunkScales cg = chunk_scales(lg[tt].hdr, sel), cu = chunk_scales(lu[tt].hdr, sel);
+          const uint2 qg = lg[tt].q[c], qu = lu[tt].q[c];
+          const bf16x8 bg = hh ? nibbles8((qg.x >> 4) & 0x0F0F0F0Fu, (qg.y >> 4) & 0x0F0F0F0Fu)
+                               : nibbles8(qg.x & 0x0F0F0F0Fu, qg.y & 0x0F0F0F0Fu);
+          const bf16x8 bu = hh ? nibbles8((qu.x >> 4) & 0x0F0F0F0Fu, (qu.y >> 4) & 0x0F0F0F0Fu)
+                               : nibbles8(qu.x & 0x0F0F0F0Fu, qu.y & 0x0F0F0F0Fu);
+          f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f}, du = {0.0f, 0.0f, 0.0f, 0.0f};
+          dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, dg, 0, 0, 0);
+          du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, du, 0, 0, 0);
+          const float sag = hh ? cg.a1 : cg.a0, sbg = hh ? cg.b1 : cg.b0;
+          const float sau = hh ? cu.a1 : cu.a0, sbu = hh ? cu.b1 : cu.b0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            ag[tt][r] = __builtin_fmaf(sag, dg[r], ag[tt][r]);
+            ag[tt][r] = __builtin_fmaf(-sbg, xsr[r], ag[tt][r]);
+            au[tt][r] = __builtin_fmaf(sau, du[r], au[tt][r]);
+            au[tt][r] = __builtin_fmaf(-sbu, xsr[r], au[tt][r]);
+          }
         }
       }
     }
-  }
-  // lane l holds pairs 4 kg .. 4 kg + 3 of W row nl; add the waves in order
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    red[((0 * kWv + wv) * kTile + nl) * kChunk + 4 * kg + r] = ag[r];
-    red[((1 * kWv + wv) * kTile + nl) * kChunk + 4 * kg + r] = au[r];
+    for (int tt = 0; tt < TPW; ++tt) lg[tt] = ng[tt], lu[tt] = nu[tt];
   }
-  __syncthreads();
-  {
-    const int row = tid / kChunk, i = tid - row * kChunk;   // 256 threads = 16 rows x 16 pairs
-    float g = red[(0 * kWv + 0) * kTile * kChunk + row * kChunk + i];
-    float u = red[(1 * kWv + 0) * kTile * kChunk + row * kChunk + i];
+  // lane l holds pairs 4 kg .. 4 kg + 3 of row rb + 16 tt + nl
 #pragma unroll
-    for (int w = 1; w < kWv; ++w) {
-      g += red[(0 * kWv + w) * kTile * kChunk + row * kChunk + i];
-      u += red[(1 * kWv + w) * kTile * kChunk + row * kChunk + i];
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * kg + r;
+      const float g = ag[tt][r], u = au[tt][r];
+      if (i < ci.n) h[(size_t)(ci.pos0 + i) * ffn + rb + kTile * tt + nl] = g / (1.0f + expf(-g)) * u;
     }
-    if (i < ci.n) h[(size_t)(ci.pos0 + i) * ffn + (int)blockIdx.x * kTile + row] = g / (1.0f + expf(-g)) * u;
-  }
 }
 
 // ---------------------------------------------------------------- 5. down
 
+template <int TPW>
 __global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict__ w_down,
                                                        const int *__restrict__ cnt, const int *__restrict__ off,
                                                        const int *__restrict__ choff, const int2 *__restrict__ chunks,
@@ -317,10 +339,9 @@ __global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict_
   if (y >= choff[E]) return;
   const ChunkInfo ci = chunk_info(chunks, cnt, off, y);
   const int gpr = ffn >> 3, rs = gpr + 4, nsub = ffn >> 5, nblk = ffn >> 8;
-  uint4 *hs_hi = lds;                                                   // [16][rs]
-  uint4 *hs_lo = lds + (size_t)kChunk * rs;                             // [16][rs]
+  uint4 *hs_hi = lds;                                                     // [16][rs]
+  uint4 *hs_lo = lds + (size_t)kChunk * rs;                               // [16][rs]
   float *hsum = reinterpret_cast<float *>(lds + (size_t)2 * kChunk * rs); // [16][nsub]
-  float *red = hsum + (size_t)kChunk * nsub;                            // [kWv][16 rows][16 pairs]
   const int tid = (int)threadIdx.x, wv = tid >> 6, l = tid & 63, nl = l & 15, kg = l >> 4;
 
   // stage h of the chunk's pairs as bf16 halves (zeros past its pairs)
@@ -362,42 +383,64 @@ __global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict_
   }
   __syncthreads();
 
-  const int n = (int)blockIdx.x * kTile + nl;   // this lane's W_down row (hidden is a multiple of 16)
-  const uint8_t *dr = w_down + ((size_t)ci.e * hidden + n) * (size_t)nblk * kQ4KBlockBytes;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // W_down rows rb .. rb + 16 TPW - 1 (the grid covers hidden exactly)
+  const int rb = ((int)blockIdx.x * kWv + wv) * (TPW * kTile);
+  const size_t row_bytes = (size_t)nblk * kQ4KBlockBytes;
+  const uint8_t *dr[TPW];
+  float acc[TPW][4];
+  SbLoad ld[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    dr[tt] = w_down + ((size_t)ci.e * hidden + rb + kTile * tt + nl) * row_bytes;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[tt][r] = 0.0f;
+    ld[tt] = load_sb(dr[tt], kg);
+  }
   const uint4 *ha = hs_hi + nl * rs + kg, *la = hs_lo + nl * rs + kg;
-  for (int b = wv; b < nblk; b += kWv) {
-    const SbLoad ld = load_sb(dr + (size_t)b * kQ4KBlockBytes, kg);
+  for (int b = 0; b < nblk; ++b) {
+    const size_t nb = (size_t)(b + 1 < nblk ? b + 1 : b) * kQ4KBlockBytes;
+    SbLoad nx[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) nx[tt] = load_sb(dr[tt] + nb, kg);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const ChunkScales cs = chunk_scales(ld.hdr, scale_selectors(c));
-      const uint2 qd = ld.q[c];
+      const ScaleSel sel = scale_selectors(c);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int jg = 8 * b + 2 * c + hh;
-        const bf16x8 bq = hh ? nibbles8((qd.x >> 4) & 0x0F0F0F0Fu, (qd.y >> 4) & 0x0F0F0F0Fu)
-                             : nibbles8(qd.x & 0x0F0F0F0Fu, qd.y & 0x0F0F0F0Fu);
-        f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ha[4 * jg]), bq, d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, la[4 * jg]), bq, d, 0, 0, 0);
-        const float sa = hh ? cs.a1 : cs.a0, sb = hh ? cs.b1 : cs.b0;
+        const bf16x8 ahi = __builtin_bit_cast(bf16x8, ha[4 * jg]), alo = __builtin_bit_cast(bf16x8, la[4 * jg]);
+        float hsr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[r] = __builtin_fmaf(sa, d[r], acc[r]);
-          acc[r] = __builtin_fmaf(-sb, hsum[(4 * kg + r) * nsub + jg], acc[r]);
+        for (int r = 0; r < 4; ++r) hsr[r] = hsum[(4 * kg + r) * nsub + jg];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+          const ChunkScales cs = chunk_scales(ld[tt].hdr, sel);
+          const uint2 qd = ld[tt].q[c];
+          const bf16x8 bq = hh ? nibbles8((qd.x >> 4) & 0x0F0F0F0Fu, (qd.y >> 4) & 0x0F0F0F0Fu)
+                               : nibbles8(qd.x & 0x0F0F0F0Fu, qd.y & 0x0F0F0F0Fu);
+          f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bq, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bq, d, 0, 0, 0);
+          const float sa = hh ? cs.a1 : cs.a0, sb = hh ? cs.b1 : cs.b0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            acc[tt][r] = __builtin_fmaf(sa, d[r], acc[tt][r]);
+            acc[tt][r] = __builtin_fmaf(-sb, hsr[r], acc[tt][r]);
+          }
         }
       }
     }
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) ld[tt] = nx[tt];
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[(wv * kTile + nl) * kChunk + 4 * kg + r] = acc[r];
-  __syncthreads();
-  {
-    const int row = tid / kChunk, i = tid - row * kChunk;
-    float v = red[row * kChunk + i];
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * kg + r;
+    if (i < ci.n) {
+      float *zr = z + (size_t)plist[ci.pos0 + i] * hidden + rb + nl;
 #pragma unroll
-    for (int w = 1; w < kWv; ++w) v += red[(w * kTile + row) * kChunk + i];
-    if (i < ci.n) z[(size_t)plist[ci.pos0 + i] * hidden + (int)blockIdx.x * kTile + row] = v;
+      for (int tt = 0; tt < TPW; ++tt) zr[kTile * tt] = acc[tt][r];
+    }
   }
 }
 
@@ -419,13 +462,53 @@ size_t moe_grouped_workspace_bytes(int t, int hidden, int ffn, int n_experts, in
   return g_layout(t, hidden, ffn, n_experts, top_k).total;
 }
 
-bool moe_grouped_fits_lds(int hidden, int ffn) {
-  const size_t a = (size_t)kChunk * ((hidden >> 3) + 4) * 16 + (size_t)kChunk * (hidden >> 5) * 4 +
-                   (size_t)2 * kWv * kTile * kChunk * 4;
-  const size_t b = (size_t)2 * kChunk * ((ffn >> 3) + 4) * 16 + (size_t)kChunk * (ffn >> 5) * 4 +
-                   (size_t)kWv * kTile * kChunk * 4;
-  return a <= (size_t)QMV_LDS_X_BYTES && b <= (size_t)QMV_LDS_X_BYTES;
+static size_t gate_up_lds_bytes(int hidden) {
+  return (size_t)kChunk * ((hidden >> 3) + 4) * 16 + (size_t)kChunk * (hidden >> 5) * 4;
 }
+static size_t down_lds_bytes(int ffn) {
+  return (size_t)2 * kChunk * ((ffn >> 3) + 4) * 16 + (size_t)kChunk * (ffn >> 5) * 4;
+}
+
+bool moe_grouped_fits_lds(int hidden, int ffn) {
+  return gate_up_lds_bytes(hidden) <= (size_t)QMV_LDS_X_BYTES && down_lds_bytes(ffn) <= (size_t)QMV_LDS_X_BYTES;
+}
+
+namespace {
+
+// Tiles per wave from the number of pairs P. Measured on the 35B-A3B layer
+// (hidden 2048, ffn 768, 128 experts, top-8): four tiles per wave is fastest
+// from 512 tokens (P = 4096) up, two at 64 tokens (P = 512).
+int tiles_per_wave(int P) {
+  if (P >= 2048) return 4;
+  return P >= 256 ? 2 : 1;
+}
+
+template <int TPW>
+int launch_gate_up(const uint8_t *w_gate, const uint8_t *w_up, const uint16_t *x, const int *cnt, const int *off,
+                   const int *choff, const int2 *chunks, const int *plist, float *h, int hidden, int ffn, int E,
+                   int K, unsigned maxch, hipStream_t s) {
+  static std::atomic<size_t> granted{0};
+  const size_t lds = gate_up_lds_bytes(hidden);
+  if (allow_dynamic_lds(reinterpret_cast<const void *>(&g_gate_up_kernel<TPW>), lds, granted, "g_gate_up_kernel lds"))
+    return QMV_ERR_HIP;
+  return launch_kernel("g_gate_up_kernel", g_gate_up_kernel<TPW>,
+                       dim3((unsigned)(ffn / (kWv * kTile * TPW)), maxch), dim3(kThr), lds, s, w_gate, w_up, x, cnt,
+                       off, choff, chunks, plist, h, hidden, ffn, E, K);
+}
+
+template <int TPW>
+int launch_down(const uint8_t *w_down, const int *cnt, const int *off, const int *choff, const int2 *chunks,
+                const int *plist, const float *h, float *z, int hidden, int ffn, int E, unsigned maxch,
+                hipStream_t s) {
+  static std::atomic<size_t> granted{0};
+  const size_t lds = down_lds_bytes(ffn);
+  if (allow_dynamic_lds(reinterpret_cast<const void *>(&g_down_kernel<TPW>), lds, granted, "g_down_kernel lds"))
+    return QMV_ERR_HIP;
+  return launch_kernel("g_down_kernel", g_down_kernel<TPW>, dim3((unsigned)(hidden / (kWv * kTile * TPW)), maxch),
+                       dim3(kThr), lds, s, w_down, cnt, off, choff, chunks, plist, h, z, hidden, ffn, E);
+}
+
+}  // namespace
 
 int launch_q4_k_moe_grouped(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
                             const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, void *ws, int t,
@@ -444,27 +527,31 @@ int launch_q4_k_moe_grouped(const void *w_gate, const void *w_up, const void *w_
   float *z = reinterpret_cast<float *>(wb + L.z);
   const int P = t * top_k;
   const unsigned maxch = (unsigned)((P + kChunk - 1) / kChunk + n_experts);
+  const uint8_t *wg = static_cast<const uint8_t *>(w_gate), *wu = static_cast<const uint8_t *>(w_up);
+  const uint8_t *wd = static_cast<const uint8_t *>(w_down);
   int rc = launch_kernel("g_route_kernel", g_route_kernel, dim3((unsigned)((t + kWv - 1) / kWv)), dim3(kThr), 0, s,
                          logits, ids, wts, topk_ids, topk_w, t, n_experts, top_k);
   if (!rc) rc = launch_kernel("g_group_kernel", g_group_kernel, dim3((unsigned)n_experts), dim3(kThr), 0, s, ids,
                               cnt, off, plist, P);
   if (!rc) rc = launch_kernel("g_chunks_kernel", g_chunks_kernel, dim3(1), dim3(kThr), 0, s, cnt, choff, chunks,
                               n_experts);
-  static std::atomic<size_t> granted_a{0}, granted_b{0};
-  const size_t lds_a = (size_t)kChunk * ((hidden >> 3) + 4) * 16 + (size_t)kChunk * (hidden >> 5) * 4 +
-                       (size_t)2 * kWv * kTile * kChunk * 4;
-  const size_t lds_b = (size_t)2 * kChunk * ((ffn >> 3) + 4) * 16 + (size_t)kChunk * (ffn >> 5) * 4 +
-                       (size_t)kWv * kTile * kChunk * 4;
-  if (!rc && (allow_dynamic_lds(reinterpret_cast<const void *>(&g_gate_up_kernel), lds_a, granted_a,
-                                "g_gate_up_kernel lds") ||
-              allow_dynamic_lds(reinterpret_cast<const void *>(&g_down_kernel), lds_b, granted_b, "g_down_kernel lds")))
-    rc = QMV_ERR_HIP;
-  if (!rc) rc = launch_kernel("g_gate_up_kernel", g_gate_up_kernel, dim3((unsigned)(ffn / kTile), maxch), dim3(kThr),
-                              lds_a, s, static_cast<const uint8_t *>(w_gate), static_cast<const uint8_t *>(w_up), x,
-                              cnt, off, choff, chunks, plist, h, hidden, ffn, n_experts, top_k);
-  if (!rc) rc = launch_kernel("g_down_kernel", g_down_kernel, dim3((unsigned)(hidden / kTile), maxch), dim3(kThr),
-                              lds_b, s, static_cast<const uint8_t *>(w_down), cnt, off, choff, chunks, plist, h, z,
-                              hidden, ffn, n_experts);
+  if (!rc) {
+    switch (tiles_per_wave(P)) {
+      case 4: rc = launch_gate_up<4>(wg, wu, x, cnt, off, choff, chunks, plist, h, hidden, ffn, n_experts, top_k,
+                                     maxch, s); break;
+      case 2: rc = launch_gate_up<2>(wg, wu, x, cnt, off, choff, chunks, plist, h, hidden, ffn, n_experts, top_k,
+                                     maxch, s); break;
+      default: rc = launch_gate_up<1>(wg, wu, x, cnt, off, choff, chunks, plist, h, hidden, ffn, n_experts, top_k,
+                                      maxch, s); break;
+    }
+  }
+  if (!rc) {
+    switch (tiles_per_wave(P)) {
+      case 4: rc = launch_down<4>(wd, cnt, off, choff, chunks, plist, h, z, hidden, ffn, n_experts, maxch, s); break;
+      case 2: rc = launch_down<2>(wd, cnt, off, choff, chunks, plist, h, z, hidden, ffn, n_experts, maxch, s); break;
+      default: rc = launch_down<1>(wd, cnt, off, choff, chunks, plist, h, z, hidden, ffn, n_experts, maxch, s); break;
+    }
+  }
   if (!rc) rc = launch_kernel("g_combine_kernel", g_combine_kernel, dim3((unsigned)t,
                               (unsigned)((hidden + kThr - 1) / kThr)), dim3(kThr), 0, s, z, wts, y, hidden, top_k);
   return rc;

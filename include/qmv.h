@@ -243,7 +243,7 @@ int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_
  *   topk_w hold all t tokens; there is no gather-list output;
  *   16 rows of x (bf16) and of h (two bf16 halves) must fit in
  *   QMV_LDS_X_BYTES with their per-32 sums (QMV_ERR_RANGE otherwise): hidden
- *   up to 4352 and ffn up to 2304;
+ *   up to 4608 and ffn up to 2304;
  *   ws, ws_bytes  at least qmv_q4_k_moe_prefill_workspace(...) bytes: the
  *                 routing, the per-expert pair lists, h (t top_k ffn fp32)
  *                 and the per-pair down products (t top_k hidden fp32),

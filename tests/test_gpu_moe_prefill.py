@@ -6,7 +6,9 @@ not depend on the other tokens of the call (a prefix of the prompt run alone
 gives bit-identical rows); run-to-run bitwise determinism; output and workspace
 guards untouched. The cases span one partial chunk of 16 pairs, experts with
 several chunks, k = 1, k = n_experts (every token takes every expert), and a
-35B-A3B-like layer (hidden 2048, 128 experts, top-8).
+35B-A3B-like layer (hidden 2048, 128 experts, top-8), and that layer at 512
+tokens with sampled tokens checked. The pair counts reach one, two and four
+weight tiles per wave.
 """
 
 import numpy as np
@@ -48,7 +50,7 @@ def _run(q, dev, bank_d, logits, x, hidden, ffn, ne, tk):
 
 
 CASES = [(3, 512, 256, 16, 4, 1), (9, 512, 256, 16, 4, 2), (37, 256, 512, 8, 2, 3), (200, 512, 256, 32, 8, 5),
-         (11, 256, 256, 8, 1, 6), (5, 256, 256, 4, 4, 7), (6, 2048, 768, 128, 8, 4)]
+         (11, 256, 256, 8, 1, 6), (5, 256, 256, 4, 4, 7), (6, 2048, 768, 128, 8, 4), (256, 512, 256, 32, 8, 8)]
 
 
 @pytest.mark.parametrize("t,hidden,ffn,ne,tk,seed", CASES)
@@ -62,6 +64,23 @@ def test_moe_prefill_parity(q, dev, t, hidden, ffn, ne, tk, seed):
     assert np.array_equal(ids, idr)
     assert np.allclose(wts, wr, rtol=2e-6, atol=0)
     err = oracle.floored_rel_err(y, yr)
+    assert err <= GEMV_TOL, err
+
+
+def test_moe_prefill_full_layer_sampled_tokens(q, dev):
+    # the timed workload: 512 tokens through the 35B-A3B layer; the oracle takes five sampled tokens
+    t, hidden, ffn, ne, tk = 512, 2048, 768, 128, 8
+    bank = synth.moe_bank(21, ne, hidden, ffn)
+    bank_d = tuple(to_dev(b, dev) for b in bank)
+    logits = synth.moe_logits(21, t, ne)
+    x = synth.bf16_normal(22, (t, hidden))
+    y, ids, wts = _run(q, dev, bank_d, logits, x, hidden, ffn, ne, tk)
+    assert np.isfinite(y).all()
+    pick = np.array([0, 137, 255, 300, 511])
+    yr, idr, wr = oracle.moe_q4_k(*bank, logits[pick], x[pick], hidden, ffn, ne, tk)
+    assert np.array_equal(ids[pick], idr)
+    assert np.allclose(wts[pick], wr, rtol=2e-6, atol=0)
+    err = oracle.floored_rel_err(y[pick], yr)
     assert err <= GEMV_TOL, err
 
 
