@@ -403,8 +403,12 @@ def bench_moe(args, torch, np, q, synth, timer, dev, sp, fmt="q4_k"):
                     raise q.QmvError(rc, "qmv_q4_k_moe_prefill")
         pstep()
         tl = timer.run(pstep, 2) / nb
-        out["prefill_T512"] = {"us_per_layer": tl * 1e6, "tokens_per_s_per_layer": t / tl}
-        log(f"[bench] {fmt} MoE prefill T={t}: {tl * 1e3:.3f} ms/layer, {t / tl:.0f} tokens/s per layer")
+        # algorithmic work: per (token, rank) pair 2 flop per weight of W_gate, W_up and W_down
+        flops = t * tk * 2 * 3 * hidden * ffn
+        out["prefill_T512"] = {"us_per_layer": tl * 1e6, "tokens_per_s_per_layer": t / tl,
+                               "TFLOPs": flops / tl / 1e12}
+        log(f"[bench] {fmt} MoE prefill T={t}: {tl * 1e3:.3f} ms/layer, {t / tl:.0f} tokens/s per layer, "
+            f"{flops / tl / 1e12:.0f} TFLOP/s")
     del banks
     return out
 
