@@ -8,14 +8,16 @@
 //              chose a lower expert, and its pairs in token order: the pair
 //              list, sorted by expert then token;
 //  3. chunks:  each expert's pairs cut into chunks of 16; the (expert, chunk)
-//              list;
+//              list (and a list of chunks of 32 for the wide gate/up form);
 //  4. gate/up: per (64 TPW rows of W_gate and W_up, chunk), each wave owning
 //              TPW tiles of 16 rows over all of K: the 16 gathered
 //              tokens' activations times each tile with one
 //              v_mfma_f32_16x16x32_bf16 per 32-weight sub-block and matrix
 //              (A = the tokens' activations, B = the quants as exact bf16
 //              integers), per sub-block acc += (d sc) D - (dmin m) X; then
-//              h = silu(g) u in fp32 per pair;
+//              h = silu(g) u in fp32 per pair. From 2048 pairs, with 32
+//              rows of x fitting in LDS, chunks of 32 pairs instead: eight
+//              waves, two MFMA row blocks per converted weight fragment;
 //  5. down:    per (64 TPW rows of W_down, chunk): the same with A = h split
 //              into two bf16 halves (h_hi = bf16(h), h_lo = bf16(h - h_hi),
 //              so the product keeps about 17 bits of h), z per pair;
@@ -49,7 +51,7 @@ constexpr int kWv = 4;       // waves per workgroup; they split the super-blocks
 constexpr int kThr = 64 * kWv;
 
 struct GLayout {
-  size_t ids, wts, cnt, off, choff, chunks, plist, h, z, total;
+  size_t ids, wts, cnt, off, choff, chunks, choff32, chunks32, plist, h, z, total;
 };
 
 inline size_t g_round(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -65,6 +67,8 @@ inline GLayout g_layout(int t, int hidden, int ffn, int E, int K) {
   L.off = o; o += g_round((size_t)E * 4);
   L.choff = o; o += g_round(((size_t)E + 1) * 4);
   L.chunks = o; o += g_round(maxch * 8);
+  L.choff32 = o; o += g_round(((size_t)E + 1) * 4);
+  L.chunks32 = o; o += g_round(((P + 31) / 32 + (size_t)E) * 8);
   L.plist = o; o += g_round(P * 4);
   L.h = o; o += g_round(P * (size_t)ffn * 4);
   L.z = o; o += g_round(P * (size_t)hidden * 4);
@@ -150,11 +154,12 @@ __global__ __launch_bounds__(kThr) void g_group_kernel(const int *__restrict__ i
 
 // One workgroup: chunk offsets per expert (an exclusive scan in expert order)
 // and the (expert, chunk) list.
+template <int CH>
 __global__ __launch_bounds__(kThr) void g_chunks_kernel(const int *__restrict__ cnt, int *__restrict__ choff,
                                                          int2 *__restrict__ chunks, const int E) {
   __shared__ int nch[QMV_MOE_MAX_EXPERTS + 1];
   const int tid = (int)threadIdx.x;
-  for (int e = tid; e < E; e += kThr) nch[e] = (cnt[e] + kChunk - 1) / kChunk;
+  for (int e = tid; e < E; e += kThr) nch[e] = (cnt[e] + CH - 1) / CH;
   __syncthreads();
   if (tid == 0) {
     int s = 0;
@@ -191,15 +196,16 @@ __device__ __forceinline__ SbLoad load_sb(const uint8_t *__restrict__ bp, const 
 struct ChunkInfo {
   int e, pos0, n;
 };
+template <int CH = kChunk>
 __device__ __forceinline__ ChunkInfo chunk_info(const int2 *__restrict__ chunks, const int *__restrict__ cnt,
                                                 const int *__restrict__ off, const int y) {
   const int2 ec = chunks[y];
   ChunkInfo ci;
   ci.e = ec.x;
-  const int first = ec.y * kChunk;
+  const int first = ec.y * CH;
   ci.pos0 = off[ec.x] + first;
   const int left = cnt[ec.x] - first;
-  ci.n = left < kChunk ? left : kChunk;
+  ci.n = left < CH ? left : CH;
   return ci;
 }
 
@@ -323,6 +329,146 @@ __global__ __launch_bounds__(kThr) void g_gate_up_kernel(const uint8_t *__restri
       const float g = ag[tt][r], u = au[tt][r];
       if (i < ci.n) h[(size_t)(ci.pos0 + i) * ffn + rb + kTile * tt + nl] = g / (1.0f + expf(-g)) * u;
     }
+}
+
+// The same product for chunks of 32 pairs: eight waves, each owning TPW tiles
+// over all of K, and two MFMA row blocks (pairs 0..15 and 16..31) per
+// converted weight fragment, so each expert's weights are read once per 32 of
+// its pairs and each conversion feeds two products.
+constexpr int kChunk32 = 32;
+constexpr int kWv32 = 8;
+constexpr int kThr32 = 64 * kWv32;
+
+template <int TPW>
+__global__ __launch_bounds__(kThr32) void g_gate_up32_kernel(const uint8_t *__restrict__ w_gate,
+                                                              const uint8_t *__restrict__ w_up,
+                                                              const uint16_t *__restrict__ x,
+                                                              const int *__restrict__ cnt, const int *__restrict__ off,
+                                                              const int *__restrict__ choff,
+                                                              const int2 *__restrict__ chunks,
+                                                              const int *__restrict__ plist, float *__restrict__ h,
+                                                              const int hidden, const int ffn, const int E,
+                                                              const int K) {
+  extern __shared__ uint4 lds[];
+  const int y = (int)blockIdx.y;
+  if (y >= choff[E]) return;   // uniform over the workgroup
+  const ChunkInfo ci = chunk_info<kChunk32>(chunks, cnt, off, y);
+  const int gpr = hidden >> 3, rs = gpr + 4, nsub = hidden >> 5, nblk = hidden >> 8;
+  uint4 *xs = lds;                                                      // [32][rs]
+  float *xsum = reinterpret_cast<float *>(lds + (size_t)kChunk32 * rs); // [32][nsub]
+  const int tid = (int)threadIdx.x, wv = tid >> 6, l = tid & 63, nl = l & 15, kg = l >> 4;
+
+  const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+  for (int g = tid; g < kChunk32 * gpr; g += kThr32) {
+    const int i = g / gpr, gg = g - i * gpr;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (i < ci.n) v = xg[(size_t)(plist[ci.pos0 + i] / K) * gpr + gg];
+    xs[i * rs + gg] = v;
+  }
+  __syncthreads();
+  for (int t = tid; t < kChunk32 * nsub; t += kThr32) {
+    const int i = t / nsub, sb = t - i * nsub;
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 g = xs[i * rs + 4 * sb + q];
+      const uint32_t v4[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s += bf16_bits_to_f32(v4[u] & 0xFFFFu);
+        s += bf16_bits_to_f32(v4[u] >> 16);
+      }
+    }
+    xsum[t] = s;
+  }
+  __syncthreads();
+
+  // rows rb .. rb + 16 TPW - 1 (the grid covers ffn exactly)
+  const int rb = ((int)blockIdx.x * kWv32 + wv) * (TPW * kTile);
+  const size_t row_bytes = (size_t)nblk * kQ4KBlockBytes;
+  const uint8_t *gr[TPW], *ur[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    gr[tt] = w_gate + ((size_t)ci.e * ffn + rb + kTile * tt + nl) * row_bytes;
+    ur[tt] = w_up + ((size_t)ci.e * ffn + rb + kTile * tt + nl) * row_bytes;
+  }
+  float ag[TPW][2][4], au[TPW][2][4];
+  SbLoad lg[TPW], lu[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ag[tt][hb][r] = 0.0f, au[tt][hb][r] = 0.0f;
+    lg[tt] = load_sb(gr[tt], kg);
+    lu[tt] = load_sb(ur[tt], kg);
+  }
+  const uint4 *xa0 = xs + nl * rs + kg, *xa1 = xs + (kTile + nl) * rs + kg;
+  for (int b = 0; b < nblk; ++b) {
+    const size_t nb = (size_t)(b + 1 < nblk ? b + 1 : b) * kQ4KBlockBytes;   // last block re-read at the end
+    SbLoad ng[TPW], nu[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      ng[tt] = load_sb(gr[tt] + nb, kg);
+      nu[tt] = load_sb(ur[tt] + nb, kg);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const ScaleSel sel = scale_selectors(c);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int jg = 8 * b + 2 * c + hh;
+        const bf16x8 av0 = __builtin_bit_cast(bf16x8, xa0[4 * jg]);
+        const bf16x8 av1 = __builtin_bit_cast(bf16x8, xa1[4 * jg]);
+        float xs0[4], xs1[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          xs0[r] = xsum[(4 * kg + r) * nsub + jg];
+          xs1[r] = xsum[(kTile + 4 * kg + r) * nsub + jg];
+        }
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+          const ChunkScales cg = chunk_scales(lg[tt].hdr, sel), cu = chunk_scales(lu[tt].hdr, sel);
+          const uint2 qg = lg[tt].q[c], qu = lu[tt].q[c];
+          const bf16x8 bg = hh ? nibbles8((qg.x >> 4) & 0x0F0F0F0Fu, (qg.y >> 4) & 0x0F0F0F0Fu)
+                               : nibbles8(qg.x & 0x0F0F0F0Fu, qg.y & 0x0F0F0F0Fu);
+          const bf16x8 bu = hh ? nibbles8((qu.x >> 4) & 0x0F0F0F0Fu, (qu.y >> 4) & 0x0F0F0F0Fu)
+                               : nibbles8(qu.x & 0x0F0F0F0Fu, qu.y & 0x0F0F0F0Fu);
+          const f32x4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+          const f32x4 dg0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av0, bg, z4, 0, 0, 0);
+          const f32x4 dg1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av1, bg, z4, 0, 0, 0);
+          const f32x4 du0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av0, bu, z4, 0, 0, 0);
+          const f32x4 du1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av1, bu, z4, 0, 0, 0);
+          const float sag = hh ? cg.a1 : cg.a0, sbg = hh ? cg.b1 : cg.b0;
+          const float sau = hh ? cu.a1 : cu.a0, sbu = hh ? cu.b1 : cu.b0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            ag[tt][0][r] = __builtin_fmaf(sag, dg0[r], ag[tt][0][r]);
+            ag[tt][0][r] = __builtin_fmaf(-sbg, xs0[r], ag[tt][0][r]);
+            ag[tt][1][r] = __builtin_fmaf(sag, dg1[r], ag[tt][1][r]);
+            ag[tt][1][r] = __builtin_fmaf(-sbg, xs1[r], ag[tt][1][r]);
+            au[tt][0][r] = __builtin_fmaf(sau, du0[r], au[tt][0][r]);
+            au[tt][0][r] = __builtin_fmaf(-sbu, xs0[r], au[tt][0][r]);
+            au[tt][1][r] = __builtin_fmaf(sau, du1[r], au[tt][1][r]);
+            au[tt][1][r] = __builtin_fmaf(-sbu, xs1[r], au[tt][1][r]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) lg[tt] = ng[tt], lu[tt] = nu[tt];
+  }
+  // lane l holds pairs 16 hb + 4 kg .. + 3 of row rb + 16 tt + nl
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = kTile * hb + 4 * kg + r;
+        const float g = ag[tt][hb][r], u = au[tt][hb][r];
+        if (i < ci.n) h[(size_t)(ci.pos0 + i) * ffn + rb + kTile * tt + nl] = g / (1.0f + expf(-g)) * u;
+      }
 }
 
 // ---------------------------------------------------------------- 5. down
@@ -465,6 +611,9 @@ size_t moe_grouped_workspace_bytes(int t, int hidden, int ffn, int n_experts, in
 static size_t gate_up_lds_bytes(int hidden) {
   return (size_t)kChunk * ((hidden >> 3) + 4) * 16 + (size_t)kChunk * (hidden >> 5) * 4;
 }
+static size_t gate_up32_lds_bytes(int hidden) {
+  return (size_t)kChunk32 * ((hidden >> 3) + 4) * 16 + (size_t)kChunk32 * (hidden >> 5) * 4;
+}
 static size_t down_lds_bytes(int ffn) {
   return (size_t)2 * kChunk * ((ffn >> 3) + 4) * 16 + (size_t)kChunk * (ffn >> 5) * 4;
 }
@@ -497,6 +646,20 @@ int launch_gate_up(const uint8_t *w_gate, const uint8_t *w_up, const uint16_t *x
 }
 
 template <int TPW>
+int launch_gate_up32(const uint8_t *w_gate, const uint8_t *w_up, const uint16_t *x, const int *cnt, const int *off,
+                     const int *choff, const int2 *chunks, const int *plist, float *h, int hidden, int ffn, int E,
+                     int K, unsigned maxch, hipStream_t s) {
+  static std::atomic<size_t> granted{0};
+  const size_t lds = gate_up32_lds_bytes(hidden);
+  if (allow_dynamic_lds(reinterpret_cast<const void *>(&g_gate_up32_kernel<TPW>), lds, granted,
+                        "g_gate_up32_kernel lds"))
+    return QMV_ERR_HIP;
+  return launch_kernel("g_gate_up32_kernel", g_gate_up32_kernel<TPW>,
+                       dim3((unsigned)(ffn / (kWv32 * kTile * TPW)), maxch), dim3(kThr32), lds, s, w_gate, w_up, x,
+                       cnt, off, choff, chunks, plist, h, hidden, ffn, E, K);
+}
+
+template <int TPW>
 int launch_down(const uint8_t *w_down, const int *cnt, const int *off, const int *choff, const int2 *chunks,
                 const int *plist, const float *h, float *z, int hidden, int ffn, int E, unsigned maxch,
                 hipStream_t s) {
@@ -522,6 +685,8 @@ int launch_q4_k_moe_grouped(const void *w_gate, const void *w_up, const void *w_
   int *off = reinterpret_cast<int *>(wb + L.off);
   int *choff = reinterpret_cast<int *>(wb + L.choff);
   int2 *chunks = reinterpret_cast<int2 *>(wb + L.chunks);
+  int *choff32 = reinterpret_cast<int *>(wb + L.choff32);
+  int2 *chunks32 = reinterpret_cast<int2 *>(wb + L.chunks32);
   int *plist = reinterpret_cast<int *>(wb + L.plist);
   float *h = reinterpret_cast<float *>(wb + L.h);
   float *z = reinterpret_cast<float *>(wb + L.z);
@@ -533,9 +698,18 @@ int launch_q4_k_moe_grouped(const void *w_gate, const void *w_up, const void *w_
                          logits, ids, wts, topk_ids, topk_w, t, n_experts, top_k);
   if (!rc) rc = launch_kernel("g_group_kernel", g_group_kernel, dim3((unsigned)n_experts), dim3(kThr), 0, s, ids,
                               cnt, off, plist, P);
-  if (!rc) rc = launch_kernel("g_chunks_kernel", g_chunks_kernel, dim3(1), dim3(kThr), 0, s, cnt, choff, chunks,
-                              n_experts);
-  if (!rc) {
+  if (!rc) rc = launch_kernel("g_chunks_kernel", g_chunks_kernel<kChunk>, dim3(1), dim3(kThr), 0, s, cnt, choff,
+                              chunks, n_experts);
+  // gate/up in chunks of 32 where there are enough pairs and 32 rows of x fit in LDS
+  const bool wide = P >= 2048 && gate_up32_lds_bytes(hidden) <= (size_t)QMV_LDS_X_BYTES;
+  if (!rc && wide)
+    rc = launch_kernel("g_chunks_kernel", g_chunks_kernel<kChunk32>, dim3(1), dim3(kThr), 0, s, cnt, choff32,
+                       chunks32, n_experts);
+  if (!rc && wide) {
+    const unsigned maxch32 = (unsigned)((P + kChunk32 - 1) / kChunk32 + n_experts);
+    rc = launch_gate_up32<2>(wg, wu, x, cnt, off, choff32, chunks32, plist, h, hidden, ffn, n_experts, top_k, maxch32,
+                             s);
+  } else if (!rc) {
     switch (tiles_per_wave(P)) {
       case 4: rc = launch_gate_up<4>(wg, wu, x, cnt, off, choff, chunks, plist, h, hidden, ffn, n_experts, top_k,
                                      maxch, s); break;
