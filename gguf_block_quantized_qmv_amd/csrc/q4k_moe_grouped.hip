@@ -19,8 +19,9 @@
 //              rows of x fitting in LDS, chunks of 32 pairs instead: eight
 //              waves, two MFMA row blocks per converted weight fragment;
 //  5. down:    per (64 TPW rows of W_down, chunk): the same with A = h split
-//              into two bf16 halves (h_hi = bf16(h), h_lo = bf16(h - h_hi),
-//              so the product keeps about 17 bits of h), z per pair;
+//              into three bf16 parts (h_hi = bf16(h), h_mi = bf16(h - h_hi),
+//              h_lo = bf16(h - h_hi - h_mi), about 24 bits of h), three
+//              MFMAs per sub-block, z per pair;
 //  6. combine: y_t = sum over ranks j of w_tj z_tj, in rank order.
 // Each expert's weights are read once per chunk of 16 of its tokens. Every
 // step has a fixed order, so results are bitwise reproducible.
@@ -486,43 +487,55 @@ __global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict_
   const ChunkInfo ci = chunk_info(chunks, cnt, off, y);
   const int gpr = ffn >> 3, rs = gpr + 4, nsub = ffn >> 5, nblk = ffn >> 8;
   uint4 *hs_hi = lds;                                                     // [16][rs]
-  uint4 *hs_lo = lds + (size_t)kChunk * rs;                               // [16][rs]
-  float *hsum = reinterpret_cast<float *>(lds + (size_t)2 * kChunk * rs); // [16][nsub]
+  uint4 *hs_mi = lds + (size_t)kChunk * rs;                               // [16][rs]
+  uint4 *hs_lo = lds + (size_t)2 * kChunk * rs;                           // [16][rs]
+  float *hsum = reinterpret_cast<float *>(lds + (size_t)3 * kChunk * rs); // [16][nsub]
   const int tid = (int)threadIdx.x, wv = tid >> 6, l = tid & 63, nl = l & 15, kg = l >> 4;
 
-  // stage h of the chunk's pairs as bf16 halves (zeros past its pairs)
+  // stage h of the chunk's pairs as three bf16 parts (zeros past its pairs):
+  // h_hi = bf16(h), h_mi = bf16(h - h_hi), h_lo = bf16(h - h_hi - h_mi); each
+  // difference is exact in fp32, so the parts keep about 24 bits of h
   for (int g = tid; g < kChunk * gpr; g += kThr) {
     const int i = g / gpr, gg = g - i * gpr;
-    uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+    uint32_t hi[4] = {0u, 0u, 0u, 0u}, mi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
     if (i < ci.n) {
       const float4 *hp = reinterpret_cast<const float4 *>(h + (size_t)(ci.pos0 + i) * ffn + 8 * gg);
       const float4 a = hp[0], b = hp[1];
       const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t h0 = f32_to_bf16_rne(v[2 * q]), h1 = f32_to_bf16_rne(v[2 * q + 1]);
-        const uint32_t l0 = f32_to_bf16_rne(v[2 * q] - bf16_bits_to_f32(h0));
-        const uint32_t l1 = f32_to_bf16_rne(v[2 * q + 1] - bf16_bits_to_f32(h1));
-        hi[q] = h0 | (h1 << 16);
-        lo[q] = l0 | (l1 << 16);
+        uint32_t p[2][3];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float v0 = v[2 * q + e];
+          p[e][0] = f32_to_bf16_rne(v0);
+          const float r1 = v0 - bf16_bits_to_f32(p[e][0]);
+          p[e][1] = f32_to_bf16_rne(r1);
+          p[e][2] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(p[e][1]));
+        }
+        hi[q] = p[0][0] | (p[1][0] << 16);
+        mi[q] = p[0][1] | (p[1][1] << 16);
+        lo[q] = p[0][2] | (p[1][2] << 16);
       }
     }
     hs_hi[i * rs + gg] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    hs_mi[i * rs + gg] = make_uint4(mi[0], mi[1], mi[2], mi[3]);
     hs_lo[i * rs + gg] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
   __syncthreads();
-  // per-sub-block sums of the values the products see (h_hi + h_lo), in index order
+  // per-sub-block sums of the values the products see (h_hi + h_mi + h_lo), in index order
   for (int t = tid; t < kChunk * nsub; t += kThr) {
     const int i = t / nsub, sb = t - i * nsub;
     float s = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint4 gh = hs_hi[i * rs + 4 * sb + q], gl = hs_lo[i * rs + 4 * sb + q];
-      const uint32_t vh[4] = {gh.x, gh.y, gh.z, gh.w}, vl[4] = {gl.x, gl.y, gl.z, gl.w};
+      const uint4 gh = hs_hi[i * rs + 4 * sb + q], gm = hs_mi[i * rs + 4 * sb + q], gl = hs_lo[i * rs + 4 * sb + q];
+      const uint32_t vh[4] = {gh.x, gh.y, gh.z, gh.w}, vm[4] = {gm.x, gm.y, gm.z, gm.w};
+      const uint32_t vl[4] = {gl.x, gl.y, gl.z, gl.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        s += bf16_bits_to_f32(vh[u] & 0xFFFFu) + bf16_bits_to_f32(vl[u] & 0xFFFFu);
-        s += bf16_bits_to_f32(vh[u] >> 16) + bf16_bits_to_f32(vl[u] >> 16);
+        s += bf16_bits_to_f32(vh[u] & 0xFFFFu) + (bf16_bits_to_f32(vm[u] & 0xFFFFu) + bf16_bits_to_f32(vl[u] & 0xFFFFu));
+        s += bf16_bits_to_f32(vh[u] >> 16) + (bf16_bits_to_f32(vm[u] >> 16) + bf16_bits_to_f32(vl[u] >> 16));
       }
     }
     hsum[t] = s;
@@ -542,7 +555,7 @@ __global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict_
     for (int r = 0; r < 4; ++r) acc[tt][r] = 0.0f;
     ld[tt] = load_sb(dr[tt], kg);
   }
-  const uint4 *ha = hs_hi + nl * rs + kg, *la = hs_lo + nl * rs + kg;
+  const uint4 *ha = hs_hi + nl * rs + kg, *ma = hs_mi + nl * rs + kg, *la = hs_lo + nl * rs + kg;
   for (int b = 0; b < nblk; ++b) {
     const size_t nb = (size_t)(b + 1 < nblk ? b + 1 : b) * kQ4KBlockBytes;
     SbLoad nx[TPW];
@@ -554,7 +567,8 @@ __global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict_
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int jg = 8 * b + 2 * c + hh;
-        const bf16x8 ahi = __builtin_bit_cast(bf16x8, ha[4 * jg]), alo = __builtin_bit_cast(bf16x8, la[4 * jg]);
+        const bf16x8 ahi = __builtin_bit_cast(bf16x8, ha[4 * jg]), ami = __builtin_bit_cast(bf16x8, ma[4 * jg]);
+        const bf16x8 alo = __builtin_bit_cast(bf16x8, la[4 * jg]);
         float hsr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) hsr[r] = hsum[(4 * kg + r) * nsub + jg];
@@ -565,8 +579,9 @@ __global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict_
           const bf16x8 bq = hh ? nibbles8((qd.x >> 4) & 0x0F0F0F0Fu, (qd.y >> 4) & 0x0F0F0F0Fu)
                                : nibbles8(qd.x & 0x0F0F0F0Fu, qd.y & 0x0F0F0F0Fu);
           f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bq, d, 0, 0, 0);
           d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bq, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ami, bq, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bq, d, 0, 0, 0);
           const float sa = hh ? cs.a1 : cs.a0, sb = hh ? cs.b1 : cs.b0;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -615,7 +630,7 @@ static size_t gate_up32_lds_bytes(int hidden) {
   return (size_t)kChunk32 * ((hidden >> 3) + 4) * 16 + (size_t)kChunk32 * (hidden >> 5) * 4;
 }
 static size_t down_lds_bytes(int ffn) {
-  return (size_t)2 * kChunk * ((ffn >> 3) + 4) * 16 + (size_t)kChunk * (ffn >> 5) * 4;
+  return (size_t)3 * kChunk * ((ffn >> 3) + 4) * 16 + (size_t)kChunk * (ffn >> 5) * 4;
 }
 
 bool moe_grouped_fits_lds(int hidden, int ffn) {

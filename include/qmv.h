@@ -241,16 +241,16 @@ int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_
  * Arguments, routing, outputs and error codes as qmv_q4_k_moe, except:
  *   1 <= t <= QMV_MOE_PREFILL_MAX_TOKENS; logits, x_bf16, y, topk_ids and
  *   topk_w hold all t tokens; there is no gather-list output;
- *   16 rows of x (bf16) and of h (two bf16 halves) must fit in
+ *   16 rows of x (bf16) and of h (three bf16 parts) must fit in
  *   QMV_LDS_X_BYTES with their per-32 sums (QMV_ERR_RANGE otherwise): hidden
- *   up to 4608 and ffn up to 2304;
+ *   up to 4608 and ffn up to 1536;
  *   ws, ws_bytes  at least qmv_q4_k_moe_prefill_workspace(...) bytes: the
  *                 routing, the per-expert pair lists, h (t top_k ffn fp32)
  *                 and the per-pair down products (t top_k hidden fp32),
  *                 each 256-byte aligned; it grows linearly with t.
  * The (token, expert) pairs are grouped by expert into chunks of 16, and each
  * chunk's gate/up and down products run on the matrix cores (bf16 MFMA, exact
- * quants; h enters the down product as two bf16 halves that keep about 17
+ * quants; h enters the down product as three bf16 parts that keep about 24
  * bits of it), so each expert's weights are read once per 16 of its tokens.
  * Results are within the same 2e-3 floored relative bound of the exact layer
  * as qmv_q4_k_moe, but not bit-identical to it: the products are summed in

@@ -276,10 +276,10 @@ def test_moe_prefill_validation():
     assert moe_prefill(t=0) == RANGE and moe_prefill(t=65537) == RANGE and moe_prefill(k=9, e=16) == RANGE
     assert moe_prefill(h=300) == SHAPE and moe_prefill(f=0) == SHAPE
     assert moe_prefill(h=10240) == RANGE                      # 16 tokens' activations exceed the LDS stage
-    # the LDS stage limits: hidden 4608 and ffn 2304 fit, one more super-block of either does not
-    assert L.qmv_q4_k_moe_prefill_workspace(1, 4608, 2304, 8, 2) > 0
+    # the LDS stage limits: hidden 4608 and ffn 1536 fit, one more super-block of either does not
+    assert L.qmv_q4_k_moe_prefill_workspace(1, 4608, 1536, 8, 2) > 0
     assert L.qmv_q4_k_moe_prefill_workspace(1, 4864, 256, 8, 2) == 0
-    assert L.qmv_q4_k_moe_prefill_workspace(1, 256, 2560, 8, 2) == 0
+    assert L.qmv_q4_k_moe_prefill_workspace(1, 256, 1792, 8, 2) == 0
     assert moe_prefill(bank=8 * 256 * 144 - 1) == SIZE
     assert moe_prefill(ws=0) == WORKSPACE and moe_prefill(ws_bytes=16) == WORKSPACE
     assert moe_prefill(x=X + 2) == ALIGN and moe_prefill(ws=WS + 128) == ALIGN

@@ -104,3 +104,36 @@ def test_moe_prefill_deterministic(q, dev):
     b = _run(q, dev, bank_d, logits, x, hidden, ffn, ne, tk)
     assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
     assert np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("t,tk", [(300, 4), (600, 4)])
+def test_moe_prefill_all_tokens_on_the_same_experts(q, dev, t, tk):
+    # tied logits: every token picks experts 0 .. k-1 (ties to the lower id), so each of them holds
+    # t pairs in many chunks; 1200 pairs run the 16-pair gate/up, 2400 the 32-pair one
+    hidden, ffn, ne = 512, 256, 16
+    bank = synth.moe_bank(31, ne, hidden, ffn)
+    bank_d = tuple(to_dev(b, dev) for b in bank)
+    logits = np.zeros((t, ne), dtype=np.float32)
+    x = synth.bf16_normal(32, (t, hidden))
+    y, ids, wts = _run(q, dev, bank_d, logits, x, hidden, ffn, ne, tk)
+    assert np.array_equal(ids, np.tile(np.arange(tk, dtype=ids.dtype), (t, 1)))
+    yr, idr, wr = oracle.moe_q4_k(*bank, logits, x, hidden, ffn, ne, tk)
+    assert np.array_equal(ids, idr)
+    assert np.allclose(wts, wr, rtol=2e-6, atol=0)
+    err = oracle.floored_rel_err(y, yr)
+    assert err <= GEMV_TOL, err
+
+
+def test_moe_prefill_many_tokens(q, dev):
+    # 4096 tokens, top-2 of 8 experts: about 1024 pairs per expert, 32 chunks of 32 each
+    t, hidden, ffn, ne, tk = 4096, 256, 256, 8, 2
+    bank = synth.moe_bank(33, ne, hidden, ffn)
+    bank_d = tuple(to_dev(b, dev) for b in bank)
+    logits = synth.moe_logits(33, t, ne)
+    x = synth.bf16_normal(34, (t, hidden))
+    y, ids, wts = _run(q, dev, bank_d, logits, x, hidden, ffn, ne, tk)
+    yr, idr, wr = oracle.moe_q4_k(*bank, logits, x, hidden, ffn, ne, tk)
+    assert np.array_equal(ids, idr)
+    assert np.allclose(wts, wr, rtol=2e-6, atol=0)
+    err = oracle.floored_rel_err(y, yr)
+    assert err <= GEMV_TOL, err
