@@ -8,7 +8,9 @@ guards untouched. The cases span one partial chunk of 16 pairs, experts with
 several chunks, k = 1, k = n_experts (every token takes every expert), and a
 35B-A3B-like layer (hidden 2048, 128 experts, top-8), and that layer at 512
 tokens with sampled tokens checked. The pair counts reach one, two and four
-weight tiles per wave.
+weight tiles per wave, and the 32-pair gate/up form; hidden 2560 at 2048 pairs
+takes the 16-pair form at four tiles per wave (32 rows of x exceed the LDS
+stage there).
 """
 
 import numpy as np
@@ -50,7 +52,8 @@ def _run(q, dev, bank_d, logits, x, hidden, ffn, ne, tk):
 
 
 CASES = [(3, 512, 256, 16, 4, 1), (9, 512, 256, 16, 4, 2), (37, 256, 512, 8, 2, 3), (200, 512, 256, 32, 8, 5),
-         (11, 256, 256, 8, 1, 6), (5, 256, 256, 4, 4, 7), (6, 2048, 768, 128, 8, 4), (256, 512, 256, 32, 8, 8)]
+         (11, 256, 256, 8, 1, 6), (5, 256, 256, 4, 4, 7), (6, 2048, 768, 128, 8, 4), (256, 512, 256, 32, 8, 8),
+         (256, 2560, 256, 8, 8, 9)]
 
 
 @pytest.mark.parametrize("t,hidden,ffn,ne,tk,seed", CASES)
