@@ -269,11 +269,11 @@ def qmm_q4_k_prefill_workspace(m: int, n: int, k: int) -> int:
     return lib.qmm_q4_k_prefill_workspace(m, n, k)
 
 
-def qmm_q4_k_prefill(w, x, n: int, k: int, y=None, ws="auto", stream=None):
+def qmm_q4_k_prefill(w, x, n: int, k: int, y=None, ws=None, stream=None):
     """Y[m, n] = X[m, k] @ bf16(dequant(w))^T on bf16 matrix cores, fp32 accumulation.
 
-    ws: "auto" allocates a workspace when the shape uses the K split, None runs
-    every output tile whole, or a uint8 device tensor to reuse.
+    ws: None allocates the workspace the shape's K split needs (if any), or a
+    uint8 device tensor of at least qmm_q4_k_prefill_workspace(m, n, k) bytes to reuse.
     """
     torch = _torch()
     _dev(w, "w", (torch.uint8,))
@@ -282,9 +282,7 @@ def qmm_q4_k_prefill(w, x, n: int, k: int, y=None, ws="auto", stream=None):
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _dev(y, "y", (torch.float32,))
-    if isinstance(ws, str):
-        if ws != "auto":
-            raise ValueError("ws must be 'auto', None or a tensor")
+    if ws is None:
         need = qmm_q4_k_prefill_workspace(m, n, k)
         ws = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
     if ws is not None:

@@ -34,7 +34,7 @@ __device__ __forceinline__ uint32_t grid_bf16(uint32_t idx) {
 // (one pad granule after every 4 sub-blocks: the 16 lanes of a row reading
 // granule q of 16 consecutive sub-blocks hit 16 distinct bank groups).
 __device__ __forceinline__ int x_slot(int s) { return 4 * s + (s >> 2); }
-__host__ __device__ constexpr int row_granules(int nsub) { return 4 * nsub + nsub / 4; }
+__host__ __device__ constexpr int row_granules(int nsub) { return layout::iq4xs_row_granules(nsub); }
 
 // Pair-interleave one 32-value sub-block: in granules g0..g3 hold x[0..31]; out
 // granule t holds the pairs (x[4t + e], x[16 + 4t + e]) for e < 4.

@@ -39,7 +39,8 @@ using namespace iq4xs;
 constexpr int kDepth = 2;          // units of loads in flight per lane
 
 constexpr int kStageSub = 2;   // sub-blocks per thread per staging round trip
-constexpr size_t kLdsPerCu = 160 * 1024;
+using layout::kLdsPerCu;
+static_assert(layout::kIq4xsTableBytes == (size_t)kTableEntries * 4, "the table's LDS bytes");
 
 // Stage sub-block s of activation row r, pair-interleaved, at xs[r * rg + x_slot(s)].
 __device__ __forceinline__ void stage_one(const uint4 *__restrict__ xg, uint4 *__restrict__ xs, const int t,
@@ -189,14 +190,11 @@ __global__ __launch_bounds__(256) void iq4xs_dequant_kernel(const uint8_t *__res
   }
 }
 
-// dynamic LDS of the GEMV: the staged activations (the table is static, 1 KiB)
-size_t gemv_dyn_lds(int m, int k) { return (size_t)m * row_granules((k >> 8) * 8) * 16; }
-size_t gemv_lds(int m, int k) { return (size_t)kTableEntries * 4 + gemv_dyn_lds(m, k); }
 
 template <int M, int G, int T>
 int launch_mgt(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t s) {
-  static std::atomic<size_t> granted{0};
-  const size_t lds = gemv_dyn_lds(M, k);
+  static LdsGrant granted;
+  const size_t lds = layout::iq4xs_gemv_dyn_lds(M, k);
   if (allow_dynamic_lds(reinterpret_cast<const void *>(&iq4xs_gemv_kernel<M, G, T>), lds, granted,
                         "iq4xs_gemv_kernel lds"))
     return QMV_ERR_HIP;
@@ -211,13 +209,11 @@ int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream
   // workgroup). Once the staged activations leave room for a single workgroup
   // per CU, that workgroup takes 512 threads, so a CU still holds 8 waves.
   if (k <= 8192) return launch_mgt<M, 16, 256>(w, x, y, n, k, s);
-  if (2 * gemv_lds(M, k) > kLdsPerCu) return launch_mgt<M, 32, 512>(w, x, y, n, k, s);
+  if (2 * layout::iq4xs_gemv_lds(M, k) > kLdsPerCu) return launch_mgt<M, 32, 512>(w, x, y, n, k, s);
   return launch_mgt<M, 32, 256>(w, x, y, n, k, s);
 }
 
 }  // namespace
-
-bool iq4xs_fits_lds(int m, int k) { return gemv_lds(m, k) <= (size_t)QMV_LDS_X_BYTES; }
 
 int launch_iq4_xs_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -365,15 +365,13 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_down_kernel(const uint8_t 
   }
 }
 
-size_t gate_up_lds(int t, int hidden) { return (size_t)t * row_granules(hidden >> 5) * 16; }
-size_t down_lds(int pairs, int ffn) { return (size_t)pairs * (size_t)(ffn >> 5) * 9 * 16; }
 
 template <int T>
 int launch_t(const void *w_gate, const void *w_up, const void *w_down, const float *logits, const uint16_t *x,
              float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, void *ws, int hidden, int ffn,
              int n_experts, int top_k, hipStream_t s) {
-  static std::atomic<size_t> granted_a{0}, granted_b{0};
-  const size_t lds_a = gate_up_lds(T, hidden), lds_b = down_lds(T * top_k, ffn);
+  static LdsGrant granted_a, granted_b;
+  const size_t lds_a = layout::iq4xs_moe_gate_up_lds(T, hidden), lds_b = layout::iq4xs_moe_down_lds(T * top_k, ffn);
   if (allow_dynamic_lds(reinterpret_cast<const void *>(&iq4xs_moe_gate_up_kernel<T>), lds_a, granted_a,
                         "iq4xs_moe_gate_up_kernel lds") ||
       allow_dynamic_lds(reinterpret_cast<const void *>(&iq4xs_moe_down_kernel<T>), lds_b, granted_b,
@@ -390,12 +388,6 @@ int launch_t(const void *w_gate, const void *w_up, const void *w_down, const flo
 }
 
 }  // namespace
-
-bool iq4xs_moe_fits_lds(int t, int hidden, int ffn, int top_k) {
-  // static LDS (routing scratch, tables, z buffer, weight tables) stays under 8 KiB
-  const size_t budget = (size_t)QMV_LDS_X_BYTES - 8192;
-  return gate_up_lds(t, hidden) <= budget && down_lds(t * top_k, ffn) <= budget;
-}
 
 int launch_iq4_xs_moe(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
                       const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, void *ws, int t,

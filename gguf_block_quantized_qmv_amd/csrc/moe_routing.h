@@ -31,7 +31,7 @@ struct Table {
   int slot_ntok[kMaxPairs];    // tokens that chose it
   int rank_pair[kMaxPairs];    // gather-list position of routing pair t*K + j (token t, rank j)
 };
-constexpr size_t kTableBytes = 4096;
+constexpr size_t kTableBytes = layout::kMoeTableBytes;
 static_assert(sizeof(Table) <= kTableBytes, "routing tables exceed their workspace slot");
 static_assert(sizeof(Table) % 4 == 0, "routing tables are copied as words");
 

@@ -68,7 +68,7 @@ __device__ __forceinline__ uint32_t unpack_scale_mins(uint32_t s0_3, uint32_t s4
 // 16-byte read per cycle over 64 banks) while the 8 granules of one chunk stay
 // contiguous and are addressed with immediate offsets.
 __device__ __forceinline__ int padded_granule(int gi) { return (gi >> 4) * 17 + (gi & 15); }
-__host__ __device__ constexpr size_t padded_row_granules(int k) { return (size_t)(k >> 7) * 17; }
+__host__ __device__ constexpr size_t padded_row_granules(int k) { return layout::q4k_row_granules(k); }
 
 // ---------------------------------------------------------------------------
 // Per-chunk arithmetic. A lane holds one 64-weight chunk c of a super-block

@@ -43,7 +43,7 @@ constexpr int kFmtQ4K = 0, kFmtQ5K = 1, kFmtQ40 = 2;
 
 template <int M>
 __host__ __device__ constexpr size_t dense_lds_bytes(int k) {
-  return (size_t)M * padded_row_granules(k) * 16 + (size_t)M * (size_t)(k >> 5) * 4;
+  return layout::q4k_x_lds(M, k);
 }
 
 // Activation staging, in two parts so the weight loads can be issued in
@@ -508,7 +508,7 @@ int launch_cfg(const void *w, const uint16_t *x, float *y, int n, int k, hipStre
   if constexpr (F == kFmtQ5K) fn = q5k_gemv_kernel<M, G, D, FULL, NS>, name = "q5k_gemv_kernel";
   else if constexpr (F == kFmtQ40) fn = q40_gemv_kernel<M, G, D, FULL, NS>, name = "q40_gemv_kernel";
   else fn = q4k_gemv_kernel<M, G, D, FULL, NS>, name = "q4k_gemv_kernel";
-  static std::atomic<size_t> granted{0};
+  static LdsGrant granted;
   if (allow_dynamic_lds(reinterpret_cast<const void *>(fn), lds, granted, name)) return QMV_ERR_HIP;
   const int rows = pick_rows(M, n, G, lds);
   const unsigned grid = (unsigned)((n + rows - 1) / rows);

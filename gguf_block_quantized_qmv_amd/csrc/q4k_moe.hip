@@ -481,19 +481,13 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__res
   }
 }
 
-size_t gate_up_lds(int t, int hidden) {
-  return (size_t)t * (padded_row_granules(hidden) * 16 + (size_t)(hidden >> 5) * 4);
-}
-size_t down_lds(int pairs, int ffn) {
-  return (size_t)pairs * ((size_t)(ffn >> 6) * 17 * 16 + (size_t)(ffn >> 5) * 4);
-}
 
 template <int T>
 int launch_t(const void *w_gate, const void *w_up, const void *w_down, const float *logits, const uint16_t *x,
              float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, void *ws, int hidden, int ffn,
              int n_experts, int top_k, hipStream_t s) {
-  static std::atomic<size_t> granted_a{0}, granted_b{0};
-  const size_t lds_a = gate_up_lds(T, hidden), lds_b = down_lds(T * top_k, ffn);
+  static LdsGrant granted_a, granted_b;
+  const size_t lds_a = layout::q4k_moe_gate_up_lds(T, hidden), lds_b = layout::q4k_moe_down_lds(T * top_k, ffn);
   if (allow_dynamic_lds(reinterpret_cast<const void *>(&moe_gate_up_kernel<T>), lds_a, granted_a,
                         "moe_gate_up_kernel lds") ||
       allow_dynamic_lds(reinterpret_cast<const void *>(&moe_down_kernel<T>), lds_b, granted_b, "moe_down_kernel lds"))
@@ -509,18 +503,6 @@ int launch_t(const void *w_gate, const void *w_up, const void *w_down, const flo
 }
 
 }  // namespace
-
-size_t moe_workspace_bytes(int t, int hidden, int ffn, int n_experts, int top_k) {
-  (void)hidden;
-  (void)n_experts;
-  return kTableBytes + (size_t)t * (size_t)top_k * (size_t)ffn * sizeof(float);
-}
-
-bool moe_fits_lds(int t, int hidden, int ffn, int top_k) {
-  // static LDS (routing scratch, tables, z buffer) stays under 4 KiB
-  const size_t budget = (size_t)QMV_LDS_X_BYTES - 4096;
-  return gate_up_lds(t, hidden) <= budget && down_lds(t * top_k, ffn) <= budget;
-}
 
 int launch_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, const float *logits, const uint16_t *x,
                     float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, void *ws, int t, int hidden, int ffn,

@@ -46,36 +46,11 @@ using moe::route_token;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kChunk = 16;   // pairs per chunk (the MFMA's M)
+constexpr int kChunk = layout::kGroupChunk;   // pairs per chunk (the MFMA's M)
 constexpr int kTile = 16;    // weight rows per tile (the MFMA's N)
 constexpr int kWv = 4;       // waves per workgroup; they split the super-blocks
 constexpr int kThr = 64 * kWv;
 
-struct GLayout {
-  size_t ids, wts, cnt, off, choff, chunks, choff32, chunks32, plist, h, z, total;
-};
-
-inline size_t g_round(size_t b) { return (b + 255) & ~(size_t)255; }
-
-inline GLayout g_layout(int t, int hidden, int ffn, int E, int K) {
-  GLayout L;
-  const size_t P = (size_t)t * (size_t)K;
-  const size_t maxch = (P + kChunk - 1) / kChunk + (size_t)E;
-  size_t o = 0;
-  L.ids = o; o += g_round(P * 4);
-  L.wts = o; o += g_round(P * 4);
-  L.cnt = o; o += g_round((size_t)E * 4);
-  L.off = o; o += g_round((size_t)E * 4);
-  L.choff = o; o += g_round(((size_t)E + 1) * 4);
-  L.chunks = o; o += g_round(maxch * 8);
-  L.choff32 = o; o += g_round(((size_t)E + 1) * 4);
-  L.chunks32 = o; o += g_round(((P + 31) / 32 + (size_t)E) * 8);
-  L.plist = o; o += g_round(P * 4);
-  L.h = o; o += g_round(P * (size_t)ffn * 4);
-  L.z = o; o += g_round(P * (size_t)hidden * 4);
-  L.total = o;
-  return L;
-}
 
 // Eight nibbles (bytes 0..3 of lo, then of hi) as eight exact bf16 integers.
 __device__ __forceinline__ bf16x8 nibbles8(const uint32_t lo, const uint32_t hi) {
@@ -336,7 +311,7 @@ __global__ __launch_bounds__(kThr) void g_gate_up_kernel(const uint8_t *__restri
 // over all of K, and two MFMA row blocks (pairs 0..15 and 16..31) per
 // converted weight fragment, so each expert's weights are read once per 32 of
 // its pairs and each conversion feeds two products.
-constexpr int kChunk32 = 32;
+constexpr int kChunk32 = layout::kGroupChunk32;
 constexpr int kWv32 = 8;
 constexpr int kThr32 = 64 * kWv32;
 
@@ -619,24 +594,6 @@ __global__ __launch_bounds__(kThr) void g_combine_kernel(const float *__restrict
 
 }  // namespace
 
-size_t moe_grouped_workspace_bytes(int t, int hidden, int ffn, int n_experts, int top_k) {
-  return g_layout(t, hidden, ffn, n_experts, top_k).total;
-}
-
-static size_t gate_up_lds_bytes(int hidden) {
-  return (size_t)kChunk * ((hidden >> 3) + 4) * 16 + (size_t)kChunk * (hidden >> 5) * 4;
-}
-static size_t gate_up32_lds_bytes(int hidden) {
-  return (size_t)kChunk32 * ((hidden >> 3) + 4) * 16 + (size_t)kChunk32 * (hidden >> 5) * 4;
-}
-static size_t down_lds_bytes(int ffn) {
-  return (size_t)3 * kChunk * ((ffn >> 3) + 4) * 16 + (size_t)kChunk * (ffn >> 5) * 4;
-}
-
-bool moe_grouped_fits_lds(int hidden, int ffn) {
-  return gate_up_lds_bytes(hidden) <= (size_t)QMV_LDS_X_BYTES && down_lds_bytes(ffn) <= (size_t)QMV_LDS_X_BYTES;
-}
-
 namespace {
 
 // Tiles per wave from the number of pairs P. Measured on the 35B-A3B layer
@@ -651,8 +608,8 @@ template <int TPW>
 int launch_gate_up(const uint8_t *w_gate, const uint8_t *w_up, const uint16_t *x, const int *cnt, const int *off,
                    const int *choff, const int2 *chunks, const int *plist, float *h, int hidden, int ffn, int E,
                    int K, unsigned maxch, hipStream_t s) {
-  static std::atomic<size_t> granted{0};
-  const size_t lds = gate_up_lds_bytes(hidden);
+  static LdsGrant granted;
+  const size_t lds = layout::group_gate_up_lds(kChunk, hidden);
   if (allow_dynamic_lds(reinterpret_cast<const void *>(&g_gate_up_kernel<TPW>), lds, granted, "g_gate_up_kernel lds"))
     return QMV_ERR_HIP;
   return launch_kernel("g_gate_up_kernel", g_gate_up_kernel<TPW>,
@@ -664,8 +621,8 @@ template <int TPW>
 int launch_gate_up32(const uint8_t *w_gate, const uint8_t *w_up, const uint16_t *x, const int *cnt, const int *off,
                      const int *choff, const int2 *chunks, const int *plist, float *h, int hidden, int ffn, int E,
                      int K, unsigned maxch, hipStream_t s) {
-  static std::atomic<size_t> granted{0};
-  const size_t lds = gate_up32_lds_bytes(hidden);
+  static LdsGrant granted;
+  const size_t lds = layout::group_gate_up_lds(kChunk32, hidden);
   if (allow_dynamic_lds(reinterpret_cast<const void *>(&g_gate_up32_kernel<TPW>), lds, granted,
                         "g_gate_up32_kernel lds"))
     return QMV_ERR_HIP;
@@ -678,8 +635,8 @@ template <int TPW>
 int launch_down(const uint8_t *w_down, const int *cnt, const int *off, const int *choff, const int2 *chunks,
                 const int *plist, const float *h, float *z, int hidden, int ffn, int E, unsigned maxch,
                 hipStream_t s) {
-  static std::atomic<size_t> granted{0};
-  const size_t lds = down_lds_bytes(ffn);
+  static LdsGrant granted;
+  const size_t lds = layout::group_down_lds(ffn);
   if (allow_dynamic_lds(reinterpret_cast<const void *>(&g_down_kernel<TPW>), lds, granted, "g_down_kernel lds"))
     return QMV_ERR_HIP;
   return launch_kernel("g_down_kernel", g_down_kernel<TPW>, dim3((unsigned)(hidden / (kWv * kTile * TPW)), maxch),
@@ -692,7 +649,7 @@ int launch_q4_k_moe_grouped(const void *w_gate, const void *w_up, const void *w_
                             const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, void *ws, int t,
                             int hidden, int ffn, int n_experts, int top_k, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const GLayout L = g_layout(t, hidden, ffn, n_experts, top_k);
+  const layout::GroupLayout L = layout::group_layout(t, hidden, ffn, n_experts, top_k);
   uint8_t *wb = static_cast<uint8_t *>(ws);
   int *ids = reinterpret_cast<int *>(wb + L.ids);
   float *wts = reinterpret_cast<float *>(wb + L.wts);
@@ -716,7 +673,7 @@ int launch_q4_k_moe_grouped(const void *w_gate, const void *w_up, const void *w_
   if (!rc) rc = launch_kernel("g_chunks_kernel", g_chunks_kernel<kChunk>, dim3(1), dim3(kThr), 0, s, cnt, choff,
                               chunks, n_experts);
   // gate/up in chunks of 32 where there are enough pairs and 32 rows of x fit in LDS
-  const bool wide = P >= 2048 && gate_up32_lds_bytes(hidden) <= (size_t)QMV_LDS_X_BYTES;
+  const bool wide = P >= 2048 && layout::group_gate_up_lds(kChunk32, hidden) <= layout::kLdsBudget;
   if (!rc && wide)
     rc = launch_kernel("g_chunks_kernel", g_chunks_kernel<kChunk32>, dim3(1), dim3(kThr), 0, s, cnt, choff32,
                        chunks32, n_experts);

@@ -89,8 +89,8 @@ struct StepRegs {
 
 // Rows past M read row 0 of X and rows past N row 0 of W: they only feed
 // outputs that are never stored. Steps past K read the last step. X granules
-// are addressed by 32-bit granule index (X is at most 2^31 granules: the
-// argument checks bound M * K).
+// are addressed by a 32-bit granule index: the argument checks bound the
+// M * K / 8 granules of X to 2^32 - 1.
 template <class C>
 __device__ __forceinline__ void load_step(const int pt, const uint4 *__restrict__ xg, const int m0, const int M,
                                           const int gpr, const uint8_t *__restrict__ w_rowp, const int nsteps, int s,
@@ -346,73 +346,19 @@ __global__ __launch_bounds__(256) void q4k_prefill_reduce_kernel(const float *__
   if (gcol + 3 < N) yr[gcol + 3] = acc.w;
 }
 
-using PrefillCfg = Cfg<128, 128, 4>;
-
-// Workgroups of the GEMM kernel resident at once on the current device (0 if
-// the runtime cannot say), cached per device.
-int resident_capacity() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int c = cache[dev].load(std::memory_order_relaxed);
-  if (c > 0) return c;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&q4k_prefill_ws_kernel<PrefillCfg>),
-                                                   2 * kThreads, PrefillCfg::kLdsBytes) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  c = per_cu * cus;
-  cache[dev].store(c, std::memory_order_relaxed);
-  return c;
-}
-
-// The split of an m x n x k product: t_main whole tiles (a multiple of the
-// resident capacity), then r_tiles tiles in `splits` K parts each so that the
-// last round fills the device. splits == 0: every tile whole.
-struct Plan {
-  int t_main, r_tiles, splits;
-};
-Plan plan_for(int m, int n, int k) {
-  using C = PrefillCfg;
-  const int tiles = ((n + C::BN - 1) / C::BN) * ((m + C::BM - 1) / C::BM);
-  const int cap = resident_capacity();
-  Plan p{tiles, 0, 0};
-  if (cap <= 0) return p;
-  const int t_main = tiles / cap * cap, r = tiles - t_main;
-  if (r == 0) return p;
-  const int nkb = k / 256;   // parts are runs of whole K blocks
-  const int most = cap / r < nkb ? cap / r : nkb;
-  if (most < 2) return p;
-  // the longest part decides the round; the fewest parts that reach it keep
-  // the partial sums (and the second launch's reads) smallest
-  const int longest = (nkb + most - 1) / most;
-  int splits = (nkb + longest - 1) / longest;
-  if (splits < 2) splits = 2;
-  return Plan{t_main, r, splits};
-}
-
-size_t plan_bytes(const Plan &p) {
-  return (size_t)p.splits * p.r_tiles * PrefillCfg::BM * PrefillCfg::BN * sizeof(float);
-}
+using PrefillCfg = Cfg<layout::kPrefillTileM, layout::kPrefillTileN, 4>;
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int m, int n, int k) { return plan_bytes(plan_for(m, n, k)); }
-
-int launch_q4_k_prefill(const void *w, const uint16_t *x, float *y, void *ws, size_t ws_bytes, int m, int n, int k,
-                        void *stream) {
+int launch_q4_k_prefill(const void *w, const uint16_t *x, float *y, void *ws, int m, int n, int k, void *stream) {
   using C = PrefillCfg;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  static std::atomic<size_t> granted{0};
+  static LdsGrant granted;
   if (allow_dynamic_lds(reinterpret_cast<const void *>(&q4k_prefill_ws_kernel<C>), C::kLdsBytes, granted,
                         "q4k_prefill_ws_kernel lds"))
     return QMV_ERR_HIP;
-  const int tiles = ((n + C::BN - 1) / C::BN) * ((m + C::BM - 1) / C::BM);
-  Plan p{tiles, 0, 0};
-  if (ws) {
-    const Plan q = plan_for(m, n, k);
-    if (q.splits > 0 && ws_bytes >= plan_bytes(q)) p = q;
-  }
+  // the checks have bounded the tiles and required the plan's workspace
+  const layout::PrefillPlan p = layout::prefill_plan(m, n, k);
   float *part = static_cast<float *>(ws);
   const int blocks = p.t_main + p.r_tiles * p.splits;
   int rc = launch_kernel("q4k_prefill_ws_kernel", q4k_prefill_ws_kernel<C>, dim3((unsigned)blocks),

@@ -398,7 +398,7 @@ template <int M, int G, int D, int NS>
 int q6_launch(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
   const size_t lds = q6_lds_bytes<M>(k);
   auto *fn = q6k_gemv_kernel<M, G, D, NS>;
-  static std::atomic<size_t> granted{0};
+  static LdsGrant granted;
   if (allow_dynamic_lds(reinterpret_cast<const void *>(fn), lds, granted, "q6k_gemv_kernel")) return QMV_ERR_HIP;
   const int rows = q6_pick_rows(M, n, G, lds);
   const unsigned grid = (unsigned)((n + rows - 1) / rows);

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void q80_dequant_kernel(const uint8_t *__restr
 template <int M>
 int launch_m(const void *w, const float *x, float *y, int n, int k, hipStream_t s) {
   const size_t lds = (size_t)M * (size_t)k * 4;
-  static std::atomic<size_t> granted{0};
+  static LdsGrant granted;
   if (allow_dynamic_lds(reinterpret_cast<const void *>(&q80_gemv_kernel<M>), lds, granted, "q80_gemv_kernel lds"))
     return QMV_ERR_HIP;
   const int rows_per_group = kWaves * kRowsPerWave;

@@ -1,13 +1,17 @@
 // C ABI of the block-quantized matrix-vector library: argument validation and
-// dispatch. Pure host code with no HIP call of its own, so every validation
-// path runs (and is tested) on machines without a GPU. See include/qmv.h for
-// the contract of each entry point.
+// dispatch. Pure host code: it calls no HIP function and reads no device
+// property, so a call's checks -- and the sizes and plans they take from
+// qmv_layout.h -- depend on its arguments alone. The CPU tests link this file
+// with stand-in launchers and no HIP runtime at all, under the address and
+// undefined-behaviour sanitizers. See include/qmv.h for the contract of each
+// entry point.
 #include "../../include/qmv.h"
 
 #include <stdint.h>
 #include <stdio.h>
 
 #include "qmv_internal.h"
+#include "qmv_layout.h"
 
 namespace qmv {
 
@@ -54,6 +58,7 @@ int check_matrix(const void *w, size_t w_bytes, int n, int k, int block_weights,
                  uintptr_t w_align) {
   if (!w) return QMV_ERR_NULL;
   if (n <= 0 || k <= 0 || k % block_weights != 0) return QMV_ERR_SHAPE;
+  if (!qmv::layout::matrix_in_range(n, k)) return QMV_ERR_RANGE;
   const size_t expect = matrix_bytes(n, k, block_weights, block_bytes);
   if (expect == 0 || w_bytes != expect) return QMV_ERR_SIZE;
   if (!aligned(w, w_align)) return QMV_ERR_ALIGN;
@@ -70,8 +75,8 @@ bool moe_args_ok(MoeFormat f, int t, int hidden, int ffn, int n_experts, int top
   return t >= 1 && t <= QMV_MOE_MAX_TOKENS && n_experts >= 1 && n_experts <= QMV_MOE_MAX_EXPERTS && top_k >= 1 &&
          top_k <= QMV_MOE_MAX_TOP_K && top_k <= n_experts && hidden > 0 && ffn > 0 && hidden % 256 == 0 &&
          ffn % 256 == 0 &&
-         (f == MoeFormat::kQ4K ? qmv::moe_fits_lds(t, hidden, ffn, top_k)
-                               : qmv::iq4xs_moe_fits_lds(t, hidden, ffn, top_k));
+         (f == MoeFormat::kQ4K ? qmv::layout::q4k_moe_fits_lds(t, hidden, ffn, top_k)
+                               : qmv::layout::iq4xs_moe_fits_lds(t, hidden, ffn, top_k));
 }
 
 // Host-side checks of a routed-expert decode call of t tokens.
@@ -95,7 +100,7 @@ int moe_check(MoeFormat f, const void *w_gate, const void *w_up, const void *w_d
       !aligned(logits, 4) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(pairs, 4) ||
       !aligned(ws, 256))
     return QMV_ERR_ALIGN;
-  const size_t need = qmv::moe_workspace_bytes(t, hidden, ffn, n_experts, top_k);
+  const size_t need = qmv::layout::moe_workspace(t, ffn, top_k);
   if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
 
   // every output (and the workspace) must be disjoint from every input and from each other
@@ -163,7 +168,7 @@ int qmv_q8_0(const void *w, size_t w_bytes, const float *x, float *y, int m, int
   if (m < 1 || m > QMV_MAX_ROWS) return QMV_ERR_RANGE;
   int rc = check_matrix(w, w_bytes, n, k, 32, 34, 4);
   if (rc) return rc;
-  if ((size_t)m * (size_t)k * 4 > QMV_LDS_X_BYTES) return QMV_ERR_RANGE;
+  if (qmv::layout::q80_x_lds(m, k) > qmv::layout::kLdsBudget) return QMV_ERR_RANGE;
   if (!aligned(x, 16) || !aligned(y, 4)) return QMV_ERR_ALIGN;
   const size_t xb = (size_t)m * k * 4, yb = (size_t)m * n * 4;
   if (overlap(y, yb, w, w_bytes) || overlap(y, yb, x, xb)) return QMV_ERR_ALIAS;
@@ -175,7 +180,7 @@ int qmv_q4_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, in
   if (m < 1 || m > QMV_MAX_ROWS) return QMV_ERR_RANGE;
   int rc = check_matrix(w, w_bytes, n, k, 256, 144, 16);
   if (rc) return rc;
-  if ((size_t)m * ((size_t)(k / 128) * 17 * 16 + (size_t)(k / 32) * 4) > QMV_LDS_X_BYTES) return QMV_ERR_RANGE;
+  if (qmv::layout::q4k_x_lds(m, k) > qmv::layout::kLdsBudget) return QMV_ERR_RANGE;
   if (!aligned(x_bf16, 16) || !aligned(y, 4)) return QMV_ERR_ALIGN;
   const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 4;
   if (overlap(y, yb, w, w_bytes) || overlap(y, yb, x_bf16, xb)) return QMV_ERR_ALIAS;
@@ -187,7 +192,7 @@ int qmv_iq4_xs(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, 
   if (m < 1 || m > QMV_MAX_ROWS) return QMV_ERR_RANGE;
   int rc = check_matrix(w, w_bytes, n, k, 256, 136, 8);
   if (rc) return rc;
-  if (!qmv::iq4xs_fits_lds(m, k)) return QMV_ERR_RANGE;
+  if (qmv::layout::iq4xs_gemv_lds(m, k) > qmv::layout::kLdsBudget) return QMV_ERR_RANGE;
   if (!aligned(x_bf16, 16) || !aligned(y, 4)) return QMV_ERR_ALIGN;
   const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 4;
   if (overlap(y, yb, w, w_bytes) || overlap(y, yb, x_bf16, xb)) return QMV_ERR_ALIAS;
@@ -196,7 +201,7 @@ int qmv_iq4_xs(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, 
 
 size_t qmv_q4_k_moe_workspace(int t, int hidden, int ffn, int n_experts, int top_k) {
   if (!moe_args_ok(MoeFormat::kQ4K, t, hidden, ffn, n_experts, top_k)) return 0;
-  return qmv::moe_workspace_bytes(t, hidden, ffn, n_experts, top_k);
+  return qmv::layout::moe_workspace(t, ffn, top_k);
 }
 
 int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes, const float *logits,
@@ -209,9 +214,9 @@ int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_
 size_t qmv_q4_k_moe_prefill_workspace(int t, int hidden, int ffn, int n_experts, int top_k) {
   if (t < 1 || t > QMV_MOE_PREFILL_MAX_TOKENS || n_experts < 1 || n_experts > QMV_MOE_MAX_EXPERTS || top_k < 1 ||
       top_k > QMV_MOE_MAX_TOP_K || top_k > n_experts || hidden <= 0 || ffn <= 0 || hidden % 256 || ffn % 256 ||
-      !qmv::moe_grouped_fits_lds(hidden, ffn))
+      !qmv::layout::group_fits_lds(hidden, ffn))
     return 0;
-  return qmv::moe_grouped_workspace_bytes(t, hidden, ffn, n_experts, top_k);
+  return qmv::layout::group_layout(t, hidden, ffn, n_experts, top_k).total;
 }
 
 int qmv_q4_k_moe_prefill(const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes,
@@ -223,7 +228,7 @@ int qmv_q4_k_moe_prefill(const void *w_gate, const void *w_up, const void *w_dow
       top_k > QMV_MOE_MAX_TOP_K || top_k > n_experts)
     return QMV_ERR_RANGE;
   if (hidden <= 0 || ffn <= 0 || hidden % 256 || ffn % 256) return QMV_ERR_SHAPE;
-  if (!qmv::moe_grouped_fits_lds(hidden, ffn)) return QMV_ERR_RANGE;
+  if (!qmv::layout::group_fits_lds(hidden, ffn)) return QMV_ERR_RANGE;
   size_t expert_bytes = 0, bank = 0;
   if (!mul_size((size_t)ffn, (size_t)(hidden / 256) * 144, &expert_bytes) ||
       !mul_size(expert_bytes, (size_t)n_experts, &bank) || bank_bytes != bank)
@@ -231,7 +236,7 @@ int qmv_q4_k_moe_prefill(const void *w_gate, const void *w_up, const void *w_dow
   if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(x_bf16, 16) ||
       !aligned(logits, 4) || !aligned(y, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(ws, 256))
     return QMV_ERR_ALIGN;
-  const size_t need = qmv::moe_grouped_workspace_bytes(t, hidden, ffn, n_experts, top_k);
+  const size_t need = qmv::layout::group_layout(t, hidden, ffn, n_experts, top_k).total;
   if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
   const size_t ta = (size_t)t, yb = ta * hidden * 4, idb = ta * top_k * 4;
   const void *in_p[] = {w_gate, w_up, w_down, logits, x_bf16};
@@ -250,7 +255,7 @@ int qmv_q4_k_moe_prefill(const void *w_gate, const void *w_up, const void *w_dow
 
 size_t qmv_iq4_xs_moe_workspace(int t, int hidden, int ffn, int n_experts, int top_k) {
   if (!moe_args_ok(MoeFormat::kIQ4XS, t, hidden, ffn, n_experts, top_k)) return 0;
-  return qmv::moe_workspace_bytes(t, hidden, ffn, n_experts, top_k);
+  return qmv::layout::moe_workspace(t, ffn, top_k);
 }
 
 int qmv_iq4_xs_moe(const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes, const float *logits,
@@ -261,8 +266,8 @@ int qmv_iq4_xs_moe(const void *w_gate, const void *w_up, const void *w_down, siz
 }
 
 size_t qmm_q4_k_prefill_workspace(int m, int n, int k) {
-  if (m < 1 || n < 1 || k < 256 || k % 256) return 0;
-  return qmv::prefill_workspace_bytes(m, n, k);
+  if (m < 1 || n < 1 || k < 256 || k % 256 || !qmv::layout::prefill_in_range(m, n, k)) return 0;
+  return qmv::layout::prefill_plan_bytes(qmv::layout::prefill_plan(m, n, k));
 }
 
 int qmm_q4_k_prefill(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, int m, int n, int k, void *ws,
@@ -271,17 +276,16 @@ int qmm_q4_k_prefill(const void *w, size_t w_bytes, const uint16_t *x_bf16, floa
   if (m < 1) return QMV_ERR_RANGE;
   int rc = check_matrix(w, w_bytes, n, k, 256, 144, 16);
   if (rc) return rc;
+  if (!qmv::layout::prefill_in_range(m, n, k)) return QMV_ERR_RANGE;
   if (!aligned(x_bf16, 16) || !aligned(y, 16) || !aligned(ws, 256)) return QMV_ERR_ALIGN;
-  size_t xb = 0, yb = 0;
-  if (!mul_size((size_t)m, (size_t)k * 2, &xb) || !mul_size((size_t)m, (size_t)n * 4, &yb)) return QMV_ERR_RANGE;
+  // no overflow: m * k / 8 <= 2^32 and the tile count (so m * n / 2^14) < 2^31
+  const size_t xb = (size_t)m * (size_t)k * 2, yb = (size_t)m * (size_t)n * 4;
+  const size_t need = qmv::layout::prefill_plan_bytes(qmv::layout::prefill_plan(m, n, k));
   if (overlap(y, yb, w, w_bytes) || overlap(y, yb, x_bf16, xb)) return QMV_ERR_ALIAS;
-  if (ws) {
-    const size_t need = qmv::prefill_workspace_bytes(m, n, k);
-    if (ws_bytes < need) return QMV_ERR_WORKSPACE;
-    const size_t wsb = need ? need : ws_bytes;
-    if (overlap(ws, wsb, w, w_bytes) || overlap(ws, wsb, x_bf16, xb) || overlap(ws, wsb, y, yb)) return QMV_ERR_ALIAS;
-  }
-  return qmv::launch_q4_k_prefill(w, x_bf16, y, ws, ws_bytes, m, n, k, stream);
+  if (need && (!ws || ws_bytes < need)) return QMV_ERR_WORKSPACE;
+  if (need && (overlap(ws, need, w, w_bytes) || overlap(ws, need, x_bf16, xb) || overlap(ws, need, y, yb)))
+    return QMV_ERR_ALIAS;
+  return qmv::launch_q4_k_prefill(w, x_bf16, y, need ? ws : nullptr, m, n, k, stream);
 }
 
 int qmv_q5_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, int m, int n, int k, void *stream) {
@@ -289,7 +293,7 @@ int qmv_q5_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, in
   if (m < 1 || m > QMV_MAX_ROWS) return QMV_ERR_RANGE;
   int rc = check_matrix(w, w_bytes, n, k, 256, 176, 16);
   if (rc) return rc;
-  if ((size_t)m * ((size_t)(k / 128) * 17 * 16 + (size_t)(k / 32) * 4) > QMV_LDS_X_BYTES) return QMV_ERR_RANGE;
+  if (qmv::layout::q4k_x_lds(m, k) > qmv::layout::kLdsBudget) return QMV_ERR_RANGE;
   if (!aligned(x_bf16, 16) || !aligned(y, 4)) return QMV_ERR_ALIGN;
   const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 4;
   if (overlap(y, yb, w, w_bytes) || overlap(y, yb, x_bf16, xb)) return QMV_ERR_ALIAS;
@@ -311,7 +315,7 @@ int qmv_q4_0(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, in
   if (k <= 0 || k % 256) return QMV_ERR_SHAPE;   // the kernel steps over groups of eight blocks
   int rc = check_matrix(w, w_bytes, n, k, 32, 18, 16);
   if (rc) return rc;
-  if ((size_t)m * ((size_t)(k / 128) * 17 * 16 + (size_t)(k / 32) * 4) > QMV_LDS_X_BYTES) return QMV_ERR_RANGE;
+  if (qmv::layout::q4k_x_lds(m, k) > qmv::layout::kLdsBudget) return QMV_ERR_RANGE;
   if (!aligned(x_bf16, 16) || !aligned(y, 4)) return QMV_ERR_ALIGN;
   const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 4;
   if (overlap(y, yb, w, w_bytes) || overlap(y, yb, x_bf16, xb)) return QMV_ERR_ALIAS;
@@ -332,7 +336,7 @@ int qmv_q6_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, in
   if (m < 1 || m > QMV_MAX_ROWS) return QMV_ERR_RANGE;
   int rc = check_matrix(w, w_bytes, n, k, 256, 210, 16);
   if (rc) return rc;
-  if ((size_t)m * ((size_t)k * 2 + (size_t)(k / 16) * 4) > QMV_LDS_X_BYTES) return QMV_ERR_RANGE;
+  if (qmv::layout::q6k_x_lds(m, k) > qmv::layout::kLdsBudget) return QMV_ERR_RANGE;
   if (!aligned(x_bf16, 16) || !aligned(y, 4)) return QMV_ERR_ALIGN;
   const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 4;
   if (overlap(y, yb, w, w_bytes) || overlap(y, yb, x_bf16, xb)) return QMV_ERR_ALIAS;

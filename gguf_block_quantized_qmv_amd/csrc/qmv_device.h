@@ -7,6 +7,8 @@
 #include <atomic>
 #include <tuple>
 
+#include "qmv_layout.h"
+
 namespace qmv {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -108,18 +110,35 @@ inline int launch_kernel(const char *name, void (*kernel)(Params...), dim3 grid,
   return 0;
 }
 
-// Allow `bytes` of dynamic LDS for `kernel` (needed above 64 KiB). The largest
-// value granted so far is remembered per call site, so the attribute is set
-// once per size increase rather than on every launch.
-inline int allow_dynamic_lds(const void *kernel, size_t bytes, std::atomic<size_t> &granted, const char *name) {
-  if (bytes <= 65536 || bytes <= granted.load(std::memory_order_relaxed)) return 0;
-  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+// Dynamic-LDS sizes already granted to one kernel, per device (the attribute
+// belongs to the kernel on the device that is current when it is set).
+struct LdsGrant {
+  static constexpr int kDevices = 64;
+  std::atomic<size_t> dev[kDevices] = {};
+};
+
+// Allow `bytes` of dynamic LDS for `kernel` on the current device (needed above
+// 64 KiB). The largest value granted so far is remembered per call site and
+// device, so the attribute is set once per size increase rather than on every
+// launch. This cache never changes what a kernel computes.
+inline int allow_dynamic_lds(const void *kernel, size_t bytes, LdsGrant &granted, const char *name) {
+  if (bytes <= 65536) return 0;
+  int d = 0;
+  hipError_t e = hipGetDevice(&d);
+  if (e == hipSuccess && (d < 0 || d >= LdsGrant::kDevices)) e = hipErrorInvalidDevice;
   if (e != hipSuccess) {
     set_error_detail(name, (int)e, hipGetErrorString(e));
     return -8;
   }
-  size_t cur = granted.load(std::memory_order_relaxed);
-  while (cur < bytes && !granted.compare_exchange_weak(cur, bytes)) {
+  std::atomic<size_t> &g = granted.dev[d];
+  if (bytes <= g.load(std::memory_order_relaxed)) return 0;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) {
+    set_error_detail(name, (int)e, hipGetErrorString(e));
+    return -8;
+  }
+  size_t cur = g.load(std::memory_order_relaxed);
+  while (cur < bytes && !g.compare_exchange_weak(cur, bytes)) {
   }
   return 0;
 }

@@ -1,6 +1,7 @@
 // Internal launch interface between the C-ABI layer (qmv_api.cpp, pure host
 // code) and the HIP kernel files. Arguments are already validated when these
-// are called; each returns QMV_OK or QMV_ERR_HIP.
+// are called; each returns QMV_OK or QMV_ERR_HIP. The sizes both sides use
+// are in qmv_layout.h.
 #pragma once
 
 #include <stddef.h>
@@ -16,7 +17,6 @@ int launch_q5_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, i
 int launch_q6_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
 int launch_q4_0_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
 int launch_iq4_xs_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
-bool iq4xs_fits_lds(int m, int k);
 int launch_dequant_iq4_xs(const void *w, float *out, int n, int k, void *stream);
 int launch_dequant_q4_k(const void *w, void *out, bool bf16, int n, int k, void *stream);
 int launch_dequant_q5_k(const void *w, float *out, int n, int k, void *stream);
@@ -26,19 +26,12 @@ int launch_dequant_q8_0(const void *w, float *out, int n, int k, void *stream);
 int launch_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
                     const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs,
                     void *ws, int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
-size_t moe_workspace_bytes(int t, int hidden, int ffn, int n_experts, int top_k);
-size_t moe_grouped_workspace_bytes(int t, int hidden, int ffn, int n_experts, int top_k);
-bool moe_grouped_fits_lds(int hidden, int ffn);
 int launch_q4_k_moe_grouped(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
                             const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, void *ws, int t,
                             int hidden, int ffn, int n_experts, int top_k, void *stream);
-bool moe_fits_lds(int t, int hidden, int ffn, int top_k);
 int launch_iq4_xs_moe(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
                       const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, void *ws, int t,
                       int hidden, int ffn, int n_experts, int top_k, void *stream);
-bool iq4xs_moe_fits_lds(int t, int hidden, int ffn, int top_k);
-int launch_q4_k_prefill(const void *w, const uint16_t *x, float *y, void *ws, size_t ws_bytes, int m, int n, int k,
-                        void *stream);
-size_t prefill_workspace_bytes(int m, int n, int k);
+int launch_q4_k_prefill(const void *w, const uint16_t *x, float *y, void *ws, int m, int n, int k, void *stream);
 
 }  // namespace qmv

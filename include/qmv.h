@@ -16,20 +16,26 @@
  * ---------------------------------------
  *  - Pointers named w*, x*, y*, out*, logits, topk_*, pairs, ws are DEVICE
  *    pointers (HIP device memory of the current device). The caller owns every
- *    buffer; the library never allocates, frees or synchronises, and keeps no
- *    mutable global state, so calls from several host threads are safe.
+ *    buffer; the library never allocates, frees or synchronises. Its only
+ *    process state never affects a result: per kernel and device, the largest
+ *    dynamic-LDS size already granted (an atomic, so the attribute is set once),
+ *    and per host thread the text behind qmv_last_error(). Calls from several
+ *    host threads are safe.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
  *    work is enqueued on it asynchronously; a return of QMV_OK means the work
  *    was enqueued, not that it finished.
- *  - Every argument is validated on the host before any HIP call is made.
- *    Invalid arguments return a negative QMV_ERR_* code and touch no memory.
+ *  - Every argument is validated on the host before any HIP call is made; the
+ *    checks, workspace sizes and launch plans depend on the arguments alone,
+ *    never on a device query. Invalid arguments return a negative QMV_ERR_*
+ *    code and touch no memory.
  *    A failed launch returns QMV_ERR_HIP. Faults during execution surface as
  *    HIP errors on the caller's next synchronisation.
  *  - Quantized matrices are row-major: row n (one output feature) is the
  *    contiguous run of its K/QK blocks along the input dimension K, rows follow
  *    each other with no padding. `w_bytes` must equal the exact byte size of
  *    that layout; any other value (a truncated or oversized buffer) is
- *    QMV_ERR_SIZE.
+ *    QMV_ERR_SIZE. n <= QMV_MAX_MATRIX_ROWS, k <= QMV_MAX_MATRIX_K and
+ *    n * k <= 2^40, else QMV_ERR_RANGE.
  *  - bf16 values travel as uint16_t bit patterns. Outputs are fp32.
  *  - Outputs must not overlap any input (QMV_ERR_ALIAS).
  *  - Results are bitwise deterministic from run to run. For the GEMV entry
@@ -74,6 +80,12 @@ extern "C" {
 #define QMV_MOE_MAX_EXPERTS 256
 #define QMV_MOE_MAX_TOP_K   8
 #define QMV_MOE_PREFILL_MAX_TOKENS 65536 /* tokens per qmv_q4_k_moe_prefill call */
+#define QMV_MAX_MATRIX_ROWS (1 << 30)      /* n of any quantized matrix (QMV_ERR_RANGE above) */
+#define QMV_MAX_MATRIX_K    (1 << 24)      /* k of any quantized matrix; also n * k <= 2^40 */
+
+/* Diagnostics. The memra README's recent-fixes list holds its engine to
+ * contextual errors instead of crashes on malformed or truncated input; these
+ * three calls give a caller that context. */
 
 /* Library version as 10000*major + 100*minor + patch. */
 int qmv_version(void);
@@ -199,7 +211,10 @@ int qmv_iq4_xs(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
 
 /*
  * Workspace bytes qmv_q4_k_moe needs for t tokens (0 if an argument is out of
- * range). The caller allocates it in device memory, 256-byte aligned.
+ * range): 4 KiB of routing tables, then h as fp32 [t * top_k][ffn]. The caller
+ * allocates it in device memory, 256-byte aligned. (The pages describe no
+ * kernel interface; a caller-owned workspace is this library's own convention,
+ * so that the library never allocates.)
  */
 size_t qmv_q4_k_moe_workspace(int t, int hidden, int ffn, int n_experts, int top_k);
 
@@ -291,11 +306,14 @@ int qmv_iq4_xs_moe(const void *w_gate, const void *w_up, const void *w_down, siz
                    int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
 
 /*
- * Workspace bytes qmm_q4_k_prefill can use for an m x n x k product on the
- * current device: 0 when the output tiles divide evenly over the workgroups
- * the device holds at once (or too few K blocks to split). Otherwise the tiles
- * past the largest multiple of that count are split along K so that the last
- * round fills the device, and this many bytes hold their parts' fp32 sums.
+ * Workspace bytes qmm_q4_k_prefill needs for an m x n x k product (0 if none,
+ * or if an argument is out of range). It depends on the shape alone. The
+ * 128 x 128 output tiles run on 512 workgroup slots (a 256-CU MI355X at two
+ * workgroups per CU); when the tile count is not a multiple of 512, the tiles
+ * past the last multiple run as parts of whole 256-value K blocks so that the
+ * last round fills the slots, and this many bytes hold the parts' fp32 sums.
+ * (A caller-owned workspace is this library's own convention: the pages
+ * describe no kernel interface.)
  */
 size_t qmm_q4_k_prefill_workspace(int m, int n, int k);
 
@@ -304,15 +322,17 @@ size_t qmm_q4_k_prefill_workspace(int m, int n, int k);
  *   w       [n rows][k/256 blocks] Q4_K, 16-byte aligned; w_bytes == n*(k/256)*144
  *   x_bf16  bf16 bits [m][k] row-major, 16-byte aligned
  *   y       fp32 [m][n] row-major, 16-byte aligned
- *   ws      NULL, or device memory of ws_bytes >= qmm_q4_k_prefill_workspace(m, n, k),
- *           256-byte aligned (its contents on entry do not matter)
- *   m >= 1, n >= 1, k % 256 == 0.
+ *   ws      device memory of ws_bytes >= qmm_q4_k_prefill_workspace(m, n, k),
+ *           256-byte aligned (its contents on entry do not matter); may be
+ *           NULL only when that size is 0, else QMV_ERR_WORKSPACE
+ *   m >= 1, n >= 1, k % 256 == 0; m * k / 8 <= 2^32 (activation granules are
+ *   indexed in 32 bits) and at most 2^31 - 1 output tiles, else QMV_ERR_RANGE.
  * Weights are dequantized to fp32, rounded once to bf16 (round to nearest
  * even) and multiplied with the bf16 activations, accumulating in fp32.
- * Each output tile is one workgroup's sequential fp32 sum over K, except, with
- * a workspace, the split tiles: there each part sums a run of whole K blocks
- * and a second launch adds the parts in K order. Results are deterministic
- * for a given shape and device.
+ * Each output tile is one workgroup's sequential fp32 sum over K, except the
+ * split tiles: there each part sums a run of whole K blocks and a second
+ * launch adds the parts in K order. The summation order -- and so every bit
+ * of the result -- depends only on (m, n, k) and the inputs, on any device.
  * Workload: prompt processing ahead of decode (the time-to-first-token figures
  * of the memra summary page's performance table).
  */
@@ -320,7 +340,10 @@ int qmm_q4_k_prefill(const void *w, size_t w_bytes, const uint16_t *x_bf16, floa
                      int m, int n, int k, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Dequantization to dense matrices (the bit-exact gate of the decode kernels).
+ * Dequantization to dense matrices, of the GGUF formats the memra README's
+ * model support table names. They expose the weights exactly as the products
+ * above decode them, so that decoding can be checked bit for bit against an
+ * independent decoder.
  *   out  fp32 [n][k] or bf16 bits [n][k], 16-byte aligned
  * fp32: each weight is the exact block value rounded once to fp32 (nearest
  * even; Q8_0 and IQ4_XS weights are exact in fp32). bf16: that fp32 value

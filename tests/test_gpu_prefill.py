@@ -32,17 +32,17 @@ def dev():
     return device()
 
 
-@pytest.mark.parametrize("ws", ["auto", None], ids=["k_split", "tile_per_group"])
 @pytest.mark.parametrize("m,n,k", [(64, 128, 1024), (100, 200, 768), (1, 16, 256), (257, 129, 2048), (128, 384, 5120),
-                                   (40, 64, 17408)])
-def test_prefill_parity(q, dev, m, n, k, ws):
-    # with a workspace, tile counts that do not divide over the device's resident
-    # workgroups split their last tiles along K (here every tile: fewer tiles than
-    # workgroups; one tile of 17408 K in many parts; ragged tiles)
+                                   (40, 64, 17408), (256, 32768, 256)])
+def test_prefill_parity(q, dev, m, n, k):
+    # tile counts that are not a multiple of the 512 workgroup slots split their
+    # last tiles along K (here every tile: fewer tiles than slots; one tile of
+    # 17408 K in many parts; ragged tiles); 256 x 32768 is exactly 512 whole
+    # tiles, and a single 256-value K block cannot split
     raw = synth.q4_k_weights(m + n, n, k)
     x = synth.bf16_normal(k + m, (m, k))
     y, buf = guarded((m, n), torch.float32, dev)
-    q.qmm_q4_k_prefill(to_dev(raw, dev), to_dev(x, dev), n, k, y=y, ws=ws)
+    q.qmm_q4_k_prefill(to_dev(raw, dev), to_dev(x, dev), n, k, y=y)
     torch.cuda.synchronize()
     assert guards_intact(buf)
     ye, yb = oracle.prefill_q4_k(raw, x, n, k)
@@ -97,23 +97,25 @@ def test_prefill_matches_dequantized_bf16_weights(q, dev):
 
 @pytest.mark.parametrize("n,k", [(17408, 5120), (5120, 17408)])
 def test_prefill_k_split_reused_workspace_and_graph_replays(q, dev, n, k):
-    # repeated calls on one workspace, and replays of a captured call, reproduce
-    # the first call bit for bit. Split and whole-tile sums are fp32 sums over K
-    # in different orders; each is gated against the oracle elsewhere, so here
-    # they must agree to that gate
+    # repeated calls on one workspace (its contents on entry do not matter), a
+    # freshly allocated one, and replays of a captured call reproduce the first
+    # call bit for bit; without the workspace the call is refused
     m = 512
     need = q.qmm_q4_k_prefill_workspace(m, n, k)
     assert need > 0, "the prompt shapes take the K split"
     w = synth.torch_q4_k_weights(70, n, k, dev)
     x = to_dev(synth.bf16_normal(71, (m, k)), dev)
-    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=dev)   # contents on entry do not matter
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=dev)
     ref = host(q.qmm_q4_k_prefill(w, x, n, k, ws=ws))
     assert np.isfinite(ref).all()
     for _ in range(2):
         again = host(q.qmm_q4_k_prefill(w, x, n, k, ws=ws))
         assert np.array_equal(again.view(np.uint32), ref.view(np.uint32))
-    plain = host(q.qmm_q4_k_prefill(w, x, n, k, ws=None))
-    assert oracle.floored_rel_err(ref, plain.astype(np.float64)) <= GEMV_TOL
+    fresh = host(q.qmm_q4_k_prefill(w, x, n, k))
+    assert np.array_equal(fresh.view(np.uint32), ref.view(np.uint32))
+    y0 = torch.empty((m, n), dtype=torch.float32, device=dev)
+    rc = q.lib.qmm_q4_k_prefill(q._ptr(w), q._nbytes(w), q._ptr(x), q._ptr(y0), m, n, k, None, 0, None)
+    assert rc == -6   # QMV_ERR_WORKSPACE
     y = torch.empty((m, n), dtype=torch.float32, device=dev)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
