@@ -5,21 +5,31 @@ Headline (the `value`): Q4_K GEMV at M=1 over the dense 27B-like FFN shapes --
 gate and up 17408x5120, down 5120x17408 -- cycling a pool of 128 independent
 layer copies (19.25 GB, far above the 256 MB Infinity Cache), reported as
 achieved GB/s of algorithmic bytes (weights + activations + outputs). One step
-is one pass over the whole pool (384 GEMVs). Also reported: the M = 1..4
-speculative-verify curve, the 1024x1024 Q8_0 GEMV latency, the routed-expert
-MoE rate (tok-equiv/s over a 48-bank pool), the M=512 prefill GEMM rate, a copy
-bandwidth calibration, the roofline of the dominant kernel from per-launch HIP
-events, and the CPU oracle timed on the host cores.
+is one pass over the whole pool (384 GEMVs).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+Sections beside it (each can be left out with --skip or chosen with --only):
+  calib        plain streaming read of the same pool (the achievable read
+               ceiling) and a 4 GiB device copy
+  percall      each GEMV of one pass bracketed by its own HIP events
+  verify       the M = 1..4 speculative-verify curve
+  q8           the 1024x1024 Q8_0 GEMV (cache-resident: a latency figure)
+  moe          routed-expert MoE decode, T = 1 and 3 (tok-equiv/s, 48-bank pool)
+  moe_prefill  the MoE over a 512-token prompt, against its HBM roofline
+  prefill      the M=512 prefill GEMM on both shapes (TFLOP/s, MFMA utilisation)
+  iq4, q5, q6, q40   the other block formats' GEMVs (and the IQ4_XS MoE)
+  cpu          the fp64 oracle on the host cores (1 thread and all cores)
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only a,b] [--skip a,b]
 """
 
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,27 +37,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "Q4_K GEMV achieved HBM GB/s (% of 8 TB/s peak) at M=1; MoE tok-equiv/s"
+SHAPES = (("gate", 17408, 5120), ("up", 17408, 5120), ("down", 5120, 17408))
+SECTIONS = ("calib", "percall", "verify", "q8", "moe", "moe_prefill", "prefill", "iq4", "q5", "q6", "q40", "cpu")
 
-# HBM bytes per q4k_gemv_kernel launch at M=1 (mean over gate, up and down) from
-# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes (profiles/q4k_gemv_m1_hbm_traffic.md),
-# each scaled by what the same counter reads for a 4 GiB device copy in the same
-# run (FETCH_SIZE reads half the bytes copied, WRITE_SIZE all of them). The figure
-# describes the kernel code hashed here (comments and whitespace excluded) and is
-# reported as null once it changes.
-GEMV_TRAFFIC = {
-    "sources": ("gguf_block_quantized_qmv_amd/csrc/q4k_gemv.hip", "gguf_block_quantized_qmv_amd/csrc/q4k_common.h",
-                "gguf_block_quantized_qmv_amd/csrc/qmv_device.h"),
-    "sha256": "e2f82a7bfb9b4910f66acc2c9acd9d81a339a99a104cd8ed6f8fa4606edfd976",
-    "bytes_per_launch": 50875056,
+# Figures that come from rocprofv3 counter passes (see profiles/), keyed to the
+# code they describe: each is reported only while the kernel's sources (comments
+# and whitespace excluded) still hash to the value measured, else null.
+_CSRC = "gguf_block_quantized_qmv_amd/csrc/"
+MEASURED = {
+    # HBM bytes per q4k_gemv_kernel launch at M=1, mean over gate, up and down:
+    # FETCH_SIZE scaled by the streaming read of a known size, plus WRITE_SIZE
+    # scaled by a 4 GiB device copy (profiles/q4k_gemv_m1_hbm_traffic.md)
+    "gemv_traffic": {"sources": (_CSRC + "q4k_gemv.hip", _CSRC + "q4k_common.h", _CSRC + "qmv_device.h",
+                                 _CSRC + "qmv_layout.h"),
+                     "sha256": "04bb29a35cc6d927614db32e7f0436be5108c497b0132d576131a74f989bc76b", "value": 50855933},
+    # MFMA utilisation of the prefill GEMM at M=512 (profiles/q4k_prefill_m512_mfma.md)
+    "prefill_mfma_util": {"sources": (_CSRC + "q4k_prefill.hip", _CSRC + "q4k_common.h", _CSRC + "qmv_device.h",
+                                      _CSRC + "qmv_layout.h"),
+                          "sha256": "b2df1496e717109e4b7d62f1d37cbdb79e50822466f86ba9efceb06fd46d5b6a",
+                          "value": {"up": 0.371, "down": 0.365}},
 }
 
 
-def gemv_sources_sha256():
-    """sha256 of the kernel's sources with comments and whitespace removed (code only)."""
-    import hashlib
-    import re
+def sources_sha256(sources) -> str:
+    """sha256 of source files with comments and whitespace removed (code only)."""
     h = hashlib.sha256()
-    for rel in GEMV_TRAFFIC["sources"]:
+    for rel in sources:
         with open(os.path.join(ROOT, rel)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -56,11 +73,11 @@ def gemv_sources_sha256():
     return h.hexdigest()
 
 
-def gemv_traffic():
-    return GEMV_TRAFFIC["bytes_per_launch"] if gemv_sources_sha256() == GEMV_TRAFFIC["sha256"] else None
-BF16_PEAK_TFLOPS = 2500.0
-METRIC = "Q4_K GEMV achieved HBM GB/s (% of 8 TB/s peak) at M=1; MoE tok-equiv/s"
-SHAPES = (("gate", 17408, 5120), ("up", 17408, 5120), ("down", 5120, 17408))
+def measured(key):
+    m = MEASURED[key]
+    if m["sha256"] is None or sources_sha256(m["sources"]) != m["sha256"]:
+        return None
+    return m["value"]
 
 
 def log(*a):
@@ -74,18 +91,19 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--copies", type=int, default=128, help="layer copies in the dense weight pool")
     p.add_argument("--moe-banks", type=int, default=48)
-    p.add_argument("--iq4-copies", type=int, default=48, help="layer copies in the IQ4_XS, Q5_K, Q6_K and Q4_0 weight pools")
-    p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
-    p.add_argument("--skip", default="", help="comma list of sections to skip: verify,q8,moe,prefill,iq4,q5,q6,q40,cpu")
+    p.add_argument("--iq4-copies", type=int, default=48, help="layer copies in the IQ4_XS, Q5_K, Q6_K and Q4_0 pools")
+    p.add_argument("--only", default="", help="comma list: run only these sections (the headline always runs; "
+                                               "'gemv' alone runs nothing else)")
+    p.add_argument("--skip", default="", help="comma list of sections to leave out: " + ",".join(SECTIONS))
     return p.parse_args()
 
 
-def current_stream_ptr(torch):
+def stream_ptr(torch):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 class Timer:
-    """HIP-event timing on the current torch stream."""
+    """HIP events on torch's current stream, which every launch here names."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -102,13 +120,29 @@ class Timer:
         return s.elapsed_time(e) / 1e3 / reps   # seconds per rep
 
 
+def checked(fn, name):
+    def call(*a):
+        rc = fn(*a)
+        if rc:
+            raise RuntimeError(f"{name} returned {rc}")
+    return call
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on exactly one GPU; the multi-GPU sharding is designed "
                                    "but not built, so only --gpus 1 is measured", "n_gpus": args.gpus}))
         sys.exit(2)
+    only = set(filter(None, args.only.split(",")))
     skip = set(filter(None, args.skip.split(",")))
+    only.discard("gemv")   # --only gemv: the headline pass alone
+    if args.only and not only:
+        only = {"none"}
+    unknown = (only | skip) - set(SECTIONS) - {"none"}
+    if unknown:
+        raise SystemExit(f"unknown sections: {sorted(unknown)}")
+    want = (lambda s: s in only) if only else (lambda s: s not in skip)
 
     import numpy as np
     import torch
@@ -120,63 +154,53 @@ def main():
     torch.cuda.set_device(dev)
     L = q.lib
     timer = Timer(torch)
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
+    sp = stream_ptr(torch)
 
-    # ------------------------------------------------------------ dense pool
+    # ------------------------------------------------------------ headline: the dense pool at M=1
     log(f"[bench] generating the Q4_K pool: {args.copies} copies x gate/up/down")
     pool = [[synth.torch_q4_k_weights(11, n, k, dev, stream=3 * c + i) for i, (_, n, k) in enumerate(SHAPES)]
             for c in range(args.copies)]
-    xs = {k: synth.bf16_normal(12, (4, k)) for _, _, k in SHAPES}
-    x_dev = {k: torch.from_numpy(v.view(np.int16)).to(dev) for k, v in xs.items()}
+    x_dev = {k: torch.from_numpy(synth.bf16_normal(12, (4, k)).view(np.int16)).to(dev) for _, _, k in SHAPES}
     y_dev = {n: torch.empty((4, n), dtype=torch.float32, device=dev) for _, n, _ in SHAPES}
     torch.cuda.synchronize()
     wbytes = [q.q4_k_bytes(n, k) for _, n, k in SHAPES]
     pool_bytes = args.copies * sum(wbytes)
+    gemv = checked(L.qmv_q4_k, "qmv_q4_k")
 
-    def calls(m, stream_ptr=None):
-        st = stream_ptr if stream_ptr is not None else sp
-        out = []
-        for c in range(args.copies):
-            for i, (_, n, k) in enumerate(SHAPES):
-                out.append((ctypes.c_void_p(pool[c][i].data_ptr()), wbytes[i], ctypes.c_void_p(x_dev[k].data_ptr()),
-                            ctypes.c_void_p(y_dev[n].data_ptr()), m, n, k, st))
-        return out
+    def calls(m, st):
+        return [(ctypes.c_void_p(pool[c][i].data_ptr()), wbytes[i], ctypes.c_void_p(x_dev[k].data_ptr()),
+                 ctypes.c_void_p(y_dev[n].data_ptr()), m, n, k, st)
+                for c in range(args.copies) for i, (_, n, k) in enumerate(SHAPES)]
 
     def algo_bytes(m):
         return args.copies * sum(wb + m * k * 2 + m * n * 4 for wb, (_, n, k) in zip(wbytes, SHAPES))
 
-    def make_step(m, stream_ptr=None):
-        cl = calls(m, stream_ptr)
-        fn = L.qmv_q4_k
+    def make_step(m, st):
+        cl = calls(m, st)
 
         def step():
             for a in cl:
-                rc = fn(*a)
-                if rc:
-                    raise q.QmvError(rc, "qmv_q4_k")
+                gemv(*a)
         return step
 
     def graph_of(m):
         # the launches must name the capture stream that torch.cuda.graph makes current
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            make_step(m, current_stream_ptr(torch))()
+            make_step(m, stream_ptr(torch))()
         return g
 
     res = {}
-    step1 = make_step(1)
+    step1 = make_step(1, sp)
     for _ in range(max(1, args.warmup)):
         step1()
     t_eager = timer.run(step1, args.steps)
     log(f"[bench] M=1 stream launches: {t_eager * 1e3:.3f} ms/step, {algo_bytes(1) / t_eager / 1e9:.1f} GB/s")
-
     g1 = graph_of(1)
     for _ in range(max(1, args.warmup)):
         g1.replay()
     t_graph = timer.run(g1.replay, args.steps)
     log(f"[bench] M=1 hipGraph replay:   {t_graph * 1e3:.3f} ms/step, {algo_bytes(1) / t_graph / 1e9:.1f} GB/s")
-
     # the replayed graph must reproduce the stream-launched result bit for bit (outputs cleared in between)
     step1()
     torch.cuda.synchronize()
@@ -188,102 +212,53 @@ def main():
     torch.cuda.synchronize()
     for n in y_dev:
         assert torch.equal(y_dev[n][:1], y_ref[n]), "graph replay and stream launch disagree"
-
+    del g1
     best_t, launch_mode = (t_graph, "hipGraph") if t_graph < t_eager else (t_eager, "stream")
     value = algo_bytes(1) / best_t / 1e9
-
-    # per-launch kernel durations (HIP events around every launch, on the launch stream)
-    cl = calls(1)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cl]
-    torch.cuda.synchronize()
-    for (s, e), a in zip(evs, cl):
-        s.record()
-        L.qmv_q4_k(*a)
-        e.record()
-    torch.cuda.synchronize()
-    dur = {name: [] for name, _, _ in SHAPES}
-    for i, (s, e) in enumerate(evs):
-        dur[SHAPES[i % 3][0]].append(s.elapsed_time(e) / 1e3)
-    per_shape = {}
-    for i, (name, n, k) in enumerate(SHAPES):
-        d = float(np.mean(dur[name]))
-        per_shape[name] = {"us": d * 1e6, "GBps": (wbytes[i] + k * 2 + n * 4) / d / 1e9}
-    # roofline: the timed region is a pass over the pool made of this kernel only, so its
-    # average launch duration is the region's time over the launches in it (HIP events on
-    # the launch stream, back-to-back launches); the per-launch bracketing above adds the
-    # launch overhead of each isolated call and is reported separately
+    # roofline of the dominant kernel: the timed region is a pass over the pool made of
+    # q4k_gemv_kernel launches only, so its average launch duration is the region's time
+    # over the launches in it (HIP events on the launch stream)
+    launches = args.copies * len(SHAPES)
     launch_bytes = float(np.mean([wb + k * 2 + n * 4 for wb, (_, n, k) in zip(wbytes, SHAPES)]))
-    avg_dur = best_t / (args.copies * len(SHAPES))
+    avg_dur = best_t / launches
     achieved = launch_bytes / avg_dur / 1e9
-    res["per_shape_m1"] = per_shape
-    res["isolated_launch_us_mean"] = float(np.mean([np.mean(v) for v in dur.values()])) * 1e6
-    log(f"[bench] per-launch: " + ", ".join(f"{k} {v['us']:.2f} us {v['GBps']:.0f} GB/s" for k, v in per_shape.items()))
 
-    # speculative verify: GB/s vs M
-    if "verify" not in skip:
+    if want("calib"):
+        res["calibration"] = bench_calib(args, torch, np, q, timer, dev, sp, pool, best_t)
+    if want("percall"):
+        res["per_launch_isolated"] = bench_percall(torch, np, calls(1, sp), gemv, wbytes)
+    if want("verify"):
         curve = {}
         for m in (1, 2, 3, 4):
             g = graph_of(m)
             g.replay()
             tm = timer.run(g.replay, max(2, args.steps // 2))
-            curve[str(m)] = {"GBps": algo_bytes(m) / tm / 1e9, "ms_per_step": tm * 1e3,
+            curve[str(m)] = {"GBps": algo_bytes(m) / tm / 1e9, "frac_of_8TBps": algo_bytes(m) / tm / 1e9 / HBM_PEAK_GBPS,
+                             "ms_per_step": tm * 1e3,
                              "weights_per_s": args.copies * sum(n * k for _, n, k in SHAPES) / tm}
             del g
         res["verify_GBps_vs_M"] = curve
         log("[bench] verify curve: " + ", ".join(f"M={m} {v['GBps']:.0f}" for m, v in curve.items()))
-
-    # copy calibration: device-to-device copy of 4 GiB (read + write bytes)
-    buf_a = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
-    buf_b = torch.empty_like(buf_a)
-    buf_b.copy_(buf_a)
-    t_copy = timer.run(lambda: buf_b.copy_(buf_a), 5)
-    res["copy_calibration_GBps"] = 2 * buf_a.numel() / t_copy / 1e9
-    del buf_a, buf_b
-    log(f"[bench] copy calibration {res['copy_calibration_GBps']:.0f} GB/s (read+write)")
-
-    # Q8_0 1024x1024 (cache-resident; latency, not a bandwidth figure)
-    if "q8" not in skip:
-        w8 = torch.from_numpy(synth.q8_0_weights(13, 1024, 1024)).to(dev)
-        x8 = torch.from_numpy(synth.f32_normal(14, (1, 1024))).to(dev)
-        y8 = torch.empty((1, 1024), dtype=torch.float32, device=dev)
-        a8 = (ctypes.c_void_p(w8.data_ptr()), w8.numel(), ctypes.c_void_p(x8.data_ptr()),
-              ctypes.c_void_p(y8.data_ptr()), 1, 1024, 1024, sp)
-        L.qmv_q8_0(*a8)
-        g8 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g8):
-            a8g = a8[:-1] + (current_stream_ptr(torch),)
-            for _ in range(100):
-                L.qmv_q8_0(*a8g)
-        g8.replay()
-        t8 = timer.run(g8.replay, 5) / 100
-        res["q8_0_1024x1024_us"] = t8 * 1e6
-        log(f"[bench] Q8_0 1024x1024: {t8 * 1e6:.2f} us/call (graph)")
-
-    if "moe" not in skip:
-        res["moe"] = bench_moe(args, torch, np, q, synth, timer, dev, sp)
-    if "prefill" not in skip:
+    if want("q8"):
+        res["q8_0_1024x1024_us"] = bench_q8(torch, np, q, synth, timer, dev, sp)
+    if want("moe") or want("moe_prefill"):
+        res.update(bench_moe(args, torch, np, q, synth, timer, dev, sp, "q4_k", want("moe"), want("moe_prefill")))
+    if want("prefill"):
         res["prefill"] = bench_prefill(args, torch, np, q, synth, timer, dev, sp, pool)
 
     del pool
     torch.cuda.empty_cache()
-    if "iq4" not in skip:
+    if want("iq4"):
         res["iq4_xs_gemv"] = bench_format(args, torch, np, q, synth, timer, dev, sp, "iq4_xs")
-        if "moe" not in skip:
-            res["moe_iq4_xs"] = bench_moe(args, torch, np, q, synth, timer, dev, sp, fmt="iq4_xs")
+        if want("moe"):
+            res.update(bench_moe(args, torch, np, q, synth, timer, dev, sp, "iq4_xs", True, False))
         torch.cuda.empty_cache()
-    if "q5" not in skip:
-        res["q5_k_gemv"] = bench_format(args, torch, np, q, synth, timer, dev, sp, "q5_k")
-        torch.cuda.empty_cache()
-    if "q6" not in skip:
-        res["q6_k_gemv"] = bench_format(args, torch, np, q, synth, timer, dev, sp, "q6_k")
-        torch.cuda.empty_cache()
-    if "q40" not in skip:
-        res["q4_0_gemv"] = bench_format(args, torch, np, q, synth, timer, dev, sp, "q4_0")
-        torch.cuda.empty_cache()
+    for sec, fmt in (("q5", "q5_k"), ("q6", "q6_k"), ("q40", "q4_0")):
+        if want(sec):
+            res[f"{fmt}_gemv"] = bench_format(args, torch, np, q, synth, timer, dev, sp, fmt)
+            torch.cuda.empty_cache()
 
-    cpu = None
-    if "cpu" not in skip:
-        cpu = cpu_baseline(args, np, synth)
+    cpu = cpu_baseline(np, synth) if want("cpu") else None
 
     line = {
         "metric": METRIC,
@@ -308,15 +283,16 @@ def main():
             "graph_replay_GBps": round(algo_bytes(1) / t_graph / 1e9, 1),
         },
         "roofline": {
-            "kernel": "q4k_gemv_kernel<1>",
+            "kernel": "q4k_gemv_kernel (M=1)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": gemv_traffic(),
+            "traffic": measured("gemv_traffic"),
             "traffic_unit": "HBM bytes per launch",
             "avg_launch_us": round(avg_dur * 1e6, 3),
+            "launches_per_step": launches,
             "algorithmic_bytes_per_launch": launch_bytes,
         },
         "cpu_baseline": cpu,
@@ -325,102 +301,189 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def bench_moe(args, torch, np, q, synth, timer, dev, sp, fmt="q4_k"):
-    hidden, ffn, ne, tk = 2048, 768, 128, 8
-    L = q.lib
-    gen = synth.torch_q4_k_weights if fmt == "q4_k" else synth.torch_iq4_xs_weights
-    entry = L.qmv_q4_k_moe if fmt == "q4_k" else L.qmv_iq4_xs_moe
-    ws_fn = L.qmv_q4_k_moe_workspace if fmt == "q4_k" else L.qmv_iq4_xs_moe_workspace
-    name = f"qmv_{fmt}_moe"
-    banks = []
-    log(f"[bench] generating the {fmt} MoE pool: {args.moe_banks} banks x {ne} experts")
-    for b in range(args.moe_banks):
-        banks.append([gen(21, ne * (ffn if i < 2 else hidden), hidden if i < 2 else ffn, dev, stream=3 * b + i)
-                      for i in range(3)])
-    bank_bytes = banks[0][0].numel()
-    out = {}
-    for t in (1, 3):
-        logits = torch.from_numpy(synth.moe_logits(22, t * args.moe_banks, ne)).to(dev).view(args.moe_banks, t, ne)
-        x = torch.from_numpy(synth.bf16_normal(23, (t, hidden)).view(np.int16)).to(dev)
-        y = torch.empty((t, hidden), dtype=torch.float32, device=dev)
-        need = ws_fn(t, hidden, ffn, ne, tk)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        ids = torch.empty((args.moe_banks, t, tk), dtype=torch.int32, device=dev)
-        def make_calls(stream_ptr):
-            return [(*(ctypes.c_void_p(banks[b][i].data_ptr()) for i in range(3)), bank_bytes,
-                     ctypes.c_void_p(logits[b].data_ptr()), ctypes.c_void_p(x.data_ptr()),
-                     ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(ids[b].data_ptr()), None, None,
-                     ctypes.c_void_p(ws.data_ptr()), need, t, hidden, ffn, ne, tk, stream_ptr)
-                    for b in range(args.moe_banks)]
+def bench_calib(args, torch, np, q, timer, dev, sp, pool, gemv_t):
+    """Plain streaming read of every matrix of the pool, one launch each (the same
+    launches and bytes as a GEMV pass, with no arithmetic), and a 4 GiB device copy."""
+    read = checked(q.lib.qmv_stream_read, "qmv_stream_read")
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    mats = [(ctypes.c_void_p(t.data_ptr()), t.numel()) for c in pool for t in c]
+    total = sum(b for _, b in mats)
 
-        def make_step(stream_ptr):
-            cl = make_calls(stream_ptr)
+    def pass_of(grid, depth, nt, mats=mats):
+        a = [(p, b, ctypes.c_void_p(sink.data_ptr()), grid, depth, nt, sp) for p, b in mats]
 
-            def step():
-                for a in cl:
-                    rc = entry(*a)
-                    if rc:
-                        raise q.QmvError(rc, name)
-            return step
-        step = make_step(sp)
-        step()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            make_step(current_stream_ptr(torch))()
-        g.replay()
-        t_eager = timer.run(step, max(2, args.steps))
-        t_graph = timer.run(g.replay, max(2, args.steps))
-        tl = min(t_eager, t_graph) / args.moe_banks
-        # distinct experts per layer decide the bytes streamed
-        idh = ids.cpu().numpy()
-        distinct = np.mean([len(np.unique(idh[b])) for b in range(args.moe_banks)])
-        expert_bytes = 3 * bank_bytes // ne
-        out[f"T{t}"] = {
-            "tok_equiv_per_s": t / (args.moe_banks * tl),
-            "us_per_layer": tl * 1e6,
-            "distinct_experts": float(distinct),
-            "GBps_distinct_expert_bytes": distinct * expert_bytes / tl / 1e9,
-            "launch": "hipGraph" if t_graph < t_eager else "stream",
-        }
-        log(f"[bench] {fmt} MoE T={t}: {tl * 1e6:.2f} us/layer, {out[f'T{t}']['tok_equiv_per_s']:.0f} tok-equiv/s, "
-            f"{out[f'T{t}']['GBps_distinct_expert_bytes']:.0f} GB/s")
-    if fmt == "q4_k":
-        # prompt-sized form: 512 tokens per call over 8 of the pool's banks
-        t, nb = 512, min(8, args.moe_banks)
-        logits = torch.from_numpy(synth.moe_logits(24, t * nb, ne)).to(dev).view(nb, t, ne)
-        x = torch.from_numpy(synth.bf16_normal(25, (t, hidden)).view(np.int16)).to(dev)
-        y = torch.empty((t, hidden), dtype=torch.float32, device=dev)
-        need = L.qmv_q4_k_moe_prefill_workspace(t, hidden, ffn, ne, tk)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        calls = [(*(ctypes.c_void_p(banks[b][i].data_ptr()) for i in range(3)), bank_bytes,
-                  ctypes.c_void_p(logits[b].data_ptr()), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
-                  None, None, ctypes.c_void_p(ws.data_ptr()), need, t, hidden, ffn, ne, tk, sp) for b in range(nb)]
-
-        def pstep():
-            for a in calls:
-                rc = L.qmv_q4_k_moe_prefill(*a)
-                if rc:
-                    raise q.QmvError(rc, "qmv_q4_k_moe_prefill")
-        pstep()
-        tl = timer.run(pstep, 2) / nb
-        # algorithmic work: per (token, rank) pair 2 flop per weight of W_gate, W_up and W_down
-        flops = t * tk * 2 * 3 * hidden * ffn
-        out["prefill_T512"] = {"us_per_layer": tl * 1e6, "tokens_per_s_per_layer": t / tl,
-                               "TFLOPs": flops / tl / 1e12}
-        log(f"[bench] {fmt} MoE prefill T={t}: {tl * 1e3:.3f} ms/layer, {t / tl:.0f} tokens/s per layer, "
-            f"{flops / tl / 1e12:.0f} TFLOP/s")
-    del banks
+        def step():
+            for x in a:
+                read(*x)
+        return step
+    # (workgroups, loads in flight per thread, non-temporal loads)
+    configs = [(512, 8, 0), (1024, 4, 0), (2048, 2, 0), (4096, 1, 0), (512, 8, 1), (1024, 4, 1), (4096, 1, 1)]
+    sweep = {}
+    for cfg in configs:
+        st = pass_of(*cfg)
+        st()
+        sweep["x".join(map(str, cfg))] = total / timer.run(st, max(2, args.steps // 2)) / 1e9
+    best = max(sweep, key=sweep.get)
+    grid, depth, nt = (int(v) for v in best.split("x"))
+    t = timer.run(pass_of(grid, depth, nt), args.steps)
+    out = {"stream_read_GBps": total / t / 1e9, "frac_of_8TBps": total / t / 1e9 / HBM_PEAK_GBPS,
+           "config": {"grid": grid, "depth": depth, "nontemporal": nt, "threads": 256},
+           "us_per_launch": t / len(mats) * 1e6, "sweep_GBps": {k: round(v, 1) for k, v in sweep.items()},
+           "gemv_over_read": (total / gemv_t) / (total / t)}
+    buf_a = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    buf_b = torch.empty_like(buf_a)
+    # one long read (4 GiB in one launch) next to the per-matrix launches: the rate without the
+    # per-launch ramp and drain
+    one = pass_of(grid, depth, nt, [(ctypes.c_void_p(buf_a.data_ptr()), buf_a.numel())])
+    one()
+    out["single_4GiB_read_GBps"] = buf_a.numel() / timer.run(one, 5) / 1e9
+    buf_b.copy_(buf_a)
+    out["device_copy_GBps_read_plus_write"] = 2 * buf_a.numel() / timer.run(lambda: buf_b.copy_(buf_a), 5) / 1e9
+    del buf_a, buf_b
+    log(f"[bench] streaming read of the pool: {out['stream_read_GBps']:.0f} GB/s ({best}, "
+        f"{out['us_per_launch']:.2f} us/launch); GEMV pass / read = {out['gemv_over_read']:.3f}; one 4 GiB read "
+        f"{out['single_4GiB_read_GBps']:.0f} GB/s; device copy {out['device_copy_GBps_read_plus_write']:.0f} GB/s "
+        f"(read+write)")
     return out
 
 
+def bench_percall(torch, np, cl, gemv, wbytes):
+    """Each launch of one pass bracketed by its own events (adds the per-call launch gap)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cl]
+    torch.cuda.synchronize()
+    for (s, e), a in zip(evs, cl):
+        s.record()
+        gemv(*a)
+        e.record()
+    torch.cuda.synchronize()
+    dur = {name: [] for name, _, _ in SHAPES}
+    for i, (s, e) in enumerate(evs):
+        dur[SHAPES[i % 3][0]].append(s.elapsed_time(e) / 1e3)
+    out = {}
+    for i, (name, n, k) in enumerate(SHAPES):
+        d = float(np.median(dur[name]))
+        out[name] = {"us_median": d * 1e6, "GBps": (wbytes[i] + k * 2 + n * 4) / d / 1e9}
+    log("[bench] isolated launches: " + ", ".join(f"{k} {v['us_median']:.2f} us" for k, v in out.items()))
+    return out
+
+
+def bench_q8(torch, np, q, synth, timer, dev, sp):
+    w8 = torch.from_numpy(synth.q8_0_weights(13, 1024, 1024)).to(dev)
+    x8 = torch.from_numpy(synth.f32_normal(14, (1, 1024))).to(dev)
+    y8 = torch.empty((1, 1024), dtype=torch.float32, device=dev)
+    f = checked(q.lib.qmv_q8_0, "qmv_q8_0")
+    a8 = (ctypes.c_void_p(w8.data_ptr()), w8.numel(), ctypes.c_void_p(x8.data_ptr()), ctypes.c_void_p(y8.data_ptr()),
+          1, 1024, 1024)
+    f(*a8, sp)
+    g8 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g8):
+        st = stream_ptr(torch)
+        for _ in range(100):
+            f(*a8, st)
+    g8.replay()
+    t8 = timer.run(g8.replay, 5) / 100
+    log(f"[bench] Q8_0 1024x1024: {t8 * 1e6:.2f} us/call (graph of 100 calls; cache-resident)")
+    return t8 * 1e6
+
+
+def bench_moe(args, torch, np, q, synth, timer, dev, sp, fmt, decode, prefill):
+    hidden, ffn, ne, tk = 2048, 768, 128, 8
+    L = q.lib
+    gen = synth.torch_q4_k_weights if fmt == "q4_k" else synth.torch_iq4_xs_weights
+    entry = checked(L.qmv_q4_k_moe if fmt == "q4_k" else L.qmv_iq4_xs_moe, f"qmv_{fmt}_moe")
+    ws_fn = L.qmv_q4_k_moe_workspace if fmt == "q4_k" else L.qmv_iq4_xs_moe_workspace
+    nb = args.moe_banks
+    log(f"[bench] generating the {fmt} MoE pool: {nb} banks x {ne} experts")
+    banks = [[gen(21, ne * (ffn if i < 2 else hidden), hidden if i < 2 else ffn, dev, stream=3 * b + i)
+              for i in range(3)] for b in range(nb)]
+    bank_bytes = banks[0][0].numel()
+    expert_bytes = 3 * bank_bytes // ne
+    res = {}
+    if decode:
+        out = {}
+        for t in (1, 3):
+            logits = torch.from_numpy(synth.moe_logits(22, t * nb, ne)).to(dev).view(nb, t, ne)
+            x = torch.from_numpy(synth.bf16_normal(23, (t, hidden)).view(np.int16)).to(dev)
+            y = torch.empty((t, hidden), dtype=torch.float32, device=dev)
+            need = ws_fn(t, hidden, ffn, ne, tk)
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            ids = torch.empty((nb, t, tk), dtype=torch.int32, device=dev)
+
+            def make_step(st):
+                cl = [(*(ctypes.c_void_p(banks[b][i].data_ptr()) for i in range(3)), bank_bytes,
+                       ctypes.c_void_p(logits[b].data_ptr()), ctypes.c_void_p(x.data_ptr()),
+                       ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(ids[b].data_ptr()), None, None,
+                       ctypes.c_void_p(ws.data_ptr()), need, t, hidden, ffn, ne, tk, st) for b in range(nb)]
+
+                def step():
+                    for a in cl:
+                        entry(*a)
+                return step
+            step = make_step(sp)
+            step()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                make_step(stream_ptr(torch))()
+            g.replay()
+            t_eager = timer.run(step, max(2, args.steps))
+            t_graph = timer.run(g.replay, max(2, args.steps))
+            tl = min(t_eager, t_graph) / nb
+            idh = ids.cpu().numpy()
+            distinct = float(np.mean([len(np.unique(idh[b])) for b in range(nb)]))
+            gbps = distinct * expert_bytes / tl / 1e9
+            out[f"T{t}"] = {"tok_equiv_per_s": t / (nb * tl), "us_per_layer": tl * 1e6, "distinct_experts": distinct,
+                            "GBps_distinct_expert_bytes": gbps, "frac_of_8TBps": gbps / HBM_PEAK_GBPS,
+                            "launch": "hipGraph" if t_graph < t_eager else "stream"}
+            log(f"[bench] {fmt} MoE T={t}: {tl * 1e6:.2f} us/layer, {t / (nb * tl):.0f} tok-equiv/s, "
+                f"{gbps:.0f} GB/s on distinct-expert bytes")
+            del g
+        res[f"moe_{fmt}" if fmt != "q4_k" else "moe"] = out
+    if prefill and fmt == "q4_k":
+        # prompt-sized form: 512 tokens per call over 8 of the pool's banks
+        t, npb = 512, min(8, nb)
+        logits = torch.from_numpy(synth.moe_logits(24, t * npb, ne)).to(dev).view(npb, t, ne)
+        x = torch.from_numpy(synth.bf16_normal(25, (t, hidden)).view(np.int16)).to(dev)
+        y = torch.empty((t, hidden), dtype=torch.float32, device=dev)
+        ids = torch.empty((npb, t, tk), dtype=torch.int32, device=dev)
+        need = L.qmv_q4_k_moe_prefill_workspace(t, hidden, ffn, ne, tk)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        pf = checked(L.qmv_q4_k_moe_prefill, "qmv_q4_k_moe_prefill")
+        cl = [(*(ctypes.c_void_p(banks[b][i].data_ptr()) for i in range(3)), bank_bytes,
+               ctypes.c_void_p(logits[b].data_ptr()), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+               ctypes.c_void_p(ids[b].data_ptr()), None, ctypes.c_void_p(ws.data_ptr()), need, t, hidden, ffn, ne, tk,
+               sp) for b in range(npb)]
+
+        def pstep():
+            for a in cl:
+                pf(*a)
+        pstep()
+        tl = timer.run(pstep, max(2, args.steps // 2)) / npb
+        idh = ids.cpu().numpy()
+        distinct = float(np.mean([len(np.unique(idh[b])) for b in range(npb)]))
+        uniq = distinct * expert_bytes
+        # algorithmic work: per (token, rank) pair 2 flop per weight of W_gate, W_up and W_down
+        flops = t * tk * 2 * 3 * hidden * ffn
+        res["moe_prefill_T512"] = {"us_per_layer": tl * 1e6, "tokens_per_s_per_layer": t / tl,
+                                   "distinct_experts": distinct, "unique_expert_bytes": uniq,
+                                   "GBps_unique_expert_bytes": uniq / tl / 1e9,
+                                   "frac_of_8TBps": uniq / tl / 1e9 / HBM_PEAK_GBPS,
+                                   "roofline_us": uniq / (HBM_PEAK_GBPS * 1e9) * 1e6,
+                                   "TFLOPs": flops / tl / 1e12}
+        log(f"[bench] {fmt} MoE prefill T={t}: {tl * 1e6:.1f} us/layer, {uniq / tl / 1e9:.0f} GB/s of unique expert "
+            f"bytes ({uniq / tl / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s; roofline {uniq / 8e12 * 1e6:.1f} us), "
+            f"{flops / tl / 1e12:.0f} TFLOP/s")
+    del banks
+    return res
+
+
 def bench_format(args, torch, np, q, synth, timer, dev, sp, fmt):
-    """GEMV of another block format (IQ4_XS, Q5_K, Q6_K or Q4_0) over a pool of layer copies
-    (the dense FFN shapes), M = 1..4."""
+    """GEMV of another block format over a pool of layer copies (the dense FFN shapes), M = 1..4."""
     L = q.lib
     copies = args.iq4_copies
     gen = {"iq4_xs": synth.torch_iq4_xs_weights, "q5_k": synth.torch_q5_k_weights,
            "q6_k": synth.torch_q6_k_weights, "q4_0": synth.torch_q4_0_weights}[fmt]
-    entry = {"iq4_xs": L.qmv_iq4_xs, "q5_k": L.qmv_q5_k, "q6_k": L.qmv_q6_k, "q4_0": L.qmv_q4_0}[fmt]
+    entry = checked({"iq4_xs": L.qmv_iq4_xs, "q5_k": L.qmv_q5_k, "q6_k": L.qmv_q6_k, "q4_0": L.qmv_q4_0}[fmt],
+                    f"qmv_{fmt}")
     nbytes = {"iq4_xs": q.iq4_xs_bytes, "q5_k": q.q5_k_bytes, "q6_k": q.q6_k_bytes, "q4_0": q.q4_0_bytes}[fmt]
     log(f"[bench] generating the {fmt} pool: {copies} layer copies")
     pool = [[gen(41, n, k, dev, stream=3 * c + i) for i, (_, n, k) in enumerate(SHAPES)] for c in range(copies)]
@@ -429,28 +492,25 @@ def bench_format(args, torch, np, q, synth, timer, dev, sp, fmt):
     shape_bytes = [nbytes(n, k) for _, n, k in SHAPES]
     out = {}
 
-    def calls_for(m, shapes):
-        return [(ctypes.c_void_p(pool[c][i].data_ptr()), pool[c][i].numel(), ctypes.c_void_p(xs[k].data_ptr()),
-                 ctypes.c_void_p(ys[n].data_ptr()), m, n, k, sp)
-                for c in range(copies) for i, (_, n, k) in enumerate(SHAPES) if i in shapes]
+    def stepper(m, shapes):
+        cl = [(ctypes.c_void_p(pool[c][i].data_ptr()), pool[c][i].numel(), ctypes.c_void_p(xs[k].data_ptr()),
+               ctypes.c_void_p(ys[n].data_ptr()), m, n, k, sp)
+              for c in range(copies) for i, (_, n, k) in enumerate(SHAPES) if i in shapes]
 
-    def stepper(cl):
         def step():
             for a in cl:
-                rc = entry(*a)
-                if rc:
-                    raise q.QmvError(rc, f"qmv_{fmt}")
+                entry(*a)
         return step
 
     for m in (1, 2, 3, 4):
-        step = stepper(calls_for(m, (0, 1, 2)))
+        step = stepper(m, (0, 1, 2))
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < 0.3:
             step()
         t = timer.run(step, max(2, args.steps // 2))
         out[f"M{m}"] = {"GBps": copies * sum(shape_bytes) / t / 1e9, "us_per_launch": t / (3 * copies) * 1e6}
     for i, (name, n, k) in enumerate(SHAPES):
-        t = timer.run(stepper(calls_for(1, (i,))), max(2, args.steps // 2)) / copies
+        t = timer.run(stepper(1, (i,)), max(2, args.steps // 2)) / copies
         out[f"M1_{name}"] = {"us_per_launch": t * 1e6, "GBps": shape_bytes[i] / t / 1e9}
     log(f"[bench] {fmt} GEMV: " + ", ".join(f"M={m} {out[f'M{m}']['GBps']:.0f} GB/s" for m in (1, 2, 3, 4)) +
         "; M=1 per launch " + ", ".join(f"{nm} {out[f'M1_{nm}']['us_per_launch']:.2f} us" for nm, _, _ in SHAPES))
@@ -462,6 +522,8 @@ def bench_prefill(args, torch, np, q, synth, timer, dev, sp, pool):
     m = 512
     out = {}
     L = q.lib
+    f = checked(L.qmm_q4_k_prefill, "qmm_q4_k_prefill")
+    util = measured("prefill_mfma_util")
     for i, (name, n, k) in enumerate(SHAPES[1:], start=1):
         x = torch.from_numpy(synth.bf16_normal(31, (m, k)).view(np.int16)).to(dev)
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
@@ -469,14 +531,12 @@ def bench_prefill(args, torch, np, q, synth, timer, dev, sp, pool):
         need = L.qmm_q4_k_prefill_workspace(m, n, k)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         ws_arg = ctypes.c_void_p(ws.data_ptr()) if need else None
-        calls = [(ctypes.c_void_p(pool[c][i].data_ptr()), pool[c][i].numel(), ctypes.c_void_p(x.data_ptr()),
-                  ctypes.c_void_p(y.data_ptr()), m, n, k, ws_arg, need, sp) for c in range(copies)]
+        cl = [(ctypes.c_void_p(pool[c][i].data_ptr()), pool[c][i].numel(), ctypes.c_void_p(x.data_ptr()),
+               ctypes.c_void_p(y.data_ptr()), m, n, k, ws_arg, need, sp) for c in range(copies)]
 
         def step():
-            for a in calls:
-                rc = L.qmm_q4_k_prefill(*a)
-                if rc:
-                    raise q.QmvError(rc, "qmm_q4_k_prefill")
+            for a in cl:
+                f(*a)
         # matrix-core clocks settle only after sustained work: about 0.3 s of
         # untimed passes before the timed ones
         t0 = time.perf_counter()
@@ -491,39 +551,110 @@ def bench_prefill(args, torch, np, q, synth, timer, dev, sp, pool):
         torch.matmul(a, b.t())
         tt = timer.run(lambda: torch.matmul(a, b.t()), 10)
         out[name] = {"us": tp * 1e6, "TFLOPs": flops / tp / 1e12, "frac_of_bf16_peak": flops / tp / 1e12 / BF16_PEAK_TFLOPS,
-                     "torch_bf16_dense_TFLOPs": flops / tt / 1e12, "k_split_workspace_bytes": need}
+                     "torch_bf16_dense_TFLOPs": flops / tt / 1e12, "k_split_workspace_bytes": need,
+                     "mfma_util_counters": (util or {}).get(name)}
         log(f"[bench] prefill {name} {m}x{n}x{k}: {tp * 1e6:.1f} us, {flops / tp / 1e12:.0f} TFLOP/s "
-            f"(torch dense bf16: {flops / tt / 1e12:.0f})")
+            f"({flops / tp / 1e12 / BF16_PEAK_TFLOPS:.3f} of 2.5 PFLOP/s; torch dense bf16: {flops / tt / 1e12:.0f})")
     return out
 
 
-def cpu_baseline(args, np, synth):
-    """The fp64 oracle on the host cores: layer copies (gate, up, down) at M=1 until the budget is spent."""
+def cpu_baseline(np, synth):
+    """The fp64 oracle as it stands, on the host cores: dequant (numpy) and the
+    products (numpy/BLAS) timed apart, once with one BLAS thread and once with
+    the whole BLAS pool, on bounded samples of each workload."""
     import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
 
-    # threads actually used: the dequant is single-threaded numpy, the matvec runs on the BLAS pool
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] + [1])
-    except ImportError:
-        cores = len(os.sched_getaffinity(0))
-    done_bytes, spent, mats = 0, 0.0, 0
-    while spent < args.cpu_seconds or mats < 3:
-        i = mats % 3
-        _, n, k = SHAPES[i]
-        raw = synth.q4_k_weights(40 + mats // 3, n, k, stream=i)
-        x = synth.bf16_normal(41, (1, k))
-        t0 = time.perf_counter()
-        oracle.qmv_q4_k(raw, x, n, k)
-        spent += time.perf_counter() - t0
-        done_bytes += raw.size
-        mats += 1
-    log(f"[bench] cpu oracle: {mats} matrices, {spent:.1f} s, {done_bytes / spent / 1e9:.3f} GB/s")
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{mats} Q4_K matrices of the dense pool shapes (gate/up 17408x5120, down 5120x17408) at M=1, "
-                      f"{done_bytes / 1e9:.2f} GB of blocks: fp64 dequant (numpy, one thread) + fp64 matvec "
-                      f"(BLAS, up to `cores` threads); input generation excluded",
-            "seconds": round(spent, 2)}
+    affinity = len(os.sched_getaffinity(0))
+    pool_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] + [1])
+
+    def timed(fn, min_s=0.2):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            r = fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_s:
+                return el / reps, r
+
+    out = {"cores_affinity": affinity, "blas_threads_all": pool_threads}
+    t_start = time.perf_counter()
+    # C1 (and the prefill's weights): sampled rows of the gate and down shapes; the
+    # dequant is the oracle's (single-threaded numpy), the products BLAS
+    samples = {"gate": (4096, 5120), "down": (1024, 17408)}
+    raws, ws = {}, {}
+    for name, (rows, k) in samples.items():
+        raws[name] = synth.q4_k_weights(40, rows, k, stream=len(name))
+        td, ws[name] = timed(lambda: oracle.dequant_q4_k(raws[name], rows, k), 0.5)
+        out[f"C1_{name}_dequant_s"] = td
+    x4 = {k: oracle.bf16_bits_to_f64(synth.bf16_normal(41, (4, k))) for _, k in samples.values()}
+    c1 = {}
+    for threads, label in ((1, "1thread"), (pool_threads, "all")):
+        with threadpool_limits(limits=threads, user_api="blas"):
+            for m in (1, 2, 3, 4):
+                qbytes = sum(raws[n].size for n in samples)
+                tdq = sum(out[f"C1_{n}_dequant_s"] for n in samples)
+                tmv = sum(timed(lambda n=n: x4[samples[n][1]][:m] @ ws[n].T)[0] for n in samples)
+                c1[f"{label}_M{m}"] = {"dequant_s": tdq, "matvec_s": tmv, "GBps": qbytes / (tdq + tmv) / 1e9,
+                                       "GBps_matvec_only": qbytes / tmv / 1e9,
+                                       "weights_per_s": sum(ws[n].size for n in samples) / (tdq + tmv)}
+    out["C1"] = c1
+    # C0: the whole 1024x1024 Q8_0 matrix
+    raw8 = synth.q8_0_weights(3, 1024, 1024)
+    x8 = synth.f32_normal(4, (1, 1024)).astype(np.float64)
+    td8, w8 = timed(lambda: oracle.dequant_q8_0(raw8, 1024, 1024))
+    c0 = {"dequant_s": td8}
+    for threads, label in ((1, "1thread"), (pool_threads, "all")):
+        with threadpool_limits(limits=threads, user_api="blas"):
+            tm8 = timed(lambda: x8 @ w8.T)[0]
+        c0[f"{label}_matvec_s"] = tm8
+        c0[f"{label}_us_per_call"] = (td8 + tm8) * 1e6
+    out["C0"] = c0
+    # C4: the prefill product on a 1024-row sample of the up shape, M = 512
+    xp = oracle.bf16_bits_to_f64(synth.bf16_normal(42, (512, 5120)))
+    w4 = ws["gate"][:1024]
+    c4 = {"dequant_s_per_1024_rows": out["C1_gate_dequant_s"] / 2}
+    for threads, label in ((1, "1thread"), (pool_threads, "all")):
+        with threadpool_limits(limits=threads, user_api="blas"):
+            tg = timed(lambda: xp @ w4.T)[0]
+        c4[f"{label}_gemm_s"] = tg
+        c4[f"{label}_GFLOPs_gemm_only"] = 2 * 512 * 1024 * 5120 / tg / 1e9
+        c4[f"{label}_GFLOPs_with_dequant"] = 2 * 512 * 1024 * 5120 / (tg + c4["dequant_s_per_1024_rows"]) / 1e9
+    out["C4"] = c4
+    # C3: one 35B-A3B bank, T = 1 and 3; the dequant of the chosen experts timed alone
+    hidden, ffn, ne, tk = 2048, 768, 128, 8
+    gate, up, down = synth.moe_bank(21, ne, hidden, ffn)
+    c3 = {}
+    for t in (1, 3):
+        logits = synth.moe_logits(22, t, ne)
+        xm = synth.bf16_normal(23, (t, hidden))
+        ids, _ = oracle.route_top_k(logits, tk)
+        experts = sorted(set(int(e) for e in ids.reshape(-1)))
+
+        def dq():
+            for e in experts:
+                oracle.dequant_q4_k(oracle.expert_matrix(gate, e, ffn, hidden), ffn, hidden)
+                oracle.dequant_q4_k(oracle.expert_matrix(up, e, ffn, hidden), ffn, hidden)
+                oracle.dequant_q4_k(oracle.expert_matrix(down, e, hidden, ffn), hidden, ffn)
+        tdq = timed(dq, 0.1)[0]
+        entry = {"distinct_experts": len(experts), "dequant_s": tdq}
+        for threads, label in ((1, "1thread"), (pool_threads, "all")):
+            with threadpool_limits(limits=threads, user_api="blas"):
+                tt = timed(lambda: oracle.moe_q4_k(gate, up, down, logits, xm, hidden, ffn, ne, tk), 0.1)[0]
+            entry[f"{label}_layer_s"] = tt
+            entry[f"{label}_tok_equiv_per_s"] = t / (48 * tt)
+        c3[f"T{t}"] = entry
+    out["C3"] = c3
+    out["wall_s"] = time.perf_counter() - t_start
+    v = c1["all_M1"]["GBps"]
+    log(f"[bench] cpu oracle: C1 M=1 {v:.4f} GB/s (all {pool_threads} BLAS threads; 1 thread "
+        f"{c1['1thread_M1']['GBps']:.4f}), C3 T=1 {c3['T1']['all_tok_equiv_per_s']:.2f} tok-equiv/s, "
+        f"C4 {c4['all_GFLOPs_with_dequant']:.1f} GFLOP/s; {out['wall_s']:.1f} s")
+    return {"value": round(v, 4), "unit": "GB/s", "cores": pool_threads, "kind": "oracle",
+            "sample": "C1 M=1: 4096 rows of the gate shape (17408x5120) and 1024 rows of the down shape "
+                      "(5120x17408), fp64 dequant (numpy, one thread) + fp64 matvec (BLAS, all pool threads); "
+                      "1-thread and per-config figures (C0, C1 M=1..4, C3 T=1/3, C4 M=512 on 1024 rows) in detail",
+            "detail": out}
 
 
 if __name__ == "__main__":

@@ -19,7 +19,7 @@ __all__ = [
     "qmv_iq4_xs_moe_workspace", "qmm_q4_k_prefill_workspace",
     "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16", "qmv_dequant_q8_0_f32",
     "qmv_dequant_iq4_xs_f32", "qmv_q5_k", "qmv_dequant_q5_k_f32", "qmv_q6_k", "qmv_dequant_q6_k_f32", "qmv_q4_0",
-    "qmv_dequant_q4_0_f32", "q4_0_bytes",
+    "qmv_dequant_q4_0_f32", "qmv_stream_read", "q4_0_bytes",
     "q4_k_bytes", "q5_k_bytes", "q6_k_bytes", "q8_0_bytes",
     "iq4_xs_bytes", "EXPORTS",
 ]
@@ -57,6 +57,7 @@ EXPORTS = {
     "qmv_dequant_q5_k_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
     "qmv_dequant_q6_k_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
     "qmv_dequant_q4_0_f32": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _vp]),
+    "qmv_stream_read": (_c_int, [_vp, _c_size, _vp, _c_int, _c_int, _c_int, _vp]),
 }
 
 
@@ -419,3 +420,14 @@ def qmv_dequant_q4_0_f32(w, n: int, k: int, out=None, stream=None):
     _dev(out, "out", (torch.float32,))
     _check(lib.qmv_dequant_q4_0_f32(_ptr(w), _nbytes(w), _ptr(out), n, k, _stream(stream)), "qmv_dequant_q4_0_f32")
     return out
+
+
+def qmv_stream_read(buf, grid: int = 1024, depth: int = 4, nontemporal: bool = False, sink=None, stream=None):
+    """Plain streaming read of a device buffer (a measurement aid); returns the
+    per-workgroup XOR words (uint32 as int32, [grid])."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(grid, dtype=torch.int32, device=buf.device)
+    _check(lib.qmv_stream_read(_ptr(buf), _nbytes(buf), _ptr(sink), grid, depth, int(nontemporal), _stream(stream)),
+           "qmv_stream_read")
+    return sink

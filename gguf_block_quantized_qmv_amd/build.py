@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqmv.so")
 
-HIP_SOURCES = ["q4k_gemv.hip", "q8_0.hip", "q4k_dequant.hip", "q4k_moe.hip", "q4k_prefill.hip", "iq4xs_gemv.hip", "iq4xs_moe.hip", "q6k_gemv.hip", "q4k_moe_grouped.hip"]
+HIP_SOURCES = ["q4k_gemv.hip", "q8_0.hip", "q4k_dequant.hip", "q4k_moe.hip", "q4k_prefill.hip", "iq4xs_gemv.hip", "iq4xs_moe.hip", "q6k_gemv.hip", "q4k_moe_grouped.hip", "calib_read.hip"]
 HOST_SOURCES = ["qmv_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

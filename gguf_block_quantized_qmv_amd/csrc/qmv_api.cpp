@@ -388,4 +388,16 @@ int qmv_dequant_q8_0_f32(const void *w, size_t w_bytes, float *out, int n, int k
   return qmv::launch_dequant_q8_0(w, out, n, k, stream);
 }
 
+int qmv_stream_read(const void *p, size_t bytes, uint32_t *sink, int grid, int depth, int nontemporal,
+                    void *stream) {
+  if (!p || !sink) return QMV_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return QMV_ERR_SIZE;
+  if (grid < 1 || grid > 65536 || (depth != 1 && depth != 2 && depth != 4 && depth != 8) ||
+      (nontemporal != 0 && nontemporal != 1))
+    return QMV_ERR_RANGE;
+  if (!aligned(p, 16) || !aligned(sink, 4)) return QMV_ERR_ALIGN;
+  if (overlap(sink, (size_t)grid * 4, p, bytes)) return QMV_ERR_ALIAS;
+  return qmv::launch_stream_read(p, bytes, sink, grid, depth, nontemporal, stream);
+}
+
 }  // extern "C"

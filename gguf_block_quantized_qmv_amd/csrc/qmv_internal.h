@@ -33,5 +33,6 @@ int launch_iq4_xs_moe(const void *w_gate, const void *w_up, const void *w_down, 
                       const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, void *ws, int t,
                       int hidden, int ffn, int n_experts, int top_k, void *stream);
 int launch_q4_k_prefill(const void *w, const uint16_t *x, float *y, void *ws, int m, int n, int k, void *stream);
+int launch_stream_read(const void *p, size_t bytes, uint32_t *sink, int grid, int depth, int nontemporal, void *stream);
 
 }  // namespace qmv

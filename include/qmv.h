@@ -359,6 +359,22 @@ int qmv_dequant_q5_k_f32(const void *w, size_t w_bytes, float *out, int n, int k
 int qmv_dequant_q6_k_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 int qmv_dequant_q4_0_f32(const void *w, size_t w_bytes, float *out, int n, int k, void *stream);
 
+/*
+ * Measurement aid, outside the product path: reads `bytes` of device memory
+ * with plain coalesced 16-byte loads (a grid-strided walk over `grid`
+ * workgroups of 256 threads, `depth` loads in flight per thread; non-temporal
+ * loads if `nontemporal` is 1) and writes the XOR of each workgroup's 32-bit
+ * words to sink[0 .. grid). The rate
+ * it reaches over the GEMVs' own weight pool is the achievable HBM read ceiling
+ * their rates are read against (the roofline stays the 8 TB/s peak).
+ *   p     16-byte aligned, bytes > 0 and a multiple of 16
+ *   sink  uint32 [grid], 4-byte aligned, not overlapping p
+ *   1 <= grid <= 65536, depth in {1, 2, 4, 8}, nontemporal in {0, 1}, else QMV_ERR_RANGE.
+ * (This library's own: the pages measure no kernel.)
+ */
+int qmv_stream_read(const void *p, size_t bytes, uint32_t *sink, int grid, int depth, int nontemporal,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

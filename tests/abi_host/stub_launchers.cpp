@@ -54,5 +54,6 @@ int launch_iq4_xs_moe(const void *, const void *, const void *, const float *, c
 int launch_q4_k_prefill(const void *, const uint16_t *, float *, void *ws, int m, int n, int k, void *) {
   return note(m, n, k, ws);
 }
+int launch_stream_read(const void *, size_t, uint32_t *, int grid, int depth, int nt, void *) { return note(grid, depth, nt); }
 
 }  // namespace qmv

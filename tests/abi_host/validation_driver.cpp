@@ -220,6 +220,22 @@ void prefill() {
       }
 }
 
+void stream_read() {
+  uint32_t *sink = static_cast<uint32_t *>(at(2));
+  EXPECT(qmv_stream_read(W, 1 << 20, sink, 2048, 4, 1, nullptr) == QMV_OK);
+  EXPECT(stub::last_m == 2048 && stub::last_n == 4 && stub::last_k == 1);
+  EXPECT(qmv_stream_read(W, 16, sink, 1, 1, 2, nullptr) == QMV_ERR_RANGE);
+  EXPECT(qmv_stream_read(nullptr, 16, sink, 1, 1, 0, nullptr) == QMV_ERR_NULL);
+  EXPECT(qmv_stream_read(W, 0, sink, 1, 1, 0, nullptr) == QMV_ERR_SIZE);
+  EXPECT(qmv_stream_read(W, 24, sink, 1, 1, 0, nullptr) == QMV_ERR_SIZE);
+  EXPECT(qmv_stream_read(W, 16, sink, 1, 3, 0, nullptr) == QMV_ERR_RANGE);
+  EXPECT(qmv_stream_read(W, 16, sink, 65537, 1, 0, nullptr) == QMV_ERR_RANGE);
+  EXPECT(qmv_stream_read(at(0, 8), 16, sink, 1, 1, 0, nullptr) == QMV_ERR_ALIGN);
+  EXPECT(qmv_stream_read(W, 1 << 20, static_cast<uint32_t *>(at(0, 1024)), 4, 1, 0, nullptr) == QMV_ERR_ALIAS);
+  for (int g : kInts)
+    for (int u : kInts) EXPECT(is_code(qmv_stream_read(W, 4096, sink, g, u, u & 3, nullptr)));
+}
+
 }  // namespace
 
 int main() {
@@ -233,6 +249,7 @@ int main() {
   moe(qmv_iq4_xs_moe, qmv_iq4_xs_moe_workspace, 136);
   moe_prefill();
   prefill();
+  stream_read();
   printf("validation driver: %d launches reached, %d failures\n", stub::launches, failures);
   return failures ? 1 : 0;
 }
