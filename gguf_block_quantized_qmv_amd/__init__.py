@@ -15,6 +15,7 @@ import os
 __all__ = [
     "QmvError", "lib", "LIB_PATH", "version",
     "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmv_q4_k_moe_prefill",
+    "qmv_q4_k_moe_noalloc",
     "qmv_q4_k_moe_prefill_workspace", "qmv_iq4_xs_moe",
     "qmv_iq4_xs_moe_workspace", "qmm_q4_k_prefill_workspace",
     "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16", "qmv_dequant_q8_0_f32",
@@ -42,6 +43,8 @@ EXPORTS = {
     "qmv_q4_k_moe_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "qmv_q4_k_moe": (_c_int, [_vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
                               _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "qmv_q4_k_moe_noalloc": (_c_int, [_vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "qmv_q4_k_moe_prefill_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "qmv_q4_k_moe_prefill": (_c_int, [_vp, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
                                       _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),

@@ -504,6 +504,40 @@ int launch_t(const void *w_gate, const void *w_up, const void *w_down, const flo
 
 }  // namespace
 
+namespace {
+
+// Scratch of qmv_q4_k_moe_noalloc: the routing tables and h of one call, in a
+// fixed device array instead of a caller's workspace. Each GPU the library
+// runs on holds its own copy until the process ends. Host code never passes
+// the array's name to a kernel (on the host it only stands in for the symbol):
+// it uses the device address hipGetSymbolAddress returns, looked up once per
+// device and kept here.
+static __device__ __align__(256) uint8_t scratch[layout::kMoeNoAllocBytes];
+std::atomic<void *> g_scratch_addr[LdsGrant::kDevices];
+
+// Device address of `scratch` on the current device, or nullptr after
+// recording the HIP error.
+void *scratch_address() {
+  int d = 0;
+  hipError_t e = hipGetDevice(&d);
+  if (e == hipSuccess && (d < 0 || d >= LdsGrant::kDevices)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    set_error_detail("qmv_q4_k_moe_noalloc device", (int)e, hipGetErrorString(e));
+    return nullptr;
+  }
+  void *p = g_scratch_addr[d].load(std::memory_order_acquire);
+  if (p) return p;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    set_error_detail("qmv_q4_k_moe_noalloc scratch address", (int)e, hipGetErrorString(e));
+    return nullptr;
+  }
+  g_scratch_addr[d].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+
 int launch_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, const float *logits, const uint16_t *x,
                     float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, void *ws, int t, int hidden, int ffn,
                     int n_experts, int top_k, void *stream) {
@@ -515,6 +549,17 @@ int launch_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, co
     case 4: return launch_t<4>(w_gate, w_up, w_down, logits, x, y, topk_ids, topk_w, pairs, ws, hidden, ffn, n_experts, top_k, s);
     default: return QMV_ERR_RANGE;
   }
+}
+
+int launch_q4_k_moe_noalloc(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
+                            const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, int t,
+                            int hidden, int ffn, int n_experts, int top_k, void *stream) {
+  // the launches write every table and h value they read, so nothing in the
+  // array needs clearing between calls
+  void *ws = scratch_address();
+  if (!ws) return QMV_ERR_HIP;
+  return launch_q4_k_moe(w_gate, w_up, w_down, logits, x, y, topk_ids, topk_w, pairs, ws, t, hidden, ffn, n_experts,
+                         top_k, stream);
 }
 
 }  // namespace qmv

@@ -79,11 +79,13 @@ bool moe_args_ok(MoeFormat f, int t, int hidden, int ffn, int n_experts, int top
                                : qmv::layout::iq4xs_moe_fits_lds(t, hidden, ffn, top_k));
 }
 
-// Host-side checks of a routed-expert decode call of t tokens.
+// Host-side checks of a routed-expert decode call of t tokens. caller_ws: the
+// call brings its own workspace (ws, ws_bytes); otherwise it runs in the
+// library's fixed scratch array, which must hold the call's workspace.
 int moe_check(MoeFormat f, const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes,
               const float *logits, const uint16_t *x_bf16, float *y, int32_t *topk_ids, float *topk_w,
               int32_t *pairs, void *ws, size_t ws_bytes, int t, int hidden, int ffn, int n_experts,
-              int top_k) {
+              int top_k, bool caller_ws = true) {
   if (!w_gate || !w_up || !w_down || !logits || !x_bf16 || !y) return QMV_ERR_NULL;
   if (t < 1 || t > QMV_MOE_MAX_TOKENS || n_experts < 1 || n_experts > QMV_MOE_MAX_EXPERTS ||
       top_k < 1 || top_k > QMV_MOE_MAX_TOP_K || top_k > n_experts)
@@ -101,7 +103,7 @@ int moe_check(MoeFormat f, const void *w_gate, const void *w_up, const void *w_d
       !aligned(ws, 256))
     return QMV_ERR_ALIGN;
   const size_t need = qmv::layout::moe_workspace(t, ffn, top_k);
-  if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
+  if (caller_ws ? (!ws || ws_bytes < need) : need > qmv::layout::kMoeNoAllocBytes) return QMV_ERR_WORKSPACE;
 
   // every output (and the workspace) must be disjoint from every input and from each other
   const size_t ta = (size_t)t;
@@ -109,7 +111,7 @@ int moe_check(MoeFormat f, const void *w_gate, const void *w_up, const void *w_d
   const void *in_p[] = {w_gate, w_up, w_down, logits, x_bf16};
   const size_t in_b[] = {bank, bank, bank, ta * n_experts * 4, ta * hidden * 2};
   const void *out_p[] = {y, topk_ids, topk_w, pairs, ws};
-  const size_t out_b[] = {yb, topk_ids ? idb : 0, topk_w ? idb : 0, pairs ? pb : 0, need};
+  const size_t out_b[] = {yb, topk_ids ? idb : 0, topk_w ? idb : 0, pairs ? pb : 0, caller_ws ? need : 0};
   for (int o = 0; o < 5; ++o) {
     for (int i = 0; i < 5; ++i)
       if (overlap(out_p[o], out_b[o], in_p[i], in_b[i])) return QMV_ERR_ALIAS;
@@ -209,6 +211,16 @@ int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_
                  size_t ws_bytes, int t, int hidden, int ffn, int n_experts, int top_k, void *stream) {
   return moe_entry(MoeFormat::kQ4K, w_gate, w_up, w_down, bank_bytes, logits, x_bf16, y, topk_ids, topk_w, pairs, ws,
                    ws_bytes, t, hidden, ffn, n_experts, top_k, stream);
+}
+
+int qmv_q4_k_moe_noalloc(const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes,
+                         const float *logits, const uint16_t *x_bf16, float *y, int32_t *topk_ids, float *topk_w,
+                         int32_t *pairs, int t, int hidden, int ffn, int n_experts, int top_k, void *stream) {
+  const int rc = moe_check(MoeFormat::kQ4K, w_gate, w_up, w_down, bank_bytes, logits, x_bf16, y, topk_ids, topk_w,
+                           pairs, nullptr, 0, t, hidden, ffn, n_experts, top_k, false);
+  if (rc) return rc;
+  return qmv::launch_q4_k_moe_noalloc(w_gate, w_up, w_down, logits, x_bf16, y, topk_ids, topk_w, pairs, t, hidden,
+                                      ffn, n_experts, top_k, stream);
 }
 
 size_t qmv_q4_k_moe_prefill_workspace(int t, int hidden, int ffn, int n_experts, int top_k) {

@@ -26,6 +26,9 @@ int launch_dequant_q8_0(const void *w, float *out, int n, int k, void *stream);
 int launch_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
                     const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs,
                     void *ws, int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
+int launch_q4_k_moe_noalloc(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
+                            const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, int t,
+                            int hidden, int ffn, int n_experts, int top_k, void *stream);
 int launch_q4_k_moe_grouped(const void *w_gate, const void *w_up, const void *w_down, const float *logits,
                             const uint16_t *x, float *y, int32_t *topk_ids, float *topk_w, void *ws, int t,
                             int hidden, int ffn, int n_experts, int top_k, void *stream);

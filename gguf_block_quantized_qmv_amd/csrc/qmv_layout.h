@@ -69,6 +69,13 @@ constexpr size_t q4k_moe_down_lds(int pairs, int ffn) {
 constexpr bool q4k_moe_fits_lds(int t, int hidden, int ffn, int top_k) {
   return q4k_moe_gate_up_lds(t, hidden) <= kLdsBudget - 4096 && q4k_moe_down_lds(t * top_k, ffn) <= kLdsBudget - 4096;
 }
+// Device scratch of the allocation-free routed-expert entry point: one fixed
+// array per GPU. Every call that passes q4k_moe_fits_lds fits in it: the down
+// stage holds t * top_k * ffn * 4.375 bytes of h rows and sums in LDS, at most
+// kLdsBudget - 4096, so h (4 bytes per value) is at most 146,051 bytes and the
+// workspace at most 4096 + 146,051 < 160 KiB.
+constexpr size_t kMoeNoAllocBytes = QMV_MOE_NOALLOC_BYTES;
+static_assert(kMoeNoAllocBytes == 160 * 1024, "the bound derived above");
 // IQ4_XS: x rows pair-interleaved as in its GEMV; h in fp32 with a 144-byte
 // sub-block stride. Static LDS stays under 8 KiB.
 constexpr size_t iq4xs_moe_gate_up_lds(int t, int hidden) {

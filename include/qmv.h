@@ -252,6 +252,27 @@ int qmv_q4_k_moe(const void *w_gate, const void *w_up, const void *w_down, size_
                  int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
 
 /*
+ * qmv_q4_k_moe without a workspace argument, for callers that cannot allocate
+ * device memory: code recorded into a HIP graph, tight serving loops, and
+ * harnesses that forbid allocation. The routing tables and h live in one
+ * fixed 160 KiB device array per GPU (QMV_MOE_NOALLOC_BYTES), which the
+ * library holds until the process ends; the call allocates and frees nothing.
+ * Every call that passes qmv_q4_k_moe's limits fits in it (the LDS limit on h
+ * bounds the workspace to under 150 KiB); a call whose workspace would exceed
+ * it returns QMV_ERR_WORKSPACE. Arguments, results (bit for bit), routing
+ * outputs and the other error codes are those of qmv_q4_k_moe. All calls on
+ * one GPU share the array, which keeps the last call's contents (each call
+ * writes every value it reads, so nothing needs clearing): calls that overlap
+ * in time on one GPU -- on different streams, or from different host threads
+ * without ordering -- race and give undefined results.
+ */
+#define QMV_MOE_NOALLOC_BYTES 163840
+int qmv_q4_k_moe_noalloc(const void *w_gate, const void *w_up, const void *w_down, size_t bank_bytes,
+                         const float *logits, const uint16_t *x_bf16, float *y,
+                         int32_t *topk_ids, float *topk_w, int32_t *pairs,
+                         int t, int hidden, int ffn, int n_experts, int top_k, void *stream);
+
+/*
  * Routed-expert MoE feed-forward for a prompt's tokens (prefill), Q4_K experts.
  * Arguments, routing, outputs and error codes as qmv_q4_k_moe, except:
  *   1 <= t <= QMV_MOE_PREFILL_MAX_TOKENS; logits, x_bf16, y, topk_ids and

@@ -43,6 +43,10 @@ int launch_q4_k_moe(const void *, const void *, const void *, const float *, con
                     float *, int32_t *, void *ws, int t, int hidden, int ffn, int, int, void *) {
   return note(t, hidden, ffn, ws);
 }
+int launch_q4_k_moe_noalloc(const void *, const void *, const void *, const float *, const uint16_t *, float *,
+                            int32_t *, float *, int32_t *, int t, int hidden, int ffn, int, int, void *) {
+  return note(t, hidden, ffn, nullptr);
+}
 int launch_q4_k_moe_grouped(const void *, const void *, const void *, const float *, const uint16_t *, float *,
                             int32_t *, float *, void *ws, int t, int hidden, int ffn, int, int, void *) {
   return note(t, hidden, ffn, ws);

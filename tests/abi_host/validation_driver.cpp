@@ -157,6 +157,38 @@ void moe(MoeFn fn, MoeWs wsfn, int block_bytes) {
           }
 }
 
+void moe_noalloc() {
+  const void *wg = at(0), *wu = at(4), *wd = at(5);
+  const float *lg = static_cast<const float *>(at(1));
+  const uint16_t *xb = static_cast<const uint16_t *>(at(1, 1 << 20));
+  int32_t *ids = static_cast<int32_t *>(at(2, 1 << 20));
+  for (int t = 1; t <= 4; ++t) {
+    const int h = 2048, f = 768, e = 128, k = 8;
+    const size_t bank = (size_t)e * f * (h / 256) * 144;
+    const int before = stub::launches;
+    EXPECT(qmv_q4_k_moe_noalloc(wg, wu, wd, bank, lg, xb, Y, ids, nullptr, nullptr, t, h, f, e, k, nullptr) == QMV_OK);
+    EXPECT(stub::launches == before + 1 && stub::last_m == t);
+    EXPECT(qmv_q4_k_moe_noalloc(wg, wu, wd, bank - 1, lg, xb, Y, ids, nullptr, nullptr, t, h, f, e, k, nullptr) ==
+           QMV_ERR_SIZE);
+    EXPECT(qmv_q4_k_moe_noalloc(wg, wu, wd, bank, lg, xb, static_cast<float *>(at(4, 256)), ids, nullptr, nullptr, t,
+                                h, f, e, k, nullptr) == QMV_ERR_ALIAS);
+  }
+  // every call within the decode limits fits the fixed scratch: sweep the LDS-limited (pairs, ffn) corner
+  for (int t = 1; t <= 4; ++t)
+    for (int k = 1; k <= 8; ++k)
+      for (int f = 256; f <= 65536; f += 256) {
+        const int h = 256, e = 8;
+        const size_t bank = (size_t)e * f * (h / 256) * 144;
+        const size_t need = qmv_q4_k_moe_workspace(t, h, f, e, k);
+        const int rc = qmv_q4_k_moe_noalloc(wg, wu, wd, bank, lg, xb, Y, ids, nullptr, nullptr, t, h, f, e, k, nullptr);
+        EXPECT(need == 0 ? rc == QMV_ERR_RANGE : rc == QMV_OK);
+        EXPECT(need <= QMV_MOE_NOALLOC_BYTES);
+      }
+  for (int t : kInts)
+    for (int f : {0, 256, 768, 1024, 4096, INT_MAX / 256 * 256})
+      EXPECT(is_code(qmv_q4_k_moe_noalloc(wg, wu, wd, 1, lg, xb, Y, ids, nullptr, nullptr, t, 2048, f, 128, 8, nullptr)));
+}
+
 void moe_prefill() {
   const void *wg = at(0), *wu = at(4), *wd = at(5);
   const float *lg = static_cast<const float *>(at(1));
@@ -247,6 +279,7 @@ int main() {
   dequant();
   moe(qmv_q4_k_moe, qmv_q4_k_moe_workspace, 144);
   moe(qmv_iq4_xs_moe, qmv_iq4_xs_moe_workspace, 136);
+  moe_noalloc();
   moe_prefill();
   prefill();
   stream_read();

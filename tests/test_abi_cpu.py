@@ -39,7 +39,7 @@ def test_header_lists_the_expected_entry_points():
         "qmv_q5_k", "qmv_dequant_q5_k_f32", "qmv_q6_k", "qmv_dequant_q6_k_f32", "qmv_q4_0",
         "qmv_dequant_q4_0_f32",
         "qmm_q4_k_prefill_workspace", "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16",
-        "qmv_dequant_q8_0_f32", "qmv_stream_read"])
+        "qmv_dequant_q8_0_f32", "qmv_stream_read", "qmv_q4_k_moe_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
