@@ -51,11 +51,11 @@ MEASURED = {
     # FETCH_SIZE scaled by the streaming read of a known size, plus WRITE_SIZE
     # scaled by a 4 GiB device copy (profiles/q4k_gemv_m1_hbm_traffic.md)
     "gemv_traffic": {"sources": (_CSRC + "q4k_gemv.hip", _CSRC + "q4k_common.h", _CSRC + "qmv_device.h",
-                                 _CSRC + "qmv_layout.h"),
+                                 _CSRC + "qmv_layout.h", _CSRC + "qmv_addr.h"),
                      "sha256": "04bb29a35cc6d927614db32e7f0436be5108c497b0132d576131a74f989bc76b", "value": 50855933},
     # MFMA utilisation of the prefill GEMM at M=512 (profiles/q4k_prefill_m512_mfma.md)
     "prefill_mfma_util": {"sources": (_CSRC + "q4k_prefill.hip", _CSRC + "q4k_common.h", _CSRC + "qmv_device.h",
-                                      _CSRC + "qmv_layout.h"),
+                                      _CSRC + "qmv_layout.h", _CSRC + "qmv_addr.h"),
                           "sha256": "b2df1496e717109e4b7d62f1d37cbdb79e50822466f86ba9efceb06fd46d5b6a",
                           "value": {"up": 0.371, "down": 0.365}},
 }

@@ -28,6 +28,7 @@
 // zero scale) and the unit loop is unrolled by kDepth, so every wait is exact.
 // Row r of the output is computed by the same instruction sequence for every M.
 #include "iq4xs_common.h"
+#include "qmv_addr.h"
 #include "qmv_internal.h"
 #include "../../include/qmv.h"
 
@@ -36,10 +37,9 @@ namespace {
 
 using namespace iq4xs;
 
-constexpr int kDepth = 2;          // units of loads in flight per lane
+constexpr int kDepth = addr::kIq4GemvDepth;   // units of loads in flight per lane
 
 constexpr int kStageSub = 2;   // sub-blocks per thread per staging round trip
-using layout::kLdsPerCu;
 static_assert(layout::kIq4xsTableBytes == (size_t)kTableEntries * 4, "the table's LDS bytes");
 
 // Stage sub-block s of activation row r, pair-interleaved, at xs[r * rg + x_slot(s)].
@@ -92,16 +92,17 @@ __global__ __launch_bounds__(T) void iq4xs_gemv_kernel(const uint8_t *__restrict
   const uint8_t *tbl_bytes = reinterpret_cast<const uint8_t *>(tbl);
   const int tid = threadIdx.x;
   const int nblk = k >> 8, nsub = nblk * 8, rg = row_granules(nsub);
-  const int row = blockIdx.x * (T / G) + tid / G;
+  const int row = addr::lane_row(blockIdx.x, tid, T, G);
   const int l = tid % G;
-  const uint8_t *row_ptr = w + (size_t)(row < n ? row : 0) * (size_t)nblk * kIQ4XSBlockBytes;
   // Lane l takes sub-blocks u = l + G t: super-block (l >> 3) + (G / 8) t, sub-block j = l & 7.
-  const int j = l & 7, qoff = 8 + 16 * j;
-  const uint8_t *lane_ptr = row_ptr + (size_t)(l >> 3) * kIQ4XSBlockBytes;
-  constexpr int kUnitBytes = (G / 8) * kIQ4XSBlockBytes;
-  const int nlive = l < nsub ? (nsub - l + G - 1) / G : 0;   // live units of this lane
-  const int nmax = (nsub + G - 1) / G;                        // live units of lane 0
-  const int nslots = (nmax + kDepth - 1) / kDepth * kDepth;
+  const addr::Iq4Lane ln = addr::iq4_lane(G, nblk, (size_t)(row < n ? row : 0), l);
+  const int j = l & 7, qoff = ln.qoff;
+  const uint8_t *row_ptr = w + ln.row_base, *lane_ptr = w + ln.lane_base;
+  const int nlive = ln.nlive;                                   // live units of this lane
+  const int nslots = addr::iq4_slots(G, nblk, kDepth);
+  auto unit_ptr = [&](const int t) -> const uint8_t * {
+    return t < nlive ? lane_ptr + addr::iq4_unit_offset(t, ln.unit_bytes) : row_ptr;
+  };
   // activation granule of unit t: x_slot(l + G t) = x_slot(l) + t * (4 G + G / 4)
   constexpr int kXStride = 4 * G + G / 4;
   const int x_l = x_slot(l < nsub ? l : 0);
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(T) void iq4xs_gemv_kernel(const uint8_t *__restrict
   Unit ring[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d)
-    load_unit(d < nlive ? lane_ptr + (size_t)d * kUnitBytes : row_ptr, qoff, ring[d]);
+    load_unit(unit_ptr(d), qoff, ring[d]);
 
   // table and activations
   if (tid < kTableEntries) tbl[tid] = grid_bf16((uint32_t)tid & 15u) | (grid_bf16((uint32_t)tid >> 4) << 16);
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(T) void iq4xs_gemv_kernel(const uint8_t *__restrict
       // refill the slot kDepth units ahead (clamped, never guarded)
       {
         const int tn = t + kDepth;
-        load_unit(tn < nlive ? lane_ptr + (size_t)tn * kUnitBytes : row_ptr, qoff, ring[d]);
+        load_unit(unit_ptr(tn), qoff, ring[d]);
       }
 #pragma unroll
       for (int r = 0; r < M; ++r) {
@@ -192,25 +193,26 @@ __global__ __launch_bounds__(256) void iq4xs_dequant_kernel(const uint8_t *__res
 
 
 template <int M, int G, int T>
-int launch_mgt(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t s) {
+int launch_mgt(const addr::Iq4Plan &p, const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t s) {
   static LdsGrant granted;
   const size_t lds = layout::iq4xs_gemv_dyn_lds(M, k);
   if (allow_dynamic_lds(reinterpret_cast<const void *>(&iq4xs_gemv_kernel<M, G, T>), lds, granted,
                         "iq4xs_gemv_kernel lds"))
     return QMV_ERR_HIP;
-  constexpr int rows = T / G;
-  return launch_kernel("iq4xs_gemv_kernel", iq4xs_gemv_kernel<M, G, T>, dim3((unsigned)((n + rows - 1) / rows)),
-                       dim3(T), lds, s, static_cast<const uint8_t *>(w), x, y, n, k);
+  return launch_kernel("iq4xs_gemv_kernel", iq4xs_gemv_kernel<M, G, T>, dim3(p.grid), dim3(T), lds, s,
+                       static_cast<const uint8_t *>(w), x, y, n, k);
 }
 
+// The plan is addr::iq4_gemv_plan: long rows take 32 lanes (more independent
+// loads per row, fewer rows per workgroup); once the staged activations leave
+// room for a single workgroup per CU, that workgroup takes 512 threads, so a
+// CU still holds 8 waves.
 template <int M>
 int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t s) {
-  // Long rows take 32 lanes (more independent loads per row, fewer rows per
-  // workgroup). Once the staged activations leave room for a single workgroup
-  // per CU, that workgroup takes 512 threads, so a CU still holds 8 waves.
-  if (k <= 8192) return launch_mgt<M, 16, 256>(w, x, y, n, k, s);
-  if (2 * layout::iq4xs_gemv_lds(M, k) > kLdsPerCu) return launch_mgt<M, 32, 512>(w, x, y, n, k, s);
-  return launch_mgt<M, 32, 256>(w, x, y, n, k, s);
+  const addr::Iq4Plan p = addr::iq4_gemv_plan(M, n, k);
+  if (p.G == 16) return launch_mgt<M, 16, 256>(p, w, x, y, n, k, s);
+  if (p.threads == 512) return launch_mgt<M, 32, 512>(p, w, x, y, n, k, s);
+  return launch_mgt<M, 32, 256>(p, w, x, y, n, k, s);
 }
 
 }  // namespace

@@ -29,6 +29,7 @@
 // (expert, token) pair does not depend on which lanes or waves run it.
 #include "iq4xs_common.h"
 #include "moe_routing.h"
+#include "qmv_addr.h"
 #include "qmv_internal.h"
 #include "../../include/qmv.h"
 
@@ -38,17 +39,18 @@ namespace {
 using namespace iq4xs;
 using namespace moe;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = addr::kIq4MoeDnWaves;
 constexpr int kThreads = 64 * kWaves;
 static_assert(kThreads == kTableEntries, "one table entry per thread");
 // gate/up: 16 lanes per W row, 4 rows per wave, 16 rows per workgroup
-constexpr int kUpLanes = 16;
-constexpr int kUpRows = kThreads / kUpLanes;
-constexpr int kUpDepth = 2;   // units (gate and up) of loads in flight per lane
+constexpr int kUpLanes = addr::kIq4MoeUpLanes;
+constexpr int kUpRows = addr::kIq4MoeUpRows;
+constexpr int kUpDepth = addr::kIq4MoeUpDepth;   // units (gate and up) of loads in flight per lane
 // down: 8 lanes per W row (one sub-block each), 8 rows per wave and workgroup
-constexpr int kDnLanes = 8;
-constexpr int kDnRows = 64 / kDnLanes;
-constexpr int kDnDepth = 4;   // (expert, super-block) units of loads in flight per lane
+constexpr int kDnLanes = addr::kIq4MoeDnLanes;
+constexpr int kDnRows = addr::kIq4MoeDnRows;
+constexpr int kDnDepth = addr::kIq4MoeDnDepth;   // (expert, super-block) units of loads in flight per lane
+static_assert(kUpRows == kThreads / kUpLanes && kDnRows == 64 / kDnLanes, "the shapes the addressing assumes");
 constexpr int kTableWords = (int)(sizeof(Table) / 4);
 static_assert(kTableWords <= kThreads, "one table word per thread");
 
@@ -111,26 +113,21 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_gate_up_kernel(
 
   const int l = tid % kUpLanes;
   const int f = blockIdx.x * kUpRows + tid / kUpLanes;
-  const size_t row_bytes = (size_t)nblk * kIQ4XSBlockBytes;
-  const size_t off = ((size_t)sl.e * (size_t)ffn + (size_t)(f < ffn ? f : 0)) * row_bytes;
-  const uint8_t *grow = w_gate + off, *urow = w_up + off;
   // lane l: sub-blocks u = l + 16 t -> super-block (l >> 3) + 2 t, sub-block j = l & 7
-  const int j = l & 7, qoff = 8 + 16 * j;
-  constexpr int kUnitBytes = (kUpLanes / 8) * kIQ4XSBlockBytes;
-  const uint8_t *gl = grow + (size_t)(l >> 3) * kIQ4XSBlockBytes;
-  const uint8_t *ul = urow + (size_t)(l >> 3) * kIQ4XSBlockBytes;
-  const int nlive = l < nsub ? (nsub - l + kUpLanes - 1) / kUpLanes : 0;
-  const int nmax = (nsub + kUpLanes - 1) / kUpLanes;
-  const int nslots = (nmax + kUpDepth - 1) / kUpDepth * kUpDepth;
+  const addr::Iq4Lane ln = addr::iq4_moe_up_lane(sl.e, ffn, hidden, blockIdx.x, tid);
+  const uint8_t *grow = w_gate + ln.row_base, *urow = w_up + ln.row_base;
+  const uint8_t *gl = w_gate + ln.lane_base, *ul = w_up + ln.lane_base;
+  const int j = l & 7, qoff = ln.qoff;
+  const int nlive = ln.nlive;
+  const int nslots = addr::iq4_slots(kUpLanes, nblk, kUpDepth);
   constexpr int kXStride = 4 * kUpLanes + kUpLanes / 4;
   const int x_l = x_slot(l < nsub ? l : 0);
 
   Unit rg_[kUpDepth], ru_[kUpDepth];
 #pragma unroll
   for (int d = 0; d < kUpDepth; ++d) {
-    const size_t o = (size_t)d * kUnitBytes;
-    load_unit(d < nlive ? gl + o : grow, qoff, rg_[d]);
-    load_unit(d < nlive ? ul + o : urow, qoff, ru_[d]);
+    load_unit((d < nlive ? gl + addr::iq4_unit_offset(d, ln.unit_bytes) : grow), qoff, rg_[d]);
+    load_unit((d < nlive ? ul + addr::iq4_unit_offset(d, ln.unit_bytes) : urow), qoff, ru_[d]);
   }
 
   int xoff[T];
@@ -155,9 +152,8 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_gate_up_kernel(
       const Pairs u2 = word_pairs(tbl_bytes, ru_[d].q1.x), u3 = word_pairs(tbl_bytes, ru_[d].q1.y);
       {
         const int tn = t + kUpDepth;
-        const size_t o = (size_t)tn * kUnitBytes;
-        load_unit(tn < nlive ? gl + o : grow, qoff, rg_[d]);
-        load_unit(tn < nlive ? ul + o : urow, qoff, ru_[d]);
+        load_unit((tn < nlive ? gl + addr::iq4_unit_offset(tn, ln.unit_bytes) : grow), qoff, rg_[d]);
+        load_unit((tn < nlive ? ul + addr::iq4_unit_offset(tn, ln.unit_bytes) : urow), qoff, ru_[d]);
       }
 #pragma unroll
       for (int r = 0; r < T; ++r) {
@@ -277,26 +273,19 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_down_kernel(const uint8_t 
 
   // wave w takes distinct experts w, w + 4, ...; lane: row i_row, sub-block j
   const int j = lane & (kDnLanes - 1), i_row = lane / kDnLanes;
-  const int n = blockIdx.x * kDnRows + i_row;
-  const size_t row_bytes = (size_t)nblk * kIQ4XSBlockBytes;
-  const size_t expert_bytes = (size_t)hidden * row_bytes;
-  const uint8_t *wrow = w_down + (size_t)(n < hidden ? n : 0) * row_bytes;   // rows past the matrix read row 0
-  const int qoff = 8 + 16 * j;
-  const int n_slots = R.n_slots;
-  const int my_slots = n_slots > wave ? (n_slots - wave + kWaves - 1) / kWaves : 0;
-  const int U = my_slots * nblk;   // units (expert, super-block), expert-major
+  const addr::Iq4DnLane ln = addr::iq4_moe_dn_lane(hidden, ffn, R.n_slots, blockIdx.x, tid);
+  const size_t expert_bytes = (size_t)hidden * (size_t)nblk * kIQ4XSBlockBytes;
+  const uint8_t *wrow = w_down + ln.row;   // rows past the matrix read row 0
+  const int qoff = ln.qoff;
+  const int U = ln.units;   // units (expert, super-block), expert-major
 
   Unit ring[kDnDepth];
   int ls = wave, lb = 0;   // next unit to load; units past U re-read this row of the first slot's expert
 #pragma unroll
   for (int u = 0; u < kDnDepth; ++u) {
     const bool ok = u < U;
-    load_unit(wrow + (size_t)R.slot_expert[ok ? ls : 0] * expert_bytes + (size_t)(ok ? lb : 0) * kIQ4XSBlockBytes,
-              qoff, ring[u]);
-    if (ok && ++lb == nblk) {
-      lb = 0;
-      ls += kWaves;
-    }
+    load_unit(addr::iq4_moe_dn_unit_at(wrow, R.slot_expert[ok ? ls : 0], expert_bytes, ok ? lb : 0), qoff, ring[u]);
+    if (ok) addr::moe_dn_next(ls, lb, nblk, kWaves);
   }
 
   const int sh_lo = 4 * j, sh_hi = 16 + 2 * j;
@@ -314,13 +303,9 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_down_kernel(const uint8_t 
         const FPairs w2 = word_fpairs(tblf_bytes, ring[u].q1.x), w3 = word_fpairs(tblf_bytes, ring[u].q1.y);
         {
           const bool ok = u0 + u + kDnDepth < U;
-          load_unit(wrow + (size_t)R.slot_expert[ok ? ls : 0] * expert_bytes +
-                        (size_t)(ok ? lb : 0) * kIQ4XSBlockBytes,
-                    qoff, ring[u]);
-          if (ok && ++lb == nblk) {
-            lb = 0;
-            ls += kWaves;
-          }
+          load_unit(addr::iq4_moe_dn_unit_at(wrow, R.slot_expert[ok ? ls : 0], expert_bytes, ok ? lb : 0), qoff,
+                    ring[u]);
+          if (ok) addr::moe_dn_next(ls, lb, nblk, kWaves);
         }
         const int sb = 8 * cb + j;
 #pragma unroll

@@ -31,6 +31,7 @@
 // body, explicit fma/dot builtins, no reassociation), so row r is bit-identical
 // for M = 1..4.
 #include "q4k_common.h"
+#include "qmv_addr.h"
 #include "qmv_internal.h"
 #include "../../include/qmv.h"
 
@@ -38,7 +39,9 @@ namespace qmv {
 namespace {
 
 // Block formats of this kernel body.
-constexpr int kFmtQ4K = 0, kFmtQ5K = 1, kFmtQ40 = 2;
+using addr::kFmtQ4K;
+using addr::kFmtQ5K;
+using addr::kFmtQ40;
 
 
 template <int M>
@@ -266,13 +269,15 @@ __device__ __forceinline__ void dense_chunk(float (&acc)[M], const uint4 hdr, co
   }
 }
 
-// Bytes per 256-weight group: a Q4_K or Q5_K super-block, or eight Q4_0 blocks.
+// The 16-byte weight loads of one step for the lane holding chunk c of the
+// block at bp: the block header (for Q5_K with the 32 bytes of the high-bit
+// plane that every chunk's lane reads; for Q4_0 the chunk's pair of 18-byte
+// blocks, read as nine dwords) and the chunk's 32 quant bytes -- the windows
+// addr::dense_window describes (checked below). The offsets are written out
+// here: the same offsets formed through the window function cost registers.
 template <int F>
-constexpr int block_bytes() { return F == kFmtQ5K ? kQ5KBlockBytes : kQ4KBlockBytes; }
+constexpr int kQuantBase = F == kFmtQ5K ? 48 : 16;
 
-// The 16-byte weight loads of one step for the lane holding chunk c of a block
-// at bp: the block header and the chunk's 32 quant bytes, and for Q5_K the 32
-// bytes of the high-bit plane (every chunk's lane reads all of them).
 template <int F>
 __device__ __forceinline__ void load_step(const uint8_t *__restrict__ bp, const int c, uint4 &hdr, uint4 &qa,
                                           uint4 &qb, uint4 &hb0, uint4 &hb1) {
@@ -288,28 +293,33 @@ __device__ __forceinline__ void load_step(const uint8_t *__restrict__ bp, const 
   if constexpr (F == kFmtQ5K) {
     hb0 = *reinterpret_cast<const uint4 *>(bp + 16);
     hb1 = *reinterpret_cast<const uint4 *>(bp + 32);
-    qa = *reinterpret_cast<const uint4 *>(bp + 48 + 32 * c);
-    qb = *reinterpret_cast<const uint4 *>(bp + 64 + 32 * c);
-  } else {
-    qa = *reinterpret_cast<const uint4 *>(bp + 16 + 32 * c);
-    qb = *reinterpret_cast<const uint4 *>(bp + 32 + 32 * c);
   }
+  qa = *reinterpret_cast<const uint4 *>(bp + kQuantBase<F> + 32 * c);
+  qb = *reinterpret_cast<const uint4 *>(bp + kQuantBase<F> + 32 * c + 16);
 }
 
-// Block address of step t for this lane, or the fallback block wfb when the
-// step does not exist for it (see the kernel); every address loaded stays
-// inside the weights.
-// NS > 0 (unrolled, t a compile-time step): only step NS - 1 can be partial,
-// and last_ok says whether this lane's block exists there. NS == 0: FULL says
-// the row is a whole number of steps.
+constexpr bool load_step_reads_the_windows() {
+  for (int c = 0; c < 4; ++c) {
+    const addr::Window q4h = addr::dense_window(kFmtQ4K, c, 0), q4q = addr::dense_window(kFmtQ4K, c, 1);
+    const addr::Window q5h = addr::dense_window(kFmtQ5K, c, 0), q5q = addr::dense_window(kFmtQ5K, c, 1);
+    const addr::Window q0 = addr::dense_window(kFmtQ40, c, 0), q0q = addr::dense_window(kFmtQ40, c, 1);
+    if (q4h.off != 0 || q4h.len != 16 || q4q.off != kQuantBase<kFmtQ4K> + 32 * c || q4q.len != 32) return false;
+    if (q5h.off != 0 || q5h.len != 48 || q5q.off != kQuantBase<kFmtQ5K> + 32 * c || q5q.len != 32) return false;
+    if (q0.off != 36 * c || q0.len != 36 || q0q.len != 0) return false;
+  }
+  return true;
+}
+static_assert(load_step_reads_the_windows(), "load_step reads exactly the windows of addr::dense_window");
+
+// Block address of step t for this lane (addr::dense_step_ok and
+// addr::dense_step_offset), or the fallback block wfb when the step has no
+// block of its own.
 template <bool FULL, int NS, int kBlocksPerStep, int F>
 __device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *wfb, const uint8_t *wl, const bool active, const int t,
                                                    const int nsteps, const int jb, const int nblk,
                                                    const bool last_ok) {
-  bool ok;
-  if constexpr (NS > 0) ok = active && t < NS && (t < NS - 1 || last_ok);
-  else ok = active && t < nsteps && (FULL || t * kBlocksPerStep + jb < nblk);
-  return ok ? wl + (size_t)(t * kBlocksPerStep) * block_bytes<F>() : wfb;
+  const bool ok = addr::dense_step_ok(active, last_ok, nsteps, jb, NS, FULL, 4 * kBlocksPerStep, nblk, t);
+  return ok ? wl + addr::dense_step_offset(4 * kBlocksPerStep, F, t) : wfb;
 }
 
 // G lanes own one output row (G = 16 or 32): a step covers G/4 super-blocks of
@@ -334,20 +344,13 @@ __device__ __forceinline__ const uint8_t *step_ptr(const uint8_t *wfb, const uin
 // kXHead: activation granules per thread loaded ahead of the weights -- enough
 // for the rows the launcher sends to each G (K <= 8192 with G = 16, K <= 18432
 // otherwise) at M = 1, capped at 9 so the head never sets the register peak.
-// Workgroups have kMinThreads..kMaxThreads threads (see pick_rows).
-constexpr int kMinThreads = 256;
-constexpr int kMaxThreads = 512;       // M = 1
-constexpr int kMaxThreadsRows = 768;   // M = 2..4: register use allows 3 waves per SIMD
-// Q5_K ring depths (steps), 16 and 32 lanes per row: at M = 1 as for Q4_K; at
-// M = 2..4 (more registers per step) 4 for both.
-template <int M>
-constexpr int q5_depth16() { return M == 1 ? 5 : 4; }
-template <int M>
-constexpr int q5_depth32() { return M == 1 ? 2 : 4; }
-// Q4_K ring depths (steps): a 5-step row (K = 5120, 16 lanes) keeps every load in
-// flight from the start; the 9-step rows of 32 lanes are fastest with 2.
-constexpr int kQ4Depth16 = 5;
-constexpr int kQ4Depth32 = 2;
+// Workgroups have kMinThreads..kMaxThreads threads (addr::balanced_rows).
+// Ring depths (addr::dense_depth): at M = 1 a 5-step row of 16 lanes (K = 5120)
+// keeps every load in flight from the start and the 9-step rows of 32 lanes are
+// fastest with 2; Q5_K at M = 2..4 (more registers per step) takes 4 for both.
+constexpr int kMinThreads = addr::kDenseMinThreads;
+constexpr int kMaxThreads = addr::dense_max_threads(1);       // M = 1
+constexpr int kMaxThreadsRows = addr::dense_max_threads(2);   // M = 2..4: register use allows 3 waves per SIMD
 
 template <int M, int G>
 constexpr int x_head() { return (G == 16 ? 4 * M : 9 * M) < 9 ? (G == 16 ? 4 * M : 9 * M) : 9; }
@@ -367,21 +370,17 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
 
   const int lane = threadIdx.x & 63;
   const int j = lane & (G - 1);
-  const int c = j & 3;
-  const int jb = j >> 2;
   // blockDim.x = (rows per workgroup) * G; the last wave may be partial
   const int nthreads = (int)blockDim.x;
-  const int row = blockIdx.x * (nthreads / G) + (int)threadIdx.x / G;
-  const bool active = row < n;
-  const int nsteps = NS > 0 ? NS : (nblk + kBlocksPerStep - 1) / kBlocksPerStep;
-  // with NS > 0 only the last step can be partial: lanes past its blocks skip it
-  const bool last_ok = jb < nblk - (nsteps - 1) * kBlocksPerStep;
+  const int row = addr::lane_row(blockIdx.x, threadIdx.x, nthreads, G);
   // loads with no block of their own (past the row, past the matrix, past a
   // partial last step) read the last block of the lane's row (of the last row
   // when the row is past the matrix), which the same or a recent load also reads
-  const uint8_t *wfb = w + ((size_t)(active ? row : n - 1) * (size_t)nblk + (size_t)(nblk - 1)) * block_bytes<F>();
-  const uint8_t *wl = w + (size_t)(active ? row : 0) * (size_t)nblk * block_bytes<F>() +
-                      (size_t)jb * block_bytes<F>();
+  const addr::DenseLane ln = addr::dense_lane(G, NS, F, n, nblk, row, j);
+  const int c = ln.c, jb = ln.jb;
+  const bool active = ln.active, last_ok = ln.last_ok;
+  const int nsteps = ln.nsteps;
+  const uint8_t *wl = w + ln.row_base + ln.blk_off, *wfb = w + ln.fb;
 
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
   constexpr int kXHead = x_head<M, G>();
@@ -478,29 +477,14 @@ __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q5k_ge
   gemv_body<M, G, D, FULL, NS, kFmtQ5K>(w, x, y, n, k);
 }
 
-// Rows per workgroup. A launch is balanced when every CU gets the same number
-// of rows: with N rows over 256 CUs, q workgroups of N / (256 q) rows each
+// The plan (lanes per row, steps, ring depth, rows per workgroup, grid) is
+// addr::dense_gemv_plan; rows per workgroup balance the rows over the 256 CUs
 // (10 rows of 32 lanes for N = 5120 at M = 1, 20 rows at M = 2..4 where the
-// activations fill the LDS). The workgroup must be whole waves with 256..512
-// threads (768 for M > 1; a partial wave costs a full wave's issue slots), and
-// q of them must fit in LDS; otherwise 256 threads.
-inline int pick_rows(const int m, const int n, const int G, const size_t lds) {
-  const int dflt = kMinThreads / G;
-  if (n % 256 != 0) return dflt;
-  const int max_threads = m == 1 ? kMaxThreads : kMaxThreadsRows;
-  const int per_cu = n / 256;
-  for (int q = 1; q <= 8; ++q) {
-    if (per_cu % q != 0) continue;
-    const int threads = (per_cu / q) * G;
-    if (threads > max_threads || threads % 64 != 0) continue;   // whole waves only
-    if (threads < kMinThreads || (size_t)q * lds > (size_t)QMV_LDS_X_BYTES) break;
-    return per_cu / q;
-  }
-  return dflt;
-}
-
-template <int M, int G, int D, bool FULL, int NS, int F>
-int launch_cfg(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
+// activations fill the LDS). Each instantiation below is the one the plan
+// names: G and NS by the switch, D = addr::dense_depth(F, M, G).
+template <int M, int G, bool FULL, int NS, int F>
+int launch_cfg(const addr::GemvPlan &p, const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
+  constexpr int D = addr::dense_depth(F, M, G);
   const size_t lds = dense_lds_bytes<M>(k);
   // only the launched format's kernel is instantiated
   void (*fn)(const uint8_t *, const uint16_t *, float *, int, int);
@@ -510,46 +494,33 @@ int launch_cfg(const void *w, const uint16_t *x, float *y, int n, int k, hipStre
   else fn = q4k_gemv_kernel<M, G, D, FULL, NS>, name = "q4k_gemv_kernel";
   static LdsGrant granted;
   if (allow_dynamic_lds(reinterpret_cast<const void *>(fn), lds, granted, name)) return QMV_ERR_HIP;
-  const int rows = pick_rows(M, n, G, lds);
-  const unsigned grid = (unsigned)((n + rows - 1) / rows);
-  return launch_kernel(name, fn, dim3(grid), dim3(rows * G), lds, stream, w, x, y, n, k);
+  return launch_kernel(name, fn, dim3(p.grid), dim3(p.rows * G), lds, stream, w, x, y, n, k);
 }
 
-// Runtime-length rows (any K).
-template <int M, int G, int D, int F>
-int launch_any(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
-  if (((k >> 8) % (G / 4)) == 0) return launch_cfg<M, G, D, true, 0, F>(w, x, y, n, k, stream);
-  return launch_cfg<M, G, D, false, 0, F>(w, x, y, n, k, stream);
-}
-
-// Lanes per row by row length: 16 up to K = 8192 (1..8 steps of 4 blocks), 32
-// beyond (steps of 8 blocks; 5..9 steps up to K = 18432, runtime loop after).
-// (FULL matters only to the runtime loop; the unrolled kernels test their
-// possibly partial last step themselves.)
 template <int M, int F>
 int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
-  constexpr int D = F == kFmtQ5K ? q5_depth16<M>() : kQ4Depth16;
-  constexpr int D32 = F == kFmtQ5K ? q5_depth32<M>() : kQ4Depth32;
-  const int nblk = k >> 8;
-  if (k <= 8192) {
-    switch ((nblk + 3) / 4) {
-      case 1: return launch_cfg<M, 16, D, false, 1, F>(w, x, y, n, k, stream);
-      case 2: return launch_cfg<M, 16, D, false, 2, F>(w, x, y, n, k, stream);
-      case 3: return launch_cfg<M, 16, D, false, 3, F>(w, x, y, n, k, stream);
-      case 4: return launch_cfg<M, 16, D, false, 4, F>(w, x, y, n, k, stream);
-      case 5: return launch_cfg<M, 16, D, false, 5, F>(w, x, y, n, k, stream);
-      case 6: return launch_cfg<M, 16, D, false, 6, F>(w, x, y, n, k, stream);
-      case 7: return launch_cfg<M, 16, D, false, 7, F>(w, x, y, n, k, stream);
-      default: return launch_cfg<M, 16, D, false, 8, F>(w, x, y, n, k, stream);
+  const addr::GemvPlan p = addr::dense_gemv_plan(F, M, n, k);
+  if (p.G == 16) {
+    switch (p.ns) {
+      case 1: return launch_cfg<M, 16, false, 1, F>(p, w, x, y, n, k, stream);
+      case 2: return launch_cfg<M, 16, false, 2, F>(p, w, x, y, n, k, stream);
+      case 3: return launch_cfg<M, 16, false, 3, F>(p, w, x, y, n, k, stream);
+      case 4: return launch_cfg<M, 16, false, 4, F>(p, w, x, y, n, k, stream);
+      case 5: return launch_cfg<M, 16, false, 5, F>(p, w, x, y, n, k, stream);
+      case 6: return launch_cfg<M, 16, false, 6, F>(p, w, x, y, n, k, stream);
+      case 7: return launch_cfg<M, 16, false, 7, F>(p, w, x, y, n, k, stream);
+      default: return launch_cfg<M, 16, false, 8, F>(p, w, x, y, n, k, stream);
     }
   }
-  switch ((nblk + 7) / 8) {
-    case 5: return launch_cfg<M, 32, D32, false, 5, F>(w, x, y, n, k, stream);
-    case 6: return launch_cfg<M, 32, D32, false, 6, F>(w, x, y, n, k, stream);
-    case 7: return launch_cfg<M, 32, D32, false, 7, F>(w, x, y, n, k, stream);
-    case 8: return launch_cfg<M, 32, D32, false, 8, F>(w, x, y, n, k, stream);
-    case 9: return launch_cfg<M, 32, D32, false, 9, F>(w, x, y, n, k, stream);
-    default: return launch_any<M, 32, D32, F>(w, x, y, n, k, stream);
+  switch (p.ns) {
+    case 5: return launch_cfg<M, 32, false, 5, F>(p, w, x, y, n, k, stream);
+    case 6: return launch_cfg<M, 32, false, 6, F>(p, w, x, y, n, k, stream);
+    case 7: return launch_cfg<M, 32, false, 7, F>(p, w, x, y, n, k, stream);
+    case 8: return launch_cfg<M, 32, false, 8, F>(p, w, x, y, n, k, stream);
+    case 9: return launch_cfg<M, 32, false, 9, F>(p, w, x, y, n, k, stream);
+    default:
+      return p.full ? launch_cfg<M, 32, true, 0, F>(p, w, x, y, n, k, stream)
+                    : launch_cfg<M, 32, false, 0, F>(p, w, x, y, n, k, stream);
   }
 }
 

@@ -36,6 +36,7 @@
 
 #include "moe_routing.h"
 #include "q4k_common.h"
+#include "qmv_addr.h"
 #include "qmv_internal.h"
 #include "../../include/qmv.h"
 
@@ -45,16 +46,38 @@ namespace {
 using namespace moe;
 
 constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kThreads = addr::kMoeThreads;
 // gate/up: 16 lanes per W row, 4 rows per wave, 16 rows per workgroup
-constexpr int kUpLanes = 16;
-constexpr int kUpRows = kWaves * (64 / kUpLanes);
-constexpr int kUpDepth = 2;  // steps of gate + up loads in flight
+constexpr int kUpLanes = addr::kMoeUpLanes;
+constexpr int kUpRows = addr::kMoeUpRows;
+constexpr int kUpDepth = addr::kMoeUpDepth;  // steps of gate + up loads in flight
 // down: 4 lanes per W row; a workgroup owns 8 rows, and its 8 lane groups of
 // 32 lanes (8 rows x 4 chunks) split the distinct experts
-constexpr int kDnRows = 8;
-constexpr int kDnGroups = kThreads / (4 * kDnRows);
-constexpr int kDnDepth = 6;  // (expert, block) units of loads in flight per lane
+constexpr int kDnRows = addr::kMoeDnRows;
+constexpr int kDnGroups = addr::kMoeDnGroups;
+constexpr int kDnDepth = addr::kMoeDnDepth;  // (expert, block) units of loads in flight per lane
+static_assert(kThreads == 64 * kWaves && kUpRows == kWaves * (64 / kUpLanes) && kDnGroups == kThreads / (4 * kDnRows),
+              "the shapes the addressing assumes");
+
+// The gate (or up) loads of one step at bp: the block header and chunk c's 32
+// quant bytes (the Q4_K windows of addr::dense_window).
+__device__ __forceinline__ void load_up_step(const uint8_t *__restrict__ bp, const int c, uint4 &h, uint4 &a,
+                                             uint4 &b) {
+  const addr::Window wh = addr::dense_window(addr::kFmtQ4K, c, 0), wq = addr::dense_window(addr::kFmtQ4K, c, 1);
+  h = *reinterpret_cast<const uint4 *>(bp + wh.off);
+  a = *reinterpret_cast<const uint4 *>(bp + wq.off);
+  b = *reinterpret_cast<const uint4 *>(bp + wq.off + 16);
+}
+
+// The W_down loads of one unit at bp (the block's first byte plus 32 c): the
+// header and chunk c's 32 quant bytes (addr::moe_dn_window).
+__device__ __forceinline__ void load_dn_unit(const uint8_t *__restrict__ bp, const int c, uint4 &h, uint4 &a,
+                                             uint4 &b) {
+  const addr::Window wh = addr::moe_dn_window(c, 0), wq = addr::moe_dn_window(c, 1);
+  h = *reinterpret_cast<const uint4 *>(bp + wh.off);
+  a = *reinterpret_cast<const uint4 *>(bp + wq.off);
+  b = *reinterpret_cast<const uint4 *>(bp + wq.off + 16);
+}
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
@@ -175,28 +198,20 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(
   if (sl.p0 < 0) return;  // fewer distinct experts than the grid allows for (uniform over the workgroup)
 
   const int j = lane & (kUpLanes - 1);
-  const int c = j & 3, jb = j >> 2;
-  const int f = blockIdx.x * kUpRows + wave * (64 / kUpLanes) + lane / kUpLanes;
-  const bool active = f < ffn;
+  const addr::MoeUpLane ln = addr::moe_up_lane(sl.e, ffn, hidden, blockIdx.x, threadIdx.x);
+  const int c = ln.c, jb = ln.jb, f = ln.f;
+  const bool active = ln.active;
   const int nblk = hidden >> 8;
-  const size_t row_bytes = (size_t)nblk * kQ4KBlockBytes;
-  const size_t off = (size_t)sl.e * (size_t)ffn * row_bytes + (size_t)(active ? f : 0) * row_bytes +
-                     (size_t)jb * kQ4KBlockBytes;
-  const uint8_t *gl = w_gate + off;
-  const uint8_t *ul = w_up + off;
-  const int nsteps = (nblk + 3) >> 2;
+  const uint8_t *gl = w_gate + ln.base;
+  const uint8_t *ul = w_up + ln.base;
+  const int nsteps = ln.nsteps;
 
   uint4 gh[kUpDepth], ga[kUpDepth], gb[kUpDepth], uh[kUpDepth], ua[kUpDepth], ub[kUpDepth];
 #pragma unroll
   for (int u = 0; u < kUpDepth; ++u) {
-    if (active && u < nsteps && 4 * u + jb < nblk) {
-      const size_t o = (size_t)(4 * u) * kQ4KBlockBytes;
-      gh[u] = *reinterpret_cast<const uint4 *>(gl + o);
-      ga[u] = *reinterpret_cast<const uint4 *>(gl + o + 16 + 32 * c);
-      gb[u] = *reinterpret_cast<const uint4 *>(gl + o + 32 + 32 * c);
-      uh[u] = *reinterpret_cast<const uint4 *>(ul + o);
-      ua[u] = *reinterpret_cast<const uint4 *>(ul + o + 16 + 32 * c);
-      ub[u] = *reinterpret_cast<const uint4 *>(ul + o + 32 + 32 * c);
+    if (addr::moe_up_step_ok(ln, nblk, u)) {
+      load_up_step(addr::moe_up_step_at(gl, u), c, gh[u], ga[u], gb[u]);
+      load_up_step(addr::moe_up_step_at(ul, u), c, uh[u], ua[u], ub[u]);
     }
   }
 
@@ -245,14 +260,9 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(
         chunk_bf16<T>(acc_u, sl.ntok, uh[u], ua[u], ub[u], sel, xb + s * 136, xoff, sb + 32 * s, soff);
       }
       const int sn = s + kUpDepth;
-      if (sn < nsteps && 4 * sn + jb < nblk) {
-        const size_t o = (size_t)(4 * sn) * kQ4KBlockBytes;
-        gh[u] = *reinterpret_cast<const uint4 *>(gl + o);
-        ga[u] = *reinterpret_cast<const uint4 *>(gl + o + 16 + 32 * c);
-        gb[u] = *reinterpret_cast<const uint4 *>(gl + o + 32 + 32 * c);
-        uh[u] = *reinterpret_cast<const uint4 *>(ul + o);
-        ua[u] = *reinterpret_cast<const uint4 *>(ul + o + 16 + 32 * c);
-        ub[u] = *reinterpret_cast<const uint4 *>(ul + o + 32 + 32 * c);
+      if (addr::moe_up_step_ok(ln, nblk, sn)) {   // active holds for every lane that gets here
+        load_up_step(addr::moe_up_step_at(gl, sn), c, gh[u], ga[u], gb[u]);
+        load_up_step(addr::moe_up_step_at(ul, sn), c, uh[u], ua[u], ub[u]);
       }
     }
   }
@@ -382,31 +392,22 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__res
   __syncthreads();
 
   // lane group grp (32 lanes: 8 rows x 4 chunks) takes distinct experts grp, grp + 8, ...
-  const int grp = tid >> 5;
-  const int c = tid & 3;
+  const addr::MoeDnLane ln = addr::moe_dn_lane(hidden, ffn, R.n_slots, blockIdx.x, tid);
+  const int grp = ln.grp;
+  const int c = ln.c;
   const int i_row = (tid & 31) >> 2;
-  const int n = blockIdx.x * kDnRows + i_row;
-  const size_t row_bytes = (size_t)nblk * kQ4KBlockBytes;
-  const size_t expert_bytes = (size_t)hidden * row_bytes;
+  const size_t expert_bytes = (size_t)hidden * (size_t)nblk * kQ4KBlockBytes;
   // rows past the matrix read row 0 (their results are never stored)
-  const uint8_t *wrow = w_down + (size_t)(n < hidden ? n : 0) * row_bytes + 32 * c;
-  const int n_slots = R.n_slots;
-  const int my_slots = n_slots > grp ? (n_slots - grp + kDnGroups - 1) / kDnGroups : 0;
-  const int U = my_slots * nblk;  // units (expert, block), expert-major
+  const uint8_t *wrow = w_down + ln.row;
+  const int U = ln.units;  // units (expert, block), expert-major
 
   uint4 wh[kDnDepth], wa[kDnDepth], wb[kDnDepth];
   int ls = grp, lb = 0;  // next unit to load
 #pragma unroll
   for (int u = 0; u < kDnDepth; ++u) {
     if (u < U) {
-      const uint8_t *bp = wrow + (size_t)R.slot_expert[ls] * expert_bytes + (size_t)lb * kQ4KBlockBytes;
-      wh[u] = *reinterpret_cast<const uint4 *>(bp - 32 * c);
-      wa[u] = *reinterpret_cast<const uint4 *>(bp + 16);
-      wb[u] = *reinterpret_cast<const uint4 *>(bp + 32);
-      if (++lb == nblk) {
-        lb = 0;
-        ls += kDnGroups;
-      }
+      load_dn_unit(addr::moe_dn_unit_at(wrow, R.slot_expert[ls], expert_bytes, lb), c, wh[u], wa[u], wb[u]);
+      addr::moe_dn_next(ls, lb, nblk, kDnGroups);
     }
   }
 
@@ -441,14 +442,8 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__res
         chunk_f32<T>(acc, ntok, wh[u], wa[u], wb[u], sel, hs + (p0 * cpr + ci) * 17, stride,
                      hsum + p0 * nsub + 2 * ci, nsub);
         if (u0 + u + kDnDepth < U) {
-          const uint8_t *bp = wrow + (size_t)R.slot_expert[ls] * expert_bytes + (size_t)lb * kQ4KBlockBytes;
-          wh[u] = *reinterpret_cast<const uint4 *>(bp - 32 * c);
-          wa[u] = *reinterpret_cast<const uint4 *>(bp + 16);
-          wb[u] = *reinterpret_cast<const uint4 *>(bp + 32);
-          if (++lb == nblk) {
-            lb = 0;
-            ls += kDnGroups;
-          }
+          load_dn_unit(addr::moe_dn_unit_at(wrow, R.slot_expert[ls], expert_bytes, lb), c, wh[u], wa[u], wb[u]);
+          addr::moe_dn_next(ls, lb, nblk, kDnGroups);
         }
         if (++cb == nblk) {
           // the expert's row is complete: one z per token, reduced over the row's four lanes (one quad)

@@ -32,6 +32,7 @@
 // sub-block: the low and high nibbles of quant bytes 32c + 8g .. + 7 of chunk c.
 #include "moe_routing.h"
 #include "q4k_common.h"
+#include "qmv_addr.h"
 #include "qmv_internal.h"
 #include "../../include/qmv.h"
 
@@ -47,7 +48,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = layout::kGroupChunk;   // pairs per chunk (the MFMA's M)
-constexpr int kTile = 16;    // weight rows per tile (the MFMA's N)
+constexpr int kTile = addr::kGroupTile;    // weight rows per tile (the MFMA's N)
 constexpr int kWv = 4;       // waves per workgroup; they split the super-blocks
 constexpr int kThr = 64 * kWv;
 
@@ -160,11 +161,12 @@ struct SbLoad {
   uint4 hdr;
   uint2 q[4];
 };
+// (The windows of addr::group_window.)
 __device__ __forceinline__ SbLoad load_sb(const uint8_t *__restrict__ bp, const int kg) {
   SbLoad r;
-  r.hdr = *reinterpret_cast<const uint4 *>(bp);
+  r.hdr = *reinterpret_cast<const uint4 *>(bp + addr::group_window(kg, 0).off);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const uint2 *>(bp + 16 + 32 * c + 8 * kg);
+  for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const uint2 *>(bp + addr::group_window(kg, 1 + c).off);
   return r;
 }
 
@@ -239,8 +241,8 @@ __global__ __launch_bounds__(kThr) void g_gate_up_kernel(const uint8_t *__restri
   const uint8_t *gr[TPW], *ur[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    gr[tt] = w_gate + ((size_t)ci.e * ffn + rb + kTile * tt + nl) * row_bytes;
-    ur[tt] = w_up + ((size_t)ci.e * ffn + rb + kTile * tt + nl) * row_bytes;
+    gr[tt] = w_gate + addr::group_row(ci.e, ffn, blockIdx.x, kWv, wv, TPW, tt, l) * row_bytes;
+    ur[tt] = w_up + addr::group_row(ci.e, ffn, blockIdx.x, kWv, wv, TPW, tt, l) * row_bytes;
   }
   float ag[TPW][4], au[TPW][4];
   SbLoad lg[TPW], lu[TPW];
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kThr) void g_gate_up_kernel(const uint8_t *__restri
   }
   const uint4 *xa = xs + nl * rs + kg;
   for (int b = 0; b < nblk; ++b) {
-    const size_t nb = (size_t)(b + 1 < nblk ? b + 1 : b) * kQ4KBlockBytes;   // last block re-read at the end
+    const size_t nb = addr::group_block(b + 1, nblk);   // last block re-read at the end
     SbLoad ng[TPW], nu[TPW];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
@@ -365,8 +367,8 @@ __global__ __launch_bounds__(kThr32) void g_gate_up32_kernel(const uint8_t *__re
   const uint8_t *gr[TPW], *ur[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    gr[tt] = w_gate + ((size_t)ci.e * ffn + rb + kTile * tt + nl) * row_bytes;
-    ur[tt] = w_up + ((size_t)ci.e * ffn + rb + kTile * tt + nl) * row_bytes;
+    gr[tt] = w_gate + addr::group_row(ci.e, ffn, blockIdx.x, kWv32, wv, TPW, tt, l) * row_bytes;
+    ur[tt] = w_up + addr::group_row(ci.e, ffn, blockIdx.x, kWv32, wv, TPW, tt, l) * row_bytes;
   }
   float ag[TPW][2][4], au[TPW][2][4];
   SbLoad lg[TPW], lu[TPW];
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(kThr32) void g_gate_up32_kernel(const uint8_t *__re
   }
   const uint4 *xa0 = xs + nl * rs + kg, *xa1 = xs + (kTile + nl) * rs + kg;
   for (int b = 0; b < nblk; ++b) {
-    const size_t nb = (size_t)(b + 1 < nblk ? b + 1 : b) * kQ4KBlockBytes;   // last block re-read at the end
+    const size_t nb = addr::group_block(b + 1, nblk);   // last block re-read at the end
     SbLoad ng[TPW], nu[TPW];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
@@ -525,14 +527,14 @@ __global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict_
   SbLoad ld[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    dr[tt] = w_down + ((size_t)ci.e * hidden + rb + kTile * tt + nl) * row_bytes;
+    dr[tt] = w_down + addr::group_row(ci.e, hidden, blockIdx.x, kWv, wv, TPW, tt, l) * row_bytes;
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[tt][r] = 0.0f;
     ld[tt] = load_sb(dr[tt], kg);
   }
   const uint4 *ha = hs_hi + nl * rs + kg, *ma = hs_mi + nl * rs + kg, *la = hs_lo + nl * rs + kg;
   for (int b = 0; b < nblk; ++b) {
-    const size_t nb = (size_t)(b + 1 < nblk ? b + 1 : b) * kQ4KBlockBytes;
+    const size_t nb = addr::group_block(b + 1, nblk);
     SbLoad nx[TPW];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) nx[tt] = load_sb(dr[tt] + nb, kg);
@@ -599,10 +601,7 @@ namespace {
 // Tiles per wave from the number of pairs P. Measured on the 35B-A3B layer
 // (hidden 2048, ffn 768, 128 experts, top-8): four tiles per wave is fastest
 // from 512 tokens (P = 4096) up, two at 64 tokens (P = 512).
-int tiles_per_wave(int P) {
-  if (P >= 2048) return 4;
-  return P >= 256 ? 2 : 1;
-}
+int tiles_per_wave(int P) { return addr::group_tiles_per_wave(P); }
 
 template <int TPW>
 int launch_gate_up(const uint8_t *w_gate, const uint8_t *w_up, const uint16_t *x, const int *cnt, const int *off,

@@ -26,6 +26,7 @@
 // is fma(d*sc, q, -(dmin*m)) (one rounding of the exact value to fp32), then
 // rounded to nearest-even bf16 by v_cvt_pk_bf16_f32.
 #include "q4k_common.h"
+#include "qmv_addr.h"
 #include "qmv_internal.h"
 #include "../../include/qmv.h"
 
@@ -37,8 +38,8 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
-constexpr int BK = 64;
-constexpr int kThreads = 256;
+constexpr int BK = addr::kPrefillBK;
+constexpr int kThreads = addr::kPrefillHalf;
 
 // Tile shape: BM rows of X x BN rows of W per workgroup, four consumer waves of
 // (BM / WM_WAVES) x (BN / WN_WAVES), DEPTH steps of global loads in flight;
@@ -95,16 +96,12 @@ template <class C>
 __device__ __forceinline__ void load_step(const int pt, const uint4 *__restrict__ xg, const int m0, const int M,
                                           const int gpr, const uint8_t *__restrict__ w_rowp, const int nsteps, int s,
                                           StepRegs<C> &r) {
-  s = s < nsteps ? s : nsteps - 1;
+  s = addr::prefill_clamp(s, nsteps);
 #pragma unroll
-  for (int i = 0; i < C::kXPerThread; ++i) {
-    const int g = pt + kThreads * i;
-    const int row = m0 + (g >> 3);
-    r.x[i] = xg[(uint32_t)(row < M ? row : 0) * (uint32_t)gpr + (uint32_t)(s * 8 + (g & 7))];
-  }
-  const uint8_t *bp = w_rowp + (size_t)(s >> 2) * kQ4KBlockBytes;
-  r.hdr = *reinterpret_cast<const uint4 *>(bp);
-  const uint8_t *qp = bp + 16 + 32 * (s & 3) + C::kQBytes * (pt % C::kWThreadsPerRow);
+  for (int i = 0; i < C::kXPerThread; ++i) r.x[i] = xg[addr::prefill_x_granule(pt, i, m0, M, gpr, s)];
+  const uint8_t *bp = w_rowp + addr::prefill_w_step(s);
+  r.hdr = *reinterpret_cast<const uint4 *>(bp + addr::prefill_w_window(s, pt, C::kWThreadsPerRow, 0).off);
+  const uint8_t *qp = bp + addr::prefill_w_window(s, pt, C::kWThreadsPerRow, 1).off;   // C::kQBytes long
   if constexpr (C::kQBytes == 16) {
     const uint4 v = *reinterpret_cast<const uint4 *>(qp);
     r.q[0] = v.x; r.q[1] = v.y; r.q[2] = v.z; r.q[3] = v.w;
@@ -169,20 +166,7 @@ __device__ __forceinline__ void read_frags(const uint4 *__restrict__ xt, const u
   for (int j = 0; j < 2; ++j) fb[j] = __builtin_bit_cast(bf16x8, wt[tslot(wn + 32 * j + frow, 2 * kk + fg)]);
 }
 
-// Tile t as (mt, nt): when the M tiles divide 8, tile t goes where block t of
-// a one-tile-per-block launch runs -- workgroups are dealt to the 8 XCDs round
-// robin by launch order -- and XCD x works only on M tile x % m_tiles, so the
-// X rows of a tile stay in that XCD's L2 for all its N tiles.
-__device__ __forceinline__ void tile_of(const int t, const int m_tiles, const int n_tiles, int &mt, int &nt) {
-  if (8 % m_tiles == 0 && n_tiles % (8 / m_tiles) == 0) {
-    const int xcd = t & 7, per = 8 / m_tiles;
-    mt = xcd % m_tiles;
-    nt = (xcd / m_tiles) + per * (t >> 3);
-  } else {
-    nt = t % n_tiles;
-    mt = t / n_tiles;
-  }
-}
+// Tile t as (mt, nt): addr::tile_of.
 
 // Wave-specialised form: eight waves per workgroup. Waves 4..7 produce -- they
 // load X and the Q4_K blocks kDepth steps ahead, dequantize W and write the
@@ -198,13 +182,11 @@ __device__ __forceinline__ void tile_of(const int t, const int m_tiles, const in
 // r_tiles + r computes part s of tile t_main + r -- a run of whole 256-value
 // K blocks -- and stores its 128 x 128 sums to that part's slot of `part`;
 // q4k_prefill_reduce_kernel adds the parts in order afterwards.
+// Two workgroups (four waves per SIMD) per CU: at most 128 VGPRs per lane.
 template <class C>
-__global__ __launch_bounds__(2 * kThreads) void q4k_prefill_ws_kernel(const uint8_t *__restrict__ w,
-                                                                      const uint16_t *__restrict__ x,
-                                                                      float *__restrict__ y, float *__restrict__ part,
-                                                                      const int M, const int N, const int K,
-                                                                      const int t_main, const int r_tiles,
-                                                                      const int splits) {
+__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(4))) void q4k_prefill_ws_kernel(
+    const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, float *__restrict__ part,
+    const int M, const int N, const int K, const int t_main, const int r_tiles, const int splits) {
   constexpr int BM = C::BM, BN = C::BN, kDepth = C::kDepth;
   extern __shared__ uint4 lds[];
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -212,24 +194,16 @@ __global__ __launch_bounds__(2 * kThreads) void q4k_prefill_ws_kernel(const uint
   const int blk = (int)blockIdx.x;
   // this block's tile and its K steps [s_begin, s_begin + nsteps), both
   // multiples of 4 (whole K blocks), so of kDepth in {2, 4}
-  int tile = blk, s_begin = 0, nsteps = K / BK, slot = -1;
-  if (blk >= t_main) {
-    const int rb = blk - t_main, r = rb % r_tiles, sp = rb / r_tiles, nkb = K >> 8;
-    tile = t_main + r;
-    s_begin = 4 * (sp * nkb / splits);
-    nsteps = 4 * ((sp + 1) * nkb / splits) - s_begin;
-    slot = sp * r_tiles + r;
-  }
+  const addr::PrefillWork wk = addr::prefill_work(blk, K, t_main, r_tiles, splits);
+  const int tile = wk.tile, s_begin = wk.s_begin, nsteps = wk.nsteps, slot = wk.slot;
   int mt, nt;
-  tile_of(tile, m_tiles, n_tiles, mt, nt);
+  addr::tile_of(tile, m_tiles, n_tiles, mt, nt);
   const int n0 = nt * BN, m0 = mt * BM;
 
   if (wave >= 4) {
     const int pt = tid - kThreads;
     const int nblk = K >> 8;
-    const int w_row = pt / C::kWThreadsPerRow;
-    const uint8_t *w_rowp = w + (size_t)(n0 + w_row < N ? n0 + w_row : 0) * (size_t)nblk * kQ4KBlockBytes +
-                            (size_t)(s_begin >> 2) * kQ4KBlockBytes;
+    const uint8_t *w_rowp = w + addr::prefill_w_row(n0, N, K, s_begin, pt, C::kWThreadsPerRow);
     const uint4 *xg = reinterpret_cast<const uint4 *>(x) + s_begin * 8;   // step s_begin of row 0
     const int gpr = K >> 3;
     StepRegs<C> ring[kDepth];
@@ -328,7 +302,7 @@ __global__ __launch_bounds__(256) void q4k_prefill_reduce_kernel(const float *__
   if (r >= r_tiles) return;
   const int row = within / (BN / 4), c4 = within % (BN / 4);
   int mt, nt;
-  tile_of(t_main + r, (M + BM - 1) / BM, (N + BN - 1) / BN, mt, nt);
+  addr::tile_of(t_main + r, (M + BM - 1) / BM, (N + BN - 1) / BN, mt, nt);
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int sp = 0; sp < splits; ++sp) {
     const float4 v = reinterpret_cast<const float4 *>(part + (size_t)(sp * r_tiles + r) * BM * BN)[within];

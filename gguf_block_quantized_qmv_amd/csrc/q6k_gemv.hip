@@ -39,6 +39,7 @@
 // Batch invariance: row r of the output runs the same instruction sequence for
 // every M and workgroup shape, so an M = 2..4 call is bit-identical per row to
 // M = 1.
+#include "qmv_addr.h"
 #include "qmv_device.h"
 #include "qmv_internal.h"
 #include "../../include/qmv.h"
@@ -46,10 +47,9 @@
 namespace qmv {
 namespace {
 
-constexpr int kQ6KBlockBytes = 210;
-constexpr int kMinThreads = 256;
-constexpr int kMaxThreads = 512;      // M = 1
-constexpr int kMaxThreadsRows = 640;  // M = 2..4: 20 rows of 32 lanes, one workgroup per CU at K = 17408
+constexpr int kQ6KBlockBytes = addr::kQ6KBytes;
+constexpr int kMaxThreads = addr::q6_max_threads(1);      // M = 1
+constexpr int kMaxThreadsRows = addr::q6_max_threads(2);  // M = 2..4: 20 rows of 32 lanes, one workgroup per CU at K = 17408
 
 // LDS slot of activation granule g of a staged row (see the header comment).
 __host__ __device__ constexpr int q6_slot(int g) { return g ^ (((g >> 4) & 1) | ((g >> 3) & 12)); }
@@ -70,22 +70,28 @@ struct Q6Raw {
 };
 
 // bp: the block's first byte; sb: 0 or 2, the block's offset into its dword.
+// The reads are the windows of addr::q6_window: the dword-aligned windows
+// around the three quant runs and the scales, and d.
 __device__ __forceinline__ void q6_load(const uint8_t *__restrict__ bp, const int sb, const int h, const int p,
                                         Q6Raw &r) {
   const uint8_t *a = bp - sb;
-  const uint32_t *pa = reinterpret_cast<const uint32_t *>(a + 64 * h + 16 * p);
-  const uint32_t *pc = reinterpret_cast<const uint32_t *>(a + 128 + 32 * h + 16 * p);
-  const uint32_t *ps = reinterpret_cast<const uint32_t *>(a + 192 + 8 * h);
+  const uint32_t *pa =
+      reinterpret_cast<const uint32_t *>(a + addr::q6_run_base(0) + addr::q6_run_h(h, 0) + addr::q6_run_p(p, 0));
+  const uint32_t *pc =
+      reinterpret_cast<const uint32_t *>(a + addr::q6_run_base(2) + addr::q6_run_h(h, 2) + addr::q6_run_p(p, 2));
+  const uint32_t *ps =
+      reinterpret_cast<const uint32_t *>(a + addr::q6_run_base(3) + addr::q6_run_h(h, 3) + addr::q6_run_p(p, 3));
+  const int b_dw = (addr::q6_run(sb, h, p, 1) - addr::q6_run(sb, h, p, 0)) / 4;   // 8
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
     r.a[i] = pa[i];
-    r.b[i] = pa[8 + i];
+    r.b[i] = pa[b_dw + i];
     r.c[i] = pc[i];
   }
   r.s[0] = ps[0];
   r.s[1] = ps[1];
-  r.s[2] = *(ps + (sb ? 2 : 1));  // the third dword only when the scales start mid-dword
-  r.d = *reinterpret_cast<const uint16_t *>(bp + 208);
+  r.s[2] = ps[(addr::q6_run(sb, h, p, 4) - addr::q6_run(sb, h, p, 3)) / 4];
+  r.d = *reinterpret_cast<const uint16_t *>(bp + addr::q6_window(sb, h, p, 5).off);
 }
 
 // The four 6-bit quants (as q' = q + 32, one per byte) of dword i of quarter c.
@@ -261,24 +267,19 @@ __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q6k_ge
 
   const int lane = threadIdx.x & 63;
   const int j = lane & (G - 1);
-  const int u = j & 3, h = u >> 1, p = u & 1;
-  const int jb = j >> 2;
   const int nthreads = (int)blockDim.x;
-  const int row = blockIdx.x * (nthreads / G) + (int)threadIdx.x / G;
-  const bool active = row < n;
-  const int nsteps = NS > 0 ? NS : (nblk + kBlocksPerStep - 1) / kBlocksPerStep;
-  const bool last_ok = jb < nblk - (nsteps - 1) * kBlocksPerStep;
+  const int row = addr::lane_row(blockIdx.x, threadIdx.x, nthreads, G);
   // dword offset of the lane's blocks: 2 bytes when (row * nblk + block) is odd;
   // the same for every step. Fallback loads read block `par` of the matrix
   // (a one-block matrix has only block 0, whose offset is 0).
-  const int par = (n * nblk > 1) ? (((active ? row : 0) * nblk + jb) & 1) : 0;
-  const int sb = 2 * par;
-  const int shift = 16 * par;
-  const uint8_t *wfb = w + par * kQ6KBlockBytes;
-  const uint8_t *wl = w + ((size_t)(active ? row : 0) * (size_t)nblk + (size_t)jb) * kQ6KBlockBytes;
+  const addr::Q6Lane ln = addr::q6_lane(G, NS, n, nblk, row, j);
+  const int h = ln.h, p = ln.p, jb = ln.jb, sb = ln.sb;
+  const bool active = ln.active, last_ok = ln.last_ok;
+  const int nsteps = ln.nsteps;
+  const int shift = 8 * sb;
+  const uint8_t *wl = w + ln.base, *wfb = w + ln.fb;
   auto step_ptr = [&](const int t) -> const uint8_t * {
-    const bool ok = active && t < nsteps && t * kBlocksPerStep + jb < nblk;
-    return ok ? wl + (size_t)(t * kBlocksPerStep) * kQ6KBlockBytes : wfb;
+    return addr::q6_step_ok(ln, G, nblk, t) ? wl + addr::q6_step_offset(G, t) : wfb;
   };
 
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
@@ -376,66 +377,44 @@ __global__ __launch_bounds__(256) void q6k_dequant_kernel(const uint8_t *__restr
   }
 }
 
-// Rows per workgroup: every CU gets the same rows when N splits over 256 CUs
-// into whole-wave workgroups of 256..512 threads (640 for M > 1) that fit the
-// LDS q at a time; otherwise 256 threads.
-inline int q6_pick_rows(const int m, const int n, const int G, const size_t lds) {
-  const int dflt = kMinThreads / G;
-  if (n % 256 != 0) return dflt;
-  const int max_threads = m == 1 ? kMaxThreads : kMaxThreadsRows;
-  const int per_cu = n / 256;
-  for (int q = 1; q <= 8; ++q) {
-    if (per_cu % q != 0) continue;
-    const int threads = (per_cu / q) * G;
-    if (threads > max_threads || threads % 64 != 0) continue;
-    if (threads < kMinThreads || (size_t)q * lds > (size_t)QMV_LDS_X_BYTES) break;
-    return per_cu / q;
-  }
-  return dflt;
-}
-
-template <int M, int G, int D, int NS>
-int q6_launch(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
+// The plan (lanes per row, steps, ring depth, rows per workgroup, grid) is
+// addr::q6_gemv_plan. Ring depths (addr::q6_depth): at M = 1 a 5-step row of
+// 16 lanes keeps every load in flight from the start, and the 9-step rows of
+// 32 lanes run fastest with 2; at M = 2..4 (more registers per step, fewer
+// waves) 3 is fastest for both. Each instantiation below is the one the plan
+// names.
+template <int M, int G, int NS>
+int q6_launch(const addr::GemvPlan &pl, const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
+  constexpr int D = addr::q6_depth(M, G);
   const size_t lds = q6_lds_bytes<M>(k);
   auto *fn = q6k_gemv_kernel<M, G, D, NS>;
   static LdsGrant granted;
   if (allow_dynamic_lds(reinterpret_cast<const void *>(fn), lds, granted, "q6k_gemv_kernel")) return QMV_ERR_HIP;
-  const int rows = q6_pick_rows(M, n, G, lds);
-  const unsigned grid = (unsigned)((n + rows - 1) / rows);
-  return launch_kernel("q6k_gemv_kernel", fn, dim3(grid), dim3(rows * G), lds, stream, w, x, y, n, k);
+  return launch_kernel("q6k_gemv_kernel", fn, dim3(pl.grid), dim3(pl.rows * G), lds, stream, w, x, y, n, k);
 }
-
-// Ring depths (steps). At M = 1 a 5-step row of 16 lanes keeps every load in
-// flight from the start, and the 9-step rows of 32 lanes run fastest with 2;
-// at M = 2..4 (more registers per step, fewer waves) 3 is fastest for both.
-template <int M>
-constexpr int q6_depth16() { return M == 1 ? 5 : 3; }
-template <int M>
-constexpr int q6_depth32() { return M == 1 ? 2 : 3; }
 
 template <int M>
 int q6_launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
-  constexpr int D = q6_depth16<M>(), D32 = q6_depth32<M>();
-  const int nblk = k >> 8;
-  if (k <= 8192) {
-    switch ((nblk + 3) / 4) {
-      case 1: return q6_launch<M, 16, D, 1>(w, x, y, n, k, stream);
-      case 2: return q6_launch<M, 16, D, 2>(w, x, y, n, k, stream);
-      case 3: return q6_launch<M, 16, D, 3>(w, x, y, n, k, stream);
-      case 4: return q6_launch<M, 16, D, 4>(w, x, y, n, k, stream);
-      case 5: return q6_launch<M, 16, D, 5>(w, x, y, n, k, stream);
-      case 6: return q6_launch<M, 16, D, 6>(w, x, y, n, k, stream);
-      case 7: return q6_launch<M, 16, D, 7>(w, x, y, n, k, stream);
-      default: return q6_launch<M, 16, D, 8>(w, x, y, n, k, stream);
+  const addr::GemvPlan p = addr::q6_gemv_plan(M, n, k);
+  if (p.G == 16) {
+    switch (p.ns) {
+      case 1: return q6_launch<M, 16, 1>(p, w, x, y, n, k, stream);
+      case 2: return q6_launch<M, 16, 2>(p, w, x, y, n, k, stream);
+      case 3: return q6_launch<M, 16, 3>(p, w, x, y, n, k, stream);
+      case 4: return q6_launch<M, 16, 4>(p, w, x, y, n, k, stream);
+      case 5: return q6_launch<M, 16, 5>(p, w, x, y, n, k, stream);
+      case 6: return q6_launch<M, 16, 6>(p, w, x, y, n, k, stream);
+      case 7: return q6_launch<M, 16, 7>(p, w, x, y, n, k, stream);
+      default: return q6_launch<M, 16, 8>(p, w, x, y, n, k, stream);
     }
   }
-  switch ((nblk + 7) / 8) {
-    case 5: return q6_launch<M, 32, D32, 5>(w, x, y, n, k, stream);
-    case 6: return q6_launch<M, 32, D32, 6>(w, x, y, n, k, stream);
-    case 7: return q6_launch<M, 32, D32, 7>(w, x, y, n, k, stream);
-    case 8: return q6_launch<M, 32, D32, 8>(w, x, y, n, k, stream);
-    case 9: return q6_launch<M, 32, D32, 9>(w, x, y, n, k, stream);
-    default: return q6_launch<M, 32, D32, 0>(w, x, y, n, k, stream);
+  switch (p.ns) {
+    case 5: return q6_launch<M, 32, 5>(p, w, x, y, n, k, stream);
+    case 6: return q6_launch<M, 32, 6>(p, w, x, y, n, k, stream);
+    case 7: return q6_launch<M, 32, 7>(p, w, x, y, n, k, stream);
+    case 8: return q6_launch<M, 32, 8>(p, w, x, y, n, k, stream);
+    case 9: return q6_launch<M, 32, 9>(p, w, x, y, n, k, stream);
+    default: return q6_launch<M, 32, 0>(p, w, x, y, n, k, stream);
   }
 }
 

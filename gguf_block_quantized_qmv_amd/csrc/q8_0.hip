@@ -3,10 +3,11 @@
 // Q8_0 block (34 bytes, 32 weights): fp16 d then int8 q[32]; w = d * q.
 // Blocks are only 2-byte aligned (34 = 2 mod 4), so a lane reads the 36-byte
 // dword-aligned window that holds its block: eight dwords plus a final dword
-// (block at offset 2 mod 4) or 16-bit half (block at offset 0 mod 4), which
-// keeps every access inside the block's own bytes, then realigns with
-// v_alignbit. 32 lanes own one output row (one block per lane per step);
+// (block at offset 2 mod 4, the window starting in the previous block's last
+// two bytes) or 16-bit half (block at offset 0 mod 4), so every access stays
+// inside the matrix, then realigns with v_alignbit. 32 lanes own one output row (one block per lane per step);
 // activations are staged in LDS as fp32 in swizzled 16-byte granules.
+#include "qmv_addr.h"
 #include "qmv_device.h"
 #include "qmv_internal.h"
 #include "../../include/qmv.h"
@@ -28,8 +29,10 @@ __device__ __forceinline__ int swizzle_granule(int g) { return g ^ ((g >> 4) & 7
 
 // Load Q8_0 block starting at byte offset `off` (even) from a dword-aligned base.
 // Returns d and the 32 quants as 8 little-endian words (q[4i..4i+3] in word i).
+// The reads are addr::q80_window(off): 36 bytes from 2 before the block when it
+// starts mid-dword, else its 34 bytes.
 __device__ __forceinline__ float load_q8_0_block(const uint8_t *__restrict__ base, size_t off, uint32_t (&q)[8]) {
-  const size_t a = off & ~(size_t)3;
+  const size_t a = off - (size_t)(-addr::q80_window(off).off);
   const bool shifted = (off & 3) != 0;  // block starts 2 bytes into its first dword
   const uint32_t *p = reinterpret_cast<const uint32_t *>(base + a);
   uint32_t dw[9];
