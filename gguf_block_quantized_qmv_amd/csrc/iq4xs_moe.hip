@@ -9,9 +9,10 @@
 //
 //  1. iq4xs_moe_gate_up_kernel, grid (F/16 row tiles) x (max distinct experts).
 //     The activations of all T tokens (pair-interleaved, as in the IQ4_XS GEMV)
-//     and the router logits are requested at once; every wave routes a token;
-//     after one barrier every wave sorts the pairs and finds its workgroup's
-//     distinct expert and the tokens that chose it. 16 lanes own a W_gate and a
+//     and the router logits are requested at once; the workgroup routes every
+//     token in one pass (as the Q4_K form does); after one barrier every wave
+//     sorts the pairs and finds its workgroup's distinct expert and the tokens
+//     that chose it. 16 lanes own a W_gate and a
 //     W_up row, lane l taking sub-blocks l, l + 16, ... of both; each index
 //     byte becomes a bf16 weight pair through a 256-entry LDS table and meets
 //     its activation pair in one dot2. h = silu(W_gate x) * (W_up x) in fp32
@@ -42,6 +43,7 @@ using namespace moe;
 constexpr int kWaves = addr::kIq4MoeDnWaves;
 constexpr int kThreads = 64 * kWaves;
 static_assert(kThreads == kTableEntries, "one table entry per thread");
+static_assert(kThreads == kRouteThreads, "the gate/up workgroup routes with every thread");
 // gate/up: 16 lanes per W row, 4 rows per wave, 16 rows per workgroup
 constexpr int kUpLanes = addr::kIq4MoeUpLanes;
 constexpr int kUpRows = addr::kIq4MoeUpRows;
@@ -64,8 +66,7 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_gate_up_kernel(
     const uint16_t *__restrict__ x, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
     int32_t *__restrict__ pairs_out, uint8_t *__restrict__ ws, const int hidden, const int ffn, const int E,
     const int K) {
-  __shared__ int sid[QMV_MOE_MAX_TOKENS][kTopK];
-  __shared__ float swt[QMV_MOE_MAX_TOKENS][kTopK];
+  __shared__ __align__(16) RouteLds rl;
   __shared__ uint32_t tbl[kTableEntries];
   extern __shared__ uint4 xs[];
   const uint8_t *tbl_bytes = reinterpret_cast<const uint8_t *>(tbl);
@@ -82,8 +83,7 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_gate_up_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) g[q] = xg[(size_t)r * (hidden >> 3) + 4 * s + q];
   }
-  const int rt = wave < T ? wave : T - 1;
-  const Logits lg = load_logits(logits, rt, E);
+  const WgLogits<T> lg = load_logits_wg<T>(logits, E);
   {
     const int t = tid < total ? tid : 0;
     const int r = t / nsub, s = t - r * nsub;
@@ -93,7 +93,8 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_gate_up_kernel(
     for (int q = 0; q < 4; ++q) xs[r * rg + x_slot(s) + q] = o[q];
   }
   tbl[tid] = grid_bf16((uint32_t)tid & 15u) | (grid_bf16((uint32_t)tid >> 4) << 16);
-  route_token(lg, rt, wave < T, E, K, sid, swt);
+  uint32_t *kr = reinterpret_cast<uint32_t *>(xs + (size_t)T * rg);   // routing rows
+  store_keys<T>(lg, E, kr, rl);
   for (int t = tid + kThreads; t < total; t += kThreads) {
     const int r = t / nsub, s = t - r * nsub;
     const uint4 *src = xg + (size_t)r * (hidden >> 3) + 4 * s;
@@ -103,12 +104,12 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_gate_up_kernel(
     for (int q = 0; q < 4; ++q) xs[r * rg + x_slot(s) + q] = o[q];
   }
   __syncthreads();
+  route_wave<T>(kr, E, K, rl);
+  __syncthreads();
 
   const int P = T * K;
-  const SortedPairs pr = sort_pairs(sid, swt, P, K);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && wave == 0)
-    write_routing(pr, P, topk_ids, topk_w, pairs_out, reinterpret_cast<Table *>(ws));
-  const Slot<T> sl = find_slot<T>(pr, (int)blockIdx.y, P);
+  const PairRank pr = pair_ranks<T>(rl, P);
+  const Slot<T> sl = my_slot<T>(pr, (int)blockIdx.y, P);
   if (sl.p0 < 0) return;  // fewer distinct experts than the grid allows for (uniform over the workgroup)
 
   const int l = tid % kUpLanes;
@@ -129,6 +130,11 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_gate_up_kernel(
     load_unit((d < nlive ? gl + addr::iq4_unit_offset(d, ln.unit_bytes) : grow), qoff, rg_[d]);
     load_unit((d < nlive ? ul + addr::iq4_unit_offset(d, ln.unit_bytes) : urow), qoff, ru_[d]);
   }
+  // the weights (softmax) and the routing outputs, off the path to the loads
+  // above: the last wave of workgroup (0, 0)
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid >= kThreads - 64)
+    write_routing(with_weights(sorted_pairs(pr, P), rl, P, K), P, topk_ids, topk_w, pairs_out,
+                  reinterpret_cast<Table *>(ws));
 
   int xoff[T];
 #pragma unroll

@@ -9,12 +9,13 @@
 //
 //  1. moe_gate_up_kernel, grid (F/16 row tiles) x (max distinct experts).
 //     The activations of all T tokens and the router logits are requested at
-//     once; then wave t routes token t (k rounds of a wave-wide argmax, ties
-//     to the lower id, then the softmax over the k chosen logits; waves past T
-//     repeat token T-1's routing without storing it). Every wave then sorts the
-//     (expert, token) pairs in registers (rank by comparison, forward lane
-//     permute) and finds its workgroup's distinct expert, the s-th smallest,
-//     and the tokens that chose it, without another barrier. Workgroup (0, 0)
+//     once; the workgroup then routes every token in one pass (each expert
+//     ranked by counting the token's larger composite keys -- logit, then the
+//     lower id -- the K of rank below K chosen in rank order), and every wave
+//     sorts the (expert, token) pairs in registers (rank by comparison,
+//     forward lane permute), forms their weights (the softmax over each
+//     token's chosen logits) and finds its workgroup's distinct expert, the
+//     s-th smallest, and the tokens that chose it. Workgroup (0, 0)
 //     writes the routing outputs and the tables launch 2 reads. The expert's
 //     gate and up rows are requested as soon as the expert is known; the
 //     activation sub-block sums are formed in LDS while they arrive. Each
@@ -56,6 +57,7 @@ constexpr int kUpDepth = addr::kMoeUpDepth;  // steps of gate + up loads in flig
 constexpr int kDnRows = addr::kMoeDnRows;
 constexpr int kDnGroups = addr::kMoeDnGroups;
 constexpr int kDnDepth = addr::kMoeDnDepth;  // (expert, block) units of loads in flight per lane
+static_assert(kThreads == kRouteThreads, "the gate/up workgroup routes with every thread");
 static_assert(kThreads == 64 * kWaves && kUpRows == kWaves * (64 / kUpLanes) && kDnGroups == kThreads / (4 * kDnRows),
               "the shapes the addressing assumes");
 
@@ -165,36 +167,35 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(
     const uint16_t *__restrict__ x, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
     int32_t *__restrict__ pairs_out, uint8_t *__restrict__ ws, const int hidden, const int ffn, const int E,
     const int K) {
-  __shared__ int sid[QMV_MOE_MAX_TOKENS][kTopK];
-  __shared__ float swt[QMV_MOE_MAX_TOKENS][kTopK];
+  __shared__ __align__(16) RouteLds rl;
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gpr = hidden >> 3, nsub = hidden >> 5;
   const int gpp = (int)padded_row_granules(hidden);
   uint4 *xs = lds;
   float *xsum = reinterpret_cast<float *>(lds + (size_t)T * gpp);
+  uint32_t *kr = reinterpret_cast<uint32_t *>(xsum + (size_t)T * nsub);   // routing rows
 
   // every token's activations and the router logits are requested together
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
   const int total = T * gpr;
   uint4 v[kStageBatch];
   load_x_batch<T>(xg, 0, total, v);
-  const int rt = wave < T ? wave : T - 1;
-  const Logits lg = load_logits(logits, rt, E);
+  const WgLogits<T> lg = load_logits_wg<T>(logits, E);
   store_x_batch<T>(xs, 0, total, gpr, gpp, v);
-  route_token(lg, rt, wave < T, E, K, sid, swt);
+  store_keys<T>(lg, E, kr, rl);
   for (int base = kStageBatch * kThreads; base < total; base += kStageBatch * kThreads) {
     uint4 vb[kStageBatch];
     load_x_batch<T>(xg, base, total, vb);
     store_x_batch<T>(xs, base, total, gpr, gpp, vb);
   }
   __syncthreads();
+  route_wave<T>(kr, E, K, rl);
+  __syncthreads();
 
   const int P = T * K;
-  const SortedPairs pr = sort_pairs(sid, swt, P, K);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && wave == 0)
-    write_routing(pr, P, topk_ids, topk_w, pairs_out, reinterpret_cast<Table *>(ws));
-  const Slot<T> sl = find_slot<T>(pr, (int)blockIdx.y, P);
+  const PairRank pr = pair_ranks<T>(rl, P);
+  const Slot<T> sl = my_slot<T>(pr, (int)blockIdx.y, P);
   if (sl.p0 < 0) return;  // fewer distinct experts than the grid allows for (uniform over the workgroup)
 
   const int j = lane & (kUpLanes - 1);
@@ -214,6 +215,12 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(
       load_up_step(addr::moe_up_step_at(ul, u), c, uh[u], ua[u], ub[u]);
     }
   }
+  // the weights (softmax) and the routing outputs, off the path to the loads
+  // above: the last wave of workgroup (0, 0), whose waves all hold the expert
+  // of slot 0
+  if (blockIdx.x == 0 && blockIdx.y == 0 && wave == kWaves - 1)
+    write_routing(with_weights(sorted_pairs(pr, P), rl, P, K), P, topk_ids, topk_w, pairs_out,
+                  reinterpret_cast<Table *>(ws));
 
   // sub-block sums of every staged token (index order) while the weights arrive
   for (int t = threadIdx.x; t < T * nsub; t += kThreads) {

@@ -60,9 +60,15 @@ constexpr size_t kMoeTableBytes = 4096;
 constexpr size_t moe_workspace(int t, int ffn, int top_k) {
   return kMoeTableBytes + (size_t)t * (size_t)top_k * (size_t)ffn * 4;
 }
-// Q4_K: x rows staged as in the dense GEMV; h rows in 64-value chunks of 17
-// granules (fp32) plus their per-32 sums. Static LDS stays under 4 KiB.
-constexpr size_t q4k_moe_gate_up_lds(int t, int hidden) { return q4k_x_lds(t, hidden); }
+// The gate/up launch routes every token in LDS: one row of 8-byte composite
+// keys per token, QMV_MOE_MAX_EXPERTS of them.
+constexpr size_t kMoeRouteBytesPerToken = (size_t)QMV_MOE_MAX_EXPERTS * 8;
+// Q4_K: x rows staged as in the dense GEMV, then the routing rows; h rows in
+// 64-value chunks of 17 granules (fp32) plus their per-32 sums. Static LDS
+// stays under 4 KiB.
+constexpr size_t q4k_moe_gate_up_lds(int t, int hidden) {
+  return q4k_x_lds(t, hidden) + (size_t)t * kMoeRouteBytesPerToken;
+}
 constexpr size_t q4k_moe_down_lds(int pairs, int ffn) {
   return (size_t)pairs * ((size_t)(ffn >> 6) * 17 * 16 + (size_t)(ffn >> 5) * 4);
 }
@@ -79,7 +85,7 @@ static_assert(kMoeNoAllocBytes == 160 * 1024, "the bound derived above");
 // IQ4_XS: x rows pair-interleaved as in its GEMV; h in fp32 with a 144-byte
 // sub-block stride. Static LDS stays under 8 KiB.
 constexpr size_t iq4xs_moe_gate_up_lds(int t, int hidden) {
-  return (size_t)t * iq4xs_row_granules(hidden >> 5) * 16;
+  return (size_t)t * iq4xs_row_granules(hidden >> 5) * 16 + (size_t)t * kMoeRouteBytesPerToken;
 }
 constexpr size_t iq4xs_moe_down_lds(int pairs, int ffn) { return (size_t)pairs * (size_t)(ffn >> 5) * 9 * 16; }
 constexpr bool iq4xs_moe_fits_lds(int t, int hidden, int ffn, int top_k) {

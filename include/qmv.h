@@ -234,9 +234,10 @@ size_t qmv_q4_k_moe_workspace(int t, int hidden, int ffn, int n_experts, int top
  *   ws, ws_bytes  workspace of at least qmv_q4_k_moe_workspace(...) bytes, 256-B aligned
  *   1 <= t <= QMV_MOE_MAX_TOKENS, 1 <= top_k <= min(QMV_MOE_MAX_TOP_K, n_experts),
  *   1 <= n_experts <= QMV_MOE_MAX_EXPERTS, hidden and ffn multiples of 256.
- *   The staged activations and h must fit in LDS next to 4 KiB of tables:
- *   t*((hidden/128)*272 + (hidden/32)*4) and t*top_k*((ffn/64)*272 + (ffn/32)*4)
- *   bytes each <= QMV_LDS_X_BYTES - 4096, else QMV_ERR_RANGE.
+ *   The staged activations (with the routing rows) and h must fit in LDS next
+ *   to 4 KiB of tables: t*((hidden/128)*272 + (hidden/32)*4 + 2048) and
+ *   t*top_k*((ffn/64)*272 + (ffn/32)*4) bytes each <= QMV_LDS_X_BYTES - 4096,
+ *   else QMV_ERR_RANGE.
  * Per token: the top_k largest logits (ties -> lower expert id) select experts
  * e_j; r_j = softmax over the selected logits; h = silu(W_gate x) * (W_up x) in
  * fp32; y = sum_j r_j * W_down[e_j] h, summed in rank order j. Each selected
@@ -313,8 +314,8 @@ size_t qmv_iq4_xs_moe_workspace(int t, int hidden, int ffn, int n_experts, int t
  * and error codes as qmv_q4_k_moe, except:
  *   w_gate, w_up, w_down  8-byte aligned banks of 136-byte IQ4_XS blocks;
  *                 bank_bytes must equal n_experts*ffn*(hidden/256)*136
- *   LDS limits    t*(hidden/32)*68 and t*top_k*(ffn/32)*144 bytes each
- *                 <= QMV_LDS_X_BYTES - 8192, else QMV_ERR_RANGE.
+ *   LDS limits    t*((hidden/32)*68 + 2048) and t*top_k*(ffn/32)*144 bytes
+ *                 each <= QMV_LDS_X_BYTES - 8192, else QMV_ERR_RANGE.
  * h = silu(W_gate x) * (W_up x) is formed in fp32 from bf16 weight pairs and
  * bf16 activations (dot2, fp32 accumulation) and W_down h in fp32 (fma). The
  * selection, its tie rule, the weights and the rank-order combine are those
