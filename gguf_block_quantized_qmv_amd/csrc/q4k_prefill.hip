@@ -56,21 +56,25 @@ struct Cfg {
   static_assert(WM_WAVES * 64 == BM && WN_WAVES * 64 == BN, "four 64x64 wave tiles");
 };
 
-// Granule g (8 bf16 of K) of tile row r sits at slot (g + f) & 7 of the row,
-// f being t = (r >> 1) & 7 with bits 1 and 2 swapped. LDS serves 16 lanes of a
-// 16-byte access per cycle from 16 bank groups (a group = 16 bytes; a row is
-// 8 groups, so rows of one parity share the same 8):
-//  * MFMA fragment reads (16 consecutive rows, one granule): the 8 rows of each
-//    parity take 8 distinct t, so 8 distinct f;
-//  * X tile writes (2 rows, all 8 granules each): distinct within a row;
-//  * W tile writes (8 rows, granules g and g + 2 from the two lanes of a row):
-//    the 4 rows of each parity take f in {0, 1, 4, 5} or {2, 3, 6, 7}, so f and
-//    f + 2 cover 8 distinct slots.
-// (A rotation by r alone put rows r and r + 8 on one group: a 2-way conflict
-// on every fragment read.)
+// Granule g (8 bf16 of K) of tile row r sits at slot (g + f(r)) & 7 of the
+// row, with f(r) = 2 ((r >> 2) & 3) + 4 (r & 1) + ((r >> 1) & 1) mod 8.
+// Measured on gfx950 (ds_read_b128 / ds_write_b128 with a bank-conflict
+// counter): a 16-byte read serves 16 lanes per cycle from 16 groups of 16 B
+// (group = slot mod 16), a 16-byte write 8 lanes per cycle from 8 groups
+// (slot mod 8). A row is 8 slots, so for reads rows of one parity share
+// their 8 groups. The layout keeps every access of the kernel conflict-free:
+//  * MFMA fragment reads (16 consecutive rows from a multiple of 16, one
+//    granule): the 8 even rows take f = 2q + {0, 1} (q = 0..3), all 8
+//    values, and the odd rows the same plus 4;
+//  * X tile writes (one row per 8 lanes, all 8 granules): distinct within a
+//    row;
+//  * W tile writes (8 lanes: rows 4k .. 4k + 3, granules g and g + 2): the
+//    four rows take f in {2q, 2q + 4, 2q + 1, 2q + 5}, and f and f + 2 cover
+//    all 8 slots.
+// (The layout before this one paired rows 2i and 2i + 1 on the same f, a
+// 2-way conflict on every W write.)
 __device__ __forceinline__ int tslot(int r, int g) {
-  const int t = (r >> 1) & 7;
-  const int f = (t & 1) | ((t & 2) << 1) | ((t & 4) >> 1);
+  const int f = 2 * ((r >> 2) & 3) + 4 * (r & 1) + ((r >> 1) & 1);
   return r * 8 + ((g + f) & 7);
 }
 
