@@ -4,6 +4,7 @@
     python -m gguf_block_quantized_qmv_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR --kernel NAME \
         --read-bytes B [--copy-bytes C] [--algo-bytes A]
     python -m gguf_block_quantized_qmv_amd.rocprof_summary mfma DIR --kernel NAME [--flops F] [--simds S]
+    python -m gguf_block_quantized_qmv_amd.rocprof_summary counters DIR [DIR ...] --kernel NAME [--ratio A/B ...]
 
 DIR is a rocprofv3 output directory (`-d DIR -f csv`): `trace` reads its
 *_kernel_trace.csv (run with --kernel-trace), `traffic` and `mfma` its
@@ -24,6 +25,9 @@ mfma     MFMA utilisation per dispatch: SQ_VALU_MFMA_BUSY_CYCLES (summed over
          implied clock, active cycles / duration, is printed as a check), and
          the bf16 MFMA work from SQ_INSTS_VALU_MFMA_MOPS_BF16 (units of 512
          flops), checked against --flops when given.
+counters per (kernel, grid, workgroup) group over one or more --pmc passes:
+         the median of every counter collected, and each --ratio A/B as the
+         ratio of the two medians (A and B counter names from any pass).
 """
 
 from __future__ import annotations
@@ -188,6 +192,34 @@ def mfma(args) -> None:
             print(f"| {key[0]} | {key[1]} x {key[2]} | " + " | ".join(f"{v:.4g}" for v in vals) + " |")
 
 
+def counters(args) -> None:
+    groups = collections.OrderedDict()
+    for d in args.dirs:
+        for r in _csv(d, "counter_collection.csv"):
+            if args.kernel in r["Kernel_Name"]:
+                key = (short_name(r["Kernel_Name"]), _grid(r) // max(1, _wg(r)), _wg(r))
+                groups.setdefault(key, collections.defaultdict(list))[r["Counter_Name"]].append(
+                    float(r["Counter_Value"]))
+    if not groups:
+        raise SystemExit(f"no dispatch of {args.kernel}")
+    names = sorted({c for g in groups.values() for c in g})
+    print("| kernel | workgroups x threads | " + " | ".join(names) + " |")
+    print("|---|---|" + "---:|" * len(names))
+    for key, g in groups.items():
+        vals = [f"{statistics.median(g[c]):.4g}" if g.get(c) else "-" for c in names]
+        print(f"| {key[0]} | {key[1]} x {key[2]} | " + " | ".join(vals) + " |")
+    if args.ratio:
+        print()
+        print("| kernel | workgroups x threads | " + " | ".join(args.ratio) + " |")
+        print("|---|---|" + "---:|" * len(args.ratio))
+        for key, g in groups.items():
+            out = []
+            for rt in args.ratio:
+                a, b = rt.split("/")
+                out.append(f"{statistics.median(g[a]) / statistics.median(g[b]):.4g}" if g.get(a) and g.get(b) else "-")
+            print(f"| {key[0]} | {key[1]} x {key[2]} | " + " | ".join(out) + " |")
+
+
 def main(argv=None) -> None:
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -212,6 +244,11 @@ def main(argv=None) -> None:
     m.add_argument("--simds", type=int, default=1024, help="SIMDs on the device (MI355X: 256 CUs x 4)")
     m.add_argument("--xcds", type=int, default=8, help="instances GRBM_GUI_ACTIVE is summed over (MI355X: 8 XCDs)")
     m.set_defaults(fn=mfma)
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--ratio", action="append", default=[], help="A/B: ratio of the medians of counters A and B")
+    c.set_defaults(fn=counters)
     args = p.parse_args(argv)
     args.fn(args)
 
