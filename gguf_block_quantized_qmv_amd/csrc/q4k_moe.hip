@@ -161,14 +161,16 @@ __device__ __forceinline__ void store_x_batch(uint4 *xs, const int base, const i
   }
 }
 
+// Workgroup (tile, slot) of launch 1: rows 16 tile .. of the slot-th distinct
+// expert's W_gate and W_up. Returns with every thread of the workgroup past
+// its last barrier (threads without a row return early).
 template <int T>
-__global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(
-    const uint8_t *__restrict__ w_gate, const uint8_t *__restrict__ w_up, const float *__restrict__ logits,
-    const uint16_t *__restrict__ x, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
-    int32_t *__restrict__ pairs_out, uint8_t *__restrict__ ws, const int hidden, const int ffn, const int E,
-    const int K) {
-  __shared__ __align__(16) RouteLds rl;
-  extern __shared__ uint4 lds[];
+__device__ __forceinline__ void gate_up_body(const uint8_t *__restrict__ w_gate, const uint8_t *__restrict__ w_up,
+                                             const float *__restrict__ logits, const uint16_t *__restrict__ x,
+                                             int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
+                                             int32_t *__restrict__ pairs_out, uint8_t *__restrict__ ws,
+                                             const int hidden, const int ffn, const int E, const int K,
+                                             const int tile, const int slot, RouteLds &rl, uint4 *lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gpr = hidden >> 3, nsub = hidden >> 5;
   const int gpp = (int)padded_row_granules(hidden);
@@ -195,11 +197,11 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(
 
   const int P = T * K;
   const PairRank pr = pair_ranks<T>(rl, P);
-  const Slot<T> sl = my_slot<T>(pr, (int)blockIdx.y, P);
+  const Slot<T> sl = my_slot<T>(pr, slot, P);
   if (sl.p0 < 0) return;  // fewer distinct experts than the grid allows for (uniform over the workgroup)
 
   const int j = lane & (kUpLanes - 1);
-  const addr::MoeUpLane ln = addr::moe_up_lane(sl.e, ffn, hidden, blockIdx.x, threadIdx.x);
+  const addr::MoeUpLane ln = addr::moe_up_lane(sl.e, ffn, hidden, tile, threadIdx.x);
   const int c = ln.c, jb = ln.jb, f = ln.f;
   const bool active = ln.active;
   const int nblk = hidden >> 8;
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(
   // the weights (softmax) and the routing outputs, off the path to the loads
   // above: the last wave of workgroup (0, 0), whose waves all hold the expert
   // of slot 0
-  if (blockIdx.x == 0 && blockIdx.y == 0 && wave == kWaves - 1)
+  if (tile == 0 && slot == 0 && wave == kWaves - 1)
     write_routing(with_weights(sorted_pairs(pr, P), rl, P, K), P, topk_ids, topk_w, pairs_out,
                   reinterpret_cast<Table *>(ws));
 
@@ -282,6 +284,18 @@ __global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(
     const float u = row16_sum(acc_u[r]);
     if (j == r) h[(size_t)(sl.p0 + r) * ffn + f] = g / (1.0f + expf(-g)) * u;
   }
+}
+
+template <int T>
+__global__ __launch_bounds__(kThreads) void moe_gate_up_kernel(
+    const uint8_t *__restrict__ w_gate, const uint8_t *__restrict__ w_up, const float *__restrict__ logits,
+    const uint16_t *__restrict__ x, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
+    int32_t *__restrict__ pairs_out, uint8_t *__restrict__ ws, const int hidden, const int ffn, const int E,
+    const int K) {
+  __shared__ __align__(16) RouteLds rl;
+  extern __shared__ uint4 lds[];
+  gate_up_body<T>(w_gate, w_up, logits, x, topk_ids, topk_w, pairs_out, ws, hidden, ffn, E, K, (int)blockIdx.x,
+                  (int)blockIdx.y, rl, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -366,13 +380,24 @@ __device__ __forceinline__ void store_h_batch(uint4 *hs, const int base, const i
   }
 }
 
+// Every pair's h from the workspace into LDS, two batches per round trip; no
+// other load is waited for in between, so each round's waits are exact.
+__device__ __forceinline__ void stage_h(const uint4 *__restrict__ hg, const int total, uint4 *hs) {
+  for (int base = 0; base < total; base += 2 * kHBatch * kThreads) {
+    uint4 hb0[kHBatch], hb1[kHBatch];
+    load_h_batch(hg, base, total, hb0);
+    load_h_batch(hg, base + kHBatch * kThreads, total, hb1);
+    store_h_batch(hs, base, total, hb0);
+    store_h_batch(hs, base + kHBatch * kThreads, total, hb1);
+  }
+}
+
+// Workgroup `tile` of launch 2: W_down rows 8 tile .. + 7 for every pair, then
+// the weighted combine.
 template <int T>
-__global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__restrict__ w_down,
-                                                            const uint8_t *__restrict__ ws, float *__restrict__ y,
-                                                            const int hidden, const int ffn, const int P) {
-  __shared__ Table R;
-  __shared__ float zbuf[kMaxPairs][kDnRows];
-  extern __shared__ uint4 lds[];
+__device__ __forceinline__ void down_body(const uint8_t *__restrict__ w_down, const uint8_t *__restrict__ ws,
+                                          float *__restrict__ y, const int hidden, const int ffn, const int P,
+                                          const int tile, Table &R, float (&zbuf)[kMaxPairs][kDnRows], uint4 *lds) {
   const int tid = threadIdx.x;
   const int cpr = ffn >> 6;   // 64-value chunks per h row
   const int nsub = ffn >> 5;
@@ -380,26 +405,18 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__res
   uint4 *hs = lds;
   float *hsum = reinterpret_cast<float *>(lds + (size_t)P * cpr * 17);
 
-  // The tables and every pair's h are in LDS before the barrier, two h batches
-  // per round trip; no load is outstanding yet, so each round's waits are
-  // exact and its loads are all in flight together.
-  const uint4 *hg = reinterpret_cast<const uint4 *>(ws + kTableBytes);
-  const int total = P * (ffn >> 2);
+  // The tables and every pair's h are in LDS before the barrier; no load is
+  // outstanding yet, so each round's waits are exact and its loads are all in
+  // flight together.
   {
     const int tword = reinterpret_cast<const int *>(ws)[tid < kTableWords ? tid : 0];
-    for (int base = 0; base < total; base += 2 * kHBatch * kThreads) {
-      uint4 hb0[kHBatch], hb1[kHBatch];
-      load_h_batch(hg, base, total, hb0);
-      load_h_batch(hg, base + kHBatch * kThreads, total, hb1);
-      store_h_batch(hs, base, total, hb0);
-      store_h_batch(hs, base + kHBatch * kThreads, total, hb1);
-    }
+    stage_h(reinterpret_cast<const uint4 *>(ws + kTableBytes), P * (ffn >> 2), hs);
     reinterpret_cast<int *>(&R)[tid < kTableWords ? tid : 0] = tword;  // lanes past the table rewrite word 0
   }
   __syncthreads();
 
   // lane group grp (32 lanes: 8 rows x 4 chunks) takes distinct experts grp, grp + 8, ...
-  const addr::MoeDnLane ln = addr::moe_dn_lane(hidden, ffn, R.n_slots, blockIdx.x, tid);
+  const addr::MoeDnLane ln = addr::moe_dn_lane(hidden, ffn, R.n_slots, tile, tid);
   const int grp = ln.grp;
   const int c = ln.c;
   const int i_row = (tid & 31) >> 2;
@@ -472,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__res
   // y[t][n] = sum over token t's experts in routing rank order of weight * z
   if (tid < T * kDnRows) {
     const int t = tid / kDnRows, i = tid % kDnRows;
-    const int nn = blockIdx.x * kDnRows + i;
+    const int nn = tile * kDnRows + i;
     const int K = P / T;
     float out = 0.0f;
     for (int j = 0; j < K; ++j) {
@@ -485,21 +502,31 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__res
 
 
 template <int T>
+__global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t *__restrict__ w_down,
+                                                            const uint8_t *__restrict__ ws, float *__restrict__ y,
+                                                            const int hidden, const int ffn, const int P) {
+  __shared__ Table R;
+  __shared__ float zbuf[kMaxPairs][kDnRows];
+  extern __shared__ uint4 lds[];
+  down_body<T>(w_down, ws, y, hidden, ffn, P, (int)blockIdx.x, R, zbuf, lds);
+}
+
+template <int T>
 int launch_t(const void *w_gate, const void *w_up, const void *w_down, const float *logits, const uint16_t *x,
              float *y, int32_t *topk_ids, float *topk_w, int32_t *pairs, void *ws, int hidden, int ffn,
              int n_experts, int top_k, hipStream_t s) {
   static LdsGrant granted_a, granted_b;
   const size_t lds_a = layout::q4k_moe_gate_up_lds(T, hidden), lds_b = layout::q4k_moe_down_lds(T * top_k, ffn);
+  const int max_slots = n_experts < T * top_k ? n_experts : T * top_k;
+  const dim3 grid_a((unsigned)((ffn + kUpRows - 1) / kUpRows), (unsigned)max_slots);
+  const dim3 grid_b((unsigned)((hidden + kDnRows - 1) / kDnRows));
   if (allow_dynamic_lds(reinterpret_cast<const void *>(&moe_gate_up_kernel<T>), lds_a, granted_a,
                         "moe_gate_up_kernel lds") ||
       allow_dynamic_lds(reinterpret_cast<const void *>(&moe_down_kernel<T>), lds_b, granted_b, "moe_down_kernel lds"))
     return QMV_ERR_HIP;
-  const int max_slots = n_experts < T * top_k ? n_experts : T * top_k;
-  const dim3 grid_a((unsigned)((ffn + kUpRows - 1) / kUpRows), (unsigned)max_slots);
   int rc = launch_kernel("moe_gate_up_kernel", moe_gate_up_kernel<T>, grid_a, dim3(kThreads), lds_a, s, w_gate, w_up,
                          logits, x, topk_ids, topk_w, pairs, ws, hidden, ffn, n_experts, top_k);
   if (rc) return rc;
-  const dim3 grid_b((unsigned)((hidden + kDnRows - 1) / kDnRows));
   return launch_kernel("moe_down_kernel", moe_down_kernel<T>, grid_b, dim3(kThreads), lds_b, s, w_down, ws, y,
                        hidden, ffn, T * top_k);
 }

@@ -79,3 +79,49 @@ def test_noalloc_rejects_what_the_workspace_entry_point_rejects():
     args = (_ptr(g), _ptr(g), _ptr(g), g.numel(), _ptr(lg), _ptr(xd), _ptr(y), None, None, None)
     assert q.lib.qmv_q4_k_moe_noalloc(*args, 5, 512, 256, 16, 4, None) == -5          # T above 4
     assert q.lib.qmv_q4_k_moe_noalloc(*args[:3], g.numel() - 1, *args[4:], 1, 512, 256, 16, 4, None) == -3
+
+
+def _noalloc(q, dev, args, y, stream):
+    g, u, d, bank, lg, xd, t, hidden, ffn, ne, tk = args
+    return q.lib.qmv_q4_k_moe_noalloc(_ptr(g), _ptr(u), _ptr(d), bank, _ptr(lg), _ptr(xd), _ptr(y), None, None, None,
+                                      t, hidden, ffn, ne, tk, stream)
+
+
+def _layer(dev, seed, hidden, ffn, ne, tk):
+    gate, up, down = synth.moe_bank(seed, ne, hidden, ffn)
+    lg = to_dev(synth.moe_logits(seed, 1, ne), dev)
+    xd = to_dev(synth.bf16_normal(seed + 1, (1, hidden)), dev)
+    g, u, d = (to_dev(a, dev) for a in (gate, up, down))
+    return (g, u, d, g.numel(), lg, xd, 1, hidden, ffn, ne, tk)
+
+
+def test_noalloc_one_token_back_to_back_and_graph_replays():
+    """One token at a time, the decode case: five calls in a row on different
+    tokens and banks each agree bit for bit with the workspace entry point,
+    and so do three replays of a captured call with other calls through the
+    same array in between (each replay must rewrite everything it reads)."""
+    import gguf_block_quantized_qmv_amd as q
+    dev = device()
+    shapes = [(2048, 768, 128, 8), (512, 256, 16, 4), (2048, 768, 128, 8), (1024, 512, 64, 6), (2048, 768, 128, 8)]
+    for i, shp in enumerate(shapes):
+        _both(q, dev, 200 + i, 1, *shp)
+
+    main = _layer(dev, 300, 2048, 768, 128, 8)
+    other = _layer(dev, 301, 2048, 768, 128, 8)
+    y_ref, _, _, _ = q.qmv_q4_k_moe(*main[:3], main[4], main[5], 2048, 768, 128, 8, routing=False)
+    y_other = torch.empty((1, 2048), dtype=torch.float32, device=dev)
+    y_graph = torch.full((1, 2048), float("nan"), dtype=torch.float32, device=dev)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert _noalloc(q, dev, main, y_graph, ctypes.c_void_p(s.cuda_stream)) == 0   # warm-up on the capture stream
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        assert _noalloc(q, dev, main, y_graph, ctypes.c_void_p(s.cuda_stream)) == 0
+    for _ in range(3):
+        y_graph.fill_(float("nan"))
+        assert _noalloc(q, dev, other, y_other, None) == 0   # another token through the same array
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_graph.view(torch.int32), y_ref.view(torch.int32))
