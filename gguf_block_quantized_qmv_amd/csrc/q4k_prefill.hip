@@ -6,18 +6,20 @@
 // are dequantized into bf16 tiles in LDS and fed to v_mfma_f32_32x32x16_bf16
 // with fp32 accumulation.
 //
-// Tiling. A 512-thread workgroup owns a 128 (rows of X) x 128 (rows of W) tile
+// Tiling. A 1024-thread workgroup owns a 256 (rows of X) x 128 (rows of W) tile
 // of Y. K advances 64 at a time -- one 64-weight chunk of each W row's
-// super-block -- through two LDS stages of 32 KiB (X tile + W tile, rows of
+// super-block -- through two LDS stages of 48 KiB (X tile + W tile, rows of
 // eight 16-byte granules, swizzled so that no 16-byte access conflicts on the
-// LDS banks). The waves split into two kinds. Four consumers each own a 64 x 64
-// quarter, four 32x32 MFMA tiles (64 fp32 accumulators per lane), and only read
-// fragments and issue matrix instructions. Four producers run kDepth steps of
+// LDS banks). The waves split into two kinds. Eight consumers each own a 64 x 64
+// part, four 32x32 MFMA tiles (64 fp32 accumulators per lane), and only read
+// fragments and issue matrix instructions. Eight producers run kDepth steps of
 // global loads ahead through a ring of registers: while the consumers work on
 // stage s, the producers write step s + 1 (loaded kDepth - 1 steps earlier) into
 // the other stage, dequantizing W, and send the loads of step s + 1 + kDepth.
-// Each SIMD runs one wave of each kind, so the dequantization issues while the
-// other wave's matrix instructions execute. Every load is unconditional (steps
+// Each SIMD runs two waves of each kind, so the dequantization issues while the
+// other waves' matrix instructions execute. The 256-row tile writes a quarter
+// fewer LDS bytes per flop than 128 x 128 (16-byte LDS writes run at about a
+// third of the read rate) and dequantizes each W chunk once per 256 rows of X. Every load is unconditional (steps
 // past K reload the last step) and the step loop is unrolled by kDepth, which
 // divides the step count because K is a multiple of 256, so each wait covers
 // exactly the slot being consumed.
@@ -47,13 +49,14 @@ constexpr int kThreads = addr::kPrefillHalf;
 template <int BM_, int BN_, int DEPTH_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, kDepth = DEPTH_;
-  static constexpr int WN_WAVES = BN / 64, WM_WAVES = 4 / WN_WAVES;   // wave tile 64 x 64
+  static constexpr int kWaves = kThreads / 64;                      // consumer (and producer) waves
+  static constexpr int WN_WAVES = BN / 64, WM_WAVES = kWaves / WN_WAVES;   // wave tile 64 x 64
   static constexpr int kXGran = BM * 8, kWGran = BN * 8, kStageGran = kXGran + kWGran;
   static constexpr size_t kLdsBytes = 2 * (size_t)kStageGran * 16;
   static constexpr int kXPerThread = kXGran / kThreads;
   static constexpr int kWThreadsPerRow = kThreads / BN;          // 2 or 4
   static constexpr int kQBytes = 32 / kWThreadsPerRow;            // quant bytes per thread: 16 or 8
-  static_assert(WM_WAVES * 64 == BM && WN_WAVES * 64 == BN, "four 64x64 wave tiles");
+  static_assert(WM_WAVES * 64 == BM && WN_WAVES * 64 == BN, "one 64x64 wave tile per consumer wave");
 };
 
 // Granule g (8 bf16 of K) of tile row r sits at slot (g + f(r)) & 7 of the
@@ -172,11 +175,11 @@ __device__ __forceinline__ void read_frags(const uint4 *__restrict__ xt, const u
 
 // Tile t as (mt, nt): addr::tile_of.
 
-// Wave-specialised form: eight waves per workgroup. Waves 4..7 produce -- they
-// load X and the Q4_K blocks kDepth steps ahead, dequantize W and write the
-// next LDS stage -- while waves 0..3 consume the current stage with MFMAs (a
-// 64 x 64 quarter each). Each SIMD runs one wave of each kind, so the
-// dequantization VALU work issues while the other wave's matrix instructions
+// Wave-specialised form: 2 kWaves waves per workgroup. Waves kWaves.. produce --
+// they load X and the Q4_K blocks kDepth steps ahead, dequantize W and write the
+// next LDS stage -- while waves 0 .. kWaves - 1 consume the current stage with
+// MFMAs (a 64 x 64 part each). Each SIMD runs waves of both kinds, so the
+// dequantization VALU work issues while the other waves' matrix instructions
 // execute. One barrier per step hands a stage from the producers to the
 // consumers and back; both kinds pass the same number of barriers.
 //
@@ -184,9 +187,9 @@ __device__ __forceinline__ void read_frags(const uint4 *__restrict__ xt, const u
 // r_tiles tiles after them, when the tile count does not divide over the
 // workgroups the device holds at once, are split along K: block t_main + s *
 // r_tiles + r computes part s of tile t_main + r -- a run of whole 256-value
-// K blocks -- and stores its 128 x 128 sums to that part's slot of `part`;
+// K blocks -- and stores its BM x BN sums to that part's slot of `part`;
 // q4k_prefill_reduce_kernel adds the parts in order afterwards.
-// Two workgroups (four waves per SIMD) per CU: at most 128 VGPRs per lane.
+// One workgroup (four waves per SIMD) per CU: at most 128 VGPRs per lane.
 template <class C>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(4))) void q4k_prefill_ws_kernel(
     const uint8_t *__restrict__ w, const uint16_t *__restrict__ x, float *__restrict__ y, float *__restrict__ part,
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(4)
   addr::tile_of(tile, m_tiles, n_tiles, mt, nt);
   const int n0 = nt * BN, m0 = mt * BM;
 
-  if (wave >= 4) {
+  if (wave >= C::kWaves) {
     const int pt = tid - kThreads;
     const int nblk = K >> 8;
     const uint8_t *w_rowp = w + addr::prefill_w_row(n0, N, K, s_begin, pt, C::kWThreadsPerRow);
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(256) void q4k_prefill_reduce_kernel(const float *__
   if (gcol + 3 < N) yr[gcol + 3] = acc.w;
 }
 
-using PrefillCfg = Cfg<layout::kPrefillTileM, layout::kPrefillTileN, 4>;
+using PrefillCfg = Cfg<layout::kPrefillTileM, layout::kPrefillTileN, 2>;
 
 }  // namespace
 

@@ -384,7 +384,7 @@ QMV_HDI P iq4_moe_dn_unit_at(P row, int e, size_t expert_bytes, int lb) {
 
 // ---- prefill GEMM ------------------------------------------------------------------
 
-constexpr int kPrefillBK = 64, kPrefillHalf = 256;
+constexpr int kPrefillBK = 64, kPrefillHalf = 512;
 
 // Tile t of an m_tiles x n_tiles grid as (mt, nt). When the M tiles divide 8,
 // tile t goes where block t of a one-tile-per-block launch runs -- workgroups
@@ -416,7 +416,7 @@ QMV_HDI PrefillWork prefill_work(int blk, int K, int t_main, int r_tiles, int sp
   }
   return w;
 }
-// Producer thread pt (0..255) of a tile with first W row n0: block 0 of its
+// Producer thread pt (0 .. kPrefillHalf - 1) of a tile with first W row n0: block 0 of its
 // work's K range in its W row (rows past N read row 0).
 QMV_HDI size_t prefill_w_row(int n0, int N, int K, int s_begin, int pt, int threads_per_row) {
   const int nblk = K >> 8, w_row = pt / threads_per_row;

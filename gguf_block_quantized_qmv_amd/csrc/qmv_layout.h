@@ -139,12 +139,12 @@ constexpr bool group_fits_lds(int hidden, int ffn) {
 
 // ---- prefill GEMM: tiles and the K split of the last round -----------------
 
-// 128 x 128 output tiles, one 512-thread workgroup each. The plan assumes the
-// workgroup slots of a 256-CU MI355X at two workgroups per CU; it is a fixed
+// 256 x 128 output tiles, one 1024-thread workgroup each. The plan assumes the
+// workgroup slots of a 256-CU MI355X at one workgroup per CU; it is a fixed
 // constant, not a device query, so the summation order -- and so the bits --
 // depends only on (m, n, k).
-constexpr int kPrefillTileM = 128, kPrefillTileN = 128;
-constexpr int kPrefillSlots = 512;
+constexpr int kPrefillTileM = 256, kPrefillTileN = 128;
+constexpr int kPrefillSlots = 256;
 
 // Tiles [0, t_main) run whole. The r_tiles tiles after them (when the tile
 // count is not a multiple of the slots) run as `splits` parts of whole

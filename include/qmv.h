@@ -330,10 +330,11 @@ int qmv_iq4_xs_moe(const void *w_gate, const void *w_up, const void *w_down, siz
 /*
  * Workspace bytes qmm_q4_k_prefill needs for an m x n x k product (0 if none,
  * or if an argument is out of range). It depends on the shape alone. The
- * 128 x 128 output tiles run on 512 workgroup slots (a 256-CU MI355X at two
- * workgroups per CU); when the tile count is not a multiple of 512, the tiles
- * past the last multiple run as parts of whole 256-value K blocks so that the
- * last round fills the slots, and this many bytes hold the parts' fp32 sums.
+ * 256 x 128 output tiles (rows of X x rows of W) run on 256 workgroup slots
+ * (a 256-CU MI355X at one workgroup per CU); when the tile count is not a
+ * multiple of 256, the tiles past the last multiple run as parts of whole
+ * 256-value K blocks so that the last round fills the slots, and this many
+ * bytes hold the parts' fp32 sums.
  * (A caller-owned workspace is this library's own convention: the pages
  * describe no kernel interface.)
  */

@@ -289,7 +289,7 @@ void prefill_case(int m, int n, int k) {
   const int BM = layout::kPrefillTileM, BN = layout::kPrefillTileN;
   const int m_tiles = (m + BM - 1) / BM, n_tiles = (n + BN - 1) / BN, tiles = m_tiles * n_tiles;
   const int blocks = p.t_main + p.r_tiles * p.splits;
-  const int nblk = k >> 8, gpr = k >> 3, kDepth = 4, tpr = addr::kPrefillHalf / BN, x_per_thread = BM * 8 / 256;
+  const int nblk = k >> 8, gpr = k >> 3, kDepth = 4, tpr = addr::kPrefillHalf / BN, x_per_thread = BM * 8 / addr::kPrefillHalf;
   const size_t row_bytes = (size_t)nblk * addr::kQ4KBytes, total = (size_t)n * row_bytes;
   const size_t x_total = (size_t)m * gpr;
   char what[160];

@@ -218,11 +218,11 @@ void prefill() {
     int m, n, k;
     size_t ws;
   } cases[] = {
-      {512, 17408, 5120, (size_t)10 * 32 * 128 * 128 * 4},   // 544 tiles: 32 split in 10 parts of 2 K blocks
-      {512, 5120, 17408, (size_t)3 * 160 * 128 * 128 * 4},   // 160 tiles in 3 parts of 23 K blocks
-      {256, 32768, 5120, 0},                                   // 512 whole tiles
+      {512, 17408, 5120, (size_t)10 * 16 * 256 * 128 * 4},   // 272 tiles: 16 split in 10 parts of 2 K blocks
+      {512, 5120, 17408, (size_t)3 * 80 * 256 * 128 * 4},    // 80 tiles in 3 parts of 23 K blocks
+      {256, 32768, 5120, 0},                                   // 256 whole tiles
       {1, 16, 256, 0},                                         // one K block cannot split
-      {64, 128, 1024, (size_t)4 * 128 * 128 * 4},            // one tile in 4 parts
+      {64, 128, 1024, (size_t)4 * 256 * 128 * 4},            // one tile in 4 parts
   };
   for (const Case &c : cases) {
     EXPECT(qmm_q4_k_prefill_workspace(c.m, c.n, c.k) == c.ws);

@@ -215,23 +215,23 @@ def test_prefill_validation():
     assert f(V(W), nb, V(X), V(X + 16), 8, 4, 512, None, 0, None) == ALIAS
     assert f(V(W), nb, V(X), V(Y), 8, 4, 512, V(WS + 128), 1 << 20, None) == ALIGN   # workspace alignment
     assert f(V(W), nb, V(X), V(Y), 8, 4, 512, V(X), 1 << 20, None) == ALIAS          # workspace over an input
-    # the K-split plan is a function of the shape alone (512 workgroup slots, 128 x 128
+    # the K-split plan is a function of the shape alone (256 workgroup slots, 256 x 128
     # tiles, parts of whole 256-value K blocks), here derived by hand:
-    #  512 x 17408 x 5120: 4 x 136 = 544 tiles = 512 whole + 32 split; 20 K blocks, at most
-    #    512 / 32 = 16 parts -> parts of ceil(20 / 16) = 2 blocks -> 10 parts: 10 * 32 * 64 KiB
-    #  512 x 5120 x 17408: 4 x 40 = 160 tiles, all split; 68 K blocks, at most 512 / 160 = 3
-    #    parts -> parts of ceil(68 / 3) = 23 blocks -> 3 parts: 3 * 160 * 64 KiB
-    #  256 x 32768 x 5120: exactly 512 tiles, none split; 1 x 16 x 256: one K block, no split
-    assert L.qmm_q4_k_prefill_workspace(512, 17408, 5120) == 10 * 32 * 128 * 128 * 4
-    assert L.qmm_q4_k_prefill_workspace(512, 5120, 17408) == 3 * 160 * 128 * 128 * 4
+    #  512 x 17408 x 5120: 2 x 136 = 272 tiles = 256 whole + 16 split; 20 K blocks, at most
+    #    256 / 16 = 16 parts -> parts of ceil(20 / 16) = 2 blocks -> 10 parts: 10 * 16 * 128 KiB
+    #  512 x 5120 x 17408: 2 x 40 = 80 tiles, all split; 68 K blocks, at most 256 / 80 = 3
+    #    parts -> parts of ceil(68 / 3) = 23 blocks -> 3 parts: 3 * 80 * 128 KiB
+    #  256 x 32768 x 5120: exactly 256 tiles, none split; 1 x 16 x 256: one K block, no split
+    assert L.qmm_q4_k_prefill_workspace(512, 17408, 5120) == 10 * 16 * 256 * 128 * 4
+    assert L.qmm_q4_k_prefill_workspace(512, 5120, 17408) == 3 * 80 * 256 * 128 * 4
     assert L.qmm_q4_k_prefill_workspace(256, 32768, 5120) == 0
     assert L.qmm_q4_k_prefill_workspace(1, 16, 256) == 0
-    assert L.qmm_q4_k_prefill_workspace(64, 128, 1024) == 4 * 1 * 128 * 128 * 4   # 1 tile in 4 parts of 1 block
+    assert L.qmm_q4_k_prefill_workspace(64, 128, 1024) == 4 * 1 * 256 * 128 * 4   # 1 tile in 4 parts of 1 block
     assert L.qmm_q4_k_prefill_workspace(0, 16, 256) == 0 and L.qmm_q4_k_prefill_workspace(1, 16, 100) == 0
     # a shape whose plan splits is refused without its workspace, or with too little
     nbp = q.q4_k_bytes(128, 1024)
     assert f(V(W), nbp, V(X), V(Y), 64, 128, 1024, None, 0, None) == WORKSPACE
-    assert f(V(W), nbp, V(X), V(Y), 64, 128, 1024, V(WS), 4 * 65536 - 1, None) == WORKSPACE
+    assert f(V(W), nbp, V(X), V(Y), 64, 128, 1024, V(WS), 4 * 131072 - 1, None) == WORKSPACE
     # the 32-bit activation granule index: m * k / 8 must stay below 2^32 (and the tiles fit an int)
     big_k = 1 << 20
     nbk = q.q4_k_bytes(4, big_k)

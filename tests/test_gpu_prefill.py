@@ -35,9 +35,9 @@ def dev():
 @pytest.mark.parametrize("m,n,k", [(64, 128, 1024), (100, 200, 768), (1, 16, 256), (257, 129, 2048), (128, 384, 5120),
                                    (40, 64, 17408), (256, 32768, 256)])
 def test_prefill_parity(q, dev, m, n, k):
-    # tile counts that are not a multiple of the 512 workgroup slots split their
+    # tile counts that are not a multiple of the 256 workgroup slots split their
     # last tiles along K (here every tile: fewer tiles than slots; one tile of
-    # 17408 K in many parts; ragged tiles); 256 x 32768 is exactly 512 whole
+    # 17408 K in many parts; ragged tiles); 256 x 32768 is exactly 256 whole
     # tiles, and a single 256-value K block cannot split
     raw = synth.q4_k_weights(m + n, n, k)
     x = synth.bf16_normal(k + m, (m, k))
