@@ -19,8 +19,10 @@
  *    buffer; the library never allocates, frees or synchronises. Its only
  *    process state never affects a result: per kernel and device, the largest
  *    dynamic-LDS size already granted (an atomic, so the attribute is set once),
- *    and per host thread the text behind qmv_last_error(). Calls from several
- *    host threads are safe.
+ *    per host thread the text behind qmv_last_error(), and for
+ *    qmv_q4_k_moe_noalloc its fixed device array (part of the library's code
+ *    object) and that array's address per device. Calls from several host
+ *    threads are safe, except overlapping qmv_q4_k_moe_noalloc calls on one GPU.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
  *    work is enqueued on it asynchronously; a return of QMV_OK means the work
  *    was enqueued, not that it finished.
