@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "QmvError", "lib", "LIB_PATH", "version",
-    "qmv_q8_0", "qmv_q4_k", "qmv_iq4_xs", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmv_q4_k_moe_prefill",
+    "qmv_q8_0", "qmv_q4_k", "qmv_q4_k_pair", "qmv_iq4_xs", "qmv_q4_k_moe", "qmv_q4_k_moe_workspace", "qmv_q4_k_moe_prefill",
     "qmv_q4_k_moe_noalloc",
     "qmv_q4_k_moe_prefill_workspace", "qmv_iq4_xs_moe",
     "qmv_iq4_xs_moe_workspace", "qmm_q4_k_prefill_workspace",
@@ -36,6 +36,7 @@ EXPORTS = {
     "qmv_last_error": (ctypes.c_char_p, []),
     "qmv_q8_0": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "qmv_q4_k": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
+    "qmv_q4_k_pair": (_c_int, [_vp, _vp, _c_size, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "qmv_iq4_xs": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "qmv_q5_k": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "qmv_q6_k": (_c_int, [_vp, _c_size, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
@@ -187,6 +188,26 @@ def qmv_q4_k(w, x, n: int, k: int, y=None, stream=None):
     _dev(y, "y", (torch.float32,))
     _check(lib.qmv_q4_k(_ptr(w), _nbytes(w), _ptr(x), _ptr(y), m, n, k, _stream(stream)), "qmv_q4_k")
     return y
+
+
+def qmv_q4_k_pair(w0, w1, x, n: int, k: int, y0=None, y1=None, stream=None):
+    """(x @ dequant(w0)^T, x @ dequant(w1)^T) for two Q4_K matrices of one shape, in one launch."""
+    torch = _torch()
+    _dev(w0, "w0", (torch.uint8,))
+    _dev(w1, "w1", (torch.uint8,))
+    _dev(x, "x", _bf16_types())
+    if _nbytes(w0) != _nbytes(w1):
+        raise ValueError("qmv_q4_k_pair: w0 and w1 must have the same size")
+    m = x.shape[0] if x.dim() == 2 else 1
+    if y0 is None:
+        y0 = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    if y1 is None:
+        y1 = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(y0, "y0", (torch.float32,))
+    _dev(y1, "y1", (torch.float32,))
+    _check(lib.qmv_q4_k_pair(_ptr(w0), _ptr(w1), _nbytes(w0), _ptr(x), _ptr(y0), _ptr(y1), m, n, k, _stream(stream)),
+           "qmv_q4_k_pair")
+    return y0, y1
 
 
 def qmv_q4_k_moe_workspace(t: int, hidden: int, ffn: int, n_experts: int, top_k: int) -> int:

@@ -355,9 +355,13 @@ constexpr int kMaxThreadsRows = addr::dense_max_threads(2);   // M = 2..4: regis
 template <int M, int G>
 constexpr int x_head() { return (G == 16 ? 4 * M : 9 * M) < 9 ? (G == 16 ? 4 * M : 9 * M) : 9; }
 
-template <int M, int G, int D, bool FULL, int NS, int F>
+// PAIR: w and w1 are two matrices of n rows on the same activations, the grid
+// covers 2n rows (addr::pair_row), and matrix 1's rows go to y1; each row runs
+// exactly the instruction sequence of the one-matrix launch.
+template <int M, int G, int D, bool FULL, int NS, int F, bool PAIR = false>
 __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const uint16_t *__restrict__ x,
-                                          float *__restrict__ y, const int n, const int k) {
+                                          float *__restrict__ y, const int n, const int k,
+                                          const uint8_t *__restrict__ w1 = nullptr, float *__restrict__ y1 = nullptr) {
   constexpr int kBlocksPerStep = G / 4;
   constexpr int kStepGranules = (G / 2) * 17;   // padded LDS granules per step
   extern __shared__ uint4 lds[];
@@ -372,7 +376,12 @@ __device__ __forceinline__ void gemv_body(const uint8_t *__restrict__ w, const u
   const int j = lane & (G - 1);
   // blockDim.x = (rows per workgroup) * G; the last wave may be partial
   const int nthreads = (int)blockDim.x;
-  const int row = addr::lane_row(blockIdx.x, threadIdx.x, nthreads, G);
+  int row = addr::lane_row(blockIdx.x, threadIdx.x, nthreads, G);
+  if constexpr (PAIR) {
+    const addr::PairRow pr = addr::pair_row(row, n);
+    row = pr.row;
+    if (pr.half) w = w1, y = y1;
+  }
   // loads with no block of their own (past the row, past the matrix, past a
   // partial last step) read the last block of the lane's row (of the last row
   // when the row is past the matrix), which the same or a recent load also reads
@@ -464,6 +473,13 @@ __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q4k_ge
 }
 
 template <int M, int G, int D, bool FULL, int NS>
+__global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q4k_gemv_pair_kernel(
+    const uint8_t *__restrict__ w0, const uint8_t *__restrict__ w1, const uint16_t *__restrict__ x,
+    float *__restrict__ y0, float *__restrict__ y1, const int n, const int k) {
+  gemv_body<M, G, D, FULL, NS, kFmtQ4K, true>(w0, x, y0, n, k, w1, y1);
+}
+
+template <int M, int G, int D, bool FULL, int NS>
 __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q40_gemv_kernel(const uint8_t *__restrict__ w,
                                                             const uint16_t *__restrict__ x,
                                                             float *__restrict__ y, const int n, const int k) {
@@ -482,10 +498,20 @@ __global__ __launch_bounds__(M == 1 ? kMaxThreads : kMaxThreadsRows) void q5k_ge
 // (10 rows of 32 lanes for N = 5120 at M = 1, 20 rows at M = 2..4 where the
 // activations fill the LDS). Each instantiation below is the one the plan
 // names: G and NS by the switch, D = addr::dense_depth(F, M, G).
-template <int M, int G, bool FULL, int NS, int F>
-int launch_cfg(const addr::GemvPlan &p, const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
+template <int M, int G, bool FULL, int NS, int F, bool PAIR = false>
+int launch_cfg(const addr::GemvPlan &p, const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream,
+               const void *w1 = nullptr, float *y1 = nullptr) {
   constexpr int D = addr::dense_depth(F, M, G);
   const size_t lds = dense_lds_bytes<M>(k);
+  if constexpr (PAIR) {
+    static_assert(F == kFmtQ4K, "the pair form is built for Q4_K");
+    static LdsGrant granted_pair;
+    if (allow_dynamic_lds(reinterpret_cast<const void *>(&q4k_gemv_pair_kernel<M, G, D, FULL, NS>), lds, granted_pair,
+                          "q4k_gemv_pair_kernel"))
+      return QMV_ERR_HIP;
+    return launch_kernel("q4k_gemv_pair_kernel", q4k_gemv_pair_kernel<M, G, D, FULL, NS>, dim3(p.grid),
+                         dim3(p.rows * G), lds, stream, w, w1, x, y, y1, n, k);
+  }
   // only the launched format's kernel is instantiated
   void (*fn)(const uint8_t *, const uint16_t *, float *, int, int);
   const char *name;
@@ -497,30 +523,33 @@ int launch_cfg(const addr::GemvPlan &p, const void *w, const uint16_t *x, float 
   return launch_kernel(name, fn, dim3(p.grid), dim3(p.rows * G), lds, stream, w, x, y, n, k);
 }
 
-template <int M, int F>
-int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream) {
-  const addr::GemvPlan p = addr::dense_gemv_plan(F, M, n, k);
+// PAIR: w1 and y1 are the second matrix and its output; the plan covers 2n
+// rows (the same G, NS and D as one matrix: they depend on k and M only).
+template <int M, int F, bool PAIR = false>
+int launch_m(const void *w, const uint16_t *x, float *y, int n, int k, hipStream_t stream, const void *w1 = nullptr,
+             float *y1 = nullptr) {
+  const addr::GemvPlan p = addr::dense_gemv_plan(F, M, PAIR ? 2 * n : n, k);
   if (p.G == 16) {
     switch (p.ns) {
-      case 1: return launch_cfg<M, 16, false, 1, F>(p, w, x, y, n, k, stream);
-      case 2: return launch_cfg<M, 16, false, 2, F>(p, w, x, y, n, k, stream);
-      case 3: return launch_cfg<M, 16, false, 3, F>(p, w, x, y, n, k, stream);
-      case 4: return launch_cfg<M, 16, false, 4, F>(p, w, x, y, n, k, stream);
-      case 5: return launch_cfg<M, 16, false, 5, F>(p, w, x, y, n, k, stream);
-      case 6: return launch_cfg<M, 16, false, 6, F>(p, w, x, y, n, k, stream);
-      case 7: return launch_cfg<M, 16, false, 7, F>(p, w, x, y, n, k, stream);
-      default: return launch_cfg<M, 16, false, 8, F>(p, w, x, y, n, k, stream);
+      case 1: return launch_cfg<M, 16, false, 1, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
+      case 2: return launch_cfg<M, 16, false, 2, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
+      case 3: return launch_cfg<M, 16, false, 3, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
+      case 4: return launch_cfg<M, 16, false, 4, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
+      case 5: return launch_cfg<M, 16, false, 5, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
+      case 6: return launch_cfg<M, 16, false, 6, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
+      case 7: return launch_cfg<M, 16, false, 7, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
+      default: return launch_cfg<M, 16, false, 8, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
     }
   }
   switch (p.ns) {
-    case 5: return launch_cfg<M, 32, false, 5, F>(p, w, x, y, n, k, stream);
-    case 6: return launch_cfg<M, 32, false, 6, F>(p, w, x, y, n, k, stream);
-    case 7: return launch_cfg<M, 32, false, 7, F>(p, w, x, y, n, k, stream);
-    case 8: return launch_cfg<M, 32, false, 8, F>(p, w, x, y, n, k, stream);
-    case 9: return launch_cfg<M, 32, false, 9, F>(p, w, x, y, n, k, stream);
+    case 5: return launch_cfg<M, 32, false, 5, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
+    case 6: return launch_cfg<M, 32, false, 6, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
+    case 7: return launch_cfg<M, 32, false, 7, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
+    case 8: return launch_cfg<M, 32, false, 8, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
+    case 9: return launch_cfg<M, 32, false, 9, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
     default:
-      return p.full ? launch_cfg<M, 32, true, 0, F>(p, w, x, y, n, k, stream)
-                    : launch_cfg<M, 32, false, 0, F>(p, w, x, y, n, k, stream);
+      return p.full ? launch_cfg<M, 32, true, 0, F, PAIR>(p, w, x, y, n, k, stream, w1, y1)
+                    : launch_cfg<M, 32, false, 0, F, PAIR>(p, w, x, y, n, k, stream, w1, y1);
   }
 }
 
@@ -533,6 +562,18 @@ int launch_q4_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, i
     case 2: return launch_m<2, kFmtQ4K>(w, x, y, n, k, s);
     case 3: return launch_m<3, kFmtQ4K>(w, x, y, n, k, s);
     case 4: return launch_m<4, kFmtQ4K>(w, x, y, n, k, s);
+    default: return QMV_ERR_RANGE;
+  }
+}
+
+int launch_q4_k_gemv_pair(const void *w0, const void *w1, const uint16_t *x, float *y0, float *y1, int m, int n, int k,
+                          void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (m) {
+    case 1: return launch_m<1, kFmtQ4K, true>(w0, x, y0, n, k, s, w1, y1);
+    case 2: return launch_m<2, kFmtQ4K, true>(w0, x, y0, n, k, s, w1, y1);
+    case 3: return launch_m<3, kFmtQ4K, true>(w0, x, y0, n, k, s, w1, y1);
+    case 4: return launch_m<4, kFmtQ4K, true>(w0, x, y0, n, k, s, w1, y1);
     default: return QMV_ERR_RANGE;
   }
 }

@@ -100,6 +100,14 @@ inline GemvPlan dense_gemv_plan(int fmt, int m, int n, int k) {
 // Output row of thread tid of workgroup bid (nthreads per workgroup).
 QMV_HDI int lane_row(int bid, int tid, int nthreads, int G) { return bid * (nthreads / G) + tid / G; }
 
+// Two matrices of n rows on one activation (qmv_q4_k_pair): the launch covers
+// 2n rows, rows [0, n) of matrix 0 then [n, 2n) of matrix 1; each is row `row`
+// of its own matrix (rows past 2n are past matrix 1, inactive in dense_lane).
+struct PairRow {
+  int half, row;
+};
+QMV_HDI PairRow pair_row(int row2, int n) { return row2 < n ? PairRow{0, row2} : PairRow{1, row2 - n}; }
+
 struct DenseLane {
   int c, jb, nsteps;
   bool active, last_ok;

@@ -189,6 +189,26 @@ int qmv_q4_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, in
   return qmv::launch_q4_k_gemv(w, x_bf16, y, m, n, k, stream);
 }
 
+int qmv_q4_k_pair(const void *w0, const void *w1, size_t w_bytes, const uint16_t *x_bf16, float *y0, float *y1, int m,
+                  int n, int k, void *stream) {
+  if (!w0 || !w1 || !x_bf16 || !y0 || !y1) return QMV_ERR_NULL;
+  if (m < 1 || m > QMV_MAX_ROWS) return QMV_ERR_RANGE;
+  int rc = check_matrix(w0, w_bytes, n, k, 256, 144, 16);
+  if (rc) return rc;
+  rc = check_matrix(w1, w_bytes, n, k, 256, 144, 16);
+  if (rc) return rc;
+  if (n > QMV_MAX_MATRIX_ROWS / 2 || !qmv::layout::matrix_in_range(2 * n, k)) return QMV_ERR_RANGE;   // one grid of 2n rows
+  if (qmv::layout::q4k_x_lds(m, k) > qmv::layout::kLdsBudget) return QMV_ERR_RANGE;
+  if (!aligned(x_bf16, 16) || !aligned(y0, 4) || !aligned(y1, 4)) return QMV_ERR_ALIGN;
+  const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 4;
+  const float *outs[2] = {y0, y1};
+  for (const float *yo : outs)
+    if (overlap(yo, yb, w0, w_bytes) || overlap(yo, yb, w1, w_bytes) || overlap(yo, yb, x_bf16, xb))
+      return QMV_ERR_ALIAS;
+  if (overlap(y0, yb, y1, yb)) return QMV_ERR_ALIAS;
+  return qmv::launch_q4_k_gemv_pair(w0, w1, x_bf16, y0, y1, m, n, k, stream);
+}
+
 int qmv_iq4_xs(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y, int m, int n, int k, void *stream) {
   if (!w || !x_bf16 || !y) return QMV_ERR_NULL;
   if (m < 1 || m > QMV_MAX_ROWS) return QMV_ERR_RANGE;

@@ -13,6 +13,8 @@ void set_error_detail(const char *what, int hip_code, const char *hip_text);
 
 int launch_q8_0_gemv(const void *w, const float *x, float *y, int m, int n, int k, void *stream);
 int launch_q4_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
+int launch_q4_k_gemv_pair(const void *w0, const void *w1, const uint16_t *x, float *y0, float *y1, int m, int n, int k,
+                          void *stream);
 int launch_q5_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
 int launch_q6_k_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);
 int launch_q4_0_gemv(const void *w, const uint16_t *x, float *y, int m, int n, int k, void *stream);

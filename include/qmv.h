@@ -131,6 +131,24 @@ int qmv_q4_k(const void *w, size_t w_bytes, const uint16_t *x_bf16, float *y,
              int m, int n, int k, void *stream);
 
 /*
+ * Two Q4_K matrices of the same shape times the same bf16 activation rows, in
+ * one launch: y0 = W0 x and y1 = W1 x, as two qmv_q4_k calls would give them,
+ * bit for bit (every row runs the same instructions). A decode step multiplies
+ * the FFN's gate and up matrices by the same activation, and one launch over
+ * both rows pays the launch's fixed start and drain once.
+ *   w0, w1  two [n rows][k/256 blocks] Q4_K matrices, 16-byte aligned, each of
+ *           w_bytes == n*(k/256)*144 bytes
+ *   x_bf16  bf16 bits [m][k] row-major, 16-byte aligned
+ *   y0, y1  fp32 [m][n] row-major each, 4-byte aligned, overlapping no input
+ *           and not each other
+ *   the limits of qmv_q4_k, and 2n rows within QMV_MAX_MATRIX_ROWS.
+ * Workload: the gate and up products of the memra README's dense Q4_K_M models
+ * at plain decode, and of the memra-bench card's K-draft verify.
+ */
+int qmv_q4_k_pair(const void *w0, const void *w1, size_t w_bytes, const uint16_t *x_bf16,
+                  float *y0, float *y1, int m, int n, int k, void *stream);
+
+/*
  * Q5_K matrix times bf16 activation rows (m = 1..4): the K-quant sibling that
  * Q4_K_M files mix in (memra README model support table; the memra-bench card
  * flags a Q5_K expert mix). 176-byte blocks: the Q4_K header, 32 bytes whose

@@ -117,6 +117,33 @@ void dense_case(int fmt, int m, int n, int k) {
   }
 }
 
+// Two matrices on one activation (qmv_q4_k_pair): one grid over 2n rows, each
+// lane reading its own matrix (addr::pair_row); both matrices are `total` bytes.
+void pair_case(int m, int n, int k) {
+  const int fmt = addr::kFmtQ4K;
+  const addr::GemvPlan p = addr::dense_gemv_plan(fmt, m, 2 * n, k);
+  const int nblk = k >> 8, bb = addr::dense_block_bytes(fmt);
+  const size_t total = (size_t)n * nblk * bb, row_bytes = (size_t)nblk * bb;
+  const int threads = p.rows * p.G;
+  char what[160];
+  std::snprintf(what, sizeof what, "pair m %d n %d k %d (G %d NS %d D %d rows %d)", m, n, k, p.G, p.ns, p.depth,
+                p.rows);
+  if ((size_t)p.grid * p.rows < 2 * (size_t)n) fail(std::string(what) + ": grid does not cover the rows");
+  for (unsigned bid : groups_of(p.grid)) {
+    for (int tid = 0; tid < threads; ++tid) {
+      const int j = (tid & 63) & (p.G - 1);
+      const addr::PairRow pr = addr::pair_row(addr::lane_row((int)bid, tid, threads, p.G), n);
+      const addr::DenseLane l = addr::dense_lane(p.G, p.ns, fmt, n, nblk, pr.row, j);
+      for (int t : ring_steps(p.ns, l.nsteps, p.depth)) {
+        const bool ok = addr::dense_step_ok(l.active, l.last_ok, l.nsteps, l.jb, p.ns, p.full, p.G, nblk, t);
+        const size_t b = ok ? l.row_base + l.blk_off + addr::dense_step_offset(p.G, fmt, t) : l.fb;
+        const size_t lo = ok ? (size_t)pr.row * row_bytes : 0, hi = ok ? lo + row_bytes : 0;
+        for (int i = 0; i < 2; ++i) check(what, b, addr::dense_window(fmt, l.c, i), total, lo, hi);
+      }
+    }
+  }
+}
+
 // ---- Q6_K GEMV --------------------------------------------------------------
 
 void q6_case(int m, int n, int k) {
@@ -448,6 +475,11 @@ int main(int argc, char **argv) {
         for (int n : ns_) dense_case(fmt, m, n, k);
       }
   lap("dense GEMV");
+  for (int m = 1; m <= 4; ++m)
+    for (int k : {256, 1024, 5120, 8448, 17408, 18432, 20480})
+      if (layout::q4k_x_lds(m, k) <= layout::kLdsBudget)
+        for (int n : {1, 3, 255, 256, 2560, 17408}) pair_case(m, n, k);
+  lap("Q4_K pair GEMV");
   for (int m = 1; m <= 4; ++m)
     for (int k : ks) {
       if (layout::q6k_x_lds(m, k) > layout::kLdsBudget) continue;

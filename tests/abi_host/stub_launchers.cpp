@@ -29,6 +29,9 @@ static int note(int m, int n, int k, const void *ws = nullptr) {
 
 int launch_q8_0_gemv(const void *, const float *, float *, int m, int n, int k, void *) { return note(m, n, k); }
 int launch_q4_k_gemv(const void *, const uint16_t *, float *, int m, int n, int k, void *) { return note(m, n, k); }
+int launch_q4_k_gemv_pair(const void *, const void *, const uint16_t *, float *, float *, int m, int n, int k, void *) {
+  return note(m, n, k);
+}
 int launch_q5_k_gemv(const void *, const uint16_t *, float *, int m, int n, int k, void *) { return note(m, n, k); }
 int launch_q6_k_gemv(const void *, const uint16_t *, float *, int m, int n, int k, void *) { return note(m, n, k); }
 int launch_q4_0_gemv(const void *, const uint16_t *, float *, int m, int n, int k, void *) { return note(m, n, k); }

@@ -88,6 +88,37 @@ void dense_formats() {
   }
 }
 
+void pair() {
+  const uint16_t *xb = static_cast<const uint16_t *>(X);
+  const void *W1 = at(4);
+  float *Y1 = static_cast<float *>(at(5));
+  for (int m = 1; m <= 4; ++m) {
+    const int before = stub::launches;
+    EXPECT(qmv_q4_k_pair(W, W1, mbytes(3, 512, 256, 144), xb, Y, Y1, m, 3, 512, nullptr) == QMV_OK);
+    EXPECT(stub::launches == before + 1 && stub::last_m == m && stub::last_n == 3 && stub::last_k == 512);
+  }
+  const size_t full = mbytes(2, 512, 256, 144);
+  for (size_t b = 0; b < full + 288; ++b)
+    if (b != full) EXPECT(qmv_q4_k_pair(W, W1, b, xb, Y, Y1, 1, 2, 512, nullptr) == QMV_ERR_SIZE);
+  EXPECT(qmv_q4_k_pair(W, nullptr, full, xb, Y, Y1, 1, 2, 512, nullptr) == QMV_ERR_NULL);
+  EXPECT(qmv_q4_k_pair(W, W1, full, xb, Y, nullptr, 1, 2, 512, nullptr) == QMV_ERR_NULL);
+  EXPECT(qmv_q4_k_pair(W, W1, full, xb, Y, static_cast<float *>(at(4, 64)), 1, 2, 512, nullptr) == QMV_ERR_ALIAS);
+  EXPECT(qmv_q4_k_pair(W, W1, full, xb, Y, Y + 1, 1, 2, 512, nullptr) == QMV_ERR_ALIAS);
+  EXPECT(qmv_q4_k_pair(W, W1, full, xb, Y, Y + 2, 1, 2, 512, nullptr) == QMV_OK);
+  EXPECT(qmv_q4_k_pair(W, W1, full, xb, Y, Y, 1, 2, 512, nullptr) == QMV_ERR_ALIAS);
+  // one grid covers 2n rows: n may be at most half the one-matrix row limit
+  for (int m : kInts)
+    for (int nn : kInts)
+      for (int kk : kInts) {
+        const size_t wb = mbytes(nn, kk, 256, 144);
+        const int before = stub::launches;
+        const int rc = qmv_q4_k_pair(W, W1, wb ? wb : 1, xb, Y, Y1, m, nn, kk, nullptr);
+        EXPECT(is_code(rc));
+        EXPECT((rc == QMV_OK) == (stub::launches == before + 1));
+        if (rc == QMV_OK) EXPECT(m >= 1 && m <= 4 && nn >= 1 && nn <= QMV_MAX_MATRIX_ROWS / 2 && kk % 256 == 0);
+      }
+}
+
 void q8_0() {
   const float *xf = static_cast<const float *>(X);
   EXPECT(qmv_q8_0(W, mbytes(4, 64, 32, 34), xf, Y, 1, 4, 64, nullptr) == QMV_OK);
@@ -275,6 +306,7 @@ int main() {
   for (int c = -20; c <= 20; ++c) EXPECT(qmv_strerror(c) != nullptr && qmv_strerror(c)[0] != '\0');
   EXPECT(qmv_last_error() != nullptr);
   dense_formats();
+  pair();
   q8_0();
   dequant();
   moe(qmv_q4_k_moe, qmv_q4_k_moe_workspace, 144);

@@ -39,7 +39,7 @@ def test_header_lists_the_expected_entry_points():
         "qmv_q5_k", "qmv_dequant_q5_k_f32", "qmv_q6_k", "qmv_dequant_q6_k_f32", "qmv_q4_0",
         "qmv_dequant_q4_0_f32",
         "qmm_q4_k_prefill_workspace", "qmm_q4_k_prefill", "qmv_dequant_q4_k_f32", "qmv_dequant_q4_k_bf16",
-        "qmv_dequant_q8_0_f32", "qmv_stream_read", "qmv_q4_k_moe_noalloc"])
+        "qmv_dequant_q8_0_f32", "qmv_stream_read", "qmv_q4_k_moe_noalloc", "qmv_q4_k_pair"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -82,6 +82,33 @@ def test_q4_k_every_truncated_or_padded_size_is_an_error():
         assert q4k(nbytes=b, n=n, k=k) == SIZE, b
     assert q4k(nbytes=full + 1, n=n, k=k) == SIZE
     assert q4k(nbytes=2 * full, n=n, k=k) == SIZE
+
+
+W1 = W + (1 << 30)   # the second matrix of a pair
+Y1 = Y + (1 << 30)
+
+
+def q4kp(w0=W, w1=W1, nbytes=None, x=X, y0=Y, y1=Y1, m=1, n=2, k=256):
+    nbytes = q.q4_k_bytes(n, k) if nbytes is None else nbytes
+    return L.qmv_q4_k_pair(V(w0), V(w1), nbytes, V(x), V(y0), V(y1), m, n, k, None)
+
+
+def test_q4_k_pair_validation():
+    assert q4kp(w0=0) == NULL and q4kp(w1=0) == NULL and q4kp(x=0) == NULL and q4kp(y0=0) == NULL
+    assert q4kp(y1=0) == NULL
+    assert q4kp(m=0) == RANGE and q4kp(m=5) == RANGE
+    assert q4kp(n=0) == SHAPE and q4kp(k=0) == SHAPE and q4kp(k=255) == SHAPE and q4kp(k=384) == SHAPE
+    assert q4kp(w0=W + 8) == ALIGN and q4kp(w1=W1 + 8) == ALIGN and q4kp(x=X + 2) == ALIGN
+    assert q4kp(y0=Y + 2) == ALIGN and q4kp(y1=Y1 + 2) == ALIGN
+    assert q4kp(m=4, k=19456) == RANGE                  # activations exceed the LDS stage
+    assert q4kp(y0=W + 64) == ALIAS and q4kp(y1=W1 + 64) == ALIAS and q4kp(y1=W + 64) == ALIAS
+    assert q4kp(y0=X, x=X) == ALIAS and q4kp(y1=X + 4, x=X) == ALIAS
+    assert q4kp(y1=Y + 4) == ALIAS                      # the outputs overlap each other
+    full = q.q4_k_bytes(2, 512)
+    for b in (0, full - 1, full + 1, 2 * full):
+        assert q4kp(nbytes=b, k=512) == SIZE, b
+    # one grid covers 2n rows: each matrix may have at most half the row limit
+    assert q4kp(n=(1 << 29) + 1, k=256, nbytes=q.q4_k_bytes((1 << 29) + 1, 256)) == RANGE
 
 
 def q5k(w=W, nbytes=None, x=X, y=Y, m=1, n=2, k=256):
