@@ -5,12 +5,15 @@ Headline (the `value`): Q4_K GEMV at M=1 over the dense 27B-like FFN shapes --
 gate and up 17408x5120, down 5120x17408 -- cycling a pool of 128 independent
 layer copies (19.25 GB, far above the 256 MB Infinity Cache), reported as
 achieved GB/s of algorithmic bytes (weights + activations + outputs). One step
-is one pass over the whole pool (384 GEMVs).
+is one decode pass over the whole pool: per layer copy one qmv_q4_k_pair launch
+(gate and up on the same activation) and one qmv_q4_k launch (down), 256
+launches and 384 GEMVs. The same pass with one launch per matrix is reported
+beside it.
 
 Sections beside it (each can be left out with --skip or chosen with --only):
-  calib        plain streaming read of the same pool (the achievable read
-               ceiling) and a 4 GiB device copy
-  percall      each GEMV of one pass bracketed by its own HIP events
+  calib        plain streaming read of the same pool with the same launches
+               (the achievable read ceiling) and a 4 GiB device copy
+  percall      each launch of one pass bracketed by its own HIP events
   verify       the M = 1..4 speculative-verify curve
   q8           the 1024x1024 Q8_0 GEMV (cache-resident: a latency figure)
   moe          routed-expert MoE decode, T = 1 and 3 (tok-equiv/s, 48-bank pool)
@@ -47,12 +50,12 @@ SECTIONS = ("calib", "percall", "verify", "q8", "moe", "moe_prefill", "prefill",
 # and whitespace excluded) still hash to the value measured, else null.
 _CSRC = "gguf_block_quantized_qmv_amd/csrc/"
 MEASURED = {
-    # HBM bytes per q4k_gemv_kernel launch at M=1, mean over gate, up and down:
-    # FETCH_SIZE scaled by the streaming read of a known size, plus WRITE_SIZE
-    # scaled by a 4 GiB device copy (profiles/q4k_gemv_m1_hbm_traffic.md)
+    # HBM bytes per q4k_gemv_pair_kernel launch at M=1 (gate and up): FETCH_SIZE
+    # scaled by the streaming read of a known size, plus WRITE_SIZE scaled by a
+    # 4 GiB device copy (profiles/q4k_gemv_m1_hbm_traffic.md)
     "gemv_traffic": {"sources": (_CSRC + "q4k_gemv.hip", _CSRC + "q4k_common.h", _CSRC + "qmv_device.h",
                                  _CSRC + "qmv_layout.h", _CSRC + "qmv_addr.h"),
-                     "sha256": "b95e5885ec9315ee47b71aa38a0ab2a50764a57f8bf9d8a0b20222b0ebcbc07b", "value": 50839514},
+                     "sha256": "0154c8c8fdf23c29d73843692da4709a5547a68a46318d7c90aa8bd829e79ae2", "value": 101097390},
     # MFMA utilisation of the prefill GEMM at M=512 (profiles/q4k_prefill_m512_mfma.md)
     "prefill_mfma_util": {"sources": (_CSRC + "q4k_prefill.hip", _CSRC + "q4k_common.h", _CSRC + "qmv_device.h",
                                       _CSRC + "qmv_layout.h", _CSRC + "qmv_addr.h"),
@@ -157,46 +160,83 @@ def main():
     sp = stream_ptr(torch)
 
     # ------------------------------------------------------------ headline: the dense pool at M=1
+    # Each layer copy keeps gate and up in one allocation (gate then up), so the
+    # calibration can read both with one launch as the pair GEMV does; the bytes
+    # are the same per-matrix generator streams as separate allocations would get.
     log(f"[bench] generating the Q4_K pool: {args.copies} copies x gate/up/down")
-    pool = [[synth.torch_q4_k_weights(11, n, k, dev, stream=3 * c + i) for i, (_, n, k) in enumerate(SHAPES)]
-            for c in range(args.copies)]
-    x_dev = {k: torch.from_numpy(synth.bf16_normal(12, (4, k)).view(np.int16)).to(dev) for _, _, k in SHAPES}
-    y_dev = {n: torch.empty((4, n), dtype=torch.float32, device=dev) for _, n, _ in SHAPES}
-    torch.cuda.synchronize()
     wbytes = [q.q4_k_bytes(n, k) for _, n, k in SHAPES]
+    (_, n_gu, k_gu), (_, n_dn, k_dn) = SHAPES[0], SHAPES[2]
+    pool, pool_gu = [], []
+    for c in range(args.copies):
+        gu = torch.empty(2 * wbytes[0], dtype=torch.uint8, device=dev)
+        for i in (0, 1):
+            gu[i * wbytes[0]:(i + 1) * wbytes[0]].copy_(synth.torch_q4_k_weights(11, n_gu, k_gu, dev,
+                                                                                  stream=3 * c + i))
+        pool_gu.append(gu)
+        pool.append([gu[:wbytes[0]], gu[wbytes[0]:], synth.torch_q4_k_weights(11, n_dn, k_dn, dev, stream=3 * c + 2)])
+    x_dev = {k: torch.from_numpy(synth.bf16_normal(12, (4, k)).view(np.int16)).to(dev) for _, _, k in SHAPES}
+    y_dev = {name: torch.empty((4, n), dtype=torch.float32, device=dev) for name, n, _ in SHAPES}
+    torch.cuda.synchronize()
     pool_bytes = args.copies * sum(wbytes)
     gemv = checked(L.qmv_q4_k, "qmv_q4_k")
+    pair = checked(L.qmv_q4_k_pair, "qmv_q4_k_pair")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
 
-    def calls(m, st):
-        return [(ctypes.c_void_p(pool[c][i].data_ptr()), wbytes[i], ctypes.c_void_p(x_dev[k].data_ptr()),
-                 ctypes.c_void_p(y_dev[n].data_ptr()), m, n, k, st)
-                for c in range(args.copies) for i, (_, n, k) in enumerate(SHAPES)]
+    def pair_call(c, m, st):
+        return (pair, (ptr(pool[c][0]), ptr(pool[c][1]), wbytes[0], ptr(x_dev[k_gu]), ptr(y_dev["gate"]),
+                       ptr(y_dev["up"]), m, n_gu, k_gu, st))
+
+    def one_call(c, i, m, st):
+        name, n, k = SHAPES[i]
+        return (gemv, (ptr(pool[c][i]), wbytes[i], ptr(x_dev[k]), ptr(y_dev[name]), m, n, k, st))
+
+    # the decode pass: per layer copy, gate and up in one pair launch, then down
+    def calls(m, st, which=("pair", "down")):
+        out = []
+        for c in range(args.copies):
+            if "pair" in which:
+                out.append(pair_call(c, m, st))
+            if "down" in which:
+                out.append(one_call(c, 2, m, st))
+        return out
+
+    def per_matrix_calls(m, st):
+        return [one_call(c, i, m, st) for c in range(args.copies) for i in range(3)]
+
+    pair_bytes = lambda m: 2 * wbytes[0] + m * k_gu * 2 + 2 * m * n_gu * 4
+    down_bytes = lambda m: wbytes[2] + m * k_dn * 2 + m * n_dn * 4
 
     def algo_bytes(m):
-        return args.copies * sum(wb + m * k * 2 + m * n * 4 for wb, (_, n, k) in zip(wbytes, SHAPES))
+        return args.copies * (pair_bytes(m) + down_bytes(m))
 
-    def make_step(m, st):
-        cl = calls(m, st)
-
+    def make_step(cl):
         def step():
-            for a in cl:
-                gemv(*a)
+            for fn, a in cl:
+                fn(*a)
         return step
 
-    def graph_of(m):
+    def graph_of(make_calls):
         # the launches must name the capture stream that torch.cuda.graph makes current
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            make_step(m, stream_ptr(torch))()
+            make_step(make_calls(stream_ptr(torch)))()
         return g
 
+    def graph_time(make_calls, reps):
+        g = graph_of(make_calls)
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        t = timer.run(g.replay, reps)
+        del g
+        return t
+
     res = {}
-    step1 = make_step(1, sp)
+    step1 = make_step(calls(1, sp))
     for _ in range(max(1, args.warmup)):
         step1()
     t_eager = timer.run(step1, args.steps)
     log(f"[bench] M=1 stream launches: {t_eager * 1e3:.3f} ms/step, {algo_bytes(1) / t_eager / 1e9:.1f} GB/s")
-    g1 = graph_of(1)
+    g1 = graph_of(lambda st: calls(1, st))
     for _ in range(max(1, args.warmup)):
         g1.replay()
     t_graph = timer.run(g1.replay, args.steps)
@@ -213,30 +253,46 @@ def main():
     for n in y_dev:
         assert torch.equal(y_dev[n][:1], y_ref[n]), "graph replay and stream launch disagree"
     del g1
+    # the pair launch must give what one launch per matrix gives, bit for bit
+    make_step(per_matrix_calls(1, sp))()
+    torch.cuda.synchronize()
+    for n in y_dev:
+        assert torch.equal(y_dev[n][:1], y_ref[n]), "pair launch and per-matrix launches disagree"
     best_t, launch_mode = (t_graph, "hipGraph") if t_graph < t_eager else (t_eager, "stream")
     value = algo_bytes(1) / best_t / 1e9
-    # roofline of the dominant kernel: the timed region is a pass over the pool made of
-    # q4k_gemv_kernel launches only, so its average launch duration is the region's time
-    # over the launches in it (HIP events on the launch stream)
-    launches = args.copies * len(SHAPES)
-    launch_bytes = float(np.mean([wb + k * 2 + n * 4 for wb, (_, n, k) in zip(wbytes, SHAPES)]))
-    avg_dur = best_t / launches
-    achieved = launch_bytes / avg_dur / 1e9
+    # roofline of the dominant kernel, the pair launch (two thirds of the bytes): a pass of
+    # the pool's pair launches alone, replayed as the decode pass is, timed with HIP events
+    # on the launch stream; its average launch duration is the region's time over its launches.
+    # The down launches get the same treatment beside it.
+    t_pair = graph_time(lambda st: calls(1, st, ("pair",)), args.steps)
+    t_down = graph_time(lambda st: calls(1, st, ("down",)), args.steps)
+    avg_dur = t_pair / args.copies
+    achieved = pair_bytes(1) / avg_dur / 1e9
+    down_avg = t_down / args.copies
+    t_pm = graph_time(lambda st: per_matrix_calls(1, st), args.steps)
+    pm_bytes = args.copies * sum(wb + k * 2 + n * 4 for wb, (_, n, k) in zip(wbytes, SHAPES))
+    res["per_matrix_pass"] = {"GBps": pm_bytes / t_pm / 1e9, "frac_of_8TBps": pm_bytes / t_pm / 1e9 / HBM_PEAK_GBPS,
+                              "ms_per_step": t_pm * 1e3, "launches_per_step": 3 * args.copies,
+                              "us_per_launch": t_pm / (3 * args.copies) * 1e6}
+    res["down_kernel"] = {"kernel": "q4k_gemv_kernel (M=1, 5120x17408)", "avg_launch_us": down_avg * 1e6,
+                          "algorithmic_bytes_per_launch": down_bytes(1),
+                          "achieved_GBps": down_bytes(1) / down_avg / 1e9,
+                          "frac": down_bytes(1) / down_avg / 1e9 / HBM_PEAK_GBPS}
+    log(f"[bench] pair launches alone {pair_bytes(1) / avg_dur / 1e9:.1f} GB/s ({avg_dur * 1e6:.2f} us/launch); "
+        f"down alone {down_bytes(1) / down_avg / 1e9:.1f} GB/s ({down_avg * 1e6:.2f} us/launch); one launch per "
+        f"matrix {pm_bytes / t_pm / 1e9:.1f} GB/s")
 
     if want("calib"):
-        res["calibration"] = bench_calib(args, torch, np, q, timer, dev, sp, pool, best_t)
+        res["calibration"] = bench_calib(args, torch, np, q, timer, dev, sp, pool, pool_gu, best_t)
     if want("percall"):
-        res["per_launch_isolated"] = bench_percall(torch, np, calls(1, sp), gemv, wbytes)
+        res["per_launch_isolated"] = bench_percall(torch, np, calls(1, sp), [pair_bytes(1), down_bytes(1)])
     if want("verify"):
         curve = {}
         for m in (1, 2, 3, 4):
-            g = graph_of(m)
-            g.replay()
-            tm = timer.run(g.replay, max(2, args.steps // 2))
+            tm = graph_time(lambda st: calls(m, st), max(2, args.steps // 2))
             curve[str(m)] = {"GBps": algo_bytes(m) / tm / 1e9, "frac_of_8TBps": algo_bytes(m) / tm / 1e9 / HBM_PEAK_GBPS,
                              "ms_per_step": tm * 1e3,
                              "weights_per_s": args.copies * sum(n * k for _, n, k in SHAPES) / tm}
-            del g
         res["verify_GBps_vs_M"] = curve
         log("[bench] verify curve: " + ", ".join(f"M={m} {v['GBps']:.0f}" for m, v in curve.items()))
     if want("q8"):
@@ -275,7 +331,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "Q4_K GEMV M=1: gate/up 17408x5120 + down 5120x17408, 128-copy pool "
-                        f"({pool_bytes / 1e9:.2f} GB), one step = one pass over the pool",
+                        f"({pool_bytes / 1e9:.2f} GB), one step = one pass over the pool: per copy one "
+                        "qmv_q4_k_pair launch (gate and up) and one qmv_q4_k launch (down)",
             "pool_bytes": pool_bytes,
             "launch": launch_mode,
             "frac_of_8TBps": round(value / HBM_PEAK_GBPS, 4),
@@ -283,7 +340,7 @@ def main():
             "graph_replay_GBps": round(algo_bytes(1) / t_graph / 1e9, 1),
         },
         "roofline": {
-            "kernel": "q4k_gemv_kernel (M=1)",
+            "kernel": "q4k_gemv_pair_kernel (M=1, gate and up 17408x5120 each)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -292,8 +349,8 @@ def main():
             "traffic": measured("gemv_traffic"),
             "traffic_unit": "HBM bytes per launch",
             "avg_launch_us": round(avg_dur * 1e6, 3),
-            "launches_per_step": launches,
-            "algorithmic_bytes_per_launch": launch_bytes,
+            "launches_timed": args.copies,
+            "algorithmic_bytes_per_launch": pair_bytes(1),
         },
         "cpu_baseline": cpu,
         "extra": res,
@@ -301,12 +358,15 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def bench_calib(args, torch, np, q, timer, dev, sp, pool, gemv_t):
-    """Plain streaming read of every matrix of the pool, one launch each (the same
-    launches and bytes as a GEMV pass, with no arithmetic), and a 4 GiB device copy."""
+def bench_calib(args, torch, np, q, timer, dev, sp, pool, pool_gu, gemv_t):
+    """Plain streaming read of the pool with the decode pass's launches (per layer copy
+    one launch over gate and up, which sit in one allocation, and one over down: the
+    same bytes, no arithmetic), the same read with one launch per matrix, and a 4 GiB
+    device copy."""
     read = checked(q.lib.qmv_stream_read, "qmv_stream_read")
     sink = torch.empty(65536, dtype=torch.int32, device=dev)
-    mats = [(ctypes.c_void_p(t.data_ptr()), t.numel()) for c in pool for t in c]
+    mats = [(ctypes.c_void_p(t.data_ptr()), t.numel()) for gu, c in zip(pool_gu, pool) for t in (gu, c[2])]
+    per_matrix = [(ctypes.c_void_p(t.data_ptr()), t.numel()) for c in pool for t in c]
     total = sum(b for _, b in mats)
 
     def pass_of(grid, depth, nt, mats=mats):
@@ -329,7 +389,8 @@ def bench_calib(args, torch, np, q, timer, dev, sp, pool, gemv_t):
     out = {"stream_read_GBps": total / t / 1e9, "frac_of_8TBps": total / t / 1e9 / HBM_PEAK_GBPS,
            "config": {"grid": grid, "depth": depth, "nontemporal": nt, "threads": 256},
            "us_per_launch": t / len(mats) * 1e6, "sweep_GBps": {k: round(v, 1) for k, v in sweep.items()},
-           "gemv_over_read": (total / gemv_t) / (total / t)}
+           "gemv_over_read": t / gemv_t}
+    out["per_matrix_read_GBps"] = total / timer.run(pass_of(grid, depth, nt, per_matrix), args.steps) / 1e9
     buf_a = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
     buf_b = torch.empty_like(buf_a)
     # one long read (4 GiB in one launch) next to the per-matrix launches: the rate without the
@@ -341,28 +402,31 @@ def bench_calib(args, torch, np, q, timer, dev, sp, pool, gemv_t):
     out["device_copy_GBps_read_plus_write"] = 2 * buf_a.numel() / timer.run(lambda: buf_b.copy_(buf_a), 5) / 1e9
     del buf_a, buf_b
     log(f"[bench] streaming read of the pool: {out['stream_read_GBps']:.0f} GB/s ({best}, "
-        f"{out['us_per_launch']:.2f} us/launch); GEMV pass / read = {out['gemv_over_read']:.3f}; one 4 GiB read "
+        f"{out['us_per_launch']:.2f} us/launch); GEMV pass / read = {out['gemv_over_read']:.3f}; one launch per "
+        f"matrix {out['per_matrix_read_GBps']:.0f} GB/s; one 4 GiB read "
         f"{out['single_4GiB_read_GBps']:.0f} GB/s; device copy {out['device_copy_GBps_read_plus_write']:.0f} GB/s "
         f"(read+write)")
     return out
 
 
-def bench_percall(torch, np, cl, gemv, wbytes):
-    """Each launch of one pass bracketed by its own events (adds the per-call launch gap)."""
+def bench_percall(torch, np, cl, launch_bytes):
+    """Each launch of one decode pass (pair, down, pair, ...) bracketed by its own events
+    (adds the per-call launch gap)."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in cl]
     torch.cuda.synchronize()
-    for (s, e), a in zip(evs, cl):
+    for (s, e), (fn, a) in zip(evs, cl):
         s.record()
-        gemv(*a)
+        fn(*a)
         e.record()
     torch.cuda.synchronize()
-    dur = {name: [] for name, _, _ in SHAPES}
+    names = ("gate+up", "down")
+    dur = {name: [] for name in names}
     for i, (s, e) in enumerate(evs):
-        dur[SHAPES[i % 3][0]].append(s.elapsed_time(e) / 1e3)
+        dur[names[i % 2]].append(s.elapsed_time(e) / 1e3)
     out = {}
-    for i, (name, n, k) in enumerate(SHAPES):
+    for name, b in zip(names, launch_bytes):
         d = float(np.median(dur[name]))
-        out[name] = {"us_median": d * 1e6, "GBps": (wbytes[i] + k * 2 + n * 4) / d / 1e9}
+        out[name] = {"us_median": d * 1e6, "GBps": b / d / 1e9}
     log("[bench] isolated launches: " + ", ".join(f"{k} {v['us_median']:.2f} us" for k, v in out.items()))
     return out
 

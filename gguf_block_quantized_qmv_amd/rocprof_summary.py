@@ -2,7 +2,7 @@
 
     python -m gguf_block_quantized_qmv_amd.rocprof_summary trace DIR [--kernel NAME] [--per-step N] [--window A:B]
     python -m gguf_block_quantized_qmv_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR --kernel NAME \
-        --read-bytes B [--copy-bytes C] [--algo-bytes A]
+        --read-bytes B [--read-pick median|max] [--copy-bytes C] [--algo-bytes A]
     python -m gguf_block_quantized_qmv_amd.rocprof_summary mfma DIR --kernel NAME [--flops F] [--simds S]
     python -m gguf_block_quantized_qmv_amd.rocprof_summary counters DIR [DIR ...] --kernel NAME [--ratio A/B ...]
 
@@ -17,7 +17,8 @@ trace    per (kernel, grid, workgroup) group: dispatches and the mean, median,
          order (e.g. one timed region of a run).
 traffic  HBM bytes per dispatch from a FETCH_SIZE pass and a WRITE_SIZE pass,
          each scaled to bytes by a dispatch of known size in the same pass:
-         FETCH_SIZE by the streaming-read kernel over --read-bytes bytes, and
+         FETCH_SIZE by the streaming-read kernel over --read-bytes bytes (its
+         median dispatch, or with --read-pick max its largest), and
          WRITE_SIZE by the runtime's device copy of --copy-bytes bytes.
 mfma     MFMA utilisation per dispatch: SQ_VALU_MFMA_BUSY_CYCLES (summed over
          SIMDs) / (active cycles * SIMDs), the active cycles being
@@ -130,9 +131,10 @@ def traffic(args) -> None:
     cp = [float(r["Counter_Value"]) for r in write if "copyBuffer" in r["Kernel_Name"]]
     if not rd:
         raise SystemExit("no stream_read_kernel dispatch in the FETCH_SIZE pass to scale it by")
-    f_scale = args.read_bytes / (statistics.median(rd) * 1024)
-    print(f"FETCH_SIZE scale: the streaming read of {args.read_bytes} B reads {statistics.median(rd):.1f} KiB "
-          f"(median of {len(rd)}), x {f_scale:.4f} to bytes.")
+    ref = max(rd) if args.read_pick == "max" else statistics.median(rd)
+    f_scale = args.read_bytes / (ref * 1024)
+    print(f"FETCH_SIZE scale: the streaming read of {args.read_bytes} B reads {ref:.1f} KiB "
+          f"({args.read_pick} of {len(rd)}), x {f_scale:.4f} to bytes.")
     if cp:
         w_scale = args.copy_bytes / (max(cp) * 1024)
         print(f"WRITE_SIZE scale: the {args.copy_bytes} B device copy writes {max(cp):.1f} KiB, x {w_scale:.4f} to bytes.")
@@ -234,6 +236,9 @@ def main(argv=None) -> None:
     f.add_argument("write_dir")
     f.add_argument("--kernel", required=True)
     f.add_argument("--read-bytes", type=float, required=True)
+    f.add_argument("--read-pick", choices=("median", "max"), default="median",
+                   help="which streaming-read dispatch is the one of --read-bytes: the median (all reads of one "
+                        "size) or the largest (one long read among shorter ones)")
     f.add_argument("--copy-bytes", type=float, default=float(1 << 32))
     f.add_argument("--algo-bytes", type=float, default=0.0)
     f.set_defaults(fn=traffic)
