@@ -84,18 +84,32 @@ __global__ __launch_bounds__(kThr) void g_route_kernel(const float *__restrict__
 // ---------------------------------------------------------------- 2. group
 
 // Workgroup e: counts, then the pairs p (= t K + j) with ids[p] == e in
-// increasing p, written at off[e] .. off[e] + cnt[e].
+// increasing p, written at off[e] .. off[e] + cnt[e]. Wave w owns the
+// contiguous run [w R, (w + 1) R) of pairs (R a multiple of 64), so after one
+// exchange of the waves' counts each wave writes its pairs at its own running
+// offset, in order, with no further barrier.
 __global__ __launch_bounds__(kThr) void g_group_kernel(const int *__restrict__ ids, int *__restrict__ cnt,
                                                         int *__restrict__ off, int *__restrict__ plist, const int P) {
   __shared__ int red[2][kWv];
-  __shared__ int wbase[kWv + 1];
   const int e = (int)blockIdx.x;
   const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int R = ((P + kWv - 1) / kWv + 63) / 64 * 64;
+  const int p0 = wave * R, p1 = p0 + R < P ? p0 + R : P;
+  // kBatch loads in flight per lane per round trip (ids past p1 read as -1)
+  constexpr int kBatch = 8;
   int lt = 0, eq = 0;
-  for (int p = tid; p < P; p += kThr) {
-    const int v = ids[p];
-    lt += v < e;
-    eq += v == e;
+  for (int base = p0; base < p1; base += 64 * kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int p = base + 64 * i + lane;
+      v[i] = p < p1 ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      lt += v[i] >= 0 && v[i] < e;
+      eq += v[i] == e;
+    }
   }
   for (int s = 32; s >= 1; s >>= 1) {
     lt += __shfl_xor(lt, s);
@@ -103,54 +117,69 @@ __global__ __launch_bounds__(kThr) void g_group_kernel(const int *__restrict__ i
   }
   if (lane == 0) red[0][wave] = lt, red[1][wave] = eq;
   __syncthreads();
-  int o = 0, n = 0;
+  int o = 0, n = 0, run = 0;
 #pragma unroll
-  for (int w = 0; w < kWv; ++w) o += red[0][w], n += red[1][w];
+  for (int w = 0; w < kWv; ++w) {
+    o += red[0][w], n += red[1][w];
+    run += w < wave ? red[1][w] : 0;
+  }
   if (tid == 0) cnt[e] = n, off[e] = o;
-  int run = o;
-  for (int base = 0; base < P; base += kThr) {
-    const int p = base + tid;
-    const bool f = p < P && ids[p] == e;
-    const unsigned long long bal = __ballot(f);
-    const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-    __syncthreads();
-    if (lane == 0) wbase[wave] = __popcll(bal);
-    __syncthreads();
-    int before = 0, total = 0;
+  run += o;
+  for (int base = p0; base < p1; base += 64 * kBatch) {
+    int v[kBatch];
 #pragma unroll
-    for (int w = 0; w < kWv; ++w) {
-      before += w < wave ? wbase[w] : 0;
-      total += wbase[w];
+    for (int i = 0; i < kBatch; ++i) {
+      const int p = base + 64 * i + lane;
+      v[i] = p < p1 ? ids[p] : -1;
     }
-    if (f) plist[run + before + rank] = p;
-    run += total;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const bool f = v[i] == e;
+      const unsigned long long bal = __ballot(f);
+      if (f) plist[run + __popcll(bal & ((1ull << lane) - 1ull))] = base + 64 * i + lane;
+      run += __popcll(bal);
+    }
   }
 }
 
 // ---------------------------------------------------------------- 3. chunks
 
 // One workgroup: chunk offsets per expert (an exclusive scan in expert order)
-// and the (expert, chunk) list.
+// and the (expert, chunk) list, for chunks of CH pairs; when choff32 is not
+// null, the same for chunks of 32 pairs (the wide gate/up form) as well.
 template <int CH>
-__global__ __launch_bounds__(kThr) void g_chunks_kernel(const int *__restrict__ cnt, int *__restrict__ choff,
-                                                         int2 *__restrict__ chunks, const int E) {
-  __shared__ int nch[QMV_MOE_MAX_EXPERTS + 1];
-  const int tid = (int)threadIdx.x;
-  for (int e = tid; e < E; e += kThr) nch[e] = (cnt[e] + CH - 1) / CH;
-  __syncthreads();
-  if (tid == 0) {
-    int s = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = nch[e];
-      nch[e] = s;
-      s += c;
-    }
-    nch[E] = s;
+__device__ __forceinline__ void chunk_list(const int *__restrict__ cnt, int *__restrict__ choff,
+                                           int2 *__restrict__ chunks, const int E, int *nch) {
+  // E <= 256 = kThr: thread e holds expert e's chunk count; an inclusive scan
+  // over the threads (in-wave shuffles, then the waves' totals), written
+  // shifted by one as the exclusive offsets
+  static_assert(QMV_MOE_MAX_EXPERTS <= kThr, "one thread per expert");
+  __shared__ int wsum[kWv];
+  const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid < E ? (cnt[tid] + CH - 1) / CH : 0;
+  int v = c;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d);
+    if (lane >= d) v += u;
   }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWv; ++w) v += w < wave ? wsum[w] : 0;
+  if (tid < E) nch[tid + 1] = v;
+  if (tid == 0) nch[0] = 0;
   __syncthreads();
   for (int e = tid; e <= E; e += kThr) choff[e] = nch[e];
   for (int e = tid; e < E; e += kThr)
     for (int c = 0; c < nch[e + 1] - nch[e]; ++c) chunks[nch[e] + c] = make_int2(e, c);
+}
+
+__global__ __launch_bounds__(kThr) void g_chunks_kernel(const int *__restrict__ cnt, int *__restrict__ choff,
+                                                         int2 *__restrict__ chunks, int *__restrict__ choff32,
+                                                         int2 *__restrict__ chunks32, const int E) {
+  __shared__ int nch[2][QMV_MOE_MAX_EXPERTS + 1];
+  chunk_list<kChunk>(cnt, choff, chunks, E, nch[0]);
+  if (choff32) chunk_list<layout::kGroupChunk32>(cnt, choff32, chunks32, E, nch[1]);
 }
 
 // ---------------------------------------------------------------- 4. gate/up
@@ -669,13 +698,10 @@ int launch_q4_k_moe_grouped(const void *w_gate, const void *w_up, const void *w_
                          logits, ids, wts, topk_ids, topk_w, t, n_experts, top_k);
   if (!rc) rc = launch_kernel("g_group_kernel", g_group_kernel, dim3((unsigned)n_experts), dim3(kThr), 0, s, ids,
                               cnt, off, plist, P);
-  if (!rc) rc = launch_kernel("g_chunks_kernel", g_chunks_kernel<kChunk>, dim3(1), dim3(kThr), 0, s, cnt, choff,
-                              chunks, n_experts);
   // gate/up in chunks of 32 where there are enough pairs and 32 rows of x fit in LDS
   const bool wide = P >= 2048 && layout::group_gate_up_lds(kChunk32, hidden) <= layout::kLdsBudget;
-  if (!rc && wide)
-    rc = launch_kernel("g_chunks_kernel", g_chunks_kernel<kChunk32>, dim3(1), dim3(kThr), 0, s, cnt, choff32,
-                       chunks32, n_experts);
+  if (!rc) rc = launch_kernel("g_chunks_kernel", g_chunks_kernel, dim3(1), dim3(kThr), 0, s, cnt, choff, chunks,
+                              wide ? choff32 : nullptr, wide ? chunks32 : nullptr, n_experts);
   if (!rc && wide) {
     const unsigned maxch32 = (unsigned)((P + kChunk32 - 1) / kChunk32 + n_experts);
     rc = launch_gate_up32<2>(wg, wu, x, cnt, off, choff32, chunks32, plist, h, hidden, ffn, n_experts, top_k, maxch32,
