@@ -452,6 +452,8 @@ constexpr int kGroupTile = 16;
 
 // Tiles of 16 rows per wave, by pair count.
 QMV_HDI int group_tiles_per_wave(int P) { return P >= 2048 ? 4 : (P >= 256 ? 2 : 1); }
+// The wide (32-pair) gate/up form: waves per workgroup and tiles per wave.
+constexpr int kGroupWideWaves = 8, kGroupWideTiles = 1;
 // Lane l of wave wv in workgroup bx (waves per workgroup: nwaves): its W row
 // for tile tt of expert e (rows of the expert: rows).
 QMV_HDI size_t group_row(int e, int rows, int bx, int nwaves, int wv, int tpw, int tt, int l) {

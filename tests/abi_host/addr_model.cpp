@@ -413,7 +413,7 @@ void grouped_case(int T, int hidden, int ffn, int E, int K) {
   const bool wide = P >= 2048 && layout::group_gate_up_lds(layout::kGroupChunk32, hidden) <= layout::kLdsBudget;
   char what[160];
   std::snprintf(what, sizeof what, "grouped T %d hidden %d ffn %d E %d K %d", T, hidden, ffn, E, K);
-  if (wide) group_matrix(what, E, ffn, hidden, 8, 2);
+  if (wide) group_matrix(what, E, ffn, hidden, addr::kGroupWideWaves, addr::kGroupWideTiles);
   else group_matrix(what, E, ffn, hidden, 4, tpw);
   group_matrix(what, E, hidden, ffn, 4, tpw);
 }
