@@ -233,9 +233,10 @@ __global__ __launch_bounds__(kThr) void g_gate_up_kernel(const uint8_t *__restri
   const int y = (int)blockIdx.y;
   if (y >= choff[E]) return;   // uniform over the workgroup
   const ChunkInfo ci = chunk_info(chunks, cnt, off, y);
-  const int gpr = hidden >> 3, rs = gpr + 4, nsub = hidden >> 5, nblk = hidden >> 8;
+  const int gpr = hidden >> 3, rs = gpr + layout::kGroupRowPad, nsub = hidden >> 5, nblk = hidden >> 8;
+  const int ss = nsub + layout::kGroupSumPad;
   uint4 *xs = lds;                                                    // [16][rs]
-  float *xsum = reinterpret_cast<float *>(lds + (size_t)kChunk * rs); // [16][nsub]
+  float *xsum = reinterpret_cast<float *>(lds + (size_t)kChunk * rs); // [16][ss]
   const int tid = (int)threadIdx.x, wv = tid >> 6, l = tid & 63, nl = l & 15, kg = l >> 4;
 
   // stage the chunk's activation rows (zeros past its pairs)
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(kThr) void g_gate_up_kernel(const uint8_t *__restri
         s += bf16_bits_to_f32(v4[u] >> 16);
       }
     }
-    xsum[t] = s;
+    xsum[i * ss + sb] = s;
   }
   __syncthreads();
 
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(kThr) void g_gate_up_kernel(const uint8_t *__restri
         const bf16x8 av = __builtin_bit_cast(bf16x8, xa[4 * jg]);
         float xsr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xsr[r] = xsum[(4 * kg + r) * nsub + jg];
+        for (int r = 0; r < 4; ++r) xsr[r] = xsum[(4 * kg + r) * ss + jg];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const ChunkScales cg = chunk_scales(lg[tt].hdr, sel), cu = chunk_scales(lu[tt].hdr, sel);
@@ -362,9 +363,10 @@ __global__ __launch_bounds__(kThr32) void g_gate_up32_kernel(const uint8_t *__re
   const int y = (int)blockIdx.y;
   if (y >= choff[E]) return;   // uniform over the workgroup
   const ChunkInfo ci = chunk_info<kChunk32>(chunks, cnt, off, y);
-  const int gpr = hidden >> 3, rs = gpr + 4, nsub = hidden >> 5, nblk = hidden >> 8;
+  const int gpr = hidden >> 3, rs = gpr + layout::kGroupRowPad, nsub = hidden >> 5, nblk = hidden >> 8;
+  const int ss = nsub + layout::kGroupSumPad;
   uint4 *xs = lds;                                                      // [32][rs]
-  float *xsum = reinterpret_cast<float *>(lds + (size_t)kChunk32 * rs); // [32][nsub]
+  float *xsum = reinterpret_cast<float *>(lds + (size_t)kChunk32 * rs); // [32][ss]
   const int tid = (int)threadIdx.x, wv = tid >> 6, l = tid & 63, nl = l & 15, kg = l >> 4;
 
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(kThr32) void g_gate_up32_kernel(const uint8_t *__re
         s += bf16_bits_to_f32(v4[u] >> 16);
       }
     }
-    xsum[t] = s;
+    xsum[i * ss + sb] = s;
   }
   __syncthreads();
 
@@ -432,8 +434,8 @@ __global__ __launch_bounds__(kThr32) void g_gate_up32_kernel(const uint8_t *__re
         float xs0[4], xs1[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          xs0[r] = xsum[(4 * kg + r) * nsub + jg];
-          xs1[r] = xsum[(kTile + 4 * kg + r) * nsub + jg];
+          xs0[r] = xsum[(4 * kg + r) * ss + jg];
+          xs1[r] = xsum[(kTile + 4 * kg + r) * ss + jg];
         }
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
@@ -493,11 +495,12 @@ __global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict_
   const int y = (int)blockIdx.y;
   if (y >= choff[E]) return;
   const ChunkInfo ci = chunk_info(chunks, cnt, off, y);
-  const int gpr = ffn >> 3, rs = gpr + 4, nsub = ffn >> 5, nblk = ffn >> 8;
+  const int gpr = ffn >> 3, rs = gpr + layout::kGroupRowPad, nsub = ffn >> 5, nblk = ffn >> 8;
+  const int ss = nsub + layout::kGroupSumPad;
   uint4 *hs_hi = lds;                                                     // [16][rs]
   uint4 *hs_mi = lds + (size_t)kChunk * rs;                               // [16][rs]
   uint4 *hs_lo = lds + (size_t)2 * kChunk * rs;                           // [16][rs]
-  float *hsum = reinterpret_cast<float *>(lds + (size_t)3 * kChunk * rs); // [16][nsub]
+  float *hsum = reinterpret_cast<float *>(lds + (size_t)3 * kChunk * rs); // [16][ss]
   const int tid = (int)threadIdx.x, wv = tid >> 6, l = tid & 63, nl = l & 15, kg = l >> 4;
 
   // stage h of the chunk's pairs as three bf16 parts (zeros past its pairs):
@@ -546,7 +549,7 @@ __global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict_
         s += bf16_bits_to_f32(vh[u] >> 16) + (bf16_bits_to_f32(vm[u] >> 16) + bf16_bits_to_f32(vl[u] >> 16));
       }
     }
-    hsum[t] = s;
+    hsum[i * ss + sb] = s;
   }
   __syncthreads();
 
@@ -579,7 +582,7 @@ __global__ __launch_bounds__(kThr) void g_down_kernel(const uint8_t *__restrict_
         const bf16x8 alo = __builtin_bit_cast(bf16x8, la[4 * jg]);
         float hsr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hsr[r] = hsum[(4 * kg + r) * nsub + jg];
+        for (int r = 0; r < 4; ++r) hsr[r] = hsum[(4 * kg + r) * ss + jg];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
           const ChunkScales cs = chunk_scales(ld[tt].hdr, sel);

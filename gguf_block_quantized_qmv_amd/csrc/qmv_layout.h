@@ -125,13 +125,24 @@ inline GroupLayout group_layout(int t, int hidden, int ffn, int n_experts, int t
   L.total = o;
   return L;
 }
-// LDS: chunk rows of x (bf16, 4 pad granules per row) and their per-32 sums;
-// for down, h as three bf16 parts and its per-32 sums.
+// LDS: chunk rows of x (bf16) and their per-32 sums; for down, h as three bf16
+// parts and its per-32 sums. Rows are padded by kGroupRowPad granules, so that
+// a row's stride is 1 mod 16 granules: the MFMA fragment reads (16 lanes, one
+// granule of 16 consecutive rows) fall in 16 distinct 16-byte bank groups
+// (gfx950 serves 16 lanes of a 16-byte LDS read per clock, group = granule mod
+// 16). A pad of 4 put those 16 lanes in 4 groups, a 4-way conflict.
+// The per-32 sums are rows of K/32 + kGroupSumPad floats: each 4-byte read
+// takes the sums of 4 pair rows 4 apart (one per 16-lane group), and an odd
+// row stride puts them in 4 distinct banks (with K/32 floats per row, a
+// multiple of 8, they shared a bank or two).
+constexpr int kGroupRowPad = 1, kGroupSumPad = 1;
 constexpr size_t group_gate_up_lds(int chunk, int hidden) {
-  return (size_t)chunk * ((size_t)(hidden >> 3) + 4) * 16 + (size_t)chunk * (size_t)(hidden >> 5) * 4;
+  return (size_t)chunk * ((size_t)(hidden >> 3) + kGroupRowPad) * 16 +
+         (size_t)chunk * ((size_t)(hidden >> 5) + kGroupSumPad) * 4;
 }
 constexpr size_t group_down_lds(int ffn) {
-  return (size_t)3 * kGroupChunk * ((size_t)(ffn >> 3) + 4) * 16 + (size_t)kGroupChunk * (size_t)(ffn >> 5) * 4;
+  return (size_t)3 * kGroupChunk * ((size_t)(ffn >> 3) + kGroupRowPad) * 16 +
+         (size_t)kGroupChunk * ((size_t)(ffn >> 5) + kGroupSumPad) * 4;
 }
 constexpr bool group_fits_lds(int hidden, int ffn) {
   return group_gate_up_lds(kGroupChunk, hidden) <= kLdsBudget && group_down_lds(ffn) <= kLdsBudget;
