@@ -55,11 +55,11 @@ MEASURED = {
     # 4 GiB device copy (profiles/q4k_gemv_m1_hbm_traffic.md)
     "gemv_traffic": {"sources": (_CSRC + "q4k_gemv.hip", _CSRC + "q4k_common.h", _CSRC + "qmv_device.h",
                                  _CSRC + "qmv_layout.h", _CSRC + "qmv_addr.h"),
-                     "sha256": "0154c8c8fdf23c29d73843692da4709a5547a68a46318d7c90aa8bd829e79ae2", "value": 101097390},
+                     "sha256": "f9a72f83928626bc37eba0ddccde42f734c43a51b2d45e3ce0ebec88f04279cd", "value": 101097390},
     # MFMA utilisation of the prefill GEMM at M=512 (profiles/q4k_prefill_m512_mfma.md)
     "prefill_mfma_util": {"sources": (_CSRC + "q4k_prefill.hip", _CSRC + "q4k_common.h", _CSRC + "qmv_device.h",
                                       _CSRC + "qmv_layout.h", _CSRC + "qmv_addr.h"),
-                          "sha256": "523d1669161aacab7fb2a9c1f6f2359be0ea2a66e80fa315a3e5f64196ebad68",
+                          "sha256": "f206eb2a9832e7362fd39b5e86a171f80965530c5649c742b947cbaecf9d0551",
                           "value": {"up": 0.374, "down": 0.388}},
 }
 
