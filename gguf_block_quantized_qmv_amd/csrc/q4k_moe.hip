@@ -49,8 +49,6 @@ using namespace moe;
 constexpr int kWaves = 4;
 constexpr int kThreads = addr::kMoeThreads;
 // gate/up: 16 lanes per W row, 4 rows per wave, 16 rows per workgroup
-constexpr int kUpLanes = addr::kMoeUpLanes;
-constexpr int kUpRows = addr::kMoeUpRows;
 constexpr int kUpDepth = addr::kMoeUpDepth;  // steps of gate + up loads in flight
 // down: 4 lanes per W row; a workgroup owns 8 rows, and its 8 lane groups of
 // 32 lanes (8 rows x 4 chunks) split the distinct experts
@@ -58,8 +56,7 @@ constexpr int kDnRows = addr::kMoeDnRows;
 constexpr int kDnGroups = addr::kMoeDnGroups;
 constexpr int kDnDepth = addr::kMoeDnDepth;  // (expert, block) units of loads in flight per lane
 static_assert(kThreads == kRouteThreads, "the gate/up workgroup routes with every thread");
-static_assert(kThreads == 64 * kWaves && kUpRows == kWaves * (64 / kUpLanes) && kDnGroups == kThreads / (4 * kDnRows),
-              "the shapes the addressing assumes");
+static_assert(kThreads == 64 * kWaves && kDnGroups == kThreads / (4 * kDnRows), "the shapes the addressing assumes");
 
 // The gate (or up) loads of one step at bp: the block header and chunk c's 32
 // quant bytes (the Q4_K windows of addr::dense_window).
@@ -161,9 +158,18 @@ __device__ __forceinline__ void store_x_batch(uint4 *xs, const int base, const i
   }
 }
 
-// Workgroup (tile, slot) of launch 1: rows 16 tile .. of the slot-th distinct
-// expert's W_gate and W_up. Returns with every thread of the workgroup past
-// its last barrier (threads without a row return early).
+// Workgroup (tile, slot) of launch 1: rows R tile .. R tile + R - 1 of the
+// slot-th distinct expert's W_gate and W_up, L lanes per row (addr::moe_up_rows,
+// addr::moe_up_lanes: 8 rows of 32 lanes for one token, 16 rows of 16 lanes for
+// more). Returns with every thread of the workgroup past its last barrier
+// (threads without a row return early).
+//
+// Both lane widths give every row the same bits, so a token's result does not
+// depend on how many tokens share the call: a lane's blocks are summed in two
+// chains, blocks b with b / 4 even and with b / 4 odd (for 32 lanes the two
+// chains sit in lanes j and j ^ 16, for 16 lanes in one lane's alternate
+// steps), the two chains are added, then summed over the 16 lanes of the
+// row's (block mod 4, chunk) positions in one fixed DPP tree.
 template <int T>
 __device__ __forceinline__ void gate_up_body(const uint8_t *__restrict__ w_gate, const uint8_t *__restrict__ w_up,
                                              const float *__restrict__ logits, const uint16_t *__restrict__ x,
@@ -200,8 +206,9 @@ __device__ __forceinline__ void gate_up_body(const uint8_t *__restrict__ w_gate,
   const Slot<T> sl = my_slot<T>(pr, slot, P);
   if (sl.p0 < 0) return;  // fewer distinct experts than the grid allows for (uniform over the workgroup)
 
+  constexpr int kUpLanes = addr::moe_up_lanes(T), kBps = kUpLanes / 4;
   const int j = lane & (kUpLanes - 1);
-  const addr::MoeUpLane ln = addr::moe_up_lane(sl.e, ffn, hidden, tile, threadIdx.x);
+  const addr::MoeUpLane ln = addr::moe_up_lane(kUpLanes, sl.e, ffn, hidden, tile, threadIdx.x);
   const int c = ln.c, jb = ln.jb, f = ln.f;
   const bool active = ln.active;
   const int nblk = hidden >> 8;
@@ -213,8 +220,8 @@ __device__ __forceinline__ void gate_up_body(const uint8_t *__restrict__ w_gate,
 #pragma unroll
   for (int u = 0; u < kUpDepth; ++u) {
     if (addr::moe_up_step_ok(ln, nblk, u)) {
-      load_up_step(addr::moe_up_step_at(gl, u), c, gh[u], ga[u], gb[u]);
-      load_up_step(addr::moe_up_step_at(ul, u), c, uh[u], ua[u], ub[u]);
+      load_up_step(addr::moe_up_step_at(gl, kBps, u), c, gh[u], ga[u], gb[u]);
+      load_up_step(addr::moe_up_step_at(ul, kBps, u), c, uh[u], ua[u], ub[u]);
     }
   }
   // the weights (softmax) and the routing outputs, off the path to the loads
@@ -253,25 +260,30 @@ __device__ __forceinline__ void gate_up_body(const uint8_t *__restrict__ w_gate,
     xoff[r] = sl.tok[r] * gpp;
     soff[r] = sl.tok[r] * nsub;
   }
-  // chunk 16s + j of the row sits at padded granule 136 s + (j >> 1) * 17 + (j & 1) * 8
+  // chunk 4 kBps s + j of the row sits at padded granule 34 kBps s + (j >> 1) * 17 + (j & 1) * 8
   const uint4 *xb = xs + (j >> 1) * 17 + (j & 1) * 8;
   const float *sb = xsum + 2 * j;
-  float acc_g[T], acc_u[T];
+  // chain 0: blocks b with b / 4 even; chain 1: b / 4 odd (16 lanes: odd steps)
+  float acc_g[2][T], acc_u[2][T];
 #pragma unroll
-  for (int r = 0; r < T; ++r) acc_g[r] = acc_u[r] = 0.0f;
+  for (int r = 0; r < T; ++r) acc_g[0][r] = acc_u[0][r] = acc_g[1][r] = acc_u[1][r] = 0.0f;
 
+  static_assert(kUpDepth == 2, "16 lanes: step parity is the ring slot");
   for (int s0 = 0; s0 < nsteps; s0 += kUpDepth) {
 #pragma unroll
     for (int u = 0; u < kUpDepth; ++u) {
       const int s = s0 + u;
-      if (s < nsteps && 4 * s + jb < nblk) {
-        chunk_bf16<T>(acc_g, sl.ntok, gh[u], ga[u], gb[u], sel, xb + s * 136, xoff, sb + 32 * s, soff);
-        chunk_bf16<T>(acc_u, sl.ntok, uh[u], ua[u], ub[u], sel, xb + s * 136, xoff, sb + 32 * s, soff);
+      constexpr int kOdd = kBps == 4 ? 1 : 0;   // chain of the ring slot u = 1
+      if (s < nsteps && kBps * s + jb < nblk) {
+        chunk_bf16<T>(acc_g[u * kOdd], sl.ntok, gh[u], ga[u], gb[u], sel, xb + s * 34 * kBps, xoff,
+                      sb + 8 * kBps * s, soff);
+        chunk_bf16<T>(acc_u[u * kOdd], sl.ntok, uh[u], ua[u], ub[u], sel, xb + s * 34 * kBps, xoff,
+                      sb + 8 * kBps * s, soff);
       }
       const int sn = s + kUpDepth;
       if (addr::moe_up_step_ok(ln, nblk, sn)) {   // active holds for every lane that gets here
-        load_up_step(addr::moe_up_step_at(gl, sn), c, gh[u], ga[u], gb[u]);
-        load_up_step(addr::moe_up_step_at(ul, sn), c, uh[u], ua[u], ub[u]);
+        load_up_step(addr::moe_up_step_at(gl, kBps, sn), c, gh[u], ga[u], gb[u]);
+        load_up_step(addr::moe_up_step_at(ul, kBps, sn), c, uh[u], ua[u], ub[u]);
       }
     }
   }
@@ -280,8 +292,16 @@ __device__ __forceinline__ void gate_up_body(const uint8_t *__restrict__ w_gate,
 #pragma unroll
   for (int r = 0; r < T; ++r) {
     if (r >= sl.ntok) break;
-    const float g = row16_sum(acc_g[r]);
-    const float u = row16_sum(acc_u[r]);
+    float vg, vu;
+    if constexpr (kUpLanes == 32) {   // lane j ^ 16 holds the other chain
+      vg = acc_g[0][r] + __shfl_xor(acc_g[0][r], 16);
+      vu = acc_u[0][r] + __shfl_xor(acc_u[0][r], 16);
+    } else {
+      vg = acc_g[0][r] + acc_g[1][r];
+      vu = acc_u[0][r] + acc_u[1][r];
+    }
+    const float g = row16_sum(vg);
+    const float u = row16_sum(vu);
     if (j == r) h[(size_t)(sl.p0 + r) * ffn + f] = g / (1.0f + expf(-g)) * u;
   }
 }
@@ -518,6 +538,7 @@ int launch_t(const void *w_gate, const void *w_up, const void *w_down, const flo
   static LdsGrant granted_a, granted_b;
   const size_t lds_a = layout::q4k_moe_gate_up_lds(T, hidden), lds_b = layout::q4k_moe_down_lds(T * top_k, ffn);
   const int max_slots = n_experts < T * top_k ? n_experts : T * top_k;
+  constexpr int kUpRows = addr::moe_up_rows(T);
   const dim3 grid_a((unsigned)((ffn + kUpRows - 1) / kUpRows), (unsigned)max_slots);
   const dim3 grid_b((unsigned)((hidden + kDnRows - 1) / kDnRows));
   if (allow_dynamic_lds(reinterpret_cast<const void *>(&moe_gate_up_kernel<T>), lds_a, granted_a,

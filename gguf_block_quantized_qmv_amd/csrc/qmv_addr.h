@@ -286,38 +286,46 @@ QMV_HDI Window iq4_window(int qoff, int i) { return i == 0 ? Window{0, 8} : Wind
 
 // ---- routed-expert decode (Q4_K experts) ---------------------------------------
 //
-// Gate/up: workgroup (x, y) takes rows 16x .. 16x + 15 of the y-th distinct
-// expert e, 16 lanes per row as the dense GEMV (4 blocks per step), every
-// load guarded by the row and block existing. Down: 4 lanes per W_down row
-// (lane c reads chunk c of each block), units (expert slot, block) in order,
-// guarded by the unit existing.
+// Gate/up: workgroup (x, y) takes rows R x .. R x + R - 1 of the y-th distinct
+// expert e, L lanes per row (L / 4 blocks per step), every load guarded by the
+// row and block existing: L = 32 and R = 8 for one token, L = 16 and R = 16
+// for two to four. One token's few expert rows then spread over twice the
+// workgroups (768 for the 35B-A3B layer, three per CU, where 384 left half the
+// CUs with two and half with one). Down: 4 lanes per W_down row (lane c reads
+// chunk c of each block), units (expert slot, block) in order, guarded by the
+// unit existing.
 
-constexpr int kMoeThreads = 256, kMoeUpRows = 16, kMoeUpLanes = 16, kMoeUpDepth = 2;
+constexpr int kMoeThreads = 256, kMoeUpDepth = 2;
+QMV_HDI constexpr int moe_up_lanes(int t) { return t == 1 ? 32 : 16; }
+QMV_HDI constexpr int moe_up_rows(int t) { return (kMoeThreads / 64) * (64 / moe_up_lanes(t)); }
 constexpr int kMoeDnRows = 8, kMoeDnGroups = 8, kMoeDnDepth = 6;
 
 struct MoeUpLane {
-  int f, c, jb, nsteps;
+  int f, c, jb, nsteps, bps;   // bps: blocks per step (lanes per row / 4)
   bool active;
   size_t base;   // the lane's block at step 0 in the chosen expert's gate (or up) matrix
 };
-QMV_HDI MoeUpLane moe_up_lane(int e, int ffn, int hidden, int bx, int tid) {
+QMV_HDI MoeUpLane moe_up_lane(int lanes, int e, int ffn, int hidden, int bx, int tid) {
   MoeUpLane l;
-  const int lane = tid & 63, wave = tid >> 6, j = lane & (kMoeUpLanes - 1);
+  const int lane = tid & 63, wave = tid >> 6, j = lane & (lanes - 1);
   l.c = j & 3;
   l.jb = j >> 2;
-  l.f = bx * kMoeUpRows + wave * (64 / kMoeUpLanes) + lane / kMoeUpLanes;
+  l.bps = lanes / 4;
+  l.f = bx * ((kMoeThreads / 64) * (64 / lanes)) + wave * (64 / lanes) + lane / lanes;
   l.active = l.f < ffn;
   const int nblk = hidden >> 8;
   const size_t row_bytes = (size_t)nblk * kQ4KBytes;
   l.base = (size_t)e * (size_t)ffn * row_bytes + (size_t)(l.active ? l.f : 0) * row_bytes + (size_t)l.jb * kQ4KBytes;
-  l.nsteps = (nblk + 3) >> 2;
+  l.nsteps = (nblk + l.bps - 1) / l.bps;
   return l;
 }
-QMV_HDI bool moe_up_step_ok(const MoeUpLane &l, int nblk, int s) { return l.active && s < l.nsteps && 4 * s + l.jb < nblk; }
+QMV_HDI bool moe_up_step_ok(const MoeUpLane &l, int nblk, int s) {
+  return l.active && s < l.nsteps && l.bps * s + l.jb < nblk;
+}
 // Step s's block from the lane's base (an offset or an address); its reads are
 // the Q4_K windows of dense_window.
 template <class P>
-QMV_HDI P moe_up_step_at(P base, int s) { return base + (size_t)(4 * s) * kQ4KBytes; }
+QMV_HDI P moe_up_step_at(P base, int bps, int s) { return base + (size_t)(bps * s) * kQ4KBytes; }
 
 struct MoeDnLane {
   int grp, c, n, my_slots, units;

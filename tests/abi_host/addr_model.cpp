@@ -220,14 +220,15 @@ void moe_q4k_case(int T, int hidden, int ffn, int E, int K) {
   const int max_slots = E < T * K ? E : T * K;
   char what[160];
   std::snprintf(what, sizeof what, "q4_k moe T %d hidden %d ffn %d E %d K %d", T, hidden, ffn, E, K);
-  const unsigned gx = (unsigned)((ffn + addr::kMoeUpRows - 1) / addr::kMoeUpRows);
+  const int up_rows = addr::moe_up_rows(T), up_lanes = addr::moe_up_lanes(T);
+  const unsigned gx = (unsigned)((ffn + up_rows - 1) / up_rows);
   for (int e : {0, E - 1}) {
     for (unsigned bx : groups_of(gx)) {
       for (int tid = 0; tid < addr::kMoeThreads; ++tid) {
-        const addr::MoeUpLane l = addr::moe_up_lane(e, ffn, hidden, (int)bx, tid);
+        const addr::MoeUpLane l = addr::moe_up_lane(up_lanes, e, ffn, hidden, (int)bx, tid);
         for (int s = 0; s < l.nsteps + addr::kMoeUpDepth; ++s) {
           if (!addr::moe_up_step_ok(l, nblk_up, s)) continue;
-          const size_t b = addr::moe_up_step_at(l.base, s);
+          const size_t b = addr::moe_up_step_at(l.base, l.bps, s);
           const size_t lo = ((size_t)e * ffn + l.f) * up_row, hi = lo + up_row;
           for (int i = 0; i < 2; ++i) check(what, b, addr::dense_window(addr::kFmtQ4K, l.c, i), up_total, lo, hi);
         }
