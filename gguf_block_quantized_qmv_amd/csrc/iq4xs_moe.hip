@@ -45,14 +45,12 @@ constexpr int kThreads = 64 * kWaves;
 static_assert(kThreads == kTableEntries, "one table entry per thread");
 static_assert(kThreads == kRouteThreads, "the gate/up workgroup routes with every thread");
 // gate/up: 16 lanes per W row, 4 rows per wave, 16 rows per workgroup
-constexpr int kUpLanes = addr::kIq4MoeUpLanes;
-constexpr int kUpRows = addr::kIq4MoeUpRows;
 constexpr int kUpDepth = addr::kIq4MoeUpDepth;   // units (gate and up) of loads in flight per lane
 // down: 8 lanes per W row (one sub-block each), 8 rows per wave and workgroup
 constexpr int kDnLanes = addr::kIq4MoeDnLanes;
 constexpr int kDnRows = addr::kIq4MoeDnRows;
 constexpr int kDnDepth = addr::kIq4MoeDnDepth;   // (expert, super-block) units of loads in flight per lane
-static_assert(kUpRows == kThreads / kUpLanes && kDnRows == 64 / kDnLanes, "the shapes the addressing assumes");
+static_assert(kThreads == 256 && kDnRows == 64 / kDnLanes, "the shapes the addressing assumes");
 constexpr int kTableWords = (int)(sizeof(Table) / 4);
 static_assert(kTableWords <= kThreads, "one table word per thread");
 
@@ -112,10 +110,15 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_gate_up_kernel(
   const Slot<T> sl = my_slot<T>(pr, (int)blockIdx.y, P);
   if (sl.p0 < 0) return;  // fewer distinct experts than the grid allows for (uniform over the workgroup)
 
+  // kUpLanes lanes per row: 32 for one token, 16 for more. Both give a row the
+  // same bits: a lane's units are summed in two chains by unit parity for 16
+  // lanes (sub-blocks l + 32 t and l + 16 + 32 t), which for 32 lanes are lanes
+  // l and l + 16; the chains are added, then summed over 16 lanes.
+  constexpr int kUpLanes = addr::iq4_moe_up_lanes(T), kUpRows = addr::iq4_moe_up_rows(T);
   const int l = tid % kUpLanes;
   const int f = blockIdx.x * kUpRows + tid / kUpLanes;
   // lane l: sub-blocks u = l + 16 t -> super-block (l >> 3) + 2 t, sub-block j = l & 7
-  const addr::Iq4Lane ln = addr::iq4_moe_up_lane(sl.e, ffn, hidden, blockIdx.x, tid);
+  const addr::Iq4Lane ln = addr::iq4_moe_up_lane(kUpLanes, sl.e, ffn, hidden, blockIdx.x, tid);
   const uint8_t *grow = w_gate + ln.row_base, *urow = w_up + ln.row_base;
   const uint8_t *gl = w_gate + ln.lane_base, *ul = w_up + ln.lane_base;
   const int j = l & 7, qoff = ln.qoff;
@@ -140,9 +143,11 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_gate_up_kernel(
 #pragma unroll
   for (int r = 0; r < T; ++r) xoff[r] = sl.tok[r] * rg;
   const int sh_lo = 4 * j, sh_hi = 16 + 2 * j;
-  float acc_g[T], acc_u[T];
+  float acc_g[2][T], acc_u[2][T];   // the two chains (32 lanes: chain 0 only)
 #pragma unroll
-  for (int r = 0; r < T; ++r) acc_g[r] = acc_u[r] = 0.0f;
+  for (int r = 0; r < T; ++r) acc_g[0][r] = acc_u[0][r] = acc_g[1][r] = acc_u[1][r] = 0.0f;
+  static_assert(kUpDepth == 2, "16 lanes: unit parity is the ring slot");
+  constexpr int kOdd = kUpLanes == 16 ? 1 : 0;
   for (int t0 = 0; t0 < nslots; t0 += kUpDepth) {
 #pragma unroll
     for (int d = 0; d < kUpDepth; ++d) {
@@ -172,8 +177,8 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_gate_up_kernel(
         float b0 = pairs_dot(u0, x0, 0.0f), b1 = pairs_dot(u1, x1, 0.0f);
         b0 = pairs_dot(u2, x2, b0);
         b1 = pairs_dot(u3, x3, b1);
-        acc_g[r] = __builtin_fmaf(dg, a0 + a1, acc_g[r]);
-        acc_u[r] = __builtin_fmaf(du, b0 + b1, acc_u[r]);
+        acc_g[d * kOdd][r] = __builtin_fmaf(dg, a0 + a1, acc_g[d * kOdd][r]);
+        acc_u[d * kOdd][r] = __builtin_fmaf(du, b0 + b1, acc_u[d * kOdd][r]);
       }
     }
   }
@@ -182,8 +187,16 @@ __global__ __launch_bounds__(kThreads) void iq4xs_moe_gate_up_kernel(
 #pragma unroll
   for (int r = 0; r < T; ++r) {
     if (r >= sl.ntok) break;
-    const float gv = group_sum<kUpLanes>(acc_g[r]);
-    const float uv = group_sum<kUpLanes>(acc_u[r]);
+    float vg, vu;
+    if constexpr (kUpLanes == 32) {   // lane l ^ 16 holds the other chain
+      vg = acc_g[0][r] + __shfl_xor(acc_g[0][r], 16);
+      vu = acc_u[0][r] + __shfl_xor(acc_u[0][r], 16);
+    } else {
+      vg = acc_g[0][r] + acc_g[1][r];
+      vu = acc_u[0][r] + acc_u[1][r];
+    }
+    const float gv = group_sum<16>(vg);
+    const float uv = group_sum<16>(vu);
     if (l == r && f < ffn) h[(size_t)(sl.p0 + r) * ffn + f] = gv / (1.0f + expf(-gv)) * uv;
   }
 }
@@ -369,6 +382,7 @@ int launch_t(const void *w_gate, const void *w_up, const void *w_down, const flo
                         "iq4xs_moe_down_kernel lds"))
     return QMV_ERR_HIP;
   const int max_slots = n_experts < T * top_k ? n_experts : T * top_k;
+  constexpr int kUpRows = addr::iq4_moe_up_rows(T);
   const dim3 grid_a((unsigned)((ffn + kUpRows - 1) / kUpRows), (unsigned)max_slots);
   int rc = launch_kernel("iq4xs_moe_gate_up_kernel", iq4xs_moe_gate_up_kernel<T>, grid_a, dim3(kThreads), lds_a, s,
                          w_gate, w_up, logits, x, topk_ids, topk_w, pairs, ws, hidden, ffn, n_experts, top_k);

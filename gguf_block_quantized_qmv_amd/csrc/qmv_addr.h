@@ -364,14 +364,17 @@ QMV_HDI Window moe_dn_window(int c, int i) { return i == 0 ? Window{-32 * c, 16}
 
 // ---- routed-expert decode (IQ4_XS experts) -------------------------------------
 
-constexpr int kIq4MoeUpRows = 16, kIq4MoeUpLanes = 16, kIq4MoeUpDepth = 2;
+constexpr int kIq4MoeUpDepth = 2;
+// Lanes per gate/up row: 32 for one token (8 rows per 256-thread workgroup),
+// 16 for two to four (16 rows), as for the Q4_K experts.
+QMV_HDI constexpr int iq4_moe_up_lanes(int t) { return t == 1 ? 32 : 16; }
+QMV_HDI constexpr int iq4_moe_up_rows(int t) { return 256 / iq4_moe_up_lanes(t); }
 constexpr int kIq4MoeDnRows = 8, kIq4MoeDnLanes = 8, kIq4MoeDnWaves = 4, kIq4MoeDnDepth = 4;
 
-// Gate/up: 16 lanes per row, rows past ffn read row 0 of the expert.
-QMV_HDI Iq4Lane iq4_moe_up_lane(int e, int ffn, int hidden, int bx, int tid) {
-  const int f = bx * kIq4MoeUpRows + tid / kIq4MoeUpLanes;
-  return iq4_lane(kIq4MoeUpLanes, hidden >> 8, (size_t)e * (size_t)ffn + (size_t)(f < ffn ? f : 0),
-                  tid % kIq4MoeUpLanes);
+// Gate/up: `lanes` lanes per row, rows past ffn read row 0 of the expert.
+QMV_HDI Iq4Lane iq4_moe_up_lane(int lanes, int e, int ffn, int hidden, int bx, int tid) {
+  const int f = bx * (256 / lanes) + tid / lanes;
+  return iq4_lane(lanes, hidden >> 8, (size_t)e * (size_t)ffn + (size_t)(f < ffn ? f : 0), tid % lanes);
 }
 // Down: lane (row i, sub-block j) of a wave; unit (slot, block) of W_down.
 struct Iq4DnLane {

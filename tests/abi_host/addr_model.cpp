@@ -264,13 +264,14 @@ void moe_iq4_case(int T, int hidden, int ffn, int E, int K) {
   const int max_slots = E < T * K ? E : T * K;
   char what[160];
   std::snprintf(what, sizeof what, "iq4_xs moe T %d hidden %d ffn %d E %d K %d", T, hidden, ffn, E, K);
-  const unsigned gx = (unsigned)((ffn + addr::kIq4MoeUpRows - 1) / addr::kIq4MoeUpRows);
-  const int nslots = addr::iq4_slots(addr::kIq4MoeUpLanes, nblk_up, addr::kIq4MoeUpDepth);
+  const int up_lanes = addr::iq4_moe_up_lanes(T), up_rows = addr::iq4_moe_up_rows(T);
+  const unsigned gx = (unsigned)((ffn + up_rows - 1) / up_rows);
+  const int nslots = addr::iq4_slots(up_lanes, nblk_up, addr::kIq4MoeUpDepth);
   for (int e : {0, E - 1}) {
     for (unsigned bx : groups_of(gx)) {
       for (int tid = 0; tid < 64 * addr::kIq4MoeDnWaves; ++tid) {
-        const int f = (int)bx * addr::kIq4MoeUpRows + tid / addr::kIq4MoeUpLanes;
-        const addr::Iq4Lane ln = addr::iq4_moe_up_lane(e, ffn, hidden, (int)bx, tid);
+        const int f = (int)bx * up_rows + tid / up_lanes;
+        const addr::Iq4Lane ln = addr::iq4_moe_up_lane(up_lanes, e, ffn, hidden, (int)bx, tid);
         for (int t : unit_steps(nslots, addr::kIq4MoeUpDepth)) {
           const bool live = t < ln.nlive;
           const size_t b = live ? ln.lane_base + addr::iq4_unit_offset(t, ln.unit_bytes) : ln.row_base;
