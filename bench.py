@@ -55,11 +55,11 @@ MEASURED = {
     # 4 GiB device copy (profiles/q4k_gemv_m1_hbm_traffic.md)
     "gemv_traffic": {"sources": (_CSRC + "q4k_gemv.hip", _CSRC + "q4k_common.h", _CSRC + "qmv_device.h",
                                  _CSRC + "qmv_layout.h", _CSRC + "qmv_addr.h"),
-                     "sha256": "f9a72f83928626bc37eba0ddccde42f734c43a51b2d45e3ce0ebec88f04279cd", "value": 101097390},
+                     "sha256": "8d050478633d4dd7826d5c86ecebb80bd5b4c9a4c22c876cff87ab939c38d9dc", "value": 101097390},
     # MFMA utilisation of the prefill GEMM at M=512 (profiles/q4k_prefill_m512_mfma.md)
     "prefill_mfma_util": {"sources": (_CSRC + "q4k_prefill.hip", _CSRC + "q4k_common.h", _CSRC + "qmv_device.h",
                                       _CSRC + "qmv_layout.h", _CSRC + "qmv_addr.h"),
-                          "sha256": "f206eb2a9832e7362fd39b5e86a171f80965530c5649c742b947cbaecf9d0551",
+                          "sha256": "fe9a9f3a48f01afcf8d6dc776be4c52274c32a771cb9028c7ff617b7c330b7b4",
                           "value": {"up": 0.374, "down": 0.388}},
 }
 
