@@ -89,3 +89,25 @@ def test_pair_rejects_overlapping_outputs(q, dev):
     with pytest.raises(q.QmvError) as e:
         q.qmv_q4_k_pair(w, w, x, n, k, y0=buf[:n].view(1, n), y1=buf[n // 2:n // 2 + n].view(1, n))
     assert e.value.code == -7   # QMV_ERR_ALIAS, raised before any launch
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_pair_full_size_sampled_rows(q, dev, m):
+    # the gate/up projections of the dense Q4_K_M decode pass in the launch the benchmark times:
+    # about 192 sampled rows of each output checked against the oracle, among them row n - 1 of
+    # matrix 0 and row 0 of matrix 1, the two sides of the boundary in the 2n-row grid
+    n, k = 17408, 5120
+    w0 = synth.torch_q4_k_weights(8100 + m, n, k, dev)
+    w1 = synth.torch_q4_k_weights(8200 + m, n, k, dev)
+    x = synth.bf16_normal(8300 + m, (m, k))
+    y0, y1 = q.qmv_q4_k_pair(w0, w1, to_dev(x, dev), n, k)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8400 + m)
+    row_bytes = (k // 256) * 144
+    for got, w, edge in ((y0, w0, [n - 1]), (y1, w1, [0])):
+        rows = np.unique(np.concatenate([rng.choice(n, 190, replace=False), edge, [n // 2]]))
+        wh = host(w.view(-1, row_bytes)[torch.as_tensor(rows, device=dev)])
+        ref = oracle.qmv_q4_k(wh.reshape(-1), x, len(rows), k)
+        yh = host(got)
+        assert np.isfinite(yh).all()
+        assert oracle.floored_rel_err(yh[:, rows], ref) <= GEMV_TOL
