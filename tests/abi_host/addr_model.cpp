@@ -508,9 +508,11 @@ int main(int argc, char **argv) {
 
   lap("largest matrices");
   // routed-expert decode: the 35B-A3B layer (hidden 2048, ffn 768, 128
-  // experts, top-8) and ragged and one-expert cases
+  // experts, top-8), ragged and one-expert cases, and rows whose last pass is
+  // partial at both lane widths (5 and 18 blocks)
   for (int T = 1; T <= 4; ++T) {
-    for (auto c : {std::vector<int>{2048, 768, 128, 8}, {256, 256, 1, 1}, {512, 1280, 16, 3}, {4096, 512, 64, 8}}) {
+    for (auto c : {std::vector<int>{2048, 768, 128, 8}, {256, 256, 1, 1}, {512, 1280, 16, 3}, {4096, 512, 64, 8},
+                   {1280, 256, 16, 4}, {4608, 256, 16, 4}}) {
       if (layout::q4k_moe_fits_lds(T, c[0], c[1], c[3])) moe_q4k_case(T, c[0], c[1], c[2], c[3]);
       if (layout::iq4xs_moe_fits_lds(T, c[0], c[1], c[3])) moe_iq4_case(T, c[0], c[1], c[2], c[3]);
     }

@@ -92,6 +92,26 @@ def test_iq4_xs_moe_token_bit_identical_alone_and_batched(q, dev):
         assert np.array_equal(y1[0].view(np.uint32), y3[t].view(np.uint32)), t
 
 
+@pytest.mark.parametrize("hidden", [256, 1280, 4608])
+def test_iq4_xs_moe_token_bit_identical_alone_and_batched_ragged_rows(q, dev, hidden):
+    # rows of 1, 5 and 18 super-blocks, so that the one-token lane width (32 lanes per row) and
+    # the several-token one (16) both end on a partial pass; a token's bits must not depend on the
+    # token count, and the batched call must pass the oracle gate
+    ffn, ne, tk = 256, 16, 4
+    bank = synth.moe_bank_iq4_xs(160 + hidden // 256, ne, hidden, ffn)
+    logits = synth.moe_logits(161, 4, ne)
+    logits[3] = logits[1]                           # tokens 1 and 3 share all experts
+    x = synth.bf16_normal(162, (4, hidden))
+    y4, ids4, *_ = _run(q, dev, bank, logits, x, hidden, ffn, ne, tk)
+    yr, idr, _ = oracle.moe_iq4_xs(*bank, logits, x, hidden, ffn, ne, tk)
+    assert np.array_equal(ids4, idr)
+    assert oracle.floored_rel_err(y4, yr) <= GEMV_TOL
+    for t in range(4):
+        y1, ids1, *_ = _run(q, dev, bank, logits[t:t + 1], x[t:t + 1], hidden, ffn, ne, tk)
+        assert np.array_equal(ids1[0], ids4[t])
+        assert np.array_equal(y1[0].view(np.uint32), y4[t].view(np.uint32)), t
+
+
 def test_iq4_xs_moe_deterministic(q, dev):
     hidden, ffn, ne, tk = 2048, 768, 128, 8
     bank = synth.moe_bank_iq4_xs(142, ne, hidden, ffn)
