@@ -111,3 +111,42 @@ def test_pair_full_size_sampled_rows(q, dev, m):
         yh = host(got)
         assert np.isfinite(yh).all()
         assert oracle.floored_rel_err(yh[:, rows], ref) <= GEMV_TOL
+
+
+def test_pair_and_down_graph_replays_match_eager(q, dev):
+    # one layer of the dense decode pass (the pair launch for gate and up, then the down launch)
+    # captured once and replayed three times, with eager calls on other inputs in between: every
+    # replay reproduces the eager outputs bit for bit
+    n, k = 17408, 5120
+    wg = synth.torch_q4_k_weights(8500, n, k, dev)
+    wu = synth.torch_q4_k_weights(8501, n, k, dev)
+    wd = synth.torch_q4_k_weights(8502, k, n, dev)
+    x = to_dev(synth.bf16_normal(8503, (1, k)), dev)
+    h = to_dev(synth.bf16_normal(8504, (1, n)), dev)
+    other = to_dev(synth.bf16_normal(8505, (1, k)), dev)
+    g_ref, u_ref = (host(t) for t in q.qmv_q4_k_pair(wg, wu, x, n, k))
+    d_ref = host(q.qmv_q4_k(wd, h, k, n))
+    yg = torch.empty((1, n), dtype=torch.float32, device=dev)
+    yu = torch.empty((1, n), dtype=torch.float32, device=dev)
+    yd = torch.empty((1, k), dtype=torch.float32, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        q.qmv_q4_k_pair(wg, wu, x, n, k, y0=yg, y1=yu)
+        q.qmv_q4_k(wd, h, k, n, y=yd)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.qmv_q4_k_pair(wg, wu, x, n, k, y0=yg, y1=yu)
+        q.qmv_q4_k(wd, h, k, n, y=yd)
+    for i in range(3):
+        for t in (yg, yu, yd):
+            t.fill_(float("nan"))
+        q.qmv_q4_k_pair(wu, wg, other, n, k)   # eager work on other inputs between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(host(yg)), _bits(g_ref)), (i, "gate")
+        assert np.array_equal(_bits(host(yu)), _bits(u_ref)), (i, "up")
+        assert np.array_equal(_bits(host(yd)), _bits(d_ref)), (i, "down")
